@@ -1,0 +1,260 @@
+"""Gated causal GQA attention at head_dim 256 for MI355X (gfx950): Python binding.
+
+A thin layer over the C ABI of libgqa_attn.so (include/gqa_attn.h) with the same
+names.  It turns torch tensors into pointers and strides, takes the stream from
+torch, allocates the workspace through torch when the caller gives none, and
+raises AttnError for a nonzero status.  Every step of the computation runs in
+the library's HIP kernels; there is no fallback: if the library is not built,
+every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _abi
+
+__all__ = [
+    "AttnError", "lib", "prefill", "decode", "kv_append", "merge", "head_chunk_plan", "workspace_bytes",
+    "describe_plan", "plan_args", "variant_name", "prompt_prefill",
+]
+
+_LIB = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_abi.STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = _abi.STATUS.get(status, str(status))
+
+
+def lib() -> C.CDLL:
+    """The loaded library (loaded once)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _abi.load()
+    return _LIB
+
+
+def _check(status: int) -> None:
+    if status != _abi.OK:
+        raise AttnError(status, lib().attn_strerror(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _abi.BF16
+    if t.dtype == torch.float16:
+        return _abi.F16
+    raise TypeError(f"q/k/v/gate must be bfloat16 or float16, got {t.dtype}")
+
+
+def _t4(t: torch.Tensor | None) -> _abi.Tensor:
+    if t is None:
+        return _abi.Tensor(None, 0, 0, 0)
+    if t.dim() != 4:
+        raise ValueError("tensors are 4-d [B, H, rows, 256]")
+    if t.stride(3) != 1:
+        raise ValueError("the last (head_dim) dimension must be contiguous")
+    return _abi.Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream_handle(t: torch.Tensor):
+    if t.is_cuda:
+        return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return C.c_void_p(0)
+
+
+def _mask_struct(mask, dtype_code: int) -> _abi.Mask:
+    if mask is None:
+        return _abi.Mask(_abi.MASK_NONE, 1, 1, 0, None, 0, 0, 0)
+    if mask.dim() != 4:
+        raise ValueError("mask must be 4-d [Bm, Hm, rows, >= kv_len]")
+    if mask.stride(3) != 1:
+        raise ValueError("the mask's key dimension must be contiguous")
+    if mask.dtype in (torch.bool, torch.uint8):
+        kind = _abi.MASK_BOOL_U8
+    elif mask.dtype == torch.float32:
+        kind = _abi.MASK_ADD_F32
+    elif (mask.dtype == torch.bfloat16 and dtype_code == _abi.BF16) or (
+            mask.dtype == torch.float16 and dtype_code == _abi.F16):
+        kind = _abi.MASK_ADD
+    else:
+        raise TypeError(f"unsupported mask dtype {mask.dtype}")
+    return _abi.Mask(kind, mask.shape[0], mask.shape[1], 0, mask.data_ptr(),
+                     mask.stride(0) if mask.shape[0] > 1 else 0, mask.stride(1) if mask.shape[1] > 1 else 0,
+                     mask.stride(2))
+
+
+def _args(q, k_cache, v_cache, gate, out, *, kv_offset, kv_len, causal, scale, head_chunk, n_splits, mask):
+    dt = _dtype_code(q)
+    a = _abi.AttnArgs()
+    a.dtype = dt
+    a.B, a.Hq, a.rows, a.D = q.shape[0], q.shape[1], q.shape[2], q.shape[3]
+    a.Hkv = k_cache.shape[1]
+    a.kv_offset = int(kv_offset)
+    a.kv_len = int(kv_len)
+    a.capacity = k_cache.shape[2]
+    a.scale = float(scale)
+    a.causal = 1 if causal else 0
+    a.head_chunk = int(head_chunk)
+    a.n_splits = int(n_splits)
+    a.q, a.gate, a.out = _t4(q), _t4(gate), _t4(out)
+    a.k_cache, a.v_cache = _t4(k_cache), _t4(v_cache)
+    a.mask = _mask_struct(mask, dt)
+    for t in (k_cache, v_cache, gate, out):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError("q, k/v cache, gate and out must share one dtype")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    return a
+
+
+def _run(op: int, q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
+         n_splits=0, mask=None, out=None, workspace=None):
+    if kv_len is None:
+        kv_len = kv_offset + q.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    a = _args(q, k_cache, v_cache, gate, out, kv_offset=kv_offset, kv_len=kv_len, causal=causal, scale=scale,
+              head_chunk=head_chunk, n_splits=n_splits, mask=mask)
+    L = lib()
+    need = C.c_size_t(0)
+    _check(L.attn_workspace_bytes(C.byref(a), op, C.byref(need)))
+    if workspace is None and need.value:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    fn = L.attn_prefill if op == _abi.OP_PREFILL else L.attn_decode
+    _check(fn(C.byref(a), ws_ptr, ws_len, _stream_handle(q)))
+    return out
+
+
+def prefill(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
+            n_splits=0, mask=None, out=None, workspace=None):
+    """attn_prefill: q/gate [B, Hq, rows, 256], caches [B, Hkv, capacity, 256]; returns out."""
+    return _run(_abi.OP_PREFILL, q, k_cache, v_cache, gate, kv_offset=kv_offset, kv_len=kv_len, causal=causal,
+                scale=scale, head_chunk=head_chunk, n_splits=n_splits, mask=mask, out=out, workspace=workspace)
+
+
+def decode(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
+           n_splits=0, mask=None, out=None, workspace=None):
+    """attn_decode: 1..32 rows; head_chunk 0 = the policy, k = chunks of k heads."""
+    return _run(_abi.OP_DECODE, q, k_cache, v_cache, gate, kv_offset=kv_offset, kv_len=kv_len, causal=causal,
+                scale=scale, head_chunk=head_chunk, n_splits=n_splits, mask=mask, out=out, workspace=workspace)
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, *, kv_offset: int) -> None:
+    """kv_append: copy [B, Hkv, rows, 256] rows into the caches at kv_offset, bit for bit."""
+    a = _abi.KvAppendArgs()
+    a.dtype = _dtype_code(k_new)
+    a.B, a.Hkv, a.rows, a.D = k_new.shape[0], k_new.shape[1], k_new.shape[2], k_new.shape[3]
+    a.kv_offset = int(kv_offset)
+    a.capacity = k_cache.shape[2]
+    a.k_new, a.v_new, a.k_cache, a.v_cache = _t4(k_new), _t4(v_new), _t4(k_cache), _t4(v_cache)
+    for t in (v_new, k_cache, v_cache):
+        if t.dtype != k_new.dtype:
+            raise TypeError("k/v rows and caches must share one dtype")
+    if v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("k and v shapes differ")
+    if k_cache.shape[0] != k_new.shape[0] or k_cache.shape[1] != k_new.shape[1]:
+        raise ValueError("cache and new rows disagree on batch or KV heads")
+    _check(lib().kv_append(C.byref(a), _stream_handle(k_new)))
+
+
+def merge(partial_o, partial_lse, gate, out=None):
+    """attn_merge: partial_o [C, B, Hq, rows, 256] fp32, partial_lse [C, B, Hq, rows] fp32 (natural log)."""
+    if partial_o.dtype != torch.float32 or partial_lse.dtype != torch.float32:
+        raise TypeError("partials are float32")
+    if not partial_o.is_contiguous() or not partial_lse.is_contiguous():
+        raise ValueError("partials must be contiguous")
+    if out is None:
+        out = torch.empty_like(gate, memory_format=torch.contiguous_format)
+    a = _abi.MergeArgs()
+    a.dtype = _dtype_code(gate)
+    a.n_chunks, a.B, a.Hq, a.rows, a.D = partial_o.shape
+    if tuple(partial_lse.shape) != tuple(partial_o.shape[:4]) or tuple(gate.shape) != tuple(partial_o.shape[1:]):
+        raise ValueError("partials and gate disagree in shape")
+    a.partial_o, a.partial_lse = partial_o.data_ptr(), partial_lse.data_ptr()
+    a.gate, a.out = _t4(gate), _t4(out)
+    _check(lib().attn_merge(C.byref(a), _stream_handle(gate)))
+    return out
+
+
+def head_chunk_plan(rows: int, n_q_heads: int, n_kv_heads: int, enabled: bool = True) -> list:
+    """Chunk sizes (heads) of one KV group under the head-chunk rule."""
+    sizes = (C.c_int * _abi.MAX_CHUNKS)()
+    n = C.c_int(0)
+    _check(lib().attn_head_chunk_plan(rows, n_q_heads, n_kv_heads, 1 if enabled else 0, sizes, _abi.MAX_CHUNKS,
+                                      C.byref(n)))
+    return list(sizes[:n.value])
+
+
+_FAKE = 1 << 20  # an aligned, never dereferenced address for shape-only planning
+
+
+def plan_args(*, B: int, Hq: int, Hkv: int, rows: int, kv_offset: int, kv_len=None, capacity=None, causal=True,
+              head_chunk=0, n_splits=0, dtype="bf16", mask_kind=_abi.MASK_NONE, Bm=1, Hm=1, D=256):
+    """An AttnArgs for planning only (workspace_bytes / describe_plan): pointers are placeholders."""
+    if kv_len is None:
+        kv_len = kv_offset + rows
+    a = _abi.AttnArgs()
+    a.dtype = _abi.BF16 if dtype == "bf16" else _abi.F16
+    a.B, a.Hq, a.Hkv, a.D, a.rows = B, Hq, Hkv, D, rows
+    a.kv_offset, a.kv_len = kv_offset, kv_len
+    a.capacity = capacity if capacity is not None else kv_len
+    a.scale, a.causal, a.head_chunk, a.n_splits = 0.0, 1 if causal else 0, head_chunk, n_splits
+    t = _abi.Tensor(_FAKE, Hq * rows * D, rows * D, D)
+    a.q = a.gate = a.out = t
+    a.k_cache = a.v_cache = _abi.Tensor(_FAKE, Hkv * a.capacity * D, a.capacity * D, D)
+    a.mask = _abi.Mask(mask_kind, Bm, Hm, 0, _FAKE if mask_kind else None, 0, 0, kv_len)
+    return a
+
+
+def workspace_bytes(args: _abi.AttnArgs, op: int = _abi.OP_PREFILL) -> int:
+    n = C.c_size_t(0)
+    _check(lib().attn_workspace_bytes(C.byref(args), op, C.byref(n)))
+    return n.value
+
+
+def describe_plan(args: _abi.AttnArgs, op: int = _abi.OP_PREFILL) -> dict:
+    info = _abi.PlanInfo()
+    _check(lib().attn_describe_plan(C.byref(args), op, C.byref(info)))
+    d = {name: getattr(info, name) for name, _ in _abi.PlanInfo._fields_ if name != "chunk_sizes"}
+    d["chunk_sizes"] = list(info.chunk_sizes[:info.n_head_chunks])
+    d["variant_name"] = variant_name(info.variant)
+    return d
+
+
+def variant_name(variant: int) -> str:
+    return lib().attn_variant_name(variant).decode()
+
+
+def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int, kv_offset: int = 0, out=None, workspace=None,
+                   head_chunk=0, n_splits=0):
+    """A prompt in query blocks: for each block, kv_append its K/V rows, then attn_prefill it.
+
+    q/gate [B, Hq, N, 256] and k/v [B, Hkv, N, 256] hold the prompt (positions kv_offset ..
+    kv_offset + N - 1); k_cache/v_cache have room for them.  Block i attends to the cache plus
+    itself ("perf(qwen36): qualify M4 head-256 attention", Summary: query blocks of 128 or 512).
+    """
+    N = q.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if workspace is None:
+        need = 0
+        for s in range(0, N, q_block):
+            rows = min(q_block, N - s)
+            a = plan_args(B=q.shape[0], Hq=q.shape[1], Hkv=k.shape[1], rows=rows, kv_offset=kv_offset + s,
+                          capacity=k_cache.shape[2], head_chunk=head_chunk, n_splits=n_splits)
+            need = max(need, workspace_bytes(a, _abi.OP_PREFILL))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    for s in range(0, N, q_block):
+        e = min(s + q_block, N)
+        kv_append(k[:, :, s:e], v[:, :, s:e], k_cache, v_cache, kv_offset=kv_offset + s)
+        prefill(q[:, :, s:e], k_cache, v_cache, gate[:, :, s:e], kv_offset=kv_offset + s, kv_len=kv_offset + e,
+                out=out[:, :, s:e], workspace=workspace, head_chunk=head_chunk, n_splits=n_splits)
+    return out

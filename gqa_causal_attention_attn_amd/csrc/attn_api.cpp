@@ -1,0 +1,352 @@
+// Host side of libgqa_attn: argument validation, the head-chunk and KV-split plans, workspace
+// sizing, and the launches.  Every check runs before anything is enqueued, so an invalid call
+// writes nothing.  Head counts are validated before any division (TensorFold PR #1009, the
+// config-reader commit: zero heads and uneven head groups are refused with ordinary errors).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "attn_internal.h"
+#include "gqa_attn.h"
+
+namespace {
+
+using gqa::kHeadDim;
+using gqa::kKeysPerTile;
+using gqa::kPairsPerWave;
+using gqa::kWavesPerBlock;
+
+constexpr int kRowPairLimit = 32;  // the head-chunk rule's 32 (head, row) pairs per call
+
+struct Plan {
+  int G;
+  int chunk;
+  int n_chunks;
+  int chunk_sizes[ATTN_MAX_CHUNKS];
+  int waves_per_chunk;
+  int n_tiles;
+  int n_splits;
+  int keys_per_split;
+  int64_t grid;
+  size_t ws_o_bytes;
+  size_t ws_bytes;
+};
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool strides_ok(const attn_tensor& t) {
+  return t.stride_b % 8 == 0 && t.stride_h % 8 == 0 && t.stride_row % 8 == 0;
+}
+
+// The rule itself, for one group of `gqa` heads (callers validated the head counts).
+int chunk_rule(int rows, int gqa, int enabled, int* sizes, int cap) {
+  int n = 0;
+  if (!enabled || rows > kRowPairLimit || (int64_t)rows * gqa <= kRowPairLimit) {
+    if (cap < 1) return -1;
+    sizes[n++] = gqa;
+    return n;
+  }
+  const int size = gqa < kRowPairLimit / rows ? gqa : kRowPairLimit / rows;
+  for (int left = gqa; left > 0; left -= size) {
+    if (n >= cap) return -1;
+    sizes[n++] = left < size ? left : size;
+  }
+  return n;
+}
+
+int validate(const attn_args* a, int op) {
+  if (!a) return ATTN_E_NULL;
+  if (op != ATTN_OP_PREFILL && op != ATTN_OP_DECODE) return ATTN_E_ARG;
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
+  if (a->B <= 0 || a->Hq <= 0 || a->Hkv <= 0) return ATTN_E_HEADS;
+  if (a->Hq % a->Hkv != 0) return ATTN_E_HEADS;
+  const int G = a->Hq / a->Hkv;
+  if (G > ATTN_MAX_CHUNKS) return ATTN_E_HEADS;
+  if (a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
+  if (a->rows < 1) return ATTN_E_ROWS;
+  if (op == ATTN_OP_DECODE && a->rows > ATTN_MAX_DECODE_ROWS) return ATTN_E_ROWS;
+  if (a->kv_offset < 0 || a->kv_len < 1 || a->capacity < a->kv_len) return ATTN_E_KV;
+  if (a->kv_len > INT32_MAX - kKeysPerTile || a->kv_offset + a->rows > INT32_MAX - kKeysPerTile) return ATTN_E_KV;
+  if (a->causal && a->kv_len < a->kv_offset + a->rows) return ATTN_E_KV;
+  if (!(a->scale >= 0.0f) || !isfinite(a->scale)) return ATTN_E_ARG;
+  if (a->causal != 0 && a->causal != 1) return ATTN_E_ARG;
+  if (a->n_splits < 0) return ATTN_E_ARG;
+  if (a->head_chunk < 0 || a->head_chunk > G) return ATTN_E_HEAD_CHUNK;
+  if (!a->q.ptr || !a->gate.ptr || !a->out.ptr || !a->k_cache.ptr || !a->v_cache.ptr) return ATTN_E_NULL;
+  const attn_tensor* ts[5] = {&a->q, &a->gate, &a->out, &a->k_cache, &a->v_cache};
+  for (const attn_tensor* t : ts) {
+    if (!aligned16(t->ptr) || !strides_ok(*t)) return ATTN_E_LAYOUT;
+  }
+  const attn_mask& m = a->mask;
+  if (m.kind < ATTN_MASK_NONE || m.kind > ATTN_MASK_ADD_F32) return ATTN_E_MASK;
+  if (m.kind != ATTN_MASK_NONE) {
+    if (!m.ptr) return ATTN_E_MASK;
+    if (m.Bm != 1 && m.Bm != a->B) return ATTN_E_MASK;
+    if (m.Hm != 1 && m.Hm != a->Hq) return ATTN_E_MASK;
+    if (m.stride_b < 0 || m.stride_h < 0 || m.stride_row < 0) return ATTN_E_MASK;
+  }
+  return ATTN_OK;
+}
+
+int make_plan(const attn_args* a, int op, Plan* P) {
+  memset(P, 0, sizeof(*P));
+  const int G = a->Hq / a->Hkv;
+  P->G = G;
+  if (a->head_chunk == 0) {
+    P->n_chunks = chunk_rule(a->rows, G, 1, P->chunk_sizes, ATTN_MAX_CHUNKS);
+  } else {
+    const int c = a->head_chunk;
+    P->n_chunks = 0;
+    for (int left = G; left > 0; left -= c) P->chunk_sizes[P->n_chunks++] = left < c ? left : c;
+  }
+  if (P->n_chunks <= 0) return ATTN_E_ARG;
+  P->chunk = P->chunk_sizes[0];
+  P->waves_per_chunk = (int)cdiv((int64_t)P->chunk * a->rows, kPairsPerWave);
+  P->n_tiles = (int)cdiv((int64_t)P->n_chunks * P->waves_per_chunk, kWavesPerBlock);
+
+  // KV splits depend only on the unchunked shape, so every head-chunk choice splits the keys
+  // the same way and gives the same bits.
+  const int64_t base_tiles = cdiv(cdiv((int64_t)G * a->rows, kPairsPerWave), kWavesPerBlock);
+  const int64_t kv_hi = a->causal ? (a->kv_len < a->kv_offset + a->rows ? a->kv_len : a->kv_offset + a->rows)
+                                  : a->kv_len;
+  const int64_t n_kt = cdiv(kv_hi, kKeysPerTile);
+  int64_t S;
+  if (a->n_splits == 0) {
+    const int64_t base = (int64_t)a->B * a->Hkv * base_tiles;
+    const int64_t want = cdiv(gqa::kTargetBlocks, base);
+    const int64_t min_tiles = op == ATTN_OP_DECODE ? 2 : 4;
+    int64_t most = n_kt / min_tiles;
+    if (most < 1) most = 1;
+    S = want < most ? want : most;
+    if (S < 1) S = 1;
+  } else {
+    S = a->n_splits < n_kt ? a->n_splits : n_kt;
+  }
+  const int64_t tps = cdiv(n_kt, S);
+  S = cdiv(n_kt, tps);
+  P->n_splits = (int)S;
+  P->keys_per_split = (int)(tps * kKeysPerTile);
+  P->grid = (int64_t)a->B * a->Hkv * S * P->n_tiles;
+  if (P->grid > INT32_MAX) return ATTN_E_ARG;
+  if (S > 1) {
+    const int64_t nrow = S * a->B * a->Hq * (int64_t)a->rows;
+    P->ws_o_bytes = (size_t)cdiv(nrow * kHeadDim * 4, 256) * 256;
+    P->ws_bytes = P->ws_o_bytes + (size_t)cdiv(nrow * 4, 256) * 256;
+  }
+  return ATTN_OK;
+}
+
+inline int variant_of(const attn_args* a) { return (a->dtype << 2) | a->mask.kind; }
+
+int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream) {
+  int st = validate(a, op);
+  if (st) return st;
+  Plan P;
+  st = make_plan(a, op, &P);
+  if (st) return st;
+  if (ws_bytes < P.ws_bytes || (P.ws_bytes && !ws)) return ATTN_E_WORKSPACE;
+  if (P.ws_bytes && !aligned16(ws)) return ATTN_E_LAYOUT;
+
+  gqa::FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = static_cast<const uint16_t*>(a->q.ptr);
+  p.gate = static_cast<const uint16_t*>(a->gate.ptr);
+  p.out = static_cast<uint16_t*>(a->out.ptr);
+  p.k = static_cast<const uint16_t*>(a->k_cache.ptr);
+  p.v = static_cast<const uint16_t*>(a->v_cache.ptr);
+  p.q_sb = a->q.stride_b, p.q_sh = a->q.stride_h, p.q_sr = a->q.stride_row;
+  p.g_sb = a->gate.stride_b, p.g_sh = a->gate.stride_h, p.g_sr = a->gate.stride_row;
+  p.o_sb = a->out.stride_b, p.o_sh = a->out.stride_h, p.o_sr = a->out.stride_row;
+  p.k_sb = a->k_cache.stride_b, p.k_sh = a->k_cache.stride_h, p.k_st = a->k_cache.stride_row;
+  p.v_sb = a->v_cache.stride_b, p.v_sh = a->v_cache.stride_h, p.v_st = a->v_cache.stride_row;
+  if (a->mask.kind != ATTN_MASK_NONE) {
+    p.mask = a->mask.ptr;
+    p.m_sb = a->mask.Bm == 1 ? 0 : a->mask.stride_b;  // an extent of 1 broadcasts
+    p.m_sh = a->mask.Hm == 1 ? 0 : a->mask.stride_h;
+    p.m_sr = a->mask.stride_row;
+  }
+  p.kv_offset = (int)a->kv_offset;
+  p.kv_len = (int)a->kv_len;
+  p.B = a->B, p.Hq = a->Hq, p.Hkv = a->Hkv, p.G = P.G, p.rows = a->rows;
+  p.causal = a->causal;
+  const float scale = a->scale > 0.0f ? a->scale : 1.0f / 16.0f;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.chunk = P.chunk;
+  p.waves_per_chunk = P.waves_per_chunk;
+  p.n_tiles = P.n_tiles;
+  p.n_splits = P.n_splits;
+  p.keys_per_split = P.keys_per_split;
+  p.grid = (int)P.grid;
+  if (P.n_splits > 1) {
+    p.part_o = static_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_o_bytes);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (gqa::launch_fwd(p, a->dtype, a->mask.kind, s) != hipSuccess) return ATTN_E_HIP;
+  if (P.n_splits > 1) {
+    gqa::MergeParams mp;
+    mp.part_o = p.part_o;
+    mp.part_lse = p.part_lse;
+    mp.gate = p.gate;
+    mp.out = p.out;
+    mp.g_sb = p.g_sb, mp.g_sh = p.g_sh, mp.g_sr = p.g_sr;
+    mp.o_sb = p.o_sb, mp.o_sh = p.o_sh, mp.o_sr = p.o_sr;
+    mp.n_chunks = P.n_splits, mp.B = a->B, mp.Hq = a->Hq, mp.rows = a->rows;
+    if (gqa::launch_merge(mp, a->dtype, s) != hipSuccess) return ATTN_E_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return GQA_ATTN_ABI_VERSION; }
+
+size_t attn_struct_size(int which) {
+  switch (which) {
+    case 0: return sizeof(attn_args);
+    case 1: return sizeof(kv_append_args);
+    case 2: return sizeof(merge_args);
+    case 3: return sizeof(attn_plan_info);
+    default: return 0;
+  }
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULL: return "a required pointer is NULL";
+    case ATTN_E_DTYPE: return "unknown dtype";
+    case ATTN_E_HEADS: return "invalid head counts (batch, query or KV heads not positive, or not a whole group)";
+    case ATTN_E_HEAD_DIM: return "head_dim must be 256";
+    case ATTN_E_ROWS: return "invalid number of query rows";
+    case ATTN_E_KV: return "invalid KV offset, length or capacity";
+    case ATTN_E_MASK: return "invalid mask (kind, extents, strides or pointer)";
+    case ATTN_E_LAYOUT: return "misaligned pointer or stride (16-byte pointers, strides in multiples of 8)";
+    case ATTN_E_HEAD_CHUNK: return "head_chunk must be 0 (policy) or 1..group size";
+    case ATTN_E_WORKSPACE: return "workspace too small";
+    case ATTN_E_HIP: return "HIP runtime error while enqueuing";
+    case ATTN_E_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_variant_name(int variant) {
+  static const char* const names[8] = {
+      "fwd_mfma32x32x16_bf16",          "fwd_mfma32x32x16_bf16_maskbool", "fwd_mfma32x32x16_bf16_maskadd",
+      "fwd_mfma32x32x16_bf16_maskf32",  "fwd_mfma32x32x16_f16",           "fwd_mfma32x32x16_f16_maskbool",
+      "fwd_mfma32x32x16_f16_maskadd",   "fwd_mfma32x32x16_f16_maskf32"};
+  return (variant >= 0 && variant < 8) ? names[variant] : "unknown";
+}
+
+int attn_head_chunk_plan(int rows, int n_q_heads, int n_kv_heads, int enabled, int* sizes, int cap, int* n_chunks) {
+  if (!sizes || !n_chunks) return ATTN_E_NULL;
+  if (rows < 1) return ATTN_E_ROWS;
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return ATTN_E_HEADS;
+  const int n = chunk_rule(rows, n_q_heads / n_kv_heads, enabled, sizes, cap);
+  if (n < 0) return ATTN_E_ARG;
+  *n_chunks = n;
+  return ATTN_OK;
+}
+
+int attn_workspace_bytes(const attn_args* a, int op, size_t* bytes) {
+  if (!bytes) return ATTN_E_NULL;
+  int st = validate(a, op);
+  if (st) return st;
+  Plan P;
+  st = make_plan(a, op, &P);
+  if (st) return st;
+  *bytes = P.ws_bytes;
+  return ATTN_OK;
+}
+
+int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
+  if (!info) return ATTN_E_NULL;
+  int st = validate(a, op);
+  if (st) return st;
+  Plan P;
+  st = make_plan(a, op, &P);
+  if (st) return st;
+  memset(info, 0, sizeof(*info));
+  info->op = op;
+  info->variant = variant_of(a);
+  info->group_size = P.G;
+  info->n_head_chunks = P.n_chunks;
+  info->head_chunk = P.chunk;
+  info->rows_per_wave = kPairsPerWave;
+  info->waves_per_block = kWavesPerBlock;
+  info->n_row_tiles = P.n_tiles;
+  info->n_splits = P.n_splits;
+  info->keys_per_split = P.keys_per_split;
+  info->keys_per_tile = kKeysPerTile;
+  info->lds_bytes = gqa::kFwdLdsBytes;
+  info->grid_blocks = P.grid;
+  info->workspace_bytes = (int64_t)P.ws_bytes;
+  for (int i = 0; i < P.n_chunks; ++i) info->chunk_sizes[i] = P.chunk_sizes[i];
+  return ATTN_OK;
+}
+
+int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* stream) {
+  return run_fwd(a, ATTN_OP_PREFILL, workspace, ws_bytes, stream);
+}
+
+int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stream) {
+  return run_fwd(a, ATTN_OP_DECODE, workspace, ws_bytes, stream);
+}
+
+int kv_append(const kv_append_args* a, void* stream) {
+  if (!a) return ATTN_E_NULL;
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
+  if (a->B <= 0 || a->Hkv <= 0) return ATTN_E_HEADS;
+  if (a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
+  if (a->rows < 1) return ATTN_E_ROWS;
+  if (a->kv_offset < 0 || a->capacity < 1 || a->kv_offset + a->rows > a->capacity || a->capacity > INT32_MAX)
+    return ATTN_E_KV;
+  const attn_tensor* ts[4] = {&a->k_new, &a->v_new, &a->k_cache, &a->v_cache};
+  for (const attn_tensor* t : ts)
+    if (!t->ptr) return ATTN_E_NULL;
+  for (const attn_tensor* t : ts)
+    if (!aligned16(t->ptr) || !strides_ok(*t)) return ATTN_E_LAYOUT;
+  gqa::AppendParams p;
+  for (int t = 0; t < 2; ++t) {
+    const attn_tensor& s = t ? a->v_new : a->k_new;
+    const attn_tensor& d = t ? a->v_cache : a->k_cache;
+    p.src[t] = static_cast<const uint16_t*>(s.ptr);
+    p.dst[t] = static_cast<uint16_t*>(d.ptr);
+    p.s_sb[t] = s.stride_b, p.s_sh[t] = s.stride_h, p.s_sr[t] = s.stride_row;
+    p.d_sb[t] = d.stride_b, p.d_sh[t] = d.stride_h, p.d_st[t] = d.stride_row;
+  }
+  p.B = a->B, p.Hkv = a->Hkv, p.rows = a->rows, p.kv_offset = (int)a->kv_offset;
+  if (gqa::launch_append(p, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
+}
+
+int attn_merge(const merge_args* a, void* stream) {
+  if (!a) return ATTN_E_NULL;
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
+  if (a->B <= 0 || a->Hq <= 0) return ATTN_E_HEADS;
+  if (a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
+  if (a->rows < 1) return ATTN_E_ROWS;
+  if (a->n_chunks < 1) return ATTN_E_ARG;
+  if ((int64_t)a->B * a->Hq * a->rows > (int64_t)INT32_MAX * 4) return ATTN_E_ARG;
+  if (!a->partial_o || !a->partial_lse || !a->gate.ptr || !a->out.ptr) return ATTN_E_NULL;
+  if (!aligned16(a->partial_o) || !aligned16(a->gate.ptr) || !aligned16(a->out.ptr) || !strides_ok(a->gate) ||
+      !strides_ok(a->out) || (reinterpret_cast<uintptr_t>(a->partial_lse) & 3u))
+    return ATTN_E_LAYOUT;
+  gqa::MergeParams p;
+  p.part_o = a->partial_o;
+  p.part_lse = a->partial_lse;
+  p.gate = static_cast<const uint16_t*>(a->gate.ptr);
+  p.out = static_cast<uint16_t*>(a->out.ptr);
+  p.g_sb = a->gate.stride_b, p.g_sh = a->gate.stride_h, p.g_sr = a->gate.stride_row;
+  p.o_sb = a->out.stride_b, p.o_sh = a->out.stride_h, p.o_sr = a->out.stride_row;
+  p.n_chunks = a->n_chunks, p.B = a->B, p.Hq = a->Hq, p.rows = a->rows;
+  if (gqa::launch_merge(p, a->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Merge pass and KV append for gfx950.
+//
+// Merge (TensorFold PR #1009, attention kernel-contract commit: decode rows over key chunks
+// and a merge of the chunks): per (b, h, r), lse = log sum_c exp(lse_c),
+// out = sum_c exp(lse_c - lse) o_c * sigmoid(gate), an empty chunk (lse_c = -Inf) adds
+// nothing and is not read, and a row with every chunk empty gives 0.  One wavefront per
+// row, four dims per lane; HBM-bound (it reads n_chunks x 1 KiB per row).
+//
+// Append (same commit, "pack, append and keep ... bit-exact"): a 16-byte copy of each new
+// K/V row into the cache; no arithmetic touches the bits.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "attn_internal.h"
+
+namespace gqa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int DT>
+__device__ __forceinline__ float to_f32(uint16_t w) {
+  if constexpr (DT == 0) return __builtin_bit_cast(float, (uint32_t)w << 16);
+  else return (float)__builtin_bit_cast(_Float16, w);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (DT == 0) return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
+  const int64_t row_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row_id >= n_rows) return;
+  const int r = (int)(row_id % p.rows);
+  const int h = (int)((row_id / p.rows) % p.Hq);
+  const int b = (int)(row_id / ((int64_t)p.rows * p.Hq));
+
+  float top = -INFINITY;
+  for (int c = lane; c < p.n_chunks; c += 64) top = fmaxf(top, p.part_lse[(int64_t)c * n_rows + row_id]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) top = fmaxf(top, __shfl_xor(top, o));
+
+  const int d0 = 4 * lane;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.0f;
+  if (top > -INFINITY) {
+    for (int c = 0; c < p.n_chunks; ++c) {
+      const float lc = p.part_lse[(int64_t)c * n_rows + row_id];
+      if (lc == -INFINITY) continue;
+      const float w = exp2f((lc - top) * kLog2e);
+      wsum += w;
+      const f32x4 oc = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)c * n_rows + row_id) * kHeadDim + d0);
+      acc += w * oc;
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
+  uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
+  const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
+  float gv[4] = {to_f32<DT>((uint16_t)(gw[0] & 0xffffu)), to_f32<DT>((uint16_t)(gw[0] >> 16)),
+                 to_f32<DT>((uint16_t)(gw[1] & 0xffffu)), to_f32<DT>((uint16_t)(gw[1] >> 16))};
+  float res[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) res[i] = acc[i] * inv * (1.0f / (1.0f + __expf(-gv[i])));
+  u32x2 ow;
+  ow[0] = pack2<DT>(res[0], res[1]);
+  ow[1] = pack2<DT>(res[2], res[3]);
+  *reinterpret_cast<u32x2*>(orow + d0) = ow;
+}
+
+// One 16-byte chunk per thread: (tensor, b, g, r, chunk of 8 elements).
+__global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
+  const int64_t per_tensor = (int64_t)p.B * p.Hkv * p.rows * (kHeadDim / 8);
+  const int64_t total = 2 * per_tensor;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int t = u >= per_tensor;
+    int64_t v = u - t * per_tensor;
+    const int c = (int)(v % (kHeadDim / 8));
+    v /= kHeadDim / 8;
+    const int r = (int)(v % p.rows);
+    v /= p.rows;
+    const int g = (int)(v % p.Hkv);
+    const int b = (int)(v / p.Hkv);
+    const u32x4 val = *reinterpret_cast<const u32x4*>(p.src[t] + b * p.s_sb[t] + g * p.s_sh[t] + r * p.s_sr[t] + 8 * c);
+    *reinterpret_cast<u32x4*>(p.dst[t] + b * p.d_sb[t] + g * p.d_sh[t] + (int64_t)(p.kv_offset + r) * p.d_st[t] +
+                              8 * c) = val;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
+  const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
+  const dim3 grid((unsigned)((n_rows + 3) / 4));
+  if (dtype == 0) hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
+  const int64_t total = 2LL * p.B * p.Hkv * p.rows * (kHeadDim / 8);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,388 @@
+// Main pass of gated causal GQA attention at head_dim 256 for gfx950 (CDNA4).
+//
+// One workgroup = one (batch b, KV head g, KV split s, tile of 4 x 32 (head, row) pairs of
+// that group).  The group's K and V are streamed through LDS in 64-key tiles and every
+// wavefront of the workgroup reuses each tile, so K/V is read once per group per split.
+// Per wavefront, 32 (head, row) pairs are the N dimension of v_mfma_f32_32x32x16 (bf16 or
+// fp16 in, fp32 accumulate):
+//
+//   S^T[key, pair] = K[key, :] . Q[pair, :]       A = K tile (LDS), B = Q (registers)
+//   O^T[dim, pair] += V^T[dim, key] . P^T[key, pair]  A = V^T tile (LDS), B = P (registers)
+//
+// With keys (and dims) on the MFMA rows and pairs on its columns, every lane owns one pair
+// (lane % 32) in both products, so the online softmax (running max, rescale, sum) needs no
+// cross-lane traffic except one swap with the lane 32 away, and the S accumulator is
+// already the B operand of the second product after a pack to 16 bits.  The KV positions
+// inside the V^T tile are permuted (bits 2 and 3 of the key index swapped) so that this
+// register order lines up with the A operand of the second product.
+//
+// The softmax follows the online (flash) formulation of the plain definition: per pair a
+// running max m (in log2 units of the scaled score), a running sum l and the accumulator O,
+// rescaled by exp2(m_old - m_new) when m moves.  m is only moved when the new maximum
+// exceeds it by more than 8 (a factor 256), which keeps every weight below 2^8 and skips
+// most rescales; the decision is per pair, so a pair's arithmetic does not depend on which
+// other pairs share its wavefront (head-chunked and unchunked launches agree bit for bit).
+// The weights are rounded to the 16-bit type once and both the sum l and P.V use the
+// rounded values.  With one split the epilogue applies 1/l and the gate sigmoid and rounds
+// once to 16 bits; with several splits it writes the normalised partial o and its natural
+// log-sum-exp for the merge pass.
+//
+// Operation: TensorFold PR #1009, attention kernel-contract commit (float64 gated GQA
+// attention as the reference, decode chunks and their merge); "Qwen head-chunked SDPA
+// (#113)", introduction (head chunks within a KV group).
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "attn_internal.h"
+
+namespace gqa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == 0) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+}
+
+// Two floats -> two 16-bit values (round to nearest even), low half = a.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (DT == 0) {
+    bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    f16x2 v = __builtin_convertvector((f32x2){a, b}, f16x2);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (DT == 0) {
+    return __builtin_bit_cast(float, w << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (DT == 0) {
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float one16(uint16_t w) {
+  return lo16<DT>((uint32_t)w);
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Workgroup i is dispatched to XCD i % 8.  Map it to a logical index so that each XCD
+// receives one contiguous range of logical workgroups (which share K/V in that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int x, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int xcd = x & 7, slot = x >> 3;
+  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// Mask value for key j of this lane's (b, h, r): returns the additive term in log2 units,
+// or -inf if the mask hides the key.
+template <int DT, int MK>
+__device__ __forceinline__ float mask_term(const void* base, int64_t row_off, int j) {
+  if constexpr (MK == 1) {
+    const uint8_t v = static_cast<const uint8_t*>(base)[row_off + j];
+    return v ? 0.0f : -INFINITY;
+  } else if constexpr (MK == 2) {
+    const float v = one16<DT>(static_cast<const uint16_t*>(base)[row_off + j]);
+    return v * kLog2e;
+  } else if constexpr (MK == 3) {
+    return static_cast<const float*>(base)[row_off + j] * kLog2e;
+  } else {
+    return 0.0f;
+  }
+}
+
+template <int DT, int MK>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFwdLdsBytes];
+  __shared__ int red_max[kWavesPerBlock];
+  __shared__ int red_min[kWavesPerBlock];
+  uint8_t* const ldsK = lds;                                // [64 keys][32 chunks of 16 B], chunk ^= key & 15
+  uint8_t* const ldsV = lds + kKeysPerTile * kHeadDim * 2;  // [256 dims][8 chunks of 16 B], chunk ^= dim & 7
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 31;  // pair slot of this lane
+  const int hf = lane >> 5;  // which half of the MFMA k-slots this lane feeds
+
+  // ---- which (b, g, split, tile) this workgroup serves
+  int bid = xcd_remap((int)blockIdx.x, p.grid);
+  const int tile_rev = bid % p.n_tiles;
+  bid /= p.n_tiles;
+  const int split = bid % p.n_splits;
+  bid /= p.n_splits;
+  const int g = bid % p.Hkv;
+  const int b = bid / p.Hkv;
+  const int tile = p.n_tiles - 1 - tile_rev;  // later rows (more keys) first
+
+  // ---- the (head, row) pair of this lane
+  const int wi = tile * kWavesPerBlock + wave;
+  const int chunk_idx = wi / p.waves_per_chunk;
+  const int f = (wi - chunk_idx * p.waves_per_chunk) * kPairsPerWave + li;
+  const int hstart = chunk_idx * p.chunk;
+  const int cs = min(p.chunk, p.G - hstart);
+  const bool valid = hstart < p.G && f < cs * p.rows;
+  const int r = valid ? f / cs : 0;
+  const int h = g * p.G + hstart + (valid ? f - (f / cs) * cs : 0);
+  const int lim = valid ? (p.causal ? min(p.kv_len, p.kv_offset + r + 1) : p.kv_len) : 0;
+
+  // ---- key range of the workgroup: [kv_lo, kv_end)
+  int wmax = lim, wmin = valid ? lim : 0x7fffffff;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    wmax = max(wmax, __shfl_xor(wmax, o));
+    wmin = min(wmin, __shfl_xor(wmin, o));
+  }
+  if (lane == 0) {
+    red_max[wave] = wmax;
+    red_min[wave] = wmin;
+  }
+  __syncthreads();
+  int kv_hi = red_max[0], lim_min = red_min[0];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w) {
+    kv_hi = max(kv_hi, red_max[w]);
+    lim_min = min(lim_min, red_min[w]);
+  }
+  const int kv_lo = split * p.keys_per_split;
+  const int kv_end = min(kv_lo + p.keys_per_split, kv_hi);
+
+  // ---- Q of this lane's pair, in the B-operand order: element t of qreg[kk] is dim 16 kk + 8 hf + t
+  u32x4 qreg[16];
+  {
+    const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)r * p.q_sr + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      qreg[kk] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+
+  const uint16_t* kbase = p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const uint16_t* vbase = p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
+  const int64_t mrow = MK ? ((p.m_sb ? (int64_t)b * p.m_sb : 0) + (p.m_sh ? (int64_t)h * p.m_sh : 0) +
+                             (int64_t)r * p.m_sr)
+                          : 0;
+
+  f32x16 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = (f32x16){};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  for (int j0 = kv_lo; j0 < kv_end; j0 += kKeysPerTile) {
+    __syncthreads();  // everyone is done with the previous tile
+    // K tile: unit u -> key u / 32, 16-byte chunk u % 32 (a wavefront reads two whole key rows)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 kv4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int u = tid + 256 * (4 * half + e);
+        const int j = j0 + (u >> 5);
+        kv4[e] = (u32x4){0u, 0u, 0u, 0u};
+        if (j < kv_end) kv4[e] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * p.k_st + 8 * (u & 31));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int u = tid + 256 * (4 * half + e);
+        const int key = u >> 5, c = u & 31;
+        *reinterpret_cast<u32x4*>(ldsK + key * 512 + ((c ^ (key & 15)) << 4)) = kv4[e];
+      }
+    }
+    // V tile, transposed to [dim][position]: unit -> 4 consecutive keys (kq) x 8 dims (dc).
+    // Keys 16s + 8a + 4c' + t sit at position 16s + 8c' + 4a + t (bits 2 and 3 swapped).
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int unit = tid + 256 * e2;
+      const int kq = unit & 15, dc = unit >> 4;
+      const int key0 = 4 * kq;
+      const int pos0 = (key0 & ~15) | ((key0 & 4) << 1) | ((key0 & 8) >> 1);
+      u32x4 rowv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int j = j0 + key0 + t;
+        rowv[t] = (u32x4){0u, 0u, 0u, 0u};
+        if (j < kv_end) rowv[t] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * p.v_st + 8 * dc);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const uint32_t a0 = rowv[0][w], a1 = rowv[1][w], a2 = rowv[2][w], a3 = rowv[3][w];
+        u32x2 col;
+        if (e & 1) {
+          col[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+          col[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+        } else {
+          col[0] = (a0 & 0xffffu) | (a1 << 16);
+          col[1] = (a2 & 0xffffu) | (a3 << 16);
+        }
+        const int dim = 8 * dc + e;
+        *reinterpret_cast<u32x2*>(ldsV + dim * 128 + (((pos0 >> 3) ^ (dim & 7)) << 4) + (pos0 & 7) * 2) = col;
+      }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      // S^T block: rows = 32 keys of this sub-tile, columns = the wave's 32 pairs
+      f32x16 sacc = (f32x16){};
+      const int krow = 32 * st + li;
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(ldsK + krow * 512 + (((2 * kk + hf) ^ (krow & 15)) << 4));
+        sacc = mfma32<DT>(a, qreg[kk], sacc);
+        if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the LDS reads in flight
+      }
+      // element q of sacc holds key jb + 8 (q / 4) + 4 hf + (q % 4) of this lane's pair
+      const int jb = j0 + 32 * st;
+      float sv[16];
+      const bool edge = MK != 0 || (jb + 32 > lim_min);
+      if (edge) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int j = jb + 8 * (q >> 2) + 4 * hf + (q & 3);
+          float t = sacc[q] * p.scale_log2;
+          if (j >= lim) t = -INFINITY;
+          if constexpr (MK != 0) {
+            if (j < lim) t += mask_term<DT, MK>(p.mask, mrow, j);
+          }
+          sv[q] = t;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) sv[q] = sacc[q] * p.scale_log2;
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int q = 1; q < 16; ++q) mx = fmaxf(mx, sv[q]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool upd = mx > m_run + kRescaleSlack;
+      const float m_next = upd ? mx : m_run;
+      const float alpha = upd ? exp2f(m_run - m_next) : 1.0f;
+      const float m_use = (m_next == -INFINITY) ? 0.0f : m_next;
+      uint32_t pw[8];
+      float lsum = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        pw[q] = pack2<DT>(exp2f(sv[2 * q] - m_use), exp2f(sv[2 * q + 1] - m_use));
+        lsum += lo16<DT>(pw[q]) + hi16<DT>(pw[q]);
+      }
+      l_run = l_run * alpha + lsum;
+      m_run = m_next;
+      if (__builtin_amdgcn_ballot_w64(upd)) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+      }
+      const u32x4 pb0 = (u32x4){pw[0], pw[1], pw[2], pw[3]};
+      const u32x4 pb1 = (u32x4){pw[4], pw[5], pw[6], pw[7]};
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int dim = 32 * db + li;
+        const uint8_t* vrow = ldsV + dim * 128;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(vrow + (((4 * st + hf) ^ (dim & 7)) << 4));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(vrow + (((4 * st + 2 + hf) ^ (dim & 7)) << 4));
+        oacc[db] = mfma32<DT>(a0, pb0, oacc[db]);
+        oacc[db] = mfma32<DT>(a1, pb1, oacc[db]);
+        if (db & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ---- epilogue: element q of oacc[db] is dim 32 db + 8 (q / 4) + 4 hf + (q % 4)
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!valid) return;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (p.n_splits == 1) {
+    const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
+    uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * hf;
+        const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
+        const float g0 = sigmoidf_(lo16<DT>(gw[0])), g1 = sigmoidf_(hi16<DT>(gw[0]));
+        const float g2 = sigmoidf_(lo16<DT>(gw[1])), g3 = sigmoidf_(hi16<DT>(gw[1]));
+        u32x2 ow;
+        ow[0] = pack2<DT>(oacc[db][4 * q4 + 0] * inv * g0, oacc[db][4 * q4 + 1] * inv * g1);
+        ow[1] = pack2<DT>(oacc[db][4 * q4 + 2] * inv * g2, oacc[db][4 * q4 + 3] * inv * g3);
+        *reinterpret_cast<u32x2*>(orow + d0) = ow;
+      }
+    }
+  } else {
+    const int64_t row_id = (((int64_t)split * p.B + b) * p.Hq + h) * p.rows + r;
+    float* prow = p.part_o + row_id * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * hf;
+        f32x4 v4 = {oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv, oacc[db][4 * q4 + 2] * inv,
+                    oacc[db][4 * q4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(prow + d0) = v4;
+      }
+    }
+    if (hf == 0) p.part_lse[row_id] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int DT, int MK>
+hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_fwd_kernel<DT, MK>), dim3(p.grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, hipStream_t stream) {
+  if (dtype == 0) {
+    switch (mask_kind) {
+      case 0: return launch_fwd_t<0, 0>(p, stream);
+      case 1: return launch_fwd_t<0, 1>(p, stream);
+      case 2: return launch_fwd_t<0, 2>(p, stream);
+      default: return launch_fwd_t<0, 3>(p, stream);
+    }
+  }
+  switch (mask_kind) {
+    case 0: return launch_fwd_t<1, 0>(p, stream);
+    case 1: return launch_fwd_t<1, 1>(p, stream);
+    case 2: return launch_fwd_t<1, 2>(p, stream);
+    default: return launch_fwd_t<1, 3>(p, stream);
+  }
+}
+
+}  // namespace gqa

@@ -1,0 +1,70 @@
+// Internal declarations shared by the host side and the kernel launchers of libgqa_attn.
+// Not part of the public ABI (include/gqa_attn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr int kHeadDim = 256;
+constexpr int kKeysPerTile = 64;     // keys staged in LDS per step
+constexpr int kWavesPerBlock = 4;    // wavefronts per workgroup of the main pass
+constexpr int kPairsPerWave = 32;    // (head, row) pairs per wavefront (one 32-wide MFMA column block)
+constexpr int kFwdLdsBytes = 2 * kKeysPerTile * kHeadDim * 2;  // K tile + transposed V tile
+constexpr int kTargetBlocks = 512;   // main-pass workgroups aimed for (256 CUs x 2 resident)
+
+// Parameters of the main (flash / split-KV) pass.  Strides are in elements.
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* gate;
+  uint16_t* out;
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* mask;
+  float* part_o;    // [n_splits, B, Hq, rows, 256] when n_splits > 1
+  float* part_lse;  // [n_splits, B, Hq, rows]
+  int64_t q_sb, q_sh, q_sr;
+  int64_t g_sb, g_sh, g_sr;
+  int64_t o_sb, o_sh, o_sr;
+  int64_t k_sb, k_sh, k_st;
+  int64_t v_sb, v_sh, v_st;
+  int64_t m_sb, m_sh, m_sr;
+  int kv_offset;
+  int kv_len;
+  int B, Hq, Hkv, G, rows;
+  int causal;
+  float scale_log2;      // scale * log2(e)
+  int chunk;             // heads per chunk
+  int waves_per_chunk;   // wavefronts serving one chunk
+  int n_tiles;           // workgroups per (batch, kv head, split)
+  int n_splits;
+  int keys_per_split;    // multiple of kKeysPerTile
+  int grid;              // workgroups in the launch
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  const uint16_t* gate;
+  uint16_t* out;
+  int64_t g_sb, g_sh, g_sr;
+  int64_t o_sb, o_sh, o_sr;
+  int n_chunks, B, Hq, rows;
+};
+
+struct AppendParams {
+  const uint16_t* src[2];
+  uint16_t* dst[2];
+  int64_t s_sb[2], s_sh[2], s_sr[2];
+  int64_t d_sb[2], d_sh[2], d_st[2];
+  int B, Hkv, rows;
+  int kv_offset;
+};
+
+// Launchers (return hipGetLastError()).  dtype 0 = bf16, 1 = fp16; mask_kind as attn_mask_kind.
+hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+
+}  // namespace gqa

@@ -1,0 +1,231 @@
+/*
+ * gqa_attn.h -- C ABI of the gated causal GQA attention library (head_dim 256, gfx950).
+ *
+ * The operation (TensorFold PR #1009, attention kernel-contract commit and
+ * Receipt "Attention"; "Qwen head-chunked SDPA (#113)", introduction):
+ *
+ *   for batch b, query head h, query row r (absolute position kv_offset + r):
+ *     g   = h / (Hq / Hkv)                       consecutive heads share a KV head
+ *     A   = { j < kv_len : j <= kv_offset + r (if causal), mask admits j }
+ *     s_j = scale * <Q[b,h,r,:], K[b,g,j,:]> + mask_add[b,h,r,j]
+ *     o   = sum_{j in A} softmax_A(s)_j * V[b,g,j,:]          (0 if A is empty)
+ *     out[b,h,r,:] = o * sigmoid(gate[b,h,r,:])
+ *
+ * with fp32 accumulation and one final rounding to the 16-bit output type.
+ * Prompts are processed in query blocks of `rows` rows that attend to the
+ * cache plus themselves ("perf(qwen36): qualify M4 head-256 attention",
+ * Summary); decode and verify rows (1..32) read the same contiguous cache.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument named as a tensor is DEVICE memory owned by the
+ *     caller; the library never allocates or frees device memory and keeps no
+ *     pointer after the call returns.  Argument structs are HOST memory, read
+ *     during the call only.
+ *   - Tensors are described by a base pointer and strides in ELEMENTS; the
+ *     last (head_dim) dimension is contiguous.  Base pointers must be 16-byte
+ *     aligned and row/head/batch strides multiples of 8 elements.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; buffers must stay alive until the stream reaches it.
+ *   - Functions return ATTN_OK (0) or an attn_status code.  All validation
+ *     happens before anything is enqueued; on an error nothing is written.
+ *     The library never aborts.
+ *   - The library holds no mutable global state and is reentrant; calls on
+ *     different streams may overlap if their output/workspace buffers differ.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_ATTN_ABI_VERSION 1
+#define ATTN_HEAD_DIM 256
+#define ATTN_MAX_DECODE_ROWS 32
+#define ATTN_MAX_CHUNKS 64
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = 1,       /* a required pointer is NULL */
+  ATTN_E_DTYPE = 2,      /* unknown dtype */
+  ATTN_E_HEADS = 3,      /* Hq <= 0, Hkv <= 0, Hq % Hkv != 0, B <= 0, or Hq/Hkv > 64 (checked before dividing) */
+  ATTN_E_HEAD_DIM = 4,   /* D != 256: fail closed */
+  ATTN_E_ROWS = 5,       /* rows < 1, or rows > 32 for attn_decode */
+  ATTN_E_KV = 6,         /* kv_offset < 0, kv_len < 1, kv_len > capacity, kv_len < kv_offset + rows when causal,
+                            or an append beyond capacity */
+  ATTN_E_MASK = 7,       /* unknown mask kind, Bm not in {1, B}, Hm not in {1, Hq}, or a NULL mask pointer */
+  ATTN_E_LAYOUT = 8,     /* misaligned pointer or stride */
+  ATTN_E_HEAD_CHUNK = 9, /* head_chunk < 0 or > Hq/Hkv */
+  ATTN_E_WORKSPACE = 10, /* workspace smaller than attn_workspace_bytes() reports */
+  ATTN_E_HIP = 11,       /* the HIP runtime reported an error when enqueuing */
+  ATTN_E_ARG = 12        /* any other invalid argument (bad op, n_splits < 0, scale not finite, ...) */
+} attn_status;
+
+typedef enum { ATTN_BF16 = 0, ATTN_F16 = 1 } attn_dtype;
+
+/* Mask kinds ("Qwen head-chunked SDPA (#113)", "Exact scope found during review": no mask,
+ * boolean and additive masks, broadcast over batch and heads).  kv is the contiguous last
+ * dimension; entries for keys >= kv_len are never read. */
+typedef enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_BOOL_U8 = 1,  /* uint8: nonzero = may attend */
+  ATTN_MASK_ADD = 2,      /* same 16-bit type as Q: added to the score, -Inf hides the key */
+  ATTN_MASK_ADD_F32 = 3   /* float32 additive */
+} attn_mask_kind;
+
+typedef enum { ATTN_OP_PREFILL = 0, ATTN_OP_DECODE = 1 } attn_op;
+
+/* A strided 4-d tensor [B, H, rows_or_tokens, 256]; strides in elements. */
+typedef struct {
+  void* ptr;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_row;
+} attn_tensor;
+
+/* Optional mask [Bm, Hm, rows, >= kv_len]; a stride may be 0 to broadcast. */
+typedef struct {
+  int32_t kind;   /* attn_mask_kind */
+  int32_t Bm;     /* 1 or B */
+  int32_t Hm;     /* 1 or Hq (indexed by the global query head) */
+  int32_t reserved;
+  const void* ptr;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_row;
+} attn_mask;
+
+/* Arguments of attn_prefill / attn_decode. */
+typedef struct {
+  int32_t dtype;       /* attn_dtype of q, k/v cache, gate, out and an ATTN_MASK_ADD mask */
+  int32_t B;           /* batch */
+  int32_t Hq;          /* query heads */
+  int32_t Hkv;         /* KV heads; Hq / Hkv = GQA group size G */
+  int32_t D;           /* head_dim, must be 256 */
+  int32_t rows;        /* query rows in this call (a query block, or 1..32 decode/verify rows) */
+  int64_t kv_offset;   /* cached keys before row 0 = absolute position of row 0 */
+  int64_t kv_len;      /* valid keys in the cache (normally kv_offset + rows, after kv_append) */
+  int64_t capacity;    /* allocated tokens per (b, kv head) in the cache */
+  float scale;         /* score scale; 0 means 1/sqrt(256) = 1/16 */
+  int32_t causal;      /* 1: row r sees keys <= kv_offset + r; 0: all keys < kv_len */
+  int32_t head_chunk;  /* 0: the head-chunk policy; k in 1..G: chunks of k heads (k = G: off) */
+  int32_t n_splits;    /* KV splits; 0 = automatic */
+  attn_tensor q;       /* [B, Hq, rows, 256] */
+  attn_tensor gate;    /* [B, Hq, rows, 256] */
+  attn_tensor out;     /* [B, Hq, rows, 256], written */
+  attn_tensor k_cache; /* [B, Hkv, capacity, 256] */
+  attn_tensor v_cache; /* [B, Hkv, capacity, 256] */
+  attn_mask mask;
+} attn_args;
+
+/* Arguments of kv_append: k_cache[b, g, kv_offset + r, :] = k_new[b, g, r, :] (and V), bit for bit. */
+typedef struct {
+  int32_t dtype;
+  int32_t B;
+  int32_t Hkv;
+  int32_t D;
+  int32_t rows;
+  int32_t reserved;
+  int64_t kv_offset;
+  int64_t capacity;
+  attn_tensor k_new;   /* [B, Hkv, rows, 256] */
+  attn_tensor v_new;   /* [B, Hkv, rows, 256] */
+  attn_tensor k_cache; /* [B, Hkv, capacity, 256], written */
+  attn_tensor v_cache; /* [B, Hkv, capacity, 256], written */
+} kv_append_args;
+
+/* Arguments of attn_merge. */
+typedef struct {
+  int32_t dtype;
+  int32_t n_chunks;         /* >= 1 */
+  int32_t B;
+  int32_t Hq;
+  int32_t rows;
+  int32_t D;
+  const float* partial_o;   /* [n_chunks, B, Hq, rows, 256] fp32, contiguous, normalised per chunk */
+  const float* partial_lse; /* [n_chunks, B, Hq, rows] fp32, contiguous, natural log; -Inf = empty chunk */
+  attn_tensor gate;         /* [B, Hq, rows, 256] */
+  attn_tensor out;          /* [B, Hq, rows, 256], written */
+} merge_args;
+
+/* The resolved plan of one call (what would run, for logging and validation). */
+typedef struct {
+  int32_t op;              /* attn_op */
+  int32_t variant;         /* kernel variant id (see attn_variant_name) */
+  int32_t group_size;      /* G = Hq / Hkv */
+  int32_t n_head_chunks;   /* chunks per KV group */
+  int32_t head_chunk;      /* heads per chunk (last chunk may be smaller) */
+  int32_t rows_per_wave;   /* (head, row) pairs per wavefront */
+  int32_t waves_per_block;
+  int32_t n_row_tiles;     /* workgroups per (batch, KV head, split) */
+  int32_t n_splits;        /* KV splits (1: the gate is applied in the same kernel) */
+  int32_t keys_per_split;
+  int32_t keys_per_tile;   /* keys staged in LDS per step */
+  int32_t lds_bytes;
+  int64_t grid_blocks;     /* workgroups of the main pass */
+  int64_t workspace_bytes; /* bytes of workspace the call needs */
+  int32_t chunk_sizes[ATTN_MAX_CHUNKS]; /* heads per chunk within a KV group, first n_head_chunks valid */
+} attn_plan_info;
+
+/* ABI version (GQA_ATTN_ABI_VERSION). */
+int attn_abi_version(void);
+
+/* sizeof of the argument structs as compiled into the library: which = 0 attn_args,
+ * 1 kv_append_args, 2 merge_args, 3 attn_plan_info.  Returns 0 for an unknown value. */
+size_t attn_struct_size(int which);
+
+/* Static description of a status code.  Never NULL. */
+const char* attn_strerror(int status);
+
+/* Name of a kernel variant id from attn_plan_info.variant.  Never NULL. */
+const char* attn_variant_name(int variant);
+
+/* The head-chunk rule of "Qwen head-chunked SDPA (#113)" (introduction; "Exact scope found
+ * during review"): if enabled and rows * G > 32 with rows <= 32, a KV group's G query heads
+ * are cut into chunks of min(G, 32 / rows) heads (integer division), the remainder forming a
+ * last, smaller chunk; otherwise one chunk of G.  Writes the chunk sizes of one group to
+ * sizes[0 .. *n_chunks) (host memory, capacity `cap`).  Pure host function; no device use.
+ * Errors: ATTN_E_ROWS (rows < 1), ATTN_E_HEADS (bad head counts), ATTN_E_NULL, ATTN_E_ARG
+ * (cap too small). */
+int attn_head_chunk_plan(int rows, int n_q_heads, int n_kv_heads, int enabled, int* sizes, int cap,
+                         int* n_chunks);
+
+/* Workspace bytes a call with these arguments needs (0 when it needs none).  op is attn_op.
+ * Validates `a` like the call itself would.  No device use. */
+int attn_workspace_bytes(const attn_args* a, int op, size_t* bytes);
+
+/* The resolved plan of a call with these arguments.  No device use. */
+int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info);
+
+/* Gated causal GQA attention for a block of query rows (any rows >= 1): the flash-style
+ * pass over the cache in 64-key tiles, split over KV when the grid would be too small, the
+ * log-sum-exp merge of the splits and the gate.  `workspace` (device, >= the bytes
+ * attn_workspace_bytes(a, ATTN_OP_PREFILL) reports; may be NULL if that is 0) holds the
+ * split partials.  Writes a->out. */
+int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/* The same operation for 1..32 decode / verify rows: a split-KV pass in which each
+ * workgroup reads its KV chunk once for all heads of the group, each wavefront serving one
+ * head chunk (a->head_chunk), then the merge pass.  TensorFold PR #1009 (attention
+ * kernel-contract commit) splits decode rows over key chunks and merges them. */
+int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/* Append `rows` new K and V rows to the cache at kv_offset: a pure bit copy (signed zeros
+ * and NaN payloads survive).  TensorFold PR #1009 compares append bit for bit. */
+int kv_append(const kv_append_args* a, void* stream);
+
+/* Combine per-chunk partials (o_c normalised within chunk c, lse_c = its log-sum-exp):
+ * out = sum_c exp(lse_c - lse) o_c / sum_c exp(lse_c - lse) * sigmoid(gate), chunks with
+ * lse_c = -Inf contribute nothing and an all-empty row gives 0.  The decode merge of
+ * TensorFold PR #1009 (attention kernel-contract commit), usable by callers that split KV
+ * across calls (a prefix and a tail, for instance). */
+int attn_merge(const merge_args* a, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

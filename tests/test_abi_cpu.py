@@ -1,0 +1,189 @@
+"""The C-ABI library on the CPU: it loads, exports what include/gqa_attn.h declares, plans
+like the oracle's head-chunk rule, and rejects every invalid argument with its status code
+before touching a device (no kernel is launched by any test here)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import gqa_causal_attention_attn_amd as ga
+from gqa_causal_attention_attn_amd import _abi
+from oracle import plan as oplan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "gqa_attn.h")) as f:
+        text = f.read()
+    body = text.split('extern "C" {', 1)[1]
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\(", body, flags=re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ga.lib()
+    declared = _declared_functions()
+    assert declared == set(_abi.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_sizes_and_version():
+    lib = ga.lib()
+    assert lib.attn_abi_version() == _abi.ABI_VERSION
+    for i, st in enumerate((_abi.AttnArgs, _abi.KvAppendArgs, _abi.MergeArgs, _abi.PlanInfo)):
+        assert lib.attn_struct_size(i) == C.sizeof(st)
+    assert lib.attn_struct_size(99) == 0
+    for code in list(_abi.STATUS) + [12345]:
+        assert lib.attn_strerror(code)
+
+
+def test_chunk_plan_matches_oracle_rule():
+    for rows in range(0, 41):
+        for hq in range(0, 34):
+            for hkv in range(0, 18):
+                valid = rows >= 1 and hq > 0 and hkv > 0 and hq % hkv == 0
+                if not valid:
+                    with pytest.raises(ga.AttnError):
+                        ga.head_chunk_plan(rows, hq, hkv)
+                    continue
+                assert ga.head_chunk_plan(rows, hq, hkv) == oplan.head_chunk_sizes(rows, hq, hkv)
+                assert ga.head_chunk_plan(rows, hq, hkv, enabled=False) == [hq // hkv]
+
+
+def test_plan_splits_do_not_depend_on_head_chunk():
+    for rows, G in ((1, 6), (4, 6), (6, 6), (9, 8), (17, 8), (32, 8), (5, 8)):
+        base = None
+        for hc in range(0, G + 1):
+            a = ga.plan_args(B=2, Hq=2 * G, Hkv=2, rows=rows, kv_offset=4097, head_chunk=hc)
+            d = ga.describe_plan(a, _abi.OP_DECODE)
+            key = (d["n_splits"], d["keys_per_split"])
+            base = base or key
+            assert key == base
+            if hc == 0:
+                assert d["chunk_sizes"] == oplan.head_chunk_sizes(rows, 2 * G, 2)
+            elif hc:
+                assert d["chunk_sizes"][0] == hc and sum(d["chunk_sizes"]) == G
+
+
+def test_plan_covers_every_key():
+    # the split plan reaches every key below the causal bound of the block
+    for rows, off in ((128, 0), (128, 32640), (512, 16384), (1, 4096), (32, 32768), (7, 63)):
+        a = ga.plan_args(B=1, Hq=24, Hkv=4, rows=rows, kv_offset=off)
+        d = ga.describe_plan(a, _abi.OP_PREFILL)
+        assert d["n_splits"] * d["keys_per_split"] >= off + rows
+        assert (d["n_splits"] - 1) * d["keys_per_split"] < off + rows
+        assert d["keys_per_split"] % d["keys_per_tile"] == 0
+
+
+def _good(**kw):
+    return ga.plan_args(**{**dict(B=1, Hq=24, Hkv=4, rows=4, kv_offset=100), **kw})
+
+
+REJECT = [
+    ("null args", None, "ATTN_E_NULL"),
+    ("dtype", dict(_set={"dtype": 7}), "ATTN_E_DTYPE"),
+    ("zero kv heads", dict(Hkv=0), "ATTN_E_HEADS"),
+    ("zero q heads", dict(Hq=0), "ATTN_E_HEADS"),
+    ("uneven groups", dict(Hq=10, Hkv=4), "ATTN_E_HEADS"),
+    ("batch 0", dict(B=0), "ATTN_E_HEADS"),
+    ("group over 64", dict(Hq=130, Hkv=2), "ATTN_E_HEADS"),
+    ("head dim 128", dict(D=128), "ATTN_E_HEAD_DIM"),
+    ("rows 0", dict(rows=0), "ATTN_E_ROWS"),
+    ("negative offset", dict(kv_offset=-1, kv_len=3), "ATTN_E_KV"),
+    ("kv_len short of causal rows", dict(kv_len=102), "ATTN_E_KV"),
+    ("kv_len beyond capacity", dict(kv_len=104, capacity=103), "ATTN_E_KV"),
+    ("kv_len 0", dict(_set={"kv_len": 0}), "ATTN_E_KV"),
+    ("head_chunk > G", dict(head_chunk=7), "ATTN_E_HEAD_CHUNK"),
+    ("head_chunk < 0", dict(head_chunk=-1), "ATTN_E_HEAD_CHUNK"),
+    ("negative splits", dict(n_splits=-2), "ATTN_E_ARG"),
+    ("nan scale", dict(_set={"scale": float("nan")}), "ATTN_E_ARG"),
+    ("null q", dict(_tensor=("q", 0, None)), "ATTN_E_NULL"),
+    ("null v cache", dict(_tensor=("v_cache", 0, None)), "ATTN_E_NULL"),
+    ("misaligned q", dict(_tensor=("q", 0, (1 << 20) + 8)), "ATTN_E_LAYOUT"),
+    ("odd row stride", dict(_tensor=("k_cache", 3, 260)), "ATTN_E_LAYOUT"),
+    ("mask kind", dict(mask_kind=9), "ATTN_E_MASK"),
+    ("mask batch extent", dict(mask_kind=1, Bm=2), "ATTN_E_MASK"),
+    ("mask head extent", dict(mask_kind=2, Hm=6), "ATTN_E_MASK"),
+    ("mask null", dict(_mask_null=True), "ATTN_E_MASK"),
+]
+
+
+def _build(spec):
+    if spec is None:
+        return None
+    spec = dict(spec)
+    setv = spec.pop("_set", {})
+    tensor = spec.pop("_tensor", None)
+    mask_null = spec.pop("_mask_null", False)
+    a = _good(**spec)
+    for k, v in setv.items():
+        setattr(a, k, v)
+    if tensor:
+        name, field, val = tensor
+        t = getattr(a, name)
+        if field == 0:
+            t.ptr = val
+        else:
+            t.stride_row = val
+        setattr(a, name, t)
+    if mask_null:
+        a.mask.kind = 1
+        a.mask.ptr = None
+    return a
+
+
+@pytest.mark.parametrize("name,spec,status", REJECT, ids=[r[0] for r in REJECT])
+@pytest.mark.parametrize("op", [_abi.OP_PREFILL, _abi.OP_DECODE])
+def test_rejections(name, spec, status, op):
+    lib = ga.lib()
+    a = _build(spec)
+    ptr = C.byref(a) if a is not None else None
+    n = C.c_size_t(0)
+    want = _abi.STATUS_CODE[status]
+    assert lib.attn_workspace_bytes(ptr, op, C.byref(n)) == want
+    fn = lib.attn_prefill if op == _abi.OP_PREFILL else lib.attn_decode
+    assert fn(ptr, None, 0, None) == want
+
+
+def test_decode_rejects_more_than_32_rows_but_prefill_accepts():
+    lib = ga.lib()
+    a = _good(rows=33)
+    n = C.c_size_t(0)
+    assert lib.attn_workspace_bytes(C.byref(a), _abi.OP_DECODE, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_ROWS"]
+    assert lib.attn_workspace_bytes(C.byref(a), _abi.OP_PREFILL, C.byref(n)) == 0
+
+
+def test_small_workspace_is_rejected_before_launch():
+    lib = ga.lib()
+    a = _good(rows=1, kv_offset=32768)
+    need = ga.workspace_bytes(a, _abi.OP_DECODE)
+    assert need > 0
+    assert lib.attn_decode(C.byref(a), C.c_void_p(1 << 20), need - 1, None) == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
+    assert lib.attn_decode(C.byref(a), None, need, None) == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
+
+
+def test_append_and_merge_rejections():
+    lib = ga.lib()
+    t = _abi.Tensor(1 << 20, 4 * 16 * 256, 16 * 256, 256)
+    a = _abi.KvAppendArgs(0, 1, 4, 256, 2, 0, 15, 16, t, t, t, t)
+    assert lib.kv_append(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_KV"]
+    a.kv_offset = 14
+    a.D = 64
+    assert lib.kv_append(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
+    a.D = 256
+    a.dtype = 3
+    assert lib.kv_append(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_DTYPE"]
+    a.dtype = 0
+    a.k_new = _abi.Tensor(None, 0, 0, 0)
+    assert lib.kv_append(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    assert lib.kv_append(None, None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    m = _abi.MergeArgs(0, 0, 1, 2, 3, 256, 1 << 20, 1 << 20, t, t)
+    assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_ARG"]
+    m.n_chunks = 2
+    m.partial_lse = (1 << 20) + 2
+    assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_LAYOUT"]
+    m.partial_o = None
+    assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_NULL"]

@@ -1,0 +1,264 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle on an MI355X.
+
+Tolerance: max abs error <= 1.5e-2 and median relative error <= 4e-3 on 16-bit outputs
+with fp32 accumulation; kv_append is compared bit for bit; head-chunk variants are
+compared bit for bit with each other.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_causal_attention_attn_amd as ga
+from oracle import reference
+from synth import inputs as syn
+from tests.gpu_util import prompt, to_bits, to_dev, to_f64
+from tests.parity import assert_close, compare
+
+pytestmark = pytest.mark.gpu
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _prompt_run(qb, kb, vb, gb, *, Hkv, q_block, dtype="bf16", head_chunk=0, n_splits=0):
+    q, k, v, g = (to_dev(x, dtype) for x in (qb, kb, vb, gb))
+    N = q.shape[2]
+    kc = torch.full((k.shape[0], Hkv, N, 256), float("nan"), dtype=q.dtype, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    out = torch.full_like(q, float("nan"))
+    ga.prompt_prefill(q, k, v, g, kc, vc, q_block=q_block, out=out, head_chunk=head_chunk, n_splits=n_splits)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+@needs_gpu
+@pytest.mark.parametrize("q_block", [128, 48])
+def test_tiny_prefill_24_over_4(q_block):
+    # batch 1, 24 query heads over 4 KV heads, 128 tokens, causal, gated
+    _say("tiny prefill qL", q_block)
+    qb, kb, vb, gb, _ = prompt(1000, B=1, Hq=24, Hkv=4, N=128)
+    out, kc, vc = _prompt_run(qb, kb, vb, gb, Hkv=4, q_block=q_block)
+    assert np.array_equal(to_bits(kc), kb) and np.array_equal(to_bits(vc), vb)
+    ref = reference.attention(syn.widen(qb), syn.widen(kb), syn.widen(vb), syn.widen(gb), n_kv_heads=4, kv_offset=0,
+                              kv_len=128)
+    _say(assert_close(to_f64(out), ref, "tiny prefill"))
+
+
+@needs_gpu
+@pytest.mark.parametrize("Hq,Hkv,N,q_block,n_splits", [
+    (24, 4, 200, 96, 0),     # ragged last block
+    (16, 2, 333, 128, 0),    # ragged, GQA 8
+    (16, 2, 300, 300, 3),    # forced KV splits + merge
+    (8, 8, 70, 70, 1),       # no grouping
+    (6, 1, 90, 32, 0),       # one KV head
+])
+def test_prefill_ragged_shapes(Hq, Hkv, N, q_block, n_splits):
+    _say("prefill", Hq, Hkv, N, q_block, n_splits)
+    qb, kb, vb, gb, _ = prompt(2000 + N, B=1, Hq=Hq, Hkv=Hkv, N=N)
+    out, _, _ = _prompt_run(qb, kb, vb, gb, Hkv=Hkv, q_block=q_block, n_splits=n_splits)
+    ref = reference.attention(syn.widen(qb), syn.widen(kb), syn.widen(vb), syn.widen(gb), n_kv_heads=Hkv,
+                              kv_offset=0, kv_len=N)
+    _say(assert_close(to_f64(out), ref, "prefill"))
+
+
+@needs_gpu
+def test_prefill_batch2_fp16_noncausal():
+    rng = syn.streams(31)
+    B, Hq, Hkv, rows, kv = 2, 16, 2, 40, 150
+    qb = syn.normal_bits(rng["q"], (B, Hq, rows, 256), "f16")
+    kb = syn.normal_bits(rng["k"], (B, Hkv, kv, 256), "f16")
+    vb = syn.normal_bits(rng["v"], (B, Hkv, kv, 256), "f16")
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, 256), "f16")
+    q, k, v, g = (to_dev(x, "f16") for x in (qb, kb, vb, gb))
+    out = ga.prefill(q, k, v, g, kv_offset=0, kv_len=kv, causal=False)
+    ref = reference.attention(*(syn.widen(x, "f16") for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=0,
+                              kv_len=kv, causal=False)
+    _say(assert_close(to_f64(out), ref, "fp16 noncausal"))
+
+
+def _decode_case(seed, *, B, Hq, Hkv, offset, rows, dtype="bf16"):
+    rng = syn.streams(seed)
+    kv_len = offset + rows
+    kb = syn.normal_bits(rng["k"], (B, Hkv, kv_len, 256), dtype)
+    vb = syn.normal_bits(rng["v"], (B, Hkv, kv_len, 256), dtype)
+    qb = syn.normal_bits(rng["q"], (B, Hq, rows, 256), dtype)
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, 256), dtype)
+    return qb, kb, vb, gb, rng
+
+
+@needs_gpu
+@pytest.mark.parametrize("rows", [1, 4])
+def test_decode_27b_shape(rows):
+    # 24 query heads over 4 KV heads, cache of 4096 keys, rows appended at offset 4096
+    _say("decode 27B rows", rows)
+    qb, kb, vb, gb, _ = _decode_case(1001, B=1, Hq=24, Hkv=4, offset=4096, rows=rows)
+    q, g = to_dev(qb), to_dev(gb)
+    cap = 4096 + 32
+    kc = torch.zeros((1, 4, cap, 256), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kc[:, :, :4096] = to_dev(kb[:, :, :4096])
+    vc[:, :, :4096] = to_dev(vb[:, :, :4096])
+    ga.kv_append(to_dev(kb[:, :, 4096:]), to_dev(vb[:, :, 4096:]), kc, vc, kv_offset=4096)
+    out = ga.decode(q, kc, vc, g, kv_offset=4096)
+    ref = reference.attention(syn.widen(qb), syn.widen(kb), syn.widen(vb), syn.widen(gb), n_kv_heads=4,
+                              kv_offset=4096, kv_len=4096 + rows)
+    _say(assert_close(to_f64(out), ref, "decode"))
+
+
+@needs_gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("offset", [4097, 32768])
+@pytest.mark.parametrize("rows", [1, 4, 5, 9, 17, 32])
+def test_head_chunked_verify(dtype, offset, rows):
+    # batch 2, 16 query heads over 2 KV heads, rows appended at the offset, broadcast additive mask
+    _say("verify", dtype, offset, rows)
+    B, Hq, Hkv = 2, 16, 2
+    qb, kb, vb, gb, rng = _decode_case(1004 + rows, B=B, Hq=Hq, Hkv=Hkv, offset=offset, rows=rows, dtype=dtype)
+    mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=1, kind="add", dtype=dtype)
+    q, k, v, g, m = (to_dev(x, dtype) for x in (qb, kb, vb, gb, mb))
+    outs = {}
+    for hc in [0] + list(range(1, 9)):
+        outs[hc] = to_bits(ga.decode(q, k, v, g, kv_offset=offset, mask=m, head_chunk=hc))
+    for hc in range(1, 9):
+        assert np.array_equal(outs[hc], outs[0]), f"head_chunk {hc} differs from the policy"
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=offset,
+                              kv_len=offset + rows, mask=syn.widen(mb, dtype), mask_kind="add")
+    _say(assert_close(syn.widen(outs[0], dtype), ref, "verify"))
+
+
+@needs_gpu
+@pytest.mark.parametrize("kind", ["full_head_add", "bool", "f32"])
+def test_verify_mask_kinds(kind):
+    B, Hq, Hkv, offset, rows = 2, 16, 2, 4097, 6
+    _say("mask kind", kind)
+    qb, kb, vb, gb, rng = _decode_case(77, B=B, Hq=Hq, Hkv=Hkv, offset=offset, rows=rows)
+    if kind == "full_head_add":
+        mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=Hq, kind="add")
+        m = to_dev(mb)
+        mref, mk = syn.widen(mb), "add"
+    elif kind == "bool":
+        mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=1, kind="bool")
+        m = torch.from_numpy(mb).cuda()
+        mref, mk = mb.astype(bool), "bool"
+    else:
+        mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=Hq, kind="add_f32")
+        mb = np.where(np.isfinite(mb), np.random.default_rng(5).standard_normal(mb.shape).astype(np.float32), mb)
+        m = torch.from_numpy(mb).cuda()
+        mref, mk = mb.astype(np.float64), "add"
+    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    out = ga.decode(q, k, v, g, kv_offset=offset, mask=m)
+    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=offset,
+                              kv_len=offset + rows, mask=mref, mask_kind=mk)
+    _say(assert_close(to_f64(out), ref, kind))
+
+
+@needs_gpu
+def test_kv_append_is_bit_exact():
+    nf = syn.nonfinite_bits("bf16")
+    rng = syn.streams(5)
+    new_k = syn.normal_bits(rng["k"], (2, 2, 5, 256))
+    new_v = syn.normal_bits(rng["v"], (2, 2, 5, 256))
+    new_k[0, 0, 0, :4] = [nf["-0"], nf["nan"], nf["+inf"], nf["-inf"]]
+    new_v[1, 1, 4, 250:] = nf["nan"]
+    cache = syn.normal_bits(rng["plant"], (2, 2, 20, 256))
+    kc, vc = to_dev(cache), to_dev(cache)
+    ga.kv_append(to_dev(new_k), to_dev(new_v), kc, vc, kv_offset=11)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kc), reference.kv_append(cache, new_k, 11))
+    assert np.array_equal(to_bits(vc), reference.kv_append(cache, new_v, 11))
+    with pytest.raises(ga.AttnError):
+        ga.kv_append(to_dev(new_k), to_dev(new_v), kc, vc, kv_offset=16)
+
+
+@needs_gpu
+def test_merge_matches_oracle():
+    rng = syn.streams(8)
+    B, Hq, Hkv, rows, kv = 1, 8, 2, 5, 90
+    q = syn.widen(syn.normal_bits(rng["q"], (B, Hq, rows, 256)))
+    k = syn.widen(syn.normal_bits(rng["k"], (B, Hkv, kv, 256)))
+    v = syn.widen(syn.normal_bits(rng["v"], (B, Hkv, kv, 256)))
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, 256))
+    chunks = [(0, 30), (30, 60), (60, 90), (90, 120)]  # the last chunk is empty
+    o, l_ = reference.partials(q, k, v, n_kv_heads=Hkv, kv_offset=kv - rows, kv_len=kv, chunks=chunks)
+    out = ga.merge(torch.from_numpy(o.astype(np.float32)).cuda(), torch.from_numpy(l_.astype(np.float32)).cuda(),
+                   to_dev(gb))
+    ref = reference.merge(o, l_, syn.widen(gb))
+    _say(assert_close(to_f64(out), ref, "merge"))
+
+
+@needs_gpu
+def test_closed_forms_on_gpu():
+    # constant V: every row returns c * sigmoid(gate); row 0 of a prompt sees one key: V_0 * sigmoid(gate)
+    qb, kb, vb, gb, _ = prompt(42, B=1, Hq=8, Hkv=2, N=100)
+    vb[:] = syn.f32_to_bits(np.full(vb.shape, 0.375, dtype=np.float32))
+    out, _, _ = _prompt_run(qb, kb, vb, gb, Hkv=2, q_block=100)
+    ref = 0.375 * reference.sigmoid(syn.widen(gb))
+    _say(assert_close(to_f64(out), ref, "constant V"))
+    qb, kb, vb, gb, _ = prompt(43, B=1, Hq=8, Hkv=2, N=64)
+    out, _, _ = _prompt_run(qb, kb, vb, gb, Hkv=2, q_block=64)
+    first = to_f64(out)[0, :, 0]
+    want = syn.widen(vb)[0, np.arange(8) // 4, 0] * reference.sigmoid(syn.widen(gb)[0, :, 0])
+    _say(assert_close(first, want, "single key"))
+
+
+@needs_gpu
+def test_empty_row_gives_zero():
+    B, Hq, Hkv, offset, rows = 1, 8, 2, 200, 3
+    qb, kb, vb, gb, rng = _decode_case(9, B=B, Hq=Hq, Hkv=Hkv, offset=offset, rows=rows)
+    mb = np.ones((1, 1, rows, offset + rows), dtype=np.uint8)
+    mb[0, 0, 1] = 0
+    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    out = to_f64(ga.decode(q, k, v, g, kv_offset=offset, mask=torch.from_numpy(mb).cuda()))
+    assert np.all(out[0, :, 1] == 0.0)
+    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=offset,
+                              kv_len=offset + rows, mask=mb.astype(bool), mask_kind="bool")
+    _say(assert_close(out, ref, "empty row"))
+
+
+@needs_gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_stress_cancellation_passes_with_fp32_accumulation(dtype):
+    rng = syn.streams(1234)
+    B, Hq, Hkv, rows, off = 1, 4, 2, 8, 24
+    qb, kb, vb, gb = syn.stress_cancellation(rng["plant"], B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_len=off + rows,
+                                             dtype=dtype)
+    q, k, v, g = (to_dev(x, dtype) for x in (qb, kb, vb, gb))
+    out = ga.decode(q, k, v, g, kv_offset=off)
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off,
+                              kv_len=off + rows)
+    _say(assert_close(syn.widen(to_bits(out), dtype), ref, "stress"))
+
+
+@needs_gpu
+def test_repeat_runs_are_bitwise_identical():
+    qb, kb, vb, gb, _ = prompt(7, B=1, Hq=16, Hkv=2, N=256)
+    a, _, _ = _prompt_run(qb, kb, vb, gb, Hkv=2, q_block=128)
+    b, _, _ = _prompt_run(qb, kb, vb, gb, Hkv=2, q_block=128)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@needs_gpu
+def test_planted_row_past_its_own_key_is_not_seen():
+    # each row's query points at the key just after its own position: a kernel that lets a
+    # row see one key too many lands far from the oracle
+    B, Hq, Hkv, off, rows = 1, 8, 2, 40, 6
+    qb, kb, vb, gb, _ = _decode_case(21, B=B, Hq=Hq, Hkv=Hkv, offset=off, rows=rows + 1)
+    k = syn.widen(kb)
+    q = syn.widen(qb)[:, :, :rows]
+    for h in range(Hq):
+        for r in range(rows):
+            q[0, h, r] = 0.5 * k[0, h // 4, off + r + 1]
+    qb2 = syn.f32_to_bits(q.astype(np.float32))
+    gb = gb[:, :, :rows]
+    dev = [to_dev(x) for x in (qb2, kb, vb, gb)]
+    out = to_f64(ga.decode(dev[0], dev[1], dev[2], dev[3], kv_offset=off, kv_len=off + rows))
+    good = reference.attention(syn.widen(qb2), k, syn.widen(vb), syn.widen(gb), n_kv_heads=Hkv, kv_offset=off,
+                               kv_len=off + rows)
+    assert compare(out, good)["ok"]
+    past = reference.attention(syn.widen(qb2), k, syn.widen(vb), syn.widen(gb), n_kv_heads=Hkv, kv_offset=off + 1,
+                               kv_len=off + rows + 1)
+    assert not compare(out, past)["ok"]
