@@ -1,31 +1,42 @@
 // Main pass of gated causal GQA attention at head_dim 256 for gfx950 (CDNA4).
 //
-// One workgroup = one (batch b, KV head g, KV split s, tile of 4 x 32 (head, row) pairs of
-// that group).  The group's K and V are streamed through LDS in 64-key tiles and every
-// wavefront of the workgroup reuses each tile, so K/V is read once per group per split.
+// One workgroup = one (batch b, KV head g, KV split s, tile of 8 x 32 (head, row) pairs of
+// that group).  The group's K and V are streamed through LDS in 64-key tiles and all eight
+// wavefronts reuse every tile, so K/V is read once per group per split.  Tiles move from
+// HBM to LDS with direct global->LDS loads (no registers, no VALU), double-buffered: tile
+// t + 1 is in flight while tile t is consumed.
+//
 // Per wavefront, 32 (head, row) pairs are the N dimension of v_mfma_f32_32x32x16 (bf16 or
 // fp16 in, fp32 accumulate):
 //
-//   S^T[key, pair] = K[key, :] . Q[pair, :]       A = K tile (LDS), B = Q (registers)
-//   O^T[dim, pair] += V^T[dim, key] . P^T[key, pair]  A = V^T tile (LDS), B = P (registers)
+//   S^T[key, pair]  = K[key, :] . Q[pair, :]          A = K tile (LDS), B = Q (registers)
+//   O^T[dim, pair] += V^T[dim, key] . P^T[key, pair]  A = V tile (LDS, transposing read), B = P
 //
 // With keys (and dims) on the MFMA rows and pairs on its columns, every lane owns one pair
-// (lane % 32) in both products, so the online softmax (running max, rescale, sum) needs no
-// cross-lane traffic except one swap with the lane 32 away, and the S accumulator is
-// already the B operand of the second product after a pack to 16 bits.  The KV positions
-// inside the V^T tile are permuted (bits 2 and 3 of the key index swapped) so that this
-// register order lines up with the A operand of the second product.
+// (lane % 32) in both products: the online softmax needs no cross-lane traffic except one
+// swap with the lane 32 away, and the S accumulator, packed to 16 bits, is already the B
+// operand of the second product.  The k-slots of that product are permuted keys: slot
+// 4a + t of lane half h holds key 16s + 8a + 4h + t, which is the order the S accumulator
+// leaves in the registers; the A operand is gathered in that order by ds_read_b64_tr_b16,
+// which hands each lane of a 16-lane group one column of a 4 x 16 block of 16-bit values
+// (4 keys x 16 dims) read as rows by the group.
 //
-// The softmax follows the online (flash) formulation of the plain definition: per pair a
-// running max m (in log2 units of the scaled score), a running sum l and the accumulator O,
-// rescaled by exp2(m_old - m_new) when m moves.  m is only moved when the new maximum
-// exceeds it by more than 8 (a factor 256), which keeps every weight below 2^8 and skips
-// most rescales; the decision is per pair, so a pair's arithmetic does not depend on which
-// other pairs share its wavefront (head-chunked and unchunked launches agree bit for bit).
-// The weights are rounded to the 16-bit type once and both the sum l and P.V use the
-// rounded values.  With one split the epilogue applies 1/l and the gate sigmoid and rounds
-// once to 16 bits; with several splits it writes the normalised partial o and its natural
-// log-sum-exp for the merge pass.
+// LDS layout of a 64-key x 256-dim tile (32 KiB): 16-byte cells (8 dims), index
+//   cell(key, c) = (c / 4) * 256 + (key / 16) * 64 + (c % 4) * 16 + slot,
+// slot = key % 16 for K and (key % 16 + 4 (c % 4)) % 16 for V; one direct load of a wavefront
+// fills one 1 KiB group (16 keys x 4 cells).  The V skew keeps the transposing reads of a
+// 16-lane group (4 keys x 2 cells) on distinct banks; K reads (16 keys, one cell) are
+// contiguous.  Every LDS address is a per-lane base plus a compile-time offset.
+//
+// The softmax is the online (flash) form of the plain definition: per pair a running max m
+// (log2 units of the scaled score), a running sum l and the accumulator O, rescaled by
+// exp2(m_old - m_new) when m moves.  m moves only when the new maximum exceeds it by more
+// than 8 (a factor 256), so weights stay below 2^8 and most rescales are skipped; the
+// decision is per pair, so a pair's arithmetic does not depend on which other pairs share
+// its wavefront (head-chunked and unchunked launches agree bit for bit).  Weights are
+// rounded to the 16-bit type once and both l and P.V use the rounded values.  With one
+// split the epilogue applies 1/l and the gate sigmoid and rounds once to 16 bits; with
+// several it writes the normalised partial o and its natural log-sum-exp for the merge.
 //
 // Operation: TensorFold PR #1009, attention kernel-contract commit (float64 gated GQA
 // attention as the reference, decode chunks and their merge); "Qwen head-chunked SDPA
@@ -40,6 +51,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -47,10 +59,13 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kThreads = kWavesPerBlock * 64;
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -67,35 +82,22 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   if constexpr (DT == 0) {
-    bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
-    return __builtin_bit_cast(uint32_t, v);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
   } else {
-    f16x2 v = __builtin_convertvector((f32x2){a, b}, f16x2);
-    return __builtin_bit_cast(uint32_t, v);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
   }
 }
 
 template <int DT>
 __device__ __forceinline__ float lo16(uint32_t w) {
-  if constexpr (DT == 0) {
-    return __builtin_bit_cast(float, w << 16);
-  } else {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-  }
+  if constexpr (DT == 0) return __builtin_bit_cast(float, w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
 }
 
 template <int DT>
 __device__ __forceinline__ float hi16(uint32_t w) {
-  if constexpr (DT == 0) {
-    return __builtin_bit_cast(float, w & 0xffff0000u);
-  } else {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ float one16(uint16_t w) {
-  return lo16<DT>((uint32_t)w);
+  if constexpr (DT == 0) return __builtin_bit_cast(float, w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
@@ -108,16 +110,14 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-// Mask value for key j of this lane's (b, h, r): returns the additive term in log2 units,
-// or -inf if the mask hides the key.
+// Additive mask term of key j for this lane's (b, h, r), in log2 units (-inf hides the key).
 template <int DT, int MK>
 __device__ __forceinline__ float mask_term(const void* base, int64_t row_off, int j) {
   if constexpr (MK == 1) {
-    const uint8_t v = static_cast<const uint8_t*>(base)[row_off + j];
-    return v ? 0.0f : -INFINITY;
+    return static_cast<const uint8_t*>(base)[row_off + j] ? 0.0f : -INFINITY;
   } else if constexpr (MK == 2) {
-    const float v = one16<DT>(static_cast<const uint16_t*>(base)[row_off + j]);
-    return v * kLog2e;
+    const uint16_t w = static_cast<const uint16_t*>(base)[row_off + j];
+    return lo16<DT>((uint32_t)w) * kLog2e;
   } else if constexpr (MK == 3) {
     return static_cast<const float*>(base)[row_off + j] * kLog2e;
   } else {
@@ -125,13 +125,34 @@ __device__ __forceinline__ float mask_term(const void* base, int64_t row_off, in
   }
 }
 
+// Issue the direct loads of one K tile and one V tile (keys j0 .. j0 + 63, clamped to jmax,
+// which only feeds keys that every pair masks) into kbuf / vbuf.  Wavefront w loads the
+// 1 KiB groups 4w .. 4w + 3 of each tile.
+__device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t* vbase, int64_t k_st, int64_t v_st,
+                                           int j0, int jmax, uint8_t* kbuf, uint8_t* vbuf, int wave, int lane) {
+  const int c_lo = lane >> 4;
+  const int key_lo_k = lane & 15;
+  const int key_lo_v = ((lane & 15) - 4 * c_lo) & 15;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int grp = wave * 4 + e;  // 0..31
+    const int c = (grp >> 2) * 4 + c_lo;
+    const int key_hi = grp & 3;
+    const int jk = min(j0 + key_hi * 16 + key_lo_k, jmax);
+    const int jv = min(j0 + key_hi * 16 + key_lo_v, jmax);
+    __builtin_amdgcn_global_load_lds(kbase + (int64_t)jk * k_st + 8 * c, (lds_void*)(kbuf + grp * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + (int64_t)jv * v_st + 8 * c, (lds_void*)(vbuf + grp * 1024), 16, 0, 0);
+  }
+}
+
 template <int DT, int MK>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kFwdLdsBytes];
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[kTileBytes];
   __shared__ int red_max[kWavesPerBlock];
   __shared__ int red_min[kWavesPerBlock];
-  uint8_t* const ldsK = lds;                                // [64 keys][32 chunks of 16 B], chunk ^= key & 15
-  uint8_t* const ldsV = lds + kKeysPerTile * kHeadDim * 2;  // [256 dims][8 chunks of 16 B], chunk ^= dim & 7
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -159,6 +180,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdParams p) {
   const int r = valid ? f / cs : 0;
   const int h = g * p.G + hstart + (valid ? f - (f / cs) * cs : 0);
   const int lim = valid ? (p.causal ? min(p.kv_len, p.kv_offset + r + 1) : p.kv_len) : 0;
+  const bool wave_active = __builtin_amdgcn_ballot_w64(valid) != 0;
 
   // ---- key range of the workgroup: [kv_lo, kv_end)
   int wmax = lim, wmin = valid ? lim : 0x7fffffff;
@@ -180,6 +202,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdParams p) {
   }
   const int kv_lo = split * p.keys_per_split;
   const int kv_end = min(kv_lo + p.keys_per_split, kv_hi);
+  const int n_kt = kv_end > kv_lo ? (kv_end - kv_lo + kKeysPerTile - 1) / kKeysPerTile : 0;
+
+  const uint16_t* kbase = p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const uint16_t* vbase = p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
 
   // ---- Q of this lane's pair, in the B-operand order: element t of qreg[kk] is dim 16 kk + 8 hf + t
   u32x4 qreg[16];
@@ -190,12 +216,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdParams p) {
       qreg[kk] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : (u32x4){0u, 0u, 0u, 0u};
     }
   }
+  const int64_t mrow = MK ? (int64_t)b * p.m_sb + (int64_t)h * p.m_sh + (int64_t)r * p.m_sr : 0;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q is in registers before the tile stream starts
+  if (n_kt > 0) issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo, kv_end - 1, kbuf0, vbuf0, wave, lane);
 
-  const uint16_t* kbase = p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
-  const uint16_t* vbase = p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
-  const int64_t mrow = MK ? ((p.m_sb ? (int64_t)b * p.m_sb : 0) + (p.m_sh ? (int64_t)h * p.m_sh : 0) +
-                             (int64_t)r * p.m_sr)
-                          : 0;
+  // per-lane LDS bases (see the layout above); everything else is a compile-time offset
+  const int k_lane = (li >> 4) * 1024 + hf * 256 + (li & 15) * 16;
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  const int tq = i16 >> 2, uq = i16 & 3;
+  const int c_lo_v = 2 * (grp16 & 1) + (uq >> 1);
+  const int xv = 4 * (grp16 >> 1) + tq + 4 * c_lo_v;
+  const int v_lane0 = c_lo_v * 256 + (xv & 15) * 16 + (uq & 1) * 8;
+  const int v_lane1 = c_lo_v * 256 + ((xv + 8) & 15) * 16 + (uq & 1) * 8;
 
   f32x16 oacc[8];
 #pragma unroll
@@ -203,69 +235,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdParams p) {
   float m_run = -INFINITY;
   float l_run = 0.0f;
 
-  for (int j0 = kv_lo; j0 < kv_end; j0 += kKeysPerTile) {
-    __syncthreads();  // everyone is done with the previous tile
-    // K tile: unit u -> key u / 32, 16-byte chunk u % 32 (a wavefront reads two whole key rows)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4 kv4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int u = tid + 256 * (4 * half + e);
-        const int j = j0 + (u >> 5);
-        kv4[e] = (u32x4){0u, 0u, 0u, 0u};
-        if (j < kv_end) kv4[e] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * p.k_st + 8 * (u & 31));
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int u = tid + 256 * (4 * half + e);
-        const int key = u >> 5, c = u & 31;
-        *reinterpret_cast<u32x4*>(ldsK + key * 512 + ((c ^ (key & 15)) << 4)) = kv4[e];
-      }
+  // One step: wait for tile t (in cur), start tile t + 1 into nxt, consume cur.  The two
+  // buffers are distinct objects, so the compiler can tell the direct loads into nxt from
+  // the reads of cur and does not wait for the former before the latter.
+  auto step = [&](int t, uint8_t* kcur, uint8_t* vcur, uint8_t* knxt, uint8_t* vnxt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t is in LDS for everyone; everyone is done with tile t - 1
+    if (t + 1 < n_kt) {
+      issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + 1) * kKeysPerTile, kv_end - 1, knxt, vnxt, wave, lane);
     }
-    // V tile, transposed to [dim][position]: unit -> 4 consecutive keys (kq) x 8 dims (dc).
-    // Keys 16s + 8a + 4c' + t sit at position 16s + 8c' + 4a + t (bits 2 and 3 swapped).
-#pragma unroll
-    for (int e2 = 0; e2 < 2; ++e2) {
-      const int unit = tid + 256 * e2;
-      const int kq = unit & 15, dc = unit >> 4;
-      const int key0 = 4 * kq;
-      const int pos0 = (key0 & ~15) | ((key0 & 4) << 1) | ((key0 & 8) >> 1);
-      u32x4 rowv[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int j = j0 + key0 + t;
-        rowv[t] = (u32x4){0u, 0u, 0u, 0u};
-        if (j < kv_end) rowv[t] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * p.v_st + 8 * dc);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const uint32_t a0 = rowv[0][w], a1 = rowv[1][w], a2 = rowv[2][w], a3 = rowv[3][w];
-        u32x2 col;
-        if (e & 1) {
-          col[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-          col[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        } else {
-          col[0] = (a0 & 0xffffu) | (a1 << 16);
-          col[1] = (a2 & 0xffffu) | (a3 << 16);
-        }
-        const int dim = 8 * dc + e;
-        *reinterpret_cast<u32x2*>(ldsV + dim * 128 + (((pos0 >> 3) ^ (dim & 7)) << 4) + (pos0 & 7) * 2) = col;
-      }
-    }
-    __syncthreads();
-
+    if (!wave_active) return;
+    const int j0 = kv_lo + t * kKeysPerTile;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       // S^T block: rows = 32 keys of this sub-tile, columns = the wave's 32 pairs
       f32x16 sacc = (f32x16){};
-      const int krow = 32 * st + li;
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(ldsK + krow * 512 + (((2 * kk + hf) ^ (krow & 15)) << 4));
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(kcur + k_lane + (kk >> 1) * 4096 + st * 2048 + (kk & 1) * 512);
         sacc = mfma32<DT>(a, qreg[kk], sacc);
-        if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the LDS reads in flight
       }
       // element q of sacc holds key jb + 8 (q / 4) + 4 hf + (q % 4) of this lane's pair
       const int jb = j0 + 32 * st;
@@ -275,12 +264,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int j = jb + 8 * (q >> 2) + 4 * hf + (q & 3);
-          float t = sacc[q] * p.scale_log2;
-          if (j >= lim) t = -INFINITY;
+          float tv = sacc[q] * p.scale_log2;
+          if (j >= lim) tv = -INFINITY;
           if constexpr (MK != 0) {
-            if (j < lim) t += mask_term<DT, MK>(p.mask, mrow, j);
+            if (j < lim) tv += mask_term<DT, MK>(p.mask, mrow, j);
           }
-          sv[q] = t;
+          sv[q] = tv;
         }
       } else {
 #pragma unroll
@@ -311,15 +300,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdParams p) {
       const u32x4 pb1 = (u32x4){pw[4], pw[5], pw[6], pw[7]};
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const int dim = 32 * db + li;
-        const uint8_t* vrow = ldsV + dim * 128;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(vrow + (((4 * st + hf) ^ (dim & 7)) << 4));
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(vrow + (((4 * st + 2 + hf) ^ (dim & 7)) << 4));
-        oacc[db] = mfma32<DT>(a0, pb0, oacc[db]);
-        oacc[db] = mfma32<DT>(a1, pb1, oacc[db]);
-        if (db & 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int off = db * 4096 + (2 * st + s) * 1024;
+          const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vcur + v_lane0 + off));
+          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vcur + v_lane1 + off));
+          const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+          const u32x4 a = (u32x4){w0[0], w0[1], w1[0], w1[1]};
+          oacc[db] = mfma32<DT>(a, s ? pb1 : pb0, oacc[db]);
+        }
       }
     }
+  };
+  for (int t = 0; t < n_kt; t += 2) {
+    step(t, kbuf0, vbuf0, kbuf1, vbuf1);
+    if (t + 1 < n_kt) step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
   }
 
   // ---- epilogue: element q of oacc[db] is dim 32 db + 8 (q / 4) + 4 hf + (q % 4)
@@ -362,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const FwdParams p) {
 
 template <int DT, int MK>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<DT, MK>), dim3(p.grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<DT, MK>), dim3(p.grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -9,10 +9,11 @@ namespace gqa {
 
 constexpr int kHeadDim = 256;
 constexpr int kKeysPerTile = 64;     // keys staged in LDS per step
-constexpr int kWavesPerBlock = 4;    // wavefronts per workgroup of the main pass
+constexpr int kWavesPerBlock = 8;    // wavefronts per workgroup of the main pass
 constexpr int kPairsPerWave = 32;    // (head, row) pairs per wavefront (one 32-wide MFMA column block)
-constexpr int kFwdLdsBytes = 2 * kKeysPerTile * kHeadDim * 2;  // K tile + transposed V tile
-constexpr int kTargetBlocks = 512;   // main-pass workgroups aimed for (256 CUs x 2 resident)
+constexpr int kTileBytes = kKeysPerTile * kHeadDim * 2;      // one K (or V) tile: 32 KiB
+constexpr int kFwdLdsBytes = 2 * 2 * kTileBytes;             // K and V tiles, double-buffered
+constexpr int kTargetBlocks = 256;   // main-pass workgroups aimed for (one per CU)
 
 // Parameters of the main (flash / split-KV) pass.  Strides are in elements.
 struct FwdParams {
