@@ -116,7 +116,9 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   int64_t S;
   if (a->n_splits == 0) {
     const int64_t base = (int64_t)a->B * a->Hkv * base_tiles;
-    const int64_t want = cdiv(gqa::kTargetBlocks, base);
+    // fill the CUs in one round of workgroups: never more than kTargetBlocks, so no second,
+    // mostly idle round follows
+    const int64_t want = gqa::kTargetBlocks / base;
     const int64_t min_tiles = op == ATTN_OP_DECODE ? 2 : 4;
     int64_t most = n_kt / min_tiles;
     if (most < 1) most = 1;

@@ -44,6 +44,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_internal.h"
 
 namespace gqa {
@@ -61,6 +63,16 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -98,6 +110,23 @@ template <int DT>
 __device__ __forceinline__ float hi16(uint32_t w) {
   if constexpr (DT == 0) return __builtin_bit_cast(float, w & 0xffff0000u);
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// One ds_read_b64_tr_b16 at a per-lane LDS byte address plus an immediate offset.  Written as
+// inline assembly so the offset stays in the instruction; the caller waits with lgkm_wait
+// before using the result (the compiler does not track this load).
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Wait until at most N LDS operations of this wave are outstanding; the operands tie the
+// wait to the registers that the following instructions read.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& a, u32x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
@@ -246,49 +275,78 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
     }
     if (!wave_active) return;
     const int j0 = kv_lo + t * kKeysPerTile;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    // address-space-3 views, so every read folds its compile-time offset into the instruction
+    const lds_u8* const kl = (const lds_u8*)kcur + k_lane;
+    const uint32_t vaddr0 = (uint32_t)(uintptr_t)((const lds_u8*)vcur + v_lane0);
+    const uint32_t vaddr1 = (uint32_t)(uintptr_t)((const lds_u8*)vcur + v_lane1);
+    static_for<2>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
       // S^T block: rows = 32 keys of this sub-tile, columns = the wave's 32 pairs
       f32x16 sacc = (f32x16){};
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(kcur + k_lane + (kk >> 1) * 4096 + st * 2048 + (kk & 1) * 512);
+        const u32x4 a = *(const lds_u32x4*)(kl + (kk >> 1) * 4096 + st * 2048 + (kk & 1) * 512);
         sacc = mfma32<DT>(a, qreg[kk], sacc);
       }
       // element q of sacc holds key jb + 8 (q / 4) + 4 hf + (q % 4) of this lane's pair
       const int jb = j0 + 32 * st;
-      float sv[16];
-      const bool edge = MK != 0 || (jb + 32 > lim_min);
-      if (edge) {
+      uint32_t pw[8];
+      float lsum = 0.0f;
+      float alpha, m_next;
+      bool upd;
+      if constexpr (MK == 0) {
+        // Raw scores; keys past the pair's causal / cache bound get -inf (only on sub-tiles that
+        // reach some pair's bound).  The scale folds into the exponent, and the max commutes
+        // with it (scale > 0), so every pair computes the same bits on either path.
+        float sm[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) sm[q] = sacc[q];
+        if (jb + 32 > lim_min) {  // wave-uniform: the sub-tile reaches some pair's bound
+          const int jl = jb + 4 * hf;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            if (jl + 8 * (q >> 2) + (q & 3) >= lim) sm[q] = -INFINITY;
+          }
+        }
+        float mr = fmaxf(fmaxf(sm[0], sm[1]), sm[2]);
+#pragma unroll
+        for (int q = 3; q < 15; q += 2) mr = fmaxf(fmaxf(mr, sm[q]), sm[q + 1]);
+        mr = fmaxf(mr, sm[15]);
+        mr = fmaxf(mr, __shfl_xor(mr, 32));
+        const float mx = mr * p.scale_log2;
+        upd = mx > m_run + kRescaleSlack;
+        m_next = upd ? mx : m_run;
+        alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_next) : 1.0f;
+        const float neg_m = (m_next == -INFINITY) ? 0.0f : -m_next;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sm[2 * q], p.scale_log2, neg_m)),
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(sm[2 * q + 1], p.scale_log2, neg_m)));
+          lsum += lo16<DT>(pw[q]) + hi16<DT>(pw[q]);
+        }
+      } else {
+        // scaled scores plus the mask term (log2 units); hidden and out-of-bound keys get -inf
+        float sv[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int j = jb + 8 * (q >> 2) + 4 * hf + (q & 3);
-          float tv = sacc[q] * p.scale_log2;
-          if (j >= lim) tv = -INFINITY;
-          if constexpr (MK != 0) {
-            if (j < lim) tv += mask_term<DT, MK>(p.mask, mrow, j);
-          }
-          sv[q] = tv;
+          const float tv = sacc[q] * p.scale_log2;
+          sv[q] = j < lim ? tv + mask_term<DT, MK>(p.mask, mrow, j) : -INFINITY;
         }
-      } else {
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) sv[q] = sacc[q] * p.scale_log2;
-      }
-      float mx = sv[0];
+        for (int q = 3; q < 15; q += 2) mx = fmaxf(fmaxf(mx, sv[q]), sv[q + 1]);
+        mx = fmaxf(mx, sv[15]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        upd = mx > m_run + kRescaleSlack;
+        m_next = upd ? mx : m_run;
+        alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_next) : 1.0f;
+        const float m_use = (m_next == -INFINITY) ? 0.0f : m_next;
 #pragma unroll
-      for (int q = 1; q < 16; ++q) mx = fmaxf(mx, sv[q]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool upd = mx > m_run + kRescaleSlack;
-      const float m_next = upd ? mx : m_run;
-      const float alpha = upd ? exp2f(m_run - m_next) : 1.0f;
-      const float m_use = (m_next == -INFINITY) ? 0.0f : m_next;
-      uint32_t pw[8];
-      float lsum = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        pw[q] = pack2<DT>(exp2f(sv[2 * q] - m_use), exp2f(sv[2 * q + 1] - m_use));
-        lsum += lo16<DT>(pw[q]) + hi16<DT>(pw[q]);
+        for (int q = 0; q < 8; ++q) {
+          pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(sv[2 * q] - m_use), __builtin_amdgcn_exp2f(sv[2 * q + 1] - m_use));
+          lsum += lo16<DT>(pw[q]) + hi16<DT>(pw[q]);
+        }
       }
       l_run = l_run * alpha + lsum;
       m_run = m_next;
@@ -298,19 +356,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
       }
       const u32x4 pb0 = (u32x4){pw[0], pw[1], pw[2], pw[3]};
       const u32x4 pb1 = (u32x4){pw[4], pw[5], pw[6], pw[7]};
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int off = db * 4096 + (2 * st + s) * 1024;
-          const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vcur + v_lane0 + off));
-          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vcur + v_lane1 + off));
-          const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
-          const u32x4 a = (u32x4){w0[0], w0[1], w1[0], w1[1]};
-          oacc[db] = mfma32<DT>(a, s ? pb1 : pb0, oacc[db]);
+      // O^T += V^T P^T over the 8 dim blocks; the V operands of block db + 1 are read while
+      // the two MFMAs of block db run
+      u32x4 va[2][2];
+      auto read_v = [&](auto dbc, u32x4 (&dst)[2]) {
+        constexpr int db = decltype(dbc)::value;
+        // dim block db, key groups 2 st and 2 st + 1 of the tile
+        constexpr int o0 = db * 4096 + (2 * st) * 1024, o1 = o0 + 1024;
+        const u32x2 w00 = ds_read_tr16<o0>(vaddr0), w01 = ds_read_tr16<o0>(vaddr1);
+        const u32x2 w10 = ds_read_tr16<o1>(vaddr0), w11 = ds_read_tr16<o1>(vaddr1);
+        dst[0] = (u32x4){w00[0], w00[1], w01[0], w01[1]};
+        dst[1] = (u32x4){w10[0], w10[1], w11[0], w11[1]};
+      };
+      read_v(std::integral_constant<int, 0>{}, va[0]);
+      static_for<8>([&](auto dbc) {
+        constexpr int db = decltype(dbc)::value;
+        if constexpr (db < 7) {
+          read_v(std::integral_constant<int, db + 1>{}, va[(db + 1) & 1]);
+          lgkm_wait<4>(va[db & 1][0], va[db & 1][1]);
+        } else {
+          lgkm_wait<0>(va[db & 1][0], va[db & 1][1]);
         }
-      }
-    }
+        oacc[db] = mfma32<DT>(va[db & 1][0], pb0, oacc[db]);
+        oacc[db] = mfma32<DT>(va[db & 1][1], pb1, oacc[db]);
+      });
+    });
   };
   for (int t = 0; t < n_kt; t += 2) {
     step(t, kbuf0, vbuf0, kbuf1, vbuf1);
