@@ -141,7 +141,7 @@ def plant_near_ties(q_bits, k_bits, *, n_kv_heads: int, rng: np.random.Generator
                         j1 = int(rng.integers(t1 * tile, t1 * tile + tile))
                         j2 = int(rng.integers(t2 * tile, min(t2 * tile + tile, r + 1)))
                     else:
-                        t = int(rng.integers(0, r // tile + 1))
+                        t = int(rng.integers(0, (r - 1) // tile + 1))  # a tile holding >= 2 keys <= r
                         lo, hi = t * tile, min(t * tile + tile, r + 1)
                         j1, j2 = sorted(int(v) for v in rng.choice(np.arange(lo, hi), size=2, replace=False))
                     k1, k2 = k64[b, g, j1], k64[b, g, j2]

@@ -69,3 +69,14 @@ def test_verify_mask_structure():
     assert 0.05 < frac < 0.15
     add = syn.verify_mask(syn.streams(1004)["mask"], rows=12, kv_offset=100, heads=3, kind="add")
     assert np.array_equal(np.isfinite(syn.bits_to_f32(add)), m.astype(bool))
+
+
+def test_near_ties_every_row_including_tile_boundaries():
+    # frac 1: every row 1..N-1, so rows sitting on a 64-key tile start (64, 128) are planted too
+    N = 140
+    rng = syn.streams(7)
+    q = syn.normal_bits(rng["q"], (1, 2, N, 256))
+    k = syn.normal_bits(rng["k"], (1, 1, N, 256))
+    q2, rec = syn.plant_near_ties(q, k, n_kv_heads=1, rng=rng["plant"], frac=1.0)
+    assert len(rec) == 2 * (N - 1)
+    assert np.all(rec[:, 3] < rec[:, 4]) and np.all(rec[:, 4] <= rec[:, 2])
