@@ -1,21 +1,27 @@
 """Benchmark of the gated causal GQA attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-  1. the 32768-token causal prompt of the 27B shape (batch 1, 24 query heads over 4 KV
-     heads, head_dim 256, bf16, gated) in query blocks of q_block rows: kv_append of the
+  1. prefill: the 32768-token causal prompt of the 27B shape (batch 1, 24 query heads over
+     4 KV heads, head_dim 256, bf16, gated) in query blocks of q_block rows: kv_append of the
      block's K/V, then attn_prefill of the block;
-  2. one head-chunked verify step of the 35B-A3B shape (batch 2, 16 query heads over 2 KV
-     heads, 32 rows appended at KV offset 32768 with a broadcast additive tree mask):
-     kv_append, then attn_decode (split-KV pass + merge).
+  2. decode: one decode row of the 35B-A3B shape (batch 2, 16 query heads over 2 KV heads)
+     appended at KV offset 32768: kv_append, then attn_decode (split-KV pass + merge), on a
+     cache chosen round-robin from enough distinct caches that the 256 MB Infinity Cache
+     cannot hold them (cold KV reads);
+  3. verify: 32 verify rows of the same shape at offset 32768 with a broadcast additive tree
+     mask (the head-chunked verify): kv_append, then attn_decode.
 Inputs are resident in HBM before timing starts.  Events on the stream the kernels run on
-bracket the timed region; the prefill and decode parts of every step are timed separately.
+bracket each part of every step.
 
 value = prefill attention TFLOP/s over the 32k prompt (algorithmic flops: 4 * 256 per
-admissible (head, row, key) triple, i.e. 4*256*24*32768*32769/2 = 1.3195e13 per prompt).
-decode.value = KV GB/s of the verify step (K+V bytes read once per KV group + Q, gate,
-out and mask bytes).  roofline = the attn_prefill pass (split kernel + merge) against the
-dense bf16 MFMA peak.  cpu_baseline = the float64 oracle on a bounded sample of the same
-prompt, on the host cores.
+admissible (head, row, key) triple: 4*256*24*32768*32769/2 = 1.3195e13 per prompt).
+decode.value = KV GB/s of the one-row decode (K and V bytes read once per KV group + Q,
+gate and out).  roofline = the attn_prefill pass (split kernel + merge) against the dense
+bf16 MFMA peak; decode.roofline = the decode call against HBM bandwidth.
+cpu_baseline = the float64 oracle on a bounded sample of the same prompt, on the host cores.
+
+`--copy-calibration BYTES` only copies a BYTES-sized device buffer once (for calibrating the
+FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exits.
 """
 
 import argparse
@@ -32,6 +38,7 @@ import torch  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+MALL_BYTES = 256 << 20      # Infinity Cache
 
 
 def _up(bits, dev):
@@ -40,6 +47,16 @@ def _up(bits, dev):
 
 def prefill_flops(Hq, N):
     return 4.0 * 256 * Hq * N * (N + 1) / 2
+
+
+def copy_calibration(nbytes):
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_calibration_bytes": int(nbytes)}), flush=True)
 
 
 def main():
@@ -51,10 +68,14 @@ def main():
     ap.add_argument("--seq", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=96)
+    ap.add_argument("--copy-calibration", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path has no multi-GPU part"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import gqa_causal_attention_attn_amd as ga
     from synth import inputs as syn
@@ -81,19 +102,28 @@ def main():
     plans = [ga.describe_plan(ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=min(qL, N - s), kv_offset=s, capacity=N), 0)
              for s in range(0, N, qL)]
 
-    # ---- verify inputs (35B-A3B shape, 32 rows at offset 32768, broadcast additive mask)
+    # ---- decode / verify inputs (35B-A3B shape at offset 32768)
     vB, vHq, vHkv, voff, vrows = 2, 16, 2, 32768, 32
     vrng = syn.streams(1004)
     vcap = voff + vrows
-    vk = _up(syn.normal_bits(vrng["k"], (vB, vHkv, vcap, 256)), dev)
-    vv = _up(syn.normal_bits(vrng["v"], (vB, vHkv, vcap, 256)), dev)
+    cache_bytes = 2 * vB * vHkv * vcap * 256 * 2
+    n_rot = max(2, int(np.ceil(4 * MALL_BYTES / cache_bytes)))  # >= 1 GiB of distinct caches
+    kbits = syn.normal_bits(vrng["k"], (vB, vHkv, vcap, 256))
+    vbits = syn.normal_bits(vrng["v"], (vB, vHkv, vcap, 256))
+    caches = [(_up(kbits, dev), _up(vbits, dev)) for _ in range(n_rot)]
+    k_new = caches[0][0][:, :, voff:].clone()
+    v_new = caches[0][1][:, :, voff:].clone()
+    dq = _up(syn.normal_bits(vrng["q"], (vB, vHq, 1, 256)), dev)
+    dg = _up(syn.normal_bits(vrng["gate"], (vB, vHq, 1, 256)), dev)
+    dout = torch.empty_like(dq)
+    da = ga.plan_args(B=vB, Hq=vHq, Hkv=vHkv, rows=1, kv_offset=voff, capacity=vcap)
+    dws = torch.empty(max(ga.workspace_bytes(da, 1), 16), dtype=torch.uint8, device=dev)
+    dplan = ga.describe_plan(da, 1)
     vq = _up(syn.normal_bits(vrng["q"], (vB, vHq, vrows, 256)), dev)
     vg = _up(syn.normal_bits(vrng["gate"], (vB, vHq, vrows, 256)), dev)
     vmask = _up(syn.verify_mask(vrng["mask"], rows=vrows, kv_offset=voff, heads=1, kind="add"), dev)
-    vk_new = vk[:, :, voff:].clone()
-    vv_new = vv[:, :, voff:].clone()
     vout = torch.empty_like(vq)
-    va = ga.plan_args(B=vB, Hq=vHq, Hkv=vHkv, rows=vrows, kv_offset=voff, mask_kind=2)
+    va = ga.plan_args(B=vB, Hq=vHq, Hkv=vHkv, rows=vrows, kv_offset=voff, capacity=vcap, mask_kind=2)
     vws = torch.empty(max(ga.workspace_bytes(va, 1), 16), dtype=torch.uint8, device=dev)
     vplan = ga.describe_plan(va, 1)
     torch.cuda.synchronize(dev)
@@ -111,48 +141,77 @@ def main():
             if per_call is not None:
                 per_call[i][1].record(stream)
 
-    def verify_pass():
-        ga.kv_append(vk_new, vv_new, vk, vv, kv_offset=voff)
-        ga.decode(vq, vk, vv, vg, kv_offset=voff, mask=vmask, out=vout, workspace=vws)
+    def decode_pass(it, evs=None):
+        kk_, vv_ = caches[it % n_rot]
+        ga.kv_append(k_new[:, :, :1], v_new[:, :, :1], kk_, vv_, kv_offset=voff)
+        if evs is not None:
+            evs[0].record(stream)
+        ga.decode(dq, kk_, vv_, dg, kv_offset=voff, out=dout, workspace=dws)
+        if evs is not None:
+            evs[1].record(stream)
 
-    for _ in range(args.warmup):
+    def verify_pass(it, evs=None):
+        kk_, vv_ = caches[(it + n_rot // 2) % n_rot]
+        ga.kv_append(k_new, v_new, kk_, vv_, kv_offset=voff)
+        if evs is not None:
+            evs[0].record(stream)
+        ga.decode(vq, kk_, vv_, vg, kv_offset=voff, mask=vmask, out=vout, workspace=vws)
+        if evs is not None:
+            evs[1].record(stream)
+
+    for w in range(args.warmup):
         prefill_pass()
-        verify_pass()
+        decode_pass(w)
+        verify_pass(w)
     torch.cuda.synchronize(dev)
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    E = torch.cuda.Event
+    ev = [[E(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    dec_ev = [[E(enable_timing=True), E(enable_timing=True)] for _ in range(K)]
+    ver_ev = [[E(enable_timing=True), E(enable_timing=True)] for _ in range(K)]
     n_calls = len(plans)
-    per_call = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(n_calls)]
-                for _ in range(K)]
+    per_call = [[[E(enable_timing=True), E(enable_timing=True)] for _ in range(n_calls)] for _ in range(K)]
     torch.cuda.synchronize(dev)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    start = E(enable_timing=True)
+    end = E(enable_timing=True)
     start.record(stream)
     for it in range(K):
         ev[it][0].record(stream)
         prefill_pass(per_call[it])
         ev[it][1].record(stream)
-        verify_pass()
+        decode_pass(it, dec_ev[it])
         ev[it][2].record(stream)
+        verify_pass(it, ver_ev[it])
+        ev[it][3].record(stream)
     end.record(stream)
     torch.cuda.synchronize(dev)
+
+    # MALL-warm decode beside it: the same cache over and over
+    warm = [[E(enable_timing=True), E(enable_timing=True)] for _ in range(K)]
+    for it in range(K):
+        decode_pass(0, warm[it])
+    torch.cuda.synchronize(dev)
+
     total_ms = start.elapsed_time(end)
     pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    ver_ms = [e[1].elapsed_time(e[2]) for e in ev]
     call_ms = np.array([[pc[0].elapsed_time(pc[1]) for pc in step] for step in per_call])
+    dec_us = np.array([e[0].elapsed_time(e[1]) for e in dec_ev]) * 1e3
+    ver_us = np.array([e[0].elapsed_time(e[1]) for e in ver_ev]) * 1e3
+    warm_us = np.array([e[0].elapsed_time(e[1]) for e in warm]) * 1e3
 
     flops = prefill_flops(Hq, N)
     pre_tflops = flops / (np.mean(pre_ms) * 1e-3) / 1e12
-    # per call: algorithmic flops of block i = 4*256*Hq*sum over its rows of (position + 1)
     call_flops = np.array([4.0 * 256 * Hq * sum(range(s + 1, min(s + qL, N) + 1)) for s in range(0, N, qL)])
     call_mean_ms = call_ms.mean(axis=0)
     achieved_tflops = float(call_flops.sum() / (call_mean_ms.sum() * 1e-3) / 1e12)
 
-    kv_bytes = 2.0 * vB * vHkv * (voff + vrows) * 256 * 2
-    io_bytes = 3.0 * vB * vHq * vrows * 256 * 2 + vrows * (voff + vrows) * 2
-    ver_gbs = (kv_bytes + io_bytes) / (np.mean(ver_ms) * 1e-3) / 1e9
-
+    kv_len = voff + vrows  # the verify rows see the whole cache; the decode row reads voff + 1 keys
+    dec_bytes = 2.0 * vB * vHkv * (voff + 1) * 256 * 2 + 3.0 * vB * vHq * 1 * 256 * 2
+    dec_gbs = dec_bytes / (np.median(dec_us) * 1e-6) / 1e9
+    warm_gbs = dec_bytes / (np.median(warm_us) * 1e-6) / 1e9
+    ver_bytes = 2.0 * vB * vHkv * kv_len * 256 * 2 + 3.0 * vB * vHq * vrows * 256 * 2 + vrows * kv_len * 2
+    ver_flops = 4.0 * 256 * vB * vHq * vrows * kv_len  # upper bound: every key admissible
     result = {
         "metric": "prefill attention TFLOP/s @32k (D256 GQA 24/4, bf16, gated); decode KV GB/s in 'decode'",
         "value": round(float(pre_tflops), 2),
@@ -167,17 +226,26 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 at the 27B and 35B-A3B attention shapes)",
         "config": {"workload": f"27B-shape causal prefill, batch 1, 24/4 heads, head_dim 256, {N} tokens in "
-                               f"query blocks of {qL}; plus 35B-A3B-shape verify, batch 2, 16/2 heads, 32 rows at "
-                               f"offset 32768, broadcast additive mask",
+                               f"query blocks of {qL}; 35B-A3B-shape decode (1 row) and head-chunked verify "
+                               f"(32 rows, broadcast additive mask), batch 2, 16/2 heads, at KV offset 32768",
                    "seq_len": N, "q_block": qL, "global_batch": B},
         "prefill": {"ms": round(float(np.mean(pre_ms)), 4), "tflops": round(float(pre_tflops), 2),
                     "frac_of_peak": round(float(pre_tflops) / PEAK_BF16_TFLOPS, 4), "calls": n_calls,
                     "workspace_bytes": int(ws_need),
                     "plan_last_block": {kk: plans[-1][kk] for kk in ("variant_name", "n_splits", "keys_per_split",
                                                                      "n_row_tiles", "grid_blocks")}},
-        "decode": {"metric": "verify KV GB/s (35B-A3B shape, 32 rows at offset 32768, MALL-warm)",
-                   "value": round(float(ver_gbs), 1), "unit": "GB/s", "us": round(float(np.mean(ver_ms)) * 1e3, 2),
-                   "frac_of_peak": round(float(ver_gbs) / PEAK_HBM_GBS, 4), "bytes": int(kv_bytes + io_bytes),
+        "decode": {"metric": "decode KV GB/s (35B-A3B shape, batch 2, 1 row at offset 32768, cold KV)",
+                   "value": round(float(dec_gbs), 1), "unit": "GB/s", "us": round(float(np.median(dec_us)), 2),
+                   "bytes": int(dec_bytes), "distinct_caches": n_rot,
+                   "mall_warm_gbs": round(float(warm_gbs), 1), "mall_warm_us": round(float(np.median(warm_us)), 2),
+                   "roofline": {"bound": "hbm", "achieved": round(float(dec_gbs), 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(float(dec_gbs) / PEAK_HBM_GBS, 4)},
+                   "plan": {kk: dplan[kk] for kk in ("variant_name", "n_splits", "keys_per_split", "n_head_chunks",
+                                                     "grid_blocks")}},
+        "verify": {"metric": "head-chunked verify, 32 rows at offset 32768, additive mask (cold KV)",
+                   "us": round(float(np.median(ver_us)), 2),
+                   "gbs": round(float(ver_bytes / (np.median(ver_us) * 1e-6) / 1e9), 1),
+                   "tflops_upper": round(float(ver_flops / (np.median(ver_us) * 1e-6) / 1e12), 1),
                    "plan": {kk: vplan[kk] for kk in ("variant_name", "n_splits", "keys_per_split", "n_head_chunks",
                                                      "grid_blocks")}},
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": PEAK_BF16_TFLOPS,

@@ -3,8 +3,9 @@
 // Merge (TensorFold PR #1009, attention kernel-contract commit: decode rows over key chunks
 // and a merge of the chunks): per (b, h, r), lse = log sum_c exp(lse_c),
 // out = sum_c exp(lse_c - lse) o_c * sigmoid(gate), an empty chunk (lse_c = -Inf) adds
-// nothing and is not read, and a row with every chunk empty gives 0.  One wavefront per
-// row, four dims per lane; HBM-bound (it reads n_chunks x 1 KiB per row).
+// nothing (its slot is selected out, never multiplied in) and a row with every chunk empty
+// gives 0.  One workgroup per row, four dims per lane, the chunk partials fetched in batches
+// of independent loads spread over four wavefronts; HBM-bound (n_chunks x 1 KiB per row).
 //
 // Append (same commit, "pack, append and keep ... bit-exact"): a 16-byte copy of each new
 // K/V row into the cache; no arithmetic touches the bits.
@@ -37,16 +38,22 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   else return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
 }
 
+// One workgroup of four wavefronts per row: wavefront w takes the chunks w, w + 4, ...; its
+// weights come from one load of the row's lse values per lane, its partials from batches of
+// eight independent loads; the four partial sums meet in LDS.
 template <int DT>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
+  __shared__ f32x4 part_acc[4][64];
+  __shared__ float part_w[4];
   const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
-  const int64_t row_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row_id >= n_rows) return;
+  const int64_t row_id = blockIdx.x;
   const int r = (int)(row_id % p.rows);
   const int h = (int)((row_id / p.rows) % p.Hq);
   const int b = (int)(row_id / ((int64_t)p.rows * p.Hq));
 
+  // largest lse of the row: lane i of every wavefront reads chunks i, i + 64, ...
   float top = -INFINITY;
   for (int c = lane; c < p.n_chunks; c += 64) top = fmaxf(top, p.part_lse[(int64_t)c * n_rows + row_id]);
 #pragma unroll
@@ -56,15 +63,38 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
   if (top > -INFINITY) {
-    for (int c = 0; c < p.n_chunks; ++c) {
-      const float lc = p.part_lse[(int64_t)c * n_rows + row_id];
-      if (lc == -INFINITY) continue;
-      const float w = exp2f((lc - top) * kLog2e);
-      wsum += w;
-      const f32x4 oc = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)c * n_rows + row_id) * kHeadDim + d0);
-      acc += w * oc;
+    for (int base = 0; base < p.n_chunks; base += 64) {
+      // lane i holds the weight of chunk base + i (0 for an empty chunk or past the end)
+      const int c = base + lane;
+      const float lc = c < p.n_chunks ? p.part_lse[(int64_t)c * n_rows + row_id] : -INFINITY;
+      const float w = lc == -INFINITY ? 0.0f : exp2f((lc - top) * kLog2e);
+      const int m = min(64, p.n_chunks - base);
+      // this wavefront's chunks of the window: base + wave + 4 i
+      for (int i0 = wave; i0 < m; i0 += 32) {
+        f32x4 oc[8];
+        float wj[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = i0 + 4 * j;
+          const int cc = min(base + i, p.n_chunks - 1);
+          oc[j] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * kHeadDim + d0);
+          wj[j] = i < m ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), i)) : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // an empty chunk is selected out, never multiplied in, so its slot cannot reach the sum
+          if (wj[j] != 0.0f) acc += wj[j] * oc[j];
+          wsum += wj[j];
+        }
+      }
     }
   }
+  part_acc[wave][lane] = acc;
+  if (lane == 0) part_w[wave] = wsum;
+  __syncthreads();
+  if (wave != 0) return;
+  acc = part_acc[0][lane] + part_acc[1][lane] + part_acc[2][lane] + part_acc[3][lane];
+  wsum = part_w[0] + part_w[1] + part_w[2] + part_w[3];
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
   const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
@@ -104,7 +134,7 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
 
 hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
-  const dim3 grid((unsigned)((n_rows + 3) / 4));
+  const dim3 grid((unsigned)n_rows);
   if (dtype == 0) hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();

@@ -154,34 +154,64 @@ __device__ __forceinline__ float mask_term(const void* base, int64_t row_off, in
   }
 }
 
-// Issue the direct loads of one K tile and one V tile (keys j0 .. j0 + 63, clamped to jmax,
-// which only feeds keys that every pair masks) into kbuf / vbuf.  Wavefront w loads the
-// 1 KiB groups 4w .. 4w + 3 of each tile.
+// Issue the direct loads of tile j0 .. j0 + 31 (keys clamped to jmax, which only feeds keys
+// that every pair masks) into the K and V halves of one LDS stage.  Wavefront w loads the
+// 1 KiB groups 2w and 2w + 1 of each tile.
 __device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t* vbase, int64_t k_st, int64_t v_st,
-                                           int j0, int jmax, uint8_t* kbuf, uint8_t* vbuf, int wave, int lane) {
+                                           int j0, int jmax, uint8_t* stage, int wave, int lane) {
   const int c_lo = lane >> 4;
   const int key_lo_k = lane & 15;
   const int key_lo_v = ((lane & 15) - 4 * c_lo) & 15;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int grp = wave * 4 + e;  // 0..31
-    const int c = (grp >> 2) * 4 + c_lo;
-    const int key_hi = grp & 3;
+  for (int e = 0; e < 2; ++e) {
+    const int grp = wave * 2 + e;  // 0..15
+    const int c = (grp >> 1) * 4 + c_lo;
+    const int key_hi = grp & 1;
     const int jk = min(j0 + key_hi * 16 + key_lo_k, jmax);
     const int jv = min(j0 + key_hi * 16 + key_lo_v, jmax);
-    __builtin_amdgcn_global_load_lds(kbase + (int64_t)jk * k_st + 8 * c, (lds_void*)(kbuf + grp * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + (int64_t)jv * v_st + 8 * c, (lds_void*)(vbuf + grp * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(kbase + (int64_t)jk * k_st + 8 * c, (lds_void*)(stage + grp * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + (int64_t)jv * v_st + 8 * c,
+                                     (lds_void*)(stage + kTileBytes + grp * 1024), 16, 0, 0);
+  }
+}
+constexpr int kLoadsPerTile = 4;  // direct-load instructions per wavefront per tile
+
+// One ds_read_b128 at a per-lane LDS byte address plus an immediate offset (inline assembly:
+// the compiler neither tracks it nor waits for it; see lgkm_wait1).
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+template <int N>
+__device__ __forceinline__ void lgkm_wait1(u32x4& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
+}
+
+// Wait until at most N direct loads of this wavefront are in flight (N a multiple of the
+// loads per tile, at most kPrefetch - 1 tiles' worth).
+__device__ __forceinline__ void wait_tiles_in_flight(int n_tiles) {
+  switch (n_tiles) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
   }
 }
 
+// max(x, x of the lane 32 away), the same value on both lanes
+__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+
+// x + (x of the lane 32 away), the same sum on both lanes
+__device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
+
 template <int DT, int MK>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[kTileBytes];
-  __shared__ int red_max[kWavesPerBlock];
-  __shared__ int red_min[kWavesPerBlock];
+  // kStages stages of (K tile, V tile), 32 KiB each: up to kPrefetch tiles in flight while one
+  // is consumed.  Stage of tile t: t % kStages.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * 2 * kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -199,6 +229,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
   const int b = bid / p.Hkv;
   const int tile = p.n_tiles - 1 - tile_rev;  // later rows (more keys) first
 
+  auto lim_of = [&](int row) { return p.causal ? min(p.kv_len, p.kv_offset + row + 1) : p.kv_len; };
+
   // ---- the (head, row) pair of this lane
   const int wi = tile * kWavesPerBlock + wave;
   const int chunk_idx = wi / p.waves_per_chunk;
@@ -208,26 +240,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
   const bool valid = hstart < p.G && f < cs * p.rows;
   const int r = valid ? f / cs : 0;
   const int h = g * p.G + hstart + (valid ? f - (f / cs) * cs : 0);
-  const int lim = valid ? (p.causal ? min(p.kv_len, p.kv_offset + r + 1) : p.kv_len) : 0;
+  const int lim = valid ? lim_of(r) : 0;
   const bool wave_active = __builtin_amdgcn_ballot_w64(valid) != 0;
 
-  // ---- key range of the workgroup: [kv_lo, kv_end)
-  int wmax = lim, wmin = valid ? lim : 0x7fffffff;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    wmax = max(wmax, __shfl_xor(wmax, o));
-    wmin = min(wmin, __shfl_xor(wmin, o));
-  }
-  if (lane == 0) {
-    red_max[wave] = wmax;
-    red_min[wave] = wmin;
-  }
-  __syncthreads();
-  int kv_hi = red_max[0], lim_min = red_min[0];
-#pragma unroll
-  for (int w = 1; w < kWavesPerBlock; ++w) {
-    kv_hi = max(kv_hi, red_max[w]);
-    lim_min = min(lim_min, red_min[w]);
+  // ---- key range of the workgroup [kv_lo, kv_end) and the smallest bound of its pairs, from
+  // the pair layout of its wavefronts (uniform arithmetic)
+  int kv_hi = 0, lim_min = 0x7fffffff;
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    const int wj = tile * kWavesPerBlock + w;
+    const int cj = wj / p.waves_per_chunk;
+    const int f0 = (wj - cj * p.waves_per_chunk) * kPairsPerWave;
+    const int hs = cj * p.chunk;
+    if (hs >= p.G) continue;
+    const int csj = min(p.chunk, p.G - hs);
+    const int npairs = csj * p.rows;
+    if (f0 >= npairs) continue;
+    kv_hi = max(kv_hi, lim_of((min(f0 + kPairsPerWave, npairs) - 1) / csj));
+    lim_min = min(lim_min, lim_of(f0 / csj));
   }
   const int kv_lo = split * p.keys_per_split;
   const int kv_end = min(kv_lo + p.keys_per_split, kv_hi);
@@ -247,16 +276,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
   }
   const int64_t mrow = MK ? (int64_t)b * p.m_sb + (int64_t)h * p.m_sh + (int64_t)r * p.m_sr : 0;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q is in registers before the tile stream starts
-  if (n_kt > 0) issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo, kv_end - 1, kbuf0, vbuf0, wave, lane);
+  for (int t = 0; t < kPrefetch && t < n_kt; ++t) {
+    issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kKeysPerTile, kv_end - 1, lds + t * 2 * kTileBytes, wave,
+               lane);
+  }
 
-  // per-lane LDS bases (see the layout above); everything else is a compile-time offset
-  const int k_lane = (li >> 4) * 1024 + hf * 256 + (li & 15) * 16;
+  // per-lane LDS byte addresses (see the layout above); every read adds a compile-time offset
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)lds;
+  const uint32_t k_lane = (li >> 4) * 1024 + hf * 256 + (li & 15) * 16;
   const int grp16 = lane >> 4, i16 = lane & 15;
   const int tq = i16 >> 2, uq = i16 & 3;
   const int c_lo_v = 2 * (grp16 & 1) + (uq >> 1);
   const int xv = 4 * (grp16 >> 1) + tq + 4 * c_lo_v;
-  const int v_lane0 = c_lo_v * 256 + (xv & 15) * 16 + (uq & 1) * 8;
-  const int v_lane1 = c_lo_v * 256 + ((xv + 8) & 15) * 16 + (uq & 1) * 8;
+  const uint32_t v_lane0 = kTileBytes + c_lo_v * 256 + (xv & 15) * 16 + (uq & 1) * 8;
+  const uint32_t v_lane1 = kTileBytes + c_lo_v * 256 + ((xv + 8) & 15) * 16 + (uq & 1) * 8;
 
   f32x16 oacc[8];
 #pragma unroll
@@ -264,131 +297,149 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
   float m_run = -INFINITY;
   float l_run = 0.0f;
 
-  // One step: wait for tile t (in cur), start tile t + 1 into nxt, consume cur.  The two
-  // buffers are distinct objects, so the compiler can tell the direct loads into nxt from
-  // the reads of cur and does not wait for the former before the latter.
-  auto step = [&](int t, uint8_t* kcur, uint8_t* vcur, uint8_t* knxt, uint8_t* vnxt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t is in LDS for everyone; everyone is done with tile t - 1
-    if (t + 1 < n_kt) {
-      issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + 1) * kKeysPerTile, kv_end - 1, knxt, vnxt, wave, lane);
+  // One step of the tile stream: wait for tile t (issued kPrefetch steps ago), sync, and
+  // start tile t + kPrefetch.  Returns the LDS address of tile t's stage.
+  int stage = 0;
+  auto stream_step = [&](int t) {
+    // tile t landed for this wavefront once only the tiles issued after it remain in flight
+    wait_tiles_in_flight(min(kPrefetch - 1, n_kt - 1 - t));
+    __builtin_amdgcn_s_barrier();  // ... and for everyone; everyone is done with tile t - 1
+    if (t + kPrefetch < n_kt) {
+      int st2 = stage + kPrefetch;
+      if (st2 >= kStages) st2 -= kStages;
+      issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + kPrefetch) * kKeysPerTile, kv_end - 1,
+                 lds + st2 * 2 * kTileBytes, wave, lane);
     }
-    if (!wave_active) return;
-    const int j0 = kv_lo + t * kKeysPerTile;
-    // address-space-3 views, so every read folds its compile-time offset into the instruction
-    const lds_u8* const kl = (const lds_u8*)kcur + k_lane;
-    const uint32_t vaddr0 = (uint32_t)(uintptr_t)((const lds_u8*)vcur + v_lane0);
-    const uint32_t vaddr1 = (uint32_t)(uintptr_t)((const lds_u8*)vcur + v_lane1);
-    static_for<2>([&](auto stc) {
-      constexpr int st = decltype(stc)::value;
-      // S^T block: rows = 32 keys of this sub-tile, columns = the wave's 32 pairs
-      f32x16 sacc = (f32x16){};
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const u32x4 a = *(const lds_u32x4*)(kl + (kk >> 1) * 4096 + st * 2048 + (kk & 1) * 512);
-        sacc = mfma32<DT>(a, qreg[kk], sacc);
-      }
-      // element q of sacc holds key jb + 8 (q / 4) + 4 hf + (q % 4) of this lane's pair
-      const int jb = j0 + 32 * st;
-      uint32_t pw[8];
-      float lsum = 0.0f;
-      float alpha, m_next;
-      bool upd;
-      if constexpr (MK == 0) {
-        // Raw scores; keys past the pair's causal / cache bound get -inf (only on sub-tiles that
-        // reach some pair's bound).  The scale folds into the exponent, and the max commutes
-        // with it (scale > 0), so every pair computes the same bits on either path.
-        float sm[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) sm[q] = sacc[q];
-        if (jb + 32 > lim_min) {  // wave-uniform: the sub-tile reaches some pair's bound
-          const int jl = jb + 4 * hf;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            if (jl + 8 * (q >> 2) + (q & 3) >= lim) sm[q] = -INFINITY;
-          }
+    const uint32_t sb = lds0 + stage * 2 * kTileBytes;
+    stage = stage + 1 == kStages ? 0 : stage + 1;
+    return sb;
+  };
+
+  if (!wave_active) {
+    // a wavefront without pairs only helps stream the tiles
+    for (int t = 0; t < n_kt; ++t) stream_step(t);
+    return;
+  }
+  for (int t = 0; t < n_kt; ++t) {
+    const uint32_t sbase = stream_step(t);
+    const int jb = kv_lo + t * kKeysPerTile;
+
+    // S^T block: rows = the 32 keys of the tile, columns = the wave's 32 pairs; K operands
+    // read two steps ahead
+    f32x16 sacc = (f32x16){};
+    {
+      const uint32_t kaddr = sbase + k_lane;
+      constexpr int kAhead = 2;  // K operands in flight beyond the one consumed
+      u32x4 kop[kAhead + 1];
+      static_for<kAhead>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        kop[i] = ds_read_b128<(i >> 1) * 2048 + (i & 1) * 512>(kaddr);
+      });
+      static_for<16>([&](auto kkc) {
+        constexpr int kk = decltype(kkc)::value;
+        if constexpr (kk + kAhead < 16) {
+          kop[(kk + kAhead) % (kAhead + 1)] =
+              ds_read_b128<((kk + kAhead) >> 1) * 2048 + ((kk + kAhead) & 1) * 512>(kaddr);
         }
-        float mr = fmaxf(fmaxf(sm[0], sm[1]), sm[2]);
+        constexpr int issued = kk + kAhead + 1 < 16 ? kk + kAhead + 1 : 16;
+        lgkm_wait1<issued - kk - 1>(kop[kk % (kAhead + 1)]);
+        sacc = mfma32<DT>(kop[kk % (kAhead + 1)], qreg[kk], sacc);
+      });
+    }
+
+    __builtin_amdgcn_sched_barrier(0);
+    // element q of sacc holds key jb + 8 (q / 4) + 4 hf + (q % 4) of this lane's pair
+    uint32_t pw[8];
+    float lsum = 0.0f;
+    float alpha, m_next;
+    bool upd;
+    if constexpr (MK == 0) {
+      // Raw scores; keys past the pair's causal / cache bound get -inf (only on tiles that
+      // reach some pair's bound).  The scale folds into the exponent, and the max commutes
+      // with it (scale > 0), so every pair computes the same bits on either path.
+      float sm[16];
 #pragma unroll
-        for (int q = 3; q < 15; q += 2) mr = fmaxf(fmaxf(mr, sm[q]), sm[q + 1]);
-        mr = fmaxf(mr, sm[15]);
-        mr = fmaxf(mr, __shfl_xor(mr, 32));
-        const float mx = mr * p.scale_log2;
-        upd = mx > m_run + kRescaleSlack;
-        m_next = upd ? mx : m_run;
-        alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_next) : 1.0f;
-        const float neg_m = (m_next == -INFINITY) ? 0.0f : -m_next;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sm[2 * q], p.scale_log2, neg_m)),
-                            __builtin_amdgcn_exp2f(__builtin_fmaf(sm[2 * q + 1], p.scale_log2, neg_m)));
-          lsum += lo16<DT>(pw[q]) + hi16<DT>(pw[q]);
-        }
-      } else {
-        // scaled scores plus the mask term (log2 units); hidden and out-of-bound keys get -inf
-        float sv[16];
+      for (int q = 0; q < 16; ++q) sm[q] = sacc[q];
+      if (jb + kKeysPerTile > lim_min) {  // wave-uniform
+        const int jl = jb + 4 * hf;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const int j = jb + 8 * (q >> 2) + 4 * hf + (q & 3);
-          const float tv = sacc[q] * p.scale_log2;
-          sv[q] = j < lim ? tv + mask_term<DT, MK>(p.mask, mrow, j) : -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-#pragma unroll
-        for (int q = 3; q < 15; q += 2) mx = fmaxf(fmaxf(mx, sv[q]), sv[q + 1]);
-        mx = fmaxf(mx, sv[15]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        upd = mx > m_run + kRescaleSlack;
-        m_next = upd ? mx : m_run;
-        alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_next) : 1.0f;
-        const float m_use = (m_next == -INFINITY) ? 0.0f : m_next;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(sv[2 * q] - m_use), __builtin_amdgcn_exp2f(sv[2 * q + 1] - m_use));
-          lsum += lo16<DT>(pw[q]) + hi16<DT>(pw[q]);
+          if (jl + 8 * (q >> 2) + (q & 3) >= lim) sm[q] = -INFINITY;
         }
       }
-      l_run = l_run * alpha + lsum;
-      m_run = m_next;
-      if (__builtin_amdgcn_ballot_w64(upd)) {
+      float mr = fmaxf(fmaxf(sm[0], sm[1]), sm[2]);
 #pragma unroll
-        for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+      for (int q = 3; q < 15; q += 2) mr = fmaxf(fmaxf(mr, sm[q]), sm[q + 1]);
+      mr = max_halves(fmaxf(mr, sm[15]));
+      const float mx = mr * p.scale_log2;
+      upd = mx > m_run + kRescaleSlack;
+      m_next = upd ? mx : m_run;
+      alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_next) : 1.0f;
+      const float neg_m = (m_next == -INFINITY) ? 0.0f : -m_next;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sm[2 * q], p.scale_log2, neg_m)),
+                          __builtin_amdgcn_exp2f(__builtin_fmaf(sm[2 * q + 1], p.scale_log2, neg_m)));
+        lsum += lo16<DT>(pw[q]) + hi16<DT>(pw[q]);
       }
-      const u32x4 pb0 = (u32x4){pw[0], pw[1], pw[2], pw[3]};
-      const u32x4 pb1 = (u32x4){pw[4], pw[5], pw[6], pw[7]};
-      // O^T += V^T P^T over the 8 dim blocks; the V operands of block db + 1 are read while
-      // the two MFMAs of block db run
-      u32x4 va[2][2];
-      auto read_v = [&](auto dbc, u32x4 (&dst)[2]) {
-        constexpr int db = decltype(dbc)::value;
-        // dim block db, key groups 2 st and 2 st + 1 of the tile
-        constexpr int o0 = db * 4096 + (2 * st) * 1024, o1 = o0 + 1024;
-        const u32x2 w00 = ds_read_tr16<o0>(vaddr0), w01 = ds_read_tr16<o0>(vaddr1);
-        const u32x2 w10 = ds_read_tr16<o1>(vaddr0), w11 = ds_read_tr16<o1>(vaddr1);
-        dst[0] = (u32x4){w00[0], w00[1], w01[0], w01[1]};
-        dst[1] = (u32x4){w10[0], w10[1], w11[0], w11[1]};
-      };
-      read_v(std::integral_constant<int, 0>{}, va[0]);
-      static_for<8>([&](auto dbc) {
-        constexpr int db = decltype(dbc)::value;
-        if constexpr (db < 7) {
-          read_v(std::integral_constant<int, db + 1>{}, va[(db + 1) & 1]);
-          lgkm_wait<4>(va[db & 1][0], va[db & 1][1]);
-        } else {
-          lgkm_wait<0>(va[db & 1][0], va[db & 1][1]);
-        }
-        oacc[db] = mfma32<DT>(va[db & 1][0], pb0, oacc[db]);
-        oacc[db] = mfma32<DT>(va[db & 1][1], pb1, oacc[db]);
-      });
+    } else {
+      // scaled scores plus the mask term (log2 units); hidden and out-of-bound keys get -inf
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int j = jb + 8 * (q >> 2) + 4 * hf + (q & 3);
+        sacc[q] = j < lim ? sacc[q] * p.scale_log2 + mask_term<DT, MK>(p.mask, mrow, j) : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
+#pragma unroll
+      for (int q = 3; q < 15; q += 2) mx = fmaxf(fmaxf(mx, sacc[q]), sacc[q + 1]);
+      mx = max_halves(fmaxf(mx, sacc[15]));
+      upd = mx > m_run + kRescaleSlack;
+      m_next = upd ? mx : m_run;
+      alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_next) : 1.0f;
+      const float m_use = (m_next == -INFINITY) ? 0.0f : m_next;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(sacc[2 * q] - m_use), __builtin_amdgcn_exp2f(sacc[2 * q + 1] - m_use));
+        lsum += lo16<DT>(pw[q]) + hi16<DT>(pw[q]);
+      }
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_next;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+    }
+    const u32x4 pb0 = (u32x4){pw[0], pw[1], pw[2], pw[3]};
+    const u32x4 pb1 = (u32x4){pw[4], pw[5], pw[6], pw[7]};
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T += V^T P^T over the 8 dim blocks; the V operands of block db + 1 are read while the
+    // two MFMAs of block db run
+    const uint32_t va0 = sbase + v_lane0, va1 = sbase + v_lane1;
+    u32x4 va[2][2];
+    auto read_v = [&](auto dbc, u32x4(&dst)[2]) {
+      constexpr int db = decltype(dbc)::value;
+      constexpr int o0 = db * 2048, o1 = o0 + 1024;  // key groups 0 and 1 of the tile
+      const u32x2 w00 = ds_read_tr16<o0>(va0), w01 = ds_read_tr16<o0>(va1);
+      const u32x2 w10 = ds_read_tr16<o1>(va0), w11 = ds_read_tr16<o1>(va1);
+      dst[0] = (u32x4){w00[0], w00[1], w01[0], w01[1]};
+      dst[1] = (u32x4){w10[0], w10[1], w11[0], w11[1]};
+    };
+    read_v(std::integral_constant<int, 0>{}, va[0]);
+    static_for<8>([&](auto dbc) {
+      constexpr int db = decltype(dbc)::value;
+      if constexpr (db < 7) {
+        read_v(std::integral_constant<int, db + 1>{}, va[(db + 1) & 1]);
+        lgkm_wait<4>(va[db & 1][0], va[db & 1][1]);
+      } else {
+        lgkm_wait<0>(va[db & 1][0], va[db & 1][1]);
+      }
+      oacc[db] = mfma32<DT>(va[db & 1][0], pb0, oacc[db]);
+      oacc[db] = mfma32<DT>(va[db & 1][1], pb1, oacc[db]);
     });
-  };
-  for (int t = 0; t < n_kt; t += 2) {
-    step(t, kbuf0, vbuf0, kbuf1, vbuf1);
-    if (t + 1 < n_kt) step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
   }
 
   // ---- epilogue: element q of oacc[db] is dim 32 db + 8 (q / 4) + 4 hf + (q % 4)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (!valid) return;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (p.n_splits == 1) {

@@ -8,11 +8,13 @@
 namespace gqa {
 
 constexpr int kHeadDim = 256;
-constexpr int kKeysPerTile = 64;     // keys staged in LDS per step
+constexpr int kKeysPerTile = 32;     // keys staged in LDS per step
 constexpr int kWavesPerBlock = 8;    // wavefronts per workgroup of the main pass
 constexpr int kPairsPerWave = 32;    // (head, row) pairs per wavefront (one 32-wide MFMA column block)
-constexpr int kTileBytes = kKeysPerTile * kHeadDim * 2;      // one K (or V) tile: 32 KiB
-constexpr int kFwdLdsBytes = 2 * 2 * kTileBytes;             // K and V tiles, double-buffered
+constexpr int kTileBytes = kKeysPerTile * kHeadDim * 2;      // one K (or V) tile: 16 KiB
+constexpr int kStages = 5;                                   // LDS stages of (K tile, V tile)
+constexpr int kPrefetch = 4;                                 // tiles in flight ahead of the one consumed
+constexpr int kFwdLdsBytes = kStages * 2 * kTileBytes;       // 160 KiB
 constexpr int kTargetBlocks = 256;   // main-pass workgroups aimed for (one per CU)
 
 // Parameters of the main (flash / split-KV) pass.  Strides are in elements.
