@@ -25,6 +25,7 @@ FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exits.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -49,6 +50,20 @@ def prefill_flops(Hq, N):
     return 4.0 * 256 * Hq * N * (N + 1) / 2
 
 
+def measured_traffic():
+    """Calibrated FETCH_SIZE + WRITE_SIZE bytes per prefill call and per decode call, from the
+    counter record under profiles/, or None when the kernel sources have changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec if h.hexdigest() == rec["sha256"] else None
+
+
 def copy_calibration(nbytes):
     dev = torch.device("cuda:0")
     src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
@@ -67,7 +82,7 @@ def main():
     ap.add_argument("--q-block", type=int, default=512)
     ap.add_argument("--seq", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=96)
+    ap.add_argument("--cpu-sample-rows", type=int, default=480)
     ap.add_argument("--copy-calibration", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -212,6 +227,7 @@ def main():
     warm_gbs = dec_bytes / (np.median(warm_us) * 1e-6) / 1e9
     ver_bytes = 2.0 * vB * vHkv * kv_len * 256 * 2 + 3.0 * vB * vHq * vrows * 256 * 2 + vrows * kv_len * 2
     ver_flops = 4.0 * 256 * vB * vHq * vrows * kv_len  # upper bound: every key admissible
+    traffic = measured_traffic() if (N, qL) == (32768, 512) else None
     result = {
         "metric": "prefill attention TFLOP/s @32k (D256 GQA 24/4, bf16, gated); decode KV GB/s in 'decode'",
         "value": round(float(pre_tflops), 2),
@@ -239,7 +255,8 @@ def main():
                    "bytes": int(dec_bytes), "distinct_caches": n_rot,
                    "mall_warm_gbs": round(float(warm_gbs), 1), "mall_warm_us": round(float(np.median(warm_us)), 2),
                    "roofline": {"bound": "hbm", "achieved": round(float(dec_gbs), 1), "peak": PEAK_HBM_GBS,
-                                "unit": "GB/s", "frac": round(float(dec_gbs) / PEAK_HBM_GBS, 4)},
+                                "unit": "GB/s", "frac": round(float(dec_gbs) / PEAK_HBM_GBS, 4),
+                                "traffic": traffic and traffic["decode_call_bytes"]},
                    "plan": {kk: dplan[kk] for kk in ("variant_name", "n_splits", "keys_per_split", "n_head_chunks",
                                                      "grid_blocks")}},
         "verify": {"metric": "head-chunked verify, 32 rows at offset 32768, additive mask (cold KV)",
@@ -249,7 +266,8 @@ def main():
                    "plan": {kk: vplan[kk] for kk in ("variant_name", "n_splits", "keys_per_split", "n_head_chunks",
                                                      "grid_blocks")}},
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic and traffic["prefill_call_bytes"],
                      "kernel": "attn_prefill pass (attn_fwd_kernel + merge_kernel when split)",
                      "avg_call_us": round(float(call_mean_ms.mean()) * 1e3, 2)},
         "setup_s": round(gen_s, 1),
