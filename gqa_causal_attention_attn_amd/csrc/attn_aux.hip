@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   if (wave != 0) return;
   acc = part_acc[0][lane] + part_acc[1][lane] + part_acc[2][lane] + part_acc[3][lane];
   wsum = part_w[0] + part_w[1] + part_w[2] + part_w[3];
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const float inv = wsum > 0.0f ? __builtin_amdgcn_rcpf(wsum) : 0.0f;
   const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
   const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
                  to_f32<DT>((uint16_t)(gw[1] & 0xffffu)), to_f32<DT>((uint16_t)(gw[1] >> 16))};
   float res[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) res[i] = acc[i] * inv * (1.0f / (1.0f + __expf(-gv[i])));
+  for (int i = 0; i < 4; ++i) res[i] = acc[i] * inv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[i]));
   u32x2 ow;
   ow[0] = pack2<DT>(res[0], res[1]);
   ow[1] = pack2<DT>(res[2], res[3]);

@@ -1,10 +1,10 @@
 // Main pass of gated causal GQA attention at head_dim 256 for gfx950 (CDNA4).
 //
 // One workgroup = one (batch b, KV head g, KV split s, tile of 8 x 32 (head, row) pairs of
-// that group).  The group's K and V are streamed through LDS in 64-key tiles and all eight
+// that group).  The group's K and V are streamed through LDS in 32-key tiles and all eight
 // wavefronts reuse every tile, so K/V is read once per group per split.  Tiles move from
-// HBM to LDS with direct global->LDS loads (no registers, no VALU), double-buffered: tile
-// t + 1 is in flight while tile t is consumed.
+// HBM to LDS with direct buffer->LDS loads (no registers, no VALU) into a ring of four
+// stages: two tiles are in flight while one is consumed.
 //
 // Per wavefront, 32 (head, row) pairs are the N dimension of v_mfma_f32_32x32x16 (bf16 or
 // fp16 in, fp32 accumulate):
@@ -14,19 +14,20 @@
 //
 // With keys (and dims) on the MFMA rows and pairs on its columns, every lane owns one pair
 // (lane % 32) in both products: the online softmax needs no cross-lane traffic except one
-// swap with the lane 32 away, and the S accumulator, packed to 16 bits, is already the B
-// operand of the second product.  The k-slots of that product are permuted keys: slot
-// 4a + t of lane half h holds key 16s + 8a + 4h + t, which is the order the S accumulator
-// leaves in the registers; the A operand is gathered in that order by ds_read_b64_tr_b16,
-// which hands each lane of a 16-lane group one column of a 4 x 16 block of 16-bit values
-// (4 keys x 16 dims) read as rows by the group.
+// exchange with the lane 32 away, and the S accumulator, packed to 16 bits, is already the
+// B operand of the second product.  The k-slots of that product follow the rows of the S
+// accumulator: slot 4a + t of lane half h is row 8a + 4h + t (+16 for the second MFMA); the
+// A operand is gathered in that order by ds_read_b64_tr_b16, which hands each lane of a
+// 16-lane group one column of a 4 x 16 block of 16-bit values (4 rows x 16 dims) that the
+// group reads as rows.
 //
-// LDS layout of a 64-key x 256-dim tile (32 KiB): 16-byte cells (8 dims), index
-//   cell(key, c) = (c / 4) * 256 + (key / 16) * 64 + (c % 4) * 16 + slot,
-// slot = key % 16 for K and (key % 16 + 4 (c % 4)) % 16 for V; one direct load of a wavefront
-// fills one 1 KiB group (16 keys x 4 cells).  The V skew keeps the transposing reads of a
-// 16-lane group (4 keys x 2 cells) on distinct banks; K reads (16 keys, one cell) are
-// contiguous.  Every LDS address is a per-lane base plus a compile-time offset.
+// LDS layout of a 32-key x 256-dim tile: sixteen groups of two whole key rows (1 KiB, the
+// unit one direct load of a wavefront fills from 1 KiB of contiguous memory), group i at
+// i * 1040 bytes: the 16-byte skew per group puts the same dims of different groups on
+// different banks.  MFMA row r holds key 2 gamma(r % 16) + r / 16 with gamma(x) = 4 (x % 4) +
+// x / 4, so the 16 lanes of a K read (16 rows, one 16-byte cell) hit 16 groups and the
+// transposing V reads (4 rows x 2 cells per 16 lanes) hit distinct banks.  Every LDS address
+// is a per-lane base plus a compile-time offset.
 //
 // The softmax is the online (flash) form of the plain definition: per pair a running max m
 // (log2 units of the scaled score), a running sum l and the accumulator O, rescaled by
@@ -112,6 +113,18 @@ __device__ __forceinline__ float hi16(uint32_t w) {
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
+// acc + (low 16-bit value of w) + (high 16-bit value of w), both values taken exactly (one
+// v_dot2 against (1, 1)).
+template <int DT>
+__device__ __forceinline__ float sum2(uint32_t w, float acc) {
+  if constexpr (DT == 0) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
+                                           false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+  }
+}
+
 // One ds_read_b64_tr_b16 at a per-lane LDS byte address plus an immediate offset.  Written as
 // inline assembly so the offset stays in the instruction; the caller waits with lgkm_wait
 // before using the result (the compiler does not track this load).
@@ -129,7 +142,9 @@ __device__ __forceinline__ void lgkm_wait(u32x4& a, u32x4& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// sigmoid with the hardware reciprocal (1 ulp): 1 / (1 + e^-x); +-Inf and NaN map as the
+// plain formula does
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Workgroup i is dispatched to XCD i % 8.  Map it to a logical index so that each XCD
 // receives one contiguous range of logical workgroups (which share K/V in that XCD's L2).
@@ -154,25 +169,33 @@ __device__ __forceinline__ float mask_term(const void* base, int64_t row_off, in
   }
 }
 
-// Issue the direct loads of tile j0 .. j0 + 31 (keys clamped to jmax, which only feeds keys
-// that every pair masks) into the K and V halves of one LDS stage.  Wavefront w loads the
-// 1 KiB groups 2w and 2w + 1 of each tile.
+// Buffer resource over `bytes` bytes from `base` (gfx9 word 3: raw, untyped).  Reads at
+// offsets past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Issue the direct loads of tile j0 .. j0 + 31 into the K and V halves of one LDS stage.
+// Group i = keys 2i and 2i + 1, two whole 512-byte rows (lane l: key 2i + l / 32, dims
+// 8 (l % 32) .. + 7), lands at i * kGroupStride; wavefront w loads groups 2w and 2w + 1
+// (keys j0 + 4w .. j0 + 4w + 3).  The per-lane byte offsets koff / voff (row l / 32, 16-byte
+// cell l % 32) stay fixed; each wavefront's four rows get a resource that ends at key kv_end,
+// so keys past the end read as zeros (every pair masks them) and nothing past it is touched.
 __device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t* vbase, int64_t k_st, int64_t v_st,
-                                           int j0, int jmax, uint8_t* stage, int wave, int lane) {
-  const int c_lo = lane >> 4;
-  const int key_lo_k = lane & 15;
-  const int key_lo_v = ((lane & 15) - 4 * c_lo) & 15;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int grp = wave * 2 + e;  // 0..15
-    const int c = (grp >> 1) * 4 + c_lo;
-    const int key_hi = grp & 1;
-    const int jk = min(j0 + key_hi * 16 + key_lo_k, jmax);
-    const int jv = min(j0 + key_hi * 16 + key_lo_v, jmax);
-    __builtin_amdgcn_global_load_lds(kbase + (int64_t)jk * k_st + 8 * c, (lds_void*)(stage + grp * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + (int64_t)jv * v_st + 8 * c,
-                                     (lds_void*)(stage + kTileBytes + grp * 1024), 16, 0, 0);
-  }
+                                           int j0, int kv_end, uint8_t* stage, int wave, uint32_t koff,
+                                           uint32_t voff) {
+  const int j = j0 + 4 * wave;
+  const int rows = min(max(kv_end - j, 0), 4);
+  const int kbytes = rows ? (rows - 1) * (int)k_st * 2 + kHeadDim * 2 : 0;
+  const int vbytes = rows ? (rows - 1) * (int)v_st * 2 + kHeadDim * 2 : 0;
+  const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + (int64_t)j * k_st, kbytes);
+  const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + (int64_t)j * v_st, vbytes);
+  uint8_t* g0 = stage + (2 * wave) * kGroupStride;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)g0, 16, koff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(g0 + kGroupStride), 16, koff + 4 * (uint32_t)k_st, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(g0 + kTileLds), 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(g0 + kTileLds + kGroupStride), 16, voff + 4 * (uint32_t)v_st,
+                                           0, 0, 0);
 }
 constexpr int kLoadsPerTile = 4;  // direct-load instructions per wavefront per tile
 
@@ -190,16 +213,17 @@ __device__ __forceinline__ void lgkm_wait1(u32x4& a) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
 }
 
-// Wait until at most N direct loads of this wavefront are in flight (N a multiple of the
-// loads per tile, at most kPrefetch - 1 tiles' worth).
+// Wait until at most n_tiles tiles' direct loads of this wavefront are in flight
+// (n_tiles <= kPrefetch - 1).
 __device__ __forceinline__ void wait_tiles_in_flight(int n_tiles) {
-  switch (n_tiles) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-  }
+  static_assert(kPrefetch == 2 && kLoadsPerTile == 4, "one case per count of tiles in flight");
+  if (n_tiles == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
 }
+
+// Key (within the tile, less 2 hf) of element q of the S accumulator: row 8 (q / 4) + 4 hf +
+// q % 4 of the MFMA holds key 2 gamma(row % 16) + row / 16, gamma(x) = 4 (x % 4) + x / 4.
+__device__ __forceinline__ constexpr int key_of(int q) { return 8 * (q & 3) + 4 * ((q >> 2) & 1) + (q >> 3); }
 
 // max(x, x of the lane 32 away), the same value on both lanes
 __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
@@ -211,11 +235,11 @@ template <int DT, int MK>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p) {
   // kStages stages of (K tile, V tile), 32 KiB each: up to kPrefetch tiles in flight while one
   // is consumed.  Stage of tile t: t % kStages.
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * 2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kFwdLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps branches on it scalar
   const int li = lane & 31;  // pair slot of this lane
   const int hf = lane >> 5;  // which half of the MFMA k-slots this lane feeds
 
@@ -259,8 +283,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
     lim_min = min(lim_min, lim_of(f0 / csj));
   }
   const int kv_lo = split * p.keys_per_split;
-  const int kv_end = min(kv_lo + p.keys_per_split, kv_hi);
+  const int kv_end = __builtin_amdgcn_readfirstlane(min(kv_lo + p.keys_per_split, kv_hi));
   const int n_kt = kv_end > kv_lo ? (kv_end - kv_lo + kKeysPerTile - 1) / kKeysPerTile : 0;
+  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
   const uint16_t* kbase = p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
   const uint16_t* vbase = p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
@@ -276,20 +301,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
   }
   const int64_t mrow = MK ? (int64_t)b * p.m_sb + (int64_t)h * p.m_sh + (int64_t)r * p.m_sr : 0;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q is in registers before the tile stream starts
+  const uint32_t koff = (uint32_t)(lane >> 5) * (uint32_t)p.k_st * 2 + 16 * (lane & 31);
+  const uint32_t voff = (uint32_t)(lane >> 5) * (uint32_t)p.v_st * 2 + 16 * (lane & 31);
   for (int t = 0; t < kPrefetch && t < n_kt; ++t) {
-    issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kKeysPerTile, kv_end - 1, lds + t * 2 * kTileBytes, wave,
-               lane);
+    issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kKeysPerTile, kv_end, lds + t * kStageLds, wave, koff, voff);
   }
 
   // per-lane LDS byte addresses (see the layout above); every read adds a compile-time offset
+  // MFMA row r of a tile holds key 2 gamma(r % 16) + r / 16 with gamma(x) = 4 (x % 4) + x / 4:
+  // each 16-lane half of a K read then touches 16 different groups, one per bank quad.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)lds;
-  const uint32_t k_lane = (li >> 4) * 1024 + hf * 256 + (li & 15) * 16;
-  const int grp16 = lane >> 4, i16 = lane & 15;
-  const int tq = i16 >> 2, uq = i16 & 3;
-  const int c_lo_v = 2 * (grp16 & 1) + (uq >> 1);
-  const int xv = 4 * (grp16 >> 1) + tq + 4 * c_lo_v;
-  const uint32_t v_lane0 = kTileBytes + c_lo_v * 256 + (xv & 15) * 16 + (uq & 1) * 8;
-  const uint32_t v_lane1 = kTileBytes + c_lo_v * 256 + ((xv + 8) & 15) * 16 + (uq & 1) * 8;
+  const int li16 = li & 15;
+  const uint32_t k_lane = (4 * (li16 & 3) + (li16 >> 2)) * kGroupStride + (li >> 4) * 512 + hf * 16;
+  // transposing V reads: lane 16 g16 + 4 t + u gives row t (key 2 (4 t + h) + 16 m + 8 a ... in
+  // MFMA-row order) and dims 32 db + 16 (g16 % 2) + 4 u .. + 3; a, m and db are immediates
+  const int g16 = lane >> 4, tq = (lane >> 2) & 3, uq = lane & 3;
+  const uint32_t v_lane = kTileLds + (4 * tq + hf) * kGroupStride + 16 * (2 * (g16 & 1) + (uq >> 1)) + 8 * (uq & 1);
 
   f32x16 oacc[8];
 #pragma unroll
@@ -307,10 +334,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
     if (t + kPrefetch < n_kt) {
       int st2 = stage + kPrefetch;
       if (st2 >= kStages) st2 -= kStages;
-      issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + kPrefetch) * kKeysPerTile, kv_end - 1,
-                 lds + st2 * 2 * kTileBytes, wave, lane);
+      issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + kPrefetch) * kKeysPerTile, kv_end, lds + st2 * kStageLds,
+                 wave, koff, voff);
     }
-    const uint32_t sb = lds0 + stage * 2 * kTileBytes;
+    const uint32_t sb = lds0 + stage * kStageLds;
     stage = stage + 1 == kStages ? 0 : stage + 1;
     return sb;
   };
@@ -320,6 +347,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
     for (int t = 0; t < n_kt; ++t) stream_step(t);
     return;
   }
+  // O^T += V^T P^T over the 8 dim blocks of the tile at LDS address sb_; the V operands of
+  // block db + 1 are read while the two MFMAs of block db run
+  auto pv = [&](uint32_t sb_, const u32x4& pb0_, const u32x4& pb1_) {
+    const uint32_t va = sb_ + v_lane;
+    u32x4 va4[2][2];
+    auto read_v = [&](auto dbc, u32x4(&dst)[2]) {
+      constexpr int db = decltype(dbc)::value;
+      // MFMA m covers rows 16 m .. 16 m + 15 (+512: odd keys); its k-slots 4 a + t take rows
+      // 8 a + 4 h + t (+2 kGroupStride for a = 1)
+      constexpr int o00 = 64 * db, o10 = o00 + 2 * kGroupStride, o01 = o00 + 512, o11 = o10 + 512;
+      const u32x2 w00 = ds_read_tr16<o00>(va), w10 = ds_read_tr16<o10>(va);
+      const u32x2 w01 = ds_read_tr16<o01>(va), w11 = ds_read_tr16<o11>(va);
+      dst[0] = (u32x4){w00[0], w00[1], w10[0], w10[1]};
+      dst[1] = (u32x4){w01[0], w01[1], w11[0], w11[1]};
+    };
+    read_v(std::integral_constant<int, 0>{}, va4[0]);
+    static_for<8>([&](auto dbc) {
+      constexpr int db = decltype(dbc)::value;
+      if constexpr (db < 7) {
+        read_v(std::integral_constant<int, db + 1>{}, va4[(db + 1) & 1]);
+        lgkm_wait<4>(va4[db & 1][0], va4[db & 1][1]);
+      } else {
+        lgkm_wait<0>(va4[db & 1][0], va4[db & 1][1]);
+      }
+      oacc[db] = mfma32<DT>(va4[db & 1][0], pb0_, oacc[db]);
+      oacc[db] = mfma32<DT>(va4[db & 1][1], pb1_, oacc[db]);
+    });
+  };
+
   for (int t = 0; t < n_kt; ++t) {
     const uint32_t sbase = stream_step(t);
     const int jb = kv_lo + t * kKeysPerTile;
@@ -333,13 +389,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
       u32x4 kop[kAhead + 1];
       static_for<kAhead>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        kop[i] = ds_read_b128<(i >> 1) * 2048 + (i & 1) * 512>(kaddr);
+        kop[i] = ds_read_b128<32 * i>(kaddr);
       });
       static_for<16>([&](auto kkc) {
         constexpr int kk = decltype(kkc)::value;
         if constexpr (kk + kAhead < 16) {
           kop[(kk + kAhead) % (kAhead + 1)] =
-              ds_read_b128<((kk + kAhead) >> 1) * 2048 + ((kk + kAhead) & 1) * 512>(kaddr);
+              ds_read_b128<32 * (kk + kAhead)>(kaddr);
         }
         constexpr int issued = kk + kAhead + 1 < 16 ? kk + kAhead + 1 : 16;
         lgkm_wait1<issued - kk - 1>(kop[kk % (kAhead + 1)]);
@@ -348,7 +404,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
     }
 
     __builtin_amdgcn_sched_barrier(0);
-    // element q of sacc holds key jb + 8 (q / 4) + 4 hf + (q % 4) of this lane's pair
+    // element q of sacc is MFMA row 8 (q / 4) + 4 hf + q % 4, i.e. key jb + key_of(q) + 2 hf of
+    // this lane's pair
     uint32_t pw[8];
     float lsum = 0.0f;
     float alpha, m_next;
@@ -361,10 +418,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
 #pragma unroll
       for (int q = 0; q < 16; ++q) sm[q] = sacc[q];
       if (jb + kKeysPerTile > lim_min) {  // wave-uniform
-        const int jl = jb + 4 * hf;
+        const int jl = jb + 2 * hf;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          if (jl + 8 * (q >> 2) + (q & 3) >= lim) sm[q] = -INFINITY;
+          if (jl + key_of(q) >= lim) sm[q] = -INFINITY;
         }
       }
       float mr = fmaxf(fmaxf(sm[0], sm[1]), sm[2]);
@@ -380,13 +437,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
       for (int q = 0; q < 8; ++q) {
         pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sm[2 * q], p.scale_log2, neg_m)),
                           __builtin_amdgcn_exp2f(__builtin_fmaf(sm[2 * q + 1], p.scale_log2, neg_m)));
-        lsum += lo16<DT>(pw[q]) + hi16<DT>(pw[q]);
+        lsum = sum2<DT>(pw[q], lsum);
       }
     } else {
       // scaled scores plus the mask term (log2 units); hidden and out-of-bound keys get -inf
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int j = jb + 8 * (q >> 2) + 4 * hf + (q & 3);
+        const int j = jb + key_of(q) + 2 * hf;
         sacc[q] = j < lim ? sacc[q] * p.scale_log2 + mask_term<DT, MK>(p.mask, mrow, j) : -INFINITY;
       }
       float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
@@ -400,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(sacc[2 * q] - m_use), __builtin_amdgcn_exp2f(sacc[2 * q + 1] - m_use));
-        lsum += lo16<DT>(pw[q]) + hi16<DT>(pw[q]);
+        lsum = sum2<DT>(pw[q], lsum);
       }
     }
     l_run = l_run * alpha + lsum;
@@ -412,36 +469,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
     const u32x4 pb0 = (u32x4){pw[0], pw[1], pw[2], pw[3]};
     const u32x4 pb1 = (u32x4){pw[4], pw[5], pw[6], pw[7]};
     __builtin_amdgcn_sched_barrier(0);
-    // O^T += V^T P^T over the 8 dim blocks; the V operands of block db + 1 are read while the
-    // two MFMAs of block db run
-    const uint32_t va0 = sbase + v_lane0, va1 = sbase + v_lane1;
-    u32x4 va[2][2];
-    auto read_v = [&](auto dbc, u32x4(&dst)[2]) {
-      constexpr int db = decltype(dbc)::value;
-      constexpr int o0 = db * 2048, o1 = o0 + 1024;  // key groups 0 and 1 of the tile
-      const u32x2 w00 = ds_read_tr16<o0>(va0), w01 = ds_read_tr16<o0>(va1);
-      const u32x2 w10 = ds_read_tr16<o1>(va0), w11 = ds_read_tr16<o1>(va1);
-      dst[0] = (u32x4){w00[0], w00[1], w01[0], w01[1]};
-      dst[1] = (u32x4){w10[0], w10[1], w11[0], w11[1]};
-    };
-    read_v(std::integral_constant<int, 0>{}, va[0]);
-    static_for<8>([&](auto dbc) {
-      constexpr int db = decltype(dbc)::value;
-      if constexpr (db < 7) {
-        read_v(std::integral_constant<int, db + 1>{}, va[(db + 1) & 1]);
-        lgkm_wait<4>(va[db & 1][0], va[db & 1][1]);
-      } else {
-        lgkm_wait<0>(va[db & 1][0], va[db & 1][1]);
-      }
-      oacc[db] = mfma32<DT>(va[db & 1][0], pb0, oacc[db]);
-      oacc[db] = mfma32<DT>(va[db & 1][1], pb1, oacc[db]);
-    });
+    pv(sbase, pb0, pb1);
   }
 
   // ---- epilogue: element q of oacc[db] is dim 32 db + 8 (q / 4) + 4 hf + (q % 4)
   const float l_tot = sum_halves(l_run);
   if (!valid) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float inv = l_tot > 0.0f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
   if (p.n_splits == 1) {
     const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
     uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;

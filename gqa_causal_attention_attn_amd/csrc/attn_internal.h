@@ -11,10 +11,13 @@ constexpr int kHeadDim = 256;
 constexpr int kKeysPerTile = 32;     // keys staged in LDS per step
 constexpr int kWavesPerBlock = 8;    // wavefronts per workgroup of the main pass
 constexpr int kPairsPerWave = 32;    // (head, row) pairs per wavefront (one 32-wide MFMA column block)
-constexpr int kTileBytes = kKeysPerTile * kHeadDim * 2;      // one K (or V) tile: 16 KiB
-constexpr int kStages = 5;                                   // LDS stages of (K tile, V tile)
-constexpr int kPrefetch = 4;                                 // tiles in flight ahead of the one consumed
-constexpr int kFwdLdsBytes = kStages * 2 * kTileBytes;       // 160 KiB
+constexpr int kTileBytes = kKeysPerTile * kHeadDim * 2;      // one K (or V) tile: 16 KiB of data
+constexpr int kGroupStride = 1040;   // LDS bytes per two-key group: 1 KiB + a 16-byte bank skew
+constexpr int kTileLds = (kKeysPerTile / 2) * kGroupStride;  // one K (or V) tile in LDS: 16,640 B
+constexpr int kStageLds = 2 * kTileLds;                      // one stage = K tile + V tile
+constexpr int kStages = 4;                                   // LDS stages of (K tile, V tile)
+constexpr int kPrefetch = 2;                                 // tiles in flight ahead of the one consumed
+constexpr int kFwdLdsBytes = kStages * kStageLds;            // 133,120 B
 constexpr int kTargetBlocks = 256;   // main-pass workgroups aimed for (one per CU)
 
 // Parameters of the main (flash / split-KV) pass.  Strides are in elements.
