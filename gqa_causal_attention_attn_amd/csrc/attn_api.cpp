@@ -14,8 +14,8 @@ namespace {
 
 using gqa::kHeadDim;
 using gqa::kKeysPerTile;
-using gqa::kPairsPerWave;
-using gqa::kWavesPerBlock;
+using gqa::kBlocksPerGroup;
+using gqa::kPairsPerBlock;
 
 constexpr int kRowPairLimit = 32;  // the head-chunk rule's 32 (head, row) pairs per call
 
@@ -24,7 +24,10 @@ struct Plan {
   int chunk;
   int n_chunks;
   int chunk_sizes[ATTN_MAX_CHUNKS];
-  int waves_per_chunk;
+  int blocks_per_chunk;
+  int shape;  // 0: 4 wavefronts x 1 column block, 1: 4 x 2, 2: 8 x 1
+  int waves;  // wavefronts per workgroup
+  int nb;     // column blocks per wavefront
   int n_tiles;
   int n_splits;
   int keys_per_split;
@@ -104,12 +107,18 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   }
   if (P->n_chunks <= 0) return ATTN_E_ARG;
   P->chunk = P->chunk_sizes[0];
-  P->waves_per_chunk = (int)cdiv((int64_t)P->chunk * a->rows, kPairsPerWave);
-  P->n_tiles = (int)cdiv((int64_t)P->n_chunks * P->waves_per_chunk, kWavesPerBlock);
+  P->blocks_per_chunk = (int)cdiv((int64_t)P->chunk * a->rows, kPairsPerBlock);
+  // four wavefronts of one 32-pair column block when they cover the whole KV group (short
+  // decode / verify), else eight wavefronts of one block (two per SIMD)
+  const int64_t n_blocks = (int64_t)P->n_chunks * P->blocks_per_chunk;
+  P->shape = n_blocks <= 4 ? 0 : 2;
+  P->waves = P->shape == 2 ? 8 : 4;
+  P->nb = P->shape == 1 ? 2 : 1;
+  P->n_tiles = (int)cdiv(n_blocks, (int64_t)P->waves * P->nb);
 
   // KV splits depend only on the unchunked shape, so every head-chunk choice splits the keys
   // the same way and gives the same bits.
-  const int64_t base_tiles = cdiv(cdiv((int64_t)G * a->rows, kPairsPerWave), kWavesPerBlock);
+  const int64_t base_tiles = cdiv(cdiv((int64_t)G * a->rows, kPairsPerBlock), kBlocksPerGroup);
   const int64_t kv_hi = a->causal ? (a->kv_len < a->kv_offset + a->rows ? a->kv_len : a->kv_offset + a->rows)
                                   : a->kv_len;
   const int64_t n_kt = cdiv(kv_hi, kKeysPerTile);
@@ -141,7 +150,7 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   return ATTN_OK;
 }
 
-inline int variant_of(const attn_args* a) { return (a->dtype << 2) | a->mask.kind; }
+inline int variant_of(const attn_args* a, int shape) { return (shape << 3) | (a->dtype << 2) | a->mask.kind; }
 
 int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream) {
   int st = validate(a, op);
@@ -177,7 +186,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream)
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / 16.0f;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.chunk = P.chunk;
-  p.waves_per_chunk = P.waves_per_chunk;
+  p.blocks_per_chunk = P.blocks_per_chunk;
   p.n_tiles = P.n_tiles;
   p.n_splits = P.n_splits;
   p.keys_per_split = P.keys_per_split;
@@ -187,7 +196,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream)
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_o_bytes);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (gqa::launch_fwd(p, a->dtype, a->mask.kind, s) != hipSuccess) return ATTN_E_HIP;
+  if (gqa::launch_fwd(p, a->dtype, a->mask.kind, P.shape, s) != hipSuccess) return ATTN_E_HIP;
   if (P.n_splits > 1) {
     gqa::MergeParams mp;
     mp.part_o = p.part_o;
@@ -238,11 +247,14 @@ const char* attn_strerror(int status) {
 }
 
 const char* attn_variant_name(int variant) {
-  static const char* const names[8] = {
-      "fwd_mfma32x32x16_bf16",          "fwd_mfma32x32x16_bf16_maskbool", "fwd_mfma32x32x16_bf16_maskadd",
-      "fwd_mfma32x32x16_bf16_maskf32",  "fwd_mfma32x32x16_f16",           "fwd_mfma32x32x16_f16_maskbool",
-      "fwd_mfma32x32x16_f16_maskadd",   "fwd_mfma32x32x16_f16_maskf32"};
-  return (variant >= 0 && variant < 8) ? names[variant] : "unknown";
+  // id = shape * 8 + dtype * 4 + mask kind
+#define GQA_NAMES(SHAPE)                                                                                        \
+  "fwd_mfma32x32x16_bf16_" SHAPE, "fwd_mfma32x32x16_bf16_maskbool_" SHAPE, "fwd_mfma32x32x16_bf16_maskadd_" SHAPE, \
+      "fwd_mfma32x32x16_bf16_maskf32_" SHAPE, "fwd_mfma32x32x16_f16_" SHAPE, "fwd_mfma32x32x16_f16_maskbool_" SHAPE, \
+      "fwd_mfma32x32x16_f16_maskadd_" SHAPE, "fwd_mfma32x32x16_f16_maskf32_" SHAPE
+  static const char* const names[24] = {GQA_NAMES("4x1"), GQA_NAMES("4x2"), GQA_NAMES("8x1")};
+#undef GQA_NAMES
+  return (variant >= 0 && variant < 24) ? names[variant] : "unknown";
 }
 
 int attn_head_chunk_plan(int rows, int n_q_heads, int n_kv_heads, int enabled, int* sizes, int cap, int* n_chunks) {
@@ -275,12 +287,12 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
   if (st) return st;
   memset(info, 0, sizeof(*info));
   info->op = op;
-  info->variant = variant_of(a);
+  info->variant = variant_of(a, P.shape);
   info->group_size = P.G;
   info->n_head_chunks = P.n_chunks;
   info->head_chunk = P.chunk;
-  info->rows_per_wave = kPairsPerWave;
-  info->waves_per_block = kWavesPerBlock;
+  info->rows_per_wave = P.nb * kPairsPerBlock;
+  info->waves_per_block = P.waves;
   info->n_row_tiles = P.n_tiles;
   info->n_splits = P.n_splits;
   info->keys_per_split = P.keys_per_split;

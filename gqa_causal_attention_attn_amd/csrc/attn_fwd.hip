@@ -78,7 +78,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kThreads = kWavesPerBlock * 64;
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -90,6 +89,52 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                   0, 0);
   }
 }
+
+// acc += A B with the accumulator in accumulation registers (AGPRs).  Written as inline
+// assembly so the accumulators stay there; the leading s_nop gives the wait states a VALU
+// write of A or B needs before an MFMA reads it.  Back-to-back accumulation into the same
+// registers needs none.
+template <int DT>
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, const u32x4& a, const u32x4& b) {
+  if constexpr (DT == 0) {
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  } else {
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
+}
+
+// acc (+)= A B with the accumulator in VGPRs (FIRST: acc = A B), as inline assembly for the
+// same reason and with the same leading wait states.
+template <int DT, bool FIRST>
+__device__ __forceinline__ void mfma32_v(f32x16& acc, const u32x4& a, const u32x4& b) {
+  if constexpr (FIRST) {
+    if constexpr (DT == 0) {
+      asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+    } else {
+      asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+    }
+  } else {
+    if constexpr (DT == 0) {
+      asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    } else {
+      asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    }
+  }
+}
+
+// Wait states between the last MFMA into sc and the first instruction that reads sc.
+__device__ __forceinline__ void acc_settle_v(f32x16& sc) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sc)); }
+
+// Wait states between the last mfma32_acc into o and any other instruction that reads o
+// (more than an 8-pass MFMA needs); tied to o so nothing that reads it moves above.
+__device__ __forceinline__ void acc_settle(f32x16 (&o)[8]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]));
+}
+
+// Pins o[db] and o[db + 1] in place: whatever reads o[db + 1] after this stays after it, so
+// the accumulators are taken out one 16-register tuple at a time.
+__device__ __forceinline__ void acc_step(f32x16& cur, f32x16& next) { asm volatile("" : "+a"(cur), "+a"(next)); }
 
 // Two floats -> two 16-bit values (round to nearest even), low half = a.
 template <int DT>
@@ -177,27 +222,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 
 // Issue the direct loads of tile j0 .. j0 + 31 into the K and V halves of one LDS stage.
 // Group i = keys 2i and 2i + 1, two whole 512-byte rows (lane l: key 2i + l / 32, dims
-// 8 (l % 32) .. + 7), lands at i * kGroupStride; wavefront w loads groups 2w and 2w + 1
-// (keys j0 + 4w .. j0 + 4w + 3).  The per-lane byte offsets koff / voff (row l / 32, 16-byte
-// cell l % 32) stay fixed; each wavefront's four rows get a resource that ends at key kv_end,
-// so keys past the end read as zeros (every pair masks them) and nothing past it is touched.
+// 8 (l % 32) .. + 7), lands at i * kGroupStride; with W wavefronts, wavefront w loads the
+// G = 16 / W groups G w .. G w + G - 1 (keys j0 + 2 G w ..).  The per-lane byte offsets
+// koff / voff (row l / 32, 16-byte cell l % 32) stay fixed; each wavefront's rows get a
+// resource that ends at key kv_end, so keys past the end read as zeros (every pair masks
+// them) and nothing past it is touched.
+template <int W>
 __device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t* vbase, int64_t k_st, int64_t v_st,
                                            int j0, int kv_end, uint8_t* stage, int wave, uint32_t koff,
                                            uint32_t voff) {
-  const int j = j0 + 4 * wave;
-  const int rows = min(max(kv_end - j, 0), 4);
+  constexpr int kGroups = 16 / W;
+  const int j = j0 + 2 * kGroups * wave;
+  const int rows = min(max(kv_end - j, 0), 2 * kGroups);
   const int kbytes = rows ? (rows - 1) * (int)k_st * 2 + kHeadDim * 2 : 0;
   const int vbytes = rows ? (rows - 1) * (int)v_st * 2 + kHeadDim * 2 : 0;
   const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + (int64_t)j * k_st, kbytes);
   const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + (int64_t)j * v_st, vbytes);
-  uint8_t* g0 = stage + (2 * wave) * kGroupStride;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)g0, 16, koff, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(g0 + kGroupStride), 16, koff + 4 * (uint32_t)k_st, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(g0 + kTileLds), 16, voff, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(g0 + kTileLds + kGroupStride), 16, voff + 4 * (uint32_t)v_st,
-                                           0, 0, 0);
+  uint8_t* g0 = stage + (kGroups * wave) * kGroupStride;
+#pragma unroll
+  for (int e = 0; e < kGroups; ++e) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(g0 + e * kGroupStride), 16, koff + 4 * e * (uint32_t)k_st,
+                                             0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(g0 + kTileLds + e * kGroupStride), 16,
+                                             voff + 4 * e * (uint32_t)v_st, 0, 0, 0);
+  }
 }
-constexpr int kLoadsPerTile = 4;  // direct-load instructions per wavefront per tile
 
 // One ds_read_b128 at a per-lane LDS byte address plus an immediate offset (inline assembly:
 // the compiler neither tracks it nor waits for it; see lgkm_wait1).
@@ -214,10 +263,12 @@ __device__ __forceinline__ void lgkm_wait1(u32x4& a) {
 }
 
 // Wait until at most n_tiles tiles' direct loads of this wavefront are in flight
-// (n_tiles <= kPrefetch - 1).
+// (n_tiles <= kPrefetch - 1); a tile is 32 / W direct loads of each of the W wavefronts.
+template <int W>
 __device__ __forceinline__ void wait_tiles_in_flight(int n_tiles) {
-  static_assert(kPrefetch == 2 && kLoadsPerTile == 4, "one case per count of tiles in flight");
+  static_assert(kPrefetch == 2, "one case per count of tiles in flight");
   if (n_tiles == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (W == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
 }
 
@@ -231,16 +282,19 @@ __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xo
 // x + (x of the lane 32 away), the same sum on both lanes
 __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
 
-template <int DT, int MK>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p) {
-  // kStages stages of (K tile, V tile), 32 KiB each: up to kPrefetch tiles in flight while one
-  // is consumed.  Stage of tile t: t % kStages.
+template <int DT, int MK, int W, int NB>
+__global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) {
+  static_assert((W == 4 && (NB == 1 || NB == 2)) || (W == 8 && NB == 1), "4 wavefronts of 1 or 2 blocks, or 8 of 1");
+  constexpr bool TWO = NB == 2;
+  constexpr int kGroupBlocks = W * NB;  // column blocks of this workgroup
+  // kStages stages of (K tile, V tile): kPrefetch tiles in flight while one is consumed and
+  // the one before it finishes its P.V product.  Stage of tile t: t % kStages.
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kFwdLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps branches on it scalar
-  const int li = lane & 31;  // pair slot of this lane
+  const int li = lane & 31;  // pair slot of this lane in each column block
   const int hf = lane >> 5;  // which half of the MFMA k-slots this lane feeds
 
   // ---- which (b, g, split, tile) this workgroup serves
@@ -255,31 +309,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
 
   auto lim_of = [&](int row) { return p.causal ? min(p.kv_len, p.kv_offset + row + 1) : p.kv_len; };
 
-  // ---- the (head, row) pair of this lane
-  const int wi = tile * kWavesPerBlock + wave;
-  const int chunk_idx = wi / p.waves_per_chunk;
-  const int f = (wi - chunk_idx * p.waves_per_chunk) * kPairsPerWave + li;
-  const int hstart = chunk_idx * p.chunk;
-  const int cs = min(p.chunk, p.G - hstart);
-  const bool valid = hstart < p.G && f < cs * p.rows;
-  const int r = valid ? f / cs : 0;
-  const int h = g * p.G + hstart + (valid ? f - (f / cs) * cs : 0);
-  const int lim = valid ? lim_of(r) : 0;
-  const bool wave_active = __builtin_amdgcn_ballot_w64(valid) != 0;
+  // ---- the (head, row) pairs of this lane: column block c of wavefront w is block NB w + c
+  // of the workgroup; a chunk of heads takes blocks_per_chunk blocks
+  auto pair_of = [&](int blk, int& h_out, int& r_out) {
+    const int bi = tile * kGroupBlocks + NB * wave + blk;
+    const int chunk_idx = bi / p.blocks_per_chunk;
+    const int f = (bi - chunk_idx * p.blocks_per_chunk) * kPairsPerBlock + li;
+    const int hstart = chunk_idx * p.chunk;
+    const int cs = min(p.chunk, p.G - hstart);
+    const bool valid = hstart < p.G && f < cs * p.rows;
+    r_out = valid ? f / cs : 0;
+    h_out = g * p.G + hstart + (valid ? f - (f / cs) * cs : 0);
+    return valid;
+  };
+  int h0, r0, h1 = 0, r1 = 0;
+  const bool valid0 = pair_of(0, h0, r0);
+  const bool valid1 = TWO && pair_of(1, h1, r1);
+  const int lim0 = valid0 ? lim_of(r0) : 0;
+  const int lim1 = valid1 ? lim_of(r1) : 0;
+  const bool act0 = __builtin_amdgcn_ballot_w64(valid0) != 0;
+  const bool act1 = __builtin_amdgcn_ballot_w64(valid1) != 0;
 
   // ---- key range of the workgroup [kv_lo, kv_end) and the smallest bound of its pairs, from
-  // the pair layout of its wavefronts (uniform arithmetic)
+  // the pair layout of its column blocks (uniform arithmetic)
   int kv_hi = 0, lim_min = 0x7fffffff;
-  for (int w = 0; w < kWavesPerBlock; ++w) {
-    const int wj = tile * kWavesPerBlock + w;
-    const int cj = wj / p.waves_per_chunk;
-    const int f0 = (wj - cj * p.waves_per_chunk) * kPairsPerWave;
+  for (int bj = tile * kGroupBlocks; bj < (tile + 1) * kGroupBlocks; ++bj) {
+    const int cj = bj / p.blocks_per_chunk;
+    const int f0 = (bj - cj * p.blocks_per_chunk) * kPairsPerBlock;
     const int hs = cj * p.chunk;
     if (hs >= p.G) continue;
     const int csj = min(p.chunk, p.G - hs);
     const int npairs = csj * p.rows;
     if (f0 >= npairs) continue;
-    kv_hi = max(kv_hi, lim_of((min(f0 + kPairsPerWave, npairs) - 1) / csj));
+    kv_hi = max(kv_hi, lim_of((min(f0 + kPairsPerBlock, npairs) - 1) / csj));
     lim_min = min(lim_min, lim_of(f0 / csj));
   }
   const int kv_lo = split * p.keys_per_split;
@@ -290,51 +352,65 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
   const uint16_t* kbase = p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
   const uint16_t* vbase = p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
 
-  // ---- Q of this lane's pair, in the B-operand order: element t of qreg[kk] is dim 16 kk + 8 hf + t
-  u32x4 qreg[16];
+  // ---- Q of this lane's pairs, in the B-operand order: element t of q*[kk] is dim
+  // 16 kk + 8 hf + t
+  u32x4 q0[16], q1[16];
   {
-    const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)r * p.q_sr + 8 * hf;
+    const uint16_t* qa = p.q + (int64_t)b * p.q_sb + (int64_t)h0 * p.q_sh + (int64_t)r0 * p.q_sr + 8 * hf;
+    const uint16_t* qb = p.q + (int64_t)b * p.q_sb + (int64_t)h1 * p.q_sh + (int64_t)r1 * p.q_sr + 8 * hf;
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-      qreg[kk] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : (u32x4){0u, 0u, 0u, 0u};
+        q0[kk] = valid0 ? *reinterpret_cast<const u32x4*>(qa + 16 * kk) : (u32x4){0u, 0u, 0u, 0u};
+      q1[kk] = TWO && valid1 ? *reinterpret_cast<const u32x4*>(qb + 16 * kk) : (u32x4){0u, 0u, 0u, 0u};
     }
   }
-  const int64_t mrow = MK ? (int64_t)b * p.m_sb + (int64_t)h * p.m_sh + (int64_t)r * p.m_sr : 0;
+  const int64_t mrow0 = MK ? (int64_t)b * p.m_sb + (int64_t)h0 * p.m_sh + (int64_t)r0 * p.m_sr : 0;
+  const int64_t mrow1 = MK ? (int64_t)b * p.m_sb + (int64_t)h1 * p.m_sh + (int64_t)r1 * p.m_sr : 0;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q is in registers before the tile stream starts
   const uint32_t koff = (uint32_t)(lane >> 5) * (uint32_t)p.k_st * 2 + 16 * (lane & 31);
   const uint32_t voff = (uint32_t)(lane >> 5) * (uint32_t)p.v_st * 2 + 16 * (lane & 31);
   for (int t = 0; t < kPrefetch && t < n_kt; ++t) {
-    issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kKeysPerTile, kv_end, lds + t * kStageLds, wave, koff, voff);
+    issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kKeysPerTile, kv_end, lds + t * kStageLds, wave, koff, voff);
   }
 
-  // per-lane LDS byte addresses (see the layout above); every read adds a compile-time offset
+  // per-lane LDS byte addresses (see the layout above); every read adds a compile-time offset.
   // MFMA row r of a tile holds key 2 gamma(r % 16) + r / 16 with gamma(x) = 4 (x % 4) + x / 4:
   // each 16-lane half of a K read then touches 16 different groups, one per bank quad.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)lds;
   const int li16 = li & 15;
   const uint32_t k_lane = (4 * (li16 & 3) + (li16 >> 2)) * kGroupStride + (li >> 4) * 512 + hf * 16;
-  // transposing V reads: lane 16 g16 + 4 t + u gives row t (key 2 (4 t + h) + 16 m + 8 a ... in
-  // MFMA-row order) and dims 32 db + 16 (g16 % 2) + 4 u .. + 3; a, m and db are immediates
+  // transposing V reads: lane 16 g16 + 4 t + u reads MFMA row 4 hf + t (+8 a, +16 m) and dims
+  // 32 db + 16 (g16 % 2) + 4 u .. + 3; a, m and db are immediates
   const int g16 = lane >> 4, tq = (lane >> 2) & 3, uq = lane & 3;
   const uint32_t v_lane = kTileLds + (4 * tq + hf) * kGroupStride + 16 * (2 * (g16 & 1) + (uq >> 1)) + 8 * (uq & 1);
 
-  f32x16 oacc[8];
+  // the accumulators live in the accumulation registers (AGPRs), everything the VALU touches
+  // every tile in VGPRs
+  f32x16 o0[8], o1[8];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) oacc[db] = (f32x16){};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
+  for (int db = 0; db < 8; ++db) {
+    o0[db] = (f32x16){};
+    asm volatile("" : "+a"(o0[db]));
+    if constexpr (TWO) {
+      o1[db] = (f32x16){};
+      asm volatile("" : "+a"(o1[db]));
+    }
+  }
+
+  float m0 = -INFINITY, l0 = 0.0f, m1 = -INFINITY, l1 = 0.0f;
 
   // One step of the tile stream: wait for tile t (issued kPrefetch steps ago), sync, and
   // start tile t + kPrefetch.  Returns the LDS address of tile t's stage.
   int stage = 0;
   auto stream_step = [&](int t) {
     // tile t landed for this wavefront once only the tiles issued after it remain in flight
-    wait_tiles_in_flight(min(kPrefetch - 1, n_kt - 1 - t));
-    __builtin_amdgcn_s_barrier();  // ... and for everyone; everyone is done with tile t - 1
+    wait_tiles_in_flight<W>(min(kPrefetch - 1, n_kt - 1 - t));
+    // ... and for everyone; everyone is done with tile t - 2, whose stage is refilled next
+    __builtin_amdgcn_s_barrier();
     if (t + kPrefetch < n_kt) {
       int st2 = stage + kPrefetch;
       if (st2 >= kStages) st2 -= kStages;
-      issue_tile(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + kPrefetch) * kKeysPerTile, kv_end, lds + st2 * kStageLds,
+      issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + kPrefetch) * kKeysPerTile, kv_end, lds + st2 * kStageLds,
                  wave, koff, voff);
     }
     const uint32_t sb = lds0 + stage * kStageLds;
@@ -342,15 +418,139 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
     return sb;
   };
 
-  if (!wave_active) {
+  if (!act0 && !act1) {
     // a wavefront without pairs only helps stream the tiles
     for (int t = 0; t < n_kt; ++t) stream_step(t);
     return;
   }
-  // O^T += V^T P^T over the 8 dim blocks of the tile at LDS address sb_; the V operands of
-  // block db + 1 are read while the two MFMAs of block db run
-  auto pv = [&](uint32_t sb_, const u32x4& pb0_, const u32x4& pb1_) {
-    const uint32_t va = sb_ + v_lane;
+
+  // ---- S^T block of the tile at sb: rows = its 32 keys, columns = the 32 pairs of block q;
+  // K operands read two steps ahead
+  auto scores = [&](uint32_t sb, const u32x4(&q)[16]) {
+    f32x16 sc;
+    const uint32_t kaddr = sb + k_lane;
+    constexpr int kAhead = 2;  // K operands in flight beyond the one consumed
+    u32x4 kop[kAhead + 1];
+    static_for<kAhead>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      kop[i] = ds_read_b128<32 * i>(kaddr);
+    });
+    static_for<16>([&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      if constexpr (kk + kAhead < 16) kop[(kk + kAhead) % (kAhead + 1)] = ds_read_b128<32 * (kk + kAhead)>(kaddr);
+      constexpr int issued = kk + kAhead + 1 < 16 ? kk + kAhead + 1 : 16;
+      lgkm_wait1<issued - kk - 1>(kop[kk % (kAhead + 1)]);
+      mfma32_v<DT, kk == 0>(sc, kop[kk % (kAhead + 1)], q[kk]);
+    });
+    acc_settle_v(sc);
+    return sc;
+  };
+
+  // ---- both S blocks of the tile at sb: two independent MFMA chains sharing every K read
+  auto scores2 = [&](uint32_t sb, f32x16& sa, f32x16& sc) {
+    const uint32_t kaddr = sb + k_lane;
+    constexpr int kAhead = 2;
+    u32x4 kop[kAhead + 1];
+    static_for<kAhead>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      kop[i] = ds_read_b128<32 * i>(kaddr);
+    });
+    static_for<16>([&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      if constexpr (kk + kAhead < 16) kop[(kk + kAhead) % (kAhead + 1)] = ds_read_b128<32 * (kk + kAhead)>(kaddr);
+      constexpr int issued = kk + kAhead + 1 < 16 ? kk + kAhead + 1 : 16;
+      lgkm_wait1<issued - kk - 1>(kop[kk % (kAhead + 1)]);
+      mfma32_v<DT, kk == 0>(sa, kop[kk % (kAhead + 1)], q0[kk]);
+      mfma32_v<DT, kk == 0>(sc, kop[kk % (kAhead + 1)], q1[kk]);
+    });
+    acc_settle_v(sa);
+    acc_settle_v(sc);
+  };
+
+  // ---- element q of an S block is MFMA row 8 (q / 4) + 4 hf + q % 4, i.e. key jb + key_of(q)
+  // + 2 hf of this lane's pair.  Scores in log2 units, with keys the pair cannot see at
+  // -inf.  Without a mask the scale folds into the exponent later (the max commutes with
+  // it, scale > 0) and only tiles that reach some pair's bound compare keys.
+  auto mask_scores = [&](f32x16& sc, int jb, int lim, int64_t mrow) {
+    if constexpr (MK == 0) {
+      if (jb + kKeysPerTile > lim_min) {  // wave-uniform
+        const int jl = jb + 2 * hf;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          if (jl + key_of(q) >= lim) sc[q] = -INFINITY;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int j = jb + key_of(q) + 2 * hf;
+        sc[q] = j < lim ? sc[q] * p.scale_log2 + mask_term<DT, MK>(p.mask, mrow, j) : -INFINITY;
+      }
+    }
+  };
+
+  // ---- online softmax of one block, in two parts.  stats: the new running max of each
+  // pair.  m moves only when the tile's max exceeds it by more than kRescaleSlack; a lane
+  // compares its own half of the pair's keys first, and only when some lane of the wavefront
+  // sees such a max are the two halves exchanged, so the common case stays off the LDS pipe.
+  // The decision per pair is the same as with the exchange every time.  Returns the factor
+  // alpha for l and o (1 when m stays) and whether any pair of the wavefront moved.
+  auto stats = [&](const f32x16& sc, float& m_run, float& alpha) {
+    float mr = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+    for (int q = 3; q < 15; q += 2) mr = fmaxf(fmaxf(mr, sc[q]), sc[q + 1]);
+    mr = fmaxf(mr, sc[15]);
+    const float scale = MK == 0 ? p.scale_log2 : 1.0f;
+    alpha = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(mr * scale > m_run + kRescaleSlack)) {
+      const float mx = max_halves(mr) * scale;
+      const bool upd = mx > m_run + kRescaleSlack;
+      const float m_next = upd ? mx : m_run;
+      alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_next) : 1.0f;
+      m_run = m_next;
+      return __builtin_amdgcn_ballot_w64(upd) != 0;
+    }
+    return false;
+  };
+
+  // exp part: the tile's weights exp2(s - m), rounded once to 16 bits and packed as the B
+  // operand of P.V; l_run = alpha l_run + the sum of the rounded weights
+  auto weights = [&](const f32x16& sc, float m_run, float alpha, float& l_run, u32x4& pb0, u32x4& pb1) {
+    const float scale = MK == 0 ? p.scale_log2 : 1.0f;
+    const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
+    uint32_t pw[8];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * q], scale, neg_m)),
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * q + 1], scale, neg_m)));
+      lsum = sum2<DT>(pw[q], lsum);
+    }
+    l_run = l_run * alpha + lsum;
+    pb0 = (u32x4){pw[0], pw[1], pw[2], pw[3]};
+    pb1 = (u32x4){pw[4], pw[5], pw[6], pw[7]};
+    // keep this work in the phase it is written in (beside the P.V issued just before),
+    // instead of letting it sink next to its use
+    asm volatile("" : "+v"(pb0), "+v"(pb1), "+v"(l_run));
+  };
+
+  // o *= alpha when some pair's max moved (issued before the P.V product that follows it)
+  auto rescale = [&](f32x16(&o)[8], float alpha, bool moved) {
+    if (moved) {
+      acc_settle(o);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        o[db] *= alpha;
+        if (db < 7) acc_step(o[db], o[db + 1]);
+      }
+      acc_settle(o);
+    }
+  };
+
+  // ---- O^T += V^T P^T over the 8 dim blocks of the tile at sb; the V operands of block
+  // db + 1 are read while the two MFMAs of block db run
+  auto pv = [&](uint32_t sb, const u32x4& pb0, const u32x4& pb1, f32x16(&o)[8]) {
+    const uint32_t va = sb + v_lane;
     u32x4 va4[2][2];
     auto read_v = [&](auto dbc, u32x4(&dst)[2]) {
       constexpr int db = decltype(dbc)::value;
@@ -371,167 +571,160 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const FwdParams p
       } else {
         lgkm_wait<0>(va4[db & 1][0], va4[db & 1][1]);
       }
-      oacc[db] = mfma32<DT>(va4[db & 1][0], pb0_, oacc[db]);
-      oacc[db] = mfma32<DT>(va4[db & 1][1], pb1_, oacc[db]);
+      o[db] = mfma32<DT>(va4[db & 1][0], pb0, o[db]);
+      o[db] = mfma32<DT>(va4[db & 1][1], pb1, o[db]);
+      asm volatile("" : "+a"(o[db]));
     });
   };
 
-  for (int t = 0; t < n_kt; ++t) {
-    const uint32_t sbase = stream_step(t);
-    const int jb = kv_lo + t * kKeysPerTile;
-
-    // S^T block: rows = the 32 keys of the tile, columns = the wave's 32 pairs; K operands
-    // read two steps ahead
-    f32x16 sacc = (f32x16){};
-    {
-      const uint32_t kaddr = sbase + k_lane;
-      constexpr int kAhead = 2;  // K operands in flight beyond the one consumed
-      u32x4 kop[kAhead + 1];
-      static_for<kAhead>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        kop[i] = ds_read_b128<32 * i>(kaddr);
-      });
-      static_for<16>([&](auto kkc) {
-        constexpr int kk = decltype(kkc)::value;
-        if constexpr (kk + kAhead < 16) {
-          kop[(kk + kAhead) % (kAhead + 1)] =
-              ds_read_b128<32 * (kk + kAhead)>(kaddr);
-        }
-        constexpr int issued = kk + kAhead + 1 < 16 ? kk + kAhead + 1 : 16;
-        lgkm_wait1<issued - kk - 1>(kop[kk % (kAhead + 1)]);
-        sacc = mfma32<DT>(kop[kk % (kAhead + 1)], qreg[kk], sacc);
-      });
-    }
-
+  // ---- the tile loop.  Matrix-core work and VALU work of different blocks and tiles are
+  // paired so that each runs beside the other:
+  //   two blocks:  [S_0(t)] [PV_1(t-1) | weights_0(t)] [S_1(t)] [PV_0(t) | weights_1(t)]
+  //   one block:   [S_0(t)] [PV_0(t-1) | weights_0(t)]
+  // The rescale of o by tile t's alpha is issued just before P_t V_t, so per pair the
+  // operations on o keep the plain order (scale by alpha_t, then add P_t V_t).
+  if (TWO && n_kt > 0) {
+    u32x4 pa0, pa1, pc0, pc1;  // packed weights of block 0 / block 1
+    float a0, a1;              // their alpha
+    bool f0, f1;               // whether some pair's max moved
+    f32x16 s0, s1;
+    uint32_t sb = stream_step(0);
+    scores2(sb, s0, s1);
+    mask_scores(s0, kv_lo, lim0, mrow0);
+    mask_scores(s1, kv_lo, lim1, mrow1);
+    f0 = stats(s0, m0, a0);
+    f1 = stats(s1, m1, a1);
+    weights(s0, m0, a0, l0, pa0, pa1);
     __builtin_amdgcn_sched_barrier(0);
-    // element q of sacc is MFMA row 8 (q / 4) + 4 hf + q % 4, i.e. key jb + key_of(q) + 2 hf of
-    // this lane's pair
-    uint32_t pw[8];
-    float lsum = 0.0f;
-    float alpha, m_next;
-    bool upd;
-    if constexpr (MK == 0) {
-      // Raw scores; keys past the pair's causal / cache bound get -inf (only on tiles that
-      // reach some pair's bound).  The scale folds into the exponent, and the max commutes
-      // with it (scale > 0), so every pair computes the same bits on either path.
-      float sm[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) sm[q] = sacc[q];
-      if (jb + kKeysPerTile > lim_min) {  // wave-uniform
-        const int jl = jb + 2 * hf;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          if (jl + key_of(q) >= lim) sm[q] = -INFINITY;
-        }
-      }
-      float mr = fmaxf(fmaxf(sm[0], sm[1]), sm[2]);
-#pragma unroll
-      for (int q = 3; q < 15; q += 2) mr = fmaxf(fmaxf(mr, sm[q]), sm[q + 1]);
-      mr = max_halves(fmaxf(mr, sm[15]));
-      const float mx = mr * p.scale_log2;
-      upd = mx > m_run + kRescaleSlack;
-      m_next = upd ? mx : m_run;
-      alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_next) : 1.0f;
-      const float neg_m = (m_next == -INFINITY) ? 0.0f : -m_next;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sm[2 * q], p.scale_log2, neg_m)),
-                          __builtin_amdgcn_exp2f(__builtin_fmaf(sm[2 * q + 1], p.scale_log2, neg_m)));
-        lsum = sum2<DT>(pw[q], lsum);
-      }
-    } else {
-      // scaled scores plus the mask term (log2 units); hidden and out-of-bound keys get -inf
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int j = jb + key_of(q) + 2 * hf;
-        sacc[q] = j < lim ? sacc[q] * p.scale_log2 + mask_term<DT, MK>(p.mask, mrow, j) : -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(sacc[0], sacc[1]), sacc[2]);
-#pragma unroll
-      for (int q = 3; q < 15; q += 2) mx = fmaxf(fmaxf(mx, sacc[q]), sacc[q + 1]);
-      mx = max_halves(fmaxf(mx, sacc[15]));
-      upd = mx > m_run + kRescaleSlack;
-      m_next = upd ? mx : m_run;
-      alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_next) : 1.0f;
-      const float m_use = (m_next == -INFINITY) ? 0.0f : m_next;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(sacc[2 * q] - m_use), __builtin_amdgcn_exp2f(sacc[2 * q + 1] - m_use));
-        lsum = sum2<DT>(pw[q], lsum);
-      }
+    pv(sb, pa0, pa1, o0);  // o0 is still 0: no rescale
+    weights(s1, m1, a1, l1, pc0, pc1);
+    uint32_t sprev = sb;
+    for (int t = 1; t < n_kt; ++t) {
+      sb = stream_step(t);
+      const int jb = kv_lo + t * kKeysPerTile;
+      __builtin_amdgcn_sched_barrier(0);
+      scores2(sb, s0, s1);
+      mask_scores(s0, jb, lim0, mrow0);
+      mask_scores(s1, jb, lim1, mrow1);
+      f0 = stats(s0, m0, a0);
+      rescale(o1, a1, f1);  // tile t - 1's alpha, before its P.V
+      __builtin_amdgcn_sched_barrier(0);
+      pv(sprev, pc0, pc1, o1);
+      weights(s0, m0, a0, l0, pa0, pa1);
+      __builtin_amdgcn_sched_barrier(0);
+      f1 = stats(s1, m1, a1);
+      rescale(o0, a0, f0);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(sb, pa0, pa1, o0);
+      weights(s1, m1, a1, l1, pc0, pc1);
+      sprev = sb;
     }
-    l_run = l_run * alpha + lsum;
-    m_run = m_next;
-    if (__builtin_amdgcn_ballot_w64(upd)) {
-#pragma unroll
-      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+    rescale(o1, a1, f1);
+    pv(sprev, pc0, pc1, o1);
+  } else if (!TWO && n_kt > 0) {
+    u32x4 pa0, pa1;
+    float a0;
+    bool f0;
+    uint32_t sb = stream_step(0);
+    f32x16 s0 = scores(sb, q0);
+    mask_scores(s0, kv_lo, lim0, mrow0);
+    f0 = stats(s0, m0, a0);
+    weights(s0, m0, a0, l0, pa0, pa1);
+    uint32_t sprev = sb;
+    for (int t = 1; t < n_kt; ++t) {
+      sb = stream_step(t);
+      const int jb = kv_lo + t * kKeysPerTile;
+      __builtin_amdgcn_sched_barrier(0);
+      s0 = scores(sb, q0);
+      mask_scores(s0, jb, lim0, mrow0);
+      // o still owes tile t - 1's alpha: keep it until its P.V is issued
+      const float a_prev = a0;
+      const bool f_prev = f0;
+      f0 = stats(s0, m0, a0);
+      rescale(o0, a_prev, f_prev);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(sprev, pa0, pa1, o0);
+      weights(s0, m0, a0, l0, pa0, pa1);
+      sprev = sb;
     }
-    const u32x4 pb0 = (u32x4){pw[0], pw[1], pw[2], pw[3]};
-    const u32x4 pb1 = (u32x4){pw[4], pw[5], pw[6], pw[7]};
-    __builtin_amdgcn_sched_barrier(0);
-    pv(sbase, pb0, pb1);
+    rescale(o0, a0, f0);
+    pv(sprev, pa0, pa1, o0);
   }
 
-  // ---- epilogue: element q of oacc[db] is dim 32 db + 8 (q / 4) + 4 hf + (q % 4)
-  const float l_tot = sum_halves(l_run);
-  if (!valid) return;
-  const float inv = l_tot > 0.0f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
-  if (p.n_splits == 1) {
-    const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
-    uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
+  // ---- epilogue: element q of o*[db] is dim 32 db + 8 (q / 4) + 4 hf + (q % 4)
+  const float lt0 = sum_halves(l0), lt1 = sum_halves(l1);
+  auto finish = [&](bool valid, int h, int r, float l_tot, float m_run, f32x16(&o)[8]) {
+    if (!valid) return;
+    const float inv = l_tot > 0.0f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
+    if (p.n_splits == 1) {
+      const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
+      uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < 8; ++db) {
+        if (db > 0) acc_step(o[db - 1], o[db]);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * db + 8 * q4 + 4 * hf;
-        const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
-        const float g0 = sigmoidf_(lo16<DT>(gw[0])), g1 = sigmoidf_(hi16<DT>(gw[0]));
-        const float g2 = sigmoidf_(lo16<DT>(gw[1])), g3 = sigmoidf_(hi16<DT>(gw[1]));
-        u32x2 ow;
-        ow[0] = pack2<DT>(oacc[db][4 * q4 + 0] * inv * g0, oacc[db][4 * q4 + 1] * inv * g1);
-        ow[1] = pack2<DT>(oacc[db][4 * q4 + 2] * inv * g2, oacc[db][4 * q4 + 3] * inv * g3);
-        *reinterpret_cast<u32x2*>(orow + d0) = ow;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * hf;
+          const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
+          const float g0 = sigmoidf_(lo16<DT>(gw[0])), g1 = sigmoidf_(hi16<DT>(gw[0]));
+          const float g2 = sigmoidf_(lo16<DT>(gw[1])), g3 = sigmoidf_(hi16<DT>(gw[1]));
+          u32x2 ow;
+          ow[0] = pack2<DT>(o[db][4 * q4 + 0] * inv * g0, o[db][4 * q4 + 1] * inv * g1);
+          ow[1] = pack2<DT>(o[db][4 * q4 + 2] * inv * g2, o[db][4 * q4 + 3] * inv * g3);
+          *reinterpret_cast<u32x2*>(orow + d0) = ow;
+        }
       }
-    }
-  } else {
-    const int64_t row_id = (((int64_t)split * p.B + b) * p.Hq + h) * p.rows + r;
-    float* prow = p.part_o + row_id * kHeadDim;
+    } else {
+      const int64_t row_id = (((int64_t)split * p.B + b) * p.Hq + h) * p.rows + r;
+      float* prow = p.part_o + row_id * kHeadDim;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < 8; ++db) {
+        if (db > 0) acc_step(o[db - 1], o[db]);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * db + 8 * q4 + 4 * hf;
-        f32x4 v4 = {oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv, oacc[db][4 * q4 + 2] * inv,
-                    oacc[db][4 * q4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(prow + d0) = v4;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * hf;
+          f32x4 v4 = {o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
+                      o[db][4 * q4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(prow + d0) = v4;
+        }
       }
+      if (hf == 0) p.part_lse[row_id] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
-    if (hf == 0) p.part_lse[row_id] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  };
+  acc_settle(o0);
+  finish(valid0, h0, r0, lt0, m0, o0);
+  if constexpr (TWO) {
+    acc_settle(o1);
+    finish(valid1, h1, r1, lt1, m1, o1);
   }
 }
 
 template <int DT, int MK>
-hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<DT, MK>), dim3(p.grid), dim3(kThreads), 0, stream, p);
+hipError_t launch_fwd_t(const FwdParams& p, int shape, hipStream_t stream) {
+  switch (shape) {
+    case 0: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 1>), dim3(p.grid), dim3(256), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 2>), dim3(p.grid), dim3(256), 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, 1>), dim3(p.grid), dim3(512), 0, stream, p); break;
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, hipStream_t stream) {
+hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream) {
   if (dtype == 0) {
     switch (mask_kind) {
-      case 0: return launch_fwd_t<0, 0>(p, stream);
-      case 1: return launch_fwd_t<0, 1>(p, stream);
-      case 2: return launch_fwd_t<0, 2>(p, stream);
-      default: return launch_fwd_t<0, 3>(p, stream);
+      case 0: return launch_fwd_t<0, 0>(p, shape, stream);
+      case 1: return launch_fwd_t<0, 1>(p, shape, stream);
+      case 2: return launch_fwd_t<0, 2>(p, shape, stream);
+      default: return launch_fwd_t<0, 3>(p, shape, stream);
     }
   }
   switch (mask_kind) {
-    case 0: return launch_fwd_t<1, 0>(p, stream);
-    case 1: return launch_fwd_t<1, 1>(p, stream);
-    case 2: return launch_fwd_t<1, 2>(p, stream);
-    default: return launch_fwd_t<1, 3>(p, stream);
+    case 0: return launch_fwd_t<1, 0>(p, shape, stream);
+    case 1: return launch_fwd_t<1, 1>(p, shape, stream);
+    case 2: return launch_fwd_t<1, 2>(p, shape, stream);
+    default: return launch_fwd_t<1, 3>(p, shape, stream);
   }
 }
 

@@ -9,8 +9,8 @@ namespace gqa {
 
 constexpr int kHeadDim = 256;
 constexpr int kKeysPerTile = 32;     // keys staged in LDS per step
-constexpr int kWavesPerBlock = 8;    // wavefronts per workgroup of the main pass
-constexpr int kPairsPerWave = 32;    // (head, row) pairs per wavefront (one 32-wide MFMA column block)
+constexpr int kBlocksPerGroup = 8;   // 32-pair column blocks of the largest workgroup
+constexpr int kPairsPerBlock = 32;   // (head, row) pairs per column block (the MFMA N dimension)
 constexpr int kTileBytes = kKeysPerTile * kHeadDim * 2;      // one K (or V) tile: 16 KiB of data
 constexpr int kGroupStride = 1040;   // LDS bytes per two-key group: 1 KiB + a 16-byte bank skew
 constexpr int kTileLds = (kKeysPerTile / 2) * kGroupStride;  // one K (or V) tile in LDS: 16,640 B
@@ -42,7 +42,7 @@ struct FwdParams {
   int causal;
   float scale_log2;      // scale * log2(e)
   int chunk;             // heads per chunk
-  int waves_per_chunk;   // wavefronts serving one chunk
+  int blocks_per_chunk;  // column blocks serving one chunk
   int n_tiles;           // workgroups per (batch, kv head, split)
   int n_splits;
   int keys_per_split;    // multiple of kKeysPerTile
@@ -69,7 +69,8 @@ struct AppendParams {
 };
 
 // Launchers (return hipGetLastError()).  dtype 0 = bf16, 1 = fp16; mask_kind as attn_mask_kind.
-hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, hipStream_t stream);
+// shape: 0 = 4 wavefronts x 1 column block, 1 = 4 x 2, 2 = 8 x 1 (wavefronts x blocks each)
+hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 
