@@ -4,8 +4,9 @@
 // and a merge of the chunks): per (b, h, r), lse = log sum_c exp(lse_c),
 // out = sum_c exp(lse_c - lse) o_c * sigmoid(gate), an empty chunk (lse_c = -Inf) adds
 // nothing (its slot is selected out, never multiplied in) and a row with every chunk empty
-// gives 0.  One workgroup per row, four dims per lane, the chunk partials fetched in batches
-// of independent loads spread over four wavefronts; HBM-bound (n_chunks x 1 KiB per row).
+// gives 0.  Few chunks: one wavefront per row with every partial loaded at once; many chunks
+// (decode): one workgroup per row, the chunk partials fetched in batches of independent loads
+// spread over four wavefronts.  HBM-bound (n_chunks x 1 KiB per row).
 //
 // Append (same commit, "pack, append and keep ... bit-exact"): a 16-byte copy of each new
 // K/V row into the cache; no arithmetic touches the bits.
@@ -110,6 +111,63 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   *reinterpret_cast<u32x2*>(orow + d0) = ow;
 }
 
+// Few chunks (prompt blocks split a handful of ways): one wavefront per row, four rows per
+// workgroup, four dims per lane, and every chunk's partial loaded at once (independent
+// 16-byte loads), so the pass streams instead of waiting on one load after another.
+constexpr int kFewChunks = 8;
+
+template <int DT>
+__global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
+  const int64_t row_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row_id >= n_rows) return;
+  const int r = (int)(row_id % p.rows);
+  const int h = (int)((row_id / p.rows) % p.Hq);
+  const int b = (int)(row_id / ((int64_t)p.rows * p.Hq));
+  const int d0 = 4 * lane;
+  float lc[kFewChunks];
+  f32x4 oc[kFewChunks];
+#pragma unroll
+  for (int c = 0; c < kFewChunks; ++c) {
+    if (c < p.n_chunks) {
+      lc[c] = p.part_lse[(int64_t)c * n_rows + row_id];
+      oc[c] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)c * n_rows + row_id) * kHeadDim + d0);
+    }
+  }
+  float top = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kFewChunks; ++c) {
+    if (c < p.n_chunks) top = fmaxf(top, lc[c]);
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.0f;
+  if (top > -INFINITY) {
+#pragma unroll
+    for (int c = 0; c < kFewChunks; ++c) {
+      // an empty chunk is selected out, never multiplied in
+      if (c < p.n_chunks && lc[c] != -INFINITY) {
+        const float w = exp2f((lc[c] - top) * kLog2e);
+        acc += w * oc[c];
+        wsum += w;
+      }
+    }
+  }
+  const float inv = wsum > 0.0f ? __builtin_amdgcn_rcpf(wsum) : 0.0f;
+  const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
+  uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
+  const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
+  float gv[4] = {to_f32<DT>((uint16_t)(gw[0] & 0xffffu)), to_f32<DT>((uint16_t)(gw[0] >> 16)),
+                 to_f32<DT>((uint16_t)(gw[1] & 0xffffu)), to_f32<DT>((uint16_t)(gw[1] >> 16))};
+  float res[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) res[i] = acc[i] * inv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[i]));
+  u32x2 ow;
+  ow[0] = pack2<DT>(res[0], res[1]);
+  ow[1] = pack2<DT>(res[2], res[3]);
+  *reinterpret_cast<u32x2*>(orow + d0) = ow;
+}
+
 // One 16-byte chunk per thread: (tensor, b, g, r, chunk of 8 elements).
 __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   const int64_t per_tensor = (int64_t)p.B * p.Hkv * p.rows * (kHeadDim / 8);
@@ -134,9 +192,15 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
 
 hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
-  const dim3 grid((unsigned)n_rows);
-  if (dtype == 0) hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, stream, p);
+  if (p.n_chunks <= kFewChunks) {
+    const dim3 grid((unsigned)((n_rows + 3) / 4));
+    if (dtype == 0) hipLaunchKernelGGL(merge_few_kernel<0>, grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(merge_few_kernel<1>, grid, dim3(256), 0, stream, p);
+  } else {
+    const dim3 grid((unsigned)n_rows);
+    if (dtype == 0) hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

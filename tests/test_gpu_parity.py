@@ -175,19 +175,27 @@ def test_kv_append_is_bit_exact():
 
 
 @needs_gpu
-def test_merge_matches_oracle():
+@pytest.mark.parametrize("n_chunks", [4, 12])  # the few-chunk and the many-chunk merge passes
+def test_merge_matches_oracle(n_chunks):
     rng = syn.streams(8)
     B, Hq, Hkv, rows, kv = 1, 8, 2, 5, 90
     q = syn.widen(syn.normal_bits(rng["q"], (B, Hq, rows, 256)))
     k = syn.widen(syn.normal_bits(rng["k"], (B, Hkv, kv, 256)))
     v = syn.widen(syn.normal_bits(rng["v"], (B, Hkv, kv, 256)))
     gb = syn.normal_bits(rng["gate"], (B, Hq, rows, 256))
-    chunks = [(0, 30), (30, 60), (60, 90), (90, 120)]  # the last chunk is empty
+    step = 120 // n_chunks
+    chunks = [(c * step, (c + 1) * step) for c in range(n_chunks)]  # the chunks past key 90 are empty
     o, l_ = reference.partials(q, k, v, n_kv_heads=Hkv, kv_offset=kv - rows, kv_len=kv, chunks=chunks)
-    out = ga.merge(torch.from_numpy(o.astype(np.float32)).cuda(), torch.from_numpy(l_.astype(np.float32)).cuda(),
-                   to_dev(gb))
+    o32, l32 = o.astype(np.float32), l_.astype(np.float32)
+    # one row empty in every chunk, with NaN partials: never multiplied in, the row is 0
+    l32[:, 0, 3, 2] = -np.inf
+    o32[:, 0, 3, 2, :] = np.nan
+    out = ga.merge(torch.from_numpy(o32).cuda(), torch.from_numpy(l32).cuda(), to_dev(gb))
     ref = reference.merge(o, l_, syn.widen(gb))
-    _say(assert_close(to_f64(out), ref, "merge"))
+    ref[0, 3, 2, :] = 0.0
+    got = to_f64(out)
+    assert np.all(got[0, 3, 2, :] == 0.0)
+    _say(assert_close(got, ref, f"merge {n_chunks} chunks"))
 
 
 @needs_gpu
