@@ -142,6 +142,7 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   P->keys_per_split = (int)(tps * kKeysPerTile);
   P->grid = (int64_t)a->B * a->Hkv * S * P->n_tiles;
   if (P->grid > INT32_MAX) return ATTN_E_ARG;
+  if ((int64_t)a->B * a->Hq * a->rows > (int64_t)INT32_MAX) return ATTN_E_ARG;  // the merge indexes rows in 32 bits
   if (S > 1) {
     const int64_t nrow = S * a->B * a->Hq * (int64_t)a->rows;
     P->ws_o_bytes = (size_t)cdiv(nrow * kHeadDim * 4, 256) * 256;
@@ -346,7 +347,7 @@ int attn_merge(const merge_args* a, void* stream) {
   if (a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
   if (a->rows < 1) return ATTN_E_ROWS;
   if (a->n_chunks < 1) return ATTN_E_ARG;
-  if ((int64_t)a->B * a->Hq * a->rows > (int64_t)INT32_MAX * 4) return ATTN_E_ARG;
+  if ((int64_t)a->B * a->Hq * a->rows > (int64_t)INT32_MAX) return ATTN_E_ARG;  // rows are indexed in 32 bits
   if (!a->partial_o || !a->partial_lse || !a->gate.ptr || !a->out.ptr) return ATTN_E_NULL;
   if (!aligned16(a->partial_o) || !aligned16(a->gate.ptr) || !aligned16(a->out.ptr) || !strides_ok(a->gate) ||
       !strides_ok(a->out) || (reinterpret_cast<uintptr_t>(a->partial_lse) & 3u))

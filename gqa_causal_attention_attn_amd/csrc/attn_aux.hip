@@ -5,8 +5,8 @@
 // out = sum_c exp(lse_c - lse) o_c * sigmoid(gate), an empty chunk (lse_c = -Inf) adds
 // nothing (its slot is selected out, never multiplied in) and a row with every chunk empty
 // gives 0.  Few chunks: one wavefront per row with every partial loaded at once; many chunks
-// (decode): one workgroup per row, the chunk partials fetched in batches of independent loads
-// spread over four wavefronts.  HBM-bound (n_chunks x 1 KiB per row).
+// (decode): one workgroup of sixteen wavefronts per row, each loading its share of the
+// chunks at once.  HBM-bound (n_chunks x 1 KiB per row).
 //
 // Append (same commit, "pack, append and keep ... bit-exact"): a 16-byte copy of each new
 // K/V row into the cache; no arithmetic touches the bits.
@@ -39,67 +39,88 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   else return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
 }
 
-// One workgroup of four wavefronts per row: wavefront w takes the chunks w, w + 4, ...; its
-// weights come from one load of the row's lse values per lane, its partials from batches of
-// eight independent loads; the four partial sums meet in LDS.
+// Many chunks (decode): one workgroup of kMergeWaves wavefronts per row; wavefront w takes the
+// chunks w, w + kMergeWaves, ... (kMergeBatch per pass).  A pass issues all of its lse and
+// partial loads (and the gate) at once; only the row's largest lse crosses the wavefronts
+// (through LDS) before the weights are applied, so a row up to kMergeWaves x kMergeBatch
+// chunks costs one round trip to memory.  The partial sums meet in LDS.
+constexpr int kMergeWaves = 16;
+constexpr int kMergeBatch = 4;
+
 template <int DT>
-__global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
-  __shared__ f32x4 part_acc[4][64];
-  __shared__ float part_w[4];
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergeParams p) {
+  __shared__ f32x4 part_acc[kMergeWaves][64];
+  __shared__ float part_w[kMergeWaves];
+  __shared__ float part_top[kMergeWaves];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
   const int64_t row_id = blockIdx.x;
-  const int r = (int)(row_id % p.rows);
-  const int h = (int)((row_id / p.rows) % p.Hq);
-  const int b = (int)(row_id / ((int64_t)p.rows * p.Hq));
-
-  // largest lse of the row: lane i of every wavefront reads chunks i, i + 64, ...
-  float top = -INFINITY;
-  for (int c = lane; c < p.n_chunks; c += 64) top = fmaxf(top, p.part_lse[(int64_t)c * n_rows + row_id]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) top = fmaxf(top, __shfl_xor(top, o));
-
+  const uint32_t bh = blockIdx.x / (uint32_t)p.rows;
+  const int r = (int)(blockIdx.x - bh * (uint32_t)p.rows);
+  const int b = (int)(bh / (uint32_t)p.Hq);
+  const int h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
   const int d0 = 4 * lane;
+  const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
+  const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
+
+  // acc and wsum are kept relative to ref, the largest lse seen so far (the same in every
+  // wavefront: each pass's largest lse is shared through LDS)
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
-  if (top > -INFINITY) {
-    for (int base = 0; base < p.n_chunks; base += 64) {
-      // lane i holds the weight of chunk base + i (0 for an empty chunk or past the end)
-      const int c = base + lane;
-      const float lc = c < p.n_chunks ? p.part_lse[(int64_t)c * n_rows + row_id] : -INFINITY;
-      const float w = lc == -INFINITY ? 0.0f : exp2f((lc - top) * kLog2e);
-      const int m = min(64, p.n_chunks - base);
-      // this wavefront's chunks of the window: base + wave + 4 i
-      for (int i0 = wave; i0 < m; i0 += 32) {
-        f32x4 oc[8];
-        float wj[8];
+  float ref = -INFINITY;
+  for (int c0 = 0; c0 < p.n_chunks; c0 += kMergeWaves * kMergeBatch) {
+    // this pass's chunks of the wavefront, all loads in flight together (indices past the
+    // last chunk re-read it and are selected out)
+    float lc[kMergeBatch];
+    f32x4 oc[kMergeBatch];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = i0 + 4 * j;
-          const int cc = min(base + i, p.n_chunks - 1);
-          oc[j] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * kHeadDim + d0);
-          wj[j] = i < m ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), i)) : 0.0f;
-        }
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int cc = min(c0 + wave + j * kMergeWaves, p.n_chunks - 1);
+      lc[j] = p.part_lse[(int64_t)cc * n_rows + row_id];
+      oc[j] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * kHeadDim + d0);
+    }
+    float top = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          // an empty chunk is selected out, never multiplied in, so its slot cannot reach the sum
-          if (wj[j] != 0.0f) acc += wj[j] * oc[j];
-          wsum += wj[j];
+    for (int j = 0; j < kMergeBatch; ++j) top = c0 + wave + j * kMergeWaves < p.n_chunks ? fmaxf(top, lc[j]) : top;
+    if (lane == 0) part_top[wave] = top;
+    __syncthreads();
+    float pass_top = part_top[0];
+#pragma unroll
+    for (int w = 1; w < kMergeWaves; ++w) pass_top = fmaxf(pass_top, part_top[w]);
+    const float new_ref = fmaxf(ref, pass_top);
+    if (ref > -INFINITY && new_ref > ref) {
+      const float f = exp2f((ref - new_ref) * kLog2e);
+      acc *= f;
+      wsum *= f;
+    }
+    ref = new_ref;
+    if (ref > -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        // an empty chunk is selected out, never multiplied in
+        if (c0 + wave + j * kMergeWaves < p.n_chunks && lc[j] != -INFINITY) {
+          const float w = exp2f((lc[j] - ref) * kLog2e);
+          acc += w * oc[j];
+          wsum += w;
         }
       }
     }
+    __syncthreads();  // part_top is rewritten by the next pass
   }
   part_acc[wave][lane] = acc;
   if (lane == 0) part_w[wave] = wsum;
   __syncthreads();
   if (wave != 0) return;
-  acc = part_acc[0][lane] + part_acc[1][lane] + part_acc[2][lane] + part_acc[3][lane];
-  wsum = part_w[0] + part_w[1] + part_w[2] + part_w[3];
+  acc = part_acc[0][lane];
+  wsum = part_w[0];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) {
+    acc += part_acc[w][lane];
+    wsum += part_w[w];
+  }
   const float inv = wsum > 0.0f ? __builtin_amdgcn_rcpf(wsum) : 0.0f;
-  const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
-  const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
   float gv[4] = {to_f32<DT>((uint16_t)(gw[0] & 0xffffu)), to_f32<DT>((uint16_t)(gw[0] >> 16)),
                  to_f32<DT>((uint16_t)(gw[1] & 0xffffu)), to_f32<DT>((uint16_t)(gw[1] >> 16))};
   float res[4];
@@ -120,26 +141,30 @@ template <int DT>
 __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
-  const int64_t row_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row_id >= n_rows) return;
-  const int r = (int)(row_id % p.rows);
-  const int h = (int)((row_id / p.rows) % p.Hq);
-  const int b = (int)(row_id / ((int64_t)p.rows * p.Hq));
+  const uint32_t row32 = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (row32 >= (uint64_t)n_rows) return;
+  const int64_t row_id = row32;
+  // (b, h, r) of the row in 32-bit arithmetic (the host keeps B Hq rows below 2^31)
+  const uint32_t bh = row32 / (uint32_t)p.rows;
+  const int r = (int)(row32 - bh * (uint32_t)p.rows);
+  const int b = (int)(bh / (uint32_t)p.Hq);
+  const int h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
   const int d0 = 4 * lane;
+  // every load is unconditional (chunk indices past the last one re-read the last one) so
+  // they are all in flight together; chunks past the last one are selected out below
   float lc[kFewChunks];
   f32x4 oc[kFewChunks];
+  const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
+  const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
 #pragma unroll
   for (int c = 0; c < kFewChunks; ++c) {
-    if (c < p.n_chunks) {
-      lc[c] = p.part_lse[(int64_t)c * n_rows + row_id];
-      oc[c] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)c * n_rows + row_id) * kHeadDim + d0);
-    }
+    const int cc = min(c, p.n_chunks - 1);
+    lc[c] = p.part_lse[(int64_t)cc * n_rows + row_id];
+    oc[c] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * kHeadDim + d0);
   }
   float top = -INFINITY;
 #pragma unroll
-  for (int c = 0; c < kFewChunks; ++c) {
-    if (c < p.n_chunks) top = fmaxf(top, lc[c]);
-  }
+  for (int c = 0; c < kFewChunks; ++c) top = c < p.n_chunks ? fmaxf(top, lc[c]) : top;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
   if (top > -INFINITY) {
@@ -154,9 +179,7 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
     }
   }
   const float inv = wsum > 0.0f ? __builtin_amdgcn_rcpf(wsum) : 0.0f;
-  const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
-  const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
   float gv[4] = {to_f32<DT>((uint16_t)(gw[0] & 0xffffu)), to_f32<DT>((uint16_t)(gw[0] >> 16)),
                  to_f32<DT>((uint16_t)(gw[1] & 0xffffu)), to_f32<DT>((uint16_t)(gw[1] >> 16))};
   float res[4];
@@ -198,8 +221,8 @@ hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
     else hipLaunchKernelGGL(merge_few_kernel<1>, grid, dim3(256), 0, stream, p);
   } else {
     const dim3 grid((unsigned)n_rows);
-    if (dtype == 0) hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(256), 0, stream, p);
+    if (dtype == 0) hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(kMergeWaves * 64), 0, stream, p);
+    else hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(kMergeWaves * 64), 0, stream, p);
   }
   return hipGetLastError();
 }

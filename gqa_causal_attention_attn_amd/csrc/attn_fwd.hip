@@ -262,14 +262,19 @@ __device__ __forceinline__ void lgkm_wait1(u32x4& a) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
 }
 
-// Wait until at most n_tiles tiles' direct loads of this wavefront are in flight
-// (n_tiles <= kPrefetch - 1); a tile is 32 / W direct loads of each of the W wavefronts.
+// Wait until at most n_tiles (<= 2) tiles' direct loads of this wavefront are in flight; a
+// tile is 32 / W direct loads of each of the W wavefronts.
 template <int W>
 __device__ __forceinline__ void wait_tiles_in_flight(int n_tiles) {
-  static_assert(kPrefetch == 2, "one case per count of tiles in flight");
-  if (n_tiles == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (W == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  if (n_tiles == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else if (n_tiles == 1) {
+    if constexpr (W == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    if constexpr (W == 4) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  }
 }
 
 // Key (within the tile, less 2 hf) of element q of the S accumulator: row 8 (q / 4) + 4 hf +
@@ -286,6 +291,13 @@ template <int DT, int MK, int W, int NB>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) {
   static_assert((W == 4 && (NB == 1 || NB == 2)) || (W == 8 && NB == 1), "4 wavefronts of 1 or 2 blocks, or 8 of 1");
   constexpr bool TWO = NB == 2;
+  // Short decode / verify (four wavefronts of one block) streams keys from HBM and has little
+  // to compute per tile: its P.V runs right after its softmax, which frees the previous tile's
+  // stage for a third tile in flight.  The other shapes keep P.V one tile behind.
+  constexpr bool LAG = !(W == 4 && NB == 1);
+  constexpr int PF = LAG ? kPrefetch : kPrefetch + 1;  // tiles in flight
+  static_assert(PF < kStages || !LAG, "the lagged P.V keeps tile t - 1 in its stage");
+  static_assert(PF <= kStages - 1 && PF <= 3, "a stage for the tile consumed");
   constexpr int kGroupBlocks = W * NB;  // column blocks of this workgroup
   // kStages stages of (K tile, V tile): kPrefetch tiles in flight while one is consumed and
   // the one before it finishes its P.V product.  Stage of tile t: t % kStages.
@@ -369,7 +381,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q is in registers before the tile stream starts
   const uint32_t koff = (uint32_t)(lane >> 5) * (uint32_t)p.k_st * 2 + 16 * (lane & 31);
   const uint32_t voff = (uint32_t)(lane >> 5) * (uint32_t)p.v_st * 2 + 16 * (lane & 31);
-  for (int t = 0; t < kPrefetch && t < n_kt; ++t) {
+  for (int t = 0; t < PF && t < n_kt; ++t) {
     issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kKeysPerTile, kv_end, lds + t * kStageLds, wave, koff, voff);
   }
 
@@ -404,13 +416,13 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   int stage = 0;
   auto stream_step = [&](int t) {
     // tile t landed for this wavefront once only the tiles issued after it remain in flight
-    wait_tiles_in_flight<W>(min(kPrefetch - 1, n_kt - 1 - t));
+    wait_tiles_in_flight<W>(min(PF - 1, n_kt - 1 - t));
     // ... and for everyone; everyone is done with tile t - 2, whose stage is refilled next
     __builtin_amdgcn_s_barrier();
-    if (t + kPrefetch < n_kt) {
-      int st2 = stage + kPrefetch;
+    if (t + PF < n_kt) {
+      int st2 = stage + PF;
       if (st2 >= kStages) st2 -= kStages;
-      issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + kPrefetch) * kKeysPerTile, kv_end, lds + st2 * kStageLds,
+      issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + PF) * kKeysPerTile, kv_end, lds + st2 * kStageLds,
                  wave, koff, voff);
     }
     const uint32_t sb = lds0 + stage * kStageLds;
@@ -621,6 +633,19 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     }
     rescale(o1, a1, f1);
     pv(sprev, pc0, pc1, o1);
+  } else if (!TWO && !LAG) {
+    for (int t = 0; t < n_kt; ++t) {
+      const uint32_t sb = stream_step(t);
+      const int jb = kv_lo + t * kKeysPerTile;
+      u32x4 pa0, pa1;
+      float a0;
+      f32x16 s0 = scores(sb, q0);
+      mask_scores(s0, jb, lim0, mrow0);
+      const bool f0 = stats(s0, m0, a0);
+      rescale(o0, a0, f0);
+      weights(s0, m0, a0, l0, pa0, pa1);
+      pv(sb, pa0, pa1, o0);
+    }
   } else if (!TWO && n_kt > 0) {
     u32x4 pa0, pa1;
     float a0;
