@@ -1,25 +1,28 @@
 // Main pass of gated causal GQA attention at head_dim 256 for gfx950 (CDNA4).
 //
-// One workgroup = one (batch b, KV head g, KV split s, tile of 8 x 32 (head, row) pairs of
-// that group).  The group's K and V are streamed through LDS in 32-key tiles and all eight
-// wavefronts reuse every tile, so K/V is read once per group per split.  Tiles move from
-// HBM to LDS with direct buffer->LDS loads (no registers, no VALU) into a ring of four
-// stages: two tiles are in flight while one is consumed.
+// One workgroup = one (batch b, KV head g, KV split s, tile of (head, row) pairs of that
+// group), one workgroup per CU.  Three shapes: eight wavefronts of one 32-pair column block
+// (prompts and long verify blocks: two wavefronts per SIMD), four wavefronts of one block
+// (short decode / verify, whose KV group fits in four blocks) and four of two blocks.  The
+// group's K and V are streamed through LDS in 32-key tiles and every wavefront reuses every
+// tile, so K/V is read once per group per split.  Tiles move from HBM to LDS with direct
+// buffer->LDS loads (no registers, no VALU) into a ring of four stages.
 //
-// Per wavefront, 32 (head, row) pairs are the N dimension of v_mfma_f32_32x32x16 (bf16 or
+// Per column block, 32 (head, row) pairs are the N dimension of v_mfma_f32_32x32x16 (bf16 or
 // fp16 in, fp32 accumulate):
 //
-//   S^T[key, pair]  = K[key, :] . Q[pair, :]          A = K tile (LDS), B = Q (registers)
+//   S^T[key, pair]  = K[key, :] . Q[pair, :]          A = K tile (LDS), B = Q (VGPRs)
 //   O^T[dim, pair] += V^T[dim, key] . P^T[key, pair]  A = V tile (LDS, transposing read), B = P
 //
 // With keys (and dims) on the MFMA rows and pairs on its columns, every lane owns one pair
-// (lane % 32) in both products: the online softmax needs no cross-lane traffic except one
-// exchange with the lane 32 away, and the S accumulator, packed to 16 bits, is already the
-// B operand of the second product.  The k-slots of that product follow the rows of the S
-// accumulator: slot 4a + t of lane half h is row 8a + 4h + t (+16 for the second MFMA); the
-// A operand is gathered in that order by ds_read_b64_tr_b16, which hands each lane of a
-// 16-lane group one column of a 4 x 16 block of 16-bit values (4 rows x 16 dims) that the
-// group reads as rows.
+// (lane % 32) of a block in both products: the online softmax needs no cross-lane traffic
+// except an exchange with the lane 32 away, and the S accumulator, packed to 16 bits, is
+// already the B operand of the second product.  The k-slots of that product follow the rows
+// of the S accumulator: slot 4a + t of lane half h is row 8a + 4h + t (+16 for the second
+// MFMA); the A operand is gathered in that order by ds_read_b64_tr_b16, which hands each lane
+// of a 16-lane group one column of a 4 x 16 block of 16-bit values (4 rows x 16 dims) that the
+// group reads as rows.  O lives in the accumulation registers (AGPRs) for the whole pass;
+// Q, S and everything the VALU touches stay in VGPRs.
 //
 // LDS layout of a 32-key x 256-dim tile: sixteen groups of two whole key rows (1 KiB, the
 // unit one direct load of a wavefront fills from 1 KiB of contiguous memory), group i at
@@ -29,15 +32,22 @@
 // transposing V reads (4 rows x 2 cells per 16 lanes) hit distinct banks.  Every LDS address
 // is a per-lane base plus a compile-time offset.
 //
+// Schedule.  On the prompt shapes the P.V product of tile t - 1 runs on the matrix cores while
+// the VALU turns tile t's scores into weights (the previous tile stays in its stage: two tiles
+// in flight); on the short-decode shape, which streams keys from HBM and has little to
+// compute, P.V follows its softmax directly and three tiles are in flight.
+//
 // The softmax is the online (flash) form of the plain definition: per pair a running max m
 // (log2 units of the scaled score), a running sum l and the accumulator O, rescaled by
-// exp2(m_old - m_new) when m moves.  m moves only when the new maximum exceeds it by more
-// than 8 (a factor 256), so weights stay below 2^8 and most rescales are skipped; the
-// decision is per pair, so a pair's arithmetic does not depend on which other pairs share
-// its wavefront (head-chunked and unchunked launches agree bit for bit).  Weights are
-// rounded to the 16-bit type once and both l and P.V use the rounded values.  With one
-// split the epilogue applies 1/l and the gate sigmoid and rounds once to 16 bits; with
-// several it writes the normalised partial o and its natural log-sum-exp for the merge.
+// exp2(m_old - m_new) just before the P.V product that follows a move of m.  m moves only
+// when the new maximum exceeds it by more than 8 (a factor 256), so weights stay below 2^8 and
+// most rescales are skipped; each lane first compares its half of the pair's keys and the two
+// halves are exchanged only when some lane of the wavefront sees such a maximum.  Every
+// decision is per pair, so a pair's arithmetic does not depend on which other pairs share its
+// wavefront (head-chunked and unchunked launches agree bit for bit).  Weights are rounded to
+// the 16-bit type once and both l and P.V use the rounded values.  With one split the epilogue
+// applies 1/l and the gate sigmoid and rounds once to 16 bits; with several it writes the
+// normalised partial o and its natural log-sum-exp for the merge.
 //
 // Operation: TensorFold PR #1009, attention kernel-contract commit (float64 gated GQA
 // attention as the reference, decode chunks and their merge); "Qwen head-chunked SDPA
