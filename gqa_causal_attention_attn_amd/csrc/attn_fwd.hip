@@ -258,6 +258,42 @@ __device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t
   }
 }
 
+// The same loads, prepared once per tile (resources and stage address in scalar registers)
+// and issued one at a time: load i < G is K group i of this wavefront, load G + i its V group.
+// The main pass spreads them between the MFMAs of a tile's scores, in the shadow of the
+// matrix cores, instead of issuing them in one burst.
+template <int W>
+struct TileDma {
+  static constexpr int kGroups = 16 / W;
+  static constexpr int kLoads = 2 * kGroups;
+  __amdgpu_buffer_rsrc_t kr, vr;
+  uint8_t* g0;
+  uint32_t koff, voff, kst, vst;
+
+  __device__ __forceinline__ void prep(const uint16_t* kbase, const uint16_t* vbase, int64_t k_st, int64_t v_st,
+                                       int j0, int kv_end, uint8_t* stage, int wave) {
+    const int j = j0 + 2 * kGroups * wave;
+    const int rows = min(max(kv_end - j, 0), 2 * kGroups);
+    const int kbytes = rows ? (rows - 1) * (int)k_st * 2 + kHeadDim * 2 : 0;
+    const int vbytes = rows ? (rows - 1) * (int)v_st * 2 + kHeadDim * 2 : 0;
+    kr = buffer_rsrc(kbase + (int64_t)j * k_st, kbytes);
+    vr = buffer_rsrc(vbase + (int64_t)j * v_st, vbytes);
+    g0 = stage + (kGroups * wave) * kGroupStride;
+  }
+
+  template <int I>
+  __device__ __forceinline__ void issue() const {
+    if constexpr (I < kGroups) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(g0 + I * kGroupStride), 16, koff + 4 * I * kst, 0, 0,
+                                               0);
+    } else {
+      constexpr int e = I - kGroups;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(g0 + kTileLds + e * kGroupStride), 16,
+                                               voff + 4 * e * vst, 0, 0, 0);
+    }
+  }
+};
+
 // One ds_read_b128 at a per-lane LDS byte address plus an immediate offset (inline assembly:
 // the compiler neither tracks it nor waits for it; see lgkm_wait1).
 template <int OFF>
@@ -285,6 +321,22 @@ __device__ __forceinline__ void wait_tiles_in_flight(int n_tiles) {
     if constexpr (W == 4) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   }
+}
+
+// This lane's index, read afresh each time (volatile): a per-lane address derived from it is
+// recomputed where it is used instead of occupying a register across the whole tile loop.
+__device__ __forceinline__ uint32_t lane_fresh() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// LDS byte offset (from a stage) of lane l's transposing V reads: lane 16 g16 + 4 t + u reads
+// MFMA row 4 hf + t (+8 a, +16 m) and dims 32 db + 16 (g16 % 2) + 4 u .. + 3, where a, m and
+// db are immediates
+__device__ __forceinline__ uint32_t v_lane_of(uint32_t l) {
+  const uint32_t g16 = l >> 4, tq = (l >> 2) & 3, uq = l & 3, hf = l >> 5;
+  return kTileLds + (4 * tq + hf) * kGroupStride + 16 * (2 * (g16 & 1) + (uq >> 1)) + 8 * (uq & 1);
 }
 
 // Key (within the tile, less 2 hf) of element q of the S accumulator: row 8 (q / 4) + 4 hf +
@@ -391,7 +443,10 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q is in registers before the tile stream starts
   const uint32_t koff = (uint32_t)(lane >> 5) * (uint32_t)p.k_st * 2 + 16 * (lane & 31);
   const uint32_t voff = (uint32_t)(lane >> 5) * (uint32_t)p.v_st * 2 + 16 * (lane & 31);
-  for (int t = 0; t < PF && t < n_kt; ++t) {
+  // the 8-wavefront shape issues every step's loads, past the last tile too (those read
+  // nothing), so its waits need no tail cases; the others stop at the last tile
+  constexpr bool EARLY = LAG && !TWO;
+  for (int t = 0; t < PF && (EARLY || t < n_kt); ++t) {
     issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kKeysPerTile, kv_end, lds + t * kStageLds, wave, koff, voff);
   }
 
@@ -401,10 +456,6 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)lds;
   const int li16 = li & 15;
   const uint32_t k_lane = (4 * (li16 & 3) + (li16 >> 2)) * kGroupStride + (li >> 4) * 512 + hf * 16;
-  // transposing V reads: lane 16 g16 + 4 t + u reads MFMA row 4 hf + t (+8 a, +16 m) and dims
-  // 32 db + 16 (g16 % 2) + 4 u .. + 3; a, m and db are immediates
-  const int g16 = lane >> 4, tq = (lane >> 2) & 3, uq = lane & 3;
-  const uint32_t v_lane = kTileLds + (4 * tq + hf) * kGroupStride + 16 * (2 * (g16 & 1) + (uq >> 1)) + 8 * (uq & 1);
 
   // the accumulators live in the accumulation registers (AGPRs), everything the VALU touches
   // every tile in VGPRs
@@ -440,15 +491,45 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     return sb;
   };
 
+  // The 8-wavefront stream: after the barrier of tile t the loads of tile t + PF are prepared,
+  // and the S product of tile t issues them one by one between its MFMAs.  Exactly one tile is
+  // in flight beyond the one consumed at every wait.
+  TileDma<W> dma;
+  dma.koff = koff, dma.voff = voff, dma.kst = (uint32_t)p.k_st, dma.vst = (uint32_t)p.v_st;
+  auto sync_step = [&](int t) {
+    wait_tiles_in_flight<W>(1);
+    __builtin_amdgcn_s_barrier();
+    int st2 = stage + PF;
+    if (st2 >= kStages) st2 -= kStages;
+    dma.prep(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + PF) * kKeysPerTile, kv_end, lds + st2 * kStageLds, wave);
+    const uint32_t sb = lds0 + stage * kStageLds;
+    stage = stage + 1 == kStages ? 0 : stage + 1;
+    return sb;
+  };
+  auto dma_hook = [&](auto kkc) {
+    constexpr int kk = decltype(kkc)::value;
+    constexpr int every = 16 / TileDma<W>::kLoads;
+    if constexpr (kk % every == 1 % every) dma.template issue<kk / every>();
+  };
+  auto no_hook = [](auto) {};
+
   if (!act0 && !act1) {
     // a wavefront without pairs only helps stream the tiles
-    for (int t = 0; t < n_kt; ++t) stream_step(t);
+    if constexpr (EARLY) {
+      for (int t = 0; t < n_kt; ++t) {
+        sync_step(t);
+        static_for<TileDma<W>::kLoads>([&](auto ic) { dma.template issue<decltype(ic)::value>(); });
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      for (int t = 0; t < n_kt; ++t) stream_step(t);
+    }
     return;
   }
 
   // ---- S^T block of the tile at sb: rows = its 32 keys, columns = the 32 pairs of block q;
   // K operands read two steps ahead
-  auto scores = [&](uint32_t sb, const u32x4(&q)[16]) {
+  auto scores = [&](uint32_t sb, const u32x4(&q)[16], auto&& hook) {
     f32x16 sc;
     const uint32_t kaddr = sb + k_lane;
     constexpr int kAhead = 2;  // K operands in flight beyond the one consumed
@@ -463,6 +544,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       constexpr int issued = kk + kAhead + 1 < 16 ? kk + kAhead + 1 : 16;
       lgkm_wait1<issued - kk - 1>(kop[kk % (kAhead + 1)]);
       mfma32_v<DT, kk == 0>(sc, kop[kk % (kAhead + 1)], q[kk]);
+      hook(kkc);
     });
     acc_settle_v(sc);
     return sc;
@@ -496,7 +578,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   auto mask_scores = [&](f32x16& sc, int jb, int lim, int64_t mrow) {
     if constexpr (MK == 0) {
       if (jb + kKeysPerTile > lim_min) {  // wave-uniform
-        const int jl = jb + 2 * hf;
+        const int jl = jb + 2 * (int)(lane_fresh() >> 5);  // recomputed: not held across the loop
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           if (jl + key_of(q) >= lim) sc[q] = -INFINITY;
@@ -572,7 +654,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // ---- O^T += V^T P^T over the 8 dim blocks of the tile at sb; the V operands of block
   // db + 1 are read while the two MFMAs of block db run
   auto pv = [&](uint32_t sb, const u32x4& pb0, const u32x4& pb1, f32x16(&o)[8]) {
-    const uint32_t va = sb + v_lane;
+    const uint32_t va = sb + v_lane_of(lane_fresh());
     u32x4 va4[2][2];
     auto read_v = [&](auto dbc, u32x4(&dst)[2]) {
       constexpr int db = decltype(dbc)::value;
@@ -649,7 +731,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       const int jb = kv_lo + t * kKeysPerTile;
       u32x4 pa0, pa1;
       float a0;
-      f32x16 s0 = scores(sb, q0);
+      f32x16 s0 = scores(sb, q0, no_hook);
       mask_scores(s0, jb, lim0, mrow0);
       const bool f0 = stats(s0, m0, a0);
       rescale(o0, a0, f0);
@@ -660,17 +742,17 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     u32x4 pa0, pa1;
     float a0;
     bool f0;
-    uint32_t sb = stream_step(0);
-    f32x16 s0 = scores(sb, q0);
+    uint32_t sb = sync_step(0);
+    f32x16 s0 = scores(sb, q0, dma_hook);
     mask_scores(s0, kv_lo, lim0, mrow0);
     f0 = stats(s0, m0, a0);
     weights(s0, m0, a0, l0, pa0, pa1);
     uint32_t sprev = sb;
     for (int t = 1; t < n_kt; ++t) {
-      sb = stream_step(t);
+      sb = sync_step(t);
       const int jb = kv_lo + t * kKeysPerTile;
       __builtin_amdgcn_sched_barrier(0);
-      s0 = scores(sb, q0);
+      s0 = scores(sb, q0, dma_hook);
       mask_scores(s0, jb, lim0, mrow0);
       // o still owes tile t - 1's alpha: keep it until its P.V is issued
       const float a_prev = a0;
@@ -685,6 +767,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     rescale(o0, a0, f0);
     pv(sprev, pa0, pa1, o0);
   }
+  // the loads past the last tile have landed before the workgroup's LDS is given up
+  if constexpr (EARLY) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: element q of o*[db] is dim 32 db + 8 (q / 4) + 4 hf + (q % 4)
   const float lt0 = sum_halves(l0), lt1 = sum_halves(l1);
