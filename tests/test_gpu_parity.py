@@ -110,6 +110,28 @@ def test_decode_27b_shape(rows):
 
 
 @needs_gpu
+@pytest.mark.parametrize("kv_len,n_splits", [
+    (1, 0), (31, 1), (33, 1), (97, 1),   # one to four tiles
+    (4000, 1), (4064, 1),                # one split: a ragged and a whole last tile
+    (4000, 0), (4000, 7),                # several splits + merge
+])
+def test_decode_short_and_split_caches(kv_len, n_splits):
+    # one 32-pair block per KV group (8 heads x 1 row) against caches shorter than a tile, one
+    # split of many tiles and several splits with the merge
+    _say("decode caches", kv_len, n_splits)
+    B, Hq, Hkv, rows = 1, 16, 2, 1
+    qb, kb, vb, gb, _ = _decode_case(3000 + kv_len, B=B, Hq=Hq, Hkv=Hkv, offset=kv_len - rows, rows=rows)
+    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    out = ga.decode(q, k, v, g, kv_offset=kv_len - rows, n_splits=n_splits)
+    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=kv_len - rows,
+                              kv_len=kv_len)
+    _say(assert_close(to_f64(out), ref, "decode"))
+    # head chunks of 3 heads: the same bits
+    chunked = ga.decode(q, k, v, g, kv_offset=kv_len - rows, n_splits=n_splits, head_chunk=3)
+    assert torch.equal(chunked.view(torch.int16), out.view(torch.int16))
+
+
+@needs_gpu
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("offset", [4097, 32768])
 @pytest.mark.parametrize("rows", [1, 4, 5, 9, 17, 32])
