@@ -26,6 +26,7 @@ struct Plan {
   int chunk_sizes[ATTN_MAX_CHUNKS];
   int blocks_per_chunk;
   int shape;  // 0: 4 wavefronts x 1 column block, 1: 4 x 2, 2: 8 x 1
+  int mask_lds;  // the main pass stages each tile's mask rows in LDS
   int waves;  // wavefronts per workgroup
   int nb;     // column blocks per wavefront
   int n_tiles;
@@ -140,6 +141,37 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   S = cdiv(n_kt, tps);
   P->n_splits = (int)S;
   P->keys_per_split = (int)(tps * kKeysPerTile);
+  // Mask rows in LDS: the mask is the same for every head, 16-byte aligned with rows of a whole
+  // number of 16-byte chunks up to kv_len (the direct loads move 16-byte chunks and a chunk that
+  // reaches past the mask's last word would read as zeros), spans < 2 GiB, and every
+  // workgroup's (head, row) pairs cover at most kMaskStageLds / (32 x word size) rows.
+  if (a->mask.kind != ATTN_MASK_NONE && P->shape != 1) {
+    const attn_mask& m = a->mask;
+    const int64_t esz = m.kind == ATTN_MASK_BOOL_U8 ? 1 : m.kind == ATTN_MASK_ADD ? 2 : 4;
+    const int64_t msb = m.Bm == 1 ? 0 : m.stride_b;
+    const int64_t span = ((int64_t)(m.Bm - 1) * msb + (int64_t)(a->rows - 1) * m.stride_row + a->kv_len) * esz;
+    bool ok = m.Hm == 1 && ((uintptr_t)m.ptr % 16) == 0 && (m.stride_row * esz) % 16 == 0 && (msb * esz) % 16 == 0 &&
+              ((int64_t)a->kv_len * esz) % 16 == 0 && span < ((int64_t)1 << 31);
+    const int64_t max_rows = gqa::kMaskStageLds / (gqa::kKeysPerTile * esz);
+    const int wg_blocks = P->waves * P->nb;
+    for (int t = 0; ok && t < P->n_tiles; ++t) {
+      int64_t lo = INT64_MAX, hi = -1;
+      for (int bj = t * wg_blocks; bj < (t + 1) * wg_blocks; ++bj) {
+        const int cj = bj / P->blocks_per_chunk;
+        const int64_t f0 = (int64_t)(bj - cj * P->blocks_per_chunk) * kPairsPerBlock;
+        const int hs = cj * P->chunk;
+        if (hs >= G) continue;
+        const int csj = P->chunk < G - hs ? P->chunk : G - hs;
+        const int64_t npairs = (int64_t)csj * a->rows;
+        if (f0 >= npairs) continue;
+        const int64_t last = (f0 + kPairsPerBlock < npairs ? f0 + kPairsPerBlock : npairs) - 1;
+        lo = f0 / csj < lo ? f0 / csj : lo;
+        hi = last / csj > hi ? last / csj : hi;
+      }
+      if (hi >= 0 && hi - lo >= max_rows) ok = false;
+    }
+    P->mask_lds = ok ? 1 : 0;
+  }
   P->grid = (int64_t)a->B * a->Hkv * S * P->n_tiles;
   if (P->grid > INT32_MAX) return ATTN_E_ARG;
   if ((int64_t)a->B * a->Hq * a->rows > (int64_t)INT32_MAX) return ATTN_E_ARG;  // the merge indexes rows in 32 bits
@@ -151,7 +183,9 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   return ATTN_OK;
 }
 
-inline int variant_of(const attn_args* a, int shape) { return (shape << 3) | (a->dtype << 2) | a->mask.kind; }
+inline int variant_of(const attn_args* a, const Plan& P) {
+  return (P.mask_lds << 5) | (P.shape << 3) | (a->dtype << 2) | a->mask.kind;
+}
 
 int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream) {
   int st = validate(a, op);
@@ -179,6 +213,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream)
     p.m_sb = a->mask.Bm == 1 ? 0 : a->mask.stride_b;  // an extent of 1 broadcasts
     p.m_sh = a->mask.Hm == 1 ? 0 : a->mask.stride_h;
     p.m_sr = a->mask.stride_row;
+    p.mask_lds = P.mask_lds;
   }
   p.kv_offset = (int)a->kv_offset;
   p.kv_len = (int)a->kv_len;
@@ -248,14 +283,17 @@ const char* attn_strerror(int status) {
 }
 
 const char* attn_variant_name(int variant) {
-  // id = shape * 8 + dtype * 4 + mask kind
+  // id = mask rows in LDS * 32 + shape * 8 + dtype * 4 + mask kind
 #define GQA_NAMES(SHAPE)                                                                                        \
   "fwd_mfma32x32x16_bf16_" SHAPE, "fwd_mfma32x32x16_bf16_maskbool_" SHAPE, "fwd_mfma32x32x16_bf16_maskadd_" SHAPE, \
       "fwd_mfma32x32x16_bf16_maskf32_" SHAPE, "fwd_mfma32x32x16_f16_" SHAPE, "fwd_mfma32x32x16_f16_maskbool_" SHAPE, \
       "fwd_mfma32x32x16_f16_maskadd_" SHAPE, "fwd_mfma32x32x16_f16_maskf32_" SHAPE
-  static const char* const names[24] = {GQA_NAMES("4x1"), GQA_NAMES("4x2"), GQA_NAMES("8x1")};
+  static const char* const names[64] = {
+      GQA_NAMES("4x1"),           GQA_NAMES("4x2"),           GQA_NAMES("8x1"),           GQA_NAMES("unused"),
+      GQA_NAMES("4x1_ldsmask"),   GQA_NAMES("unused"),        GQA_NAMES("8x1_ldsmask"),   GQA_NAMES("unused")};
 #undef GQA_NAMES
-  return (variant >= 0 && variant < 24) ? names[variant] : "unknown";
+  static const bool used[8] = {true, true, true, false, true, false, true, false};  // shape groups
+  return (variant >= 0 && variant < 64 && used[variant >> 3]) ? names[variant] : "unknown";
 }
 
 int attn_head_chunk_plan(int rows, int n_q_heads, int n_kv_heads, int enabled, int* sizes, int cap, int* n_chunks) {
@@ -288,7 +326,7 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
   if (st) return st;
   memset(info, 0, sizeof(*info));
   info->op = op;
-  info->variant = variant_of(a, P.shape);
+  info->variant = variant_of(a, P);
   info->group_size = P.G;
   info->n_head_chunks = P.n_chunks;
   info->head_chunk = P.chunk;

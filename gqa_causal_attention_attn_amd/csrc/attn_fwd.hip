@@ -209,16 +209,30 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-// Additive mask term of key j for this lane's (b, h, r), in log2 units (-inf hides the key).
+// Additive term of a mask word (the u8 flag, the 16-bit value or the fp32 bits), in log2
+// units (-inf hides the key).
+template <int DT, int MK>
+__device__ __forceinline__ float mask_term_of(uint32_t w) {
+  if constexpr (MK == 1) {
+    return w ? 0.0f : -INFINITY;
+  } else if constexpr (MK == 2) {
+    return lo16<DT>(w) * kLog2e;
+  } else if constexpr (MK == 3) {
+    return __builtin_bit_cast(float, w) * kLog2e;
+  } else {
+    return 0.0f;
+  }
+}
+
+// The term of key j for this lane's (b, h, r), read from memory.
 template <int DT, int MK>
 __device__ __forceinline__ float mask_term(const void* base, int64_t row_off, int j) {
   if constexpr (MK == 1) {
-    return static_cast<const uint8_t*>(base)[row_off + j] ? 0.0f : -INFINITY;
+    return mask_term_of<DT, MK>(static_cast<const uint8_t*>(base)[row_off + j]);
   } else if constexpr (MK == 2) {
-    const uint16_t w = static_cast<const uint16_t*>(base)[row_off + j];
-    return lo16<DT>((uint32_t)w) * kLog2e;
+    return mask_term_of<DT, MK>(static_cast<const uint16_t*>(base)[row_off + j]);
   } else if constexpr (MK == 3) {
-    return static_cast<const float*>(base)[row_off + j] * kLog2e;
+    return mask_term_of<DT, MK>(__builtin_bit_cast(uint32_t, static_cast<const float*>(base)[row_off + j]));
   } else {
     return 0.0f;
   }
@@ -310,17 +324,23 @@ __device__ __forceinline__ void lgkm_wait1(u32x4& a) {
 
 // Wait until at most n_tiles (<= 2) tiles' direct loads of this wavefront are in flight; a
 // tile is 32 / W direct loads of each of the W wavefronts.
-template <int W>
-__device__ __forceinline__ void wait_tiles_in_flight(int n_tiles) {
+template <int W, int PLUS>
+__device__ __forceinline__ void wait_tiles_in_flight_n(int n_tiles) {
+  constexpr int kPerTile = 32 / W + PLUS;
   if (n_tiles == 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else if (n_tiles == 1) {
-    if constexpr (W == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(kPerTile) : "memory");
   } else {
-    if constexpr (W == 4) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * kPerTile) : "memory");
   }
+}
+
+// mask_loads: this wavefront also issues one direct load of mask rows per tile.
+template <int W>
+__device__ __forceinline__ void wait_tiles_in_flight(int n_tiles, bool mask_loads = false) {
+  if (mask_loads) wait_tiles_in_flight_n<W, 1>(n_tiles);
+  else wait_tiles_in_flight_n<W, 0>(n_tiles);
 }
 
 // This lane's index, read afresh each time (volatile): a per-lane address derived from it is
@@ -349,9 +369,10 @@ __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xo
 // x + (x of the lane 32 away), the same sum on both lanes
 __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
 
-template <int DT, int MK, int W, int NB>
+template <int DT, int MK, int W, int NB, bool ML = false>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) {
   static_assert((W == 4 && (NB == 1 || NB == 2)) || (W == 8 && NB == 1), "4 wavefronts of 1 or 2 blocks, or 8 of 1");
+  static_assert(!ML || (MK != 0 && NB == 1), "mask rows in LDS: masked one-block shapes");
   constexpr bool TWO = NB == 2;
   // Short decode / verify (four wavefronts of one block) streams keys from HBM and has little
   // to compute per tile: its P.V runs right after its softmax, which frees the previous tile's
@@ -363,7 +384,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   constexpr int kGroupBlocks = W * NB;  // column blocks of this workgroup
   // kStages stages of (K tile, V tile): kPrefetch tiles in flight while one is consumed and
   // the one before it finishes its P.V product.  Stage of tile t: t % kStages.
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kFwdLdsBytes];
+  // with the mask rows in LDS, kStages stages of them follow the K/V stages
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kFwdLdsBytes + (ML ? kStages * kMaskStageLds : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -406,7 +428,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
   // ---- key range of the workgroup [kv_lo, kv_end) and the smallest bound of its pairs, from
   // the pair layout of its column blocks (uniform arithmetic)
-  int kv_hi = 0, lim_min = 0x7fffffff;
+  int kv_hi = 0, lim_min = 0x7fffffff, r_lo = 0x7fffffff, r_hi = 0;
   for (int bj = tile * kGroupBlocks; bj < (tile + 1) * kGroupBlocks; ++bj) {
     const int cj = bj / p.blocks_per_chunk;
     const int f0 = (bj - cj * p.blocks_per_chunk) * kPairsPerBlock;
@@ -417,6 +439,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     if (f0 >= npairs) continue;
     kv_hi = max(kv_hi, lim_of((min(f0 + kPairsPerBlock, npairs) - 1) / csj));
     lim_min = min(lim_min, lim_of(f0 / csj));
+    r_lo = min(r_lo, f0 / csj);
+    r_hi = max(r_hi, (min(f0 + kPairsPerBlock, npairs) - 1) / csj);
   }
   const int kv_lo = split * p.keys_per_split;
   const int kv_end = __builtin_amdgcn_readfirstlane(min(kv_lo + p.keys_per_split, kv_hi));
@@ -425,6 +449,30 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
   const uint16_t* kbase = p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
   const uint16_t* vbase = p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
+
+  // ---- mask rows staged in LDS (ML: the mask is the same for every head and the rows r_lo ..
+  // r_hi of every workgroup fit a mask stage, which the host checked): the 32-key window of
+  // those rows for each tile is loaded with the tile (wavefronts 0-3 load 1 KiB each: stage byte
+  // 1024 w + 16 l is byte (1024 w + 16 l) % kMaskRowBytes of window row (1024 w + 16 l) /
+  // kMaskRowBytes), and a lane reads its words from LDS.  Otherwise each lane loads its words
+  // from memory.
+  constexpr int kMaskEsz = MK == 1 ? 1 : MK == 2 ? 2 : 4;
+  constexpr int kMaskRowBytes = kKeysPerTile * kMaskEsz;
+  constexpr int kMaskRows = kMaskStageLds / kMaskRowBytes;
+  constexpr bool mlds = ML;
+  const bool mwave = ML && wave < 4;  // this wavefront issues a mask load per tile
+  const int mbytes = mlds ? (int)(((int64_t)(p.rows - 1) * p.m_sr + p.kv_len) * kMaskEsz) : 0;
+  const __amdgpu_buffer_rsrc_t mrs =
+      buffer_rsrc(static_cast<const uint8_t*>(p.mask) + (mlds ? (int64_t)b * p.m_sb * kMaskEsz : 0), mbytes);
+  const uint32_t mpos = (uint32_t)(wave * 1024 + lane * 16);
+  const uint32_t mvoff =
+      mlds ? (uint32_t)(r_lo + mpos / kMaskRowBytes) * (uint32_t)p.m_sr * kMaskEsz + mpos % kMaskRowBytes : 0u;
+  auto issue_mask = [&](int j0, int st) {
+    if (mwave) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(mrs, (lds_void*)(lds + kFwdLdsBytes + st * kMaskStageLds + wave * 1024),
+                                               16, mvoff + (uint32_t)j0 * kMaskEsz, 0, 0, 0);
+    }
+  };
 
   // ---- Q of this lane's pairs, in the B-operand order: element t of q*[kk] is dim
   // 16 kk + 8 hf + t
@@ -447,6 +495,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // nothing), so its waits need no tail cases; the others stop at the last tile
   constexpr bool EARLY = LAG && !TWO;
   for (int t = 0; t < PF && (EARLY || t < n_kt); ++t) {
+    issue_mask(kv_lo + t * kKeysPerTile, t);
     issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kKeysPerTile, kv_end, lds + t * kStageLds, wave, koff, voff);
   }
 
@@ -477,12 +526,13 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   int stage = 0;
   auto stream_step = [&](int t) {
     // tile t landed for this wavefront once only the tiles issued after it remain in flight
-    wait_tiles_in_flight<W>(min(PF - 1, n_kt - 1 - t));
+    wait_tiles_in_flight<W>(min(PF - 1, n_kt - 1 - t), mwave);
     // ... and for everyone; everyone is done with tile t - 2, whose stage is refilled next
     __builtin_amdgcn_s_barrier();
     if (t + PF < n_kt) {
       int st2 = stage + PF;
       if (st2 >= kStages) st2 -= kStages;
+      issue_mask(kv_lo + (t + PF) * kKeysPerTile, st2);
       issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + PF) * kKeysPerTile, kv_end, lds + st2 * kStageLds,
                  wave, koff, voff);
     }
@@ -497,10 +547,11 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   TileDma<W> dma;
   dma.koff = koff, dma.voff = voff, dma.kst = (uint32_t)p.k_st, dma.vst = (uint32_t)p.v_st;
   auto sync_step = [&](int t) {
-    wait_tiles_in_flight<W>(1);
+    wait_tiles_in_flight<W>(1, mwave);
     __builtin_amdgcn_s_barrier();
     int st2 = stage + PF;
     if (st2 >= kStages) st2 -= kStages;
+    issue_mask(kv_lo + (t + PF) * kKeysPerTile, st2);
     dma.prep(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + PF) * kKeysPerTile, kv_end, lds + st2 * kStageLds, wave);
     const uint32_t sb = lds0 + stage * kStageLds;
     stage = stage + 1 == kStages ? 0 : stage + 1;
@@ -591,6 +642,41 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
         sc[q] = j < lim ? sc[q] * p.scale_log2 + mask_term<DT, MK>(p.mask, mrow, j) : -INFINITY;
       }
     }
+  };
+
+  // The same with the tile's mask window in LDS (the stage of K/V stage address sb): the words
+  // of keys q and q + 8 are adjacent, one read each.
+  auto mask_lds_apply = [&](f32x16& sc, int jb, int lim, uint32_t sb) {
+    if constexpr (MK != 0) {
+      const int rho = min(max(r0 - r_lo, 0), kMaskRows - 1);
+      const uint32_t mst = lds0 + kFwdLdsBytes + ((sb - lds0) / kStageLds) * kMaskStageLds;
+      const lds_u8* row = reinterpret_cast<const lds_u8*>((uintptr_t)(mst + rho * kMaskRowBytes + 2 * hf * kMaskEsz));
+      auto apply = [&](int q, uint32_t w) {
+        const int j = jb + key_of(q) + 2 * hf;
+        sc[q] = j < lim ? sc[q] * p.scale_log2 + mask_term_of<DT, MK>(w) : -INFINITY;
+      };
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const lds_u8* at = row + key_of(q) * kMaskEsz;
+        if constexpr (MK == 1) {
+          const uint16_t x = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(at);
+          apply(q, x & 0xffu);
+          apply(q + 8, x >> 8);
+        } else if constexpr (MK == 2) {
+          const uint32_t x = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(at);
+          apply(q, x & 0xffffu);
+          apply(q + 8, x >> 16);
+        } else {
+          const u32x2 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(at);
+          apply(q, x[0]);
+          apply(q + 8, x[1]);
+        }
+      }
+    }
+  };
+  auto mask_any = [&](f32x16& sc, int jb, int lim, int64_t mrow, uint32_t sb) {
+    if constexpr (ML) mask_lds_apply(sc, jb, lim, sb);
+    else mask_scores(sc, jb, lim, mrow);
   };
 
   // ---- online softmax of one block, in two parts.  stats: the new running max of each
@@ -732,7 +818,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       u32x4 pa0, pa1;
       float a0;
       f32x16 s0 = scores(sb, q0, no_hook);
-      mask_scores(s0, jb, lim0, mrow0);
+      mask_any(s0, jb, lim0, mrow0, sb);
       const bool f0 = stats(s0, m0, a0);
       rescale(o0, a0, f0);
       weights(s0, m0, a0, l0, pa0, pa1);
@@ -744,7 +830,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     bool f0;
     uint32_t sb = sync_step(0);
     f32x16 s0 = scores(sb, q0, dma_hook);
-    mask_scores(s0, kv_lo, lim0, mrow0);
+    mask_any(s0, kv_lo, lim0, mrow0, sb);
     f0 = stats(s0, m0, a0);
     weights(s0, m0, a0, l0, pa0, pa1);
     uint32_t sprev = sb;
@@ -753,7 +839,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       const int jb = kv_lo + t * kKeysPerTile;
       __builtin_amdgcn_sched_barrier(0);
       s0 = scores(sb, q0, dma_hook);
-      mask_scores(s0, jb, lim0, mrow0);
+      mask_any(s0, jb, lim0, mrow0, sb);
       // o still owes tile t - 1's alpha: keep it until its P.V is issued
       const float a_prev = a0;
       const bool f_prev = f0;
@@ -820,6 +906,13 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
 template <int DT, int MK>
 hipError_t launch_fwd_t(const FwdParams& p, int shape, hipStream_t stream) {
+  if constexpr (MK != 0) {
+    if (p.mask_lds && shape != 1) {
+      if (shape == 0) hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 1, true>), dim3(p.grid), dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, 1, true>), dim3(p.grid), dim3(512), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   switch (shape) {
     case 0: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 1>), dim3(p.grid), dim3(256), 0, stream, p); break;
     case 1: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 2>), dim3(p.grid), dim3(256), 0, stream, p); break;

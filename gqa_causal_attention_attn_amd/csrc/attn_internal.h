@@ -19,6 +19,7 @@ constexpr int kStages = 4;                                   // LDS stages of (K
 constexpr int kPrefetch = 2;                                 // tiles in flight ahead of the one consumed
 constexpr int kFwdLdsBytes = kStages * kStageLds;            // 133,120 B
 constexpr int kTargetBlocks = 256;   // main-pass workgroups aimed for (one per CU)
+constexpr int kMaskStageLds = 4096;  // LDS bytes per stage for the mask rows of a tile (masked kernels)
 
 // Parameters of the main (flash / split-KV) pass.  Strides are in elements.
 struct FwdParams {
@@ -47,6 +48,8 @@ struct FwdParams {
   int n_splits;
   int keys_per_split;    // multiple of kKeysPerTile
   int grid;              // workgroups in the launch
+  int mask_lds;          // the mask is the same for every head, 16-byte aligned and < 2 GiB: its
+                         // tile rows may be staged in LDS with direct loads
 };
 
 struct MergeParams {

@@ -178,6 +178,60 @@ def test_verify_mask_kinds(kind):
     _say(assert_close(to_f64(out), ref, kind))
 
 
+def _strided_mask(m, row_stride):
+    """m ([Bm, Hm, rows, kv] on the GPU) copied into storage with the given row stride."""
+    Bm, Hm, rows, kv = m.shape
+    store = torch.zeros((Bm, Hm, rows, row_stride), dtype=m.dtype, device="cuda")
+    store[..., :kv] = m
+    return store[..., :kv]
+
+
+@needs_gpu
+@pytest.mark.parametrize("kind", ["bool", "add", "f32"])
+@pytest.mark.parametrize("rows,Bm", [(6, 1), (32, 1), (32, 2)])
+def test_mask_rows_in_lds(kind, rows, Bm):
+    # A head-broadcast mask with 16-byte aligned rows is staged in LDS with each K/V tile (rows 6:
+    # the four-wavefront shape; rows 32: eight wavefronts).  The same mask in storage whose row
+    # stride is not a multiple of 16 bytes takes the per-lane loads: both must give the same bits
+    # and match the oracle.  (A row that ends inside a 16-byte chunk also takes the per-lane
+    # loads: test_head_chunked_verify covers those lengths.)
+    _say("mask rows in LDS", kind, rows, Bm)
+    B, Hq, Hkv = 2, 16, 2
+    offset = 4112 - rows  # kv_len a multiple of 16 words: every row ends on a 16-byte chunk
+    kv = offset + rows
+    qb, kb, vb, gb, rng = _decode_case(600 + rows, B=B, Hq=Hq, Hkv=Hkv, offset=offset, rows=rows)
+    masks = [syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=1,
+                             kind={"bool": "bool", "add": "add", "f32": "add_f32"}[kind]) for _ in range(Bm)]
+    mb = np.concatenate(masks, axis=0)
+    if kind == "f32":
+        mb = np.where(np.isfinite(mb), np.random.default_rng(9).standard_normal(mb.shape).astype(np.float32), mb)
+    if kind == "add":
+        mdev = to_dev(mb)
+        mref, mk = syn.widen(mb), "add"
+    else:
+        mdev = torch.from_numpy(mb).cuda()
+        mref, mk = (mb.astype(bool), "bool") if kind == "bool" else (mb.astype(np.float64), "add")
+    esz = mdev.element_size()
+    odd = kv
+    while (odd * esz) % 16 == 0:
+        odd += 1
+    aligned = _strided_mask(mdev, (kv * esz + 63) // 64 * 64 // esz)
+    unaligned = _strided_mask(mdev, odd)
+    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    names = []
+    for m in (aligned, unaligned):
+        a = ga._args(q, k, v, g, torch.empty_like(q), kv_offset=offset, kv_len=kv, causal=True, scale=0.0,
+                     head_chunk=0, n_splits=0, mask=m)
+        names.append(ga.describe_plan(a, 1)["variant_name"])
+    assert "ldsmask" in names[0] and "ldsmask" not in names[1], names
+    out_a = ga.decode(q, k, v, g, kv_offset=offset, mask=aligned)
+    out_u = ga.decode(q, k, v, g, kv_offset=offset, mask=unaligned)
+    assert torch.equal(out_a.view(torch.int16), out_u.view(torch.int16))
+    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=offset,
+                              kv_len=kv, mask=mref, mask_kind=mk)
+    _say(assert_close(to_f64(out_a), ref, f"mask in LDS {kind}"))
+
+
 @needs_gpu
 def test_kv_append_is_bit_exact():
     nf = syn.nonfinite_bits("bf16")
