@@ -17,7 +17,7 @@ import torch
 from . import _abi
 
 __all__ = [
-    "AttnError", "lib", "prefill", "decode", "kv_append", "merge", "head_chunk_plan", "workspace_bytes",
+    "AttnError", "lib", "prefill", "decode", "kv_append", "kv_keep", "merge", "head_chunk_plan", "workspace_bytes",
     "describe_plan", "plan_args", "variant_name", "prompt_prefill",
 ]
 
@@ -164,6 +164,35 @@ def kv_append(k_new, v_new, k_cache, v_cache, *, kv_offset: int) -> None:
         raise ValueError("cache and new rows disagree on batch or KV heads")
     _check(lib().kv_append(C.byref(a), _stream_handle(k_new)))
 
+
+
+def kv_keep(k_cache, v_cache, *, kv_offset: int, rows: int, keep) -> None:
+    """kv_keep: in each batch entry, move the kept rows of the verify block at kv_offset (rows
+    rows) to kv_offset, kv_offset + 1, ... in row order, bit for bit.  keep[b] is a bitmask
+    (bit r = keep row r) or a sequence of row indices."""
+    masks = []
+    for k in keep:
+        if isinstance(k, int):
+            masks.append(k)
+        else:
+            m = 0
+            for r in k:
+                m |= 1 << int(r)
+            masks.append(m)
+    if len(masks) != k_cache.shape[0]:
+        raise ValueError("keep needs one entry per batch entry")
+    arr = (C.c_uint32 * max(1, len(masks)))(*[m & 0xFFFFFFFF for m in masks])
+    if any(m >> 32 for m in masks):
+        raise ValueError("keep bits past row 31")
+    a = _abi.KvKeepArgs()
+    a.dtype = _dtype_code(k_cache)
+    a.B, a.Hkv, a.D, a.rows = k_cache.shape[0], k_cache.shape[1], k_cache.shape[3], int(rows)
+    a.kv_offset, a.capacity = int(kv_offset), k_cache.shape[2]
+    a.keep = C.cast(arr, C.POINTER(C.c_uint32))
+    a.k_cache, a.v_cache = _t4(k_cache), _t4(v_cache)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache differ")
+    _check(lib().kv_keep(C.byref(a), _stream_handle(k_cache)))
 
 def merge(partial_o, partial_lse, gate, out=None):
     """attn_merge: partial_o [C, B, Hq, rows, 256] fp32, partial_lse [C, B, Hq, rows] fp32 (natural log)."""

@@ -7,7 +7,7 @@ The struct sizes are checked against the library's own (attn_struct_size) when i
 import ctypes as C
 import os
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 HEAD_DIM = 256
 MAX_DECODE_ROWS = 32
 MAX_CHUNKS = 64
@@ -27,7 +27,9 @@ OP_PREFILL, OP_DECODE = 0, 1
 EXPORTS = (
     "attn_abi_version", "attn_struct_size", "attn_strerror", "attn_variant_name", "attn_head_chunk_plan",
     "attn_workspace_bytes", "attn_describe_plan", "attn_prefill", "attn_decode", "kv_append", "attn_merge",
+    "kv_keep",
 )
+KEEP_MAX_BATCH = 64
 
 
 class Tensor(C.Structure):
@@ -51,6 +53,12 @@ class KvAppendArgs(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("B", C.c_int32), ("Hkv", C.c_int32), ("D", C.c_int32), ("rows", C.c_int32),
                 ("reserved", C.c_int32), ("kv_offset", C.c_int64), ("capacity", C.c_int64), ("k_new", Tensor),
                 ("v_new", Tensor), ("k_cache", Tensor), ("v_cache", Tensor)]
+
+
+class KvKeepArgs(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("B", C.c_int32), ("Hkv", C.c_int32), ("D", C.c_int32), ("rows", C.c_int32),
+                ("reserved", C.c_int32), ("kv_offset", C.c_int64), ("capacity", C.c_int64),
+                ("keep", C.POINTER(C.c_uint32)), ("k_cache", Tensor), ("v_cache", Tensor)]
 
 
 class MergeArgs(C.Structure):
@@ -99,9 +107,11 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.kv_append.argtypes = [P(KvAppendArgs), C.c_void_p]
     lib.attn_merge.restype = C.c_int
     lib.attn_merge.argtypes = [P(MergeArgs), C.c_void_p]
+    lib.kv_keep.restype = C.c_int
+    lib.kv_keep.argtypes = [P(KvKeepArgs), C.c_void_p]
     if lib.attn_abi_version() != ABI_VERSION:
         raise RuntimeError("libgqa_attn ABI version mismatch")
-    for i, st in enumerate((AttnArgs, KvAppendArgs, MergeArgs, PlanInfo)):
+    for i, st in enumerate((AttnArgs, KvAppendArgs, MergeArgs, PlanInfo, KvKeepArgs)):
         if lib.attn_struct_size(i) != C.sizeof(st):
             raise RuntimeError(f"struct {st.__name__} size mismatch: lib {lib.attn_struct_size(i)} vs {C.sizeof(st)}")
     return lib

@@ -257,6 +257,7 @@ size_t attn_struct_size(int which) {
   switch (which) {
     case 0: return sizeof(attn_args);
     case 1: return sizeof(kv_append_args);
+    case 4: return sizeof(kv_keep_args);
     case 2: return sizeof(merge_args);
     case 3: return sizeof(attn_plan_info);
     default: return 0;
@@ -375,6 +376,33 @@ int kv_append(const kv_append_args* a, void* stream) {
   }
   p.B = a->B, p.Hkv = a->Hkv, p.rows = a->rows, p.kv_offset = (int)a->kv_offset;
   if (gqa::launch_append(p, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
+}
+
+int kv_keep(const kv_keep_args* a, void* stream) {
+  if (!a || !a->keep) return ATTN_E_NULL;
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
+  if (a->B <= 0 || a->B > gqa::kKeepMaxBatch || a->Hkv <= 0) return ATTN_E_HEADS;
+  if ((int64_t)a->B * a->Hkv > INT32_MAX) return ATTN_E_HEADS;
+  if (a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
+  if (a->rows < 1 || a->rows > ATTN_MAX_DECODE_ROWS) return ATTN_E_ROWS;
+  if (a->kv_offset < 0 || a->capacity < 1 || a->kv_offset + a->rows > a->capacity || a->capacity > INT32_MAX)
+    return ATTN_E_KV;
+  for (int b = 0; b < a->B; ++b)
+    if (a->rows < 32 && (a->keep[b] >> a->rows) != 0u) return ATTN_E_ARG;
+  if (!a->k_cache.ptr || !a->v_cache.ptr) return ATTN_E_NULL;
+  if (!aligned16(a->k_cache.ptr) || !aligned16(a->v_cache.ptr) || !strides_ok(a->k_cache) || !strides_ok(a->v_cache))
+    return ATTN_E_LAYOUT;
+  gqa::KeepParams p;
+  memset(&p, 0, sizeof(p));
+  for (int t = 0; t < 2; ++t) {
+    const attn_tensor& c = t ? a->v_cache : a->k_cache;
+    p.cache[t] = static_cast<uint16_t*>(c.ptr);
+    p.c_sb[t] = c.stride_b, p.c_sh[t] = c.stride_h, p.c_st[t] = c.stride_row;
+  }
+  p.Hkv = a->Hkv, p.rows = a->rows, p.kv_offset = (int)a->kv_offset;
+  for (int b = 0; b < a->B; ++b) p.keep[b] = a->keep[b];
+  if (gqa::launch_keep(p, a->B, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
 }
 

@@ -211,7 +211,45 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   }
 }
 
+// kv_keep: one workgroup per (b, g).  Every kept row of the block is read into registers
+// (1024 16-byte chunks of K and 1024 of V at most: 8 per thread), the workgroup waits until all
+// reads have landed, and only then are the rows written to their new places (row r goes to
+// kv_offset + the number of kept rows below r <= r), so moving rows in place is safe.
+__global__ __launch_bounds__(256) void keep_kernel(const KeepParams p) {
+  constexpr int kChunks = kHeadDim / 8;                        // 16-byte chunks per row
+  constexpr int kPerThread = 2 * 32 * kChunks / 256;           // both tensors, 32 rows at most
+  const int b = blockIdx.x / p.Hkv, g = blockIdx.x % p.Hkv;
+  const uint32_t m = p.keep[b];
+  u32x4 val[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int u = threadIdx.x + 256 * k;
+    const int t = u / (32 * kChunks), r = (u / kChunks) % 32, c = u % kChunks;
+    if (r < p.rows && ((m >> r) & 1u)) {
+      val[k] = *reinterpret_cast<const u32x4*>(p.cache[t] + b * p.c_sb[t] + g * p.c_sh[t] +
+                                               (int64_t)(p.kv_offset + r) * p.c_st[t] + 8 * c);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every read of this (b, g) has landed ...
+  __syncthreads();                                   // ... in every thread, before any write
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int u = threadIdx.x + 256 * k;
+    const int t = u / (32 * kChunks), r = (u / kChunks) % 32, c = u % kChunks;
+    if (r < p.rows && ((m >> r) & 1u)) {
+      const int d = __builtin_popcount(m & ((1u << r) - 1u));
+      *reinterpret_cast<u32x4*>(p.cache[t] + b * p.c_sb[t] + g * p.c_sh[t] + (int64_t)(p.kv_offset + d) * p.c_st[t] +
+                                8 * c) = val[k];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_keep(const KeepParams& p, int B, hipStream_t stream) {
+  hipLaunchKernelGGL(keep_kernel, dim3((unsigned)(B * p.Hkv)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;

@@ -71,10 +71,20 @@ struct AppendParams {
   int kv_offset;
 };
 
+constexpr int kKeepMaxBatch = 64;  // keep masks travel in the kernel arguments
+
+struct KeepParams {
+  uint16_t* cache[2];       // K, V
+  int64_t c_sb[2], c_sh[2], c_st[2];
+  int Hkv, rows, kv_offset;
+  uint32_t keep[kKeepMaxBatch];
+};
+
 // Launchers (return hipGetLastError()).  dtype 0 = bf16, 1 = fp16; mask_kind as attn_mask_kind.
 // shape: 0 = 4 wavefronts x 1 column block, 1 = 4 x 2, 2 = 8 x 1 (wavefronts x blocks each)
 hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_keep(const KeepParams& p, int B, hipStream_t stream);
 
 }  // namespace gqa

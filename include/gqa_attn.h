@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GQA_ATTN_ABI_VERSION 1
+#define GQA_ATTN_ABI_VERSION 2
 #define ATTN_HEAD_DIM 256
 #define ATTN_MAX_DECODE_ROWS 32
 #define ATTN_MAX_CHUNKS 64
@@ -137,6 +137,28 @@ typedef struct {
   attn_tensor v_cache; /* [B, Hkv, capacity, 256], written */
 } kv_append_args;
 
+/* Arguments of kv_keep.  After a verify block of `rows` rows was appended at kv_offset and some
+ * of its rows were accepted: for each batch entry b, the rows r with bit r of keep[b] set move,
+ * in increasing r, to cache rows kv_offset, kv_offset + 1, ... of every KV head, bit for bit;
+ * the block's rows after the kept ones are left as they were.  An accepted path of a draft tree
+ * whose rows are numbered parents first (a chain being the special case 0, 1, 2, ...) keeps
+ * its order.  TensorFold PR #1009 (attention kernel-contract commit) compares keep bit for bit,
+ * also a second time on the caches the first call left. */
+typedef struct {
+  int32_t dtype;
+  int32_t B;              /* 1..64 */
+  int32_t Hkv;
+  int32_t D;
+  int32_t rows;           /* rows of the verify block: 1..32 */
+  int32_t reserved;
+  int64_t kv_offset;      /* cache index of the block's first row */
+  int64_t capacity;
+  const uint32_t* keep;   /* host array [B]: bit r set = keep row r (bits at or past rows must be 0);
+                             read during the call only */
+  attn_tensor k_cache;    /* [B, Hkv, capacity, 256]: rows kv_offset .. kv_offset + rows - 1 rewritten */
+  attn_tensor v_cache;    /* [B, Hkv, capacity, 256], the same */
+} kv_keep_args;
+
 /* Arguments of attn_merge. */
 typedef struct {
   int32_t dtype;
@@ -174,7 +196,7 @@ typedef struct {
 int attn_abi_version(void);
 
 /* sizeof of the argument structs as compiled into the library: which = 0 attn_args,
- * 1 kv_append_args, 2 merge_args, 3 attn_plan_info.  Returns 0 for an unknown value. */
+ * 1 kv_append_args, 2 merge_args, 3 attn_plan_info, 4 kv_keep_args.  Returns 0 for an unknown value. */
 size_t attn_struct_size(int which);
 
 /* Static description of a status code.  Never NULL. */
@@ -216,6 +238,13 @@ int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stre
 /* Append `rows` new K and V rows to the cache at kv_offset: a pure bit copy (signed zeros
  * and NaN payloads survive).  TensorFold PR #1009 compares append bit for bit. */
 int kv_append(const kv_append_args* a, void* stream);
+
+/* Compact the kept rows of a verify block in the caches, in place (see kv_keep_args): a pure bit
+ * copy.  Errors (nothing is written): ATTN_E_NULL (a, keep or a cache pointer), ATTN_E_DTYPE,
+ * ATTN_E_HEADS (B not in 1..64 or Hkv < 1), ATTN_E_HEAD_DIM, ATTN_E_ROWS (rows not in 1..32),
+ * ATTN_E_KV (kv_offset < 0 or the block past capacity), ATTN_E_ARG (a keep bit at or past
+ * rows), ATTN_E_LAYOUT.  TensorFold PR #1009 compares keep bit for bit. */
+int kv_keep(const kv_keep_args* a, void* stream);
 
 /* Combine per-chunk partials (o_c normalised within chunk c, lse_c = its log-sum-exp):
  * out = sum_c exp(lse_c - lse) o_c / sum_c exp(lse_c - lse) * sigmoid(gate), chunks with

@@ -52,6 +52,7 @@ __all__ = [
     "merge",
     "head_chunked",
     "kv_append",
+    "kv_keep",
 ]
 
 _ROW_BLOCK = 256  # rows evaluated together; each row is computed independently
@@ -287,4 +288,26 @@ def kv_append(cache_bits, new_bits, kv_offset: int):
     if kv_offset < 0 or kv_offset + rows > cache.shape[2]:
         raise ValueError("append beyond the cache capacity")
     cache[:, :, kv_offset:kv_offset + rows] = new
+    return cache
+
+
+def kv_keep(cache_bits, kv_offset: int, rows: int, keep):
+    """After a verify block of `rows` rows at kv_offset: in each batch entry b, the rows r whose
+    bit is set in keep[b] move, in increasing r, to kv_offset, kv_offset + 1, ...; the block's
+    rows after them are unchanged.  A pure copy of raw bit patterns, as the TensorFold PR #1009
+    kernel-contract commit compares keep (bit for bit, also a second time on the caches the
+    first left).  cache [B, Hkv, cap, D]; keep: one bitmask per batch entry; returns a new array.
+    """
+    cache = np.array(cache_bits, copy=True)
+    if kv_offset < 0 or kv_offset + rows > cache.shape[2] or not 1 <= rows <= 32:
+        raise ValueError("verify block outside the cache")
+    if len(keep) != cache.shape[0]:
+        raise ValueError("one keep mask per batch entry")
+    src = np.asarray(cache_bits)
+    for b, m in enumerate(keep):
+        if m >> rows:
+            raise ValueError("keep bit past the block")
+        kept = [r for r in range(rows) if (m >> r) & 1]
+        for i, r in enumerate(kept):
+            cache[b, :, kv_offset + i] = src[b, :, kv_offset + r]
     return cache

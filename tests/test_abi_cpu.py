@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_sizes_and_version():
     lib = ga.lib()
     assert lib.attn_abi_version() == _abi.ABI_VERSION
-    for i, st in enumerate((_abi.AttnArgs, _abi.KvAppendArgs, _abi.MergeArgs, _abi.PlanInfo)):
+    for i, st in enumerate((_abi.AttnArgs, _abi.KvAppendArgs, _abi.MergeArgs, _abi.PlanInfo, _abi.KvKeepArgs)):
         assert lib.attn_struct_size(i) == C.sizeof(st)
     assert lib.attn_struct_size(99) == 0
     for code in list(_abi.STATUS) + [12345]:
@@ -187,3 +187,32 @@ def test_append_and_merge_rejections():
     assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_LAYOUT"]
     m.partial_o = None
     assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+
+
+def test_keep_rejections():
+    lib = ga.lib()
+    t = _abi.Tensor(1 << 20, 2 * 40 * 256, 40 * 256, 256)
+    masks = (C.c_uint32 * 2)(0b101, 0b1)
+    keep = C.cast(masks, C.POINTER(C.c_uint32))
+    a = _abi.KvKeepArgs(0, 2, 2, 256, 3, 0, 36, 40, keep, t, t)
+    a.kv_offset = 38
+    assert lib.kv_keep(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_KV"]
+    a.kv_offset = 36
+    a.rows = 33
+    assert lib.kv_keep(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_ROWS"]
+    a.rows = 0
+    assert lib.kv_keep(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_ROWS"]
+    a.rows = 2                                   # bit 2 of 0b101 is past the block
+    assert lib.kv_keep(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_ARG"]
+    a.rows = 3
+    a.B = 65
+    assert lib.kv_keep(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_HEADS"]
+    a.B = 2
+    a.D = 128
+    assert lib.kv_keep(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
+    a.D = 256
+    a.k_cache = _abi.Tensor((1 << 20) + 8, 2 * 40 * 256, 40 * 256, 256)
+    assert lib.kv_keep(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_LAYOUT"]
+    a.keep = None
+    assert lib.kv_keep(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    assert lib.kv_keep(None, None) == _abi.STATUS_CODE["ATTN_E_NULL"]

@@ -251,6 +251,33 @@ def test_kv_append_is_bit_exact():
 
 
 @needs_gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_kv_keep_is_bit_exact(dtype):
+    # a verify block of 32 rows at offset 100: batch entry 0 keeps a tree path, entry 1 a chain,
+    # entry 2 nothing, entry 3 everything; then a second keep on the caches the first left
+    nf = syn.nonfinite_bits(dtype)
+    rng = syn.streams(17)
+    B, Hkv, cap, off, rows = 4, 2, 160, 100, 32
+    cache = syn.normal_bits(rng["k"], (B, Hkv, cap, 256), dtype)
+    cache[0, 1, off + 9, :3] = [nf["nan"], nf["-0"], nf["-inf"]]
+    vcache = syn.normal_bits(rng["v"], (B, Hkv, cap, 256), dtype)
+    keep = [(1 << 0) | (1 << 3) | (1 << 9) | (1 << 30), (1 << 7) - 1, 0, 0xFFFFFFFF]
+    kc, vc = to_dev(cache, dtype), to_dev(vcache, dtype)
+    ga.kv_keep(kc, vc, kv_offset=off, rows=rows, keep=keep)
+    torch.cuda.synchronize()
+    want_k = reference.kv_keep(cache, off, rows, keep)
+    want_v = reference.kv_keep(vcache, off, rows, keep)
+    assert np.array_equal(to_bits(kc), want_k) and np.array_equal(to_bits(vc), want_v)
+    keep2 = [0b0110, 0b1010101, 0, 1 << 31]
+    ga.kv_keep(kc, vc, kv_offset=off, rows=rows, keep=keep2)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kc), reference.kv_keep(want_k, off, rows, keep2))
+    assert np.array_equal(to_bits(vc), reference.kv_keep(want_v, off, rows, keep2))
+    with pytest.raises(ga.AttnError):
+        ga.kv_keep(kc, vc, kv_offset=off, rows=3, keep=[0b1000, 0, 0, 0])
+
+
+@needs_gpu
 @pytest.mark.parametrize("n_chunks", [4, 12, 100])  # few-chunk pass; many-chunk pass in one and in two rounds
 def test_merge_matches_oracle(n_chunks):
     rng = syn.streams(8)

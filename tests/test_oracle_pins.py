@@ -234,6 +234,35 @@ def test_scale_default_is_one_over_sixteen():
     np.testing.assert_array_equal(a, b)
 
 
+def test_kv_keep_moves_kept_rows_in_order():
+    # pins from the definition, written out by hand: a chain (rows 0..n-1 kept) leaves the cache
+    # unchanged; a tree path {1, 3, 4} lands at offsets 0, 1, 2 in that order; the rows after
+    # the kept ones and everything outside the block stay; NaN payloads and -0 survive
+    nf = syn.nonfinite_bits("bf16")
+    cache = np.arange(2 * 1 * 12 * 4, dtype=np.uint16).reshape(2, 1, 12, 4)
+    cache[0, 0, 7, 0] = nf["nan"]
+    cache[1, 0, 5, 3] = nf["-0"]
+    off, rows = 3, 6                        # block rows are cache rows 3..8
+    chain = reference.kv_keep(cache, off, rows, [0b111, 0b111111])
+    np.testing.assert_array_equal(chain, cache)
+    out = reference.kv_keep(cache, off, rows, [0b011010, 0b000001])
+    want = cache.copy()
+    want[0, 0, 3] = cache[0, 0, 4]          # row 1 -> slot 0
+    want[0, 0, 4] = cache[0, 0, 6]          # row 3 -> slot 1
+    want[0, 0, 5] = cache[0, 0, 7]          # row 4 -> slot 2 (carries the NaN payload)
+    np.testing.assert_array_equal(out, want)
+    assert out[0, 0, 5, 0] == nf["nan"] and out[1, 0, 5, 3] == nf["-0"]
+    # a second keep on the cache the first left: keep slots {0, 2} of the 3 kept rows
+    twice = reference.kv_keep(out, off, 3, [0b101, 0b1])
+    want2 = out.copy()
+    want2[0, 0, 4] = out[0, 0, 5]
+    np.testing.assert_array_equal(twice, want2)
+    with pytest.raises(ValueError):
+        reference.kv_keep(cache, off, rows, [1 << rows, 0])
+    with pytest.raises(ValueError):
+        reference.kv_keep(cache, 8, rows, [1, 1])
+
+
 def test_kv_append_is_a_bit_copy():
     nf = syn.nonfinite_bits("bf16")
     cache = np.zeros((1, 2, 8, 4), dtype=np.uint16)
