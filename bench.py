@@ -3,7 +3,9 @@
 One step = one pass of the whole path over one batch of synthetic input:
   1. prefill: the 32768-token causal prompt of the 27B shape (batch 1, 24 query heads over
      4 KV heads, head_dim 256, bf16, gated) in query blocks of q_block rows: kv_append of the
-     block's K/V, then attn_prefill of the block;
+     block's K/V, then the block's attn_prefill, issued as its two launches (the main pass by
+     attn_prefill_partials, then attn_merge when the keys are split) on one stream, so that
+     events can bracket the main pass alone;
   2. decode: one decode row of the 35B-A3B shape (batch 2, 16 query heads over 2 KV heads)
      appended at KV offset 32768: kv_append, then attn_decode (split-KV pass + merge), on a
      cache chosen round-robin from enough distinct caches that the 256 MB Infinity Cache
@@ -16,8 +18,9 @@ bracket each part of every step.
 value = prefill attention TFLOP/s over the 32k prompt (algorithmic flops: 4 * 256 per
 admissible (head, row, key) triple: 4*256*24*32768*32769/2 = 1.3195e13 per prompt).
 decode.value = KV GB/s of the one-row decode (K and V bytes read once per KV group + Q,
-gate and out).  roofline = the attn_prefill pass (split kernel + merge) against the dense
-bf16 MFMA peak; decode.roofline = the decode call against HBM bandwidth.
+gate and out).  roofline = the dominant kernel, the main pass of a prefill block (event-timed
+on its stream, averaged over the 64 blocks), against the dense bf16 MFMA peak;
+decode.roofline = the decode call against HBM bandwidth.
 cpu_baseline = the float64 oracle on a bounded sample of the same prompt, on the host cores.
 
 `--copy-calibration BYTES` only copies a BYTES-sized device buffer once (for calibrating the
@@ -152,9 +155,12 @@ def main():
             ga.kv_append(k[:, :, s:e], v[:, :, s:e], kc, vc, kv_offset=s)
             if per_call is not None:
                 per_call[i][0].record(stream)
-            ga.prefill(q[:, :, s:e], kc, vc, g[:, :, s:e], kv_offset=s, kv_len=e, out=out[:, :, s:e], workspace=ws)
+            _, parts = ga.prefill_partials(q[:, :, s:e], kc, vc, g[:, :, s:e], kv_offset=s, kv_len=e,
+                                           out=out[:, :, s:e], workspace=ws)
             if per_call is not None:
                 per_call[i][1].record(stream)
+            if parts is not None:
+                ga.merge(parts[0], parts[1], g[:, :, s:e], out=out[:, :, s:e])
 
     def decode_pass(it, evs=None):
         kk_, vv_ = caches[it % n_rot]
@@ -267,9 +273,9 @@ def main():
                                                      "grid_blocks")}},
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic and traffic["prefill_call_bytes"],
-                     "kernel": "attn_prefill pass (attn_fwd_kernel + merge_kernel when split)",
-                     "avg_call_us": round(float(call_mean_ms.mean()) * 1e3, 2)},
+                     "traffic": traffic and traffic.get("prefill_main_bytes"),
+                     "kernel": "attn_fwd_kernel (main pass of a prefill block)",
+                     "avg_launch_us": round(float(call_mean_ms.mean()) * 1e3, 2)},
         "setup_s": round(gen_s, 1),
     }
 

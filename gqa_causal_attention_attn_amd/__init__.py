@@ -17,7 +17,8 @@ import torch
 from . import _abi
 
 __all__ = [
-    "AttnError", "lib", "prefill", "decode", "kv_append", "kv_keep", "merge", "head_chunk_plan", "workspace_bytes",
+    "AttnError", "lib", "prefill", "prefill_partials", "decode", "kv_append", "kv_keep", "merge", "head_chunk_plan",
+    "workspace_bytes",
     "describe_plan", "plan_args", "variant_name", "prompt_prefill",
 ]
 
@@ -131,6 +132,32 @@ def _run(op: int, q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, cau
     fn = L.attn_prefill if op == _abi.OP_PREFILL else L.attn_decode
     _check(fn(C.byref(a), ws_ptr, ws_len, _stream_handle(q)))
     return out
+
+
+def prefill_partials(q, k_cache, v_cache, gate, *, kv_offset: int, workspace, kv_len=None, causal=True, scale=0.0,
+                     head_chunk=0, n_splits=0, mask=None, out=None):
+    """attn_prefill_partials: the main pass only.  Returns (out, partials).  partials is None when
+    the plan kept the keys in one chunk (out is then final); otherwise it is (partial_o,
+    partial_lse), views into `workspace` (a uint8 tensor) to finish with
+    merge(partial_o, partial_lse, gate, out) on a stream ordered after this one."""
+    if kv_len is None:
+        kv_len = kv_offset + q.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    a = _args(q, k_cache, v_cache, gate, out, kv_offset=kv_offset, kv_len=kv_len, causal=causal, scale=scale,
+              head_chunk=head_chunk, n_splits=n_splits, mask=mask)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    n, off = C.c_int32(0), C.c_size_t(0)
+    _check(lib().attn_prefill_partials(C.byref(a), workspace.data_ptr(), workspace.numel(), _stream_handle(q),
+                                       C.byref(n), C.byref(off)))
+    if n.value == 1:
+        return out, None
+    B, Hq, rows = q.shape[0], q.shape[1], q.shape[2]
+    cnt = n.value * B * Hq * rows
+    po = workspace[:cnt * 1024].view(torch.float32).view(n.value, B, Hq, rows, 256)
+    pl = workspace[off.value:off.value + cnt * 4].view(torch.float32).view(n.value, B, Hq, rows)
+    return out, (po, pl)
 
 
 def prefill(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
@@ -263,12 +290,14 @@ def variant_name(variant: int) -> str:
 
 
 def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int, kv_offset: int = 0, out=None, workspace=None,
-                   head_chunk=0, n_splits=0):
+                   head_chunk=0, n_splits=0, overlap_merge=False):
     """A prompt in query blocks: for each block, kv_append its K/V rows, then attn_prefill it.
 
     q/gate [B, Hq, N, 256] and k/v [B, Hkv, N, 256] hold the prompt (positions kv_offset ..
     kv_offset + N - 1); k_cache/v_cache have room for them.  Block i attends to the cache plus
     itself ("perf(qwen36): qualify M4 head-256 attention", Summary: query blocks of 128 or 512).
+    With overlap_merge, each block's merge runs on a second stream beside the next block's main
+    pass (two workspaces, alternating); the caller's stream waits for the last merge.
     """
     N = q.shape[2]
     if out is None:
@@ -281,9 +310,33 @@ def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int, kv_offset: 
                           capacity=k_cache.shape[2], head_chunk=head_chunk, n_splits=n_splits)
             need = max(need, workspace_bytes(a, _abi.OP_PREFILL))
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    for s in range(0, N, q_block):
+    if not overlap_merge:
+        for s in range(0, N, q_block):
+            e = min(s + q_block, N)
+            kv_append(k[:, :, s:e], v[:, :, s:e], k_cache, v_cache, kv_offset=kv_offset + s)
+            prefill(q[:, :, s:e], k_cache, v_cache, gate[:, :, s:e], kv_offset=kv_offset + s, kv_len=kv_offset + e,
+                    out=out[:, :, s:e], workspace=workspace, head_chunk=head_chunk, n_splits=n_splits)
+        return out
+    main = torch.cuda.current_stream(q.device)
+    side = torch.cuda.Stream(device=q.device)
+    spaces = [workspace, torch.empty_like(workspace)]
+    merged = [None, None]  # per workspace: the event after the merge that last read it
+    for i, s in enumerate(range(0, N, q_block)):
         e = min(s + q_block, N)
+        slot = i % 2
+        if merged[slot] is not None:
+            main.wait_event(merged[slot])
         kv_append(k[:, :, s:e], v[:, :, s:e], k_cache, v_cache, kv_offset=kv_offset + s)
-        prefill(q[:, :, s:e], k_cache, v_cache, gate[:, :, s:e], kv_offset=kv_offset + s, kv_len=kv_offset + e,
-                out=out[:, :, s:e], workspace=workspace, head_chunk=head_chunk, n_splits=n_splits)
+        _, parts = prefill_partials(q[:, :, s:e], k_cache, v_cache, gate[:, :, s:e], kv_offset=kv_offset + s,
+                                    kv_len=kv_offset + e, out=out[:, :, s:e], workspace=spaces[slot],
+                                    head_chunk=head_chunk, n_splits=n_splits)
+        if parts is not None:
+            ready = torch.cuda.Event()
+            ready.record(main)
+            side.wait_event(ready)
+            with torch.cuda.stream(side):
+                merge(parts[0], parts[1], gate[:, :, s:e], out=out[:, :, s:e])
+            merged[slot] = torch.cuda.Event()
+            merged[slot].record(side)
+    main.wait_stream(side)
     return out

@@ -27,7 +27,7 @@ OP_PREFILL, OP_DECODE = 0, 1
 EXPORTS = (
     "attn_abi_version", "attn_struct_size", "attn_strerror", "attn_variant_name", "attn_head_chunk_plan",
     "attn_workspace_bytes", "attn_describe_plan", "attn_prefill", "attn_decode", "kv_append", "attn_merge",
-    "kv_keep",
+    "kv_keep", "attn_prefill_partials",
 )
 KEEP_MAX_BATCH = 64
 
@@ -107,6 +107,9 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.kv_append.argtypes = [P(KvAppendArgs), C.c_void_p]
     lib.attn_merge.restype = C.c_int
     lib.attn_merge.argtypes = [P(MergeArgs), C.c_void_p]
+    lib.attn_prefill_partials.restype = C.c_int
+    lib.attn_prefill_partials.argtypes = [P(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p, P(C.c_int32),
+                                          P(C.c_size_t)]
     lib.kv_keep.restype = C.c_int
     lib.kv_keep.argtypes = [P(KvKeepArgs), C.c_void_p]
     if lib.attn_abi_version() != ABI_VERSION:

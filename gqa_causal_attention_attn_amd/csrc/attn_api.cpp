@@ -187,7 +187,8 @@ inline int variant_of(const attn_args* a, const Plan& P) {
   return (P.mask_lds << 5) | (P.shape << 3) | (a->dtype << 2) | a->mask.kind;
 }
 
-int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream) {
+int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream, bool merge = true,
+            int32_t* n_chunks = nullptr, size_t* lse_offset = nullptr) {
   int st = validate(a, op);
   if (st) return st;
   Plan P;
@@ -232,8 +233,10 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream)
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_o_bytes);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_chunks) *n_chunks = P.n_splits;
+  if (lse_offset) *lse_offset = P.n_splits > 1 ? P.ws_o_bytes : 0;
   if (gqa::launch_fwd(p, a->dtype, a->mask.kind, P.shape, s) != hipSuccess) return ATTN_E_HIP;
-  if (P.n_splits > 1) {
+  if (P.n_splits > 1 && merge) {
     gqa::MergeParams mp;
     mp.part_o = p.part_o;
     mp.part_lse = p.part_lse;
@@ -346,6 +349,12 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
 
 int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* stream) {
   return run_fwd(a, ATTN_OP_PREFILL, workspace, ws_bytes, stream);
+}
+
+int attn_prefill_partials(const attn_args* a, void* workspace, size_t ws_bytes, void* stream, int32_t* n_chunks,
+                          size_t* lse_offset) {
+  if (!n_chunks || !lse_offset) return ATTN_E_NULL;
+  return run_fwd(a, ATTN_OP_PREFILL, workspace, ws_bytes, stream, false, n_chunks, lse_offset);
 }
 
 int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stream) {

@@ -229,6 +229,17 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info);
  * split partials.  Writes a->out. */
 int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
 
+/* The main pass of attn_prefill alone, for callers that overlap one query block's merge with
+ * the next block's main pass (two workspaces, the merges on a second stream).  *n_chunks
+ * receives the number of KV chunks of the plan.  With *n_chunks = 1 the call is complete and out
+ * is written.  With *n_chunks > 1 out is not written: the normalised partials stay in the
+ * workspace, o at offset 0 ([n_chunks, B, Hq, rows, 256] fp32) and the natural-log lse at byte
+ * offset *lse_offset ([n_chunks, B, Hq, rows] fp32), and the caller completes the call with
+ * attn_merge (gate and out as here) on a stream ordered after this one, before the workspace is
+ * reused.  Errors as attn_prefill, plus ATTN_E_NULL for a null n_chunks or lse_offset. */
+int attn_prefill_partials(const attn_args* a, void* workspace, size_t ws_bytes, void* stream, int32_t* n_chunks,
+                          size_t* lse_offset);
+
 /* The same operation for 1..32 decode / verify rows: a split-KV pass in which each
  * workgroup reads its KV chunk once for all heads of the group, each wavefront serving one
  * head chunk (a->head_chunk), then the merge pass.  TensorFold PR #1009 (attention

@@ -216,3 +216,15 @@ def test_keep_rejections():
     a.keep = None
     assert lib.kv_keep(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
     assert lib.kv_keep(None, None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+
+
+def test_prefill_partials_needs_its_outputs():
+    lib = ga.lib()
+    a = _good(rows=512, kv_offset=4096)
+    n, off = C.c_int32(7), C.c_size_t(7)
+    assert lib.attn_prefill_partials(C.byref(a), None, 0, None, None, C.byref(off)) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    assert lib.attn_prefill_partials(C.byref(a), None, 0, None, C.byref(n), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    need = ga.workspace_bytes(a, _abi.OP_PREFILL)
+    assert need > 0
+    st = lib.attn_prefill_partials(C.byref(a), None, 0, None, C.byref(n), C.byref(off))
+    assert st == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]

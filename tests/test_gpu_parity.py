@@ -66,6 +66,28 @@ def test_prefill_ragged_shapes(Hq, Hkv, N, q_block, n_splits):
 
 
 @needs_gpu
+@pytest.mark.parametrize("n_splits", [0, 3])
+def test_prompt_with_merges_on_a_second_stream(n_splits):
+    # attn_prefill_partials + attn_merge on a second stream, two workspaces alternating: the
+    # same bits as attn_prefill block by block
+    _say("overlapped merges", n_splits)
+    qb, kb, vb, gb, _ = prompt(2100 + n_splits, B=1, Hq=24, Hkv=4, N=700)
+    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    outs = []
+    for overlap in (False, True):
+        kc = torch.full((1, 4, 700, 256), float("nan"), dtype=q.dtype, device="cuda")
+        vc = torch.full_like(kc, float("nan"))
+        out = torch.full_like(q, float("nan"))
+        ga.prompt_prefill(q, k, v, g, kc, vc, q_block=128, out=out, n_splits=n_splits, overlap_merge=overlap)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    ref = reference.attention(syn.widen(qb), syn.widen(kb), syn.widen(vb), syn.widen(gb), n_kv_heads=4,
+                              kv_offset=0, kv_len=700)
+    _say(assert_close(to_f64(outs[1]), ref, "overlapped merges"))
+
+
+@needs_gpu
 def test_prefill_batch2_fp16_noncausal():
     rng = syn.streams(31)
     B, Hq, Hkv, rows, kv = 2, 16, 2, 40, 150
