@@ -8,8 +8,10 @@
 // (decode): one workgroup of sixteen wavefronts per row, each loading its share of the
 // chunks at once.  HBM-bound (n_chunks x 1 KiB per row).
 //
-// Append (same commit, "pack, append and keep ... bit-exact"): a 16-byte copy of each new
-// K/V row into the cache; no arithmetic touches the bits.
+// Append and keep (the same commit compares both bit for bit, keep a second time on the caches
+// the first call left): 16-byte copies of K/V rows into the cache, no arithmetic on the bits.
+// Keep compacts the accepted rows of a verify block in place, one workgroup per (b, g) reading
+// every kept row before writing any.
 #include <hip/hip_runtime.h>
 #include <math.h>
 

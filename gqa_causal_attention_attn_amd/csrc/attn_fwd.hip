@@ -34,8 +34,16 @@
 //
 // Schedule.  On the prompt shapes the P.V product of tile t - 1 runs on the matrix cores while
 // the VALU turns tile t's scores into weights (the previous tile stays in its stage: two tiles
-// in flight); on the short-decode shape, which streams keys from HBM and has little to
-// compute, P.V follows its softmax directly and three tiles are in flight.
+// in flight); on the eight-wavefront shape each wavefront's direct loads of tile t + 2 are
+// issued one by one between the MFMAs of S(t), after the barrier that freed their stage.  On
+// the short-decode shape, which streams keys from HBM and has little to compute, P.V follows
+// its softmax directly and three tiles are in flight.
+//
+// Masks.  A mask that is the same for every head, with 16-byte aligned rows, may be staged in
+// LDS (the ML variants, chosen by the host): each tile's 32-key window of the workgroup's mask
+// rows rides in a 4 KiB stage of its own beside K and V, loaded by wavefronts 0-3 with the same
+// direct loads and waits, and each lane reads its words from there.  Otherwise each lane loads
+// its words from memory.  Both give the same bits.
 //
 // The softmax is the online (flash) form of the plain definition: per pair a running max m
 // (log2 units of the scaled score), a running sum l and the accumulator O, rescaled by
