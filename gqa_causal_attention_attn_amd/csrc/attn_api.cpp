@@ -238,6 +238,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
   if (gqa::launch_fwd(p, a->dtype, a->mask.kind, P.shape, s) != hipSuccess) return ATTN_E_HIP;
   if (P.n_splits > 1 && merge) {
     gqa::MergeParams mp;
+    memset(&mp, 0, sizeof(mp));
     mp.part_o = p.part_o;
     mp.part_lse = p.part_lse;
     mp.gate = p.gate;
@@ -245,6 +246,14 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
     mp.g_sb = p.g_sb, mp.g_sh = p.g_sh, mp.g_sr = p.g_sr;
     mp.o_sb = p.o_sb, mp.o_sh = p.o_sh, mp.o_sr = p.o_sr;
     mp.n_chunks = P.n_splits, mp.B = a->B, mp.Hq = a->Hq, mp.rows = a->rows;
+    gqa::RepairParams& f = mp.fix;  // the inputs of this main pass, for the merge's repair
+    f.q = p.q, f.k = p.k, f.v = p.v, f.mask = p.mask;
+    f.q_sb = p.q_sb, f.q_sh = p.q_sh, f.q_sr = p.q_sr;
+    f.k_sb = p.k_sb, f.k_sh = p.k_sh, f.k_st = p.k_st;
+    f.v_sb = p.v_sb, f.v_sh = p.v_sh, f.v_st = p.v_st;
+    f.m_sb = p.m_sb, f.m_sh = p.m_sh, f.m_sr = p.m_sr;
+    f.mask_kind = a->mask.kind, f.G = P.G, f.kv_offset = p.kv_offset, f.kv_len = p.kv_len;
+    f.causal = p.causal, f.keys_per_split = P.keys_per_split, f.scale_log2 = p.scale_log2;
     if (gqa::launch_merge(mp, a->dtype, s) != hipSuccess) return ATTN_E_HIP;
   }
   return ATTN_OK;
@@ -428,6 +437,7 @@ int attn_merge(const merge_args* a, void* stream) {
       !strides_ok(a->out) || (reinterpret_cast<uintptr_t>(a->partial_lse) & 3u))
     return ATTN_E_LAYOUT;
   gqa::MergeParams p;
+  memset(&p, 0, sizeof(p));  // no main-pass inputs: no repair
   p.part_o = a->partial_o;
   p.part_lse = a->partial_lse;
   p.gate = static_cast<const uint16_t*>(a->gate.ptr);

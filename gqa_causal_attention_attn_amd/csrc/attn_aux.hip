@@ -4,9 +4,10 @@
 // and a merge of the chunks): per (b, h, r), lse = log sum_c exp(lse_c),
 // out = sum_c exp(lse_c - lse) o_c * sigmoid(gate), an empty chunk (lse_c = -Inf) adds
 // nothing (its slot is selected out, never multiplied in) and a row with every chunk empty
-// gives 0.  Few chunks: one wavefront per row with every partial loaded at once; many chunks
-// (decode): one workgroup of sixteen wavefronts per row, each loading its share of the
-// chunks at once.  HBM-bound (n_chunks x 1 KiB per row).
+// gives 0; a chunk whose lse is NaN makes the row NaN.  Few chunks: one wavefront per row
+// with every partial loaded at once; many chunks (decode): one workgroup of sixteen
+// wavefronts per row, each loading its share of the chunks at once.  HBM-bound
+// (n_chunks x 1 KiB per row).
 //
 // Append and keep (the same commit compares both bit for bit, keep a second time on the caches
 // the first call left): 16-byte copies of K/V rows into the cache, no arithmetic on the bits.
@@ -41,6 +42,85 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   else return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
 }
 
+// Nonfinite repair of a row (b, h, r) whose chunk partials hold a NaN (a key hidden from the
+// row met a nonfinite V value in a tile the row shared with others, and 0 * Inf became NaN):
+// the row's output computed again from the main pass's inputs over its admissible keys only,
+// by the plain definition in fp32, one key at a time, the whole wavefront on the row (each
+// lane 4 dims, dims 4 lane .. + 3; every score is summed across the wavefront and taken from
+// lane 0, so all lanes use the same one), gated and rounded once.  A NaN that the definition
+// itself produces comes out NaN again.  Only rows with such a chunk get here.
+template <int DT>
+__device__ __forceinline__ void exact_row(const RepairParams& f, int b, int h, int r, int lane, u32x2 gw,
+                                          uint16_t* orow) {
+  const int g = h / f.G;
+  const int hi = f.causal ? min(f.kv_len, f.kv_offset + r + 1) : f.kv_len;
+  const int lo = 0;
+  const u32x2 qw = *reinterpret_cast<const u32x2*>(f.q + (int64_t)b * f.q_sb + (int64_t)h * f.q_sh +
+                                                   (int64_t)r * f.q_sr + 4 * lane);
+  const float q0 = to_f32<DT>((uint16_t)(qw[0] & 0xffffu)), q1 = to_f32<DT>((uint16_t)(qw[0] >> 16));
+  const float q2 = to_f32<DT>((uint16_t)(qw[1] & 0xffffu)), q3 = to_f32<DT>((uint16_t)(qw[1] >> 16));
+  const uint16_t* kb = f.k + (int64_t)b * f.k_sb + (int64_t)g * f.k_sh + 4 * lane;
+  const uint16_t* vb = f.v + (int64_t)b * f.v_sb + (int64_t)g * f.v_sh + 4 * lane;
+  const int64_t mrow = (int64_t)b * f.m_sb + (int64_t)h * f.m_sh + (int64_t)r * f.m_sr;
+  // the score of key j in log2 units; adm: the mask does not hide it
+  auto score = [&](int j, bool& adm) {
+    float mt = 0.0f;
+    if (f.mask_kind == 1) mt = static_cast<const uint8_t*>(f.mask)[mrow + j] ? 0.0f : -INFINITY;
+    else if (f.mask_kind == 2) mt = to_f32<DT>(static_cast<const uint16_t*>(f.mask)[mrow + j]);
+    else if (f.mask_kind == 3) mt = static_cast<const float*>(f.mask)[mrow + j];
+    adm = mt > -INFINITY;
+    const u32x2 kw = *reinterpret_cast<const u32x2*>(kb + (int64_t)j * f.k_st);
+    float part = q0 * to_f32<DT>((uint16_t)(kw[0] & 0xffffu));
+    part = __builtin_fmaf(q1, to_f32<DT>((uint16_t)(kw[0] >> 16)), part);
+    part = __builtin_fmaf(q2, to_f32<DT>((uint16_t)(kw[1] & 0xffffu)), part);
+    part = __builtin_fmaf(q3, to_f32<DT>((uint16_t)(kw[1] >> 16)), part);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    part = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, part)));
+    return (part * f.scale_log2) + mt * kLog2e;
+  };
+  bool any = false, nan_s = false;
+  float m = -INFINITY;
+#pragma nounroll
+  for (int j = lo; j < hi; ++j) {
+    bool adm;
+    const float x = score(j, adm);
+    if (!adm) continue;
+    any = true;
+    nan_s = nan_s || __builtin_isnan(x);
+    m = fmaxf(m, x);
+  }
+  if (nan_s) m = NAN;  // the max of a set holding NaN
+  float l = 0.0f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma nounroll
+  for (int j = lo; j < hi; ++j) {
+    bool adm;
+    const float x = score(j, adm);
+    if (!adm) continue;
+    const float w = exp2f(x - m);
+    l += w;
+    const u32x2 vw = *reinterpret_cast<const u32x2*>(vb + (int64_t)j * f.v_st);
+    acc[0] = __builtin_fmaf(w, to_f32<DT>((uint16_t)(vw[0] & 0xffffu)), acc[0]);
+    acc[1] = __builtin_fmaf(w, to_f32<DT>((uint16_t)(vw[0] >> 16)), acc[1]);
+    acc[2] = __builtin_fmaf(w, to_f32<DT>((uint16_t)(vw[1] & 0xffffu)), acc[2]);
+    acc[3] = __builtin_fmaf(w, to_f32<DT>((uint16_t)(vw[1] >> 16)), acc[3]);
+  }
+  const float inv = any ? 1.0f / l : 0.0f;  // a row with no admissible key gives 0
+  const float gv[4] = {to_f32<DT>((uint16_t)(gw[0] & 0xffffu)), to_f32<DT>((uint16_t)(gw[0] >> 16)),
+                       to_f32<DT>((uint16_t)(gw[1] & 0xffffu)), to_f32<DT>((uint16_t)(gw[1] >> 16))};
+  float res[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) res[i] = acc[i] * inv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[i]));
+  u32x2 ow;
+  ow[0] = pack2<DT>(res[0], res[1]);
+  ow[1] = pack2<DT>(res[2], res[3]);
+  *reinterpret_cast<u32x2*>(orow + 4 * lane) = ow;
+}
+
+// whether any of the four values is NaN
+__device__ __forceinline__ bool has_nan4(const f32x4& x) { return __builtin_isnan(x[0] + x[1] + x[2] + x[3]); }
+
 // Many chunks (decode): one workgroup of kMergeWaves wavefronts per row; wavefront w takes the
 // chunks w, w + kMergeWaves, ... (kMergeBatch per pass).  A pass issues all of its lse and
 // partial loads (and the gate) at once; only the row's largest lse crosses the wavefronts
@@ -71,6 +151,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergePara
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
   float ref = -INFINITY;
+  bool nan_l = false;  // a chunk whose lse is NaN makes the row NaN, as the unsplit definition does
   for (int c0 = 0; c0 < p.n_chunks; c0 += kMergeWaves * kMergeBatch) {
     // this pass's chunks of the wavefront, all loads in flight together (indices past the
     // last chunk re-read it and are selected out)
@@ -84,7 +165,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergePara
     }
     float top = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) top = c0 + wave + j * kMergeWaves < p.n_chunks ? fmaxf(top, lc[j]) : top;
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const bool in = c0 + wave + j * kMergeWaves < p.n_chunks;
+      top = in ? fmaxf(top, lc[j]) : top;
+      nan_l = nan_l || (in && __builtin_isnan(lc[j]));
+    }
     if (lane == 0) part_top[wave] = top;
     __syncthreads();
     float pass_top = part_top[0];
@@ -111,7 +196,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergePara
     __syncthreads();  // part_top is rewritten by the next pass
   }
   part_acc[wave][lane] = acc;
-  if (lane == 0) part_w[wave] = wsum;
+  if (lane == 0) part_w[wave] = nan_l ? NAN : wsum;
   __syncthreads();
   if (wave != 0) return;
   acc = part_acc[0][lane];
@@ -121,8 +206,15 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergePara
     acc += part_acc[w][lane];
     wsum += part_w[w];
   }
-  const float inv = wsum > 0.0f ? __builtin_amdgcn_rcpf(wsum) : 0.0f;
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
+  // a NaN in the sums (a chunk's partial or lse held one) with the main pass's inputs at hand:
+  // the row is computed again (a wavefront-uniform branch)
+  if (p.fix.q && __builtin_amdgcn_ballot_w64(__builtin_isnan(wsum) || has_nan4(acc)) != 0) {
+    exact_row<DT>(p.fix, b, h, r, lane, gw, orow);
+    return;
+  }
+  // a NaN weight sum carries a NaN chunk of some wavefront
+  const float inv = __builtin_isnan(wsum) ? NAN : wsum > 0.0f ? __builtin_amdgcn_rcpf(wsum) : 0.0f;
   float gv[4] = {to_f32<DT>((uint16_t)(gw[0] & 0xffffu)), to_f32<DT>((uint16_t)(gw[0] >> 16)),
                  to_f32<DT>((uint16_t)(gw[1] & 0xffffu)), to_f32<DT>((uint16_t)(gw[1] >> 16))};
   float res[4];
@@ -165,8 +257,12 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
     oc[c] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * kHeadDim + d0);
   }
   float top = -INFINITY;
+  bool nan_l = false;  // a chunk whose lse is NaN makes the row NaN, as the unsplit definition does
 #pragma unroll
-  for (int c = 0; c < kFewChunks; ++c) top = c < p.n_chunks ? fmaxf(top, lc[c]) : top;
+  for (int c = 0; c < kFewChunks; ++c) {
+    top = c < p.n_chunks ? fmaxf(top, lc[c]) : top;
+    nan_l = nan_l || (c < p.n_chunks && __builtin_isnan(lc[c]));
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
   if (top > -INFINITY) {
@@ -180,8 +276,14 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
       }
     }
   }
-  const float inv = wsum > 0.0f ? __builtin_amdgcn_rcpf(wsum) : 0.0f;
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
+  // a NaN in a chunk's partial or lse with the main pass's inputs at hand: the row is computed
+  // again (one wavefront per row)
+  if (p.fix.q && __builtin_amdgcn_ballot_w64(nan_l || __builtin_isnan(wsum) || has_nan4(acc)) != 0) {
+    exact_row<DT>(p.fix, b, h, r, lane, gw, orow);
+    return;
+  }
+  const float inv = nan_l ? NAN : wsum > 0.0f ? __builtin_amdgcn_rcpf(wsum) : 0.0f;
   float gv[4] = {to_f32<DT>((uint16_t)(gw[0] & 0xffffu)), to_f32<DT>((uint16_t)(gw[0] >> 16)),
                  to_f32<DT>((uint16_t)(gw[1] & 0xffffu)), to_f32<DT>((uint16_t)(gw[1] >> 16))};
   float res[4];

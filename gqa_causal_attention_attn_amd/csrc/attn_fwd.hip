@@ -377,7 +377,92 @@ __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xo
 // x + (x of the lane 32 away), the same sum on both lanes
 __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
 
-template <int DT, int MK, int W, int NB, bool ML = false>
+// Nonfinite repair of one (head, row) pair of a launch that keeps the keys in one split: the
+// pair's gated output computed again over the admissible keys of [kv_lo, j_end) only, one key
+// at a time, in fp32 on the VALU.  This lane writes the dims 32 db + 8 q4 + 4 hf + (0..3) of
+// the pair, as the epilogue does.
+// It runs only for inputs that hold nonfinite values; one dim block per pass over the keys keeps
+// its registers few.
+template <int DT, int MK>
+__device__ __forceinline__ void exact_pair(const FwdParams& p, int b, int h, int r, int hf, int kv_lo,
+                                        int j_end, int64_t mrow, const uint16_t* kbase, const uint16_t* vbase) {
+  const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)r * p.q_sr;
+  // admissible: not hidden by the mask (the range is the caller's); x = the score in log2 units
+  auto score = [&](int j, bool& adm) {
+    float mt = 0.0f;
+    if constexpr (MK != 0) mt = mask_term<DT, MK>(p.mask, mrow, j);
+    adm = mt > -INFINITY;
+    const uint16_t* krow = kbase + (int64_t)j * p.k_st;
+    float acc = 0.0f;
+#pragma nounroll
+    for (int d = 0; d < kHeadDim; d += 8) {
+      const u32x4 qa = *reinterpret_cast<const u32x4*>(qrow + d);
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + d);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = __builtin_fmaf(lo16<DT>(qa[e]), lo16<DT>(ka[e]), acc);
+        acc = __builtin_fmaf(hi16<DT>(qa[e]), hi16<DT>(ka[e]), acc);
+      }
+    }
+    return acc * p.scale_log2 + mt;
+  };
+  bool any = false, nan_s = false;
+  float m = -INFINITY;
+#pragma nounroll
+  for (int j = kv_lo; j < j_end; ++j) {
+    bool adm;
+    const float x = score(j, adm);
+    if (!adm) continue;
+    any = true;
+    nan_s = nan_s || __builtin_isnan(x);
+    m = fmaxf(m, x);
+  }
+  if (nan_s) m = NAN;  // the max of a set holding NaN
+  float l = 0.0f, inv = 0.0f;
+  const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
+  uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
+  // one dim block (32 db ..) per pass over the keys
+#pragma nounroll
+  for (int c = 0; c < 8; ++c) {
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    if (any) {
+#pragma nounroll
+      for (int j = kv_lo; j < j_end; ++j) {
+        bool adm;
+        const float x = score(j, adm);
+        if (!adm) continue;
+        const float w = exp2f(x - m);
+        if (c == 0) l += w;
+        const uint16_t* vrow = vbase + (int64_t)j * p.v_st;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = 32 * c + 8 * i + 4 * hf;
+          const u32x2 vv = *reinterpret_cast<const u32x2*>(vrow + d0);
+          acc[4 * i + 0] = __builtin_fmaf(w, lo16<DT>(vv[0]), acc[4 * i + 0]);
+          acc[4 * i + 1] = __builtin_fmaf(w, hi16<DT>(vv[0]), acc[4 * i + 1]);
+          acc[4 * i + 2] = __builtin_fmaf(w, lo16<DT>(vv[1]), acc[4 * i + 2]);
+          acc[4 * i + 3] = __builtin_fmaf(w, hi16<DT>(vv[1]), acc[4 * i + 3]);
+        }
+      }
+    }
+    if (c == 0) inv = any ? 1.0f / l : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * c + 8 * i + 4 * hf;
+      const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
+      u32x2 ow;
+      ow[0] = pack2<DT>(acc[4 * i] * inv * sigmoidf_(lo16<DT>(gw[0])),
+                        acc[4 * i + 1] * inv * sigmoidf_(hi16<DT>(gw[0])));
+      ow[1] = pack2<DT>(acc[4 * i + 2] * inv * sigmoidf_(lo16<DT>(gw[1])),
+                        acc[4 * i + 3] * inv * sigmoidf_(hi16<DT>(gw[1])));
+      *reinterpret_cast<u32x2*>(orow + d0) = ow;
+    }
+  }
+}
+
+template <int DT, int MK, int W, int NB, bool ML, bool SPLIT>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) {
   static_assert((W == 4 && (NB == 1 || NB == 2)) || (W == 8 && NB == 1), "4 wavefronts of 1 or 2 blocks, or 8 of 1");
   static_assert(!ML || (MK != 0 && NB == 1), "mask rows in LDS: masked one-block shapes");
@@ -866,10 +951,13 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
   // ---- epilogue: element q of o*[db] is dim 32 db + 8 (q / 4) + 4 hf + (q % 4)
   const float lt0 = sum_halves(l0), lt1 = sum_halves(l1);
+  // returns whether a NaN came out of o / l (one split only: the nonfinite repair below then
+  // redoes the pair; split partials are checked and redone by the merge)
   auto finish = [&](bool valid, int h, int r, float l_tot, float m_run, f32x16(&o)[8]) {
-    if (!valid) return;
+    bool nan_seen = false;
+    if (!valid) return nan_seen;
     const float inv = l_tot > 0.0f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
-    if (p.n_splits == 1) {
+    if constexpr (!SPLIT) {
       const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
       uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
 #pragma unroll
@@ -881,9 +969,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
           const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
           const float g0 = sigmoidf_(lo16<DT>(gw[0])), g1 = sigmoidf_(hi16<DT>(gw[0]));
           const float g2 = sigmoidf_(lo16<DT>(gw[1])), g3 = sigmoidf_(hi16<DT>(gw[1]));
+          const float x0 = o[db][4 * q4 + 0] * inv, x1 = o[db][4 * q4 + 1] * inv;
+          const float x2 = o[db][4 * q4 + 2] * inv, x3 = o[db][4 * q4 + 3] * inv;
+          nan_seen = nan_seen || __builtin_isnan(x0 + x1 + x2 + x3);  // see the repair below
           u32x2 ow;
-          ow[0] = pack2<DT>(o[db][4 * q4 + 0] * inv * g0, o[db][4 * q4 + 1] * inv * g1);
-          ow[1] = pack2<DT>(o[db][4 * q4 + 2] * inv * g2, o[db][4 * q4 + 3] * inv * g3);
+          ow[0] = pack2<DT>(x0 * g0, x1 * g1);
+          ow[1] = pack2<DT>(x2 * g2, x3 * g3);
           *reinterpret_cast<u32x2*>(orow + d0) = ow;
         }
       }
@@ -901,32 +992,65 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
           *reinterpret_cast<f32x4*>(prow + d0) = v4;
         }
       }
-      if (hf == 0) p.part_lse[row_id] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      // an empty chunk has l = 0 and lse = -inf; a NaN sum keeps its NaN (the merge redoes the row)
+      if (hf == 0) {
+        p.part_lse[row_id] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : l_tot == 0.0f ? -INFINITY : NAN;
+      }
+    }
+    return nan_seen;
+  };
+
+  // ---- nonfinite repair.  A key that a pair cannot see still sits in the tile that P.V
+  // multiplies, with weight 0, and a V value of +-Inf or NaN there makes 0 * Inf = NaN, a
+  // product the definition never forms (it sums over the admissible keys only).  With one
+  // split, a pair whose output holds a NaN is therefore computed again, key by key over this
+  // workgroup's key range, touching admissible keys only: plain fp32 on the VALU, slow,
+  // reached only by inputs that hold nonfinite values (a NaN that the definition itself
+  // produces comes out NaN again).  With several splits the merge does the same per chunk
+  // (kept out of this kernel: the repair's code alone changes how the compiler schedules the
+  // tile loop).
+  // a pair (its own lane or the lane 32 away) whose normalised O came out NaN is computed again
+  auto repair = [&](bool nan_seen, bool valid, int h, int r, int lim, int64_t mrow) {
+    if constexpr (!SPLIT) {
+      const uint64_t bm = __builtin_amdgcn_ballot_w64(nan_seen);
+      if (bm != 0 && valid && (((bm >> li) | (bm >> (li + 32))) & 1u) != 0) {
+        exact_pair<DT, MK>(p, b, h, r, hf, kv_lo, min(kv_end, lim), mrow, kbase, vbase);
+      }
     }
   };
   acc_settle(o0);
-  finish(valid0, h0, r0, lt0, m0, o0);
+  repair(finish(valid0, h0, r0, lt0, m0, o0), valid0, h0, r0, lim0, mrow0);
   if constexpr (TWO) {
     acc_settle(o1);
-    finish(valid1, h1, r1, lt1, m1, o1);
+    repair(finish(valid1, h1, r1, lt1, m1, o1), valid1, h1, r1, lim1, mrow1);
   }
 }
 
-template <int DT, int MK>
-hipError_t launch_fwd_t(const FwdParams& p, int shape, hipStream_t stream) {
+template <int DT, int MK, bool SPLIT>
+hipError_t launch_fwd_s(const FwdParams& p, int shape, hipStream_t stream) {
   if constexpr (MK != 0) {
     if (p.mask_lds && shape != 1) {
-      if (shape == 0) hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 1, true>), dim3(p.grid), dim3(256), 0, stream, p);
-      else hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, 1, true>), dim3(p.grid), dim3(512), 0, stream, p);
+      if (shape == 0) {
+        hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 1, true, SPLIT>), dim3(p.grid), dim3(256), 0, stream, p);
+      } else {
+        hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, 1, true, SPLIT>), dim3(p.grid), dim3(512), 0, stream, p);
+      }
       return hipGetLastError();
     }
   }
   switch (shape) {
-    case 0: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 1>), dim3(p.grid), dim3(256), 0, stream, p); break;
-    case 1: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 2>), dim3(p.grid), dim3(256), 0, stream, p); break;
-    default: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, 1>), dim3(p.grid), dim3(512), 0, stream, p); break;
+    case 0: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 1, false, SPLIT>), dim3(p.grid), dim3(256), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 2, false, SPLIT>), dim3(p.grid), dim3(256), 0, stream, p); break;
+    default: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, 1, false, SPLIT>), dim3(p.grid), dim3(512), 0, stream, p); break;
   }
   return hipGetLastError();
+}
+
+// the split flag is a compile-time choice: the epilogue writes either the gated output or the
+// split partials, and only the former carries the in-kernel nonfinite repair
+template <int DT, int MK>
+hipError_t launch_fwd_t(const FwdParams& p, int shape, hipStream_t stream) {
+  return p.n_splits > 1 ? launch_fwd_s<DT, MK, true>(p, shape, stream) : launch_fwd_s<DT, MK, false>(p, shape, stream);
 }
 
 }  // namespace

@@ -52,6 +52,22 @@ struct FwdParams {
                          // tile rows may be staged in LDS with direct loads
 };
 
+// The main pass's inputs, handed to the merge so that it can compute a chunk partial again
+// when the main pass left a NaN in it (a key hidden from a row met a nonfinite V value in a
+// tile the row shares with others).  q == nullptr: no repair (a merge called on its own).
+struct RepairParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* mask;
+  int64_t q_sb, q_sh, q_sr;
+  int64_t k_sb, k_sh, k_st;
+  int64_t v_sb, v_sh, v_st;
+  int64_t m_sb, m_sh, m_sr;
+  int mask_kind, G, kv_offset, kv_len, causal, keys_per_split;
+  float scale_log2;
+};
+
 struct MergeParams {
   const float* part_o;
   const float* part_lse;
@@ -60,6 +76,7 @@ struct MergeParams {
   int64_t g_sb, g_sh, g_sr;
   int64_t o_sb, o_sh, o_sr;
   int n_chunks, B, Hq, rows;
+  RepairParams fix;
 };
 
 struct AppendParams {

@@ -230,17 +230,23 @@ def merge(o_parts, lse_parts, gate):
     """Combine chunk partials: out = sum_c exp(lse_c - lse) o_c * sigmoid(gate).
 
     lse = log sum_c exp(lse_c); chunks with lse_c = -Inf contribute nothing and a
-    row whose chunks are all empty gives 0.  o_parts [C, ...] float, lse_parts [C, ...].
+    row whose chunks are all empty gives 0.  A chunk whose lse_c is NaN (its keys
+    held a NaN score, or +Inf) makes the row NaN, as the unsplit definition does.
+    o_parts [C, ...] float, lse_parts [C, ...].
     """
     o_parts = np.asarray(o_parts, dtype=np.float64)
     lse_parts = np.asarray(lse_parts, dtype=np.float64)
-    top = lse_parts.max(axis=0)
+    nan_row = np.isnan(lse_parts).any(axis=0)
+    fin = np.isfinite(lse_parts)
+    top = np.where(fin, lse_parts, -np.inf).max(axis=0)
     has = np.isfinite(top)
     top_safe = np.where(has, top, 0.0)
-    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - top_safe[None]), 0.0)
+    w = np.where(fin, np.exp(np.where(fin, lse_parts, 0.0) - top_safe[None]), 0.0)
     total = w.sum(axis=0)
-    o = (w[..., None] * o_parts).sum(axis=0) / np.where(has, total, 1.0)[..., None]
+    with np.errstate(invalid="ignore"):
+        o = (w[..., None] * o_parts).sum(axis=0) / np.where(has, total, 1.0)[..., None]
     o = np.where(has[..., None], o, 0.0)
+    o = np.where(nan_row[..., None], np.nan, o)
     return o * sigmoid(gate) if gate is not None else o
 
 

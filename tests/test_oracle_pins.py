@@ -201,6 +201,27 @@ def test_split_and_merge_equals_unsplit(chunks):
     assert _rel(merged, full) <= 1e-13
 
 
+def test_split_and_merge_keeps_nonfinite_classes():
+    # a +Inf key score in one chunk (NaN rows in the unsplit definition: exp(Inf - Inf)) and a
+    # +Inf in V at a visible key (+Inf in that dim): the merge of the chunk partials gives the
+    # classes of the unsplit result, and its finite values
+    q, k, v, g, kv_len = _tiny(12, 1, 4, 2, 6, 24)
+    k = k.copy()
+    v = v.copy()
+    k[0, 0, 10, 0] = np.inf
+    q[0, 0:2, :, 0] = np.abs(q[0, 0:2, :, 0]) + 0.5   # heads 0 and 1 see s = +Inf at key 10
+    v[0, 1, 5, 3] = np.inf
+    full = reference.attention(q, k, v, g, n_kv_heads=2, kv_offset=24, kv_len=kv_len)
+    assert np.isnan(full[0, 0:2]).all() and np.isposinf(full[0, 2:4, :, 3]).all()
+    for chunks in ([(0, 7), (7, 19), (19, 30)], [(0, 11), (11, 30)]):
+        o, l_ = reference.partials(q, k, v, n_kv_heads=2, kv_offset=24, kv_len=kv_len, chunks=chunks)
+        merged = reference.merge(o, l_, g)
+        fin = np.isfinite(full)
+        assert np.array_equal(np.isnan(merged), np.isnan(full))
+        assert np.array_equal(merged[~fin & ~np.isnan(full)], full[~fin & ~np.isnan(full)])
+        assert np.max(np.abs(merged[fin] - full[fin])) <= 1e-12
+
+
 def test_merge_of_empty_chunks_is_zero():
     o = np.zeros((3, 1, 1, 2, 4))
     l_ = np.full((3, 1, 1, 2), -np.inf)
