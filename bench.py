@@ -216,6 +216,7 @@ def main():
     # time the host.  Here a spin kernel holds the stream while the host enqueues n_dev calls
     # back to back, and events around them time the device alone.
     n_dev = 48
+    held = [True]  # every timed batch was enqueued while the spin kernel still held the stream
 
     def device_timed(fn):
         t0 = time.perf_counter()
@@ -230,7 +231,7 @@ def main():
         cyc_per_ms = 1_000_000 / a_.elapsed_time(b_)
         hold_ms = max(20.0, 3e3 * host_s * n_dev)
         out_us = []
-        for _ in range(3):
+        while len(out_us) < 3:
             torch.cuda._sleep(int(hold_ms * cyc_per_ms))
             s_, e_ = E(enable_timing=True), E(enable_timing=True)
             t1 = time.perf_counter()
@@ -240,8 +241,12 @@ def main():
             e_.record(stream)
             enq_ms = (time.perf_counter() - t1) * 1e3
             torch.cuda.synchronize(dev)
-            if enq_ms >= hold_ms:
-                raise RuntimeError(f"host enqueue ({enq_ms:.1f} ms) outlasted the hold ({hold_ms:.1f} ms)")
+            if enq_ms >= hold_ms and hold_ms < 2000.0:  # the host caught up: hold longer, time again
+                hold_ms *= 4
+                continue
+            # (under a profiler that serialises dispatches the host always catches up; such a run
+            # is flagged in device_timed and its figures are not device times)
+            held[0] = held[0] and enq_ms < hold_ms
             out_us.append(s_.elapsed_time(e_) / n_dev * 1e3)
         return float(np.median(out_us))
 
@@ -308,7 +313,7 @@ def main():
                              "device time of attn_decode: main pass + merge)",
                    "value": round(float(dec_gbs), 1), "unit": "GB/s", "us": round(dec_dev_us, 2),
                    "bytes": int(dec_bytes), "distinct_caches": n_rot,
-                   "step_with_append_us": round(dec_step_us, 2),
+                   "step_with_append_us": round(dec_step_us, 2), "device_timed": held[0],
                    "host_bound_call_us": round(float(np.median(dec_us)), 2),
                    "mall_warm_gbs": round(float(warm_gbs), 1), "mall_warm_us": round(warm_dev_us, 2),
                    "roofline": {"bound": "hbm", "achieved": round(float(dec_gbs), 1), "peak": PEAK_HBM_GBS,
