@@ -13,10 +13,14 @@ One step = one pass of the whole path over one batch of synthetic input:
   3. verify: 32 verify rows of the same shape at offset 32768 with a broadcast additive tree
      mask (the head-chunked verify): kv_append, then attn_decode.
 Inputs are resident in HBM before timing starts.  Events on the stream the kernels run on
-bracket each part of every step.  A decode or verify call takes the host (Python, ctypes)
-longer to issue than the GPU takes to run it, so their figures come from a second measurement
-after the step loop: a spin kernel holds the stream while the host enqueues 48 calls back to
-back (rotating over the cold caches), and events around those calls time the device alone.
+bracket each part of every step; torch's spin kernel holds the stream before the timed steps
+so that the host is ahead of the device when they start.  A decode or verify call takes the
+host (Python, ctypes) longer to issue than the GPU takes to run it, so their figures come from
+a second measurement after the step loop: the spin kernel holds the stream while the host
+enqueues 48 calls back to back (rotating over the cold caches), and events around those calls
+time the device alone.  The same prompt is also run in query blocks of 128 (kv_append +
+attn_prefill per block, enqueued under a hold, events around the loop) and reported beside the
+512-row figure with its workspace bytes.
 
 value = prefill attention TFLOP/s over the 32k prompt (algorithmic flops: 4 * 256 per
 admissible (head, row, key) triple: 4*256*24*32768*32769/2 = 1.3195e13 per prompt).
@@ -189,8 +193,23 @@ def main():
         verify_pass(w)
     torch.cuda.synchronize(dev)
 
-    K = args.steps
+    # torch's spin kernel: cycles per millisecond, and the host time of one step, so that a hold
+    # of the stream can let the host get ahead of the device before a timed region starts
     E = torch.cuda.Event
+    c0_, c1_ = E(enable_timing=True), E(enable_timing=True)
+    c0_.record(stream)
+    torch.cuda._sleep(1_000_000)
+    c1_.record(stream)
+    torch.cuda.synchronize(dev)
+    cyc_per_ms = 1_000_000 / c0_.elapsed_time(c1_)
+    t0 = time.perf_counter()
+    prefill_pass()
+    decode_pass(0)
+    verify_pass(0)
+    step_host_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize(dev)
+
+    K = args.steps
     ev = [[E(enable_timing=True) for _ in range(4)] for _ in range(K)]
     dec_ev = [[E(enable_timing=True), E(enable_timing=True)] for _ in range(K)]
     ver_ev = [[E(enable_timing=True), E(enable_timing=True)] for _ in range(K)]
@@ -199,6 +218,7 @@ def main():
     torch.cuda.synchronize(dev)
     start = E(enable_timing=True)
     end = E(enable_timing=True)
+    torch.cuda._sleep(int(min(step_host_ms * K, 2000.0) * cyc_per_ms))  # the host gets ahead
     start.record(stream)
     for it in range(K):
         ev[it][0].record(stream)
@@ -223,12 +243,6 @@ def main():
         fn(0)
         torch.cuda.synchronize(dev)
         host_s = (time.perf_counter() - t0)
-        a_, b_ = E(enable_timing=True), E(enable_timing=True)
-        a_.record(stream)
-        torch.cuda._sleep(1_000_000)
-        b_.record(stream)
-        torch.cuda.synchronize(dev)
-        cyc_per_ms = 1_000_000 / a_.elapsed_time(b_)
         hold_ms = max(20.0, 3e3 * host_s * n_dev)
         out_us = []
         while len(out_us) < 3:
@@ -262,6 +276,39 @@ def main():
     def ver_call(i):
         kk_, vv_ = caches[i % n_rot]
         ga.decode(vq, kk_, vv_, vg, kv_offset=voff, mask=vmask, out=vout, workspace=vws)
+
+    # the same 32k prompt in query blocks of the other size (qL 128 when the step uses 512):
+    # kv_append + attn_prefill per block, events around the whole loop
+    qL2 = 128 if qL != 128 else 512
+    ws2_need = max(ga.workspace_bytes(ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=min(qL2, N - s), kv_offset=s, capacity=N),
+                                      0) for s in range(0, N, qL2))
+    ws2 = torch.empty(max(ws2_need, 16), dtype=torch.uint8, device=dev)
+
+    def prefill_pass2():
+        for s in range(0, N, qL2):
+            e = min(s + qL2, N)
+            ga.kv_append(k[:, :, s:e], v[:, :, s:e], kc, vc, kv_offset=s)
+            ga.prefill(q[:, :, s:e], kc, vc, g[:, :, s:e], kv_offset=s, kv_len=e, out=out[:, :, s:e], workspace=ws2)
+
+    t0 = time.perf_counter()
+    prefill_pass2()
+    torch.cuda.synchronize(dev)
+    hold2_ms = max(20.0, 2e3 * (time.perf_counter() - t0))
+    p2_ms = []
+    while len(p2_ms) < max(2, K // 2):
+        torch.cuda._sleep(int(hold2_ms * cyc_per_ms))  # the host enqueues the loop while the stream is held
+        a2, b2 = E(enable_timing=True), E(enable_timing=True)
+        t1 = time.perf_counter()
+        a2.record(stream)
+        prefill_pass2()
+        b2.record(stream)
+        enq_ms = (time.perf_counter() - t1) * 1e3
+        torch.cuda.synchronize(dev)
+        if enq_ms >= hold2_ms and hold2_ms < 2000.0:
+            hold2_ms *= 4
+            continue
+        held[0] = held[0] and enq_ms < hold2_ms
+        p2_ms.append(a2.elapsed_time(b2))
 
     dec_dev_us = device_timed(dec_call)
     warm_dev_us = device_timed(lambda i: dec_call(i, cold=False))
@@ -309,6 +356,10 @@ def main():
                     "workspace_bytes": int(ws_need),
                     "plan_last_block": {kk: plans[-1][kk] for kk in ("variant_name", "n_splits", "keys_per_split",
                                                                      "n_row_tiles", "grid_blocks")}},
+        f"prefill_q_block_{qL2}": {"ms": round(float(np.median(p2_ms)), 4),
+                                   "tflops": round(float(flops / (np.median(p2_ms) * 1e-3) / 1e12), 2),
+                                   "calls": len(range(0, N, qL2)), "workspace_bytes": int(ws2_need),
+                                   "timing": "events around the block loop (kv_append + attn_prefill per block)"},
         "decode": {"metric": "decode KV GB/s (35B-A3B shape, batch 2, 1 row at offset 32768, cold KV; "
                              "device time of attn_decode: main pass + merge)",
                    "value": round(float(dec_gbs), 1), "unit": "GB/s", "us": round(dec_dev_us, 2),

@@ -121,16 +121,17 @@ __device__ __forceinline__ void exact_row(const RepairParams& f, int b, int h, i
 // whether any of the four values is NaN
 __device__ __forceinline__ bool has_nan4(const f32x4& x) { return __builtin_isnan(x[0] + x[1] + x[2] + x[3]); }
 
-// Many chunks (decode): one workgroup of kMergeWaves wavefronts per row; wavefront w takes the
-// chunks w, w + kMergeWaves, ... (kMergeBatch per pass).  A pass issues all of its lse and
-// partial loads (and the gate) at once; only the row's largest lse crosses the wavefronts
-// (through LDS) before the weights are applied, so a row up to kMergeWaves x kMergeBatch
-// chunks costs one round trip to memory.  The partial sums meet in LDS.
-constexpr int kMergeWaves = 16;
+// Many chunks: one workgroup of MW wavefronts per row (MW = 4, 8 or 16, the fewest whose
+// MW x kMergeBatch slots hold the chunks, up to 16); wavefront w takes the chunks w, w + MW, ...
+// (kMergeBatch per pass).  A pass issues all of its lse and partial loads (and the gate) at
+// once; only the row's largest lse crosses the wavefronts (through LDS) before the weights are
+// applied, so a row up to MW x kMergeBatch chunks costs one round trip to memory.  The partial
+// sums meet in LDS.
 constexpr int kMergeBatch = 4;
 
-template <int DT>
-__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergeParams p) {
+template <int DT, int MW>
+__global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
+  constexpr int kMergeWaves = MW;
   __shared__ f32x4 part_acc[kMergeWaves][64];
   __shared__ float part_w[kMergeWaves];
   __shared__ float part_top[kMergeWaves];
@@ -363,8 +364,17 @@ hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
     else hipLaunchKernelGGL(merge_few_kernel<1>, grid, dim3(256), 0, stream, p);
   } else {
     const dim3 grid((unsigned)n_rows);
-    if (dtype == 0) hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(kMergeWaves * 64), 0, stream, p);
-    else hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(kMergeWaves * 64), 0, stream, p);
+    const int mw = p.n_chunks <= 4 * kMergeBatch ? 4 : p.n_chunks <= 8 * kMergeBatch ? 8 : 16;
+    if (mw == 4) {
+      if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 4>), grid, dim3(4 * 64), 0, stream, p);
+      else hipLaunchKernelGGL((merge_kernel<1, 4>), grid, dim3(4 * 64), 0, stream, p);
+    } else if (mw == 8) {
+      if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 8>), grid, dim3(8 * 64), 0, stream, p);
+      else hipLaunchKernelGGL((merge_kernel<1, 8>), grid, dim3(8 * 64), 0, stream, p);
+    } else {
+      if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 16>), grid, dim3(16 * 64), 0, stream, p);
+      else hipLaunchKernelGGL((merge_kernel<1, 16>), grid, dim3(16 * 64), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

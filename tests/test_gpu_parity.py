@@ -300,7 +300,8 @@ def test_kv_keep_is_bit_exact(dtype):
 
 
 @needs_gpu
-@pytest.mark.parametrize("n_chunks", [4, 12, 100])  # few-chunk pass; many-chunk pass in one and in two rounds
+# few-chunk pass; many-chunk pass with 4, 8 and 16 wavefronts per row, in one round and in two
+@pytest.mark.parametrize("n_chunks", [4, 12, 21, 40, 100])
 def test_merge_matches_oracle(n_chunks):
     rng = syn.streams(8)
     B, Hq, Hkv, rows, kv = 1, 8, 2, 5, 90
