@@ -296,23 +296,24 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   *reinterpret_cast<u32x2*>(orow + d0) = ow;
 }
 
-// One 16-byte chunk per thread: (tensor, b, g, r, chunk of 8 elements).
+// One 16-byte chunk per thread.  Workgroup row y = (tensor, b, g); x runs over (row r, chunk c
+// of 8 elements) = 32 r + c, so the index arithmetic is shifts (one division per workgroup row).
 __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
-  const int64_t per_tensor = (int64_t)p.B * p.Hkv * p.rows * (kHeadDim / 8);
-  const int64_t total = 2 * per_tensor;
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
-       u += (int64_t)gridDim.x * blockDim.x) {
-    const int t = u >= per_tensor;
-    int64_t v = u - t * per_tensor;
-    const int c = (int)(v % (kHeadDim / 8));
-    v /= kHeadDim / 8;
-    const int r = (int)(v % p.rows);
-    v /= p.rows;
-    const int g = (int)(v % p.Hkv);
-    const int b = (int)(v / p.Hkv);
-    const u32x4 val = *reinterpret_cast<const u32x4*>(p.src[t] + b * p.s_sb[t] + g * p.s_sh[t] + r * p.s_sr[t] + 8 * c);
-    *reinterpret_cast<u32x4*>(p.dst[t] + b * p.d_sb[t] + g * p.d_sh[t] + (int64_t)(p.kv_offset + r) * p.d_st[t] +
-                              8 * c) = val;
+  const int64_t bg = (int64_t)p.B * p.Hkv;
+  const int64_t n = (int64_t)p.rows * (kHeadDim / 8);
+  for (int64_t y = blockIdx.y; y < 2 * bg; y += gridDim.y) {
+    const int t = y >= bg;
+    const int64_t yb = y - (t ? bg : 0);
+    const int b = (int)(yb / p.Hkv), g = (int)(yb - (int64_t)b * p.Hkv);
+    const uint16_t* src = p.src[t] + b * p.s_sb[t] + g * p.s_sh[t];
+    uint16_t* dst = p.dst[t] + b * p.d_sb[t] + g * p.d_sh[t] + (int64_t)p.kv_offset * p.d_st[t];
+    const int64_t s_sr = p.s_sr[t], d_st = p.d_st[t];
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < n; u += (int64_t)gridDim.x * 256) {
+      const int64_t r = u >> 5;
+      const int c = (int)(u & 31);
+      const u32x4 val = *reinterpret_cast<const u32x4*>(src + r * s_sr + 8 * c);
+      *reinterpret_cast<u32x4*>(dst + r * d_st + 8 * c) = val;
+    }
   }
 }
 
@@ -380,10 +381,11 @@ hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
 }
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-  const int64_t total = 2LL * p.B * p.Hkv * p.rows * (kHeadDim / 8);
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  int64_t bx = ((int64_t)p.rows * (kHeadDim / 8) + 255) / 256;
+  if (bx > 1024) bx = 1024;
+  int64_t by = 2LL * p.B * p.Hkv;
+  if (by > 65535) by = 65535;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)bx, (unsigned)by), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -271,6 +271,22 @@ def test_kv_append_is_bit_exact():
     with pytest.raises(ga.AttnError):
         ga.kv_append(to_dev(new_k), to_dev(new_v), kc, vc, kv_offset=16)
 
+@needs_gpu
+@pytest.mark.parametrize("B,Hkv,rows,offset", [(3, 5, 300, 40), (1, 4, 512, 0), (2, 2, 1, 777)])
+def test_kv_append_of_prompt_views(B, Hkv, rows, offset):
+    # the new rows are a view of a longer prompt tensor (row stride 256, head stride 256 x its
+    # length), as when a prompt is appended block by block; several row blocks and (b, g) pairs
+    rng = syn.streams(6 + rows)
+    big = syn.normal_bits(rng["k"], (B, Hkv, rows + 70, 256))
+    bigv = syn.normal_bits(rng["v"], (B, Hkv, rows + 70, 256))
+    cache = syn.normal_bits(rng["plant"], (B, Hkv, offset + rows + 9, 256))
+    kc, vc = to_dev(cache), to_dev(cache)
+    k, v = to_dev(big), to_dev(bigv)
+    ga.kv_append(k[:, :, 33:33 + rows], v[:, :, 33:33 + rows], kc, vc, kv_offset=offset)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kc), reference.kv_append(cache, big[:, :, 33:33 + rows], offset))
+    assert np.array_equal(to_bits(vc), reference.kv_append(cache, bigv[:, :, 33:33 + rows], offset))
+
 
 @needs_gpu
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
