@@ -20,7 +20,8 @@ a second measurement after the step loop: the spin kernel holds the stream while
 enqueues 48 calls back to back (rotating over the cold caches), and events around those calls
 time the device alone.  The same prompt is also run in query blocks of 128 (kv_append +
 attn_prefill per block, enqueued under a hold, events around the loop) and reported beside the
-512-row figure with its workspace bytes.
+512-row figure with its workspace bytes, and through the composed (materialised-score) route
+at both block sizes for comparison (prefill_composed: time and transient workspace bytes).
 
 value = prefill attention TFLOP/s over the 32k prompt (algorithmic flops: 4 * 256 per
 admissible (head, row, key) triple: 4*256*24*32768*32769/2 = 1.3195e13 per prompt).
@@ -94,6 +95,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=480)
     ap.add_argument("--copy-calibration", type=int, default=0)
+    ap.add_argument("--no-composed", action="store_true", help="skip the composed-route comparison")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path has no multi-GPU part"}))
@@ -310,6 +312,39 @@ def main():
         held[0] = held[0] and enq_ms < hold2_ms
         p2_ms.append(a2.elapsed_time(b2))
 
+    # the composed (materialised-score) route on the same prompt, at both block sizes: the
+    # comparison arm, kv_append + attn_prefill_composed per block, enqueued under a hold
+    comp = {}
+    if not args.no_composed:
+        for qb_ in (512, 128):
+            need = max(ga.workspace_bytes(ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=min(qb_, N - s), kv_offset=s,
+                                                       capacity=N), 2) for s in range(0, N, qb_))
+            wsc = torch.empty(need, dtype=torch.uint8, device=dev)
+
+            def comp_pass():
+                for s in range(0, N, qb_):
+                    e = min(s + qb_, N)
+                    ga.kv_append(k[:, :, s:e], v[:, :, s:e], kc, vc, kv_offset=s)
+                    ga.prefill_composed(q[:, :, s:e], kc, vc, g[:, :, s:e], kv_offset=s, kv_len=e,
+                                        out=out[:, :, s:e], workspace=wsc)
+
+            comp_pass()
+            torch.cuda.synchronize(dev)
+            cms = []
+            for _ in range(2):
+                torch.cuda._sleep(int(50.0 * cyc_per_ms))
+                a3, b3 = E(enable_timing=True), E(enable_timing=True)
+                a3.record(stream)
+                comp_pass()
+                b3.record(stream)
+                torch.cuda.synchronize(dev)
+                cms.append(a3.elapsed_time(b3))
+            comp[qb_] = {"ms": round(float(np.median(cms)), 3),
+                         "tflops": round(float(prefill_flops(Hq, N) / (np.median(cms) * 1e-3) / 1e12), 2),
+                         "workspace_bytes": int(need), "calls": len(range(0, N, qb_))}
+            del wsc
+            torch.cuda.empty_cache()
+
     dec_dev_us = device_timed(dec_call)
     warm_dev_us = device_timed(lambda i: dec_call(i, cold=False))
     dec_step_us = device_timed(dec_step)
@@ -357,9 +392,12 @@ def main():
                     "plan_last_block": {kk: plans[-1][kk] for kk in ("variant_name", "n_splits", "keys_per_split",
                                                                      "n_row_tiles", "grid_blocks")}},
         f"prefill_q_block_{qL2}": {"ms": round(float(np.median(p2_ms)), 4),
-                                   "tflops": round(float(flops / (np.median(p2_ms) * 1e-3) / 1e12), 2),
+                                   "tflops": round(float(prefill_flops(Hq, N) / (np.median(p2_ms) * 1e-3) / 1e12), 2),
                                    "calls": len(range(0, N, qL2)), "workspace_bytes": int(ws2_need),
                                    "timing": "events around the block loop (kv_append + attn_prefill per block)"},
+        "prefill_composed": {"route": "materialised scores: fp32 Q K^T, row softmax to 16-bit weights, P V + gate "
+                                      "(attn_prefill_composed), kv_append per block; events around the block loop",
+                             **{f"q_block_{kk}": vv for kk, vv in comp.items()}},
         "decode": {"metric": "decode KV GB/s (35B-A3B shape, batch 2, 1 row at offset 32768, cold KV; "
                              "device time of attn_decode: main pass + merge)",
                    "value": round(float(dec_gbs), 1), "unit": "GB/s", "us": round(dec_dev_us, 2),

@@ -17,7 +17,7 @@ import torch
 from . import _abi
 
 __all__ = [
-    "AttnError", "lib", "prefill", "prefill_partials", "decode", "kv_append", "kv_keep", "merge", "head_chunk_plan",
+    "AttnError", "lib", "prefill", "prefill_partials", "prefill_composed", "decode", "kv_append", "kv_keep", "merge", "head_chunk_plan",
     "workspace_bytes",
     "describe_plan", "plan_args", "variant_name", "prompt_prefill",
 ]
@@ -129,7 +129,8 @@ def _run(op: int, q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, cau
         workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    fn = L.attn_prefill if op == _abi.OP_PREFILL else L.attn_decode
+    fn = {_abi.OP_PREFILL: L.attn_prefill, _abi.OP_DECODE: L.attn_decode,
+          _abi.OP_COMPOSED: L.attn_prefill_composed}[op]
     _check(fn(C.byref(a), ws_ptr, ws_len, _stream_handle(q)))
     return out
 
@@ -172,6 +173,15 @@ def decode(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=Tru
     """attn_decode: 1..32 rows; head_chunk 0 = the policy, k = chunks of k heads."""
     return _run(_abi.OP_DECODE, q, k_cache, v_cache, gate, kv_offset=kv_offset, kv_len=kv_len, causal=causal,
                 scale=scale, head_chunk=head_chunk, n_splits=n_splits, mask=mask, out=out, workspace=workspace)
+
+
+def prefill_composed(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, out=None,
+                     workspace=None):
+    """attn_prefill_composed: the composed (materialised-score) route for the same block, for
+    comparison with attn_prefill; no mask.  workspace: a uint8 device tensor of at least
+    workspace_bytes(args, OP_COMPOSED) bytes (allocated here when None)."""
+    return _run(_abi.OP_COMPOSED, q, k_cache, v_cache, gate, kv_offset=kv_offset, kv_len=kv_len, causal=causal,
+                scale=scale, out=out, workspace=workspace)
 
 
 def kv_append(k_new, v_new, k_cache, v_cache, *, kv_offset: int) -> None:
@@ -290,8 +300,9 @@ def variant_name(variant: int) -> str:
 
 
 def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int, kv_offset: int = 0, out=None, workspace=None,
-                   head_chunk=0, n_splits=0, overlap_merge=False):
-    """A prompt in query blocks: for each block, kv_append its K/V rows, then attn_prefill it.
+                   head_chunk=0, n_splits=0, overlap_merge=False, composed=False):
+    """A prompt in query blocks: for each block, kv_append its K/V rows, then attn_prefill it
+    (attn_prefill_composed with composed=True).
 
     q/gate [B, Hq, N, 256] and k/v [B, Hkv, N, 256] hold the prompt (positions kv_offset ..
     kv_offset + N - 1); k_cache/v_cache have room for them.  Block i attends to the cache plus
@@ -302,6 +313,15 @@ def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int, kv_offset: 
     N = q.shape[2]
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if composed:
+        if overlap_merge:
+            raise ValueError("the composed route has no merge to overlap")
+        for s in range(0, N, q_block):
+            e = min(s + q_block, N)
+            kv_append(k[:, :, s:e], v[:, :, s:e], k_cache, v_cache, kv_offset=kv_offset + s)
+            prefill_composed(q[:, :, s:e], k_cache, v_cache, gate[:, :, s:e], kv_offset=kv_offset + s,
+                             kv_len=kv_offset + e, out=out[:, :, s:e], workspace=workspace)
+        return out
     if workspace is None:
         need = 0
         for s in range(0, N, q_block):

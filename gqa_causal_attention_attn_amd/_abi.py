@@ -7,7 +7,7 @@ The struct sizes are checked against the library's own (attn_struct_size) when i
 import ctypes as C
 import os
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 HEAD_DIM = 256
 MAX_DECODE_ROWS = 32
 MAX_CHUNKS = 64
@@ -22,12 +22,12 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 
 BF16, F16 = 0, 1
 MASK_NONE, MASK_BOOL_U8, MASK_ADD, MASK_ADD_F32 = 0, 1, 2, 3
-OP_PREFILL, OP_DECODE = 0, 1
+OP_PREFILL, OP_DECODE, OP_COMPOSED = 0, 1, 2
 
 EXPORTS = (
     "attn_abi_version", "attn_struct_size", "attn_strerror", "attn_variant_name", "attn_head_chunk_plan",
     "attn_workspace_bytes", "attn_describe_plan", "attn_prefill", "attn_decode", "kv_append", "attn_merge",
-    "kv_keep", "attn_prefill_partials",
+    "kv_keep", "attn_prefill_partials", "attn_prefill_composed",
 )
 KEEP_MAX_BATCH = 64
 
@@ -99,7 +99,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.attn_workspace_bytes.argtypes = [P(AttnArgs), C.c_int, P(C.c_size_t)]
     lib.attn_describe_plan.restype = C.c_int
     lib.attn_describe_plan.argtypes = [P(AttnArgs), C.c_int, P(PlanInfo)]
-    for name in ("attn_prefill", "attn_decode"):
+    for name in ("attn_prefill", "attn_decode", "attn_prefill_composed"):
         fn = getattr(lib, name)
         fn.restype = C.c_int
         fn.argtypes = [P(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p]

@@ -63,7 +63,7 @@ int chunk_rule(int rows, int gqa, int enabled, int* sizes, int cap) {
 
 int validate(const attn_args* a, int op) {
   if (!a) return ATTN_E_NULL;
-  if (op != ATTN_OP_PREFILL && op != ATTN_OP_DECODE) return ATTN_E_ARG;
+  if (op != ATTN_OP_PREFILL && op != ATTN_OP_DECODE && op != ATTN_OP_COMPOSED) return ATTN_E_ARG;
   if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
   if (a->B <= 0 || a->Hq <= 0 || a->Hkv <= 0) return ATTN_E_HEADS;
   if (a->Hq % a->Hkv != 0) return ATTN_E_HEADS;
@@ -92,7 +92,30 @@ int validate(const attn_args* a, int op) {
     if (m.Hm != 1 && m.Hm != a->Hq) return ATTN_E_MASK;
     if (m.stride_b < 0 || m.stride_h < 0 || m.stride_row < 0) return ATTN_E_MASK;
   }
+  if (op == ATTN_OP_COMPOSED) {
+    if (m.kind != ATTN_MASK_NONE) return ATTN_E_MASK;
+    if ((int64_t)a->B * a->Hq > 65535 || (int64_t)a->B * a->Hq * a->rows > (int64_t)INT32_MAX) return ATTN_E_ARG;
+  }
   return ATTN_OK;
+}
+
+// Workspace of the composed arm: scores (fp32), weights (16-bit), 1 / l; each part 256-aligned.
+struct ComposedLayout {
+  int64_t kv_hi, kvp;
+  size_t s_bytes, p_bytes, l_bytes;
+};
+
+inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+ComposedLayout composed_layout(const attn_args* a) {
+  ComposedLayout L;
+  L.kv_hi = a->causal ? (a->kv_len < a->kv_offset + a->rows ? a->kv_len : a->kv_offset + a->rows) : a->kv_len;
+  L.kvp = cdiv(L.kv_hi, kKeysPerTile) * kKeysPerTile;
+  const int64_t n = (int64_t)a->B * a->Hq * a->rows;
+  L.s_bytes = round256((size_t)n * L.kvp * 4);
+  L.p_bytes = round256((size_t)n * L.kvp * 2);
+  L.l_bytes = round256((size_t)n * 4);
+  return L;
 }
 
 int make_plan(const attn_args* a, int op, Plan* P) {
@@ -323,6 +346,11 @@ int attn_workspace_bytes(const attn_args* a, int op, size_t* bytes) {
   if (!bytes) return ATTN_E_NULL;
   int st = validate(a, op);
   if (st) return st;
+  if (op == ATTN_OP_COMPOSED) {
+    const ComposedLayout L = composed_layout(a);
+    *bytes = L.s_bytes + L.p_bytes + L.l_bytes;
+    return ATTN_OK;
+  }
   Plan P;
   st = make_plan(a, op, &P);
   if (st) return st;
@@ -332,6 +360,7 @@ int attn_workspace_bytes(const attn_args* a, int op, size_t* bytes) {
 
 int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
   if (!info) return ATTN_E_NULL;
+  if (op == ATTN_OP_COMPOSED) return ATTN_E_ARG;
   int st = validate(a, op);
   if (st) return st;
   Plan P;
@@ -368,6 +397,37 @@ int attn_prefill_partials(const attn_args* a, void* workspace, size_t ws_bytes, 
 
 int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stream) {
   return run_fwd(a, ATTN_OP_DECODE, workspace, ws_bytes, stream);
+}
+
+int attn_prefill_composed(const attn_args* a, void* workspace, size_t ws_bytes, void* stream) {
+  int st = validate(a, ATTN_OP_COMPOSED);
+  if (st) return st;
+  const ComposedLayout L = composed_layout(a);
+  if (!workspace || ws_bytes < L.s_bytes + L.p_bytes + L.l_bytes) return ATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_E_LAYOUT;
+  gqa::ComposedParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = static_cast<const uint16_t*>(a->q.ptr);
+  p.k = static_cast<const uint16_t*>(a->k_cache.ptr);
+  p.v = static_cast<const uint16_t*>(a->v_cache.ptr);
+  p.gate = static_cast<const uint16_t*>(a->gate.ptr);
+  p.out = static_cast<uint16_t*>(a->out.ptr);
+  p.q_sb = a->q.stride_b, p.q_sh = a->q.stride_h, p.q_sr = a->q.stride_row;
+  p.k_sb = a->k_cache.stride_b, p.k_sh = a->k_cache.stride_h, p.k_st = a->k_cache.stride_row;
+  p.v_sb = a->v_cache.stride_b, p.v_sh = a->v_cache.stride_h, p.v_st = a->v_cache.stride_row;
+  p.g_sb = a->gate.stride_b, p.g_sh = a->gate.stride_h, p.g_sr = a->gate.stride_row;
+  p.o_sb = a->out.stride_b, p.o_sh = a->out.stride_h, p.o_sr = a->out.stride_row;
+  char* ws = static_cast<char*>(workspace);
+  p.s = reinterpret_cast<float*>(ws);
+  p.pw = reinterpret_cast<uint16_t*>(ws + L.s_bytes);
+  p.inv_l = reinterpret_cast<float*>(ws + L.s_bytes + L.p_bytes);
+  p.kvp = L.kvp;
+  p.B = a->B, p.Hq = a->Hq, p.G = a->Hq / a->Hkv, p.rows = a->rows;
+  p.kv_offset = (int)a->kv_offset, p.kv_len = (int)a->kv_len, p.causal = a->causal, p.kv_hi = (int)L.kv_hi;
+  const float scale = a->scale > 0.0f ? a->scale : 1.0f / 16.0f;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  if (gqa::launch_composed(p, a->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
 }
 
 int kv_append(const kv_append_args* a, void* stream) {

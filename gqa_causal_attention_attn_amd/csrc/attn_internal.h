@@ -97,11 +97,33 @@ struct KeepParams {
   uint32_t keep[kKeepMaxBatch];
 };
 
+// Parameters of the composed (materialised-score) arm: the fused pass's inputs plus the
+// workspace of scores s, 16-bit weights pw (both [B, Hq, rows, kvp]) and 1 / l per row.
+struct ComposedParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* gate;
+  uint16_t* out;
+  int64_t q_sb, q_sh, q_sr;
+  int64_t k_sb, k_sh, k_st;
+  int64_t v_sb, v_sh, v_st;
+  int64_t g_sb, g_sh, g_sr;
+  int64_t o_sb, o_sh, o_sr;
+  float* s;
+  uint16_t* pw;
+  float* inv_l;
+  int64_t kvp;  // keys per row of s and pw: the key range rounded up to 32
+  int B, Hq, G, rows, kv_offset, kv_len, causal, kv_hi;
+  float scale_log2;
+};
+
 // Launchers (return hipGetLastError()).  dtype 0 = bf16, 1 = fp16; mask_kind as attn_mask_kind.
 // shape: 0 = 4 wavefronts x 1 column block, 1 = 4 x 2, 2 = 8 x 1 (wavefronts x blocks each)
 hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_keep(const KeepParams& p, int B, hipStream_t stream);
+hipError_t launch_composed(const ComposedParams& p, int dtype, hipStream_t stream);
 
 }  // namespace gqa

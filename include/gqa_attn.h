@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GQA_ATTN_ABI_VERSION 2
+#define GQA_ATTN_ABI_VERSION 3
 #define ATTN_HEAD_DIM 256
 #define ATTN_MAX_DECODE_ROWS 32
 #define ATTN_MAX_CHUNKS 64
@@ -76,7 +76,7 @@ typedef enum {
   ATTN_MASK_ADD_F32 = 3   /* float32 additive */
 } attn_mask_kind;
 
-typedef enum { ATTN_OP_PREFILL = 0, ATTN_OP_DECODE = 1 } attn_op;
+typedef enum { ATTN_OP_PREFILL = 0, ATTN_OP_DECODE = 1, ATTN_OP_COMPOSED = 2 } attn_op;
 
 /* A strided 4-d tensor [B, H, rows_or_tokens, 256]; strides in elements. */
 typedef struct {
@@ -215,18 +215,23 @@ const char* attn_variant_name(int variant);
 int attn_head_chunk_plan(int rows, int n_q_heads, int n_kv_heads, int enabled, int* sizes, int cap,
                          int* n_chunks);
 
-/* Workspace bytes a call with these arguments needs (0 when it needs none).  op is attn_op.
- * Validates `a` like the call itself would.  No device use. */
+/* Workspace bytes a call with these arguments needs (0 when it needs none).  op is attn_op
+ * (ATTN_OP_COMPOSED: attn_prefill_composed).  Validates `a` like the call itself would.  No
+ * device use. */
 int attn_workspace_bytes(const attn_args* a, int op, size_t* bytes);
 
-/* The resolved plan of a call with these arguments.  No device use. */
+/* The resolved plan of a call with these arguments (op ATTN_OP_PREFILL or ATTN_OP_DECODE;
+ * ATTN_E_ARG otherwise).  No device use. */
 int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info);
 
 /* Gated causal GQA attention for a block of query rows (any rows >= 1): the flash-style
- * pass over the cache in 64-key tiles, split over KV when the grid would be too small, the
+ * pass over the cache in 32-key tiles, split over KV when the grid would be too small, the
  * log-sum-exp merge of the splits and the gate.  `workspace` (device, >= the bytes
  * attn_workspace_bytes(a, ATTN_OP_PREFILL) reports; may be NULL if that is 0) holds the
- * split partials.  Writes a->out. */
+ * split partials.  Writes a->out.  Keys a row cannot see never reach it, also when their
+ * V (or K) rows hold +-Inf or NaN (TensorFold PR #1009: -Inf times a zero probability must
+ * not become NaN): a pair whose result came out NaN is computed again over its admissible
+ * keys, in the epilogue (one split) or in the merge (several). */
 int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
 
 /* The main pass of attn_prefill alone, for callers that overlap one query block's merge with
@@ -236,7 +241,9 @@ int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* str
  * workspace, o at offset 0 ([n_chunks, B, Hq, rows, 256] fp32) and the natural-log lse at byte
  * offset *lse_offset ([n_chunks, B, Hq, rows] fp32), and the caller completes the call with
  * attn_merge (gate and out as here) on a stream ordered after this one, before the workspace is
- * reused.  Errors as attn_prefill, plus ATTN_E_NULL for a null n_chunks or lse_offset. */
+ * reused.  Errors as attn_prefill, plus ATTN_E_NULL for a null n_chunks or lse_offset.  The
+ * merge called on its own has no inputs to redo a row from: with nonfinite inputs a hidden key
+ * may leave NaN in the result of this pair of calls (attn_prefill repairs it). */
 int attn_prefill_partials(const attn_args* a, void* workspace, size_t ws_bytes, void* stream, int32_t* n_chunks,
                           size_t* lse_offset);
 
@@ -245,6 +252,19 @@ int attn_prefill_partials(const attn_args* a, void* workspace, size_t ws_bytes, 
  * head chunk (a->head_chunk), then the merge pass.  TensorFold PR #1009 (attention
  * kernel-contract commit) splits decode rows over key chunks and merges them. */
 int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/* The composed (materialised-score) route for the same block, for comparison with the fused
+ * kernel ("perf(qwen36): qualify M4 head-256 attention", Summary: composed against fused
+ * attention for head_dim 256 at query blocks of 128 and 512 rows).  Three passes through the
+ * workspace: the fp32 scores Q K^T of every key of the block's key range, the row softmax
+ * writing weights rounded to the 16-bit type (and 1 / their sum), then P V with the gate.
+ * Same arguments and result as attn_prefill (within the same tolerance) except: no mask
+ * (ATTN_E_MASK otherwise), head_chunk and n_splits are ignored, inputs are taken to be finite.
+ * `workspace` (device) must hold attn_workspace_bytes(a, ATTN_OP_COMPOSED) bytes:
+ * B Hq rows kvp (4 + 2) + B Hq rows 4 bytes (each part rounded up to 256), kvp = the key range
+ * (kv_len, or kv_offset + rows when causal) rounded up to 32.  ATTN_E_ARG when B Hq > 65535 or
+ * B Hq rows > 2^31 - 1. */
+int attn_prefill_composed(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
 
 /* Append `rows` new K and V rows to the cache at kv_offset: a pure bit copy (signed zeros
  * and NaN payloads survive).  TensorFold PR #1009 compares append bit for bit. */
@@ -261,7 +281,8 @@ int kv_keep(const kv_keep_args* a, void* stream);
  * out = sum_c exp(lse_c - lse) o_c / sum_c exp(lse_c - lse) * sigmoid(gate), chunks with
  * lse_c = -Inf contribute nothing and an all-empty row gives 0.  The decode merge of
  * TensorFold PR #1009 (attention kernel-contract commit), usable by callers that split KV
- * across calls (a prefix and a tail, for instance). */
+ * across calls (a prefix and a tail, for instance).  A chunk whose lse_c is NaN makes the row
+ * NaN. */
 int attn_merge(const merge_args* a, void* stream);
 
 #ifdef __cplusplus

@@ -136,7 +136,7 @@ def _build(spec):
 
 
 @pytest.mark.parametrize("name,spec,status", REJECT, ids=[r[0] for r in REJECT])
-@pytest.mark.parametrize("op", [_abi.OP_PREFILL, _abi.OP_DECODE])
+@pytest.mark.parametrize("op", [_abi.OP_PREFILL, _abi.OP_DECODE, _abi.OP_COMPOSED])
 def test_rejections(name, spec, status, op):
     lib = ga.lib()
     a = _build(spec)
@@ -144,8 +144,35 @@ def test_rejections(name, spec, status, op):
     n = C.c_size_t(0)
     want = _abi.STATUS_CODE[status]
     assert lib.attn_workspace_bytes(ptr, op, C.byref(n)) == want
-    fn = lib.attn_prefill if op == _abi.OP_PREFILL else lib.attn_decode
+    fn = {_abi.OP_PREFILL: lib.attn_prefill, _abi.OP_DECODE: lib.attn_decode,
+          _abi.OP_COMPOSED: lib.attn_prefill_composed}[op]
     assert fn(ptr, None, 0, None) == want
+
+
+def test_composed_workspace_and_rejections():
+    # the composed route: scores fp32 + weights 16-bit per (b, h, row, key of the range rounded
+    # up to 32) + 1 / l per row, each part rounded up to 256 bytes; no mask; no plan to describe
+    lib = ga.lib()
+    r256 = lambda x: (x + 255) // 256 * 256
+    for rows, off in ((5, 3), (512, 32256), (1, 0)):
+        a = _good(rows=rows, kv_offset=off)
+        kvp = (off + rows + 31) // 32 * 32
+        n = a.B * a.Hq * rows
+        assert ga.workspace_bytes(a, _abi.OP_COMPOSED) == r256(n * kvp * 4) + r256(n * kvp * 2) + r256(n * 4)
+    a = _good(rows=5, kv_offset=3)
+    need = ga.workspace_bytes(a, _abi.OP_COMPOSED)
+    assert lib.attn_prefill_composed(C.byref(a), C.c_void_p(1 << 20), need - 1, None) == \
+        _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
+    assert lib.attn_prefill_composed(C.byref(a), None, need, None) == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
+    assert lib.attn_prefill_composed(C.byref(a), C.c_void_p((1 << 20) + 8), need, None) == \
+        _abi.STATUS_CODE["ATTN_E_LAYOUT"]
+    m = _good(rows=5, kv_offset=3, mask_kind=2)
+    m.mask.ptr = 1 << 20
+    n = C.c_size_t(0)
+    assert lib.attn_workspace_bytes(C.byref(m), _abi.OP_COMPOSED, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_MASK"]
+    assert lib.attn_workspace_bytes(C.byref(m), _abi.OP_PREFILL, C.byref(n)) == 0
+    info = _abi.PlanInfo()
+    assert lib.attn_describe_plan(C.byref(a), _abi.OP_COMPOSED, C.byref(info)) == _abi.STATUS_CODE["ATTN_E_ARG"]
 
 
 def test_decode_rejects_more_than_32_rows_but_prefill_accepts():
