@@ -339,9 +339,22 @@ def main():
                 b3.record(stream)
                 torch.cuda.synchronize(dev)
                 cms.append(a3.elapsed_time(b3))
+            # HBM bytes the route must move: per (head, row, key of the block's range, rounded
+            # up to 32) the fp32 score written once and read twice and the 16-bit weight written
+            # and read once (16 B), plus Q, gate and out (3 x 512 B per (head, row)) and K/V of
+            # the range once per KV head
+            cbytes = 0.0
+            for s in range(0, N, qb_):
+                e = min(s + qb_, N)
+                kvp = -(-e // 32) * 32
+                cbytes += B * Hq * (e - s) * (kvp * 16.0 + 3 * 512) + 2.0 * B * Hkv * e * 512
+            cgbs = cbytes / (np.median(cms) * 1e-3) / 1e9
             comp[qb_] = {"ms": round(float(np.median(cms)), 3),
                          "tflops": round(float(prefill_flops(Hq, N) / (np.median(cms) * 1e-3) / 1e12), 2),
-                         "workspace_bytes": int(need), "calls": len(range(0, N, qb_))}
+                         "workspace_bytes": int(need), "calls": len(range(0, N, qb_)),
+                         "roofline": {"bound": "hbm", "achieved": round(float(cgbs), 1), "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": round(float(cgbs) / PEAK_HBM_GBS, 4),
+                                      "bytes": int(cbytes)}}
             del wsc
             torch.cuda.empty_cache()
 
