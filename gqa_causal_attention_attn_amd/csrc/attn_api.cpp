@@ -69,7 +69,9 @@ int validate(const attn_args* a, int op) {
   if (a->Hq % a->Hkv != 0) return ATTN_E_HEADS;
   const int G = a->Hq / a->Hkv;
   if (G > ATTN_MAX_CHUNKS) return ATTN_E_HEADS;
-  if (a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
+  // head_dim 256 only, except on the composed route (64, 128, 256): an unqualified head dim
+  // fails closed
+  if (a->D != ATTN_HEAD_DIM && !(op == ATTN_OP_COMPOSED && (a->D == 64 || a->D == 128))) return ATTN_E_HEAD_DIM;
   if (a->rows < 1) return ATTN_E_ROWS;
   if (op == ATTN_OP_DECODE && a->rows > ATTN_MAX_DECODE_ROWS) return ATTN_E_ROWS;
   if (a->kv_offset < 0 || a->kv_len < 1 || a->capacity < a->kv_len) return ATTN_E_KV;
@@ -422,9 +424,10 @@ int attn_prefill_composed(const attn_args* a, void* workspace, size_t ws_bytes, 
   p.pw = reinterpret_cast<uint16_t*>(ws + L.s_bytes);
   p.inv_l = reinterpret_cast<float*>(ws + L.s_bytes + L.p_bytes);
   p.kvp = L.kvp;
+  p.D = a->D;
   p.B = a->B, p.Hq = a->Hq, p.G = a->Hq / a->Hkv, p.rows = a->rows;
   p.kv_offset = (int)a->kv_offset, p.kv_len = (int)a->kv_len, p.causal = a->causal, p.kv_hi = (int)L.kv_hi;
-  const float scale = a->scale > 0.0f ? a->scale : 1.0f / 16.0f;
+  const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   p.scale_log2 = scale * 1.4426950408889634f;
   if (gqa::launch_composed(p, a->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
@@ -434,7 +437,7 @@ int kv_append(const kv_append_args* a, void* stream) {
   if (!a) return ATTN_E_NULL;
   if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
   if (a->B <= 0 || a->Hkv <= 0) return ATTN_E_HEADS;
-  if (a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
+  if (a->D != 64 && a->D != 128 && a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
   if (a->rows < 1) return ATTN_E_ROWS;
   if (a->kv_offset < 0 || a->capacity < 1 || a->kv_offset + a->rows > a->capacity || a->capacity > INT32_MAX)
     return ATTN_E_KV;
@@ -453,6 +456,7 @@ int kv_append(const kv_append_args* a, void* stream) {
     p.d_sb[t] = d.stride_b, p.d_sh[t] = d.stride_h, p.d_st[t] = d.stride_row;
   }
   p.B = a->B, p.Hkv = a->Hkv, p.rows = a->rows, p.kv_offset = (int)a->kv_offset;
+  p.chunk_shift = a->D == 64 ? 3 : a->D == 128 ? 4 : 5;
   if (gqa::launch_append(p, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
 }

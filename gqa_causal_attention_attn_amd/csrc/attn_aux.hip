@@ -297,10 +297,12 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
 }
 
 // One 16-byte chunk per thread.  Workgroup row y = (tensor, b, g); x runs over (row r, chunk c
-// of 8 elements) = 32 r + c, so the index arithmetic is shifts (one division per workgroup row).
+// of 8 elements) = (r << chunk_shift) + c, so the index arithmetic is shifts (one division per
+// workgroup row).  Head dims 64, 128 and 256.
 __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   const int64_t bg = (int64_t)p.B * p.Hkv;
-  const int64_t n = (int64_t)p.rows * (kHeadDim / 8);
+  const int64_t n = (int64_t)p.rows << p.chunk_shift;
+  const int cmask = (1 << p.chunk_shift) - 1;
   for (int64_t y = blockIdx.y; y < 2 * bg; y += gridDim.y) {
     const int t = y >= bg;
     const int64_t yb = y - (t ? bg : 0);
@@ -309,8 +311,8 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
     uint16_t* dst = p.dst[t] + b * p.d_sb[t] + g * p.d_sh[t] + (int64_t)p.kv_offset * p.d_st[t];
     const int64_t s_sr = p.s_sr[t], d_st = p.d_st[t];
     for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < n; u += (int64_t)gridDim.x * 256) {
-      const int64_t r = u >> 5;
-      const int c = (int)(u & 31);
+      const int64_t r = u >> p.chunk_shift;
+      const int c = (int)(u & cmask);
       const u32x4 val = *reinterpret_cast<const u32x4*>(src + r * s_sr + 8 * c);
       *reinterpret_cast<u32x4*>(dst + r * d_st + 8 * c) = val;
     }
@@ -381,7 +383,7 @@ hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
 }
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-  int64_t bx = ((int64_t)p.rows * (kHeadDim / 8) + 255) / 256;
+  int64_t bx = (((int64_t)p.rows << p.chunk_shift) + 255) / 256;
   if (bx > 1024) bx = 1024;
   int64_t by = 2LL * p.B * p.Hkv;
   if (by > 65535) by = 65535;

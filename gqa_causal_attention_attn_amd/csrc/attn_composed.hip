@@ -1,4 +1,4 @@
-// Composed (materialised-score) arm of gated causal GQA attention at head_dim 256, gfx950.
+// Composed (materialised-score) arm of gated causal GQA attention, gfx950.
 //
 // "perf(qwen36): qualify M4 head-256 attention" (d-inference PR #640, Summary) weighs a
 // composed attention route against the fused kernel for head_dim 256 at query blocks of 128
@@ -14,6 +14,7 @@
 //   3. P.V:     O[b, h, r, :] = sum_j P[b,h,r,j] V[b,g,j,:] on MFMA (V staged in LDS), times
 //      1 / l and sigmoid(gate), rounded once to the 16-bit output.
 //
+// Head dims 64, 128 and 256 (a template parameter; the fused kernel is written for 256 only).
 // No mask: the arm serves the prompt comparison (causal or not).  The transient workspace is
 // B Hq rows kvp (4 + 2) bytes + B Hq rows 4 bytes, kvp = the block's key range rounded up to
 // 32 keys: 2.4 GB for a 512-row block of 24 heads at the end of a 32k prompt, against the fused
@@ -75,7 +76,7 @@ __device__ __forceinline__ int row_lim(const ComposedParams& p, int r) {
 // dims 16 kk + 8 (l / 32) .. + 7) and B = Q (lane: row l % 32, the same dims), both loaded
 // straight from memory; accumulator element i of lane l is key 8 (i / 4) + 4 (l / 32) + i % 4
 // of row l % 32, four consecutive keys per group of four, stored as one 16-byte write.
-template <int DT>
+template <int DT, int D>
 __global__ __launch_bounds__(256) void composed_scores_kernel(const ComposedParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31, hf = lane >> 5;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void composed_scores_kernel(const ComposedPara
   const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)min(row, p.rows - 1) * p.q_sr;
   f32x16 acc = {};
 #pragma unroll
-  for (int kk = 0; kk < 16; ++kk) {
+  for (int kk = 0; kk < D / 16; ++kk) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * kk + 8 * hf);
     const u32x4 bq = *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * hf);
     acc = mfma<DT>(a, bq, acc);
@@ -139,20 +140,25 @@ __global__ __launch_bounds__(256) void composed_softmax_kernel(const ComposedPar
   if (tid == 0) p.inv_l[row_id] = 1.0f / ((red[0] + red[1]) + (red[2] + red[3]));
 }
 
-// Pass 3.  Workgroup = four wavefronts on one (b, h) and 32 rows; wavefront w owns dims
-// 64 w .. 64 w + 63 (two 32-dim MFMA blocks).  O^T[dim, row] += V^T[dim, key] . P^T[key, row]
-// over 32-key steps: the V rows of the step are staged in LDS by the whole workgroup (16 KiB),
+// Pass 3.  Workgroup = four wavefronts on one (b, h) and 32 rows; wavefront w owns the 32-dim
+// MFMA blocks NBW w .. NBW w + NBW - 1 (two at head_dim 256, one at 128; at 64 wavefronts 2 and
+// 3 only stage V).  O^T[dim, row] += V^T[dim, key] . P^T[key, row] over 32-key steps: the V
+// rows of the step are staged in LDS by the whole workgroup (64 D bytes),
 // A = V^T (lane: dim l % 32, keys 8 (l / 32) .. + 7, eight 16-bit LDS reads) and B = P (lane:
 // row l % 32, the same keys, one 16-byte load).  The epilogue applies 1 / l and the gate.
-template <int DT>
+template <int DT, int D>
 __global__ __launch_bounds__(256) void composed_pv_kernel(const ComposedParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t vt[32][256];
+  constexpr int NBW = D >= 256 ? D / 128 : 1;         // 32-dim blocks per wavefront
+  constexpr int kChunkShift = D == 256 ? 5 : D == 128 ? 4 : 3;  // log2 of the 16-byte chunks per row
+  static_assert(D == 64 || D == 128 || D == 256, "head dims 64, 128, 256");
+  __shared__ __attribute__((aligned(16))) uint16_t vt[32][D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hf = lane >> 5;
   const int r0 = blockIdx.x * 32;
   const int bh = blockIdx.y;
   const int b = bh / p.Hq, h = bh - b * p.Hq, g = h / p.G;
   const int row = r0 + li;
+  const bool mfma_wave = wave * NBW < D / 32;  // wavefront-uniform
   // keys up to the last row's bound; the weights past each row's own bound are 0
   const int kend = row_lim(p, min(r0 + 31, p.rows - 1));
   const uint16_t* vbase = p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
@@ -160,22 +166,23 @@ __global__ __launch_bounds__(256) void composed_pv_kernel(const ComposedParams p
   f32x16 acc0 = {}, acc1 = {};
   for (int j0 = 0; j0 < kend; j0 += 32) {
     __syncthreads();  // the previous step's V reads are done
-    // 32 keys x 256 dims: thread t copies 16-byte chunks t, t + 256, t + 512, t + 768
+    // 32 keys x D dims: thread t copies 16-byte chunks t, t + 256, ... (D / 64 of them)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = tid + 256 * e, kr = c >> 5, cc = c & 31;
+    for (int e = 0; e < D / 64; ++e) {
+      const int c = tid + 256 * e, kr = c >> kChunkShift, cc = c & ((1 << kChunkShift) - 1);
       const int key = min(j0 + kr, p.kv_len - 1);  // keys past kv_len carry weight 0
       *reinterpret_cast<u32x4*>(&vt[kr][8 * cc]) =
           *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * p.v_st + 8 * cc);
     }
     __syncthreads();
+    if (!mfma_wave) continue;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int kb = 16 * ks + 8 * hf;  // this lane's 8 keys of the 16-key MFMA step
       const u32x4 pb = *reinterpret_cast<const u32x4*>(prow + j0 + kb);
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const int d = 64 * wave + 32 * blk + li;
+      for (int blk = 0; blk < NBW; ++blk) {
+        const int d = 32 * (NBW * wave + blk) + li;
         u32x4 va;
 #pragma unroll
         for (int t = 0; t < 4; ++t) va[t] = (uint32_t)vt[kb + 2 * t][d] | ((uint32_t)vt[kb + 2 * t + 1][d] << 16);
@@ -184,18 +191,18 @@ __global__ __launch_bounds__(256) void composed_pv_kernel(const ComposedParams p
       }
     }
   }
-  if (row >= p.rows) return;
+  if (row >= p.rows || !mfma_wave) return;
   const int64_t row_id = (int64_t)bh * p.rows + row;
   const float inv = p.inv_l[row_id];
   const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)row * p.g_sr;
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)row * p.o_sr;
   // accumulator element i of lane l: dim 8 (i / 4) + 4 (l / 32) + i % 4 of the block, row l % 32
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
+  for (int blk = 0; blk < NBW; ++blk) {
     const f32x16& acc = blk == 0 ? acc0 : acc1;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int d0 = 64 * wave + 32 * blk + 8 * a + 4 * hf;
+      const int d0 = 32 * (NBW * wave + blk) + 8 * a + 4 * hf;
       const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
       float res[4];
 #pragma unroll
@@ -213,19 +220,30 @@ __global__ __launch_bounds__(256) void composed_pv_kernel(const ComposedParams p
 
 }  // namespace
 
-hipError_t launch_composed(const ComposedParams& p, int dtype, hipStream_t stream) {
+namespace {
+
+template <int DT, int D>
+void launch_composed_t(const ComposedParams& p, hipStream_t stream) {
   const dim3 g1((unsigned)((p.kvp / 32 + 3) / 4), (unsigned)((p.rows + 31) / 32), (unsigned)(p.B * p.Hq));
   const dim3 g2((unsigned)((int64_t)p.B * p.Hq * p.rows));
   const dim3 g3((unsigned)((p.rows + 31) / 32), (unsigned)(p.B * p.Hq));
-  if (dtype == 0) {
-    hipLaunchKernelGGL(composed_scores_kernel<0>, g1, dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(composed_softmax_kernel<0>, g2, dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(composed_pv_kernel<0>, g3, dim3(256), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(composed_scores_kernel<1>, g1, dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(composed_softmax_kernel<1>, g2, dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(composed_pv_kernel<1>, g3, dim3(256), 0, stream, p);
-  }
+  hipLaunchKernelGGL((composed_scores_kernel<DT, D>), g1, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(composed_softmax_kernel<DT>, g2, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((composed_pv_kernel<DT, D>), g3, dim3(256), 0, stream, p);
+}
+
+template <int DT>
+void launch_composed_d(const ComposedParams& p, hipStream_t stream) {
+  if (p.D == 64) launch_composed_t<DT, 64>(p, stream);
+  else if (p.D == 128) launch_composed_t<DT, 128>(p, stream);
+  else launch_composed_t<DT, 256>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_composed(const ComposedParams& p, int dtype, hipStream_t stream) {
+  if (dtype == 0) launch_composed_d<0>(p, stream);
+  else launch_composed_d<1>(p, stream);
   return hipGetLastError();
 }
 

@@ -86,6 +86,7 @@ struct AppendParams {
   int64_t d_sb[2], d_sh[2], d_st[2];
   int B, Hkv, rows;
   int kv_offset;
+  int chunk_shift;  // log2 of the 16-byte chunks per row: 3, 4 or 5 (head dim 64, 128 or 256)
 };
 
 constexpr int kKeepMaxBatch = 64;  // keep masks travel in the kernel arguments
@@ -114,6 +115,7 @@ struct ComposedParams {
   uint16_t* pw;
   float* inv_l;
   int64_t kvp;  // keys per row of s and pw: the key range rounded up to 32
+  int D;        // head dim: 64, 128 or 256
   int B, Hq, G, rows, kv_offset, kv_len, causal, kv_hi;
   float scale_log2;
 };

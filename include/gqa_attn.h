@@ -52,7 +52,7 @@ typedef enum {
   ATTN_E_NULL = 1,       /* a required pointer is NULL */
   ATTN_E_DTYPE = 2,      /* unknown dtype */
   ATTN_E_HEADS = 3,      /* Hq <= 0, Hkv <= 0, Hq % Hkv != 0, B <= 0, or Hq/Hkv > 64 (checked before dividing) */
-  ATTN_E_HEAD_DIM = 4,   /* D != 256: fail closed */
+  ATTN_E_HEAD_DIM = 4,   /* D != 256 (64 and 128 also for attn_prefill_composed and kv_append): fail closed */
   ATTN_E_ROWS = 5,       /* rows < 1, or rows > 32 for attn_decode */
   ATTN_E_KV = 6,         /* kv_offset < 0, kv_len < 1, kv_len > capacity, kv_len < kv_offset + rows when causal,
                             or an append beyond capacity */
@@ -258,8 +258,10 @@ int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stre
  * attention for head_dim 256 at query blocks of 128 and 512 rows).  Three passes through the
  * workspace: the fp32 scores Q K^T of every key of the block's key range, the row softmax
  * writing weights rounded to the 16-bit type (and 1 / their sum), then P V with the gate.
- * Same arguments and result as attn_prefill (within the same tolerance) except: no mask
+ * Same arguments and result as attn_prefill (within the same tolerance) except: head_dim may
+ * also be 64 or 128 (the fused kernels are written for 256 and fail closed on others), no mask
  * (ATTN_E_MASK otherwise), head_chunk and n_splits are ignored, inputs are taken to be finite.
+ * scale = 0 means 1 / sqrt(head_dim).
  * `workspace` (device) must hold attn_workspace_bytes(a, ATTN_OP_COMPOSED) bytes:
  * B Hq rows kvp (4 + 2) + B Hq rows 4 bytes (each part rounded up to 256), kvp = the key range
  * (kv_len, or kv_offset + rows when causal) rounded up to 32.  ATTN_E_ARG when B Hq > 65535 or
@@ -267,7 +269,8 @@ int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stre
 int attn_prefill_composed(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
 
 /* Append `rows` new K and V rows to the cache at kv_offset: a pure bit copy (signed zeros
- * and NaN payloads survive).  TensorFold PR #1009 compares append bit for bit. */
+ * and NaN payloads survive).  head_dim 64, 128 or 256.  TensorFold PR #1009 compares append
+ * bit for bit. */
 int kv_append(const kv_append_args* a, void* stream);
 
 /* Compact the kept rows of a verify block in the caches, in place (see kv_keep_args): a pure bit

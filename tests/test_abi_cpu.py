@@ -90,7 +90,7 @@ REJECT = [
     ("uneven groups", dict(Hq=10, Hkv=4), "ATTN_E_HEADS"),
     ("batch 0", dict(B=0), "ATTN_E_HEADS"),
     ("group over 64", dict(Hq=130, Hkv=2), "ATTN_E_HEADS"),
-    ("head dim 128", dict(D=128), "ATTN_E_HEAD_DIM"),
+    ("head dim 96", dict(D=96), "ATTN_E_HEAD_DIM"),
     ("rows 0", dict(rows=0), "ATTN_E_ROWS"),
     ("negative offset", dict(kv_offset=-1, kv_len=3), "ATTN_E_KV"),
     ("kv_len short of causal rows", dict(kv_len=102), "ATTN_E_KV"),
@@ -149,6 +149,26 @@ def test_rejections(name, spec, status, op):
     assert fn(ptr, None, 0, None) == want
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_other_head_dims_only_on_the_composed_route(D):
+    # the fused kernels are written for head_dim 256 and fail closed on others; the composed
+    # route (and the append it relies on) take 64 and 128 too
+    lib = ga.lib()
+    a = _good(D=D)
+    n = C.c_size_t(0)
+    assert lib.attn_workspace_bytes(C.byref(a), _abi.OP_PREFILL, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
+    assert lib.attn_workspace_bytes(C.byref(a), _abi.OP_DECODE, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
+    assert lib.attn_prefill(C.byref(a), None, 0, None) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
+    assert lib.attn_workspace_bytes(C.byref(a), _abi.OP_COMPOSED, C.byref(n)) == 0 and n.value > 0
+    t = _abi.Tensor(1 << 20, 4 * 16 * D, 16 * D, D)
+    for d, want in ((D, None), (96, "ATTN_E_HEAD_DIM")):
+        ap = _abi.KvAppendArgs()
+        ap.dtype, ap.B, ap.Hkv, ap.rows, ap.D, ap.kv_offset, ap.capacity = 0, 1, 4, 2, d, 0, 16
+        ap.k_new, ap.v_new, ap.k_cache, ap.v_cache = t, t, t, t
+        if want:
+            assert lib.kv_append(C.byref(ap), None) == _abi.STATUS_CODE[want]
+
+
 def test_composed_workspace_and_rejections():
     # the composed route: scores fp32 + weights 16-bit per (b, h, row, key of the range rounded
     # up to 32) + 1 / l per row, each part rounded up to 256 bytes; no mask; no plan to describe
@@ -198,7 +218,7 @@ def test_append_and_merge_rejections():
     a = _abi.KvAppendArgs(0, 1, 4, 256, 2, 0, 15, 16, t, t, t, t)
     assert lib.kv_append(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_KV"]
     a.kv_offset = 14
-    a.D = 64
+    a.D = 96
     assert lib.kv_append(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
     a.D = 256
     a.dtype = 3

@@ -88,3 +88,29 @@ def test_composed_8k_prompt_in_512_row_blocks_sampled():
     ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=0, kv_len=N,
                               rows=rows)
     _say(assert_close(to_f64(out)[:, :, rows], ref, "composed 8k sampled"))
+
+
+@needs_gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_composed_other_head_dims(D, dtype):
+    # head dims the fused kernels refuse: 8 query heads over 2 KV heads, 150 causal rows in
+    # blocks of 64 (kv_append + attn_prefill_composed), scale 1 / sqrt(D); the append bit for bit
+    _say("composed head dim", D, dtype)
+    Hq, Hkv, N = 8, 2, 150
+    rng = syn.streams(5300 + D)
+    qb = syn.normal_bits(rng["q"], (1, Hq, N, D), dtype)
+    kb = syn.normal_bits(rng["k"], (1, Hkv, N, D), dtype)
+    vb = syn.normal_bits(rng["v"], (1, Hkv, N, D), dtype)
+    gb = syn.normal_bits(rng["gate"], (1, Hq, N, D), dtype)
+    q, k, v, g = (to_dev(x, dtype) for x in (qb, kb, vb, gb))
+    kc = torch.full((1, Hkv, N, D), float("nan"), dtype=q.dtype, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    out = ga.prompt_prefill(q, k, v, g, kc, vc, q_block=64, composed=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kc), kb) and np.array_equal(to_bits(vc), vb)
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=0,
+                              kv_len=N)
+    _say(assert_close(syn.widen(to_bits(out), dtype), ref, f"composed D={D}"))
+    with pytest.raises(ga.AttnError):
+        ga.prefill(q, kc, vc, g, kv_offset=0, kv_len=N)  # the fused route fails closed
