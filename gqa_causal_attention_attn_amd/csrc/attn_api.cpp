@@ -69,9 +69,8 @@ int validate(const attn_args* a, int op) {
   if (a->Hq % a->Hkv != 0) return ATTN_E_HEADS;
   const int G = a->Hq / a->Hkv;
   if (G > ATTN_MAX_CHUNKS) return ATTN_E_HEADS;
-  // head_dim 256 only, except on the composed route (64, 128, 256): an unqualified head dim
-  // fails closed
-  if (a->D != ATTN_HEAD_DIM && !(op == ATTN_OP_COMPOSED && (a->D == 64 || a->D == 128))) return ATTN_E_HEAD_DIM;
+  // head dims 256, 128 and 64 (the last two by their own kernels); any other fails closed
+  if (a->D != ATTN_HEAD_DIM && a->D != 64 && a->D != 128) return ATTN_E_HEAD_DIM;
   if (a->rows < 1) return ATTN_E_ROWS;
   if (op == ATTN_OP_DECODE && a->rows > ATTN_MAX_DECODE_ROWS) return ATTN_E_ROWS;
   if (a->kv_offset < 0 || a->kv_len < 1 || a->capacity < a->kv_len) return ATTN_E_KV;
@@ -93,6 +92,11 @@ int validate(const attn_args* a, int op) {
     if (m.Bm != 1 && m.Bm != a->B) return ATTN_E_MASK;
     if (m.Hm != 1 && m.Hm != a->Hq) return ATTN_E_MASK;
     if (m.stride_b < 0 || m.stride_h < 0 || m.stride_row < 0) return ATTN_E_MASK;
+  }
+  if (a->D != ATTN_HEAD_DIM && op != ATTN_OP_COMPOSED) {
+    // the fused pass for head dims 64 and 128: no mask; one workgroup per 32 rows of a head
+    if (m.kind != ATTN_MASK_NONE) return ATTN_E_MASK;
+    if (a->B > 65535 || a->Hq > 65535) return ATTN_E_ARG;
   }
   if (op == ATTN_OP_COMPOSED) {
     if (m.kind != ATTN_MASK_NONE) return ATTN_E_MASK;
@@ -212,10 +216,37 @@ inline int variant_of(const attn_args* a, const Plan& P) {
   return (P.mask_lds << 5) | (P.shape << 3) | (a->dtype << 2) | a->mask.kind;
 }
 
+// The fused pass for head dims 64 and 128 (no workspace, no split, no merge).
+int run_small_d(const attn_args* a, void* stream) {
+  gqa::SmallDParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = static_cast<const uint16_t*>(a->q.ptr);
+  p.k = static_cast<const uint16_t*>(a->k_cache.ptr);
+  p.v = static_cast<const uint16_t*>(a->v_cache.ptr);
+  p.gate = static_cast<const uint16_t*>(a->gate.ptr);
+  p.out = static_cast<uint16_t*>(a->out.ptr);
+  p.q_sb = a->q.stride_b, p.q_sh = a->q.stride_h, p.q_sr = a->q.stride_row;
+  p.k_sb = a->k_cache.stride_b, p.k_sh = a->k_cache.stride_h, p.k_st = a->k_cache.stride_row;
+  p.v_sb = a->v_cache.stride_b, p.v_sh = a->v_cache.stride_h, p.v_st = a->v_cache.stride_row;
+  p.g_sb = a->gate.stride_b, p.g_sh = a->gate.stride_h, p.g_sr = a->gate.stride_row;
+  p.o_sb = a->out.stride_b, p.o_sh = a->out.stride_h, p.o_sr = a->out.stride_row;
+  p.D = a->D, p.B = a->B, p.Hq = a->Hq, p.G = a->Hq / a->Hkv, p.rows = a->rows;
+  p.kv_offset = (int)a->kv_offset, p.kv_len = (int)a->kv_len, p.causal = a->causal;
+  const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  if (gqa::launch_small_d(p, a->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
+}
+
 int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream, bool merge = true,
             int32_t* n_chunks = nullptr, size_t* lse_offset = nullptr) {
   int st = validate(a, op);
   if (st) return st;
+  if (a->D != kHeadDim) {
+    if (n_chunks) *n_chunks = 1;
+    if (lse_offset) *lse_offset = 0;
+    return run_small_d(a, stream);
+  }
   Plan P;
   st = make_plan(a, op, &P);
   if (st) return st;
@@ -331,6 +362,8 @@ const char* attn_variant_name(int variant) {
       GQA_NAMES("4x1_ldsmask"),   GQA_NAMES("unused"),        GQA_NAMES("8x1_ldsmask"),   GQA_NAMES("unused")};
 #undef GQA_NAMES
   static const bool used[8] = {true, true, true, false, true, false, true, false};  // shape groups
+  if (variant == 64) return "fwd_small_d64";
+  if (variant == 65) return "fwd_small_d128";
   return (variant >= 0 && variant < 64 && used[variant >> 3]) ? names[variant] : "unknown";
 }
 
@@ -353,6 +386,10 @@ int attn_workspace_bytes(const attn_args* a, int op, size_t* bytes) {
     *bytes = L.s_bytes + L.p_bytes + L.l_bytes;
     return ATTN_OK;
   }
+  if (a->D != kHeadDim) {  // the fused pass for head dims 64 and 128 needs none
+    *bytes = 0;
+    return ATTN_OK;
+  }
   Plan P;
   st = make_plan(a, op, &P);
   if (st) return st;
@@ -365,6 +402,24 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
   if (op == ATTN_OP_COMPOSED) return ATTN_E_ARG;
   int st = validate(a, op);
   if (st) return st;
+  if (a->D != kHeadDim) {  // the fused pass for head dims 64 and 128: one plan
+    memset(info, 0, sizeof(*info));
+    info->op = op;
+    info->variant = a->D == 64 ? 64 : 65;
+    info->group_size = a->Hq / a->Hkv;
+    info->n_head_chunks = 1;
+    info->head_chunk = info->group_size;
+    info->rows_per_wave = 32;
+    info->waves_per_block = 1;
+    info->n_row_tiles = (a->rows + 31) / 32;
+    info->n_splits = 1;
+    info->keys_per_split = (int)a->kv_len;
+    info->keys_per_tile = kKeysPerTile;
+    info->lds_bytes = 2 * 32 * (a->D + 8) * 2;
+    info->grid_blocks = (int64_t)info->n_row_tiles * a->Hq * a->B;
+    info->chunk_sizes[0] = info->group_size;
+    return ATTN_OK;
+  }
   Plan P;
   st = make_plan(a, op, &P);
   if (st) return st;

@@ -120,6 +120,22 @@ struct ComposedParams {
   float scale_log2;
 };
 
+// Parameters of the fused pass for head dims 64 and 128 (attn_small_d.hip): no mask, no split.
+struct SmallDParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* gate;
+  uint16_t* out;
+  int64_t q_sb, q_sh, q_sr;
+  int64_t k_sb, k_sh, k_st;
+  int64_t v_sb, v_sh, v_st;
+  int64_t g_sb, g_sh, g_sr;
+  int64_t o_sb, o_sh, o_sr;
+  int D, B, Hq, G, rows, kv_offset, kv_len, causal;
+  float scale_log2;
+};
+
 // Launchers (return hipGetLastError()).  dtype 0 = bf16, 1 = fp16; mask_kind as attn_mask_kind.
 // shape: 0 = 4 wavefronts x 1 column block, 1 = 4 x 2, 2 = 8 x 1 (wavefronts x blocks each)
 hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream);
@@ -127,5 +143,6 @@ hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_keep(const KeepParams& p, int B, hipStream_t stream);
 hipError_t launch_composed(const ComposedParams& p, int dtype, hipStream_t stream);
+hipError_t launch_small_d(const SmallDParams& p, int dtype, hipStream_t stream);
 
 }  // namespace gqa

@@ -150,23 +150,29 @@ def test_rejections(name, spec, status, op):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_other_head_dims_only_on_the_composed_route(D):
-    # the fused kernels are written for head_dim 256 and fail closed on others; the composed
-    # route (and the append it relies on) take 64 and 128 too
+def test_other_head_dims(D):
+    # head dims 64 and 128 run on their own fused pass (no workspace, no mask) and on the
+    # composed route; the append takes them; any other head dim fails closed everywhere
     lib = ga.lib()
     a = _good(D=D)
-    n = C.c_size_t(0)
-    assert lib.attn_workspace_bytes(C.byref(a), _abi.OP_PREFILL, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
-    assert lib.attn_workspace_bytes(C.byref(a), _abi.OP_DECODE, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
-    assert lib.attn_prefill(C.byref(a), None, 0, None) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
+    n = C.c_size_t(1)
+    for op in (_abi.OP_PREFILL, _abi.OP_DECODE):
+        assert lib.attn_workspace_bytes(C.byref(a), op, C.byref(n)) == 0 and n.value == 0
+        info = ga.describe_plan(a, op)
+        assert info["variant_name"] == f"fwd_small_d{D}" and info["n_splits"] == 1
     assert lib.attn_workspace_bytes(C.byref(a), _abi.OP_COMPOSED, C.byref(n)) == 0 and n.value > 0
-    t = _abi.Tensor(1 << 20, 4 * 16 * D, 16 * D, D)
-    for d, want in ((D, None), (96, "ATTN_E_HEAD_DIM")):
-        ap = _abi.KvAppendArgs()
-        ap.dtype, ap.B, ap.Hkv, ap.rows, ap.D, ap.kv_offset, ap.capacity = 0, 1, 4, 2, d, 0, 16
-        ap.k_new, ap.v_new, ap.k_cache, ap.v_cache = t, t, t, t
-        if want:
-            assert lib.kv_append(C.byref(ap), None) == _abi.STATUS_CODE[want]
+    m = _good(D=D, mask_kind=2)
+    m.mask.ptr = 1 << 20
+    for op in (_abi.OP_PREFILL, _abi.OP_DECODE, _abi.OP_COMPOSED):
+        assert lib.attn_workspace_bytes(C.byref(m), op, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_MASK"]
+    odd = _good(D=96)
+    for op in (_abi.OP_PREFILL, _abi.OP_DECODE, _abi.OP_COMPOSED):
+        assert lib.attn_workspace_bytes(C.byref(odd), op, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
+    t = _abi.Tensor(1 << 20, 4 * 16 * 96, 16 * 96, 96)
+    ap = _abi.KvAppendArgs()
+    ap.dtype, ap.B, ap.Hkv, ap.rows, ap.D, ap.kv_offset, ap.capacity = 0, 1, 4, 2, 96, 0, 16
+    ap.k_new, ap.v_new, ap.k_cache, ap.v_cache = t, t, t, t
+    assert lib.kv_append(C.byref(ap), None) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
 
 
 def test_composed_workspace_and_rejections():

@@ -94,8 +94,9 @@ def test_composed_8k_prompt_in_512_row_blocks_sampled():
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_composed_other_head_dims(D, dtype):
-    # head dims the fused kernels refuse: 8 query heads over 2 KV heads, 150 causal rows in
-    # blocks of 64 (kv_append + attn_prefill_composed), scale 1 / sqrt(D); the append bit for bit
+    # head dims 64 and 128: 8 query heads over 2 KV heads, 150 causal rows in blocks of 64
+    # (kv_append + attn_prefill_composed, then the fused pass), scale 1 / sqrt(D); the append
+    # bit for bit
     _say("composed head dim", D, dtype)
     Hq, Hkv, N = 8, 2, 150
     rng = syn.streams(5300 + D)
@@ -112,5 +113,35 @@ def test_composed_other_head_dims(D, dtype):
     ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=0,
                               kv_len=N)
     _say(assert_close(syn.widen(to_bits(out), dtype), ref, f"composed D={D}"))
-    with pytest.raises(ga.AttnError):
-        ga.prefill(q, kc, vc, g, kv_offset=0, kv_len=N)  # the fused route fails closed
+    # the fused pass for this head dim, same blocks
+    kc2, vc2 = torch.zeros_like(kc), torch.zeros_like(vc)
+    fused = ga.prompt_prefill(q, k, v, g, kc2, vc2, q_block=64)
+    torch.cuda.synchronize()
+    _say(assert_close(syn.widen(to_bits(fused), dtype), ref, f"fused D={D}"))
+
+
+@needs_gpu
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("rows,offset,causal,B", [(1, 1000, True, 1), (5, 777, True, 2), (32, 4096, True, 1),
+                                                   (70, 0, False, 2)])
+def test_fused_small_head_dims(D, rows, offset, causal, B):
+    # the fused pass for head dims 64 and 128: decode / verify rows over a cache, and a
+    # non-causal block; head-chunk requests change nothing (one workgroup per 32 rows of a head)
+    _say("fused small D", D, rows, offset, causal, B)
+    Hq, Hkv = 16, 2
+    kv = offset + rows if causal else 150
+    rng = syn.streams(5400 + D + rows)
+    qb = syn.normal_bits(rng["q"], (B, Hq, rows, D))
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D))
+    kb = syn.normal_bits(rng["k"], (B, Hkv, kv + 7, D))
+    vb = syn.normal_bits(rng["v"], (B, Hkv, kv + 7, D))
+    q, g, k, v = (to_dev(x) for x in (qb, gb, kb, vb))
+    call = ga.decode if rows <= 32 else ga.prefill
+    out = call(q, k, v, g, kv_offset=offset, kv_len=kv, causal=causal)
+    torch.cuda.synchronize()
+    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=offset,
+                              kv_len=kv, causal=causal)
+    _say(assert_close(to_f64(out), ref, f"fused D={D}"))
+    if rows <= 32:
+        again = ga.decode(q, k, v, g, kv_offset=offset, kv_len=kv, causal=causal, head_chunk=1)
+        assert torch.equal(again.view(torch.int16), out.view(torch.int16))
