@@ -358,6 +358,42 @@ def main():
             del wsc
             torch.cuda.empty_cache()
 
+    # head dims 64 and 128 (their own fused pass, no split): the same 32k prompt shape in blocks
+    # of 512 rows, kv_append + attn_prefill, enqueued under a hold
+    small = {}
+    if not args.no_composed:
+        for D_ in (128, 64):
+            srng = syn.streams(1005 + D_)
+            sq, sk, sv, sg = (_up(syn.normal_bits(srng[nm], (B, H, N, D_)), dev)
+                              for nm, H in (("q", Hq), ("k", Hkv), ("v", Hkv), ("gate", Hq)))
+            skc = torch.empty((B, Hkv, N, D_), dtype=torch.bfloat16, device=dev)
+            svc = torch.empty_like(skc)
+            sout = torch.empty_like(sq)
+
+            def small_pass():
+                for s in range(0, N, qL):
+                    e = min(s + qL, N)
+                    ga.kv_append(sk[:, :, s:e], sv[:, :, s:e], skc, svc, kv_offset=s)
+                    ga.prefill(sq[:, :, s:e], skc, svc, sg[:, :, s:e], kv_offset=s, kv_len=e, out=sout[:, :, s:e])
+
+            small_pass()
+            torch.cuda.synchronize(dev)
+            sms = []
+            for _ in range(2):
+                torch.cuda._sleep(int(50.0 * cyc_per_ms))
+                a4, b4 = E(enable_timing=True), E(enable_timing=True)
+                a4.record(stream)
+                small_pass()
+                b4.record(stream)
+                torch.cuda.synchronize(dev)
+                sms.append(a4.elapsed_time(b4))
+            sflops = 4.0 * D_ * Hq * N * (N + 1) / 2
+            stf = sflops / (np.median(sms) * 1e-3) / 1e12
+            small[D_] = {"ms": round(float(np.median(sms)), 3), "tflops": round(float(stf), 2),
+                         "frac_of_peak": round(float(stf) / PEAK_BF16_TFLOPS, 4)}
+            del sq, sk, sv, sg, skc, svc, sout
+            torch.cuda.empty_cache()
+
     dec_dev_us = device_timed(dec_call)
     warm_dev_us = device_timed(lambda i: dec_call(i, cold=False))
     dec_step_us = device_timed(dec_step)
@@ -411,6 +447,9 @@ def main():
         "prefill_composed": {"route": "materialised scores: fp32 Q K^T, row softmax to 16-bit weights, P V + gate "
                                       "(attn_prefill_composed), kv_append per block; events around the block loop",
                              **{f"q_block_{kk}": vv for kk, vv in comp.items()}},
+        "prefill_small_head_dims": {"route": "fused pass for head dims 64 and 128 (one wavefront per 32 rows of a "
+                                             "head, no split), 24/4 heads, same prompt and blocks",
+                                    **{f"head_dim_{kk}": vv for kk, vv in small.items()}},
         "decode": {"metric": "decode KV GB/s (35B-A3B shape, batch 2, 1 row at offset 32768, cold KV; "
                              "device time of attn_decode: main pass + merge)",
                    "value": round(float(dec_gbs), 1), "unit": "GB/s", "us": round(dec_dev_us, 2),

@@ -52,7 +52,7 @@ typedef enum {
   ATTN_E_NULL = 1,       /* a required pointer is NULL */
   ATTN_E_DTYPE = 2,      /* unknown dtype */
   ATTN_E_HEADS = 3,      /* Hq <= 0, Hkv <= 0, Hq % Hkv != 0, B <= 0, or Hq/Hkv > 64 (checked before dividing) */
-  ATTN_E_HEAD_DIM = 4,   /* D != 256 (64 and 128 also for attn_prefill_composed and kv_append): fail closed */
+  ATTN_E_HEAD_DIM = 4,   /* D not 256, 128 or 64: fail closed */
   ATTN_E_ROWS = 5,       /* rows < 1, or rows > 32 for attn_decode */
   ATTN_E_KV = 6,         /* kv_offset < 0, kv_len < 1, kv_len > capacity, kv_len < kv_offset + rows when causal,
                             or an append beyond capacity */
@@ -233,6 +233,9 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info);
  * not become NaN): a pair whose result came out NaN is computed again over its admissible
  * keys, in the epilogue (one split) or in the merge (several). */
 int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
+/* Head dims 64 and 128 (attn_prefill, attn_decode, attn_prefill_partials) run a plainer fused
+ * pass of their own: no workspace (attn_workspace_bytes reports 0), one chunk, no mask
+ * (ATTN_E_MASK), scale = 0 means 1 / sqrt(head_dim), inputs taken to be finite. */
 
 /* The main pass of attn_prefill alone, for callers that overlap one query block's merge with
  * the next block's main pass (two workspaces, the merges on a second stream).  *n_chunks
@@ -258,8 +261,7 @@ int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stre
  * attention for head_dim 256 at query blocks of 128 and 512 rows).  Three passes through the
  * workspace: the fp32 scores Q K^T of every key of the block's key range, the row softmax
  * writing weights rounded to the 16-bit type (and 1 / their sum), then P V with the gate.
- * Same arguments and result as attn_prefill (within the same tolerance) except: head_dim may
- * also be 64 or 128 (the fused kernels are written for 256 and fail closed on others), no mask
+ * Same arguments and result as attn_prefill (within the same tolerance) except: no mask
  * (ATTN_E_MASK otherwise), head_chunk and n_splits are ignored, inputs are taken to be finite.
  * scale = 0 means 1 / sqrt(head_dim).
  * `workspace` (device) must hold attn_workspace_bytes(a, ATTN_OP_COMPOSED) bytes:
