@@ -109,7 +109,7 @@ typedef struct {
   int64_t kv_offset;   /* cached keys before row 0 = absolute position of row 0 */
   int64_t kv_len;      /* valid keys in the cache (normally kv_offset + rows, after kv_append) */
   int64_t capacity;    /* allocated tokens per (b, kv head) in the cache */
-  float scale;         /* score scale; 0 means 1/sqrt(256) = 1/16 */
+  float scale;         /* score scale; 0 means 1/sqrt(head_dim) (1/16 at 256) */
   int32_t causal;      /* 1: row r sees keys <= kv_offset + r; 0: all keys < kv_len */
   int32_t head_chunk;  /* 0: the head-chunk policy; k in 1..G: chunks of k heads (k = G: off) */
   int32_t n_splits;    /* KV splits; 0 = automatic */
