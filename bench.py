@@ -358,8 +358,8 @@ def main():
             del wsc
             torch.cuda.empty_cache()
 
-    # head dims 64 and 128 (their own fused pass, no split): the same 32k prompt shape in blocks
-    # of 512 rows, kv_append + attn_prefill, enqueued under a hold
+    # head dims 64 and 128 (their own fused pass, keys split where its grid is small): the same
+    # 32k prompt shape in blocks of 512 rows, kv_append + attn_prefill, enqueued under a hold
     small = {}
     if not args.no_composed:
         for D_ in (128, 64):
@@ -369,12 +369,16 @@ def main():
             skc = torch.empty((B, Hkv, N, D_), dtype=torch.bfloat16, device=dev)
             svc = torch.empty_like(skc)
             sout = torch.empty_like(sq)
+            sneed = max(ga.workspace_bytes(ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=min(qL, N - s), kv_offset=s, D=D_))
+                        for s in range(0, N, qL))
+            sws = torch.empty(max(sneed, 16), dtype=torch.uint8, device=dev)
 
             def small_pass():
                 for s in range(0, N, qL):
                     e = min(s + qL, N)
                     ga.kv_append(sk[:, :, s:e], sv[:, :, s:e], skc, svc, kv_offset=s)
-                    ga.prefill(sq[:, :, s:e], skc, svc, sg[:, :, s:e], kv_offset=s, kv_len=e, out=sout[:, :, s:e])
+                    ga.prefill(sq[:, :, s:e], skc, svc, sg[:, :, s:e], kv_offset=s, kv_len=e, out=sout[:, :, s:e],
+                               workspace=sws)
 
             small_pass()
             torch.cuda.synchronize(dev)
@@ -391,7 +395,7 @@ def main():
             stf = sflops / (np.median(sms) * 1e-3) / 1e12
             small[D_] = {"ms": round(float(np.median(sms)), 3), "tflops": round(float(stf), 2),
                          "frac_of_peak": round(float(stf) / PEAK_BF16_TFLOPS, 4)}
-            del sq, sk, sv, sg, skc, svc, sout
+            del sq, sk, sv, sg, skc, svc, sout, sws
             torch.cuda.empty_cache()
 
     dec_dev_us = device_timed(dec_call)
@@ -448,7 +452,8 @@ def main():
                                       "(attn_prefill_composed), kv_append per block; events around the block loop",
                              **{f"q_block_{kk}": vv for kk, vv in comp.items()}},
         "prefill_small_head_dims": {"route": "fused pass for head dims 64 and 128 (one wavefront per 32 rows of a "
-                                             "head, no split), 24/4 heads, same prompt and blocks",
+                                             "head, keys split when the grid is small, then the merge), "
+                                             "24/4 heads, same prompt and blocks",
                                     **{f"head_dim_{kk}": vv for kk, vv in small.items()}},
         "decode": {"metric": "decode KV GB/s (35B-A3B shape, batch 2, 1 row at offset 32768, cold KV; "
                              "device time of attn_decode: main pass + merge)",

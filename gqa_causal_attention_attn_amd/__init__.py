@@ -154,9 +154,9 @@ def prefill_partials(q, k_cache, v_cache, gate, *, kv_offset: int, workspace, kv
                                        C.byref(n), C.byref(off)))
     if n.value == 1:
         return out, None
-    B, Hq, rows = q.shape[0], q.shape[1], q.shape[2]
+    B, Hq, rows, D = q.shape
     cnt = n.value * B * Hq * rows
-    po = workspace[:cnt * 1024].view(torch.float32).view(n.value, B, Hq, rows, 256)
+    po = workspace[:cnt * D * 4].view(torch.float32).view(n.value, B, Hq, rows, D)
     pl = workspace[off.value:off.value + cnt * 4].view(torch.float32).view(n.value, B, Hq, rows)
     return out, (po, pl)
 
@@ -232,7 +232,7 @@ def kv_keep(k_cache, v_cache, *, kv_offset: int, rows: int, keep) -> None:
     _check(lib().kv_keep(C.byref(a), _stream_handle(k_cache)))
 
 def merge(partial_o, partial_lse, gate, out=None):
-    """attn_merge: partial_o [C, B, Hq, rows, 256] fp32, partial_lse [C, B, Hq, rows] fp32 (natural log)."""
+    """attn_merge: partial_o [C, B, Hq, rows, D] fp32 (D 256, 128 or 64), partial_lse [C, B, Hq, rows] fp32 (natural log)."""
     if partial_o.dtype != torch.float32 or partial_lse.dtype != torch.float32:
         raise TypeError("partials are float32")
     if not partial_o.is_contiguous() or not partial_lse.is_contiguous():
@@ -327,7 +327,7 @@ def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int, kv_offset: 
         for s in range(0, N, q_block):
             rows = min(q_block, N - s)
             a = plan_args(B=q.shape[0], Hq=q.shape[1], Hkv=k.shape[1], rows=rows, kv_offset=kv_offset + s,
-                          capacity=k_cache.shape[2], head_chunk=head_chunk, n_splits=n_splits)
+                          capacity=k_cache.shape[2], head_chunk=head_chunk, n_splits=n_splits, D=q.shape[3])
             need = max(need, workspace_bytes(a, _abi.OP_PREFILL))
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if not overlap_merge:

@@ -217,7 +217,49 @@ inline int variant_of(const attn_args* a, const Plan& P) {
 }
 
 // The fused pass for head dims 64 and 128 (no workspace, no split, no merge).
-int run_small_d(const attn_args* a, void* stream) {
+// KV splits of the fused pass for head dims 64 and 128.  Its workgroups are one wavefront of
+// 32 rows of one head, about nine to a CU by LDS, so a block with fewer than ~2048 of them
+// splits its keys (at least 8 tiles of 32 per split) to fill the chip; partials and lse rows
+// as for head dim 256, rows of D.
+struct SmallPlan {
+  int n_splits, keys_per_split;
+  size_t ws_o_bytes, ws_bytes;
+};
+
+SmallPlan small_plan(const attn_args* a) {
+  SmallPlan P;
+  memset(&P, 0, sizeof(P));
+  const int64_t kv_hi = a->causal ? (a->kv_len < a->kv_offset + a->rows ? a->kv_len : a->kv_offset + a->rows)
+                                  : a->kv_len;
+  const int64_t n_kt = cdiv(kv_hi, kKeysPerTile);
+  int64_t S;
+  if (a->n_splits == 0) {
+    const int64_t base = (int64_t)a->B * a->Hq * cdiv(a->rows, 32);
+    const int64_t want = 2048 / base;
+    const int64_t most = n_kt / 8;
+    S = want < most ? want : most;
+    if (S < 1) S = 1;
+  } else {
+    S = a->n_splits < n_kt ? a->n_splits : n_kt;
+  }
+  const int64_t tps = cdiv(n_kt, S);
+  S = cdiv(n_kt, tps);
+  P.n_splits = (int)S;
+  P.keys_per_split = (int)(tps * kKeysPerTile);
+  if (S > 1) {
+    const int64_t nrow = S * a->B * a->Hq * (int64_t)a->rows;
+    P.ws_o_bytes = (size_t)cdiv(nrow * a->D * 4, 256) * 256;
+    P.ws_bytes = P.ws_o_bytes + (size_t)cdiv(nrow * 4, 256) * 256;
+  }
+  return P;
+}
+
+int run_small_d(const attn_args* a, void* ws, size_t ws_bytes, void* stream, bool merge, int32_t* n_chunks,
+                size_t* lse_offset) {
+  const SmallPlan P = small_plan(a);
+  if (ws_bytes < P.ws_bytes || (P.ws_bytes && !ws)) return ATTN_E_WORKSPACE;
+  if (P.ws_bytes && !aligned16(ws)) return ATTN_E_LAYOUT;
+  if ((int64_t)a->B * P.n_splits > 65535) return ATTN_E_ARG;  // grid z
   gqa::SmallDParams p;
   memset(&p, 0, sizeof(p));
   p.q = static_cast<const uint16_t*>(a->q.ptr);
@@ -234,7 +276,24 @@ int run_small_d(const attn_args* a, void* stream) {
   p.kv_offset = (int)a->kv_offset, p.kv_len = (int)a->kv_len, p.causal = a->causal;
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   p.scale_log2 = scale * 1.4426950408889634f;
-  if (gqa::launch_small_d(p, a->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
+  p.n_splits = P.n_splits, p.keys_per_split = P.keys_per_split;
+  if (P.n_splits > 1) {
+    p.part_o = static_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_o_bytes);
+  }
+  if (n_chunks) *n_chunks = P.n_splits;
+  if (lse_offset) *lse_offset = P.n_splits > 1 ? P.ws_o_bytes : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (gqa::launch_small_d(p, a->dtype, s) != hipSuccess) return ATTN_E_HIP;
+  if (P.n_splits > 1 && merge) {
+    gqa::MergeParams mp;
+    memset(&mp, 0, sizeof(mp));  // no repair (these inputs are taken to be finite)
+    mp.part_o = p.part_o, mp.part_lse = p.part_lse, mp.gate = p.gate, mp.out = p.out;
+    mp.g_sb = p.g_sb, mp.g_sh = p.g_sh, mp.g_sr = p.g_sr;
+    mp.o_sb = p.o_sb, mp.o_sh = p.o_sh, mp.o_sr = p.o_sr;
+    mp.n_chunks = P.n_splits, mp.B = a->B, mp.Hq = a->Hq, mp.rows = a->rows, mp.D = a->D;
+    if (gqa::launch_merge(mp, a->dtype, s) != hipSuccess) return ATTN_E_HIP;
+  }
   return ATTN_OK;
 }
 
@@ -242,11 +301,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
             int32_t* n_chunks = nullptr, size_t* lse_offset = nullptr) {
   int st = validate(a, op);
   if (st) return st;
-  if (a->D != kHeadDim) {
-    if (n_chunks) *n_chunks = 1;
-    if (lse_offset) *lse_offset = 0;
-    return run_small_d(a, stream);
-  }
+  if (a->D != kHeadDim) return run_small_d(a, ws, ws_bytes, stream, merge, n_chunks, lse_offset);
   Plan P;
   st = make_plan(a, op, &P);
   if (st) return st;
@@ -301,7 +356,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
     mp.out = p.out;
     mp.g_sb = p.g_sb, mp.g_sh = p.g_sh, mp.g_sr = p.g_sr;
     mp.o_sb = p.o_sb, mp.o_sh = p.o_sh, mp.o_sr = p.o_sr;
-    mp.n_chunks = P.n_splits, mp.B = a->B, mp.Hq = a->Hq, mp.rows = a->rows;
+    mp.n_chunks = P.n_splits, mp.B = a->B, mp.Hq = a->Hq, mp.rows = a->rows, mp.D = kHeadDim;
     gqa::RepairParams& f = mp.fix;  // the inputs of this main pass, for the merge's repair
     f.q = p.q, f.k = p.k, f.v = p.v, f.mask = p.mask;
     f.q_sb = p.q_sb, f.q_sh = p.q_sh, f.q_sr = p.q_sr;
@@ -386,8 +441,8 @@ int attn_workspace_bytes(const attn_args* a, int op, size_t* bytes) {
     *bytes = L.s_bytes + L.p_bytes + L.l_bytes;
     return ATTN_OK;
   }
-  if (a->D != kHeadDim) {  // the fused pass for head dims 64 and 128 needs none
-    *bytes = 0;
+  if (a->D != kHeadDim) {  // the fused pass for head dims 64 and 128: partials of its splits
+    *bytes = small_plan(a).ws_bytes;
     return ATTN_OK;
   }
   Plan P;
@@ -412,11 +467,13 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
     info->rows_per_wave = 32;
     info->waves_per_block = 1;
     info->n_row_tiles = (a->rows + 31) / 32;
-    info->n_splits = 1;
-    info->keys_per_split = (int)a->kv_len;
+    const SmallPlan P = small_plan(a);
+    info->n_splits = P.n_splits;
+    info->keys_per_split = P.keys_per_split;
     info->keys_per_tile = kKeysPerTile;
     info->lds_bytes = 2 * 32 * (a->D + 8) * 2;
-    info->grid_blocks = (int64_t)info->n_row_tiles * a->Hq * a->B;
+    info->grid_blocks = (int64_t)info->n_row_tiles * a->Hq * a->B * P.n_splits;
+    info->workspace_bytes = (int64_t)P.ws_bytes;
     info->chunk_sizes[0] = info->group_size;
     return ATTN_OK;
   }
@@ -547,7 +604,7 @@ int attn_merge(const merge_args* a, void* stream) {
   if (!a) return ATTN_E_NULL;
   if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
   if (a->B <= 0 || a->Hq <= 0) return ATTN_E_HEADS;
-  if (a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
+  if (a->D != ATTN_HEAD_DIM && a->D != 64 && a->D != 128) return ATTN_E_HEAD_DIM;
   if (a->rows < 1) return ATTN_E_ROWS;
   if (a->n_chunks < 1) return ATTN_E_ARG;
   if ((int64_t)a->B * a->Hq * a->rows > (int64_t)INT32_MAX) return ATTN_E_ARG;  // rows are indexed in 32 bits
@@ -563,7 +620,7 @@ int attn_merge(const merge_args* a, void* stream) {
   p.out = static_cast<uint16_t*>(a->out.ptr);
   p.g_sb = a->gate.stride_b, p.g_sh = a->gate.stride_h, p.g_sr = a->gate.stride_row;
   p.o_sb = a->out.stride_b, p.o_sh = a->out.stride_h, p.o_sr = a->out.stride_row;
-  p.n_chunks = a->n_chunks, p.B = a->B, p.Hq = a->Hq, p.rows = a->rows;
+  p.n_chunks = a->n_chunks, p.B = a->B, p.Hq = a->Hq, p.rows = a->rows, p.D = a->D;
   if (gqa::launch_merge(p, a->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
 }

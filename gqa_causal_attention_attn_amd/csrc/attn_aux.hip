@@ -144,8 +144,9 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
   const int b = (int)(bh / (uint32_t)p.Hq);
   const int h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
   const int d0 = 4 * lane;
+  const int dl = min(d0, p.D - 4);  // lanes past the head dim re-read its last 4 dims and store nothing
   const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
-  const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
+  const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + dl);
 
   // acc and wsum are kept relative to ref, the largest lse seen so far (the same in every
   // wavefront: each pass's largest lse is shared through LDS)
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
     for (int j = 0; j < kMergeBatch; ++j) {
       const int cc = min(c0 + wave + j * kMergeWaves, p.n_chunks - 1);
       lc[j] = p.part_lse[(int64_t)cc * n_rows + row_id];
-      oc[j] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * kHeadDim + d0);
+      oc[j] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * p.D + dl);
     }
     float top = -INFINITY;
 #pragma unroll
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
   u32x2 ow;
   ow[0] = pack2<DT>(res[0], res[1]);
   ow[1] = pack2<DT>(res[2], res[3]);
-  *reinterpret_cast<u32x2*>(orow + d0) = ow;
+  if (d0 < p.D) *reinterpret_cast<u32x2*>(orow + d0) = ow;
 }
 
 // Few chunks (prompt blocks split a handful of ways): one wavefront per row, four rows per
@@ -245,17 +246,18 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   const int b = (int)(bh / (uint32_t)p.Hq);
   const int h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
   const int d0 = 4 * lane;
+  const int dl = min(d0, p.D - 4);  // lanes past the head dim re-read its last 4 dims and store nothing
   // every load is unconditional (chunk indices past the last one re-read the last one) so
   // they are all in flight together; chunks past the last one are selected out below
   float lc[kFewChunks];
   f32x4 oc[kFewChunks];
   const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
-  const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
+  const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + dl);
 #pragma unroll
   for (int c = 0; c < kFewChunks; ++c) {
     const int cc = min(c, p.n_chunks - 1);
     lc[c] = p.part_lse[(int64_t)cc * n_rows + row_id];
-    oc[c] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * kHeadDim + d0);
+    oc[c] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * p.D + dl);
   }
   float top = -INFINITY;
   bool nan_l = false;  // a chunk whose lse is NaN makes the row NaN, as the unsplit definition does
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   u32x2 ow;
   ow[0] = pack2<DT>(res[0], res[1]);
   ow[1] = pack2<DT>(res[2], res[3]);
-  *reinterpret_cast<u32x2*>(orow + d0) = ow;
+  if (d0 < p.D) *reinterpret_cast<u32x2*>(orow + d0) = ow;
 }
 
 // One 16-byte chunk per thread.  Workgroup row y = (tensor, b, g); x runs over (row r, chunk c

@@ -76,6 +76,7 @@ struct MergeParams {
   int64_t g_sb, g_sh, g_sr;
   int64_t o_sb, o_sh, o_sr;
   int n_chunks, B, Hq, rows;
+  int D;  // head dim: 256, 128 or 64 (the partials' row length); the repair is for 256 only
   RepairParams fix;
 };
 
@@ -134,6 +135,10 @@ struct SmallDParams {
   int64_t o_sb, o_sh, o_sr;
   int D, B, Hq, G, rows, kv_offset, kv_len, causal;
   float scale_log2;
+  int n_splits;        // KV splits (1: the output is written; else the partials below)
+  int keys_per_split;  // multiple of 32
+  float* part_o;       // [n_splits, B, Hq, rows, D] when n_splits > 1
+  float* part_lse;     // [n_splits, B, Hq, rows]
 };
 
 // Launchers (return hipGetLastError()).  dtype 0 = bf16, 1 = fp16; mask_kind as attn_mask_kind.

@@ -4,8 +4,10 @@
 // kernel-contract commit), for the smaller head dims of the family ("perf(qwen36): qualify M4
 // head-256 attention", Summary: other head dims exist and take their own route rather than the
 // head-256 one).  A plainer kernel than the head-256 one: one wavefront per workgroup, 32 query
-// rows of one head, every key of the row tile's range in 32-key tiles staged in LDS by the
-// wavefront itself (rows padded by 16 bytes), no KV split and no merge.
+// rows of one head and one KV split of the row tile's key range, in 32-key tiles staged in LDS
+// by the wavefront itself (rows padded by 16 bytes).  With several splits the epilogue writes
+// the normalised partial o and its natural-log lse (the head-256 partial format, rows of D)
+// for the merge.
 //
 //   S^T[key, row]  = K[key, :] . Q[row, :]           A = K (LDS), B = Q (VGPRs), D/16 MFMAs
 //   O^T[dim, row] += V^T[dim, key] . P^T[key, row]   A = V^T gathered from LDS, B = P
@@ -29,6 +31,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -69,12 +72,13 @@ __global__ __launch_bounds__(64) void attn_small_d_kernel(const SmallDParams p) 
   __shared__ __attribute__((aligned(16))) uint16_t vs[32 * kRow];
   const int lane = threadIdx.x, li = lane & 31, hf = lane >> 5;
   const int r0 = blockIdx.x * 32;
-  const int h = blockIdx.y, b = blockIdx.z, g = h / p.G;
+  const int h = blockIdx.y, b = blockIdx.z / p.n_splits, split = blockIdx.z - b * p.n_splits, g = h / p.G;
   const int row = r0 + li;
   const bool valid = row < p.rows;
   const int lim = valid ? (p.causal ? min(p.kv_len, p.kv_offset + row + 1) : p.kv_len) : 0;
   const int last = min(r0 + 31, p.rows - 1);
-  const int kv_end = p.causal ? min(p.kv_len, p.kv_offset + last + 1) : p.kv_len;
+  const int kv_lo = split * p.keys_per_split;
+  const int kv_end = min(kv_lo + p.keys_per_split, p.causal ? min(p.kv_len, p.kv_offset + last + 1) : p.kv_len);
 
   // Q of this lane's row in the B-operand order: element t of q[kk] is dim 16 kk + 8 hf + t
   u32x4 q[D / 16];
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(64) void attn_small_d_kernel(const SmallDParams p) 
   for (int db = 0; db < kBlocks; ++db) o[db] = (f32x16){};
   float m = -INFINITY, l = 0.0f;
 
-  for (int j0 = 0; j0 < kv_end; j0 += 32) {
+  for (int j0 = kv_lo; j0 < kv_end; j0 += 32) {
     // stage the tile: 32 rows of K and of V, D / 8 16-byte chunks each; lane l copies chunks
     // l, l + 64, ... (keys past kv_len re-read the last key; every row masks them)
 #pragma unroll
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(64) void attn_small_d_kernel(const SmallDParams p) 
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = j0 + key_of(i, hf);
-      s[i] = j < lim ? s[i] * p.scale_log2 : -INFINITY;
+      s[i] = j < lim && j < kv_end ? s[i] * p.scale_log2 : -INFINITY;
       mt = fmaxf(mt, s[i]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -157,6 +161,21 @@ __global__ __launch_bounds__(64) void attn_small_d_kernel(const SmallDParams p) 
 
   if (!valid) return;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // a row with no admissible key gives 0
+  if (p.n_splits > 1) {
+    // this split's partial: o / l (dims 32 db + 8 a + 4 hf + t) and lse = ln 2 (m + log2 l)
+    const int64_t row_id = (((int64_t)split * p.B + b) * p.Hq + h) * p.rows + row;
+    float* prow = p.part_o + row_id * D;
+#pragma unroll
+    for (int db = 0; db < kBlocks; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * a + 4 * hf) =
+            (f32x4){o[db][4 * a] * inv, o[db][4 * a + 1] * inv, o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv};
+      }
+    }
+    if (hf == 0) p.part_lse[row_id] = l > 0.0f ? (m + __log2f(l)) * 0.6931471805599453f : -INFINITY;
+    return;
+  }
   const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)row * p.g_sr;
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)row * p.o_sr;
   // accumulator element i of lane l: dim 32 db + 8 (i / 4) + 4 hf + i % 4 of row l % 32
@@ -182,7 +201,7 @@ __global__ __launch_bounds__(64) void attn_small_d_kernel(const SmallDParams p) 
 
 template <int DT>
 void launch_small_d_t(const SmallDParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.rows + 31) / 32), (unsigned)p.Hq, (unsigned)p.B);
+  const dim3 grid((unsigned)((p.rows + 31) / 32), (unsigned)p.Hq, (unsigned)(p.B * p.n_splits));
   if (p.D == 64) hipLaunchKernelGGL((attn_small_d_kernel<DT, 64>), grid, dim3(64), 0, stream, p);
   else hipLaunchKernelGGL((attn_small_d_kernel<DT, 128>), grid, dim3(64), 0, stream, p);
 }

@@ -166,11 +166,11 @@ typedef struct {
   int32_t B;
   int32_t Hq;
   int32_t rows;
-  int32_t D;
-  const float* partial_o;   /* [n_chunks, B, Hq, rows, 256] fp32, contiguous, normalised per chunk */
+  int32_t D;                /* head dim: 256, 128 or 64 (else ATTN_E_HEAD_DIM) */
+  const float* partial_o;   /* [n_chunks, B, Hq, rows, D] fp32, contiguous, normalised per chunk */
   const float* partial_lse; /* [n_chunks, B, Hq, rows] fp32, contiguous, natural log; -Inf = empty chunk */
-  attn_tensor gate;         /* [B, Hq, rows, 256] */
-  attn_tensor out;          /* [B, Hq, rows, 256], written */
+  attn_tensor gate;         /* [B, Hq, rows, D] */
+  attn_tensor out;          /* [B, Hq, rows, D], written */
 } merge_args;
 
 /* The resolved plan of one call (what would run, for logging and validation). */
@@ -234,14 +234,16 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info);
  * keys, in the epilogue (one split) or in the merge (several). */
 int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
 /* Head dims 64 and 128 (attn_prefill, attn_decode, attn_prefill_partials) run a plainer fused
- * pass of their own: no workspace (attn_workspace_bytes reports 0), one chunk, no mask
- * (ATTN_E_MASK), scale = 0 means 1 / sqrt(head_dim), inputs taken to be finite. */
+ * pass of their own: one wavefront per 32 rows of a head, split over KV when those are fewer
+ * than the chip holds (the workspace then holds the partials, rows of head_dim, and the merge
+ * follows), one head chunk, no mask (ATTN_E_MASK), scale = 0 means 1 / sqrt(head_dim),
+ * inputs taken to be finite (no repair). */
 
 /* The main pass of attn_prefill alone, for callers that overlap one query block's merge with
  * the next block's main pass (two workspaces, the merges on a second stream).  *n_chunks
  * receives the number of KV chunks of the plan.  With *n_chunks = 1 the call is complete and out
  * is written.  With *n_chunks > 1 out is not written: the normalised partials stay in the
- * workspace, o at offset 0 ([n_chunks, B, Hq, rows, 256] fp32) and the natural-log lse at byte
+ * workspace, o at offset 0 ([n_chunks, B, Hq, rows, head_dim] fp32) and the natural-log lse at byte
  * offset *lse_offset ([n_chunks, B, Hq, rows] fp32), and the caller completes the call with
  * attn_merge (gate and out as here) on a stream ordered after this one, before the workspace is
  * reused.  Errors as attn_prefill, plus ATTN_E_NULL for a null n_chunks or lse_offset.  The

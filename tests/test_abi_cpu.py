@@ -151,13 +151,13 @@ def test_rejections(name, spec, status, op):
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_other_head_dims(D):
-    # head dims 64 and 128 run on their own fused pass (no workspace, no mask) and on the
+    # head dims 64 and 128 run on their own fused pass (no mask) and on the
     # composed route; the append takes them; any other head dim fails closed everywhere
     lib = ga.lib()
     a = _good(D=D)
     n = C.c_size_t(1)
     for op in (_abi.OP_PREFILL, _abi.OP_DECODE):
-        assert lib.attn_workspace_bytes(C.byref(a), op, C.byref(n)) == 0 and n.value == 0
+        assert lib.attn_workspace_bytes(C.byref(a), op, C.byref(n)) == 0 and n.value == 0  # no split here
         info = ga.describe_plan(a, op)
         assert info["variant_name"] == f"fwd_small_d{D}" and info["n_splits"] == 1
     assert lib.attn_workspace_bytes(C.byref(a), _abi.OP_COMPOSED, C.byref(n)) == 0 and n.value > 0
@@ -173,6 +173,37 @@ def test_other_head_dims(D):
     ap.dtype, ap.B, ap.Hkv, ap.rows, ap.D, ap.kv_offset, ap.capacity = 0, 1, 4, 2, 96, 0, 16
     ap.k_new, ap.v_new, ap.k_cache, ap.v_cache = t, t, t, t
     assert lib.kv_append(C.byref(ap), None) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_small_head_dim_splits(D):
+    # the fused pass for head dims 64 and 128 splits the keys when its one-wavefront workgroups
+    # (32 rows of one head) number fewer than 2048, at least 8 tiles of 32 keys per split; the
+    # workspace holds fp32 partials of D per (split, b, h, row) and an lse per row, each part
+    # rounded up to 256 bytes
+    lib = ga.lib()
+    r256 = lambda x: (x + 255) // 256 * 256
+    cases = [  # (B, Hq, Hkv, rows, kv_offset, n_splits asked, splits expected, keys per split)
+        (2, 16, 2, 1, 32767, 0, 64, 512),      # one decode row at 32k: 32 workgroups before splitting
+        (1, 24, 4, 512, 32256, 0, 5, 6560),    # the last 512-row block of a 32k prompt
+        (1, 24, 4, 4, 100, 0, 1, 128),         # too few keys to split
+        (1, 24, 4, 512, 0, 0, 2, 256),         # the first block: 16 tiles, 5 splits wanted, 2 at most
+        (1, 8, 2, 33, 1000, 3, 3, 352),        # asked for 3
+    ]
+    for B, Hq, Hkv, rows, off, asked, S, kps in cases:
+        a = _good(D=D, B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off, n_splits=asked)
+        info = ga.describe_plan(a, _abi.OP_PREFILL)
+        assert (info["n_splits"], info["keys_per_split"]) == (S, kps), (B, Hq, rows, off, info)
+        nrow = S * B * Hq * rows
+        want = 0 if S == 1 else r256(nrow * D * 4) + r256(nrow * 4)
+        assert ga.workspace_bytes(a, _abi.OP_PREFILL) == want and info["workspace_bytes"] == want
+        assert info["grid_blocks"] == (rows + 31) // 32 * Hq * B * S
+        if S > 1:
+            assert lib.attn_prefill(C.byref(a), C.c_void_p(1 << 20), want - 1, None) == \
+                _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
+            assert lib.attn_prefill(C.byref(a), None, want, None) == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
+            assert lib.attn_prefill(C.byref(a), C.c_void_p((1 << 20) + 8), want, None) == \
+                _abi.STATUS_CODE["ATTN_E_LAYOUT"]
 
 
 def test_composed_workspace_and_rejections():

@@ -145,3 +145,37 @@ def test_fused_small_head_dims(D, rows, offset, causal, B):
     if rows <= 32:
         again = ga.decode(q, k, v, g, kv_offset=offset, kv_len=kv, causal=causal, head_chunk=1)
         assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+
+
+@needs_gpu
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fused_small_head_dims_split_keys(D, dtype):
+    # the same pass with its keys split (the planned count, then 1, 3 and 7 asked) and merged:
+    # 100 causal rows at offset 2900 (ragged last row tile, split bounds inside row tiles), and
+    # the main pass alone plus attn_merge giving the same bits as the whole call
+    _say("fused small D splits", D, dtype)
+    B, Hq, Hkv, rows, off = 2, 8, 2, 100, 2900
+    kv = off + rows
+    rng = syn.streams(5500 + D)
+    qb = syn.normal_bits(rng["q"], (B, Hq, rows, D), dtype)
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D), dtype)
+    kb = syn.normal_bits(rng["k"], (B, Hkv, kv, D), dtype)
+    vb = syn.normal_bits(rng["v"], (B, Hkv, kv, D), dtype)
+    q, g, k, v = (to_dev(x, dtype) for x in (qb, gb, kb, vb))
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off,
+                              kv_len=kv)
+    a = ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off, D=D)
+    assert ga.describe_plan(a, 0)["n_splits"] > 1
+    outs = {}
+    for ns in (0, 1, 3, 7):
+        outs[ns] = ga.prefill(q, k, v, g, kv_offset=off, n_splits=ns)
+        torch.cuda.synchronize()
+        _say(assert_close(syn.widen(to_bits(outs[ns]), dtype), ref, f"fused D={D} n_splits={ns}"))
+    ws = torch.empty(ga.workspace_bytes(ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off, D=D,
+                                                     n_splits=3), 0), dtype=torch.uint8, device="cuda")
+    out, parts = ga.prefill_partials(q, k, v, g, kv_offset=off, n_splits=3, workspace=ws)
+    assert parts is not None and parts[0].shape == (3, B, Hq, rows, D)
+    ga.merge(parts[0], parts[1], g, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), outs[3].view(torch.int16))
