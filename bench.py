@@ -452,7 +452,8 @@ def main():
                                       "(attn_prefill_composed), kv_append per block; events around the block loop",
                              **{f"q_block_{kk}": vv for kk, vv in comp.items()}},
         "prefill_small_head_dims": {"route": "fused pass for head dims 64 and 128 (one wavefront per 32 rows of a "
-                                             "head, keys split when the grid is small, then the merge), "
+                                             "head, two heads of a group sharing K/V tiles, keys split when "
+                                             "the grid is small, then the merge), "
                                              "24/4 heads, same prompt and blocks",
                                     **{f"head_dim_{kk}": vv for kk, vv in small.items()}},
         "decode": {"metric": "decode KV GB/s (35B-A3B shape, batch 2, 1 row at offset 32768, cold KV; "

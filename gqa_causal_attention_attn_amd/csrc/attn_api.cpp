@@ -216,12 +216,15 @@ inline int variant_of(const attn_args* a, const Plan& P) {
   return (P.mask_lds << 5) | (P.shape << 3) | (a->dtype << 2) | a->mask.kind;
 }
 
-// The fused pass for head dims 64 and 128 (no workspace, no split, no merge).
-// KV splits of the fused pass for head dims 64 and 128.  Its workgroups are one wavefront of
-// 32 rows of one head, about nine to a CU by LDS, so a block with fewer than ~2048 of them
-// splits its keys (at least 8 tiles of 32 per split) to fill the chip; partials and lse rows
-// as for head dim 256, rows of D.
+// Plan of the fused pass for head dims 64 and 128.  A workgroup holds hw wavefronts, each 32
+// rows of one head, for hw heads of one KV group that share its K/V tiles in LDS: two when G is
+// even (three or four left wave slots of a CU idle at D = 128, 237 registers a wavefront, and
+// measured slower).  About eight to twelve wavefronts fit a CU, so a block with fewer than
+// ~2048 wavefronts
+// splits its keys (at least 8 tiles of 32 per split) to fill the chip; partials and lse rows as
+// for head dim 256, rows of D.
 struct SmallPlan {
+  int hw;  // heads of one KV group per workgroup (one wavefront each), sharing the K/V tiles
   int n_splits, keys_per_split;
   size_t ws_o_bytes, ws_bytes;
 };
@@ -229,6 +232,8 @@ struct SmallPlan {
 SmallPlan small_plan(const attn_args* a) {
   SmallPlan P;
   memset(&P, 0, sizeof(P));
+  const int G = a->Hq / a->Hkv;
+  P.hw = G % 2 == 0 ? 2 : 1;
   const int64_t kv_hi = a->causal ? (a->kv_len < a->kv_offset + a->rows ? a->kv_len : a->kv_offset + a->rows)
                                   : a->kv_len;
   const int64_t n_kt = cdiv(kv_hi, kKeysPerTile);
@@ -276,7 +281,7 @@ int run_small_d(const attn_args* a, void* ws, size_t ws_bytes, void* stream, boo
   p.kv_offset = (int)a->kv_offset, p.kv_len = (int)a->kv_len, p.causal = a->causal;
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.n_splits = P.n_splits, p.keys_per_split = P.keys_per_split;
+  p.hw = P.hw, p.n_splits = P.n_splits, p.keys_per_split = P.keys_per_split;
   if (P.n_splits > 1) {
     p.part_o = static_cast<float*>(ws);
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_o_bytes);
@@ -464,15 +469,15 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
     info->group_size = a->Hq / a->Hkv;
     info->n_head_chunks = 1;
     info->head_chunk = info->group_size;
-    info->rows_per_wave = 32;
-    info->waves_per_block = 1;
-    info->n_row_tiles = (a->rows + 31) / 32;
     const SmallPlan P = small_plan(a);
+    info->rows_per_wave = 32;
+    info->waves_per_block = P.hw;
+    info->n_row_tiles = (a->rows + 31) / 32;
     info->n_splits = P.n_splits;
     info->keys_per_split = P.keys_per_split;
     info->keys_per_tile = kKeysPerTile;
     info->lds_bytes = 2 * 32 * (a->D + 8) * 2;
-    info->grid_blocks = (int64_t)info->n_row_tiles * a->Hq * a->B * P.n_splits;
+    info->grid_blocks = (int64_t)info->n_row_tiles * (a->Hq / P.hw) * a->B * P.n_splits;
     info->workspace_bytes = (int64_t)P.ws_bytes;
     info->chunk_sizes[0] = info->group_size;
     return ATTN_OK;

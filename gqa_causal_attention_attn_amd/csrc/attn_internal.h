@@ -135,6 +135,7 @@ struct SmallDParams {
   int64_t o_sb, o_sh, o_sr;
   int D, B, Hq, G, rows, kv_offset, kv_len, causal;
   float scale_log2;
+  int hw;              // heads (wavefronts) per workgroup: 2, or 1 when G is odd
   int n_splits;        // KV splits (1: the output is written; else the partials below)
   int keys_per_split;  // multiple of 32
   float* part_o;       // [n_splits, B, Hq, rows, D] when n_splits > 1

@@ -3,11 +3,12 @@
 // The same operation as the head_dim-256 main pass (TensorFold PR #1009, attention
 // kernel-contract commit), for the smaller head dims of the family ("perf(qwen36): qualify M4
 // head-256 attention", Summary: other head dims exist and take their own route rather than the
-// head-256 one).  A plainer kernel than the head-256 one: one wavefront per workgroup, 32 query
-// rows of one head and one KV split of the row tile's key range, in 32-key tiles staged in LDS
-// by the wavefront itself (rows padded by 16 bytes).  With several splits the epilogue writes
-// the normalised partial o and its natural-log lse (the head-256 partial format, rows of D)
-// for the merge.
+// head-256 one).  A plainer kernel than the head-256 one: HW (2, or 1 for an odd group)
+// wavefronts per workgroup, each 32 query rows of one head, HW heads of one KV group, and one
+// KV split of the row tile's key range, in 32-key tiles staged in LDS by all the wavefronts
+// together and read by each (rows padded by 16 bytes).  With several splits the epilogue
+// writes the normalised partial o and its natural-log lse (the head-256 partial format, rows
+// of D) for the merge.
 //
 //   S^T[key, row]  = K[key, :] . Q[row, :]           A = K (LDS), B = Q (VGPRs), D/16 MFMAs
 //   O^T[dim, row] += V^T[dim, key] . P^T[key, row]   A = V^T gathered from LDS, B = P
@@ -63,16 +64,17 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // Key (within the tile) of accumulator element i for lane half hf.
 __device__ __forceinline__ constexpr int key_of(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
 
-template <int DT, int D>
-__global__ __launch_bounds__(64) void attn_small_d_kernel(const SmallDParams p) {
+template <int DT, int D, int HW>
+__global__ __launch_bounds__(64 * HW) void attn_small_d_kernel(const SmallDParams p) {
   static_assert(D == 64 || D == 128, "head dims 64 and 128");
   constexpr int kRow = D + 8;  // LDS row stride in 16-bit elements (16 bytes of padding)
   constexpr int kBlocks = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t ks[32 * kRow];
   __shared__ __attribute__((aligned(16))) uint16_t vs[32 * kRow];
-  const int lane = threadIdx.x, li = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, hf = lane >> 5;
   const int r0 = blockIdx.x * 32;
-  const int h = blockIdx.y, b = blockIdx.z / p.n_splits, split = blockIdx.z - b * p.n_splits, g = h / p.G;
+  const int h0 = blockIdx.y * HW, h = h0 + (tid >> 6);  // HW divides G: one KV group
+  const int b = blockIdx.z / p.n_splits, split = blockIdx.z - b * p.n_splits, g = h0 / p.G;
   const int row = r0 + li;
   const bool valid = row < p.rows;
   const int lim = valid ? (p.causal ? min(p.kv_len, p.kv_offset + row + 1) : p.kv_len) : 0;
@@ -94,18 +96,21 @@ __global__ __launch_bounds__(64) void attn_small_d_kernel(const SmallDParams p) 
   float m = -INFINITY, l = 0.0f;
 
   for (int j0 = kv_lo; j0 < kv_end; j0 += 32) {
-    // stage the tile: 32 rows of K and of V, D / 8 16-byte chunks each; lane l copies chunks
-    // l, l + 64, ... (keys past kv_len re-read the last key; every row masks them)
+    // stage the tile: 32 rows of K and of V, D / 8 16-byte chunks each; thread t copies chunks
+    // t, t + 64 HW, ... (keys past kv_len re-read the last key; every row masks them)
+    constexpr int kChunks = 32 * (D / 8);
 #pragma unroll
-    for (int e = 0; e < 32 * (D / 8) / 64; ++e) {
-      const int c = lane + 64 * e, kr = c / (D / 8), cc = c % (D / 8);
+    for (int e = 0; e < (kChunks + 64 * HW - 1) / (64 * HW); ++e) {
+      const int c = tid + 64 * HW * e;
+      if (kChunks % (64 * HW) != 0 && c >= kChunks) break;
+      const int kr = c / (D / 8), cc = c % (D / 8);
       const int key = min(j0 + kr, p.kv_len - 1);
       *reinterpret_cast<u32x4*>(&ks[kr * kRow + 8 * cc]) =
           *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * p.k_st + 8 * cc);
       *reinterpret_cast<u32x4*>(&vs[kr * kRow + 8 * cc]) =
           *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * p.v_st + 8 * cc);
     }
-    __syncthreads();  // one wavefront: orders its LDS writes before the reads below
+    __syncthreads();  // the tile is in LDS before any wavefront reads it
 
     // scores (raw dot products) of this lane's row against keys key_of(i, hf)
     f32x16 s = {};
@@ -199,11 +204,17 @@ __global__ __launch_bounds__(64) void attn_small_d_kernel(const SmallDParams p) 
   }
 }
 
+template <int DT, int D>
+void launch_small_d_h(const SmallDParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.rows + 31) / 32), (unsigned)(p.Hq / p.hw), (unsigned)(p.B * p.n_splits));
+  if (p.hw == 2) hipLaunchKernelGGL((attn_small_d_kernel<DT, D, 2>), grid, dim3(128), 0, stream, p);
+  else hipLaunchKernelGGL((attn_small_d_kernel<DT, D, 1>), grid, dim3(64), 0, stream, p);
+}
+
 template <int DT>
 void launch_small_d_t(const SmallDParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.rows + 31) / 32), (unsigned)p.Hq, (unsigned)(p.B * p.n_splits));
-  if (p.D == 64) hipLaunchKernelGGL((attn_small_d_kernel<DT, 64>), grid, dim3(64), 0, stream, p);
-  else hipLaunchKernelGGL((attn_small_d_kernel<DT, 128>), grid, dim3(64), 0, stream, p);
+  if (p.D == 64) launch_small_d_h<DT, 64>(p, stream);
+  else launch_small_d_h<DT, 128>(p, stream);
 }
 
 }  // namespace

@@ -177,8 +177,8 @@ def test_other_head_dims(D):
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_small_head_dim_splits(D):
-    # the fused pass for head dims 64 and 128 splits the keys when its one-wavefront workgroups
-    # (32 rows of one head) number fewer than 2048, at least 8 tiles of 32 keys per split; the
+    # the fused pass for head dims 64 and 128 splits the keys when its wavefronts (32 rows of
+    # one head each, two heads of a group to a workgroup, one if G is odd) number fewer than 2048, at least 8 tiles of 32 keys per split; the
     # workspace holds fp32 partials of D per (split, b, h, row) and an lse per row, each part
     # rounded up to 256 bytes
     lib = ga.lib()
@@ -197,7 +197,10 @@ def test_small_head_dim_splits(D):
         nrow = S * B * Hq * rows
         want = 0 if S == 1 else r256(nrow * D * 4) + r256(nrow * 4)
         assert ga.workspace_bytes(a, _abi.OP_PREFILL) == want and info["workspace_bytes"] == want
-        assert info["grid_blocks"] == (rows + 31) // 32 * Hq * B * S
+        G = Hq // Hkv
+        hw = 2 if G % 2 == 0 else 1  # heads per workgroup
+        assert info["waves_per_block"] == hw
+        assert info["grid_blocks"] == (rows + 31) // 32 * (Hq // hw) * B * S
         if S > 1:
             assert lib.attn_prefill(C.byref(a), C.c_void_p(1 << 20), want - 1, None) == \
                 _abi.STATUS_CODE["ATTN_E_WORKSPACE"]

@@ -179,3 +179,24 @@ def test_fused_small_head_dims_split_keys(D, dtype):
     ga.merge(parts[0], parts[1], g, out=out)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), outs[3].view(torch.int16))
+
+
+@needs_gpu
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(24, 4), (6, 3), (5, 5), (16, 2)])
+def test_fused_small_head_dims_heads_per_workgroup(D, Hq, Hkv):
+    # workgroups of two heads of a KV group sharing K/V tiles (G 6, 2 and 8) and of one head
+    # (G 1); 70 causal rows at offset 1500 (ragged row tile), keys split as planned
+    _say("fused small D heads per workgroup", D, Hq, Hkv)
+    B, rows, off = 1, 70, 1500
+    kv = off + rows
+    rng = syn.streams(5600 + D + Hq)
+    qb = syn.normal_bits(rng["q"], (B, Hq, rows, D))
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D))
+    kb = syn.normal_bits(rng["k"], (B, Hkv, kv, D))
+    vb = syn.normal_bits(rng["v"], (B, Hkv, kv, D))
+    q, g, k, v = (to_dev(x) for x in (qb, gb, kb, vb))
+    out = ga.prefill(q, k, v, g, kv_offset=off)
+    torch.cuda.synchronize()
+    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off, kv_len=kv)
+    _say(assert_close(to_f64(out), ref, f"fused D={D} {Hq}/{Hkv}"))
