@@ -476,7 +476,7 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
     info->n_splits = P.n_splits;
     info->keys_per_split = P.keys_per_split;
     info->keys_per_tile = kKeysPerTile;
-    info->lds_bytes = 2 * 32 * (a->D + 8) * 2;
+    info->lds_bytes = 32 * (a->D + 8) * 2 + 32 * (a->D == 64 ? a->D + 32 : a->D + 8) * 2;  // K and V tiles
     info->grid_blocks = (int64_t)info->n_row_tiles * (a->Hq / P.hw) * a->B * P.n_splits;
     info->workspace_bytes = (int64_t)P.ws_bytes;
     info->chunk_sizes[0] = info->group_size;

@@ -200,6 +200,7 @@ def test_small_head_dim_splits(D):
         G = Hq // Hkv
         hw = 2 if G % 2 == 0 else 1  # heads per workgroup
         assert info["waves_per_block"] == hw
+        assert info["lds_bytes"] == {64: 10752, 128: 17408}[D]  # K and V tiles of 32 padded rows
         assert info["grid_blocks"] == (rows + 31) // 32 * (Hq // hw) * B * S
         if S > 1:
             assert lib.attn_prefill(C.byref(a), C.c_void_p(1 << 20), want - 1, None) == \
