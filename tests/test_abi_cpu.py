@@ -275,6 +275,9 @@ def test_append_and_merge_rejections():
     assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_LAYOUT"]
     m.partial_o = None
     assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    for D in (96, 32, 512):  # head dims 256, 128 and 64 only
+        m2 = _abi.MergeArgs(0, 2, 1, 2, 3, D, 1 << 20, 1 << 20, t, t)
+        assert lib.attn_merge(C.byref(m2), None) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
 
 
 def test_keep_rejections():

@@ -316,15 +316,17 @@ def test_kv_keep_is_bit_exact(dtype):
 
 
 @needs_gpu
-# few-chunk pass; many-chunk pass with 4, 8 and 16 wavefronts per row, in one round and in two
+# few-chunk pass; many-chunk pass with 4, 8 and 16 wavefronts per row, in one round and in two;
+# rows of 256, 128 and 64 (lanes past the head dim store nothing)
+@pytest.mark.parametrize("D", [256, 128, 64])
 @pytest.mark.parametrize("n_chunks", [4, 12, 21, 40, 100])
-def test_merge_matches_oracle(n_chunks):
+def test_merge_matches_oracle(n_chunks, D):
     rng = syn.streams(8)
     B, Hq, Hkv, rows, kv = 1, 8, 2, 5, 90
-    q = syn.widen(syn.normal_bits(rng["q"], (B, Hq, rows, 256)))
-    k = syn.widen(syn.normal_bits(rng["k"], (B, Hkv, kv, 256)))
-    v = syn.widen(syn.normal_bits(rng["v"], (B, Hkv, kv, 256)))
-    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, 256))
+    q = syn.widen(syn.normal_bits(rng["q"], (B, Hq, rows, D)))
+    k = syn.widen(syn.normal_bits(rng["k"], (B, Hkv, kv, D)))
+    v = syn.widen(syn.normal_bits(rng["v"], (B, Hkv, kv, D)))
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D))
     step = max(1, 120 // n_chunks)
     chunks = [(c * step, (c + 1) * step) for c in range(n_chunks)]  # the chunks past key 90 are empty
     o, l_ = reference.partials(q, k, v, n_kv_heads=Hkv, kv_offset=kv - rows, kv_len=kv, chunks=chunks)
@@ -332,12 +334,14 @@ def test_merge_matches_oracle(n_chunks):
     # one row empty in every chunk, with NaN partials: never multiplied in, the row is 0
     l32[:, 0, 3, 2] = -np.inf
     o32[:, 0, 3, 2, :] = np.nan
-    out = ga.merge(torch.from_numpy(o32).cuda(), torch.from_numpy(l32).cuda(), to_dev(gb))
+    # out starts as NaN: every element of the head dim is written, and nothing past it exists
+    out = torch.full((B, Hq, rows, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ga.merge(torch.from_numpy(o32).cuda(), torch.from_numpy(l32).cuda(), to_dev(gb), out=out)
     ref = reference.merge(o, l_, syn.widen(gb))
     ref[0, 3, 2, :] = 0.0
     got = to_f64(out)
     assert np.all(got[0, 3, 2, :] == 0.0)
-    _say(assert_close(got, ref, f"merge {n_chunks} chunks"))
+    _say(assert_close(got, ref, f"merge {n_chunks} chunks, D={D}"))
 
 
 @needs_gpu
