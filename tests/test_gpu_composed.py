@@ -200,3 +200,28 @@ def test_fused_small_head_dims_heads_per_workgroup(D, Hq, Hkv):
     torch.cuda.synchronize()
     ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off, kv_len=kv)
     _say(assert_close(to_f64(out), ref, f"fused D={D} {Hq}/{Hkv}"))
+
+
+@needs_gpu
+@pytest.mark.parametrize("D", [128, 64])
+def test_fused_small_head_dims_32k_prompt_sampled(D):
+    # the benchmark's launch configuration for these head dims: a 32768-token prompt at 24 query
+    # heads over 4 KV heads in blocks of 512 rows (kv_append + attn_prefill, keys split as
+    # planned); rows sampled across the prompt and every head against the oracle
+    _say("fused small D 32k", D)
+    N, Hq, Hkv = 32768, 24, 4
+    rng = syn.streams(5700 + D)
+    qb = syn.normal_bits(rng["q"], (1, Hq, N, D))
+    kb = syn.normal_bits(rng["k"], (1, Hkv, N, D))
+    vb = syn.normal_bits(rng["v"], (1, Hkv, N, D))
+    gb = syn.normal_bits(rng["gate"], (1, Hq, N, D))
+    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    kc = torch.zeros((1, Hkv, N, D), dtype=q.dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    out = ga.prompt_prefill(q, k, v, g, kc, vc, q_block=512)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k) and torch.equal(vc, v)
+    rows = np.array([0, 31, 32, 511, 512, 4097, 16383, 20000, 32255, 32256, 32767])
+    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=0, kv_len=N,
+                              rows=rows)
+    _say(assert_close(to_f64(out[:, :, rows]), ref, f"fused D={D} 32k sampled"))
