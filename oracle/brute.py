@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import math
 
-__all__ = ["attention"]
+__all__ = ["attention", "probabilities"]
 
 
 def _sigmoid(x: float) -> float:
@@ -68,4 +68,44 @@ def attention(q, k, v, gate, *, n_kv_heads: int, kv_offset: int, kv_len: int, ca
                 out_h.append(row)
             out_b.append(out_h)
         out.append(out_b)
+    return out
+
+
+def probabilities(q, k, *, n_kv_heads: int, kv_offset: int, kv_len: int, causal: bool = True, scale=None,
+                  mask=None, mask_kind=None, b: int = 0, h: int = 0):
+    """Softmax weights of one (b, h): p[r][j] = exp(s_j - m) / sum over A of exp(s_i - m) for j in A,
+    0 off A (steps 2, 4 and 5 of the definition), one scalar at a time.
+
+    q: [B][Hq][R][D]; k: [B][Hkv][cap][D]; mask [Bm][Hm][R][kv_len].  Returns [R][kv_len] floats.
+    """
+    Hq, R, D = len(q[0]), len(q[0][0]), len(q[0][0][0])
+    G = Hq // n_kv_heads
+    g = h // G
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = []
+    for r in range(R):
+        scores = {}
+        for j in range(kv_len):
+            if causal and j > kv_offset + r:
+                continue
+            add = 0.0
+            if mask is not None and mask_kind not in (None, "none"):
+                mv = mask[b if len(mask) > 1 else 0][h if len(mask[0]) > 1 else 0][r][j]
+                if mask_kind == "bool":
+                    if not mv:
+                        continue
+                elif mv == -math.inf:
+                    continue
+                else:
+                    add = float(mv)
+            scores[j] = scale * math.fsum(float(q[b][h][r][d]) * float(k[b][g][j][d]) for d in range(D)) + add
+        row = [0.0] * kv_len
+        if scores:
+            top = max(scores.values())
+            weights = {j: math.exp(s - top) for j, s in scores.items()}
+            total = math.fsum(weights.values())
+            for j, w in weights.items():
+                row[j] = w / total
+        out.append(row)
     return out

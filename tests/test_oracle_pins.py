@@ -165,6 +165,40 @@ def test_probabilities_sum_to_one_and_future_is_zero():
             assert np.all(p[r, :13 + r + 1] > 0.0)
 
 
+@pytest.mark.parametrize("case", range(len(TINY_CASES)))
+def test_probabilities_agree_with_brute_force(case):
+    # every head of every group, against math.fsum / math.exp loops (the mask cases carry finite
+    # nonzero additive values, and GQA groups of 2, 3, 4 and 8 heads)
+    B, Hq, Hkv, rows, off, causal, dim, mkind = TINY_CASES[case]
+    q, k, v, g, kv_len = _tiny(40 + case, B, Hq, Hkv, rows, off, dim)
+    mask, kind = _mask_for(mkind, np.random.default_rng(50 + case), B, Hq, rows, kv_len)
+    for b in range(B):
+        for h in range(Hq):
+            ref = reference.probabilities(q, k, n_kv_heads=Hkv, kv_offset=off, kv_len=kv_len, causal=causal,
+                                          mask=mask, mask_kind=kind, b=b, h=h)
+            bf = np.array(brute.probabilities(q.tolist(), k.tolist(), n_kv_heads=Hkv, kv_offset=off, kv_len=kv_len,
+                                              causal=causal, mask=None if mask is None else mask.tolist(),
+                                              mask_kind=kind, b=b, h=h))
+            assert np.max(np.abs(ref - bf)) <= 1e-13
+
+
+def test_probabilities_controls_are_caught():
+    # planted mistakes in the weights (a wrong scale; the wrong KV head for a query head) must
+    # miss the brute-force weights by far more than rounding
+    B, Hq, Hkv, rows, off = 1, 8, 2, 5, 6
+    q, k, v, g, kv_len = _tiny(60, B, Hq, Hkv, rows, off)
+    bf = [np.array(brute.probabilities(q.tolist(), k.tolist(), n_kv_heads=Hkv, kv_offset=off, kv_len=kv_len, h=h))
+          for h in range(Hq)]
+    for h in range(Hq):
+        wrong_scale = reference.probabilities(q, k, n_kv_heads=Hkv, kv_offset=off, kv_len=kv_len, h=h, scale=1 / 8)
+        assert np.max(np.abs(wrong_scale - bf[h])) > 1e-3
+        # h % Hkv instead of h // G: the other group's keys (for heads whose group changes)
+        k_swapped = k[:, ::-1].copy()
+        if (h % Hkv) != (h // (Hq // Hkv)):
+            wrong_group = reference.probabilities(q, k_swapped, n_kv_heads=Hkv, kv_offset=off, kv_len=kv_len, h=h)
+            assert np.max(np.abs(wrong_group - bf[h])) > 1e-3
+
+
 @pytest.mark.parametrize("rows,G", [(4, 12), (6, 6), (9, 8), (32, 8), (5, 8)])
 def test_head_chunked_equals_unchunked_bitwise(rows, G):
     Hkv = 2
