@@ -25,10 +25,9 @@ struct Plan {
   int n_chunks;
   int chunk_sizes[ATTN_MAX_CHUNKS];
   int blocks_per_chunk;
-  int shape;  // 0: 4 wavefronts x 1 column block, 1: 4 x 2, 2: 8 x 1
+  int shape;     // 0: 4 wavefronts of one column block each, 2: 8 wavefronts (1 is not used)
   int mask_lds;  // the main pass stages each tile's mask rows in LDS
-  int waves;  // wavefronts per workgroup
-  int nb;     // column blocks per wavefront
+  int waves;     // wavefronts per workgroup
   int n_tiles;
   int n_splits;
   int keys_per_split;
@@ -100,7 +99,8 @@ int validate(const attn_args* a, int op) {
   }
   if (op == ATTN_OP_COMPOSED) {
     if (m.kind != ATTN_MASK_NONE) return ATTN_E_MASK;
-    if ((int64_t)a->B * a->Hq > 65535 || (int64_t)a->B * a->Hq * a->rows > (int64_t)INT32_MAX) return ATTN_E_ARG;
+    // the softmax pass runs one workgroup of 256 per row
+    if ((int64_t)a->B * a->Hq > 65535 || !gqa::grid_fits((int64_t)a->B * a->Hq * a->rows, 256)) return ATTN_E_ARG;
   }
   return ATTN_OK;
 }
@@ -143,8 +143,7 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   const int64_t n_blocks = (int64_t)P->n_chunks * P->blocks_per_chunk;
   P->shape = n_blocks <= 4 ? 0 : 2;
   P->waves = P->shape == 2 ? 8 : 4;
-  P->nb = P->shape == 1 ? 2 : 1;
-  P->n_tiles = (int)cdiv(n_blocks, (int64_t)P->waves * P->nb);
+  P->n_tiles = (int)cdiv(n_blocks, (int64_t)P->waves);
 
   // KV splits depend only on the unchunked shape, so every head-chunk choice splits the keys
   // the same way and gives the same bits.
@@ -174,7 +173,7 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   // number of 16-byte chunks up to kv_len (the direct loads move 16-byte chunks and a chunk that
   // reaches past the mask's last word would read as zeros), spans < 2 GiB, and every
   // workgroup's (head, row) pairs cover at most kMaskStageLds / (32 x word size) rows.
-  if (a->mask.kind != ATTN_MASK_NONE && P->shape != 1) {
+  if (a->mask.kind != ATTN_MASK_NONE) {
     const attn_mask& m = a->mask;
     const int64_t esz = m.kind == ATTN_MASK_BOOL_U8 ? 1 : m.kind == ATTN_MASK_ADD ? 2 : 4;
     const int64_t msb = m.Bm == 1 ? 0 : m.stride_b;
@@ -182,7 +181,7 @@ int make_plan(const attn_args* a, int op, Plan* P) {
     bool ok = m.Hm == 1 && ((uintptr_t)m.ptr % 16) == 0 && (m.stride_row * esz) % 16 == 0 && (msb * esz) % 16 == 0 &&
               ((int64_t)a->kv_len * esz) % 16 == 0 && span < ((int64_t)1 << 31);
     const int64_t max_rows = gqa::kMaskStageLds / (gqa::kKeysPerTile * esz);
-    const int wg_blocks = P->waves * P->nb;
+    const int wg_blocks = P->waves;
     for (int t = 0; ok && t < P->n_tiles; ++t) {
       int64_t lo = INT64_MAX, hi = -1;
       for (int bj = t * wg_blocks; bj < (t + 1) * wg_blocks; ++bj) {
@@ -202,8 +201,10 @@ int make_plan(const attn_args* a, int op, Plan* P) {
     P->mask_lds = ok ? 1 : 0;
   }
   P->grid = (int64_t)a->B * a->Hkv * S * P->n_tiles;
-  if (P->grid > INT32_MAX) return ATTN_E_ARG;
-  if ((int64_t)a->B * a->Hq * a->rows > (int64_t)INT32_MAX) return ATTN_E_ARG;  // the merge indexes rows in 32 bits
+  if (P->grid > INT32_MAX || !gqa::grid_fits(P->grid, 64 * P->waves)) return ATTN_E_ARG;
+  const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
+  if (n_rows > (int64_t)INT32_MAX) return ATTN_E_ARG;  // the merge indexes rows in 32 bits
+  if (S > 1 && !gqa::merge_fits((int)S, n_rows)) return ATTN_E_ARG;
   if (S > 1) {
     const int64_t nrow = S * a->B * a->Hq * (int64_t)a->rows;
     P->ws_o_bytes = (size_t)cdiv(nrow * kHeadDim * 4, 256) * 256;
@@ -229,8 +230,10 @@ struct SmallPlan {
   size_t ws_o_bytes, ws_bytes;
 };
 
-SmallPlan small_plan(const attn_args* a) {
-  SmallPlan P;
+// The plan and the checks of its launch limits (grid z = B x splits, x = 32-row tiles of up to
+// 128 threads, and the merge), so that the planning calls and the run reject the same shapes.
+int small_plan(const attn_args* a, SmallPlan* out) {
+  SmallPlan& P = *out;
   memset(&P, 0, sizeof(P));
   const int G = a->Hq / a->Hkv;
   P.hw = G % 2 == 0 ? 2 : 1;
@@ -256,15 +259,19 @@ SmallPlan small_plan(const attn_args* a) {
     P.ws_o_bytes = (size_t)cdiv(nrow * a->D * 4, 256) * 256;
     P.ws_bytes = P.ws_o_bytes + (size_t)cdiv(nrow * 4, 256) * 256;
   }
-  return P;
+  const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
+  if ((int64_t)a->B * S > 65535 || !gqa::grid_fits(cdiv(a->rows, 32), 128)) return ATTN_E_ARG;
+  if (n_rows > (int64_t)INT32_MAX || (S > 1 && !gqa::merge_fits((int)S, n_rows))) return ATTN_E_ARG;
+  return ATTN_OK;
 }
 
 int run_small_d(const attn_args* a, void* ws, size_t ws_bytes, void* stream, bool merge, int32_t* n_chunks,
                 size_t* lse_offset) {
-  const SmallPlan P = small_plan(a);
+  SmallPlan P;
+  const int st = small_plan(a, &P);
+  if (st) return st;
   if (ws_bytes < P.ws_bytes || (P.ws_bytes && !ws)) return ATTN_E_WORKSPACE;
   if (P.ws_bytes && !aligned16(ws)) return ATTN_E_LAYOUT;
-  if ((int64_t)a->B * P.n_splits > 65535) return ATTN_E_ARG;  // grid z
   gqa::SmallDParams p;
   memset(&p, 0, sizeof(p));
   p.q = static_cast<const uint16_t*>(a->q.ptr);
@@ -398,7 +405,7 @@ const char* attn_strerror(int status) {
     case ATTN_E_NULL: return "a required pointer is NULL";
     case ATTN_E_DTYPE: return "unknown dtype";
     case ATTN_E_HEADS: return "invalid head counts (batch, query or KV heads not positive, or not a whole group)";
-    case ATTN_E_HEAD_DIM: return "head_dim must be 256";
+    case ATTN_E_HEAD_DIM: return "unsupported head_dim (256, 128 or 64; kv_keep takes 256 only)";
     case ATTN_E_ROWS: return "invalid number of query rows";
     case ATTN_E_KV: return "invalid KV offset, length or capacity";
     case ATTN_E_MASK: return "invalid mask (kind, extents, strides or pointer)";
@@ -418,10 +425,10 @@ const char* attn_variant_name(int variant) {
       "fwd_mfma32x32x16_bf16_maskf32_" SHAPE, "fwd_mfma32x32x16_f16_" SHAPE, "fwd_mfma32x32x16_f16_maskbool_" SHAPE, \
       "fwd_mfma32x32x16_f16_maskadd_" SHAPE, "fwd_mfma32x32x16_f16_maskf32_" SHAPE
   static const char* const names[64] = {
-      GQA_NAMES("4x1"),           GQA_NAMES("4x2"),           GQA_NAMES("8x1"),           GQA_NAMES("unused"),
+      GQA_NAMES("4x1"),           GQA_NAMES("unused"),        GQA_NAMES("8x1"),           GQA_NAMES("unused"),
       GQA_NAMES("4x1_ldsmask"),   GQA_NAMES("unused"),        GQA_NAMES("8x1_ldsmask"),   GQA_NAMES("unused")};
 #undef GQA_NAMES
-  static const bool used[8] = {true, true, true, false, true, false, true, false};  // shape groups
+  static const bool used[8] = {true, false, true, false, true, false, true, false};  // shape groups
   if (variant == 64) return "fwd_small_d64";
   if (variant == 65) return "fwd_small_d128";
   return (variant >= 0 && variant < 64 && used[variant >> 3]) ? names[variant] : "unknown";
@@ -447,7 +454,10 @@ int attn_workspace_bytes(const attn_args* a, int op, size_t* bytes) {
     return ATTN_OK;
   }
   if (a->D != kHeadDim) {  // the fused pass for head dims 64 and 128: partials of its splits
-    *bytes = small_plan(a).ws_bytes;
+    SmallPlan P;
+    st = small_plan(a, &P);
+    if (st) return st;
+    *bytes = P.ws_bytes;
     return ATTN_OK;
   }
   Plan P;
@@ -463,13 +473,15 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
   int st = validate(a, op);
   if (st) return st;
   if (a->D != kHeadDim) {  // the fused pass for head dims 64 and 128: one plan
+    SmallPlan P;
+    st = small_plan(a, &P);
+    if (st) return st;
     memset(info, 0, sizeof(*info));
     info->op = op;
     info->variant = a->D == 64 ? 64 : 65;
     info->group_size = a->Hq / a->Hkv;
     info->n_head_chunks = 1;
     info->head_chunk = info->group_size;
-    const SmallPlan P = small_plan(a);
     info->rows_per_wave = 32;
     info->waves_per_block = P.hw;
     info->n_row_tiles = (a->rows + 31) / 32;
@@ -491,7 +503,7 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
   info->group_size = P.G;
   info->n_head_chunks = P.n_chunks;
   info->head_chunk = P.chunk;
-  info->rows_per_wave = P.nb * kPairsPerBlock;
+  info->rows_per_wave = kPairsPerBlock;
   info->waves_per_block = P.waves;
   info->n_row_tiles = P.n_tiles;
   info->n_splits = P.n_splits;
@@ -556,7 +568,9 @@ int kv_append(const kv_append_args* a, void* stream) {
   if (a->B <= 0 || a->Hkv <= 0) return ATTN_E_HEADS;
   if (a->D != 64 && a->D != 128 && a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
   if (a->rows < 1) return ATTN_E_ROWS;
-  if (a->kv_offset < 0 || a->capacity < 1 || a->kv_offset + a->rows > a->capacity || a->capacity > INT32_MAX)
+  // (the planted late-append build writes one row further: its bound moves with it)
+  if (a->kv_offset < 0 || a->capacity < 1 || a->kv_offset + a->rows + (GQA_CONTROL == 3 ? 1 : 0) > a->capacity ||
+      a->capacity > INT32_MAX)
     return ATTN_E_KV;
   const attn_tensor* ts[4] = {&a->k_new, &a->v_new, &a->k_cache, &a->v_cache};
   for (const attn_tensor* t : ts)
@@ -582,7 +596,7 @@ int kv_keep(const kv_keep_args* a, void* stream) {
   if (!a || !a->keep) return ATTN_E_NULL;
   if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
   if (a->B <= 0 || a->B > gqa::kKeepMaxBatch || a->Hkv <= 0) return ATTN_E_HEADS;
-  if ((int64_t)a->B * a->Hkv > INT32_MAX) return ATTN_E_HEADS;
+  if (!gqa::grid_fits((int64_t)a->B * a->Hkv, 256)) return ATTN_E_HEADS;  // one workgroup of 256 per (b, g)
   if (a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
   if (a->rows < 1 || a->rows > ATTN_MAX_DECODE_ROWS) return ATTN_E_ROWS;
   if (a->kv_offset < 0 || a->capacity < 1 || a->kv_offset + a->rows > a->capacity || a->capacity > INT32_MAX)
@@ -612,7 +626,8 @@ int attn_merge(const merge_args* a, void* stream) {
   if (a->D != ATTN_HEAD_DIM && a->D != 64 && a->D != 128) return ATTN_E_HEAD_DIM;
   if (a->rows < 1) return ATTN_E_ROWS;
   if (a->n_chunks < 1) return ATTN_E_ARG;
-  if ((int64_t)a->B * a->Hq * a->rows > (int64_t)INT32_MAX) return ATTN_E_ARG;  // rows are indexed in 32 bits
+  const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
+  if (n_rows > (int64_t)INT32_MAX || !gqa::merge_fits(a->n_chunks, n_rows)) return ATTN_E_ARG;  // 32-bit rows, launch size
   if (!a->partial_o || !a->partial_lse || !a->gate.ptr || !a->out.ptr) return ATTN_E_NULL;
   if (!aligned16(a->partial_o) || !aligned16(a->gate.ptr) || !aligned16(a->out.ptr) || !strides_ok(a->gate) ||
       !strides_ok(a->out) || (reinterpret_cast<uintptr_t>(a->partial_lse) & 3u))

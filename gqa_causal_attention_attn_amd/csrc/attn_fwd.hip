@@ -1,9 +1,9 @@
 // Main pass of gated causal GQA attention at head_dim 256 for gfx950 (CDNA4).
 //
 // One workgroup = one (batch b, KV head g, KV split s, tile of (head, row) pairs of that
-// group), one workgroup per CU.  Three shapes: eight wavefronts of one 32-pair column block
-// (prompts and long verify blocks: two wavefronts per SIMD), four wavefronts of one block
-// (short decode / verify, whose KV group fits in four blocks) and four of two blocks.  The
+// group), one workgroup per CU.  Two shapes: eight wavefronts of one 32-pair column block each
+// (prompts and long verify blocks: two wavefronts per SIMD) and four wavefronts of one block
+// (short decode / verify, whose KV group fits in four blocks).  The
 // group's K and V are streamed through LDS in 32-key tiles and every wavefront reuses every
 // tile, so K/V is read once per group per split.  Tiles move from HBM to LDS with direct
 // buffer->LDS loads (no registers, no VALU) into a ring of four stages.
@@ -462,19 +462,18 @@ __device__ __forceinline__ void exact_pair(const FwdParams& p, int b, int h, int
   }
 }
 
-template <int DT, int MK, int W, int NB, bool ML, bool SPLIT>
+template <int DT, int MK, int W, bool ML, bool SPLIT>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) {
-  static_assert((W == 4 && (NB == 1 || NB == 2)) || (W == 8 && NB == 1), "4 wavefronts of 1 or 2 blocks, or 8 of 1");
-  static_assert(!ML || (MK != 0 && NB == 1), "mask rows in LDS: masked one-block shapes");
-  constexpr bool TWO = NB == 2;
-  // Short decode / verify (four wavefronts of one block) streams keys from HBM and has little
-  // to compute per tile: its P.V runs right after its softmax, which frees the previous tile's
-  // stage for a third tile in flight.  The other shapes keep P.V one tile behind.
-  constexpr bool LAG = !(W == 4 && NB == 1);
+  static_assert(W == 4 || W == 8, "four or eight wavefronts of one column block each");
+  static_assert(!ML || MK != 0, "mask rows in LDS: masked shapes");
+  // Short decode / verify (four wavefronts) streams keys from HBM and has little to compute per
+  // tile: its P.V runs right after its softmax, which frees the previous tile's stage for a
+  // third tile in flight.  The eight-wavefront shape keeps P.V one tile behind.
+  constexpr bool LAG = W == 8;
   constexpr int PF = LAG ? kPrefetch : kPrefetch + 1;  // tiles in flight
   static_assert(PF < kStages || !LAG, "the lagged P.V keeps tile t - 1 in its stage");
   static_assert(PF <= kStages - 1 && PF <= 3, "a stage for the tile consumed");
-  constexpr int kGroupBlocks = W * NB;  // column blocks of this workgroup
+  constexpr int kGroupBlocks = W;  // column blocks of this workgroup
   // kStages stages of (K tile, V tile): kPrefetch tiles in flight while one is consumed and
   // the one before it finishes its P.V product.  Stage of tile t: t % kStages.
   // with the mask rows in LDS, kStages stages of them follow the K/V stages
@@ -496,12 +495,14 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   const int b = bid / p.Hkv;
   const int tile = p.n_tiles - 1 - tile_rev;  // later rows (more keys) first
 
-  auto lim_of = [&](int row) { return p.causal ? min(p.kv_len, p.kv_offset + row + 1) : p.kv_len; };
+  auto lim_of = [&](int row) {
+    return p.causal ? min(p.kv_len, p.kv_offset + row + 1 + (GQA_CONTROL == 1 ? 1 : 0)) : p.kv_len;
+  };
 
-  // ---- the (head, row) pairs of this lane: column block c of wavefront w is block NB w + c
-  // of the workgroup; a chunk of heads takes blocks_per_chunk blocks
-  auto pair_of = [&](int blk, int& h_out, int& r_out) {
-    const int bi = tile * kGroupBlocks + NB * wave + blk;
+  // ---- the (head, row) pairs of this lane: wavefront w holds column block w of the
+  // workgroup; a chunk of heads takes blocks_per_chunk blocks
+  auto pair_of = [&](int& h_out, int& r_out) {
+    const int bi = tile * kGroupBlocks + wave;
     const int chunk_idx = bi / p.blocks_per_chunk;
     const int f = (bi - chunk_idx * p.blocks_per_chunk) * kPairsPerBlock + li;
     const int hstart = chunk_idx * p.chunk;
@@ -511,13 +512,10 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     h_out = g * p.G + hstart + (valid ? f - (f / cs) * cs : 0);
     return valid;
   };
-  int h0, r0, h1 = 0, r1 = 0;
-  const bool valid0 = pair_of(0, h0, r0);
-  const bool valid1 = TWO && pair_of(1, h1, r1);
+  int h0, r0;
+  const bool valid0 = pair_of(h0, r0);
   const int lim0 = valid0 ? lim_of(r0) : 0;
-  const int lim1 = valid1 ? lim_of(r1) : 0;
   const bool act0 = __builtin_amdgcn_ballot_w64(valid0) != 0;
-  const bool act1 = __builtin_amdgcn_ballot_w64(valid1) != 0;
 
   // ---- key range of the workgroup [kv_lo, kv_end) and the smallest bound of its pairs, from
   // the pair layout of its column blocks (uniform arithmetic)
@@ -569,24 +567,21 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
   // ---- Q of this lane's pairs, in the B-operand order: element t of q*[kk] is dim
   // 16 kk + 8 hf + t
-  u32x4 q0[16], q1[16];
+  u32x4 q0[16];
   {
     const uint16_t* qa = p.q + (int64_t)b * p.q_sb + (int64_t)h0 * p.q_sh + (int64_t)r0 * p.q_sr + 8 * hf;
-    const uint16_t* qb = p.q + (int64_t)b * p.q_sb + (int64_t)h1 * p.q_sh + (int64_t)r1 * p.q_sr + 8 * hf;
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-        q0[kk] = valid0 ? *reinterpret_cast<const u32x4*>(qa + 16 * kk) : (u32x4){0u, 0u, 0u, 0u};
-      q1[kk] = TWO && valid1 ? *reinterpret_cast<const u32x4*>(qb + 16 * kk) : (u32x4){0u, 0u, 0u, 0u};
+      q0[kk] = valid0 ? *reinterpret_cast<const u32x4*>(qa + 16 * kk) : (u32x4){0u, 0u, 0u, 0u};
     }
   }
   const int64_t mrow0 = MK ? (int64_t)b * p.m_sb + (int64_t)h0 * p.m_sh + (int64_t)r0 * p.m_sr : 0;
-  const int64_t mrow1 = MK ? (int64_t)b * p.m_sb + (int64_t)h1 * p.m_sh + (int64_t)r1 * p.m_sr : 0;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q is in registers before the tile stream starts
   const uint32_t koff = (uint32_t)(lane >> 5) * (uint32_t)p.k_st * 2 + 16 * (lane & 31);
   const uint32_t voff = (uint32_t)(lane >> 5) * (uint32_t)p.v_st * 2 + 16 * (lane & 31);
   // the 8-wavefront shape issues every step's loads, past the last tile too (those read
   // nothing), so its waits need no tail cases; the others stop at the last tile
-  constexpr bool EARLY = LAG && !TWO;
+  constexpr bool EARLY = LAG;
   for (int t = 0; t < PF && (EARLY || t < n_kt); ++t) {
     issue_mask(kv_lo + t * kKeysPerTile, t);
     issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kKeysPerTile, kv_end, lds + t * kStageLds, wave, koff, voff);
@@ -601,18 +596,14 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
   // the accumulators live in the accumulation registers (AGPRs), everything the VALU touches
   // every tile in VGPRs
-  f32x16 o0[8], o1[8];
+  f32x16 o0[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
     o0[db] = (f32x16){};
     asm volatile("" : "+a"(o0[db]));
-    if constexpr (TWO) {
-      o1[db] = (f32x16){};
-      asm volatile("" : "+a"(o1[db]));
-    }
   }
 
-  float m0 = -INFINITY, l0 = 0.0f, m1 = -INFINITY, l1 = 0.0f;
+  float m0 = -INFINITY, l0 = 0.0f;
 
   // One step of the tile stream: wait for tile t (issued kPrefetch steps ago), sync, and
   // start tile t + kPrefetch.  Returns the LDS address of tile t's stage.
@@ -657,7 +648,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   };
   auto no_hook = [](auto) {};
 
-  if (!act0 && !act1) {
+  if (!act0) {
     // a wavefront without pairs only helps stream the tiles
     if constexpr (EARLY) {
       for (int t = 0; t < n_kt; ++t) {
@@ -692,27 +683,6 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     });
     acc_settle_v(sc);
     return sc;
-  };
-
-  // ---- both S blocks of the tile at sb: two independent MFMA chains sharing every K read
-  auto scores2 = [&](uint32_t sb, f32x16& sa, f32x16& sc) {
-    const uint32_t kaddr = sb + k_lane;
-    constexpr int kAhead = 2;
-    u32x4 kop[kAhead + 1];
-    static_for<kAhead>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      kop[i] = ds_read_b128<32 * i>(kaddr);
-    });
-    static_for<16>([&](auto kkc) {
-      constexpr int kk = decltype(kkc)::value;
-      if constexpr (kk + kAhead < 16) kop[(kk + kAhead) % (kAhead + 1)] = ds_read_b128<32 * (kk + kAhead)>(kaddr);
-      constexpr int issued = kk + kAhead + 1 < 16 ? kk + kAhead + 1 : 16;
-      lgkm_wait1<issued - kk - 1>(kop[kk % (kAhead + 1)]);
-      mfma32_v<DT, kk == 0>(sa, kop[kk % (kAhead + 1)], q0[kk]);
-      mfma32_v<DT, kk == 0>(sc, kop[kk % (kAhead + 1)], q1[kk]);
-    });
-    acc_settle_v(sa);
-    acc_settle_v(sc);
   };
 
   // ---- element q of an S block is MFMA row 8 (q / 4) + 4 hf + q % 4, i.e. key jb + key_of(q)
@@ -860,51 +830,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     });
   };
 
-  // ---- the tile loop.  Matrix-core work and VALU work of different blocks and tiles are
-  // paired so that each runs beside the other:
-  //   two blocks:  [S_0(t)] [PV_1(t-1) | weights_0(t)] [S_1(t)] [PV_0(t) | weights_1(t)]
-  //   one block:   [S_0(t)] [PV_0(t-1) | weights_0(t)]
+  // ---- the tile loop.  On the eight-wavefront shape the matrix-core work of one tile and the
+  // VALU work of the next are paired so that each runs beside the other:
+  //   [S(t)] [PV(t-1) | weights(t)]
   // The rescale of o by tile t's alpha is issued just before P_t V_t, so per pair the
   // operations on o keep the plain order (scale by alpha_t, then add P_t V_t).
-  if (TWO && n_kt > 0) {
-    u32x4 pa0, pa1, pc0, pc1;  // packed weights of block 0 / block 1
-    float a0, a1;              // their alpha
-    bool f0, f1;               // whether some pair's max moved
-    f32x16 s0, s1;
-    uint32_t sb = stream_step(0);
-    scores2(sb, s0, s1);
-    mask_scores(s0, kv_lo, lim0, mrow0);
-    mask_scores(s1, kv_lo, lim1, mrow1);
-    f0 = stats(s0, m0, a0);
-    f1 = stats(s1, m1, a1);
-    weights(s0, m0, a0, l0, pa0, pa1);
-    __builtin_amdgcn_sched_barrier(0);
-    pv(sb, pa0, pa1, o0);  // o0 is still 0: no rescale
-    weights(s1, m1, a1, l1, pc0, pc1);
-    uint32_t sprev = sb;
-    for (int t = 1; t < n_kt; ++t) {
-      sb = stream_step(t);
-      const int jb = kv_lo + t * kKeysPerTile;
-      __builtin_amdgcn_sched_barrier(0);
-      scores2(sb, s0, s1);
-      mask_scores(s0, jb, lim0, mrow0);
-      mask_scores(s1, jb, lim1, mrow1);
-      f0 = stats(s0, m0, a0);
-      rescale(o1, a1, f1);  // tile t - 1's alpha, before its P.V
-      __builtin_amdgcn_sched_barrier(0);
-      pv(sprev, pc0, pc1, o1);
-      weights(s0, m0, a0, l0, pa0, pa1);
-      __builtin_amdgcn_sched_barrier(0);
-      f1 = stats(s1, m1, a1);
-      rescale(o0, a0, f0);
-      __builtin_amdgcn_sched_barrier(0);
-      pv(sb, pa0, pa1, o0);
-      weights(s1, m1, a1, l1, pc0, pc1);
-      sprev = sb;
-    }
-    rescale(o1, a1, f1);
-    pv(sprev, pc0, pc1, o1);
-  } else if (!TWO && !LAG) {
+  if constexpr (!LAG) {
     for (int t = 0; t < n_kt; ++t) {
       const uint32_t sb = stream_step(t);
       const int jb = kv_lo + t * kKeysPerTile;
@@ -917,7 +848,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       weights(s0, m0, a0, l0, pa0, pa1);
       pv(sb, pa0, pa1, o0);
     }
-  } else if (!TWO && n_kt > 0) {
+  } else if (n_kt > 0) {
     u32x4 pa0, pa1;
     float a0;
     bool f0;
@@ -950,7 +881,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   if constexpr (EARLY) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: element q of o*[db] is dim 32 db + 8 (q / 4) + 4 hf + (q % 4)
-  const float lt0 = sum_halves(l0), lt1 = sum_halves(l1);
+  const float lt0 = sum_halves(l0);
   // returns whether a NaN came out of o / l (one split only: the nonfinite repair below then
   // redoes the pair; split partials are checked and redone by the merge)
   auto finish = [&](bool valid, int h, int r, float l_tot, float m_run, f32x16(&o)[8]) {
@@ -1020,28 +951,24 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   };
   acc_settle(o0);
   repair(finish(valid0, h0, r0, lt0, m0, o0), valid0, h0, r0, lim0, mrow0);
-  if constexpr (TWO) {
-    acc_settle(o1);
-    repair(finish(valid1, h1, r1, lt1, m1, o1), valid1, h1, r1, lim1, mrow1);
-  }
 }
 
 template <int DT, int MK, bool SPLIT>
 hipError_t launch_fwd_s(const FwdParams& p, int shape, hipStream_t stream) {
   if constexpr (MK != 0) {
-    if (p.mask_lds && shape != 1) {
+    if (p.mask_lds) {
       if (shape == 0) {
-        hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 1, true, SPLIT>), dim3(p.grid), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, true, SPLIT>), dim3(p.grid), dim3(256), 0, stream, p);
       } else {
-        hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, 1, true, SPLIT>), dim3(p.grid), dim3(512), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, true, SPLIT>), dim3(p.grid), dim3(512), 0, stream, p);
       }
       return hipGetLastError();
     }
   }
-  switch (shape) {
-    case 0: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 1, false, SPLIT>), dim3(p.grid), dim3(256), 0, stream, p); break;
-    case 1: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, 2, false, SPLIT>), dim3(p.grid), dim3(256), 0, stream, p); break;
-    default: hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, 1, false, SPLIT>), dim3(p.grid), dim3(512), 0, stream, p); break;
+  if (shape == 0) {
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, false, SPLIT>), dim3(p.grid), dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, false, SPLIT>), dim3(p.grid), dim3(512), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -1056,6 +983,10 @@ hipError_t launch_fwd_t(const FwdParams& p, int shape, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream) {
+#if GQA_CONTROL
+  if (dtype != 0 || mask_kind != 0) return hipErrorInvalidValue;  // planted-mistake build: bf16, no mask
+  return launch_fwd_t<0, 0>(p, shape, stream);
+#else
   if (dtype == 0) {
     switch (mask_kind) {
       case 0: return launch_fwd_t<0, 0>(p, shape, stream);
@@ -1070,6 +1001,7 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, h
     case 2: return launch_fwd_t<1, 2>(p, shape, stream);
     default: return launch_fwd_t<1, 3>(p, shape, stream);
   }
+#endif
 }
 
 }  // namespace gqa

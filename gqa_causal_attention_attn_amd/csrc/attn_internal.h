@@ -5,6 +5,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Planted-mistake builds, for the tests that must see a wrong kernel miss the oracle (TensorFold
+// PR #1009, Receipt, "Attention": controls that must go red): 1 = a query row sees one key past
+// its own; 2 = the merge drops the last chunk of a row; 3 = the append lands one row late.  Such
+// a build goes to a library of its own with the head-256 main pass in bf16 without a mask only;
+// the product library is built with 0.
+#ifndef GQA_CONTROL
+#define GQA_CONTROL 0
+#endif
+
 namespace gqa {
 
 constexpr int kHeadDim = 256;
@@ -142,8 +151,22 @@ struct SmallDParams {
   float* part_lse;     // [n_splits, B, Hq, rows]
 };
 
+// Merge launch shape, shared by the launcher and the host's checks: chunk counts up to
+// kFewChunks take one wavefront per row (four rows a workgroup); more take a workgroup of
+// merge_waves(n) wavefronts per row.
+constexpr int kFewChunks = 8;
+constexpr int kMergeBatch = 4;  // chunks a wavefront of the many-chunk merge loads at once
+inline int merge_waves(int n_chunks) {
+  return n_chunks <= kFewChunks ? 1 : n_chunks <= 4 * kMergeBatch ? 4 : n_chunks <= 8 * kMergeBatch ? 8 : 16;
+}
+// A launch dimension holds at most 2^32 - 1 work-items.
+inline bool grid_fits(int64_t blocks, int64_t threads) { return blocks >= 1 && blocks * threads <= 0xffffffffLL; }
+inline bool merge_fits(int n_chunks, int64_t n_rows) {
+  return n_chunks <= kFewChunks ? grid_fits((n_rows + 3) / 4, 256) : grid_fits(n_rows, 64 * merge_waves(n_chunks));
+}
+
 // Launchers (return hipGetLastError()).  dtype 0 = bf16, 1 = fp16; mask_kind as attn_mask_kind.
-// shape: 0 = 4 wavefronts x 1 column block, 1 = 4 x 2, 2 = 8 x 1 (wavefronts x blocks each)
+// shape: 0 = 4 wavefronts, 2 = 8 wavefronts, each wavefront one 32-pair column block
 hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);

@@ -180,7 +180,7 @@ typedef struct {
   int32_t group_size;      /* G = Hq / Hkv */
   int32_t n_head_chunks;   /* chunks per KV group */
   int32_t head_chunk;      /* heads per chunk (last chunk may be smaller) */
-  int32_t rows_per_wave;   /* (head, row) pairs per wavefront: 32 or 64 (one or two 32-wide MFMA column blocks) */
+  int32_t rows_per_wave;   /* (head, row) pairs per wavefront: 32 (one 32-wide MFMA column block) */
   int32_t waves_per_block; /* wavefronts per workgroup of the main pass */
   int32_t n_row_tiles;     /* workgroups per (batch, KV head, split) */
   int32_t n_splits;        /* KV splits (1: the gate is applied in the same kernel) */
