@@ -2,11 +2,17 @@
 
 Usage: python -m gqa_causal_attention_attn_amd.build  (or call build()).
 Every call compiles from source; nothing is cached.
+
+Besides the library, build() compiles the planted-mistake libraries
+(libgqa_attn_control{1,2,3}.so, the sources with -DGQA_CONTROL=n: a row that sees one key
+past its own, a merge that drops its last chunk, an append one row late).  Only the tests that
+must see them miss the oracle load them.
 """
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -14,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgqa_attn.so")
 SOURCES = ["attn_fwd.hip", "attn_aux.hip", "attn_composed.hip", "attn_small_d.hip", "attn_api.cpp"]
 ARCH = "gfx950"
+CONTROLS = (1, 2, 3)
 
 FLAGS = [
     f"--offload-arch={ARCH}",
@@ -35,24 +42,49 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    objs = []
-    tmp_dir = os.path.join(PKG, "_build")
-    os.makedirs(tmp_dir, exist_ok=True)
-    for src in SOURCES:
-        obj = os.path.join(tmp_dir, src + ".o")
-        cmd = [hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+def control_lib(n: int) -> str:
+    return os.path.join(PKG, f"libgqa_attn_control{n}.so")
+
+
+def _jobs(verbose, extra):
+    """(library path, [(compile command, object)]) for the library and each control build."""
+    out = []
+    for n in (0,) + CONTROLS:
+        tmp_dir = os.path.join(PKG, "_build" if n == 0 else f"_build_control{n}")
+        os.makedirs(tmp_dir, exist_ok=True)
+        defs = [] if n == 0 else [f"-DGQA_CONTROL={n}"]
+        cmds = []
+        for src in SOURCES:
+            obj = os.path.join(tmp_dir, src + ".o")
+            cmds.append(([hipcc(), *FLAGS, *defs, *extra, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+        out.append((LIB if n == 0 else control_lib(n), cmds))
+    return out
+
+
+def build(verbose: bool = False, extra=(), controls: bool = True) -> str:
+    """Compile every source and link the shared libraries; returns the library's path."""
+    jobs = _jobs(verbose, extra)
+    if not controls:
+        jobs = jobs[:1]
+    compiles = [c for _, cmds in jobs for c in cmds]
+    # the head-256 main pass of the library is by far the longest compile: start it first
+    compiles.sort(key=lambda c: (not c[1].endswith("attn_fwd.hip.o"), "_control" in c[1]))
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd[0]), flush=True)
+        subprocess.run(cmd[0], check=True)
+
+    workers = max(1, min(6, (os.cpu_count() or 2) - 1))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(run, compiles))
+    for lib, cmds in jobs:
+        tmp_lib = lib + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o in cmds], "-o", tmp_lib]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        objs.append(obj)
-    tmp_lib = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp_lib, LIB)
+        os.replace(tmp_lib, lib)
     return LIB
 
 

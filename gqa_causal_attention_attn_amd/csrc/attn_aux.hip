@@ -127,8 +127,6 @@ __device__ __forceinline__ bool has_nan4(const f32x4& x) { return __builtin_isna
 // once; only the row's largest lse crosses the wavefronts (through LDS) before the weights are
 // applied, so a row up to MW x kMergeBatch chunks costs one round trip to memory.  The partial
 // sums meet in LDS.
-constexpr int kMergeBatch = 4;
-
 template <int DT, int MW>
 __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
   constexpr int kMergeWaves = MW;
@@ -154,21 +152,22 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
   float wsum = 0.0f;
   float ref = -INFINITY;
   bool nan_l = false;  // a chunk whose lse is NaN makes the row NaN, as the unsplit definition does
-  for (int c0 = 0; c0 < p.n_chunks; c0 += kMergeWaves * kMergeBatch) {
+  const int nch = GQA_CONTROL == 2 ? max(p.n_chunks - 1, 1) : p.n_chunks;
+  for (int c0 = 0; c0 < nch; c0 += kMergeWaves * kMergeBatch) {
     // this pass's chunks of the wavefront, all loads in flight together (indices past the
     // last chunk re-read it and are selected out)
     float lc[kMergeBatch];
     f32x4 oc[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const int cc = min(c0 + wave + j * kMergeWaves, p.n_chunks - 1);
+      const int cc = min(c0 + wave + j * kMergeWaves, nch - 1);
       lc[j] = p.part_lse[(int64_t)cc * n_rows + row_id];
       oc[j] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * p.D + dl);
     }
     float top = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const bool in = c0 + wave + j * kMergeWaves < p.n_chunks;
+      const bool in = c0 + wave + j * kMergeWaves < nch;
       top = in ? fmaxf(top, lc[j]) : top;
       nan_l = nan_l || (in && __builtin_isnan(lc[j]));
     }
@@ -188,7 +187,7 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
 #pragma unroll
       for (int j = 0; j < kMergeBatch; ++j) {
         // an empty chunk is selected out, never multiplied in
-        if (c0 + wave + j * kMergeWaves < p.n_chunks && lc[j] != -INFINITY) {
+        if (c0 + wave + j * kMergeWaves < nch && lc[j] != -INFINITY) {
           const float w = exp2f((lc[j] - ref) * kLog2e);
           acc += w * oc[j];
           wsum += w;
@@ -231,8 +230,6 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
 // Few chunks (prompt blocks split a handful of ways): one wavefront per row, four rows per
 // workgroup, four dims per lane, and every chunk's partial loaded at once (independent
 // 16-byte loads), so the pass streams instead of waiting on one load after another.
-constexpr int kFewChunks = 8;
-
 template <int DT>
 __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   const int lane = threadIdx.x & 63;
@@ -251,11 +248,12 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   // they are all in flight together; chunks past the last one are selected out below
   float lc[kFewChunks];
   f32x4 oc[kFewChunks];
+  const int nch = GQA_CONTROL == 2 ? max(p.n_chunks - 1, 1) : p.n_chunks;
   const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
   const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + dl);
 #pragma unroll
   for (int c = 0; c < kFewChunks; ++c) {
-    const int cc = min(c, p.n_chunks - 1);
+    const int cc = min(c, nch - 1);
     lc[c] = p.part_lse[(int64_t)cc * n_rows + row_id];
     oc[c] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * p.D + dl);
   }
@@ -263,8 +261,8 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   bool nan_l = false;  // a chunk whose lse is NaN makes the row NaN, as the unsplit definition does
 #pragma unroll
   for (int c = 0; c < kFewChunks; ++c) {
-    top = c < p.n_chunks ? fmaxf(top, lc[c]) : top;
-    nan_l = nan_l || (c < p.n_chunks && __builtin_isnan(lc[c]));
+    top = c < nch ? fmaxf(top, lc[c]) : top;
+    nan_l = nan_l || (c < nch && __builtin_isnan(lc[c]));
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
@@ -272,7 +270,7 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
 #pragma unroll
     for (int c = 0; c < kFewChunks; ++c) {
       // an empty chunk is selected out, never multiplied in
-      if (c < p.n_chunks && lc[c] != -INFINITY) {
+      if (c < nch && lc[c] != -INFINITY) {
         const float w = exp2f((lc[c] - top) * kLog2e);
         acc += w * oc[c];
         wsum += w;
@@ -310,7 +308,8 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
     const int64_t yb = y - (t ? bg : 0);
     const int b = (int)(yb / p.Hkv), g = (int)(yb - (int64_t)b * p.Hkv);
     const uint16_t* src = p.src[t] + b * p.s_sb[t] + g * p.s_sh[t];
-    uint16_t* dst = p.dst[t] + b * p.d_sb[t] + g * p.d_sh[t] + (int64_t)p.kv_offset * p.d_st[t];
+    uint16_t* dst = p.dst[t] + b * p.d_sb[t] + g * p.d_sh[t] +
+                    (int64_t)(p.kv_offset + (GQA_CONTROL == 3 ? 1 : 0)) * p.d_st[t];
     const int64_t s_sr = p.s_sr[t], d_st = p.d_st[t];
     for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < n; u += (int64_t)gridDim.x * 256) {
       const int64_t r = u >> p.chunk_shift;
@@ -369,7 +368,7 @@ hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
     else hipLaunchKernelGGL(merge_few_kernel<1>, grid, dim3(256), 0, stream, p);
   } else {
     const dim3 grid((unsigned)n_rows);
-    const int mw = p.n_chunks <= 4 * kMergeBatch ? 4 : p.n_chunks <= 8 * kMergeBatch ? 8 : 16;
+    const int mw = merge_waves(p.n_chunks);
     if (mw == 4) {
       if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 4>), grid, dim3(4 * 64), 0, stream, p);
       else hipLaunchKernelGGL((merge_kernel<1, 4>), grid, dim3(4 * 64), 0, stream, p);
