@@ -319,3 +319,28 @@ def test_prefill_partials_needs_its_outputs():
     assert need > 0
     st = lib.attn_prefill_partials(C.byref(a), None, 0, None, C.byref(n), C.byref(off))
     assert st == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
+
+
+def test_launch_size_limits_are_rejected_by_planning_and_run_alike():
+    # a decode whose merge would exceed a launch (4.19M rows x 16 wavefronts), and a head-dim-64
+    # plan whose grid z (batch x splits) passes 65535: the planning calls reject them as the run
+    # would, before anything is enqueued
+    a = ga.plan_args(B=4096, Hq=32, Hkv=1, rows=32, kv_offset=4096, n_splits=40)
+    for fn in (lambda: ga.workspace_bytes(a, _abi.OP_DECODE), lambda: ga.describe_plan(a, _abi.OP_DECODE)):
+        with pytest.raises(ga.AttnError) as e:
+            fn()
+        assert e.value.name == "ATTN_E_ARG"
+    assert ga.lib().attn_decode(C.byref(a), None, 0, None) == _abi.STATUS_CODE["ATTN_E_ARG"]
+    a.n_splits = 8  # one wavefront a row: fits
+    assert ga.workspace_bytes(a, _abi.OP_DECODE) > 0
+    s = ga.plan_args(B=40000, Hq=2, Hkv=2, rows=1, kv_offset=4096, n_splits=2, D=64)
+    with pytest.raises(ga.AttnError):
+        ga.workspace_bytes(s, _abi.OP_PREFILL)
+    assert ga.lib().attn_prefill(C.byref(s), None, 0, None) == _abi.STATUS_CODE["ATTN_E_ARG"]
+    s.n_splits = 1
+    assert ga.workspace_bytes(s, _abi.OP_PREFILL) == 0
+
+
+def test_strerror_names_the_head_dims():
+    msg = ga.lib().attn_strerror(_abi.STATUS_CODE["ATTN_E_HEAD_DIM"]).decode()
+    assert "256" in msg and "128" in msg and "64" in msg
