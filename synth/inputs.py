@@ -170,7 +170,8 @@ def plant_near_ties(q_bits, k_bits, *, n_kv_heads: int, rng: np.random.Generator
 
 
 def verify_mask(rng: np.random.Generator, *, rows: int, kv_offset: int, heads: int = 1,
-                drop: float = 0.1, kind: str = "add", dtype: str = "bf16") -> np.ndarray:
+                drop: float = 0.1, kind: str = "add", dtype: str = "bf16", values: str = "zero",
+                batch: int = 1) -> np.ndarray:
     """Verify-block mask [1, heads, rows, kv_offset + rows] for speculative-decoding verify rows.
 
     Prefix keys (positions < kv_offset) are hidden independently with
@@ -181,22 +182,32 @@ def verify_mask(rng: np.random.Generator, *, rows: int, kv_offset: int, heads: i
 
     kind "add": 16-bit bits of 0 (attend) / -Inf (hidden) in ``dtype``;
     kind "add_f32": float32 0 / -Inf; kind "bool": uint8 1 (attend) / 0.
+    values "normal" (additive kinds): an admitted key holds a finite N(0, 1) value
+    instead of 0 (drawn after the pattern, in float32, then rounded to ``dtype`` for
+    kind "add"), the holes stay -Inf.  ``batch`` > 1 gives a [batch, heads, ...] mask with
+    a pattern of its own per batch entry.
     """
+    if values not in ("zero", "normal"):
+        raise ValueError(f"values must be 'zero' or 'normal', got {values!r}")
     kv_len = kv_offset + rows
-    keep = rng.random((1, heads, rows, kv_len)) >= drop
-    for h in range(heads):
-        parent = [-1] + [int(rng.integers(0, r)) for r in range(1, rows)]
-        for r in range(rows):
-            anc = set()
-            a = r
-            while a >= 0:
-                anc.add(a)
-                a = parent[a]
-            for rp in range(rows):
-                keep[0, h, r, kv_offset + rp] = rp in anc
+    keep = rng.random((batch, heads, rows, kv_len)) >= drop
+    for bb in range(batch):
+        for h in range(heads):
+            parent = [-1] + [int(rng.integers(0, r)) for r in range(1, rows)]
+            for r in range(rows):
+                anc = set()
+                a = r
+                while a >= 0:
+                    anc.add(a)
+                    a = parent[a]
+                for rp in range(rows):
+                    keep[bb, h, r, kv_offset + rp] = rp in anc
     if kind == "bool":
         return keep.astype(np.uint8)
-    vals = np.where(keep, np.float32(0.0), np.float32(-np.inf)).astype(np.float32)
+    fill = np.float32(0.0)
+    if values == "normal":
+        fill = rng.standard_normal(keep.shape, dtype=np.float32)
+    vals = np.where(keep, fill, np.float32(-np.inf)).astype(np.float32)
     if kind == "add_f32":
         return vals
     if kind == "add":

@@ -33,3 +33,21 @@ def prompt(seed, *, B, Hq, Hkv, N, dtype="bf16", near_ties=False):
     if near_ties:
         q, rec = syn.plant_near_ties(q, k, n_kv_heads=Hkv, rng=rng["plant"], dtype=dtype)
     return q, k, v, g, rec
+
+
+def strided_mask(m, row_stride):
+    """m ([Bm, Hm, rows, kv] on the GPU) copied into storage with the given row stride (elements)."""
+    Bm, Hm, rows, kv = m.shape
+    store = torch.zeros((Bm, Hm, rows, row_stride), dtype=m.dtype, device=m.device)
+    store[..., :kv] = m
+    return store[..., :kv]
+
+
+def lds_and_lane_strides(kv, esz):
+    """Row strides (elements) for a mask of kv keys: one 64-byte aligned (the planner may stage
+    its rows in LDS) and one that is not a multiple of 16 bytes (per-lane loads)."""
+    aligned = (kv * esz + 63) // 64 * 64 // esz
+    odd = kv
+    while (odd * esz) % 16 == 0:
+        odd += 1
+    return aligned, odd

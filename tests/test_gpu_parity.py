@@ -12,7 +12,7 @@ import torch
 import gqa_causal_attention_attn_amd as ga
 from oracle import reference
 from synth import inputs as syn
-from tests.gpu_util import prompt, to_bits, to_dev, to_f64
+from tests.gpu_util import lds_and_lane_strides, prompt, strided_mask, to_bits, to_dev, to_f64
 from tests.parity import assert_close, compare
 
 pytestmark = pytest.mark.gpu
@@ -156,13 +156,15 @@ def test_decode_short_and_split_caches(kv_len, n_splits):
 @needs_gpu
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("offset", [4097, 32768])
-@pytest.mark.parametrize("rows", [1, 4, 5, 9, 17, 32])
+# rows 6, 8 and 12 give the policy plans [5, 3], [4, 4] and [2, 2, 2, 2] for groups of 8
+@pytest.mark.parametrize("rows", [1, 4, 5, 6, 8, 9, 12, 17, 32])
 def test_head_chunked_verify(dtype, offset, rows):
     # batch 2, 16 query heads over 2 KV heads, rows appended at the offset, broadcast additive mask
     _say("verify", dtype, offset, rows)
     B, Hq, Hkv = 2, 16, 2
     qb, kb, vb, gb, rng = _decode_case(1004 + rows, B=B, Hq=Hq, Hkv=Hkv, offset=offset, rows=rows, dtype=dtype)
-    mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=1, kind="add", dtype=dtype)
+    mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=1, kind="add", dtype=dtype,
+                         values="normal")
     q, k, v, g, m = (to_dev(x, dtype) for x in (qb, kb, vb, gb, mb))
     outs = {}
     for hc in [0] + list(range(1, 9)):
@@ -175,37 +177,35 @@ def test_head_chunked_verify(dtype, offset, rows):
 
 
 @needs_gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("kind", ["full_head_add", "bool", "f32"])
-def test_verify_mask_kinds(kind):
+def test_verify_mask_kinds(kind, dtype):
+    # full-head masks (one pattern per query head, N(0, 1) values at admitted keys), a bool
+    # mask and an fp32 additive mask; every head-chunk variant agrees bit for bit
     B, Hq, Hkv, offset, rows = 2, 16, 2, 4097, 6
-    _say("mask kind", kind)
-    qb, kb, vb, gb, rng = _decode_case(77, B=B, Hq=Hq, Hkv=Hkv, offset=offset, rows=rows)
+    _say("mask kind", kind, dtype)
+    qb, kb, vb, gb, rng = _decode_case(77, B=B, Hq=Hq, Hkv=Hkv, offset=offset, rows=rows, dtype=dtype)
     if kind == "full_head_add":
-        mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=Hq, kind="add")
-        m = to_dev(mb)
-        mref, mk = syn.widen(mb), "add"
+        mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=Hq, kind="add", dtype=dtype,
+                             values="normal")
+        m = to_dev(mb, dtype)
+        mref, mk = syn.widen(mb, dtype), "add"
     elif kind == "bool":
         mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=1, kind="bool")
         m = torch.from_numpy(mb).cuda()
         mref, mk = mb.astype(bool), "bool"
     else:
-        mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=Hq, kind="add_f32")
-        mb = np.where(np.isfinite(mb), np.random.default_rng(5).standard_normal(mb.shape).astype(np.float32), mb)
+        mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=Hq, kind="add_f32", values="normal")
         m = torch.from_numpy(mb).cuda()
         mref, mk = mb.astype(np.float64), "add"
-    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    q, k, v, g = (to_dev(x, dtype) for x in (qb, kb, vb, gb))
     out = ga.decode(q, k, v, g, kv_offset=offset, mask=m)
-    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=offset,
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=offset,
                               kv_len=offset + rows, mask=mref, mask_kind=mk)
-    _say(assert_close(to_f64(out), ref, kind))
-
-
-def _strided_mask(m, row_stride):
-    """m ([Bm, Hm, rows, kv] on the GPU) copied into storage with the given row stride."""
-    Bm, Hm, rows, kv = m.shape
-    store = torch.zeros((Bm, Hm, rows, row_stride), dtype=m.dtype, device="cuda")
-    store[..., :kv] = m
-    return store[..., :kv]
+    _say(assert_close(syn.widen(to_bits(out), dtype), ref, kind))
+    for hc in (1, 3, 8):
+        again = ga.decode(q, k, v, g, kv_offset=offset, mask=m, head_chunk=hc)
+        assert torch.equal(again.view(torch.int16), out.view(torch.int16)), f"head_chunk {hc}"
 
 
 @needs_gpu
@@ -233,12 +233,9 @@ def test_mask_rows_in_lds(kind, rows, Bm):
     else:
         mdev = torch.from_numpy(mb).cuda()
         mref, mk = (mb.astype(bool), "bool") if kind == "bool" else (mb.astype(np.float64), "add")
-    esz = mdev.element_size()
-    odd = kv
-    while (odd * esz) % 16 == 0:
-        odd += 1
-    aligned = _strided_mask(mdev, (kv * esz + 63) // 64 * 64 // esz)
-    unaligned = _strided_mask(mdev, odd)
+    lds_stride, lane_stride = lds_and_lane_strides(kv, mdev.element_size())
+    aligned = strided_mask(mdev, lds_stride)
+    unaligned = strided_mask(mdev, lane_stride)
     q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
     names = []
     for m in (aligned, unaligned):

@@ -71,6 +71,23 @@ def test_verify_mask_structure():
     assert np.array_equal(np.isfinite(syn.bits_to_f32(add)), m.astype(bool))
 
 
+def test_verify_mask_normal_values():
+    # finite N(0, 1) values at the admitted keys, -Inf exactly where the 0/-Inf mask of the same
+    # seed has its holes; batch entries get patterns of their own
+    for dtype in ("bf16", "f16"):
+        zero = syn.verify_mask(syn.streams(5)["mask"], rows=9, kv_offset=300, heads=2, kind="add", dtype=dtype)
+        vals = syn.verify_mask(syn.streams(5)["mask"], rows=9, kv_offset=300, heads=2, kind="add", dtype=dtype,
+                               values="normal")
+        z, v = syn.widen(zero, dtype), syn.widen(vals, dtype)
+        assert np.array_equal(np.isfinite(z), np.isfinite(v))
+        fin = v[np.isfinite(v)]
+        assert np.count_nonzero(fin) > 0.99 * fin.size
+        assert 0.8 < fin.std() < 1.2 and abs(fin.mean()) < 0.1
+    f32 = syn.verify_mask(syn.streams(6)["mask"], rows=5, kv_offset=40, kind="add_f32", values="normal", batch=2)
+    assert f32.shape == (2, 1, 5, 45) and f32.dtype == np.float32
+    assert not np.array_equal(np.isfinite(f32[0]), np.isfinite(f32[1]))
+
+
 def test_near_ties_every_row_including_tile_boundaries():
     # frac 1: every row 1..N-1, so rows sitting on a 64-key tile start (64, 128) are planted too
     N = 140
