@@ -17,7 +17,8 @@ import torch
 from . import _abi
 
 __all__ = [
-    "AttnError", "lib", "prefill", "prefill_partials", "prefill_composed", "decode", "kv_append", "kv_keep", "merge", "head_chunk_plan",
+    "AttnError", "lib", "prefill", "prefill_partials", "prefill_composed", "decode", "decode_noalloc", "kv_append",
+    "kv_keep", "merge", "head_chunk_plan",
     "workspace_bytes",
     "describe_plan", "plan_args", "variant_name", "prompt_prefill",
 ]
@@ -173,6 +174,18 @@ def decode(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=Tru
     """attn_decode: 1..32 rows; head_chunk 0 = the policy, k = chunks of k heads."""
     return _run(_abi.OP_DECODE, q, k_cache, v_cache, gate, kv_offset=kv_offset, kv_len=kv_len, causal=causal,
                 scale=scale, head_chunk=head_chunk, n_splits=n_splits, mask=mask, out=out, workspace=workspace)
+
+
+def decode_noalloc(q, k_cache, v_cache, gate, *, out, kv_offset: int, kv_len=None, causal=True, scale=0.0,
+                   head_chunk=0, n_splits=0, mask=None):
+    """attn_decode_noalloc: attn_decode with the split partials in the library's own device
+    scratch (64 MiB per GPU); the call allocates nothing, so `out` is the caller's."""
+    if kv_len is None:
+        kv_len = kv_offset + q.shape[2]
+    a = _args(q, k_cache, v_cache, gate, out, kv_offset=kv_offset, kv_len=kv_len, causal=causal, scale=scale,
+              head_chunk=head_chunk, n_splits=n_splits, mask=mask)
+    _check(lib().attn_decode_noalloc(C.byref(a), _stream_handle(q)))
+    return out
 
 
 def prefill_composed(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, out=None,

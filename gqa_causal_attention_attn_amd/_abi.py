@@ -7,7 +7,7 @@ The struct sizes are checked against the library's own (attn_struct_size) when i
 import ctypes as C
 import os
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 HEAD_DIM = 256
 MAX_DECODE_ROWS = 32
 MAX_CHUNKS = 64
@@ -27,8 +27,9 @@ OP_PREFILL, OP_DECODE, OP_COMPOSED = 0, 1, 2
 EXPORTS = (
     "attn_abi_version", "attn_struct_size", "attn_strerror", "attn_variant_name", "attn_head_chunk_plan",
     "attn_workspace_bytes", "attn_describe_plan", "attn_prefill", "attn_decode", "kv_append", "attn_merge",
-    "kv_keep", "attn_prefill_partials", "attn_prefill_composed",
+    "kv_keep", "attn_prefill_partials", "attn_prefill_composed", "attn_decode_noalloc",
 )
+SCRATCH_BYTES = 64 << 20  # the device scratch of attn_decode_noalloc, per GPU
 KEEP_MAX_BATCH = 64
 
 
@@ -110,6 +111,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.attn_prefill_partials.restype = C.c_int
     lib.attn_prefill_partials.argtypes = [P(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p, P(C.c_int32),
                                           P(C.c_size_t)]
+    lib.attn_decode_noalloc.restype = C.c_int
+    lib.attn_decode_noalloc.argtypes = [P(AttnArgs), C.c_void_p]
     lib.kv_keep.restype = C.c_int
     lib.kv_keep.argtypes = [P(KvKeepArgs), C.c_void_p]
     if lib.attn_abi_version() != ABI_VERSION:

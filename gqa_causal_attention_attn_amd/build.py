@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgqa_attn.so")
-SOURCES = ["attn_fwd.hip", "attn_aux.hip", "attn_composed.hip", "attn_small_d.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_aux.hip", "attn_composed.hip", "attn_small_d.hip", "attn_noalloc.hip", "attn_api.cpp"]
 ARCH = "gfx950"
 CONTROLS = (1, 2, 3)
 

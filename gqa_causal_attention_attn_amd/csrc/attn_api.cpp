@@ -530,6 +530,18 @@ int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stre
   return run_fwd(a, ATTN_OP_DECODE, workspace, ws_bytes, stream);
 }
 
+int attn_decode_noalloc(const attn_args* a, void* stream) {
+  int st = validate(a, ATTN_OP_DECODE);
+  if (st) return st;
+  size_t need = 0;
+  st = attn_workspace_bytes(a, ATTN_OP_DECODE, &need);
+  if (st) return st;
+  if (need > gqa::kScratchBytes) return ATTN_E_WORKSPACE;  // the partials do not fit the scratch
+  void* ws = nullptr;
+  if (need > 0 && gqa::scratch_of_current_device(&ws) != hipSuccess) return ATTN_E_HIP;
+  return run_fwd(a, ATTN_OP_DECODE, ws, need > 0 ? gqa::kScratchBytes : 0, stream);
+}
+
 int attn_prefill_composed(const attn_args* a, void* workspace, size_t ws_bytes, void* stream) {
   int st = validate(a, ATTN_OP_COMPOSED);
   if (st) return st;

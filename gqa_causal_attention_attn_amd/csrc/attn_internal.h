@@ -29,6 +29,7 @@ constexpr int kPrefetch = 2;                                 // tiles in flight 
 constexpr int kFwdLdsBytes = kStages * kStageLds;            // 133,120 B
 constexpr int kTargetBlocks = 256;   // main-pass workgroups aimed for (one per CU)
 constexpr int kMaskStageLds = 4096;  // LDS bytes per stage for the mask rows of a tile (masked kernels)
+constexpr size_t kScratchBytes = (size_t)64 << 20;  // the device scratch of attn_decode_noalloc, per GPU
 
 // Parameters of the main (flash / split-KV) pass.  Strides are in elements.
 struct FwdParams {
@@ -173,5 +174,8 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_keep(const KeepParams& p, int B, hipStream_t stream);
 hipError_t launch_composed(const ComposedParams& p, int dtype, hipStream_t stream);
 hipError_t launch_small_d(const SmallDParams& p, int dtype, hipStream_t stream);
+// Device address of the library's scratch array on the current device (looked up on the first
+// call per device and kept; attn_noalloc.hip).
+hipError_t scratch_of_current_device(void** ptr);
 
 }  // namespace gqa

@@ -31,6 +31,7 @@
  *     The library never aborts.
  *   - The library holds no mutable global state and is reentrant; calls on
  *     different streams may overlap if their output/workspace buffers differ.
+ *     The one exception is attn_decode_noalloc's device scratch (see there).
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GQA_ATTN_ABI_VERSION 3
+#define GQA_ATTN_ABI_VERSION 4
 #define ATTN_HEAD_DIM 256
 #define ATTN_MAX_DECODE_ROWS 32
 #define ATTN_MAX_CHUNKS 64
@@ -257,6 +258,27 @@ int attn_prefill_partials(const attn_args* a, void* workspace, size_t ws_bytes, 
  * head chunk (a->head_chunk), then the merge pass.  TensorFold PR #1009 (attention
  * kernel-contract commit) splits decode rows over key chunks and merges them. */
 int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/* attn_decode for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same plan, kernels and result as
+ * attn_decode (bit for bit), with the split partials in the library's own device scratch
+ * instead of a caller workspace.  The caller still passes its inputs and outputs; the call
+ * allocates nothing.
+ *   - The scratch is a 64 MiB device array (GQA_ATTN_SCRATCH_BYTES) that every GPU the library
+ *     runs on holds until the process ends.  Its address on a device is looked up on the first
+ *     call made with that device current (make that first call outside graph capture); the
+ *     stream must belong to the current device.
+ *   - A plan whose partials (attn_workspace_bytes(a, ATTN_OP_DECODE)) exceed the scratch is
+ *     rejected with ATTN_E_WORKSPACE before anything is enqueued (set n_splits lower to fit).
+ *     At head_dim 256 the partials of n_splits chunks take n_splits B Hq rows 1028 bytes: 32
+ *     rows of 16 heads at batch 2 fit up to 63 chunks.
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
+ *     different streams) race and must be ordered by the caller.  Nothing in the scratch needs
+ *     to start at zero: the main pass writes every partial the merge reads.
+ * Errors: those of attn_decode, ATTN_E_WORKSPACE as above, ATTN_E_HIP if the scratch's address
+ * cannot be found on the current device. */
+#define GQA_ATTN_SCRATCH_BYTES (64u << 20)
+int attn_decode_noalloc(const attn_args* a, void* stream);
 
 /* The composed (materialised-score) route for the same block, for comparison with the fused
  * kernel ("perf(qwen36): qualify M4 head-256 attention", Summary: composed against fused

@@ -121,6 +121,11 @@ hipError_t launch_composed(const ComposedParams& p, int, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t scratch_of_current_device(void** ptr) {
+  *ptr = kWs;
+  return hipSuccess;
+}
+
 hipError_t launch_small_d(const SmallDParams& p, int, hipStream_t) {
   ++g_launch_other;
   g_small = p;
