@@ -25,8 +25,9 @@ struct Plan {
   int n_chunks;
   int chunk_sizes[ATTN_MAX_CHUNKS];
   int blocks_per_chunk;
-  int shape;     // 0: 4 wavefronts of one column block each, 2: 8 wavefronts (1 is not used)
-  int mask_lds;  // the main pass stages each tile's mask rows in LDS
+  int shape;     // 0: 4 wavefronts of one column block each; 2: 8 wavefronts, P.V one tile behind
+                 // (prompts); 3: 8 wavefronts without the lag (decode / verify); 1 is not used
+  int mask_lds;  // the main pass stages each tile's mask window in LDS: 0 no, 1 rows, 2 words
   int waves;     // wavefronts per workgroup
   int n_tiles;
   int n_splits;
@@ -139,10 +140,12 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   P->chunk = P->chunk_sizes[0];
   P->blocks_per_chunk = (int)cdiv((int64_t)P->chunk * a->rows, kPairsPerBlock);
   // four wavefronts of one 32-pair column block when they cover the whole KV group (short
-  // decode / verify), else eight wavefronts of one block (two per SIMD)
+  // decode / verify), else eight wavefronts of one block (two per SIMD): with the P.V product one
+  // tile behind for prompts, without it (one more tile in flight) for decode / verify rows, whose
+  // keys stream from HBM
   const int64_t n_blocks = (int64_t)P->n_chunks * P->blocks_per_chunk;
-  P->shape = n_blocks <= 4 ? 0 : 2;
-  P->waves = P->shape == 2 ? 8 : 4;
+  P->shape = n_blocks <= 4 ? 0 : op == ATTN_OP_DECODE ? 3 : 2;
+  P->waves = P->shape == 0 ? 4 : 8;
   P->n_tiles = (int)cdiv(n_blocks, (int64_t)P->waves);
 
   // KV splits depend only on the unchunked shape, so every head-chunk choice splits the keys
@@ -169,20 +172,20 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   S = cdiv(n_kt, tps);
   P->n_splits = (int)S;
   P->keys_per_split = (int)(tps * kKeysPerTile);
-  // Mask rows in LDS: the mask is the same for every head, 16-byte aligned with rows of a whole
-  // number of 16-byte chunks up to kv_len (the direct loads move 16-byte chunks and a chunk that
-  // reaches past the mask's last word would read as zeros), spans < 2 GiB, and every
-  // workgroup's (head, row) pairs cover at most kMaskStageLds / (32 x word size) rows.
+  // Mask window in LDS.  The mask is the same for every head (Hm = 1), spans < 2 GiB, and every
+  // workgroup's (head, row) pairs cover few enough mask rows: at most 32 for one dword per key
+  // (any row stride and kv_len; the word offsets of the window's 32 rows stay below 2^32), else,
+  // on the prompt shape only, 16-byte row chunks of at most 4 KiB of rows, when rows are
+  // 16-byte aligned and end on a whole chunk at kv_len (a chunk that reached past the mask's last
+  // word would read as zeros).
   if (a->mask.kind != ATTN_MASK_NONE) {
     const attn_mask& m = a->mask;
     const int64_t esz = m.kind == ATTN_MASK_BOOL_U8 ? 1 : m.kind == ATTN_MASK_ADD ? 2 : 4;
     const int64_t msb = m.Bm == 1 ? 0 : m.stride_b;
     const int64_t span = ((int64_t)(m.Bm - 1) * msb + (int64_t)(a->rows - 1) * m.stride_row + a->kv_len) * esz;
-    bool ok = m.Hm == 1 && ((uintptr_t)m.ptr % 16) == 0 && (m.stride_row * esz) % 16 == 0 && (msb * esz) % 16 == 0 &&
-              ((int64_t)a->kv_len * esz) % 16 == 0 && span < ((int64_t)1 << 31);
-    const int64_t max_rows = gqa::kMaskStageLds / (gqa::kKeysPerTile * esz);
+    int64_t window = 0;  // most mask rows any workgroup's pairs cover
     const int wg_blocks = P->waves;
-    for (int t = 0; ok && t < P->n_tiles; ++t) {
+    for (int t = 0; t < P->n_tiles; ++t) {
       int64_t lo = INT64_MAX, hi = -1;
       for (int bj = t * wg_blocks; bj < (t + 1) * wg_blocks; ++bj) {
         const int cj = bj / P->blocks_per_chunk;
@@ -196,9 +199,15 @@ int make_plan(const attn_args* a, int op, Plan* P) {
         lo = f0 / csj < lo ? f0 / csj : lo;
         hi = last / csj > hi ? last / csj : hi;
       }
-      if (hi >= 0 && hi - lo >= max_rows) ok = false;
+      if (hi >= 0 && hi - lo + 1 > window) window = hi - lo + 1;
     }
-    P->mask_lds = ok ? 1 : 0;
+    const bool base = m.Hm == 1 && span < ((int64_t)1 << 31);
+    const bool words = base && window <= 32 &&
+                       ((int64_t)(a->rows + 32) * m.stride_row + a->kv_len + kKeysPerTile) * esz < ((int64_t)1 << 32);
+    const bool rows16 = base && P->shape == 2 && ((uintptr_t)m.ptr % 16) == 0 && (m.stride_row * esz) % 16 == 0 &&
+                        (msb * esz) % 16 == 0 && ((int64_t)a->kv_len * esz) % 16 == 0 &&
+                        window <= 4096 / (kKeysPerTile * esz);
+    P->mask_lds = words ? 2 : rows16 ? 1 : 0;
   }
   P->grid = (int64_t)a->B * a->Hkv * S * P->n_tiles;
   if (P->grid > INT32_MAX || !gqa::grid_fits(P->grid, 64 * P->waves)) return ATTN_E_ARG;
@@ -213,8 +222,9 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   return ATTN_OK;
 }
 
+// id = mask layout * 32 + shape * 8 + dtype * 4 + mask kind; head dims 64 / 128: 96 / 97
 inline int variant_of(const attn_args* a, const Plan& P) {
-  return (P.mask_lds << 5) | (P.shape << 3) | (a->dtype << 2) | a->mask.kind;
+  return P.mask_lds * 32 + P.shape * 8 + a->dtype * 4 + a->mask.kind;
 }
 
 // Plan of the fused pass for head dims 64 and 128.  A workgroup holds hw wavefronts, each 32
@@ -419,19 +429,25 @@ const char* attn_strerror(int status) {
 }
 
 const char* attn_variant_name(int variant) {
-  // id = mask rows in LDS * 32 + shape * 8 + dtype * 4 + mask kind
+  // id = mask layout in LDS * 32 + shape * 8 + dtype * 4 + mask kind (see variant_of)
 #define GQA_NAMES(SHAPE)                                                                                        \
   "fwd_mfma32x32x16_bf16_" SHAPE, "fwd_mfma32x32x16_bf16_maskbool_" SHAPE, "fwd_mfma32x32x16_bf16_maskadd_" SHAPE, \
       "fwd_mfma32x32x16_bf16_maskf32_" SHAPE, "fwd_mfma32x32x16_f16_" SHAPE, "fwd_mfma32x32x16_f16_maskbool_" SHAPE, \
       "fwd_mfma32x32x16_f16_maskadd_" SHAPE, "fwd_mfma32x32x16_f16_maskf32_" SHAPE
-  static const char* const names[64] = {
-      GQA_NAMES("4x1"),           GQA_NAMES("unused"),        GQA_NAMES("8x1"),           GQA_NAMES("unused"),
-      GQA_NAMES("4x1_ldsmask"),   GQA_NAMES("unused"),        GQA_NAMES("8x1_ldsmask"),   GQA_NAMES("unused")};
+  static const char* const names[96] = {
+      GQA_NAMES("4x1"),         GQA_NAMES("unused"), GQA_NAMES("8x1"),         GQA_NAMES("8x1_stream"),
+      GQA_NAMES("unused"),      GQA_NAMES("unused"), GQA_NAMES("8x1_ldsrows"), GQA_NAMES("unused"),
+      GQA_NAMES("4x1_ldswords"), GQA_NAMES("unused"), GQA_NAMES("8x1_ldswords"), GQA_NAMES("8x1_stream_ldswords")};
 #undef GQA_NAMES
-  static const bool used[8] = {true, false, true, false, true, false, true, false};  // shape groups
-  if (variant == 64) return "fwd_small_d64";
-  if (variant == 65) return "fwd_small_d128";
-  return (variant >= 0 && variant < 64 && used[variant >> 3]) ? names[variant] : "unknown";
+  // shape groups that exist (mask layout * 4 + shape)
+  static const bool used[12] = {true, false, true, true, false, false, true, false, true, false, true, true};
+  if (variant == 96) return "fwd_small_d64";
+  if (variant == 97) return "fwd_small_d128";
+  if (variant < 0 || variant >= 96) return "unknown";
+  const int group = variant >> 3;
+  const bool masked = (variant & 3) != 0;
+  // unmasked variants have no mask layout; masked ones exist in every layout of their shape
+  return used[group] && (masked || group < 4) ? names[variant] : "unknown";
 }
 
 int attn_head_chunk_plan(int rows, int n_q_heads, int n_kv_heads, int enabled, int* sizes, int cap, int* n_chunks) {
@@ -478,7 +494,7 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
     if (st) return st;
     memset(info, 0, sizeof(*info));
     info->op = op;
-    info->variant = a->D == 64 ? 64 : 65;
+    info->variant = a->D == 64 ? 96 : 97;
     info->group_size = a->Hq / a->Hkv;
     info->n_head_chunks = 1;
     info->head_chunk = info->group_size;

@@ -1,9 +1,10 @@
 // Main pass of gated causal GQA attention at head_dim 256 for gfx950 (CDNA4).
 //
 // One workgroup = one (batch b, KV head g, KV split s, tile of (head, row) pairs of that
-// group), one workgroup per CU.  Two shapes: eight wavefronts of one 32-pair column block each
-// (prompts and long verify blocks: two wavefronts per SIMD) and four wavefronts of one block
-// (short decode / verify, whose KV group fits in four blocks).  The
+// group), one workgroup per CU.  Shapes: eight wavefronts of one 32-pair column block each (two
+// wavefronts per SIMD), with the P.V product one tile behind (prompts) or without that lag and
+// one more tile in flight (verify blocks, which stream their keys from HBM), and four
+// wavefronts of one block (short decode / verify, whose KV group fits in four blocks).  The
 // group's K and V are streamed through LDS in 32-key tiles and every wavefront reuses every
 // tile, so K/V is read once per group per split.  Tiles move from HBM to LDS with direct
 // buffer->LDS loads (no registers, no VALU) into a ring of four stages.
@@ -32,18 +33,22 @@
 // transposing V reads (4 rows x 2 cells per 16 lanes) hit distinct banks.  Every LDS address
 // is a per-lane base plus a compile-time offset.
 //
-// Schedule.  On the prompt shapes the P.V product of tile t - 1 runs on the matrix cores while
+// Schedule.  On the prompt shape the P.V product of tile t - 1 runs on the matrix cores while
 // the VALU turns tile t's scores into weights (the previous tile stays in its stage: two tiles
-// in flight); on the eight-wavefront shape each wavefront's direct loads of tile t + 2 are
-// issued one by one between the MFMAs of S(t), after the barrier that freed their stage.  On
-// the short-decode shape, which streams keys from HBM and has little to compute, P.V follows
-// its softmax directly and three tiles are in flight.
+// in flight), and each wavefront's direct loads of tile t + 2 are issued one by one between the
+// MFMAs of S(t), after the barrier that freed their stage.  The shapes that stream keys from
+// HBM (decode and verify blocks, whose keys each workgroup reads alone) are bound by the
+// latency of those loads rather than by the matrix cores: there P.V follows its softmax
+// directly, which frees the previous tile's stage for a third tile in flight.
 //
-// Masks.  A mask that is the same for every head, with 16-byte aligned rows, may be staged in
-// LDS (the ML variants, chosen by the host): each tile's 32-key window of the workgroup's mask
-// rows rides in a 4 KiB stage of its own beside K and V, loaded by wavefronts 0-3 with the same
-// direct loads and waits, and each lane reads its words from there.  Otherwise each lane loads
-// its words from memory.  Both give the same bits.
+// Masks.  A mask that is the same for every head may be staged in LDS beside each K/V tile
+// (chosen by the host), in one of two layouts.  Words: each key's mask word in a dword of its
+// own (1-, 2- and 4-byte direct loads each write one zero-extended dword per lane), the window's
+// rows at a 264-byte pitch so that lanes of different rows read different banks; any row stride
+// and any kv_len, at most 32 rows per workgroup; every wavefront issues 16 / W of the 16 loads of
+// a tile.  Rows: 16-byte chunks of rows whose pitch is a multiple of 16 bytes, up to 4 KiB of
+// rows, loaded by wavefronts 0-3 (kept for prompt workgroups whose pairs span more than 32
+// rows).  Otherwise each lane loads its words from memory.  All three give the same bits.
 //
 // The softmax is the online (flash) form of the plain definition: per pair a running max m
 // (log2 units of the scaled score), a running sum l and the accumulator O, rescaled by
@@ -344,11 +349,17 @@ __device__ __forceinline__ void wait_tiles_in_flight_n(int n_tiles) {
   }
 }
 
-// mask_loads: this wavefront also issues one direct load of mask rows per tile.
-template <int W>
-__device__ __forceinline__ void wait_tiles_in_flight(int n_tiles, bool mask_loads = false) {
-  if (mask_loads) wait_tiles_in_flight_n<W, 1>(n_tiles);
-  else wait_tiles_in_flight_n<W, 0>(n_tiles);
+// The mask loads a wavefront adds to each tile's: none (ML = 0), one 16-byte row load on
+// wavefronts 0-3 (ML = 1, mask_wave), or 16 / W word loads on every wavefront (ML = 2).
+template <int W, int ML>
+__device__ __forceinline__ void wait_tiles_in_flight(int n_tiles, bool mask_wave) {
+  if constexpr (ML == 2) {
+    wait_tiles_in_flight_n<W, 16 / W>(n_tiles);
+  } else if (ML == 1 && mask_wave) {
+    wait_tiles_in_flight_n<W, 1>(n_tiles);
+  } else {
+    wait_tiles_in_flight_n<W, 0>(n_tiles);
+  }
 }
 
 // This lane's index, read afresh each time (volatile): a per-lane address derived from it is
@@ -462,21 +473,21 @@ __device__ __forceinline__ void exact_pair(const FwdParams& p, int b, int h, int
   }
 }
 
-template <int DT, int MK, int W, bool ML, bool SPLIT>
+template <int DT, int MK, int W, bool LAG, int ML, bool SPLIT>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) {
   static_assert(W == 4 || W == 8, "four or eight wavefronts of one column block each");
-  static_assert(!ML || MK != 0, "mask rows in LDS: masked shapes");
-  // Short decode / verify (four wavefronts) streams keys from HBM and has little to compute per
-  // tile: its P.V runs right after its softmax, which frees the previous tile's stage for a
-  // third tile in flight.  The eight-wavefront shape keeps P.V one tile behind.
-  constexpr bool LAG = W == 8;
+  static_assert(!LAG || W == 8, "the lagged P.V is an eight-wavefront schedule");
+  static_assert(ML >= 0 && ML <= 2 && (ML == 0 || MK != 0), "mask in LDS: masked kernels");
+  // LAG: P.V one tile behind its softmax (prompts).  Without it (decode / verify, which stream
+  // their keys from HBM) P.V runs right after its softmax, which frees the previous tile's stage
+  // for a third tile in flight.
   constexpr int PF = LAG ? kPrefetch : kPrefetch + 1;  // tiles in flight
   static_assert(PF < kStages || !LAG, "the lagged P.V keeps tile t - 1 in its stage");
   static_assert(PF <= kStages - 1 && PF <= 3, "a stage for the tile consumed");
   constexpr int kGroupBlocks = W;  // column blocks of this workgroup
   // kStages stages of (K tile, V tile): kPrefetch tiles in flight while one is consumed and
   // the one before it finishes its P.V product.  Stage of tile t: t % kStages.
-  // with the mask rows in LDS, kStages stages of them follow the K/V stages
+  // with the mask in LDS, kStages stages of its window follow the K/V stages
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kFwdLdsBytes + (ML ? kStages * kMaskStageLds : 0)];
 
   const int tid = threadIdx.x;
@@ -541,27 +552,49 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   const uint16_t* kbase = p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
   const uint16_t* vbase = p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
 
-  // ---- mask rows staged in LDS (ML: the mask is the same for every head and the rows r_lo ..
-  // r_hi of every workgroup fit a mask stage, which the host checked): the 32-key window of
-  // those rows for each tile is loaded with the tile (wavefronts 0-3 load 1 KiB each: stage byte
+  // ---- the mask in LDS (ML > 0: the mask is the same for every head and the workgroup's rows
+  // r_lo .. r_hi fit a mask stage, which the host checked).  ML = 1: the 32-key window of those
+  // rows for each tile in 16-byte chunks (wavefronts 0-3 load 1 KiB each: stage byte
   // 1024 w + 16 l is byte (1024 w + 16 l) % kMaskRowBytes of window row (1024 w + 16 l) /
-  // kMaskRowBytes), and a lane reads its words from LDS.  Otherwise each lane loads its words
-  // from memory.
+  // kMaskRowBytes).  ML = 2: one dword per key (load n = 0 .. 15 of a tile covers window rows
+  // 2n and 2n + 1, lane l row 2n + l / 32 and key l % 32, at stage byte n kWordPitch + 4 l).
+  // Keys past the mask's end read as zeros; every pair masks them.  ML = 0: each lane loads its
+  // words from memory.
   constexpr int kMaskEsz = MK == 1 ? 1 : MK == 2 ? 2 : 4;
   constexpr int kMaskRowBytes = kKeysPerTile * kMaskEsz;
-  constexpr int kMaskRows = kMaskStageLds / kMaskRowBytes;
-  constexpr bool mlds = ML;
-  const bool mwave = ML && wave < 4;  // this wavefront issues a mask load per tile
-  const int mbytes = mlds ? (int)(((int64_t)(p.rows - 1) * p.m_sr + p.kv_len) * kMaskEsz) : 0;
+  constexpr int kMaskRows = ML == 2 ? 32 : 4096 / kMaskRowBytes;
+  constexpr int kWordPitch = 264;           // ML = 2: bytes per load (two rows of 32 dwords + skew)
+  constexpr int kWordLoads = 16 / W;        // ML = 2: loads per tile of each wavefront
+  static_assert(ML != 2 || 16 * kWordPitch <= kMaskStageLds, "word layout fits a mask stage");
+  const bool mwave = ML == 1 && wave < 4;  // ML = 1: this wavefront issues a mask load per tile
+  const int mbytes = ML ? (int)(((int64_t)(p.rows - 1) * p.m_sr + p.kv_len) * kMaskEsz) : 0;
   const __amdgpu_buffer_rsrc_t mrs =
-      buffer_rsrc(static_cast<const uint8_t*>(p.mask) + (mlds ? (int64_t)b * p.m_sb * kMaskEsz : 0), mbytes);
+      buffer_rsrc(static_cast<const uint8_t*>(p.mask) + (ML ? (int64_t)b * p.m_sb * kMaskEsz : 0), mbytes);
   const uint32_t mpos = (uint32_t)(wave * 1024 + lane * 16);
   const uint32_t mvoff =
-      mlds ? (uint32_t)(r_lo + mpos / kMaskRowBytes) * (uint32_t)p.m_sr * kMaskEsz + mpos % kMaskRowBytes : 0u;
+      ML == 1 ? (uint32_t)(r_lo + mpos / kMaskRowBytes) * (uint32_t)p.m_sr * kMaskEsz + mpos % kMaskRowBytes : 0u;
+  uint32_t mwoff[ML == 2 ? kWordLoads : 1];  // ML = 2: byte offset of this lane's word of each load
+#pragma unroll
+  for (int i = 0; i < (ML == 2 ? kWordLoads : 1); ++i) {
+    const int n = wave * kWordLoads + i;
+    mwoff[i] = ML == 2 ? ((uint32_t)(r_lo + 2 * n + (lane >> 5)) * (uint32_t)p.m_sr + (uint32_t)(lane & 31)) *
+                             (uint32_t)kMaskEsz
+                       : 0u;
+  }
   auto issue_mask = [&](int j0, int st) {
-    if (mwave) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(mrs, (lds_void*)(lds + kFwdLdsBytes + st * kMaskStageLds + wave * 1024),
-                                               16, mvoff + (uint32_t)j0 * kMaskEsz, 0, 0, 0);
+    if constexpr (ML == 1) {
+      if (mwave) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            mrs, (lds_void*)(lds + kFwdLdsBytes + st * kMaskStageLds + wave * 1024), 16,
+            mvoff + (uint32_t)j0 * kMaskEsz, 0, 0, 0);
+      }
+    } else if constexpr (ML == 2) {
+#pragma unroll
+      for (int i = 0; i < kWordLoads; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            mrs, (lds_void*)(lds + kFwdLdsBytes + st * kMaskStageLds + (wave * kWordLoads + i) * kWordPitch),
+            kMaskEsz, mwoff[i], j0 * kMaskEsz, 0, 0);
+      }
     }
   };
 
@@ -610,7 +643,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   int stage = 0;
   auto stream_step = [&](int t) {
     // tile t landed for this wavefront once only the tiles issued after it remain in flight
-    wait_tiles_in_flight<W>(min(PF - 1, n_kt - 1 - t), mwave);
+    wait_tiles_in_flight<W, ML>(min(PF - 1, n_kt - 1 - t), mwave);
     // ... and for everyone; everyone is done with tile t - 2, whose stage is refilled next
     __builtin_amdgcn_s_barrier();
     if (t + PF < n_kt) {
@@ -631,7 +664,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   TileDma<W> dma;
   dma.koff = koff, dma.voff = voff, dma.kst = (uint32_t)p.k_st, dma.vst = (uint32_t)p.v_st;
   auto sync_step = [&](int t) {
-    wait_tiles_in_flight<W>(1, mwave);
+    wait_tiles_in_flight<W, ML>(1, mwave);
     __builtin_amdgcn_s_barrier();
     int st2 = stage + PF;
     if (st2 >= kStages) st2 -= kStages;
@@ -710,35 +743,46 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // The same with the tile's mask window in LDS (the stage of K/V stage address sb): the words
   // of keys q and q + 8 are adjacent, one read each.
   auto mask_lds_apply = [&](f32x16& sc, int jb, int lim, uint32_t sb) {
-    if constexpr (MK != 0) {
+    if constexpr (ML != 0) {
       const int rho = min(max(r0 - r_lo, 0), kMaskRows - 1);
       const uint32_t mst = lds0 + kFwdLdsBytes + ((sb - lds0) / kStageLds) * kMaskStageLds;
-      const lds_u8* row = reinterpret_cast<const lds_u8*>((uintptr_t)(mst + rho * kMaskRowBytes + 2 * hf * kMaskEsz));
       auto apply = [&](int q, uint32_t w) {
         const int j = jb + key_of(q) + 2 * hf;
         sc[q] = j < lim ? sc[q] * p.scale_log2 + mask_term_of<DT, MK>(w) : -INFINITY;
       };
+      if constexpr (ML == 2) {
+        const uint32_t row = mst + (rho >> 1) * kWordPitch + (rho & 1) * 128 + 2 * hf * 4;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const lds_u8* at = row + key_of(q) * kMaskEsz;
-        if constexpr (MK == 1) {
-          const uint16_t x = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(at);
-          apply(q, x & 0xffu);
-          apply(q + 8, x >> 8);
-        } else if constexpr (MK == 2) {
-          const uint32_t x = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(at);
-          apply(q, x & 0xffffu);
-          apply(q + 8, x >> 16);
-        } else {
-          const u32x2 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(at);
+        for (int q = 0; q < 8; ++q) {
+          const u32x2 x =
+              *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>((uintptr_t)(row + key_of(q) * 4));
           apply(q, x[0]);
           apply(q + 8, x[1]);
+        }
+      } else {
+        const lds_u8* row = reinterpret_cast<const lds_u8*>((uintptr_t)(mst + rho * kMaskRowBytes + 2 * hf * kMaskEsz));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const lds_u8* at = row + key_of(q) * kMaskEsz;
+          if constexpr (MK == 1) {
+            const uint16_t x = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(at);
+            apply(q, x & 0xffu);
+            apply(q + 8, x >> 8);
+          } else if constexpr (MK == 2) {
+            const uint32_t x = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(at);
+            apply(q, x & 0xffffu);
+            apply(q + 8, x >> 16);
+          } else {
+            const u32x2 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(at);
+            apply(q, x[0]);
+            apply(q + 8, x[1]);
+          }
         }
       }
     }
   };
   auto mask_any = [&](f32x16& sc, int jb, int lim, int64_t mrow, uint32_t sb) {
-    if constexpr (ML) mask_lds_apply(sc, jb, lim, sb);
+    if constexpr (ML != 0) mask_lds_apply(sc, jb, lim, sb);
     else mask_scores(sc, jb, lim, mrow);
   };
 
@@ -953,23 +997,28 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   repair(finish(valid0, h0, r0, lt0, m0, o0), valid0, h0, r0, lim0, mrow0);
 }
 
+// shape 0: four wavefronts; 2: eight with the lagged P.V; 3: eight without it.  ml: the mask
+// layout in LDS (0: none, per-lane loads; 1: 16-byte rows, shape 2 only; 2: words).
 template <int DT, int MK, bool SPLIT>
 hipError_t launch_fwd_s(const FwdParams& p, int shape, hipStream_t stream) {
+  const dim3 grid(p.grid), b4(256), b8(512);
+  const int ml = MK != 0 ? p.mask_lds : 0;
   if constexpr (MK != 0) {
-    if (p.mask_lds) {
-      if (shape == 0) {
-        hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, true, SPLIT>), dim3(p.grid), dim3(256), 0, stream, p);
-      } else {
-        hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, true, SPLIT>), dim3(p.grid), dim3(512), 0, stream, p);
-      }
+    if (ml == 2) {
+      if (shape == 0) hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, false, 2, SPLIT>), grid, b4, 0, stream, p);
+      else if (shape == 2) hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, true, 2, SPLIT>), grid, b8, 0, stream, p);
+      else hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, false, 2, SPLIT>), grid, b8, 0, stream, p);
+      return hipGetLastError();
+    }
+    if (ml == 1) {
+      if (shape != 2) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, true, 1, SPLIT>), grid, b8, 0, stream, p);
       return hipGetLastError();
     }
   }
-  if (shape == 0) {
-    hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, false, SPLIT>), dim3(p.grid), dim3(256), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, false, SPLIT>), dim3(p.grid), dim3(512), 0, stream, p);
-  }
+  if (shape == 0) hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, false, 0, SPLIT>), grid, b4, 0, stream, p);
+  else if (shape == 2) hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, true, 0, SPLIT>), grid, b8, 0, stream, p);
+  else hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, false, 0, SPLIT>), grid, b8, 0, stream, p);
   return hipGetLastError();
 }
 

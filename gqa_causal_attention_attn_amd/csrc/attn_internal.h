@@ -28,7 +28,7 @@ constexpr int kStages = 4;                                   // LDS stages of (K
 constexpr int kPrefetch = 2;                                 // tiles in flight ahead of the one consumed
 constexpr int kFwdLdsBytes = kStages * kStageLds;            // 133,120 B
 constexpr int kTargetBlocks = 256;   // main-pass workgroups aimed for (one per CU)
-constexpr int kMaskStageLds = 4096;  // LDS bytes per stage for the mask rows of a tile (masked kernels)
+constexpr int kMaskStageLds = 4352;  // LDS bytes per stage for the mask window of a tile (masked kernels)
 constexpr size_t kScratchBytes = (size_t)64 << 20;  // the device scratch of attn_decode_noalloc, per GPU
 
 // Parameters of the main (flash / split-KV) pass.  Strides are in elements.
@@ -58,8 +58,8 @@ struct FwdParams {
   int n_splits;
   int keys_per_split;    // multiple of kKeysPerTile
   int grid;              // workgroups in the launch
-  int mask_lds;          // the mask is the same for every head, 16-byte aligned and < 2 GiB: its
-                         // tile rows may be staged in LDS with direct loads
+  int mask_lds;          // mask window of each tile staged in LDS: 0 no (per-lane loads), 1 in
+                         // 16-byte row chunks, 2 one dword per key (see attn_fwd.hip)
 };
 
 // The main pass's inputs, handed to the merge so that it can compute a chunk partial again
@@ -167,7 +167,8 @@ inline bool merge_fits(int n_chunks, int64_t n_rows) {
 }
 
 // Launchers (return hipGetLastError()).  dtype 0 = bf16, 1 = fp16; mask_kind as attn_mask_kind.
-// shape: 0 = 4 wavefronts, 2 = 8 wavefronts, each wavefront one 32-pair column block
+// shape: 0 = 4 wavefronts, 2 = 8 wavefronts with the P.V product one tile behind (prompts),
+// 3 = 8 wavefronts without that lag (decode / verify); each wavefront one 32-pair column block
 hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);

@@ -85,7 +85,9 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, h
   g_fwd_shape = shape;
   CHECK(dtype == 0 || dtype == 1, "dtype %d", dtype);
   CHECK(mask_kind >= 0 && mask_kind <= 3, "mask kind %d", mask_kind);
-  CHECK(shape == 0 || shape == 2, "shape %d", shape);
+  CHECK(shape == 0 || shape == 2 || shape == 3, "shape %d", shape);
+  CHECK(p.mask_lds >= 0 && p.mask_lds <= 2 && (p.mask_lds != 1 || shape == 2) && (mask_kind != 0 || p.mask_lds == 0),
+        "mask layout %d on shape %d", p.mask_lds, shape);
   CHECK(p.grid == (int64_t)p.B * p.Hkv * p.n_splits * p.n_tiles, "grid %d", p.grid);
   CHECK(p.keys_per_split % kKeysPerTile == 0, "keys_per_split %d", p.keys_per_split);
   CHECK((p.n_splits > 1) == (p.part_o != nullptr), "partials %d", p.n_splits);
@@ -297,7 +299,8 @@ void sweep() {
                   CHECK(g_fwd.grid == info.grid_blocks && g_fwd.n_splits == info.n_splits &&
                             g_fwd.keys_per_split == info.keys_per_split && g_fwd.n_tiles == info.n_row_tiles,
                         "launched plan differs from the described one");
-                  CHECK((g_fwd_shape == 2 ? 8 : 4) == info.waves_per_block, "shape");
+                  CHECK((g_fwd_shape == 0 ? 4 : 8) == info.waves_per_block, "shape");
+                  CHECK(g_fwd_shape != 3 || op == ATTN_OP_DECODE, "the streaming shape is for decode rows");
                   if (split) {
                     const char* lse = reinterpret_cast<const char*>(g_fwd.part_lse);
                     CHECK(reinterpret_cast<const char*>(g_fwd.part_o) == kWs && lse > kWs &&

@@ -4,11 +4,11 @@ An additive mask adds its value to the score of every key it admits and hides th
 holds -Inf ("Qwen head-chunked SDPA (#113)", "Exact scope found during review": the caller's mask
 is passed to every chunk and broadcast).  A mask holding only 0 and -Inf cannot tell a correct
 scaling of the value from a wrong one (0 times anything is 0), so every mask here holds N(0, 1)
-values at the admitted keys.  Each case runs the mask through both of the main pass's paths (its
-rows staged in LDS beside each K/V tile, and per-lane loads), which must give the same bits, on
-the four-wavefront decode shape and the eight-wavefront verify and prompt shapes, with one KV
-split (the gated output written by the main pass) and with the planned splits (partials and the
-merge), in bf16 and fp16, against the float64 oracle.
+values at the admitted keys.  Each case runs the mask through the main pass's paths (its window
+staged in LDS beside each K/V tile as one dword per key or as 16-byte row chunks, and per-lane
+loads), which must give the same bits, on the four-wavefront decode shape and the eight-wavefront
+verify and prompt shapes, with one KV split (the gated output written by the main pass) and with
+the planned splits (partials and the merge), in bf16 and fp16, against the float64 oracle.
 """
 
 import numpy as np
@@ -33,11 +33,13 @@ def _say(*a):
     print(*a, flush=True)
 
 
-# (name, B, Hq, Hkv, rows, kv_offset, op, mask batch extent, expected shape in the variant name)
+# (name, B, Hq, Hkv, rows, kv_offset, op, mask batch extent, shape in the variant name, mask rows a
+# workgroup covers)
 CASES = [
-    ("decode_4x1", 2, 16, 2, 6, 4106, ga._abi.OP_DECODE, 2, "4x1"),
-    ("verify_8x1", 2, 16, 2, 32, 4080, ga._abi.OP_DECODE, 1, "8x1"),
-    ("prompt_8x1", 1, 24, 4, 160, 352, ga._abi.OP_PREFILL, 1, "8x1"),
+    ("decode_4x1", 2, 16, 2, 6, 4106, ga._abi.OP_DECODE, 2, "4x1", 6),
+    ("verify_8x1", 2, 16, 2, 32, 4080, ga._abi.OP_DECODE, 1, "8x1_stream", 32),
+    ("prompt_8x1_32rows", 1, 16, 2, 96, 416, ga._abi.OP_PREFILL, 1, "8x1", 32),
+    ("prompt_8x1_43rows", 1, 24, 4, 160, 352, ga._abi.OP_PREFILL, 1, "8x1", 43),
 ]
 
 
@@ -67,44 +69,73 @@ def _run(op, q, k, v, g, off, kv, m, n_splits):
     return out
 
 
+def _expected_layouts(window, kind, name):
+    """Variant-name markers of the three storages: 64-byte aligned rows, rows at an odd stride
+    (both the same for every head), and a copy per query head (per-lane loads)."""
+    if window <= 32:
+        return "ldswords", "ldswords", None
+    esz = {"add": 2, "add_f32": 4}[kind]
+    rows16 = "_8x1" in name and window <= 4096 // (32 * esz)
+    return ("ldsrows" if rows16 else None), None, None
+
+
 @needs_gpu
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("n_splits", [0, 1])
 @pytest.mark.parametrize("case", range(len(CASES)), ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("kind", ["add", "add_f32"])
-def test_additive_mask_values_both_paths(case, n_splits, dtype, kind):
-    name, B, Hq, Hkv, rows, off, op, Bm, shape = CASES[case]
+def test_additive_mask_values_every_path(case, n_splits, dtype, kind):
+    name, B, Hq, Hkv, rows, off, op, Bm, shape, window = CASES[case]
     _say("mask values", name, dtype, kind, "n_splits", n_splits)
     kv = off + rows
-    assert (kv * 2) % 16 == 0  # every mask row ends on a 16-byte chunk: the LDS path is possible
     qb, kb, vb, gb, mb = _inputs(5000 + case, B, Hq, Hkv, rows, off, dtype, Bm, kind)
     mdev, mref = _mask_dev(mb, kind, dtype)
     q, k, v, g = (to_dev(x, dtype) for x in (qb, kb, vb, gb))
     lds_stride, lane_stride = lds_and_lane_strides(kv, mdev.element_size())
-    m_lds, m_lane = strided_mask(mdev, lds_stride), strided_mask(mdev, lane_stride)
-    names = []
-    for m in (m_lds, m_lane):
+    storages = [strided_mask(mdev, lds_stride), strided_mask(mdev, lane_stride),
+                mdev.expand(Bm, Hq, rows, kv).contiguous()]
+    want = _expected_layouts(window, kind, name)
+    outs = []
+    for m, marker in zip(storages, want):
         a = ga._args(q, k, v, g, torch.empty_like(q), kv_offset=off, kv_len=kv, causal=True, scale=0.0,
                      head_chunk=0, n_splits=n_splits, mask=m)
         d = ga.describe_plan(a, op)
-        names.append(d["variant_name"])
+        vn = d["variant_name"]
         assert (d["n_splits"] == 1) == (n_splits == 1), d
-    # a workgroup of the prompt shape covers 43 mask rows: more than an LDS stage holds in fp32
-    # words (32), so that case takes the per-lane loads on both storages
-    staged = not (kind == "add_f32" and name == "prompt_8x1")
-    assert ("ldsmask" in names[0]) == staged and "ldsmask" not in names[1], names
-    assert all(shape in n for n in names), names
-    out_lds = _run(op, q, k, v, g, off, kv, m_lds, n_splits)
-    out_lane = _run(op, q, k, v, g, off, kv, m_lane, n_splits)
-    assert torch.equal(out_lds.view(torch.int16), out_lane.view(torch.int16)), "mask paths differ"
+        assert f"_{shape}" in vn and (marker in vn if marker else "lds" not in vn), (vn, marker)
+        outs.append(_run(op, q, k, v, g, off, kv, m, n_splits))
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16)), "mask paths differ"
     ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off,
                               kv_len=kv, mask=mref, mask_kind="add")
-    _say(assert_close(syn.widen(to_bits(out_lds), dtype), ref, f"mask values {name}"))
+    _say(assert_close(syn.widen(to_bits(outs[0]), dtype), ref, f"mask values {name}"))
     # the values matter: the same call with the mask's finite entries zeroed lands elsewhere
     zeroed = np.where(np.isfinite(mref), 0.0, -np.inf)
     ref0 = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off,
                                kv_len=kv, mask=zeroed, mask_kind="add")
-    assert not compare(syn.widen(to_bits(out_lds), dtype), ref0)["ok"]
+    assert not compare(syn.widen(to_bits(outs[0]), dtype), ref0)["ok"]
+
+
+@needs_gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("rows", [1, 4, 9, 32])
+def test_decode_mask_rows_at_any_length(dtype, rows):
+    # the decode workload's masks end mid-chunk (kv_len 32769, 32772, ...): the word layout stages
+    # them in LDS anyway, and agrees with the per-lane loads of a full-head copy and the oracle
+    _say("mask at any length", dtype, rows)
+    B, Hq, Hkv, off = 2, 16, 2, 32768
+    kv = off + rows
+    qb, kb, vb, gb, mb = _inputs(5200 + rows, B, Hq, Hkv, rows, off, dtype, 1, "add")
+    q, k, v, g, m = (to_dev(x, dtype) for x in (qb, kb, vb, gb, mb))
+    a = ga._args(q, k, v, g, torch.empty_like(q), kv_offset=off, kv_len=kv, causal=True, scale=0.0, head_chunk=0,
+                 n_splits=0, mask=m)
+    assert "ldswords" in ga.describe_plan(a, ga._abi.OP_DECODE)["variant_name"]
+    out = ga.decode(q, k, v, g, kv_offset=off, mask=m)
+    full = ga.decode(q, k, v, g, kv_offset=off, mask=m.expand(1, Hq, rows, kv).contiguous())
+    assert torch.equal(out.view(torch.int16), full.view(torch.int16))
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off,
+                              kv_len=kv, mask=syn.widen(mb, dtype), mask_kind="add")
+    _say(assert_close(syn.widen(to_bits(out), dtype), ref, "mask at any length"))
 
 
 @needs_gpu

@@ -211,15 +211,13 @@ def test_verify_mask_kinds(kind, dtype):
 @needs_gpu
 @pytest.mark.parametrize("kind", ["bool", "add", "f32"])
 @pytest.mark.parametrize("rows,Bm", [(6, 1), (32, 1), (32, 2)])
-def test_mask_rows_in_lds(kind, rows, Bm):
-    # A head-broadcast mask with 16-byte aligned rows is staged in LDS with each K/V tile (rows 6:
-    # the four-wavefront shape; rows 32: eight wavefronts).  The same mask in storage whose row
-    # stride is not a multiple of 16 bytes takes the per-lane loads: both must give the same bits
-    # and match the oracle.  (A row that ends inside a 16-byte chunk also takes the per-lane
-    # loads: test_head_chunked_verify covers those lengths.)
-    _say("mask rows in LDS", kind, rows, Bm)
+def test_mask_paths_agree(kind, rows, Bm):
+    # A head-broadcast mask is staged in LDS with each K/V tile, one dword per key, whatever its
+    # row stride (rows 6: the four-wavefront shape; rows 32: eight wavefronts); a copy with one
+    # pattern per query head takes the per-lane loads.  All give the same bits and match the oracle.
+    _say("mask paths", kind, rows, Bm)
     B, Hq, Hkv = 2, 16, 2
-    offset = 4112 - rows  # kv_len a multiple of 16 words: every row ends on a 16-byte chunk
+    offset = 4112 - rows
     kv = offset + rows
     qb, kb, vb, gb, rng = _decode_case(600 + rows, B=B, Hq=Hq, Hkv=Hkv, offset=offset, rows=rows)
     masks = [syn.verify_mask(rng["mask"], rows=rows, kv_offset=offset, heads=1,
@@ -234,21 +232,21 @@ def test_mask_rows_in_lds(kind, rows, Bm):
         mdev = torch.from_numpy(mb).cuda()
         mref, mk = (mb.astype(bool), "bool") if kind == "bool" else (mb.astype(np.float64), "add")
     lds_stride, lane_stride = lds_and_lane_strides(kv, mdev.element_size())
-    aligned = strided_mask(mdev, lds_stride)
-    unaligned = strided_mask(mdev, lane_stride)
+    storages = [strided_mask(mdev, lds_stride), strided_mask(mdev, lane_stride),
+                mdev.expand(Bm, Hq, rows, kv).contiguous()]
     q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
     names = []
-    for m in (aligned, unaligned):
+    for m in storages:
         a = ga._args(q, k, v, g, torch.empty_like(q), kv_offset=offset, kv_len=kv, causal=True, scale=0.0,
                      head_chunk=0, n_splits=0, mask=m)
         names.append(ga.describe_plan(a, 1)["variant_name"])
-    assert "ldsmask" in names[0] and "ldsmask" not in names[1], names
-    out_a = ga.decode(q, k, v, g, kv_offset=offset, mask=aligned)
-    out_u = ga.decode(q, k, v, g, kv_offset=offset, mask=unaligned)
-    assert torch.equal(out_a.view(torch.int16), out_u.view(torch.int16))
+    assert "ldswords" in names[0] and "ldswords" in names[1] and "lds" not in names[2], names
+    outs = [ga.decode(q, k, v, g, kv_offset=offset, mask=m) for m in storages]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=offset,
                               kv_len=kv, mask=mref, mask_kind=mk)
-    _say(assert_close(to_f64(out_a), ref, f"mask in LDS {kind}"))
+    _say(assert_close(to_f64(outs[0]), ref, f"mask paths {kind}"))
 
 
 @needs_gpu
