@@ -3,7 +3,8 @@
 Usage: python -m gqa_causal_attention_attn_amd.build  (or call build()).
 Every call compiles from source; nothing is cached.
 
-Besides the library, build() compiles the planted-mistake libraries
+Besides the library, build() compiles the achievable-peak probes of the benchmark
+(libgqa_probes.so, include/gqa_probes.h) and the planted-mistake libraries
 (libgqa_attn_control{1,2,3}.so, the sources with -DGQA_CONTROL=n: a row that sees one key
 past its own, a merge that drops its last chunk, an append one row late).  Only the tests that
 must see them miss the oracle load them.
@@ -61,11 +62,19 @@ def _jobs(verbose, extra):
     return out
 
 
+PROBES_LIB = os.path.join(PKG, "libgqa_probes.so")
+
+
 def build(verbose: bool = False, extra=(), controls: bool = True) -> str:
     """Compile every source and link the shared libraries; returns the library's path."""
     jobs = _jobs(verbose, extra)
     if not controls:
         jobs = jobs[:1]
+    # the achievable-peak probes of the benchmark (libgqa_probes.so)
+    pdir = os.path.join(PKG, "_build_probes")
+    os.makedirs(pdir, exist_ok=True)
+    pobj = os.path.join(pdir, "probes.hip.o")
+    jobs.append((PROBES_LIB, [([hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, "probes.hip"), "-o", pobj], pobj)]))
     compiles = [c for _, cmds in jobs for c in cmds]
     # the head-256 main pass of the library is by far the longest compile: start it first
     compiles.sort(key=lambda c: (not c[1].endswith("attn_fwd.hip.o"), "_control" in c[1]))
