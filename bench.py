@@ -59,7 +59,8 @@ import torch  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 MALL_BYTES = 256 << 20      # Infinity Cache
-ONLY = ("prefill", "decode", "verify", "decode_f16", "verify_f16", "decode_27b", "prefill_8k")
+ONLY = ("prefill", "decode", "verify", "decode_f16", "verify_f16", "decode_27b", "prefill_8k", "prefill_d128",
+        "prefill_d64")
 
 
 def _up(bits, dev, dtype="bf16"):
@@ -168,17 +169,16 @@ class Plans:
         G = Hq // Hkv
         problems = []
         name_v = d["variant_name"]
-        if D == 256:
-            if f"_{dtype}_" not in name_v + "_":
-                problems.append("dtype")
-            want_mask = {0: None, 1: "maskbool", 2: "maskadd", 3: "maskf32"}[mask_kind]
-            if (want_mask is None) != ("mask" not in name_v) or (want_mask and want_mask not in name_v):
-                problems.append("mask kind")
-            want_chunks = ga.head_chunk_plan(rows, Hq, Hkv) if head_chunk == 0 else (
-                [head_chunk] * (G // head_chunk) + ([G % head_chunk] if G % head_chunk else []))
-            if d["chunk_sizes"] != want_chunks:
-                problems.append("head chunks")
-        elif name_v != f"fwd_small_d{D}":
+        if f"_{dtype}_" not in name_v + "_":
+            problems.append("dtype")
+        want_mask = {0: None, 1: "maskbool", 2: "maskadd", 3: "maskf32"}[mask_kind]
+        if (want_mask is None) != ("mask" not in name_v) or (want_mask and want_mask not in name_v):
+            problems.append("mask kind")
+        want_chunks = ga.head_chunk_plan(rows, Hq, Hkv) if head_chunk == 0 else (
+            [head_chunk] * (G // head_chunk) + ([G % head_chunk] if G % head_chunk else []))
+        if d["chunk_sizes"] != want_chunks:
+            problems.append("head chunks")
+        if (name_v.rsplit("_", 1)[-1] == f"d{D}") != (D != 256) or d["keys_per_tile"] != 8192 // D:
             problems.append("head dim route")
         if n_splits and d["n_splits"] > n_splits:
             problems.append("splits")
@@ -379,9 +379,18 @@ def main():
             kset = DecodeSet(1001, 1, 24, 4, 4096, 4, "bf16", False)
             kset.prep(1, "decode_27b")
             fn = (lambda i: kset.call(1, i))
-        else:
+        elif args.only == "prefill_8k":
             pr = _prompt_8k(ga, syn, dev, plans)
             fn = (lambda i: pr["run"]())
+        else:
+            Dp = int(args.only[len("prefill_d"):])
+            pq, pk, pv, pg, pkc, pvc, pout = _prompt_inputs(syn, dev, B, Hq, Hkv, N, Dp)
+            need = 16
+            for i, s in enumerate(range(0, N, qL)):
+                need = max(need, plans.check(f"prefill_32k_D{Dp}_qL{qL}_block{i}", op=0, B=B, Hq=Hq, Hkv=Hkv,
+                                             rows=min(qL, N - s), kv_offset=s, D=Dp)["workspace_bytes"])
+            wsp = torch.empty(need, dtype=torch.uint8, device=dev)
+            fn = (lambda i: ga.prompt_prefill(pq, pk, pv, pg, pkc, pvc, q_block=qL, out=pout, workspace=wsp))
         for i in range(args.warmup):
             fn(i)
         torch.cuda.synchronize(dev)
@@ -490,12 +499,7 @@ def main():
         if D == 256:
             pq, pk, pv, pg, pkc, pvc, pout = q, k, v, g, kc, vc, out
         else:
-            srng = syn.streams(1005 + D)
-            pq, pk, pv, pg = (_up(syn.normal_bits(srng[nm], (B, H, N, D)), dev)
-                              for nm, H in (("q", Hq), ("k", Hkv), ("v", Hkv), ("gate", Hq)))
-            pkc = torch.empty((B, Hkv, N, D), dtype=torch.bfloat16, device=dev)
-            pvc = torch.empty_like(pkc)
-            pout = torch.empty_like(pq)
+            pq, pk, pv, pg, pkc, pvc, pout = _prompt_inputs(syn, dev, B, Hq, Hkv, N, D)
         op = 2 if composed else 0
         need = max(ga.workspace_bytes(ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=min(qb_, N - s), kv_offset=s,
                                                    capacity=N, D=D), op) for s in range(0, N, qb_))
@@ -593,7 +597,7 @@ def main():
         "prefill_q_blocks": q_blocks,
         "prefill_composed": {"route": "materialised scores: fp32 Q K^T, row softmax to 16-bit weights, P V + gate "
                                       "(attn_prefill_composed), kv_append per block", **composed_fig},
-        "prefill_small_head_dims": {"route": "fused pass for head dims 64 and 128, 24/4 heads, the same prompt "
+        "prefill_small_head_dims": {"route": "the main pass at head dims 64 and 128, 24/4 heads, the same prompt "
                                              "length", **small},
         "decode": {"metric": "decode KV GB/s (35B-A3B shape, batch 2, 16/2 heads, 1 row at offset 32768 with its "
                              "broadcast additive mask, cold KV; device time of attn_decode: main pass + merge)",
@@ -629,6 +633,15 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host, args.cpu_sample_rows, N)
     print(json.dumps(result), flush=True)
+
+
+def _prompt_inputs(syn, dev, B, Hq, Hkv, N, D):
+    """A seeded prompt at head dim D: q, k, v, gate, empty K/V caches and the output."""
+    r = syn.streams(1005 + D)
+    q, k, v, g = (_up(syn.normal_bits(r[nm], (B, H, N, D)), dev)
+                  for nm, H in (("q", Hq), ("k", Hkv), ("v", Hkv), ("gate", Hq)))
+    kc = torch.empty((B, Hkv, N, D), dtype=torch.bfloat16, device=dev)
+    return q, k, v, g, kc, torch.empty_like(kc), torch.empty_like(q)
 
 
 def _prompt_8k(ga, syn, dev, plans):

@@ -19,7 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgqa_attn.so")
-SOURCES = ["attn_fwd.hip", "attn_aux.hip", "attn_composed.hip", "attn_small_d.hip", "attn_noalloc.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd_d256.hip", "attn_fwd_d128.hip", "attn_fwd_d64.hip", "attn_aux.hip", "attn_composed.hip",
+           "attn_noalloc.hip", "attn_api.cpp"]
 ARCH = "gfx950"
 CONTROLS = (1, 2, 3)
 
@@ -76,8 +77,8 @@ def build(verbose: bool = False, extra=(), controls: bool = True) -> str:
     pobj = os.path.join(pdir, "probes.hip.o")
     jobs.append((PROBES_LIB, [([hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, "probes.hip"), "-o", pobj], pobj)]))
     compiles = [c for _, cmds in jobs for c in cmds]
-    # the head-256 main pass of the library is by far the longest compile: start it first
-    compiles.sort(key=lambda c: (not c[1].endswith("attn_fwd.hip.o"), "_control" in c[1]))
+    # the main passes of the library are by far the longest compiles: start them first
+    compiles.sort(key=lambda c: ("attn_fwd_d" not in c[1], "_control" in c[1]))
 
     def run(cmd):
         if verbose:

@@ -7,6 +7,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <string>
+#include <vector>
+
 #include "attn_internal.h"
 #include "gqa_attn.h"
 
@@ -74,7 +77,8 @@ int validate(const attn_args* a, int op) {
   if (a->rows < 1) return ATTN_E_ROWS;
   if (op == ATTN_OP_DECODE && a->rows > ATTN_MAX_DECODE_ROWS) return ATTN_E_ROWS;
   if (a->kv_offset < 0 || a->kv_len < 1 || a->capacity < a->kv_len) return ATTN_E_KV;
-  if (a->kv_len > INT32_MAX - kKeysPerTile || a->kv_offset + a->rows > INT32_MAX - kKeysPerTile) return ATTN_E_KV;
+  // (kernels index keys in 32 bits, up to a tile of 128 keys past kv_len)
+  if (a->kv_len > INT32_MAX - 128 || a->kv_offset + a->rows > INT32_MAX - 128) return ATTN_E_KV;
   if (a->causal && a->kv_len < a->kv_offset + a->rows) return ATTN_E_KV;
   if (!(a->scale >= 0.0f) || !isfinite(a->scale)) return ATTN_E_ARG;
   if (a->causal != 0 && a->causal != 1) return ATTN_E_ARG;
@@ -92,11 +96,6 @@ int validate(const attn_args* a, int op) {
     if (m.Bm != 1 && m.Bm != a->B) return ATTN_E_MASK;
     if (m.Hm != 1 && m.Hm != a->Hq) return ATTN_E_MASK;
     if (m.stride_b < 0 || m.stride_h < 0 || m.stride_row < 0) return ATTN_E_MASK;
-  }
-  if (a->D != ATTN_HEAD_DIM && op != ATTN_OP_COMPOSED) {
-    // the fused pass for head dims 64 and 128: no mask; one workgroup per 32 rows of a head
-    if (m.kind != ATTN_MASK_NONE) return ATTN_E_MASK;
-    if (a->B > 65535 || a->Hq > 65535) return ATTN_E_ARG;
   }
   if (op == ATTN_OP_COMPOSED) {
     if (m.kind != ATTN_MASK_NONE) return ATTN_E_MASK;
@@ -153,7 +152,8 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   const int64_t base_tiles = cdiv(cdiv((int64_t)G * a->rows, kPairsPerBlock), kBlocksPerGroup);
   const int64_t kv_hi = a->causal ? (a->kv_len < a->kv_offset + a->rows ? a->kv_len : a->kv_offset + a->rows)
                                   : a->kv_len;
-  const int64_t n_kt = cdiv(kv_hi, kKeysPerTile);
+  const int T = gqa::tile_keys(a->D);  // keys per tile of the main pass
+  const int64_t n_kt = cdiv(kv_hi, T);
   int64_t S;
   if (a->n_splits == 0) {
     const int64_t base = (int64_t)a->B * a->Hkv * base_tiles;
@@ -171,13 +171,13 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   const int64_t tps = cdiv(n_kt, S);
   S = cdiv(n_kt, tps);
   P->n_splits = (int)S;
-  P->keys_per_split = (int)(tps * kKeysPerTile);
+  P->keys_per_split = (int)(tps * T);
   // Mask window in LDS.  The mask is the same for every head (Hm = 1), spans < 2 GiB, and every
-  // workgroup's (head, row) pairs cover few enough mask rows: at most 32 for one dword per key
-  // (any row stride and kv_len; the word offsets of the window's 32 rows stay below 2^32), else,
-  // on the prompt shape only, 16-byte row chunks of at most 4 KiB of rows, when rows are
-  // 16-byte aligned and end on a whole chunk at kv_len (a chunk that reached past the mask's last
-  // word would read as zeros).
+  // workgroup's (head, row) pairs cover few enough mask rows: at most 1024 / T for one dword per
+  // key (32 at head dim 256; any row stride and kv_len; the word offsets of the window's rows
+  // stay below 2^32), else, on the prompt shape at head dim 256 only, 16-byte row chunks of at
+  // most 4 KiB of rows, when rows are 16-byte aligned and end on a whole chunk at kv_len (a chunk
+  // that reached past the mask's last word would read as zeros).
   if (a->mask.kind != ATTN_MASK_NONE) {
     const attn_mask& m = a->mask;
     const int64_t esz = m.kind == ATTN_MASK_BOOL_U8 ? 1 : m.kind == ATTN_MASK_ADD ? 2 : 4;
@@ -202,9 +202,11 @@ int make_plan(const attn_args* a, int op, Plan* P) {
       if (hi >= 0 && hi - lo + 1 > window) window = hi - lo + 1;
     }
     const bool base = m.Hm == 1 && span < ((int64_t)1 << 31);
-    const bool words = base && window <= 32 &&
-                       ((int64_t)(a->rows + 32) * m.stride_row + a->kv_len + kKeysPerTile) * esz < ((int64_t)1 << 32);
-    const bool rows16 = base && P->shape == 2 && ((uintptr_t)m.ptr % 16) == 0 && (m.stride_row * esz) % 16 == 0 &&
+    const int64_t word_rows = 1024 / T;
+    const bool words = base && window <= word_rows &&
+                       ((int64_t)(a->rows + word_rows) * m.stride_row + a->kv_len + T) * esz < ((int64_t)1 << 32);
+    const bool rows16 = base && a->D == kHeadDim && P->shape == 2 && ((uintptr_t)m.ptr % 16) == 0 &&
+                        (m.stride_row * esz) % 16 == 0 &&
                         (msb * esz) % 16 == 0 && ((int64_t)a->kv_len * esz) % 16 == 0 &&
                         window <= 4096 / (kKeysPerTile * esz);
     P->mask_lds = words ? 2 : rows16 ? 1 : 0;
@@ -216,7 +218,7 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   if (S > 1 && !gqa::merge_fits((int)S, n_rows)) return ATTN_E_ARG;
   if (S > 1) {
     const int64_t nrow = S * a->B * a->Hq * (int64_t)a->rows;
-    P->ws_o_bytes = (size_t)cdiv(nrow * kHeadDim * 4, 256) * 256;
+    P->ws_o_bytes = (size_t)cdiv(nrow * a->D * 4, 256) * 256;
     P->ws_bytes = P->ws_o_bytes + (size_t)cdiv(nrow * 4, 256) * 256;
   }
   return ATTN_OK;
@@ -224,106 +226,14 @@ int make_plan(const attn_args* a, int op, Plan* P) {
 
 // id = mask layout * 32 + shape * 8 + dtype * 4 + mask kind; head dims 64 / 128: 96 / 97
 inline int variant_of(const attn_args* a, const Plan& P) {
-  return P.mask_lds * 32 + P.shape * 8 + a->dtype * 4 + a->mask.kind;
-}
-
-// Plan of the fused pass for head dims 64 and 128.  A workgroup holds hw wavefronts, each 32
-// rows of one head, for hw heads of one KV group that share its K/V tiles in LDS: two when G is
-// even (three or four left wave slots of a CU idle at D = 128, 237 registers a wavefront, and
-// measured slower).  About eight to twelve wavefronts fit a CU, so a block with fewer than
-// ~2048 wavefronts
-// splits its keys (at least 8 tiles of 32 per split) to fill the chip; partials and lse rows as
-// for head dim 256, rows of D.
-struct SmallPlan {
-  int hw;  // heads of one KV group per workgroup (one wavefront each), sharing the K/V tiles
-  int n_splits, keys_per_split;
-  size_t ws_o_bytes, ws_bytes;
-};
-
-// The plan and the checks of its launch limits (grid z = B x splits, x = 32-row tiles of up to
-// 128 threads, and the merge), so that the planning calls and the run reject the same shapes.
-int small_plan(const attn_args* a, SmallPlan* out) {
-  SmallPlan& P = *out;
-  memset(&P, 0, sizeof(P));
-  const int G = a->Hq / a->Hkv;
-  P.hw = G % 2 == 0 ? 2 : 1;
-  const int64_t kv_hi = a->causal ? (a->kv_len < a->kv_offset + a->rows ? a->kv_len : a->kv_offset + a->rows)
-                                  : a->kv_len;
-  const int64_t n_kt = cdiv(kv_hi, kKeysPerTile);
-  int64_t S;
-  if (a->n_splits == 0) {
-    const int64_t base = (int64_t)a->B * a->Hq * cdiv(a->rows, 32);
-    const int64_t want = 2048 / base;
-    const int64_t most = n_kt / 8;
-    S = want < most ? want : most;
-    if (S < 1) S = 1;
-  } else {
-    S = a->n_splits < n_kt ? a->n_splits : n_kt;
-  }
-  const int64_t tps = cdiv(n_kt, S);
-  S = cdiv(n_kt, tps);
-  P.n_splits = (int)S;
-  P.keys_per_split = (int)(tps * kKeysPerTile);
-  if (S > 1) {
-    const int64_t nrow = S * a->B * a->Hq * (int64_t)a->rows;
-    P.ws_o_bytes = (size_t)cdiv(nrow * a->D * 4, 256) * 256;
-    P.ws_bytes = P.ws_o_bytes + (size_t)cdiv(nrow * 4, 256) * 256;
-  }
-  const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
-  if ((int64_t)a->B * S > 65535 || !gqa::grid_fits(cdiv(a->rows, 32), 128)) return ATTN_E_ARG;
-  if (n_rows > (int64_t)INT32_MAX || (S > 1 && !gqa::merge_fits((int)S, n_rows))) return ATTN_E_ARG;
-  return ATTN_OK;
-}
-
-int run_small_d(const attn_args* a, void* ws, size_t ws_bytes, void* stream, bool merge, int32_t* n_chunks,
-                size_t* lse_offset) {
-  SmallPlan P;
-  const int st = small_plan(a, &P);
-  if (st) return st;
-  if (ws_bytes < P.ws_bytes || (P.ws_bytes && !ws)) return ATTN_E_WORKSPACE;
-  if (P.ws_bytes && !aligned16(ws)) return ATTN_E_LAYOUT;
-  gqa::SmallDParams p;
-  memset(&p, 0, sizeof(p));
-  p.q = static_cast<const uint16_t*>(a->q.ptr);
-  p.k = static_cast<const uint16_t*>(a->k_cache.ptr);
-  p.v = static_cast<const uint16_t*>(a->v_cache.ptr);
-  p.gate = static_cast<const uint16_t*>(a->gate.ptr);
-  p.out = static_cast<uint16_t*>(a->out.ptr);
-  p.q_sb = a->q.stride_b, p.q_sh = a->q.stride_h, p.q_sr = a->q.stride_row;
-  p.k_sb = a->k_cache.stride_b, p.k_sh = a->k_cache.stride_h, p.k_st = a->k_cache.stride_row;
-  p.v_sb = a->v_cache.stride_b, p.v_sh = a->v_cache.stride_h, p.v_st = a->v_cache.stride_row;
-  p.g_sb = a->gate.stride_b, p.g_sh = a->gate.stride_h, p.g_sr = a->gate.stride_row;
-  p.o_sb = a->out.stride_b, p.o_sh = a->out.stride_h, p.o_sr = a->out.stride_row;
-  p.D = a->D, p.B = a->B, p.Hq = a->Hq, p.G = a->Hq / a->Hkv, p.rows = a->rows;
-  p.kv_offset = (int)a->kv_offset, p.kv_len = (int)a->kv_len, p.causal = a->causal;
-  const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.hw = P.hw, p.n_splits = P.n_splits, p.keys_per_split = P.keys_per_split;
-  if (P.n_splits > 1) {
-    p.part_o = static_cast<float*>(ws);
-    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_o_bytes);
-  }
-  if (n_chunks) *n_chunks = P.n_splits;
-  if (lse_offset) *lse_offset = P.n_splits > 1 ? P.ws_o_bytes : 0;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (gqa::launch_small_d(p, a->dtype, s) != hipSuccess) return ATTN_E_HIP;
-  if (P.n_splits > 1 && merge) {
-    gqa::MergeParams mp;
-    memset(&mp, 0, sizeof(mp));  // no repair (these inputs are taken to be finite)
-    mp.part_o = p.part_o, mp.part_lse = p.part_lse, mp.gate = p.gate, mp.out = p.out;
-    mp.g_sb = p.g_sb, mp.g_sh = p.g_sh, mp.g_sr = p.g_sr;
-    mp.o_sb = p.o_sb, mp.o_sh = p.o_sh, mp.o_sr = p.o_sr;
-    mp.n_chunks = P.n_splits, mp.B = a->B, mp.Hq = a->Hq, mp.rows = a->rows, mp.D = a->D;
-    if (gqa::launch_merge(mp, a->dtype, s) != hipSuccess) return ATTN_E_HIP;
-  }
-  return ATTN_OK;
+  const int dslot = a->D == 256 ? 0 : a->D == 128 ? 1 : 2;
+  return dslot * 96 + P.mask_lds * 32 + P.shape * 8 + a->dtype * 4 + a->mask.kind;
 }
 
 int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream, bool merge = true,
             int32_t* n_chunks = nullptr, size_t* lse_offset = nullptr) {
   int st = validate(a, op);
   if (st) return st;
-  if (a->D != kHeadDim) return run_small_d(a, ws, ws_bytes, stream, merge, n_chunks, lse_offset);
   Plan P;
   st = make_plan(a, op, &P);
   if (st) return st;
@@ -353,7 +263,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
   p.kv_len = (int)a->kv_len;
   p.B = a->B, p.Hq = a->Hq, p.Hkv = a->Hkv, p.G = P.G, p.rows = a->rows;
   p.causal = a->causal;
-  const float scale = a->scale > 0.0f ? a->scale : 1.0f / 16.0f;
+  const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   p.scale_log2 = scale * 1.4426950408889634f;
   p.chunk = P.chunk;
   p.blocks_per_chunk = P.blocks_per_chunk;
@@ -368,7 +278,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_chunks) *n_chunks = P.n_splits;
   if (lse_offset) *lse_offset = P.n_splits > 1 ? P.ws_o_bytes : 0;
-  if (gqa::launch_fwd(p, a->dtype, a->mask.kind, P.shape, s) != hipSuccess) return ATTN_E_HIP;
+  if (gqa::launch_fwd(p, a->D, a->dtype, a->mask.kind, P.shape, s) != hipSuccess) return ATTN_E_HIP;
   if (P.n_splits > 1 && merge) {
     gqa::MergeParams mp;
     memset(&mp, 0, sizeof(mp));
@@ -378,7 +288,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
     mp.out = p.out;
     mp.g_sb = p.g_sb, mp.g_sh = p.g_sh, mp.g_sr = p.g_sr;
     mp.o_sb = p.o_sb, mp.o_sh = p.o_sh, mp.o_sr = p.o_sr;
-    mp.n_chunks = P.n_splits, mp.B = a->B, mp.Hq = a->Hq, mp.rows = a->rows, mp.D = kHeadDim;
+    mp.n_chunks = P.n_splits, mp.B = a->B, mp.Hq = a->Hq, mp.rows = a->rows, mp.D = a->D;
     gqa::RepairParams& f = mp.fix;  // the inputs of this main pass, for the merge's repair
     f.q = p.q, f.k = p.k, f.v = p.v, f.mask = p.mask;
     f.q_sb = p.q_sb, f.q_sh = p.q_sh, f.q_sr = p.q_sr;
@@ -429,25 +339,24 @@ const char* attn_strerror(int status) {
 }
 
 const char* attn_variant_name(int variant) {
-  // id = mask layout in LDS * 32 + shape * 8 + dtype * 4 + mask kind (see variant_of)
-#define GQA_NAMES(SHAPE)                                                                                        \
-  "fwd_mfma32x32x16_bf16_" SHAPE, "fwd_mfma32x32x16_bf16_maskbool_" SHAPE, "fwd_mfma32x32x16_bf16_maskadd_" SHAPE, \
-      "fwd_mfma32x32x16_bf16_maskf32_" SHAPE, "fwd_mfma32x32x16_f16_" SHAPE, "fwd_mfma32x32x16_f16_maskbool_" SHAPE, \
-      "fwd_mfma32x32x16_f16_maskadd_" SHAPE, "fwd_mfma32x32x16_f16_maskf32_" SHAPE
-  static const char* const names[96] = {
-      GQA_NAMES("4x1"),         GQA_NAMES("unused"), GQA_NAMES("8x1"),         GQA_NAMES("8x1_stream"),
-      GQA_NAMES("unused"),      GQA_NAMES("unused"), GQA_NAMES("8x1_ldsrows"), GQA_NAMES("unused"),
-      GQA_NAMES("4x1_ldswords"), GQA_NAMES("unused"), GQA_NAMES("8x1_ldswords"), GQA_NAMES("8x1_stream_ldswords")};
-#undef GQA_NAMES
-  // shape groups that exist (mask layout * 4 + shape)
-  static const bool used[12] = {true, false, true, true, false, false, true, false, true, false, true, true};
-  if (variant == 96) return "fwd_small_d64";
-  if (variant == 97) return "fwd_small_d128";
-  if (variant < 0 || variant >= 96) return "unknown";
-  const int group = variant >> 3;
-  const bool masked = (variant & 3) != 0;
-  // unmasked variants have no mask layout; masked ones exist in every layout of their shape
-  return used[group] && (masked || group < 4) ? names[variant] : "unknown";
+  // id = head-dim slot (256, 128, 64) * 96 + mask layout in LDS * 32 + shape * 8 + dtype * 4 +
+  // mask kind (see variant_of); ids of variants that do not exist name "unknown"
+  static const std::vector<std::string> names = [] {
+    std::vector<std::string> v(3 * 96);
+    static const char* const kinds[4] = {"", "_maskbool", "_maskadd", "_maskf32"};
+    static const char* const shapes[4] = {"_4x1", "", "_8x1", "_8x1_stream"};
+    static const char* const layouts[3] = {"", "_ldsrows", "_ldswords"};
+    static const char* const dims[3] = {"", "_d128", "_d64"};
+    for (int id = 0; id < 3 * 96; ++id) {
+      const int dslot = id / 96, r = id % 96, ml = r / 32, shape = (r / 8) % 4, dtype = (r / 4) % 2, kind = r % 4;
+      if (shape == 1 || (ml != 0 && kind == 0) || (ml == 1 && (shape != 2 || dslot != 0))) continue;
+      v[id] = std::string("fwd_mfma32x32x16_") + (dtype ? "f16" : "bf16") + kinds[kind] + shapes[shape] + layouts[ml] +
+              dims[dslot];
+    }
+    return v;
+  }();
+  if (variant < 0 || variant >= (int)names.size() || names[variant].empty()) return "unknown";
+  return names[variant].c_str();
 }
 
 int attn_head_chunk_plan(int rows, int n_q_heads, int n_kv_heads, int enabled, int* sizes, int cap, int* n_chunks) {
@@ -469,13 +378,6 @@ int attn_workspace_bytes(const attn_args* a, int op, size_t* bytes) {
     *bytes = L.s_bytes + L.p_bytes + L.l_bytes;
     return ATTN_OK;
   }
-  if (a->D != kHeadDim) {  // the fused pass for head dims 64 and 128: partials of its splits
-    SmallPlan P;
-    st = small_plan(a, &P);
-    if (st) return st;
-    *bytes = P.ws_bytes;
-    return ATTN_OK;
-  }
   Plan P;
   st = make_plan(a, op, &P);
   if (st) return st;
@@ -488,28 +390,6 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
   if (op == ATTN_OP_COMPOSED) return ATTN_E_ARG;
   int st = validate(a, op);
   if (st) return st;
-  if (a->D != kHeadDim) {  // the fused pass for head dims 64 and 128: one plan
-    SmallPlan P;
-    st = small_plan(a, &P);
-    if (st) return st;
-    memset(info, 0, sizeof(*info));
-    info->op = op;
-    info->variant = a->D == 64 ? 96 : 97;
-    info->group_size = a->Hq / a->Hkv;
-    info->n_head_chunks = 1;
-    info->head_chunk = info->group_size;
-    info->rows_per_wave = 32;
-    info->waves_per_block = P.hw;
-    info->n_row_tiles = (a->rows + 31) / 32;
-    info->n_splits = P.n_splits;
-    info->keys_per_split = P.keys_per_split;
-    info->keys_per_tile = kKeysPerTile;
-    info->lds_bytes = 32 * (a->D + 8) * 2 + 32 * (a->D == 64 ? a->D + 32 : a->D + 8) * 2;  // K and V tiles
-    info->grid_blocks = (int64_t)info->n_row_tiles * (a->Hq / P.hw) * a->B * P.n_splits;
-    info->workspace_bytes = (int64_t)P.ws_bytes;
-    info->chunk_sizes[0] = info->group_size;
-    return ATTN_OK;
-  }
   Plan P;
   st = make_plan(a, op, &P);
   if (st) return st;
@@ -524,8 +404,8 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
   info->n_row_tiles = P.n_tiles;
   info->n_splits = P.n_splits;
   info->keys_per_split = P.keys_per_split;
-  info->keys_per_tile = kKeysPerTile;
-  info->lds_bytes = gqa::kFwdLdsBytes;
+  info->keys_per_tile = gqa::tile_keys(a->D);
+  info->lds_bytes = gqa::kFwdLdsBytes + (P.mask_lds ? gqa::kStages * gqa::kMaskStageLds : 0);
   info->grid_blocks = P.grid;
   info->workspace_bytes = (int64_t)P.ws_bytes;
   for (int i = 0; i < P.n_chunks; ++i) info->chunk_sizes[i] = P.chunk_sizes[i];

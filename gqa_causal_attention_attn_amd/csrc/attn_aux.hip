@@ -45,22 +45,26 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // Nonfinite repair of a row (b, h, r) whose chunk partials hold a NaN (a key hidden from the
 // row met a nonfinite V value in a tile the row shared with others, and 0 * Inf became NaN):
 // the row's output computed again from the main pass's inputs over its admissible keys only,
-// by the plain definition in fp32, one key at a time, the whole wavefront on the row (each
-// lane 4 dims, dims 4 lane .. + 3; every score is summed across the wavefront and taken from
-// lane 0, so all lanes use the same one), gated and rounded once.  A NaN that the definition
-// itself produces comes out NaN again.  Only rows with such a chunk get here.
+// by the plain definition in fp32, one key at a time, the whole wavefront on the row (lanes
+// below D / 4 hold 4 dims each, dims 4 lane .. + 3, the others none; every score is summed
+// across the wavefront and taken from lane 0, so all lanes use the same one), gated and rounded
+// once.  A NaN that the definition itself produces comes out NaN again.  Only rows with such a
+// chunk get here.
 template <int DT>
-__device__ __forceinline__ void exact_row(const RepairParams& f, int b, int h, int r, int lane, u32x2 gw,
+__device__ __forceinline__ void exact_row(const RepairParams& f, int D, int b, int h, int r, int lane, u32x2 gw,
                                           uint16_t* orow) {
   const int g = h / f.G;
   const int hi = f.causal ? min(f.kv_len, f.kv_offset + r + 1) : f.kv_len;
   const int lo = 0;
-  const u32x2 qw = *reinterpret_cast<const u32x2*>(f.q + (int64_t)b * f.q_sb + (int64_t)h * f.q_sh +
-                                                   (int64_t)r * f.q_sr + 4 * lane);
+  const bool on = 4 * lane < D;  // this lane holds dims of the row
+  const int dl = on ? 4 * lane : 0;
+  const u32x2 qw0 = *reinterpret_cast<const u32x2*>(f.q + (int64_t)b * f.q_sb + (int64_t)h * f.q_sh +
+                                                    (int64_t)r * f.q_sr + dl);
+  const u32x2 qw = on ? qw0 : (u32x2){0u, 0u};
   const float q0 = to_f32<DT>((uint16_t)(qw[0] & 0xffffu)), q1 = to_f32<DT>((uint16_t)(qw[0] >> 16));
   const float q2 = to_f32<DT>((uint16_t)(qw[1] & 0xffffu)), q3 = to_f32<DT>((uint16_t)(qw[1] >> 16));
-  const uint16_t* kb = f.k + (int64_t)b * f.k_sb + (int64_t)g * f.k_sh + 4 * lane;
-  const uint16_t* vb = f.v + (int64_t)b * f.v_sb + (int64_t)g * f.v_sh + 4 * lane;
+  const uint16_t* kb = f.k + (int64_t)b * f.k_sb + (int64_t)g * f.k_sh + dl;
+  const uint16_t* vb = f.v + (int64_t)b * f.v_sb + (int64_t)g * f.v_sh + dl;
   const int64_t mrow = (int64_t)b * f.m_sb + (int64_t)h * f.m_sh + (int64_t)r * f.m_sr;
   // the score of key j in log2 units; adm: the mask does not hide it
   auto score = [&](int j, bool& adm) {
@@ -74,6 +78,7 @@ __device__ __forceinline__ void exact_row(const RepairParams& f, int b, int h, i
     part = __builtin_fmaf(q1, to_f32<DT>((uint16_t)(kw[0] >> 16)), part);
     part = __builtin_fmaf(q2, to_f32<DT>((uint16_t)(kw[1] & 0xffffu)), part);
     part = __builtin_fmaf(q3, to_f32<DT>((uint16_t)(kw[1] >> 16)), part);
+    part = on ? part : 0.0f;  // lanes past the head dim add nothing (not even 0 * Inf)
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
     part = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, part)));
@@ -115,7 +120,7 @@ __device__ __forceinline__ void exact_row(const RepairParams& f, int b, int h, i
   u32x2 ow;
   ow[0] = pack2<DT>(res[0], res[1]);
   ow[1] = pack2<DT>(res[2], res[3]);
-  *reinterpret_cast<u32x2*>(orow + 4 * lane) = ow;
+  if (on) *reinterpret_cast<u32x2*>(orow + dl) = ow;
 }
 
 // whether any of the four values is NaN
@@ -210,8 +215,8 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
   // a NaN in the sums (a chunk's partial or lse held one) with the main pass's inputs at hand:
   // the row is computed again (a wavefront-uniform branch)
-  if (p.fix.q && __builtin_amdgcn_ballot_w64(__builtin_isnan(wsum) || has_nan4(acc)) != 0) {
-    exact_row<DT>(p.fix, b, h, r, lane, gw, orow);
+  if (p.fix.q && __builtin_amdgcn_ballot_w64(__builtin_isnan(wsum) || (d0 < p.D && has_nan4(acc))) != 0) {
+    exact_row<DT>(p.fix, p.D, b, h, r, lane, gw, orow);
     return;
   }
   // a NaN weight sum carries a NaN chunk of some wavefront
@@ -280,8 +285,8 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
   // a NaN in a chunk's partial or lse with the main pass's inputs at hand: the row is computed
   // again (one wavefront per row)
-  if (p.fix.q && __builtin_amdgcn_ballot_w64(nan_l || __builtin_isnan(wsum) || has_nan4(acc)) != 0) {
-    exact_row<DT>(p.fix, b, h, r, lane, gw, orow);
+  if (p.fix.q && __builtin_amdgcn_ballot_w64(nan_l || __builtin_isnan(wsum) || (d0 < p.D && has_nan4(acc))) != 0) {
+    exact_row<DT>(p.fix, p.D, b, h, r, lane, gw, orow);
     return;
   }
   const float inv = nan_l ? NAN : wsum > 0.0f ? __builtin_amdgcn_rcpf(wsum) : 0.0f;

@@ -1,16 +1,18 @@
-// Main pass of gated causal GQA attention at head_dim 256 for gfx950 (CDNA4).
+// Main pass of gated causal GQA attention for gfx950 (CDNA4), head dims 256, 128 and 64 (a
+// template parameter; attn_fwd_d256.hip, attn_fwd_d128.hip and attn_fwd_d64.hip instantiate it).
+#pragma once
 //
 // One workgroup = one (batch b, KV head g, KV split s, tile of (head, row) pairs of that
 // group), one workgroup per CU.  Shapes: eight wavefronts of one 32-pair column block each (two
 // wavefronts per SIMD), with the P.V product one tile behind (prompts) or without that lag and
 // one more tile in flight (verify blocks, which stream their keys from HBM), and four
 // wavefronts of one block (short decode / verify, whose KV group fits in four blocks).  The
-// group's K and V are streamed through LDS in 32-key tiles and every wavefront reuses every
-// tile, so K/V is read once per group per split.  Tiles move from HBM to LDS with direct
-// buffer->LDS loads (no registers, no VALU) into a ring of four stages.
+// group's K and V are streamed through LDS in tiles of 16 KiB each (8192 / D keys) and every
+// wavefront reuses every tile, so K/V is read once per group per split.  Tiles move from HBM to
+// LDS with direct buffer->LDS loads (no registers, no VALU) into a ring of four stages.
 //
 // Per column block, 32 (head, row) pairs are the N dimension of v_mfma_f32_32x32x16 (bf16 or
-// fp16 in, fp32 accumulate):
+// fp16 in, fp32 accumulate), the keys of a tile the M dimension of the scores in S blocks of 32:
 //
 //   S^T[key, pair]  = K[key, :] . Q[pair, :]          A = K tile (LDS), B = Q (VGPRs)
 //   O^T[dim, pair] += V^T[dim, key] . P^T[key, pair]  A = V tile (LDS, transposing read), B = P
@@ -20,18 +22,19 @@
 // except an exchange with the lane 32 away, and the S accumulator, packed to 16 bits, is
 // already the B operand of the second product.  The k-slots of that product follow the rows
 // of the S accumulator: slot 4a + t of lane half h is row 8a + 4h + t (+16 for the second
-// MFMA); the A operand is gathered in that order by ds_read_b64_tr_b16, which hands each lane
-// of a 16-lane group one column of a 4 x 16 block of 16-bit values (4 rows x 16 dims) that the
-// group reads as rows.  O lives in the accumulation registers (AGPRs) for the whole pass;
-// Q, S and everything the VALU touches stay in VGPRs.
+// MFMA of the S block); the A operand is gathered in that order by ds_read_b64_tr_b16, which
+// hands each lane of a 16-lane group one column of a 4 x 16 block of 16-bit values (4 rows x 16
+// dims) that the group reads as rows.  O lives in the accumulation registers (AGPRs) for the
+// whole pass; Q, S and everything the VALU touches stay in VGPRs.  Whatever the head dim, a tile
+// costs each wavefront 16 MFMAs of scores and 16 of P.V and 16 KiB of K and of V reads from LDS.
 //
-// LDS layout of a 32-key x 256-dim tile: sixteen groups of two whole key rows (1 KiB, the
-// unit one direct load of a wavefront fills from 1 KiB of contiguous memory), group i at
-// i * 1040 bytes: the 16-byte skew per group puts the same dims of different groups on
-// different banks.  MFMA row r holds key 2 gamma(r % 16) + r / 16 with gamma(x) = 4 (x % 4) +
-// x / 4, so the 16 lanes of a K read (16 rows, one 16-byte cell) hit 16 groups and the
-// transposing V reads (4 rows x 2 cells per 16 lanes) hit distinct banks.  Every LDS address
-// is a per-lane base plus a compile-time offset.
+// LDS layout of a tile: sixteen groups of R = 512 / D whole key rows (1 KiB, the unit one
+// direct load of a wavefront fills from R consecutive rows), group i at i * 1040 bytes: the
+// 16-byte skew per group puts the same dims of different groups on different banks.  MFMA row r
+// of S block sb holds key R gamma(r % 16) + 2 sb + r / 16 with gamma(x) = 4 (x % 4) + x / 4, so
+// the 16 lanes of a quarter of a K read (16 rows, one 16-byte cell) hit 16 groups and the
+// transposing V reads (4 rows x 2 cells per 16 lanes, the 4 rows in groups 4 apart) hit
+// distinct banks.  Every LDS address is a per-lane base plus a compile-time offset.
 //
 // Schedule.  On the prompt shape the P.V product of tile t - 1 runs on the matrix cores while
 // the VALU turns tile t's scores into weights (the previous tile stays in its stage: two tiles
@@ -150,9 +153,17 @@ __device__ __forceinline__ void acc_settle_v(f32x16& sc) { asm volatile("s_nop 7
 
 // Wait states between the last mfma32_acc into o and any other instruction that reads o
 // (more than an 8-pass MFMA needs); tied to o so nothing that reads it moves above.
-__device__ __forceinline__ void acc_settle(f32x16 (&o)[8]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]));
+template <int N>
+__device__ __forceinline__ void acc_settle(f32x16 (&o)[N]) {
+  static_assert(N == 8 || N == 4 || N == 2, "8, 4 or 2 dim blocks");
+  if constexpr (N == 8) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]));
+  } else if constexpr (N == 4) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+  } else {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]));
+  }
 }
 
 // Pins o[db] and o[db + 1] in place: whatever reads o[db + 1] after this stays after it, so
@@ -257,31 +268,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
-// Issue the direct loads of tile j0 .. j0 + 31 into the K and V halves of one LDS stage.
-// Group i = keys 2i and 2i + 1, two whole 512-byte rows (lane l: key 2i + l / 32, dims
-// 8 (l % 32) .. + 7), lands at i * kGroupStride; with W wavefronts, wavefront w loads the
-// G = 16 / W groups G w .. G w + G - 1 (keys j0 + 2 G w ..).  The per-lane byte offsets
-// koff / voff (row l / 32, 16-byte cell l % 32) stay fixed; each wavefront's rows get a
-// resource that ends at key kv_end, so keys past the end read as zeros (every pair masks
-// them) and nothing past it is touched.
-template <int W>
+// Issue the direct loads of the tile of keys j0 .. j0 + 8192 / D - 1 into the K and V halves of
+// one LDS stage.  Group i = the R = 512 / D consecutive keys R i .. R i + R - 1, R whole rows of
+// 2 D bytes (lane l: key R i + l / (D / 8), dims 8 (l % (D / 8)) .. + 7), lands at
+// i * kGroupStride; with W wavefronts, wavefront w loads the G = 16 / W groups G w .. G w + G - 1
+// (keys j0 + R G w ..).  The per-lane byte offsets koff / voff (row and 16-byte cell) stay fixed;
+// each wavefront's rows get a resource that ends at key kv_end, so keys past the end read as
+// zeros (every pair masks them) and nothing past it is touched.
+template <int W, int D>
 __device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t* vbase, int64_t k_st, int64_t v_st,
                                            int j0, int kv_end, uint8_t* stage, int wave, uint32_t koff,
                                            uint32_t voff) {
   constexpr int kGroups = 16 / W;
-  const int j = j0 + 2 * kGroups * wave;
-  const int rows = min(max(kv_end - j, 0), 2 * kGroups);
-  const int kbytes = rows ? (rows - 1) * (int)k_st * 2 + kHeadDim * 2 : 0;
-  const int vbytes = rows ? (rows - 1) * (int)v_st * 2 + kHeadDim * 2 : 0;
+  constexpr int kRpg = 512 / D;
+  const int j = j0 + kRpg * kGroups * wave;
+  const int rows = min(max(kv_end - j, 0), kRpg * kGroups);
+  const int kbytes = rows ? (rows - 1) * (int)k_st * 2 + 2 * D : 0;
+  const int vbytes = rows ? (rows - 1) * (int)v_st * 2 + 2 * D : 0;
   const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + (int64_t)j * k_st, kbytes);
   const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + (int64_t)j * v_st, vbytes);
   uint8_t* g0 = stage + (kGroups * wave) * kGroupStride;
 #pragma unroll
   for (int e = 0; e < kGroups; ++e) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(g0 + e * kGroupStride), 16, koff + 4 * e * (uint32_t)k_st,
-                                             0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(g0 + e * kGroupStride), 16,
+                                             koff + 2 * kRpg * e * (uint32_t)k_st, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(g0 + kTileLds + e * kGroupStride), 16,
-                                             voff + 4 * e * (uint32_t)v_st, 0, 0, 0);
+                                             voff + 2 * kRpg * e * (uint32_t)v_st, 0, 0, 0);
   }
 }
 
@@ -289,20 +301,21 @@ __device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t
 // and issued one at a time: load i < G is K group i of this wavefront, load G + i its V group.
 // The main pass spreads them between the MFMAs of a tile's scores, in the shadow of the
 // matrix cores, instead of issuing them in one burst.
-template <int W>
+template <int W, int D>
 struct TileDma {
   static constexpr int kGroups = 16 / W;
   static constexpr int kLoads = 2 * kGroups;
+  static constexpr int kRpg = 512 / D;
   __amdgpu_buffer_rsrc_t kr, vr;
   uint8_t* g0;
   uint32_t koff, voff, kst, vst;
 
   __device__ __forceinline__ void prep(const uint16_t* kbase, const uint16_t* vbase, int64_t k_st, int64_t v_st,
                                        int j0, int kv_end, uint8_t* stage, int wave) {
-    const int j = j0 + 2 * kGroups * wave;
-    const int rows = min(max(kv_end - j, 0), 2 * kGroups);
-    const int kbytes = rows ? (rows - 1) * (int)k_st * 2 + kHeadDim * 2 : 0;
-    const int vbytes = rows ? (rows - 1) * (int)v_st * 2 + kHeadDim * 2 : 0;
+    const int j = j0 + kRpg * kGroups * wave;
+    const int rows = min(max(kv_end - j, 0), kRpg * kGroups);
+    const int kbytes = rows ? (rows - 1) * (int)k_st * 2 + 2 * D : 0;
+    const int vbytes = rows ? (rows - 1) * (int)v_st * 2 + 2 * D : 0;
     kr = buffer_rsrc(kbase + (int64_t)j * k_st, kbytes);
     vr = buffer_rsrc(vbase + (int64_t)j * v_st, vbytes);
     g0 = stage + (kGroups * wave) * kGroupStride;
@@ -311,12 +324,12 @@ struct TileDma {
   template <int I>
   __device__ __forceinline__ void issue() const {
     if constexpr (I < kGroups) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(g0 + I * kGroupStride), 16, koff + 4 * I * kst, 0, 0,
-                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(g0 + I * kGroupStride), 16, koff + 2 * kRpg * I * kst,
+                                               0, 0, 0);
     } else {
       constexpr int e = I - kGroups;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(g0 + kTileLds + e * kGroupStride), 16,
-                                               voff + 4 * e * vst, 0, 0, 0);
+                                               voff + 2 * kRpg * e * vst, 0, 0, 0);
     }
   }
 };
@@ -378,9 +391,20 @@ __device__ __forceinline__ uint32_t v_lane_of(uint32_t l) {
   return kTileLds + (4 * tq + hf) * kGroupStride + 16 * (2 * (g16 & 1) + (uq >> 1)) + 8 * (uq & 1);
 }
 
-// Key (within the tile, less 2 hf) of element q of the S accumulator: row 8 (q / 4) + 4 hf +
-// q % 4 of the MFMA holds key 2 gamma(row % 16) + row / 16, gamma(x) = 4 (x % 4) + x / 4.
-__device__ __forceinline__ constexpr int key_of(int q) { return 8 * (q & 3) + 4 * ((q >> 2) & 1) + (q >> 3); }
+// Key (within the tile, less R hf, R = 512 / D rows per group) of element q of S block sb: row
+// 8 (q / 4) + 4 hf + q % 4 of the block's MFMA holds key R gamma(row % 16) + 2 sb + row / 16,
+// gamma(x) = 4 (x % 4) + x / 4.
+template <int D>
+__device__ __forceinline__ constexpr int key_of(int q, int sb = 0) {
+  return (512 / D) * (4 * (q & 3) + 2 * ((q >> 2) & 1)) + 2 * sb + (q >> 3);
+}
+
+// LDS byte offset (from a lane's K base) of the K operand of S MFMA f of a tile (S block
+// f / (D / 16), k-step f % (D / 16): rows 2 sb + r / 16 of the groups, dims 16 kk + 8 hf ..)
+template <int D>
+__device__ __forceinline__ constexpr int k_operand_offset(int f) {
+  return 2 * (f / (D / 16)) * (2 * D) + 32 * (f % (D / 16));
+}
 
 // max(x, x of the lane 32 away), the same value on both lanes
 __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
@@ -394,7 +418,7 @@ __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 
 // the pair, as the epilogue does.
 // It runs only for inputs that hold nonfinite values; one dim block per pass over the keys keeps
 // its registers few.
-template <int DT, int MK>
+template <int D, int DT, int MK>
 __device__ __forceinline__ void exact_pair(const FwdParams& p, int b, int h, int r, int hf, int kv_lo,
                                         int j_end, int64_t mrow, const uint16_t* kbase, const uint16_t* vbase) {
   const uint16_t* qrow = p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)r * p.q_sr;
@@ -406,7 +430,7 @@ __device__ __forceinline__ void exact_pair(const FwdParams& p, int b, int h, int
     const uint16_t* krow = kbase + (int64_t)j * p.k_st;
     float acc = 0.0f;
 #pragma nounroll
-    for (int d = 0; d < kHeadDim; d += 8) {
+    for (int d = 0; d < D; d += 8) {
       const u32x4 qa = *reinterpret_cast<const u32x4*>(qrow + d);
       const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + d);
 #pragma unroll
@@ -434,7 +458,7 @@ __device__ __forceinline__ void exact_pair(const FwdParams& p, int b, int h, int
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
   // one dim block (32 db ..) per pass over the keys
 #pragma nounroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < D / 32; ++c) {
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
@@ -473,11 +497,24 @@ __device__ __forceinline__ void exact_pair(const FwdParams& p, int b, int h, int
   }
 }
 
-template <int DT, int MK, int W, bool LAG, int ML, bool SPLIT>
+template <int D, int DT, int MK, int W, bool LAG, int ML, bool SPLIT>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) {
+  static_assert(D == 256 || D == 128 || D == 64, "head dims 256, 128 and 64");
+  // A K (or V) tile is 16 KiB whatever the head dim: 8192 / D keys in 16 groups of R = 512 / D
+  // rows; the scores of a tile are T / 32 S blocks of 32 keys, each D / 16 MFMA k-steps, so a
+  // tile costs every wavefront 16 MFMAs for S and 16 for P.V at any head dim.
+  constexpr int kRowBytes = 2 * D;
+  constexpr int kRpg = 512 / D;            // rows per 1 KiB group
+  constexpr int kTileKeys = 8192 / D;      // keys per tile
+  constexpr int kSB = kTileKeys / 32;      // S blocks per tile
+  constexpr int kKSteps = D / 16;          // MFMA k-steps per S block
+  constexpr int kDB = D / 32;              // 32-dim blocks of O
+  constexpr int kCells = D / 8;            // 16-byte cells per row
+  static_assert(kSB * kKSteps == 16 && kDB * kSB == 8, "16 S MFMAs and 8 P.V steps per tile");
   static_assert(W == 4 || W == 8, "four or eight wavefronts of one column block each");
   static_assert(!LAG || W == 8, "the lagged P.V is an eight-wavefront schedule");
   static_assert(ML >= 0 && ML <= 2 && (ML == 0 || MK != 0), "mask in LDS: masked kernels");
+  static_assert(ML != 1 || D == 256, "16-byte mask rows: head dim 256 only");
   // LAG: P.V one tile behind its softmax (prompts).  Without it (decode / verify, which stream
   // their keys from HBM) P.V runs right after its softmax, which frees the previous tile's stage
   // for a third tile in flight.
@@ -546,26 +583,37 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   }
   const int kv_lo = split * p.keys_per_split;
   const int kv_end = __builtin_amdgcn_readfirstlane(min(kv_lo + p.keys_per_split, kv_hi));
-  const int n_kt = kv_end > kv_lo ? (kv_end - kv_lo + kKeysPerTile - 1) / kKeysPerTile : 0;
+  const int n_kt = kv_end > kv_lo ? (kv_end - kv_lo + kTileKeys - 1) / kTileKeys : 0;
   lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
   const uint16_t* kbase = p.k + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
   const uint16_t* vbase = p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
 
   // ---- the mask in LDS (ML > 0: the mask is the same for every head and the workgroup's rows
-  // r_lo .. r_hi fit a mask stage, which the host checked).  ML = 1: the 32-key window of those
-  // rows for each tile in 16-byte chunks (wavefronts 0-3 load 1 KiB each: stage byte
-  // 1024 w + 16 l is byte (1024 w + 16 l) % kMaskRowBytes of window row (1024 w + 16 l) /
-  // kMaskRowBytes).  ML = 2: one dword per key (load n = 0 .. 15 of a tile covers window rows
-  // 2n and 2n + 1, lane l row 2n + l / 32 and key l % 32, at stage byte n kWordPitch + 4 l).
-  // Keys past the mask's end read as zeros; every pair masks them.  ML = 0: each lane loads its
-  // words from memory.
+  // r_lo .. r_hi fit a mask stage, which the host checked).  ML = 1 (head dim 256): the 32-key
+  // window of those rows for each tile in 16-byte chunks (wavefronts 0-3 load 1 KiB each: stage
+  // byte 1024 w + 16 l is byte (1024 w + 16 l) % kMaskRowBytes of window row (1024 w + 16 l) /
+  // kMaskRowBytes).  ML = 2: one dword per key of the tile's window of 1024 / T rows of T keys;
+  // load n = 0 .. 15 covers words 64 n .. 64 n + 63 of the window in row order (lane l: row
+  // (64 n + l) / T, key (64 n + l) % T); window row rho starts at word_row(rho) (rows 8 bytes
+  // apart in their banks).  Keys past the mask's end read as zeros; every pair masks them.
+  // ML = 0: each lane loads its words from memory.
   constexpr int kMaskEsz = MK == 1 ? 1 : MK == 2 ? 2 : 4;
-  constexpr int kMaskRowBytes = kKeysPerTile * kMaskEsz;
-  constexpr int kMaskRows = ML == 2 ? 32 : 4096 / kMaskRowBytes;
-  constexpr int kWordPitch = 264;           // ML = 2: bytes per load (two rows of 32 dwords + skew)
-  constexpr int kWordLoads = 16 / W;        // ML = 2: loads per tile of each wavefront
-  static_assert(ML != 2 || 16 * kWordPitch <= kMaskStageLds, "word layout fits a mask stage");
+  constexpr int kMaskRowBytes = kTileKeys * kMaskEsz;
+  constexpr int kMaskRows = ML == 2 ? 1024 / kTileKeys : 4096 / kMaskRowBytes;
+  constexpr int kWordLoads = 16 / W;  // ML = 2: loads per tile of each wavefront
+  // byte of window row rho in the stage: T = 32 two rows per 264-byte load, T = 64 one row per
+  // load (264 bytes), T = 128 one row per two loads (520 bytes)
+  auto word_row = [](int rho) {
+    if constexpr (kTileKeys == 32) return (rho >> 1) * 264 + (rho & 1) * 128;
+    else if constexpr (kTileKeys == 64) return rho * 264;
+    else return rho * 520;
+  };
+  auto word_load = [](int n) {  // stage byte of load n
+    if constexpr (kTileKeys == 128) return (n >> 1) * 520 + (n & 1) * 256;
+    else return n * 264;
+  };
+  static_assert(ML != 2 || kMaskRows * kTileKeys == 1024, "16 loads of 64 words a tile");
   const bool mwave = ML == 1 && wave < 4;  // ML = 1: this wavefront issues a mask load per tile
   const int mbytes = ML ? (int)(((int64_t)(p.rows - 1) * p.m_sr + p.kv_len) * kMaskEsz) : 0;
   const __amdgpu_buffer_rsrc_t mrs =
@@ -576,8 +624,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   uint32_t mwoff[ML == 2 ? kWordLoads : 1];  // ML = 2: byte offset of this lane's word of each load
 #pragma unroll
   for (int i = 0; i < (ML == 2 ? kWordLoads : 1); ++i) {
-    const int n = wave * kWordLoads + i;
-    mwoff[i] = ML == 2 ? ((uint32_t)(r_lo + 2 * n + (lane >> 5)) * (uint32_t)p.m_sr + (uint32_t)(lane & 31)) *
+    const int f = 64 * (wave * kWordLoads + i) + lane;
+    mwoff[i] = ML == 2 ? ((uint32_t)(r_lo + f / kTileKeys) * (uint32_t)p.m_sr + (uint32_t)(f % kTileKeys)) *
                              (uint32_t)kMaskEsz
                        : 0u;
   }
@@ -592,7 +640,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 #pragma unroll
       for (int i = 0; i < kWordLoads; ++i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            mrs, (lds_void*)(lds + kFwdLdsBytes + st * kMaskStageLds + (wave * kWordLoads + i) * kWordPitch),
+            mrs, (lds_void*)(lds + kFwdLdsBytes + st * kMaskStageLds + word_load(wave * kWordLoads + i)),
             kMaskEsz, mwoff[i], j0 * kMaskEsz, 0, 0);
       }
     }
@@ -600,38 +648,40 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
   // ---- Q of this lane's pairs, in the B-operand order: element t of q*[kk] is dim
   // 16 kk + 8 hf + t
-  u32x4 q0[16];
+  u32x4 q0[kKSteps];
   {
     const uint16_t* qa = p.q + (int64_t)b * p.q_sb + (int64_t)h0 * p.q_sh + (int64_t)r0 * p.q_sr + 8 * hf;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
+    for (int kk = 0; kk < kKSteps; ++kk) {
       q0[kk] = valid0 ? *reinterpret_cast<const u32x4*>(qa + 16 * kk) : (u32x4){0u, 0u, 0u, 0u};
     }
   }
   const int64_t mrow0 = MK ? (int64_t)b * p.m_sb + (int64_t)h0 * p.m_sh + (int64_t)r0 * p.m_sr : 0;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q is in registers before the tile stream starts
-  const uint32_t koff = (uint32_t)(lane >> 5) * (uint32_t)p.k_st * 2 + 16 * (lane & 31);
-  const uint32_t voff = (uint32_t)(lane >> 5) * (uint32_t)p.v_st * 2 + 16 * (lane & 31);
+  const uint32_t koff = (uint32_t)(lane / kCells) * (uint32_t)p.k_st * 2 + 16 * (lane % kCells);
+  const uint32_t voff = (uint32_t)(lane / kCells) * (uint32_t)p.v_st * 2 + 16 * (lane % kCells);
   // the 8-wavefront shape issues every step's loads, past the last tile too (those read
   // nothing), so its waits need no tail cases; the others stop at the last tile
   constexpr bool EARLY = LAG;
   for (int t = 0; t < PF && (EARLY || t < n_kt); ++t) {
-    issue_mask(kv_lo + t * kKeysPerTile, t);
-    issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kKeysPerTile, kv_end, lds + t * kStageLds, wave, koff, voff);
+    issue_mask(kv_lo + t * kTileKeys, t);
+    issue_tile<W, D>(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kTileKeys, kv_end, lds + t * kStageLds, wave, koff,
+                     voff);
   }
 
   // per-lane LDS byte addresses (see the layout above); every read adds a compile-time offset.
-  // MFMA row r of a tile holds key 2 gamma(r % 16) + r / 16 with gamma(x) = 4 (x % 4) + x / 4:
-  // each 16-lane half of a K read then touches 16 different groups, one per bank quad.
+  // MFMA row r of S block sb holds key R gamma(r % 16) + 2 sb + r / 16 with gamma(x) =
+  // 4 (x % 4) + x / 4: the 16 lanes of a quarter of a K read then touch 16 different groups, one
+  // per bank quad, and the 4 keys of a transposing V read sit 64 bytes apart in their banks.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_u8*)lds;
   const int li16 = li & 15;
-  const uint32_t k_lane = (4 * (li16 & 3) + (li16 >> 2)) * kGroupStride + (li >> 4) * 512 + hf * 16;
+  const uint32_t k_lane = (4 * (li16 & 3) + (li16 >> 2)) * kGroupStride + (li >> 4) * kRowBytes + hf * 16;
 
   // the accumulators live in the accumulation registers (AGPRs), everything the VALU touches
   // every tile in VGPRs
-  f32x16 o0[8];
+  f32x16 o0[kDB];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
+  for (int db = 0; db < kDB; ++db) {
     o0[db] = (f32x16){};
     asm volatile("" : "+a"(o0[db]));
   }
@@ -649,9 +699,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     if (t + PF < n_kt) {
       int st2 = stage + PF;
       if (st2 >= kStages) st2 -= kStages;
-      issue_mask(kv_lo + (t + PF) * kKeysPerTile, st2);
-      issue_tile<W>(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + PF) * kKeysPerTile, kv_end, lds + st2 * kStageLds,
-                 wave, koff, voff);
+      issue_mask(kv_lo + (t + PF) * kTileKeys, st2);
+      issue_tile<W, D>(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + PF) * kTileKeys, kv_end, lds + st2 * kStageLds,
+                       wave, koff, voff);
     }
     const uint32_t sb = lds0 + stage * kStageLds;
     stage = stage + 1 == kStages ? 0 : stage + 1;
@@ -661,22 +711,22 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // The 8-wavefront stream: after the barrier of tile t the loads of tile t + PF are prepared,
   // and the S product of tile t issues them one by one between its MFMAs.  Exactly one tile is
   // in flight beyond the one consumed at every wait.
-  TileDma<W> dma;
+  TileDma<W, D> dma;
   dma.koff = koff, dma.voff = voff, dma.kst = (uint32_t)p.k_st, dma.vst = (uint32_t)p.v_st;
   auto sync_step = [&](int t) {
     wait_tiles_in_flight<W, ML>(1, mwave);
     __builtin_amdgcn_s_barrier();
     int st2 = stage + PF;
     if (st2 >= kStages) st2 -= kStages;
-    issue_mask(kv_lo + (t + PF) * kKeysPerTile, st2);
-    dma.prep(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + PF) * kKeysPerTile, kv_end, lds + st2 * kStageLds, wave);
+    issue_mask(kv_lo + (t + PF) * kTileKeys, st2);
+    dma.prep(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + PF) * kTileKeys, kv_end, lds + st2 * kStageLds, wave);
     const uint32_t sb = lds0 + stage * kStageLds;
     stage = stage + 1 == kStages ? 0 : stage + 1;
     return sb;
   };
   auto dma_hook = [&](auto kkc) {
     constexpr int kk = decltype(kkc)::value;
-    constexpr int every = 16 / TileDma<W>::kLoads;
+    constexpr int every = 16 / TileDma<W, D>::kLoads;
     if constexpr (kk % every == 1 % every) dma.template issue<kk / every>();
   };
   auto no_hook = [](auto) {};
@@ -686,7 +736,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     if constexpr (EARLY) {
       for (int t = 0; t < n_kt; ++t) {
         sync_step(t);
-        static_for<TileDma<W>::kLoads>([&](auto ic) { dma.template issue<decltype(ic)::value>(); });
+        static_for<TileDma<W, D>::kLoads>([&](auto ic) { dma.template issue<decltype(ic)::value>(); });
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
@@ -695,93 +745,103 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     return;
   }
 
-  // ---- S^T block of the tile at sb: rows = its 32 keys, columns = the 32 pairs of block q;
-  // K operands read two steps ahead
-  auto scores = [&](uint32_t sb, const u32x4(&q)[16], auto&& hook) {
-    f32x16 sc;
+  // ---- the S^T blocks of the tile at sb (stage address): block i = 32 keys (rows) x the 32
+  // pairs of this wavefront's column block; the 16 MFMAs of a tile (kSB blocks of kKSteps
+  // k-steps) with the K operands read two steps ahead
+  auto scores = [&](uint32_t sb, const u32x4(&q)[kKSteps], auto&& hook, f32x16(&sc)[kSB]) {
     const uint32_t kaddr = sb + k_lane;
     constexpr int kAhead = 2;  // K operands in flight beyond the one consumed
     u32x4 kop[kAhead + 1];
     static_for<kAhead>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      kop[i] = ds_read_b128<32 * i>(kaddr);
+      kop[i] = ds_read_b128<k_operand_offset<D>(i)>(kaddr);
     });
-    static_for<16>([&](auto kkc) {
-      constexpr int kk = decltype(kkc)::value;
-      if constexpr (kk + kAhead < 16) kop[(kk + kAhead) % (kAhead + 1)] = ds_read_b128<32 * (kk + kAhead)>(kaddr);
-      constexpr int issued = kk + kAhead + 1 < 16 ? kk + kAhead + 1 : 16;
-      lgkm_wait1<issued - kk - 1>(kop[kk % (kAhead + 1)]);
-      mfma32_v<DT, kk == 0>(sc, kop[kk % (kAhead + 1)], q[kk]);
-      hook(kkc);
+    static_for<16>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      if constexpr (f + kAhead < 16)
+        kop[(f + kAhead) % (kAhead + 1)] = ds_read_b128<k_operand_offset<D>(f + kAhead)>(kaddr);
+      constexpr int issued = f + kAhead + 1 < 16 ? f + kAhead + 1 : 16;
+      lgkm_wait1<issued - f - 1>(kop[f % (kAhead + 1)]);
+      mfma32_v<DT, f % kKSteps == 0>(sc[f / kKSteps], kop[f % (kAhead + 1)], q[f % kKSteps]);
+      hook(fc);
     });
-    acc_settle_v(sc);
-    return sc;
+    static_for<kSB>([&](auto ic) { acc_settle_v(sc[decltype(ic)::value]); });
   };
 
-  // ---- element q of an S block is MFMA row 8 (q / 4) + 4 hf + q % 4, i.e. key jb + key_of(q)
-  // + 2 hf of this lane's pair.  Scores in log2 units, with keys the pair cannot see at
-  // -inf.  Without a mask the scale folds into the exponent later (the max commutes with
+  // ---- element q of S block i is MFMA row 8 (q / 4) + 4 hf + q % 4, i.e. key jb +
+  // key_of<D>(q, i) + R hf of this lane's pair.  Scores in log2 units, with keys the pair cannot
+  // see at -inf.  Without a mask the scale folds into the exponent later (the max commutes with
   // it, scale > 0) and only tiles that reach some pair's bound compare keys.
-  auto mask_scores = [&](f32x16& sc, int jb, int lim, int64_t mrow) {
+  auto mask_scores = [&](f32x16(&sc)[kSB], int jb, int lim, int64_t mrow) {
     if constexpr (MK == 0) {
-      if (jb + kKeysPerTile > lim_min) {  // wave-uniform
-        const int jl = jb + 2 * (int)(lane_fresh() >> 5);  // recomputed: not held across the loop
+      if (jb + kTileKeys > lim_min) {  // wave-uniform
+        const int jl = jb + kRpg * (int)(lane_fresh() >> 5);  // recomputed: not held across the loop
+        static_for<kSB>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          if (jl + key_of(q) >= lim) sc[q] = -INFINITY;
-        }
+          for (int q = 0; q < 16; ++q) {
+            if (jl + key_of<D>(q, i) >= lim) sc[i][q] = -INFINITY;
+          }
+        });
       }
     } else {
+      static_for<kSB>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int j = jb + key_of(q) + 2 * hf;
-        sc[q] = j < lim ? sc[q] * p.scale_log2 + mask_term<DT, MK>(p.mask, mrow, j) : -INFINITY;
-      }
+        for (int q = 0; q < 16; ++q) {
+          const int j = jb + key_of<D>(q, i) + kRpg * hf;
+          sc[i][q] = j < lim ? sc[i][q] * p.scale_log2 + mask_term<DT, MK>(p.mask, mrow, j) : -INFINITY;
+        }
+      });
     }
   };
 
   // The same with the tile's mask window in LDS (the stage of K/V stage address sb): the words
   // of keys q and q + 8 are adjacent, one read each.
-  auto mask_lds_apply = [&](f32x16& sc, int jb, int lim, uint32_t sb) {
+  auto mask_lds_apply = [&](f32x16(&sc)[kSB], int jb, int lim, uint32_t sb) {
     if constexpr (ML != 0) {
       const int rho = min(max(r0 - r_lo, 0), kMaskRows - 1);
       const uint32_t mst = lds0 + kFwdLdsBytes + ((sb - lds0) / kStageLds) * kMaskStageLds;
-      auto apply = [&](int q, uint32_t w) {
-        const int j = jb + key_of(q) + 2 * hf;
-        sc[q] = j < lim ? sc[q] * p.scale_log2 + mask_term_of<DT, MK>(w) : -INFINITY;
-      };
-      if constexpr (ML == 2) {
-        const uint32_t row = mst + (rho >> 1) * kWordPitch + (rho & 1) * 128 + 2 * hf * 4;
+      static_for<kSB>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        auto apply = [&](int q, uint32_t w) {
+          const int j = jb + key_of<D>(q, i) + kRpg * hf;
+          sc[i][q] = j < lim ? sc[i][q] * p.scale_log2 + mask_term_of<DT, MK>(w) : -INFINITY;
+        };
+        if constexpr (ML == 2) {
+          const uint32_t row = mst + word_row(rho) + kRpg * hf * 4;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const u32x2 x =
-              *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>((uintptr_t)(row + key_of(q) * 4));
-          apply(q, x[0]);
-          apply(q + 8, x[1]);
-        }
-      } else {
-        const lds_u8* row = reinterpret_cast<const lds_u8*>((uintptr_t)(mst + rho * kMaskRowBytes + 2 * hf * kMaskEsz));
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const lds_u8* at = row + key_of(q) * kMaskEsz;
-          if constexpr (MK == 1) {
-            const uint16_t x = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(at);
-            apply(q, x & 0xffu);
-            apply(q + 8, x >> 8);
-          } else if constexpr (MK == 2) {
-            const uint32_t x = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(at);
-            apply(q, x & 0xffffu);
-            apply(q + 8, x >> 16);
-          } else {
-            const u32x2 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(at);
+          for (int q = 0; q < 8; ++q) {
+            const u32x2 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+                (uintptr_t)(row + key_of<D>(q, i) * 4));
             apply(q, x[0]);
             apply(q + 8, x[1]);
           }
+        } else {
+          const lds_u8* row =
+              reinterpret_cast<const lds_u8*>((uintptr_t)(mst + rho * kMaskRowBytes + kRpg * hf * kMaskEsz));
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const lds_u8* at = row + key_of<D>(q, i) * kMaskEsz;
+            if constexpr (MK == 1) {
+              const uint16_t x = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(at);
+              apply(q, x & 0xffu);
+              apply(q + 8, x >> 8);
+            } else if constexpr (MK == 2) {
+              const uint32_t x = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(at);
+              apply(q, x & 0xffffu);
+              apply(q + 8, x >> 16);
+            } else {
+              const u32x2 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(at);
+              apply(q, x[0]);
+              apply(q + 8, x[1]);
+            }
+          }
         }
-      }
+      });
     }
   };
-  auto mask_any = [&](f32x16& sc, int jb, int lim, int64_t mrow, uint32_t sb) {
+  auto mask_any = [&](f32x16(&sc)[kSB], int jb, int lim, int64_t mrow, uint32_t sb) {
     if constexpr (ML != 0) mask_lds_apply(sc, jb, lim, sb);
     else mask_scores(sc, jb, lim, mrow);
   };
@@ -792,11 +852,16 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // sees such a max are the two halves exchanged, so the common case stays off the LDS pipe.
   // The decision per pair is the same as with the exchange every time.  Returns the factor
   // alpha for l and o (1 when m stays) and whether any pair of the wavefront moved.
-  auto stats = [&](const f32x16& sc, float& m_run, float& alpha) {
-    float mr = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+  auto stats = [&](const f32x16(&sc)[kSB], float& m_run, float& alpha) {
+    float mr = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
 #pragma unroll
-    for (int q = 3; q < 15; q += 2) mr = fmaxf(fmaxf(mr, sc[q]), sc[q + 1]);
-    mr = fmaxf(mr, sc[15]);
+    for (int q = 3; q < 15; q += 2) mr = fmaxf(fmaxf(mr, sc[0][q]), sc[0][q + 1]);
+    mr = fmaxf(mr, sc[0][15]);
+#pragma unroll
+    for (int i = 1; i < kSB; ++i) {
+#pragma unroll
+      for (int q = 0; q < 16; q += 2) mr = fmaxf(fmaxf(mr, sc[i][q]), sc[i][q + 1]);
+    }
     const float scale = MK == 0 ? p.scale_log2 : 1.0f;
     alpha = 1.0f;
     if (__builtin_amdgcn_ballot_w64(mr * scale > m_run + kRescaleSlack)) {
@@ -811,65 +876,79 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   };
 
   // exp part: the tile's weights exp2(s - m), rounded once to 16 bits and packed as the B
-  // operand of P.V; l_run = alpha l_run + the sum of the rounded weights
-  auto weights = [&](const f32x16& sc, float m_run, float alpha, float& l_run, u32x4& pb0, u32x4& pb1) {
+  // operands of P.V (S block i: pb0[i] for its first 16 keys, pb1[i] for the other 16);
+  // l_run = alpha l_run + the sum of the rounded weights
+  auto weights = [&](const f32x16(&sc)[kSB], float m_run, float alpha, float& l_run, u32x4(&pb0)[kSB],
+                     u32x4(&pb1)[kSB]) {
     const float scale = MK == 0 ? p.scale_log2 : 1.0f;
     const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
-    uint32_t pw[8];
     float lsum = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * q], scale, neg_m)),
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * q + 1], scale, neg_m)));
-      lsum = sum2<DT>(pw[q], lsum);
+    for (int i = 0; i < kSB; ++i) {
+      uint32_t pw[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        pw[q] = pack2<DT>(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[i][2 * q], scale, neg_m)),
+                          __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i][2 * q + 1], scale, neg_m)));
+        lsum = sum2<DT>(pw[q], lsum);
+      }
+      pb0[i] = (u32x4){pw[0], pw[1], pw[2], pw[3]};
+      pb1[i] = (u32x4){pw[4], pw[5], pw[6], pw[7]};
     }
     l_run = l_run * alpha + lsum;
-    pb0 = (u32x4){pw[0], pw[1], pw[2], pw[3]};
-    pb1 = (u32x4){pw[4], pw[5], pw[6], pw[7]};
     // keep this work in the phase it is written in (beside the P.V issued just before),
     // instead of letting it sink next to its use
-    asm volatile("" : "+v"(pb0), "+v"(pb1), "+v"(l_run));
+    if constexpr (kSB == 1) {
+      asm volatile("" : "+v"(pb0[0]), "+v"(pb1[0]), "+v"(l_run));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSB; ++i) asm volatile("" : "+v"(pb0[i]), "+v"(pb1[i]));
+      asm volatile("" : "+v"(l_run));
+    }
   };
 
   // o *= alpha when some pair's max moved (issued before the P.V product that follows it)
-  auto rescale = [&](f32x16(&o)[8], float alpha, bool moved) {
+  auto rescale = [&](f32x16(&o)[kDB], float alpha, bool moved) {
     if (moved) {
       acc_settle(o);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < kDB; ++db) {
         o[db] *= alpha;
-        if (db < 7) acc_step(o[db], o[db + 1]);
+        if (db < kDB - 1) acc_step(o[db], o[db + 1]);
       }
       acc_settle(o);
     }
   };
 
-  // ---- O^T += V^T P^T over the 8 dim blocks of the tile at sb; the V operands of block
-  // db + 1 are read while the two MFMAs of block db run
-  auto pv = [&](uint32_t sb, const u32x4& pb0, const u32x4& pb1, f32x16(&o)[8]) {
+  // ---- O^T += V^T P^T over the tile at sb in 8 steps (dim block s / kSB, S block s % kSB);
+  // the V operands of step s + 1 are read while the two MFMAs of step s run
+  auto pv = [&](uint32_t sb, const u32x4(&pb0)[kSB], const u32x4(&pb1)[kSB], f32x16(&o)[kDB]) {
     const uint32_t va = sb + v_lane_of(lane_fresh());
     u32x4 va4[2][2];
-    auto read_v = [&](auto dbc, u32x4(&dst)[2]) {
-      constexpr int db = decltype(dbc)::value;
-      // MFMA m covers rows 16 m .. 16 m + 15 (+512: odd keys); its k-slots 4 a + t take rows
-      // 8 a + 4 h + t (+2 kGroupStride for a = 1)
-      constexpr int o00 = 64 * db, o10 = o00 + 2 * kGroupStride, o01 = o00 + 512, o11 = o10 + 512;
+    auto read_v = [&](auto sc_, u32x4(&dst)[2]) {
+      constexpr int st = decltype(sc_)::value;
+      constexpr int db = st / kSB, sbk = st % kSB;
+      // MFMA m of S block sbk covers its rows 16 m .. 16 m + 15 (row 2 sbk + m of each group);
+      // its k-slots 4 a + t take rows 8 a + 4 h + t (+2 kGroupStride for a = 1)
+      constexpr int o00 = 64 * db + 2 * sbk * kRowBytes, o10 = o00 + 2 * kGroupStride;
+      constexpr int o01 = o00 + kRowBytes, o11 = o10 + kRowBytes;
       const u32x2 w00 = ds_read_tr16<o00>(va), w10 = ds_read_tr16<o10>(va);
       const u32x2 w01 = ds_read_tr16<o01>(va), w11 = ds_read_tr16<o11>(va);
       dst[0] = (u32x4){w00[0], w00[1], w10[0], w10[1]};
       dst[1] = (u32x4){w01[0], w01[1], w11[0], w11[1]};
     };
     read_v(std::integral_constant<int, 0>{}, va4[0]);
-    static_for<8>([&](auto dbc) {
-      constexpr int db = decltype(dbc)::value;
-      if constexpr (db < 7) {
-        read_v(std::integral_constant<int, db + 1>{}, va4[(db + 1) & 1]);
-        lgkm_wait<4>(va4[db & 1][0], va4[db & 1][1]);
+    static_for<8>([&](auto sc_) {
+      constexpr int st = decltype(sc_)::value;
+      constexpr int db = st / kSB, sbk = st % kSB;
+      if constexpr (st < 7) {
+        read_v(std::integral_constant<int, st + 1>{}, va4[(st + 1) & 1]);
+        lgkm_wait<4>(va4[st & 1][0], va4[st & 1][1]);
       } else {
-        lgkm_wait<0>(va4[db & 1][0], va4[db & 1][1]);
+        lgkm_wait<0>(va4[st & 1][0], va4[st & 1][1]);
       }
-      o[db] = mfma32<DT>(va4[db & 1][0], pb0, o[db]);
-      o[db] = mfma32<DT>(va4[db & 1][1], pb1, o[db]);
+      o[db] = mfma32<DT>(va4[st & 1][0], pb0[sbk], o[db]);
+      o[db] = mfma32<DT>(va4[st & 1][1], pb1[sbk], o[db]);
       asm volatile("" : "+a"(o[db]));
     });
   };
@@ -882,10 +961,11 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   if constexpr (!LAG) {
     for (int t = 0; t < n_kt; ++t) {
       const uint32_t sb = stream_step(t);
-      const int jb = kv_lo + t * kKeysPerTile;
-      u32x4 pa0, pa1;
+      const int jb = kv_lo + t * kTileKeys;
+      u32x4 pa0[kSB], pa1[kSB];
       float a0;
-      f32x16 s0 = scores(sb, q0, no_hook);
+      f32x16 s0[kSB];
+      scores(sb, q0, no_hook, s0);
       mask_any(s0, jb, lim0, mrow0, sb);
       const bool f0 = stats(s0, m0, a0);
       rescale(o0, a0, f0);
@@ -893,20 +973,21 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       pv(sb, pa0, pa1, o0);
     }
   } else if (n_kt > 0) {
-    u32x4 pa0, pa1;
+    u32x4 pa0[kSB], pa1[kSB];
     float a0;
     bool f0;
     uint32_t sb = sync_step(0);
-    f32x16 s0 = scores(sb, q0, dma_hook);
+    f32x16 s0[kSB];
+    scores(sb, q0, dma_hook, s0);
     mask_any(s0, kv_lo, lim0, mrow0, sb);
     f0 = stats(s0, m0, a0);
     weights(s0, m0, a0, l0, pa0, pa1);
     uint32_t sprev = sb;
     for (int t = 1; t < n_kt; ++t) {
       sb = sync_step(t);
-      const int jb = kv_lo + t * kKeysPerTile;
+      const int jb = kv_lo + t * kTileKeys;
       __builtin_amdgcn_sched_barrier(0);
-      s0 = scores(sb, q0, dma_hook);
+      scores(sb, q0, dma_hook, s0);
       mask_any(s0, jb, lim0, mrow0, sb);
       // o still owes tile t - 1's alpha: keep it until its P.V is issued
       const float a_prev = a0;
@@ -928,7 +1009,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   const float lt0 = sum_halves(l0);
   // returns whether a NaN came out of o / l (one split only: the nonfinite repair below then
   // redoes the pair; split partials are checked and redone by the merge)
-  auto finish = [&](bool valid, int h, int r, float l_tot, float m_run, f32x16(&o)[8]) {
+  auto finish = [&](bool valid, int h, int r, float l_tot, float m_run, f32x16(&o)[kDB]) {
     bool nan_seen = false;
     if (!valid) return nan_seen;
     const float inv = l_tot > 0.0f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
@@ -936,7 +1017,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
       uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < kDB; ++db) {
         if (db > 0) acc_step(o[db - 1], o[db]);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -955,9 +1036,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       }
     } else {
       const int64_t row_id = (((int64_t)split * p.B + b) * p.Hq + h) * p.rows + r;
-      float* prow = p.part_o + row_id * kHeadDim;
+      float* prow = p.part_o + row_id * D;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < kDB; ++db) {
         if (db > 0) acc_step(o[db - 1], o[db]);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -989,7 +1070,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     if constexpr (!SPLIT) {
       const uint64_t bm = __builtin_amdgcn_ballot_w64(nan_seen);
       if (bm != 0 && valid && (((bm >> li) | (bm >> (li + 32))) & 1u) != 0) {
-        exact_pair<DT, MK>(p, b, h, r, hf, kv_lo, min(kv_end, lim), mrow, kbase, vbase);
+        exact_pair<D, DT, MK>(p, b, h, r, hf, kv_lo, min(kv_end, lim), mrow, kbase, vbase);
       }
     }
   };
@@ -998,59 +1079,65 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 }
 
 // shape 0: four wavefronts; 2: eight with the lagged P.V; 3: eight without it.  ml: the mask
-// layout in LDS (0: none, per-lane loads; 1: 16-byte rows, shape 2 only; 2: words).
-template <int DT, int MK, bool SPLIT>
+// layout in LDS (0: none, per-lane loads; 1: 16-byte rows, shape 2 at head dim 256 only; 2: words).
+template <int D, int DT, int MK, bool SPLIT>
 hipError_t launch_fwd_s(const FwdParams& p, int shape, hipStream_t stream) {
   const dim3 grid(p.grid), b4(256), b8(512);
   const int ml = MK != 0 ? p.mask_lds : 0;
   if constexpr (MK != 0) {
     if (ml == 2) {
-      if (shape == 0) hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, false, 2, SPLIT>), grid, b4, 0, stream, p);
-      else if (shape == 2) hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, true, 2, SPLIT>), grid, b8, 0, stream, p);
-      else hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, false, 2, SPLIT>), grid, b8, 0, stream, p);
+      if (shape == 0) hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MK, 4, false, 2, SPLIT>), grid, b4, 0, stream, p);
+      else if (shape == 2) hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MK, 8, true, 2, SPLIT>), grid, b8, 0, stream, p);
+      else hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MK, 8, false, 2, SPLIT>), grid, b8, 0, stream, p);
       return hipGetLastError();
     }
     if (ml == 1) {
-      if (shape != 2) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, true, 1, SPLIT>), grid, b8, 0, stream, p);
-      return hipGetLastError();
+      if constexpr (D != 256) {
+        return hipErrorInvalidValue;
+      } else {
+        if (shape != 2) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MK, 8, true, 1, SPLIT>), grid, b8, 0, stream, p);
+        return hipGetLastError();
+      }
     }
   }
-  if (shape == 0) hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 4, false, 0, SPLIT>), grid, b4, 0, stream, p);
-  else if (shape == 2) hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, true, 0, SPLIT>), grid, b8, 0, stream, p);
-  else hipLaunchKernelGGL((attn_fwd_kernel<DT, MK, 8, false, 0, SPLIT>), grid, b8, 0, stream, p);
+  if (shape == 0) hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MK, 4, false, 0, SPLIT>), grid, b4, 0, stream, p);
+  else if (shape == 2) hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MK, 8, true, 0, SPLIT>), grid, b8, 0, stream, p);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MK, 8, false, 0, SPLIT>), grid, b8, 0, stream, p);
   return hipGetLastError();
 }
 
 // the split flag is a compile-time choice: the epilogue writes either the gated output or the
 // split partials, and only the former carries the in-kernel nonfinite repair
-template <int DT, int MK>
+template <int D, int DT, int MK>
 hipError_t launch_fwd_t(const FwdParams& p, int shape, hipStream_t stream) {
-  return p.n_splits > 1 ? launch_fwd_s<DT, MK, true>(p, shape, stream) : launch_fwd_s<DT, MK, false>(p, shape, stream);
+  return p.n_splits > 1 ? launch_fwd_s<D, DT, MK, true>(p, shape, stream)
+                        : launch_fwd_s<D, DT, MK, false>(p, shape, stream);
 }
 
-}  // namespace
-
-hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream) {
+// every variant of head dim D (the planted-mistake builds: head dim 256 in bf16 without a mask)
+template <int D>
+hipError_t launch_fwd_d(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream) {
 #if GQA_CONTROL
-  if (dtype != 0 || mask_kind != 0) return hipErrorInvalidValue;  // planted-mistake build: bf16, no mask
-  return launch_fwd_t<0, 0>(p, shape, stream);
+  if (D != 256 || dtype != 0 || mask_kind != 0) return hipErrorInvalidValue;
+  return launch_fwd_t<256, 0, 0>(p, shape, stream);
 #else
   if (dtype == 0) {
     switch (mask_kind) {
-      case 0: return launch_fwd_t<0, 0>(p, shape, stream);
-      case 1: return launch_fwd_t<0, 1>(p, shape, stream);
-      case 2: return launch_fwd_t<0, 2>(p, shape, stream);
-      default: return launch_fwd_t<0, 3>(p, shape, stream);
+      case 0: return launch_fwd_t<D, 0, 0>(p, shape, stream);
+      case 1: return launch_fwd_t<D, 0, 1>(p, shape, stream);
+      case 2: return launch_fwd_t<D, 0, 2>(p, shape, stream);
+      default: return launch_fwd_t<D, 0, 3>(p, shape, stream);
     }
   }
   switch (mask_kind) {
-    case 0: return launch_fwd_t<1, 0>(p, shape, stream);
-    case 1: return launch_fwd_t<1, 1>(p, shape, stream);
-    case 2: return launch_fwd_t<1, 2>(p, shape, stream);
-    default: return launch_fwd_t<1, 3>(p, shape, stream);
+    case 0: return launch_fwd_t<D, 1, 0>(p, shape, stream);
+    case 1: return launch_fwd_t<D, 1, 1>(p, shape, stream);
+    case 2: return launch_fwd_t<D, 1, 2>(p, shape, stream);
+    default: return launch_fwd_t<D, 1, 3>(p, shape, stream);
   }
 #endif
 }
 
+}  // namespace
 }  // namespace gqa

@@ -17,7 +17,9 @@
 namespace gqa {
 
 constexpr int kHeadDim = 256;
-constexpr int kKeysPerTile = 32;     // keys staged in LDS per step
+constexpr int kKeysPerTile = 32;     // keys staged in LDS per step at head dim 256
+// keys per tile of the main pass at head dim D: a K (or V) tile is 16 KiB whatever D
+constexpr int tile_keys(int D) { return 8192 / D; }
 constexpr int kBlocksPerGroup = 8;   // 32-pair column blocks of the largest workgroup
 constexpr int kPairsPerBlock = 32;   // (head, row) pairs per column block (the MFMA N dimension)
 constexpr int kTileBytes = kKeysPerTile * kHeadDim * 2;      // one K (or V) tile: 16 KiB of data
@@ -39,7 +41,7 @@ struct FwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const void* mask;
-  float* part_o;    // [n_splits, B, Hq, rows, 256] when n_splits > 1
+  float* part_o;    // [n_splits, B, Hq, rows, D] when n_splits > 1
   float* part_lse;  // [n_splits, B, Hq, rows]
   int64_t q_sb, q_sh, q_sr;
   int64_t g_sb, g_sh, g_sr;
@@ -86,7 +88,7 @@ struct MergeParams {
   int64_t g_sb, g_sh, g_sr;
   int64_t o_sb, o_sh, o_sr;
   int n_chunks, B, Hq, rows;
-  int D;  // head dim: 256, 128 or 64 (the partials' row length); the repair is for 256 only
+  int D;  // head dim: 256, 128 or 64 (the partials' row length)
   RepairParams fix;
 };
 
@@ -131,27 +133,6 @@ struct ComposedParams {
   float scale_log2;
 };
 
-// Parameters of the fused pass for head dims 64 and 128 (attn_small_d.hip): no mask, no split.
-struct SmallDParams {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const uint16_t* gate;
-  uint16_t* out;
-  int64_t q_sb, q_sh, q_sr;
-  int64_t k_sb, k_sh, k_st;
-  int64_t v_sb, v_sh, v_st;
-  int64_t g_sb, g_sh, g_sr;
-  int64_t o_sb, o_sh, o_sr;
-  int D, B, Hq, G, rows, kv_offset, kv_len, causal;
-  float scale_log2;
-  int hw;              // heads (wavefronts) per workgroup: 2, or 1 when G is odd
-  int n_splits;        // KV splits (1: the output is written; else the partials below)
-  int keys_per_split;  // multiple of 32
-  float* part_o;       // [n_splits, B, Hq, rows, D] when n_splits > 1
-  float* part_lse;     // [n_splits, B, Hq, rows]
-};
-
 // Merge launch shape, shared by the launcher and the host's checks: chunk counts up to
 // kFewChunks take one wavefront per row (four rows a workgroup); more take a workgroup of
 // merge_waves(n) wavefronts per row.
@@ -168,13 +149,20 @@ inline bool merge_fits(int n_chunks, int64_t n_rows) {
 
 // Launchers (return hipGetLastError()).  dtype 0 = bf16, 1 = fp16; mask_kind as attn_mask_kind.
 // shape: 0 = 4 wavefronts, 2 = 8 wavefronts with the P.V product one tile behind (prompts),
-// 3 = 8 wavefronts without that lag (decode / verify); each wavefront one 32-pair column block
-hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream);
+// 3 = 8 wavefronts without that lag (decode / verify); each wavefront one 32-pair column block.
+// The main pass per head dim (attn_fwd_d256.hip, attn_fwd_d128.hip, attn_fwd_d64.hip).
+hipError_t launch_fwd_256(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream);
+hipError_t launch_fwd_128(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream);
+hipError_t launch_fwd_64(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t stream);
+inline hipError_t launch_fwd(const FwdParams& p, int D, int dtype, int mask_kind, int shape, hipStream_t stream) {
+  return D == 256 ? launch_fwd_256(p, dtype, mask_kind, shape, stream)
+                  : D == 128 ? launch_fwd_128(p, dtype, mask_kind, shape, stream)
+                             : launch_fwd_64(p, dtype, mask_kind, shape, stream);
+}
 hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_keep(const KeepParams& p, int B, hipStream_t stream);
 hipError_t launch_composed(const ComposedParams& p, int dtype, hipStream_t stream);
-hipError_t launch_small_d(const SmallDParams& p, int dtype, hipStream_t stream);
 // Device address of the library's scratch array on the current device (looked up on the first
 // call per device and kept; attn_noalloc.hip).
 hipError_t scratch_of_current_device(void** ptr);

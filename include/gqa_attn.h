@@ -1,5 +1,6 @@
 /*
- * gqa_attn.h -- C ABI of the gated causal GQA attention library (head_dim 256, gfx950).
+ * gqa_attn.h -- C ABI of the gated causal GQA attention library (head_dim 256, also 128 and
+ * 64; gfx950).
  *
  * The operation (TensorFold PR #1009, attention kernel-contract commit and
  * Receipt "Attention"; "Qwen head-chunked SDPA (#113)", introduction):
@@ -105,7 +106,7 @@ typedef struct {
   int32_t B;           /* batch */
   int32_t Hq;          /* query heads */
   int32_t Hkv;         /* KV heads; Hq / Hkv = GQA group size G */
-  int32_t D;           /* head_dim, must be 256 */
+  int32_t D;           /* head_dim: 256, 128 or 64 (else ATTN_E_HEAD_DIM) */
   int32_t rows;        /* query rows in this call (a query block, or 1..32 decode/verify rows) */
   int64_t kv_offset;   /* cached keys before row 0 = absolute position of row 0 */
   int64_t kv_len;      /* valid keys in the cache (normally kv_offset + rows, after kv_append) */
@@ -226,7 +227,8 @@ int attn_workspace_bytes(const attn_args* a, int op, size_t* bytes);
 int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info);
 
 /* Gated causal GQA attention for a block of query rows (any rows >= 1): the flash-style
- * pass over the cache in 32-key tiles, split over KV when the grid would be too small, the
+ * pass over the cache in 16 KiB K/V tiles (8192 / head_dim keys: 32 at 256, 64 at 128, 128 at
+ * 64), split over KV when the grid would be too small, the
  * log-sum-exp merge of the splits and the gate.  `workspace` (device, >= the bytes
  * attn_workspace_bytes(a, ATTN_OP_PREFILL) reports; may be NULL if that is 0) holds the
  * split partials.  Writes a->out.  Keys a row cannot see never reach it, also when their
@@ -234,11 +236,9 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info);
  * not become NaN): a pair whose result came out NaN is computed again over its admissible
  * keys, in the epilogue (one split) or in the merge (several). */
 int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
-/* Head dims 64 and 128 (attn_prefill, attn_decode, attn_prefill_partials) run a plainer fused
- * pass of their own: one wavefront per 32 rows of a head, split over KV when those are fewer
- * than the chip holds (the workspace then holds the partials, rows of head_dim, and the merge
- * follows), one head chunk, no mask (ATTN_E_MASK), scale = 0 means 1 / sqrt(head_dim),
- * inputs taken to be finite (no repair). */
+/* Head dims 128 and 64 (attn_prefill, attn_decode, attn_prefill_partials and
+ * attn_decode_noalloc) take the same main pass, plans, head chunks, masks and nonfinite repair
+ * as 256; the partials hold rows of head_dim floats, and scale = 0 means 1 / sqrt(head_dim). */
 
 /* The main pass of attn_prefill alone, for callers that overlap one query block's merge with
  * the next block's main pass (two workspaces, the merges on a second stream).  *n_chunks

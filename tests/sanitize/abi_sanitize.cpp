@@ -27,7 +27,6 @@ long g_checks = 0;
 long g_launch_fwd = 0, g_launch_merge = 0, g_launch_other = 0;
 gqa::FwdParams g_fwd;
 gqa::MergeParams g_merge;
-gqa::SmallDParams g_small;
 int g_fwd_shape = -1;
 
 #define CHECK(cond, ...)                                       \
@@ -79,7 +78,7 @@ char* const kWs = kDev + (uintptr_t(6) << 36);
 // ---- stub launchers: record and check, never touch memory
 namespace gqa {
 
-hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t) {
+hipError_t launch_fwd_any(const FwdParams& p, int dtype, int mask_kind, int shape) {
   ++g_launch_fwd;
   g_fwd = p;
   g_fwd_shape = shape;
@@ -89,10 +88,20 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int mask_kind, int shape, h
   CHECK(p.mask_lds >= 0 && p.mask_lds <= 2 && (p.mask_lds != 1 || shape == 2) && (mask_kind != 0 || p.mask_lds == 0),
         "mask layout %d on shape %d", p.mask_lds, shape);
   CHECK(p.grid == (int64_t)p.B * p.Hkv * p.n_splits * p.n_tiles, "grid %d", p.grid);
-  CHECK(p.keys_per_split % kKeysPerTile == 0, "keys_per_split %d", p.keys_per_split);
+  CHECK(p.keys_per_split % 32 == 0, "keys_per_split %d", p.keys_per_split);
   CHECK((p.n_splits > 1) == (p.part_o != nullptr), "partials %d", p.n_splits);
   CHECK(p.G * p.Hkv == p.Hq && p.chunk >= 1 && p.chunk <= p.G, "chunk %d", p.chunk);
   return hipSuccess;
+}
+
+hipError_t launch_fwd_256(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t) {
+  return launch_fwd_any(p, dtype, mask_kind, shape);
+}
+hipError_t launch_fwd_128(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t) {
+  return launch_fwd_any(p, dtype, mask_kind, shape);
+}
+hipError_t launch_fwd_64(const FwdParams& p, int dtype, int mask_kind, int shape, hipStream_t) {
+  return launch_fwd_any(p, dtype, mask_kind, shape);
 }
 
 hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t) {
@@ -128,14 +137,6 @@ hipError_t scratch_of_current_device(void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_small_d(const SmallDParams& p, int, hipStream_t) {
-  ++g_launch_other;
-  g_small = p;
-  CHECK(p.D == 64 || p.D == 128, "D %d", p.D);
-  CHECK((int64_t)p.B * p.n_splits <= 65535, "grid z");
-  CHECK((p.n_splits > 1) == (p.part_o != nullptr), "partials %d", p.n_splits);
-  return hipSuccess;
-}
 
 }  // namespace gqa
 
@@ -242,14 +243,13 @@ void launch_limits() {
   // fewer splits fit (one wavefront per row for <= 8 chunks)
   a.n_splits = 8;
   CHECK(attn_workspace_bytes(&a, ATTN_OP_DECODE, &bytes) == ATTN_OK, "8 splits fit");
-  // head dims 64/128: B x splits past grid z
-  auto s = args(40000, 2, 2, 1, 4096, 64);
-  s.n_splits = 2;
-  CHECK(attn_workspace_bytes(&s, ATTN_OP_PREFILL, &bytes) == ATTN_E_ARG, "small-D grid z: workspace");
-  CHECK(attn_describe_plan(&s, ATTN_OP_PREFILL, &info) == ATTN_E_ARG, "small-D grid z: describe");
-  CHECK(attn_prefill(&s, kWs, SIZE_MAX / 2, kStream) == ATTN_E_ARG, "small-D grid z: run");
-  s.n_splits = 1;
-  CHECK(attn_workspace_bytes(&s, ATTN_OP_PREFILL, &bytes) == ATTN_OK, "small-D one split fits");
+  // head dim 64 (128-key tiles): the same merge limit
+  auto s64 = args(4096, 32, 1, 32, 8192, 64);
+  s64.n_splits = 40;
+  CHECK(attn_workspace_bytes(&s64, ATTN_OP_DECODE, &bytes) == ATTN_E_ARG, "head dim 64 merge too large: workspace");
+  CHECK(attn_decode(&s64, kWs, SIZE_MAX / 2, kStream) == ATTN_E_ARG, "head dim 64 merge too large: run");
+  s64.n_splits = 8;
+  CHECK(attn_workspace_bytes(&s64, ATTN_OP_DECODE, &bytes) == ATTN_OK, "head dim 64, 8 splits fit");
   // the merge called on its own
   merge_args m;
   memset(&m, 0, sizeof(m));
@@ -294,24 +294,21 @@ void sweep() {
                                                     : attn_decode(&a, kWs, bytes, kStream);
                 CHECK(r == ATTN_OK, "run %d", r);
                 const bool split = info.n_splits > 1;
-                if (D == 256) {
-                  CHECK(g_launch_fwd == f0 + 1 && g_launch_merge == m0 + (split ? 1 : 0), "launch count");
-                  CHECK(g_fwd.grid == info.grid_blocks && g_fwd.n_splits == info.n_splits &&
-                            g_fwd.keys_per_split == info.keys_per_split && g_fwd.n_tiles == info.n_row_tiles,
-                        "launched plan differs from the described one");
-                  CHECK((g_fwd_shape == 0 ? 4 : 8) == info.waves_per_block, "shape");
-                  CHECK(g_fwd_shape != 3 || op == ATTN_OP_DECODE, "the streaming shape is for decode rows");
-                  if (split) {
-                    const char* lse = reinterpret_cast<const char*>(g_fwd.part_lse);
-                    CHECK(reinterpret_cast<const char*>(g_fwd.part_o) == kWs && lse > kWs &&
-                              lse + 4 * (size_t)info.n_splits * B * hh[0] * rows <= kWs + bytes,
-                          "partials outside the workspace");
-                    CHECK(g_merge.n_chunks == info.n_splits, "merge chunks");
-                  }
-                } else {
-                  CHECK(g_launch_other == o0 + 1 && g_launch_merge == m0 + (split ? 1 : 0), "small-D launches");
-                  CHECK(g_small.n_splits == info.n_splits && g_small.keys_per_split == info.keys_per_split,
-                        "small-D plan differs");
+                CHECK(g_launch_fwd == f0 + 1 && g_launch_merge == m0 + (split ? 1 : 0) && g_launch_other == o0,
+                      "launch count");
+                CHECK(g_fwd.grid == info.grid_blocks && g_fwd.n_splits == info.n_splits &&
+                          g_fwd.keys_per_split == info.keys_per_split && g_fwd.n_tiles == info.n_row_tiles,
+                      "launched plan differs from the described one");
+                CHECK(g_fwd.keys_per_split % info.keys_per_tile == 0 && info.keys_per_tile == 8192 / D,
+                      "tile keys %d at head dim %d", info.keys_per_tile, D);
+                CHECK((g_fwd_shape == 0 ? 4 : 8) == info.waves_per_block, "shape");
+                CHECK(g_fwd_shape != 3 || op == ATTN_OP_DECODE, "the streaming shape is for decode rows");
+                if (split) {
+                  const char* lse = reinterpret_cast<const char*>(g_fwd.part_lse);
+                  CHECK(reinterpret_cast<const char*>(g_fwd.part_o) == kWs && lse > kWs &&
+                            lse + 4 * (size_t)info.n_splits * B * hh[0] * rows <= kWs + bytes,
+                        "partials outside the workspace");
+                  CHECK(g_merge.n_chunks == info.n_splits && g_merge.D == D, "merge chunks / head dim");
                 }
                 if (op == ATTN_OP_PREFILL) {
                   int32_t n = 0;

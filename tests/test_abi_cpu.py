@@ -151,20 +151,24 @@ def test_rejections(name, spec, status, op):
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_other_head_dims(D):
-    # head dims 64 and 128 run on their own fused pass (no mask) and on the
-    # composed route; the append takes them; any other head dim fails closed everywhere
+    # head dims 64 and 128 run on the same main pass as 256 (16 KiB tiles of 8192 / D keys),
+    # masks included, and on the composed route; the append takes them; any other head dim fails
+    # closed everywhere
     lib = ga.lib()
     a = _good(D=D)
     n = C.c_size_t(1)
     for op in (_abi.OP_PREFILL, _abi.OP_DECODE):
         assert lib.attn_workspace_bytes(C.byref(a), op, C.byref(n)) == 0 and n.value == 0  # no split here
         info = ga.describe_plan(a, op)
-        assert info["variant_name"] == f"fwd_small_d{D}" and info["n_splits"] == 1
+        assert info["variant_name"] == f"fwd_mfma32x32x16_bf16_4x1_d{D}" and info["n_splits"] == 1
+        assert info["keys_per_tile"] == 8192 // D
     assert lib.attn_workspace_bytes(C.byref(a), _abi.OP_COMPOSED, C.byref(n)) == 0 and n.value > 0
     m = _good(D=D, mask_kind=2)
     m.mask.ptr = 1 << 20
-    for op in (_abi.OP_PREFILL, _abi.OP_DECODE, _abi.OP_COMPOSED):
-        assert lib.attn_workspace_bytes(C.byref(m), op, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_MASK"]
+    for op in (_abi.OP_PREFILL, _abi.OP_DECODE):
+        assert lib.attn_workspace_bytes(C.byref(m), op, C.byref(n)) == 0
+        assert ga.describe_plan(m, op)["variant_name"] == f"fwd_mfma32x32x16_bf16_maskadd_4x1_ldswords_d{D}"
+    assert lib.attn_workspace_bytes(C.byref(m), _abi.OP_COMPOSED, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_MASK"]
     odd = _good(D=96)
     for op in (_abi.OP_PREFILL, _abi.OP_DECODE, _abi.OP_COMPOSED):
         assert lib.attn_workspace_bytes(C.byref(odd), op, C.byref(n)) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
@@ -175,39 +179,34 @@ def test_other_head_dims(D):
     assert lib.kv_append(C.byref(ap), None) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_small_head_dim_splits(D):
-    # the fused pass for head dims 64 and 128 splits the keys when its wavefronts (32 rows of
-    # one head each, two heads of a group to a workgroup, one if G is odd) number fewer than 2048, at least 8 tiles of 32 keys per split; the
-    # workspace holds fp32 partials of D per (split, b, h, row) and an lse per row, each part
-    # rounded up to 256 bytes
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_tile_keys_per_head_dim(D):
+    # the main pass moves 16 KiB K and V tiles at every head dim: 8192 / D keys a tile; splits
+    # are whole tiles, the workspace holds fp32 partials of D per (split, b, h, row) and an lse per
+    # row, each part rounded up to 256 bytes
     lib = ga.lib()
+    T = 8192 // D
     r256 = lambda x: (x + 255) // 256 * 256
-    cases = [  # (B, Hq, Hkv, rows, kv_offset, n_splits asked, splits expected, keys per split)
-        (2, 16, 2, 1, 32767, 0, 64, 512),      # one decode row at 32k: 32 workgroups before splitting
-        (1, 24, 4, 512, 32256, 0, 5, 6560),    # the last 512-row block of a 32k prompt
-        (1, 24, 4, 4, 100, 0, 1, 128),         # too few keys to split
-        (1, 24, 4, 512, 0, 0, 2, 256),         # the first block: 16 tiles, 5 splits wanted, 2 at most
-        (1, 8, 2, 33, 1000, 3, 3, 352),        # asked for 3
-    ]
-    for B, Hq, Hkv, rows, off, asked, S, kps in cases:
-        a = _good(D=D, B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off, n_splits=asked)
-        info = ga.describe_plan(a, _abi.OP_PREFILL)
-        assert (info["n_splits"], info["keys_per_split"]) == (S, kps), (B, Hq, rows, off, info)
-        nrow = S * B * Hq * rows
-        want = 0 if S == 1 else r256(nrow * D * 4) + r256(nrow * 4)
-        assert ga.workspace_bytes(a, _abi.OP_PREFILL) == want and info["workspace_bytes"] == want
-        G = Hq // Hkv
-        hw = 2 if G % 2 == 0 else 1  # heads per workgroup
-        assert info["waves_per_block"] == hw
-        assert info["lds_bytes"] == {64: 10752, 128: 17408}[D]  # K and V tiles of 32 padded rows
-        assert info["grid_blocks"] == (rows + 31) // 32 * (Hq // hw) * B * S
-        if S > 1:
-            assert lib.attn_prefill(C.byref(a), C.c_void_p(1 << 20), want - 1, None) == \
-                _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
-            assert lib.attn_prefill(C.byref(a), None, want, None) == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
-            assert lib.attn_prefill(C.byref(a), C.c_void_p((1 << 20) + 8), want, None) == \
-                _abi.STATUS_CODE["ATTN_E_LAYOUT"]
+    for B, Hq, Hkv, rows, off, asked in ((2, 16, 2, 1, 32767, 0), (1, 24, 4, 512, 32256, 0), (1, 24, 4, 4, 100, 0),
+                                         (1, 8, 2, 33, 1000, 3), (1, 16, 2, 32, 32768, 0)):
+        for op in (_abi.OP_PREFILL, _abi.OP_DECODE):
+            if op == _abi.OP_DECODE and rows > 32:
+                continue
+            a = _good(D=D, B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off, n_splits=asked)
+            info = ga.describe_plan(a, op)
+            S, kps = info["n_splits"], info["keys_per_split"]
+            assert info["keys_per_tile"] == T and kps % T == 0
+            assert S * kps >= off + rows and (S - 1) * kps < off + rows
+            if asked:
+                assert S <= asked
+            nrow = S * B * Hq * rows
+            want = 0 if S == 1 else r256(nrow * D * 4) + r256(nrow * 4)
+            assert ga.workspace_bytes(a, op) == want and info["workspace_bytes"] == want
+            if S > 1:
+                fn = lib.attn_prefill if op == _abi.OP_PREFILL else lib.attn_decode
+                assert fn(C.byref(a), C.c_void_p(1 << 20), want - 1, None) == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
+                assert fn(C.byref(a), None, want, None) == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
+                assert fn(C.byref(a), C.c_void_p((1 << 20) + 8), want, None) == _abi.STATUS_CODE["ATTN_E_LAYOUT"]
 
 
 def test_composed_workspace_and_rejections():
@@ -322,9 +321,8 @@ def test_prefill_partials_needs_its_outputs():
 
 
 def test_launch_size_limits_are_rejected_by_planning_and_run_alike():
-    # a decode whose merge would exceed a launch (4.19M rows x 16 wavefronts), and a head-dim-64
-    # plan whose grid z (batch x splits) passes 65535: the planning calls reject them as the run
-    # would, before anything is enqueued
+    # a decode whose merge would exceed a launch (4.19M rows x 16 wavefronts), at head dims 256 and
+    # 64: the planning calls reject it as the run would, before anything is enqueued
     a = ga.plan_args(B=4096, Hq=32, Hkv=1, rows=32, kv_offset=4096, n_splits=40)
     for fn in (lambda: ga.workspace_bytes(a, _abi.OP_DECODE), lambda: ga.describe_plan(a, _abi.OP_DECODE)):
         with pytest.raises(ga.AttnError) as e:
@@ -333,12 +331,12 @@ def test_launch_size_limits_are_rejected_by_planning_and_run_alike():
     assert ga.lib().attn_decode(C.byref(a), None, 0, None) == _abi.STATUS_CODE["ATTN_E_ARG"]
     a.n_splits = 8  # one wavefront a row: fits
     assert ga.workspace_bytes(a, _abi.OP_DECODE) > 0
-    s = ga.plan_args(B=40000, Hq=2, Hkv=2, rows=1, kv_offset=4096, n_splits=2, D=64)
+    s = ga.plan_args(B=4096, Hq=32, Hkv=1, rows=32, kv_offset=8192, n_splits=40, D=64)
     with pytest.raises(ga.AttnError):
-        ga.workspace_bytes(s, _abi.OP_PREFILL)
-    assert ga.lib().attn_prefill(C.byref(s), None, 0, None) == _abi.STATUS_CODE["ATTN_E_ARG"]
-    s.n_splits = 1
-    assert ga.workspace_bytes(s, _abi.OP_PREFILL) == 0
+        ga.workspace_bytes(s, _abi.OP_DECODE)
+    assert ga.lib().attn_decode(C.byref(s), None, 0, None) == _abi.STATUS_CODE["ATTN_E_ARG"]
+    s.n_splits = 8
+    assert ga.workspace_bytes(s, _abi.OP_DECODE) > 0
 
 
 def test_strerror_names_the_head_dims():

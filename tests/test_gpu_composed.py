@@ -121,28 +121,33 @@ def test_composed_other_head_dims(D, dtype):
 
 
 @needs_gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("rows,offset,causal,B", [(1, 1000, True, 1), (5, 777, True, 2), (32, 4096, True, 1),
                                                    (70, 0, False, 2)])
-def test_fused_small_head_dims(D, rows, offset, causal, B):
-    # the fused pass for head dims 64 and 128: decode / verify rows over a cache, and a
-    # non-causal block; head-chunk requests change nothing (one workgroup per 32 rows of a head)
-    _say("fused small D", D, rows, offset, causal, B)
+def test_fused_small_head_dims(D, rows, offset, causal, B, dtype):
+    # the main pass at head dims 64 and 128: decode / verify rows over a cache (the heads of a KV
+    # group stacked in one workgroup, or one head a workgroup when chunked by one: the same bits),
+    # and a non-causal block
+    _say("fused small D", D, rows, offset, causal, B, dtype)
     Hq, Hkv = 16, 2
     kv = offset + rows if causal else 150
     rng = syn.streams(5400 + D + rows)
-    qb = syn.normal_bits(rng["q"], (B, Hq, rows, D))
-    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D))
-    kb = syn.normal_bits(rng["k"], (B, Hkv, kv + 7, D))
-    vb = syn.normal_bits(rng["v"], (B, Hkv, kv + 7, D))
-    q, g, k, v = (to_dev(x) for x in (qb, gb, kb, vb))
+    qb = syn.normal_bits(rng["q"], (B, Hq, rows, D), dtype)
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D), dtype)
+    kb = syn.normal_bits(rng["k"], (B, Hkv, kv + 7, D), dtype)
+    vb = syn.normal_bits(rng["v"], (B, Hkv, kv + 7, D), dtype)
+    q, g, k, v = (to_dev(x, dtype) for x in (qb, gb, kb, vb))
     call = ga.decode if rows <= 32 else ga.prefill
     out = call(q, k, v, g, kv_offset=offset, kv_len=kv, causal=causal)
     torch.cuda.synchronize()
-    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=offset,
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=offset,
                               kv_len=kv, causal=causal)
-    _say(assert_close(to_f64(out), ref, f"fused D={D}"))
+    _say(assert_close(syn.widen(to_bits(out), dtype), ref, f"fused D={D}"))
     if rows <= 32:
+        if rows < 32:  # the policy stacks several heads of the group in a workgroup
+            a0 = ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=offset, kv_len=kv, causal=causal, D=D)
+            assert ga.describe_plan(a0, 1)["n_head_chunks"] < Hq // Hkv
         again = ga.decode(q, k, v, g, kv_offset=offset, kv_len=kv, causal=causal, head_chunk=1)
         assert torch.equal(again.view(torch.int16), out.view(torch.int16))
 
@@ -182,46 +187,49 @@ def test_fused_small_head_dims_split_keys(D, dtype):
 
 
 @needs_gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(24, 4), (6, 3), (5, 5), (16, 2)])
-def test_fused_small_head_dims_heads_per_workgroup(D, Hq, Hkv):
-    # workgroups of two heads of a KV group sharing K/V tiles (G 6, 2 and 8) and of one head
-    # (G 1); 70 causal rows at offset 1500 (ragged row tile), keys split as planned
-    _say("fused small D heads per workgroup", D, Hq, Hkv)
+def test_fused_small_head_dims_heads_per_workgroup(D, Hq, Hkv, dtype):
+    # the heads of a KV group sharing K/V tiles in one workgroup (G 6, 2 and 8) and one head
+    # alone (G 1); 70 causal rows at offset 1500 (ragged row tile), keys split as planned
+    _say("fused small D heads per workgroup", D, Hq, Hkv, dtype)
     B, rows, off = 1, 70, 1500
     kv = off + rows
     rng = syn.streams(5600 + D + Hq)
-    qb = syn.normal_bits(rng["q"], (B, Hq, rows, D))
-    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D))
-    kb = syn.normal_bits(rng["k"], (B, Hkv, kv, D))
-    vb = syn.normal_bits(rng["v"], (B, Hkv, kv, D))
-    q, g, k, v = (to_dev(x) for x in (qb, gb, kb, vb))
+    qb = syn.normal_bits(rng["q"], (B, Hq, rows, D), dtype)
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D), dtype)
+    kb = syn.normal_bits(rng["k"], (B, Hkv, kv, D), dtype)
+    vb = syn.normal_bits(rng["v"], (B, Hkv, kv, D), dtype)
+    q, g, k, v = (to_dev(x, dtype) for x in (qb, gb, kb, vb))
     out = ga.prefill(q, k, v, g, kv_offset=off)
     torch.cuda.synchronize()
-    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off, kv_len=kv)
-    _say(assert_close(to_f64(out), ref, f"fused D={D} {Hq}/{Hkv}"))
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off,
+                              kv_len=kv)
+    _say(assert_close(syn.widen(to_bits(out), dtype), ref, f"fused D={D} {Hq}/{Hkv}"))
 
 
 @needs_gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [128, 64])
-def test_fused_small_head_dims_32k_prompt_sampled(D):
+def test_fused_small_head_dims_32k_prompt_sampled(D, dtype):
     # the benchmark's launch configuration for these head dims: a 32768-token prompt at 24 query
     # heads over 4 KV heads in blocks of 512 rows (kv_append + attn_prefill, keys split as
     # planned); rows sampled across the prompt and every head against the oracle
-    _say("fused small D 32k", D)
+    _say("fused small D 32k", D, dtype)
     N, Hq, Hkv = 32768, 24, 4
     rng = syn.streams(5700 + D)
-    qb = syn.normal_bits(rng["q"], (1, Hq, N, D))
-    kb = syn.normal_bits(rng["k"], (1, Hkv, N, D))
-    vb = syn.normal_bits(rng["v"], (1, Hkv, N, D))
-    gb = syn.normal_bits(rng["gate"], (1, Hq, N, D))
-    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    qb = syn.normal_bits(rng["q"], (1, Hq, N, D), dtype)
+    kb = syn.normal_bits(rng["k"], (1, Hkv, N, D), dtype)
+    vb = syn.normal_bits(rng["v"], (1, Hkv, N, D), dtype)
+    gb = syn.normal_bits(rng["gate"], (1, Hq, N, D), dtype)
+    q, k, v, g = (to_dev(x, dtype) for x in (qb, kb, vb, gb))
     kc = torch.zeros((1, Hkv, N, D), dtype=q.dtype, device="cuda")
     vc = torch.zeros_like(kc)
     out = ga.prompt_prefill(q, k, v, g, kc, vc, q_block=512)
     torch.cuda.synchronize()
     assert torch.equal(kc, k) and torch.equal(vc, v)
     rows = np.array([0, 31, 32, 511, 512, 4097, 16383, 20000, 32255, 32256, 32767])
-    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=0, kv_len=N,
-                              rows=rows)
-    _say(assert_close(to_f64(out[:, :, rows]), ref, f"fused D={D} 32k sampled"))
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=0,
+                              kv_len=N, rows=rows)
+    _say(assert_close(to_f64(out[:, :, rows]), ref, f"fused D={D} {dtype} 32k sampled"))
