@@ -250,6 +250,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="the timed step only (no side figures)")
     ap.add_argument("--only", choices=ONLY, help="run one workload --steps times (profiler runs)")
     ap.add_argument("--probes", action="store_true", help="run the achievable-peak probes only")
+    ap.add_argument("--q-block-sweep", action="store_true",
+                    help="fused prompt time per query block, head dim, shape and prompt length only")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path has no multi-GPU part "
@@ -273,6 +275,9 @@ def main():
 
     if args.probes:
         print(json.dumps({"probes": probes(dev, timer)}), flush=True)
+        return
+    if args.q_block_sweep:
+        print(json.dumps({"q_block_sweep": q_block_sweep(ga, syn, dev, timer, plans)}), flush=True)
         return
 
     t_setup = time.time()
@@ -544,8 +549,19 @@ def main():
             composed_fig[f"q_block_{qb_}"] = f
             torch.cuda.empty_cache()
         for D_ in (128, 64):
-            small[f"head_dim_{D_}"] = {f"q_block_{qb_}": prompt_figures(qb_, D=D_) for qb_ in (512, 128)}
+            small[f"head_dim_{D_}"] = {f"q_block_{qb_}": prompt_figures(qb_, D=D_) for qb_ in (512, 128, 1024, 2048)}
+            for qb_ in (512, 128):
+                small[f"head_dim_{D_}"][f"composed_q_block_{qb_}"] = prompt_figures(qb_, composed=True, D=D_)
+                torch.cuda.empty_cache()
             torch.cuda.empty_cache()
+        # the prompt policy (attn_prompt_policy) on this device for the same prompt at each head dim
+        policy = {}
+        for D_ in (256, 128, 64):
+            pol = ga.prompt_policy(D=D_, B=B, Hq=Hq, Hkv=Hkv, n_tokens=N)
+            policy[f"head_dim_{D_}"] = {"choice": pol, **prompt_figures(pol["q_block"], D=D_)}
+            torch.cuda.empty_cache()
+        extras["prefill_policy"] = {"route": "the block size and route attn_prompt_policy picks for this device",
+                                    "device_key": dict(zip(("gfx", "n_cus"), ga.device_key())), **policy}
         pr = _prompt_8k(ga, syn, dev, plans)
         pr["run"]()
         torch.cuda.synchronize(dev)
@@ -633,6 +649,48 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host, args.cpu_sample_rows, N)
     print(json.dumps(result), flush=True)
+
+
+SWEEP_Q_BLOCKS = (128, 256, 512, 1024, 2048, 4096, 8192, 32768)
+
+
+def q_block_sweep(ga, syn, dev, timer, plans):
+    """Device time of a whole causal prompt on the fused route (kv_append + attn_prefill per
+    query block) for every query-block size up to the prompt length, at head dims 256, 128 and
+    64, the 24/4 and 16/2 head shapes and prompts of 2048, 8192 and 32768 tokens: the
+    measurements behind the prompt policy (attn_prompt_policy).  One line per case as it ends."""
+    out = []
+    for D in (256, 128, 64):
+        for Hq, Hkv in ((24, 4), (16, 2)):
+            for N in (2048, 8192, 32768):
+                pq, pk, pv, pg, pkc, pvc, pout = _prompt_inputs(syn, dev, 1, Hq, Hkv, N, D)
+                row = {"head_dim": D, "Hq": Hq, "Hkv": Hkv, "n_tokens": N, "ms": {}, "workspace_bytes": {}}
+                for qL in SWEEP_Q_BLOCKS:
+                    if qL > N:
+                        continue
+                    need = 16
+                    for i, s in enumerate(range(0, N, qL)):
+                        need = max(need, plans.check(f"sweep_D{D}_{Hq}x{Hkv}_N{N}_qL{qL}_block{i}", op=0, B=1,
+                                                     Hq=Hq, Hkv=Hkv, rows=min(qL, N - s), kv_offset=s,
+                                                     D=D)["workspace_bytes"])
+                    wsp = torch.empty(need, dtype=torch.uint8, device=dev)
+
+                    def run(i=0):
+                        ga.prompt_prefill(pq, pk, pv, pg, pkc, pvc, q_block=qL, out=pout, workspace=wsp)
+
+                    run()
+                    torch.cuda.synchronize(dev)
+                    row["ms"][str(qL)] = round(timer.time(run, 1, 3), 4)
+                    row["workspace_bytes"][str(qL)] = int(need)
+                    del wsp
+                best = min(row["ms"], key=lambda k: row["ms"][k])
+                row["fastest_q_block"] = int(best)
+                row["tflops_at_fastest"] = round(prefill_flops(Hq, N, D) / (row["ms"][best] * 1e-3) / 1e12, 1)
+                print(json.dumps(row), flush=True)
+                out.append(row)
+                del pq, pk, pv, pg, pkc, pvc, pout
+                torch.cuda.empty_cache()
+    return out
 
 
 def _prompt_inputs(syn, dev, B, Hq, Hkv, N, D):

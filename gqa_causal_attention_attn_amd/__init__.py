@@ -312,18 +312,52 @@ def variant_name(variant: int) -> str:
     return lib().attn_variant_name(variant).decode()
 
 
-def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int, kv_offset: int = 0, out=None, workspace=None,
-                   head_chunk=0, n_splits=0, overlap_merge=False, composed=False):
+def device_key(device=None):
+    """(gfx number, compute units) of a CUDA device for attn_prompt_policy; (0, 0) without one."""
+    if not torch.cuda.is_available():
+        return 0, 0
+    props = torch.cuda.get_device_properties(device if device is not None else torch.cuda.current_device())
+    arch = getattr(props, "gcnArchName", "") or ""
+    digits = arch[3:].split(":")[0] if arch.startswith("gfx") else ""
+    gfx = int(digits) if digits.isdigit() else 0
+    return gfx, int(props.multi_processor_count)
+
+
+def prompt_policy(*, D: int, B: int, Hq: int, Hkv: int, n_tokens: int, dtype: str = "bf16", gfx=None,
+                  n_cus=None) -> dict:
+    """attn_prompt_policy: route and query-block size for a prompt of n_tokens rows.  gfx and
+    n_cus default to those of the current device."""
+    if gfx is None or n_cus is None:
+        dg, dc = device_key()
+        gfx = dg if gfx is None else gfx
+        n_cus = dc if n_cus is None else n_cus
+    qy = _abi.PromptQuery(D, B, Hq, Hkv, n_tokens, _abi.BF16 if dtype == "bf16" else _abi.F16, gfx, n_cus)
+    ch = _abi.PromptChoice()
+    _check(lib().attn_prompt_policy(C.byref(qy), C.byref(ch)))
+    return {"route": {_abi.OP_PREFILL: "fused", _abi.OP_COMPOSED: "composed"}[ch.route], "q_block": ch.q_block,
+            "qualified": bool(ch.qualified), "reason": _abi.POLICY_REASON[ch.reason], "n_calls": ch.n_calls}
+
+
+def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int = 0, kv_offset: int = 0, out=None,
+                   workspace=None, head_chunk=0, n_splits=0, overlap_merge=False, composed=False):
     """A prompt in query blocks: for each block, kv_append its K/V rows, then attn_prefill it
     (attn_prefill_composed with composed=True).
 
-    q/gate [B, Hq, N, 256] and k/v [B, Hkv, N, 256] hold the prompt (positions kv_offset ..
+    q/gate [B, Hq, N, D] and k/v [B, Hkv, N, D] hold the prompt (positions kv_offset ..
     kv_offset + N - 1); k_cache/v_cache have room for them.  Block i attends to the cache plus
     itself ("perf(qwen36): qualify M4 head-256 attention", Summary: query blocks of 128 or 512).
+    q_block = 0 takes the block size (and route) of attn_prompt_policy for this device.
     With overlap_merge, each block's merge runs on a second stream beside the next block's main
     pass (two workspaces, alternating); the caller's stream waits for the last merge.
     """
     N = q.shape[2]
+    if q_block == 0:
+        pol = prompt_policy(D=q.shape[3], B=q.shape[0], Hq=q.shape[1], Hkv=k.shape[1], n_tokens=N,
+                            dtype="bf16" if q.dtype == torch.bfloat16 else "f16", gfx=None, n_cus=None)
+        q_block = pol["q_block"]
+        composed = composed or pol["route"] == "composed"
+    if q_block < 1:
+        raise ValueError("q_block must be positive (or 0 for the prompt policy)")
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if composed:

@@ -7,7 +7,7 @@ The struct sizes are checked against the library's own (attn_struct_size) when i
 import ctypes as C
 import os
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 HEAD_DIM = 256
 MAX_DECODE_ROWS = 32
 MAX_CHUNKS = 64
@@ -27,7 +27,7 @@ OP_PREFILL, OP_DECODE, OP_COMPOSED = 0, 1, 2
 EXPORTS = (
     "attn_abi_version", "attn_struct_size", "attn_strerror", "attn_variant_name", "attn_head_chunk_plan",
     "attn_workspace_bytes", "attn_describe_plan", "attn_prefill", "attn_decode", "kv_append", "attn_merge",
-    "kv_keep", "attn_prefill_partials", "attn_prefill_composed", "attn_decode_noalloc",
+    "kv_keep", "attn_prefill_partials", "attn_prefill_composed", "attn_decode_noalloc", "attn_prompt_policy",
 )
 SCRATCH_BYTES = 64 << 20  # the device scratch of attn_decode_noalloc, per GPU
 KEEP_MAX_BATCH = 64
@@ -76,6 +76,18 @@ class PlanInfo(C.Structure):
                 ("workspace_bytes", C.c_int64), ("chunk_sizes", C.c_int32 * MAX_CHUNKS)]
 
 
+class PromptQuery(C.Structure):
+    _fields_ = [("D", C.c_int32), ("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32),
+                ("n_tokens", C.c_int64), ("dtype", C.c_int32), ("gfx", C.c_int32), ("n_cus", C.c_int32)]
+
+
+class PromptChoice(C.Structure):
+    _fields_ = [("route", C.c_int32), ("q_block", C.c_int32), ("qualified", C.c_int32), ("reason", C.c_int32),
+                ("n_calls", C.c_int64)]
+
+
+POLICY_REASON = {0: "whole_prompt", 1: "table", 2: "unqualified_default"}
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_attn.so")
 
 
@@ -115,9 +127,11 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.attn_decode_noalloc.argtypes = [P(AttnArgs), C.c_void_p]
     lib.kv_keep.restype = C.c_int
     lib.kv_keep.argtypes = [P(KvKeepArgs), C.c_void_p]
+    lib.attn_prompt_policy.restype = C.c_int
+    lib.attn_prompt_policy.argtypes = [P(PromptQuery), P(PromptChoice)]
     if lib.attn_abi_version() != ABI_VERSION:
         raise RuntimeError("libgqa_attn ABI version mismatch")
-    for i, st in enumerate((AttnArgs, KvAppendArgs, MergeArgs, PlanInfo, KvKeepArgs)):
+    for i, st in enumerate((AttnArgs, KvAppendArgs, MergeArgs, PlanInfo, KvKeepArgs, PromptQuery, PromptChoice)):
         if lib.attn_struct_size(i) != C.sizeof(st):
             raise RuntimeError(f"struct {st.__name__} size mismatch: lib {lib.attn_struct_size(i)} vs {C.sizeof(st)}")
     return lib

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include <string>
 #include <vector>
 
@@ -315,6 +317,8 @@ size_t attn_struct_size(int which) {
     case 4: return sizeof(kv_keep_args);
     case 2: return sizeof(merge_args);
     case 3: return sizeof(attn_plan_info);
+    case 5: return sizeof(attn_prompt_query);
+    case 6: return sizeof(attn_prompt_choice);
     default: return 0;
   }
 }
@@ -366,6 +370,51 @@ int attn_head_chunk_plan(int rows, int n_q_heads, int n_kv_heads, int enabled, i
   const int n = chunk_rule(rows, n_q_heads / n_kv_heads, enabled, sizes, cap);
   if (n < 0) return ATTN_E_ARG;
   *n_chunks = n;
+  return ATTN_OK;
+}
+
+int attn_prompt_policy(const attn_prompt_query* q, attn_prompt_choice* out) {
+  if (!q || !out) return ATTN_E_NULL;
+  if (q->D != 256 && q->D != 128 && q->D != 64) return ATTN_E_HEAD_DIM;
+  if (q->B < 1 || q->Hq < 1 || q->Hkv < 1 || q->Hq % q->Hkv != 0) return ATTN_E_HEADS;
+  if (q->n_tokens < 1) return ATTN_E_ROWS;
+  if (q->dtype != ATTN_BF16 && q->dtype != ATTN_F16) return ATTN_E_DTYPE;
+  // Fastest fused block size on gfx950 with 256 compute units, per head dim and group size
+  // (measured at G = 6 and G = 8 for prompts up to and beyond 8192 rows; the composed route
+  // never won).  Rows of {head dim, largest G, block rows}.
+  struct Row {
+    int D, g_max, q_block;
+  };
+  static const Row kTable[] = {
+      {256, 6, 8192}, {256, 1 << 30, 4096}, {128, 6, 8192}, {128, 1 << 30, 4096},
+      {64, 6, 8192},  {64, 1 << 30, 4096},
+  };
+  constexpr int64_t kWhole = 2048;  // up to this many rows the whole prompt is one call
+  const int G = q->Hq / q->Hkv;
+  out->route = ATTN_OP_PREFILL;
+  out->qualified = (q->gfx == 950 && q->n_cus == 256) ? 1 : 0;
+  int64_t qb;
+  if (!out->qualified) {
+    qb = 512;
+    out->reason = ATTN_POLICY_DEFAULT;
+  } else if (q->n_tokens <= kWhole) {
+    qb = q->n_tokens;
+    out->reason = ATTN_POLICY_WHOLE;
+  } else {
+    qb = 512;
+    for (const Row& r : kTable) {
+      if (r.D == q->D && G <= r.g_max) {
+        qb = r.q_block;
+        break;
+      }
+    }
+    // the table holds at batch 1: keep the rows of a block times the batch
+    qb = std::max<int64_t>(512, qb / q->B);
+    out->reason = ATTN_POLICY_TABLE;
+  }
+  qb = std::min<int64_t>(qb, q->n_tokens);
+  out->q_block = (int32_t)qb;
+  out->n_calls = (q->n_tokens + qb - 1) / qb;
   return ATTN_OK;
 }
 

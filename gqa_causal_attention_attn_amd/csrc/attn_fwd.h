@@ -116,18 +116,6 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
-// acc += A B with the accumulator in accumulation registers (AGPRs).  Written as inline
-// assembly so the accumulators stay there; the leading s_nop gives the wait states a VALU
-// write of A or B needs before an MFMA reads it.  Back-to-back accumulation into the same
-// registers needs none.
-template <int DT>
-__device__ __forceinline__ void mfma32_acc(f32x16& acc, const u32x4& a, const u32x4& b) {
-  if constexpr (DT == 0) {
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  } else {
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  }
-}
 
 // acc (+)= A B with the accumulator in VGPRs (FIRST: acc = A B), as inline assembly for the
 // same reason and with the same leading wait states.
@@ -151,7 +139,7 @@ __device__ __forceinline__ void mfma32_v(f32x16& acc, const u32x4& a, const u32x
 // Wait states between the last MFMA into sc and the first instruction that reads sc.
 __device__ __forceinline__ void acc_settle_v(f32x16& sc) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sc)); }
 
-// Wait states between the last mfma32_acc into o and any other instruction that reads o
+// Wait states between the last MFMA into o and any other instruction that reads o
 // (more than an 8-pass MFMA needs); tied to o so nothing that reads it moves above.
 template <int N>
 __device__ __forceinline__ void acc_settle(f32x16 (&o)[N]) {

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GQA_ATTN_ABI_VERSION 4
+#define GQA_ATTN_ABI_VERSION 5
 #define ATTN_HEAD_DIM 256
 #define ATTN_MAX_DECODE_ROWS 32
 #define ATTN_MAX_CHUNKS 64
@@ -194,11 +194,40 @@ typedef struct {
   int32_t chunk_sizes[ATTN_MAX_CHUNKS]; /* heads per chunk within a KV group, first n_head_chunks valid */
 } attn_plan_info;
 
+/* A prompt to be run as query blocks (kv_append + attn_prefill per block), for
+ * attn_prompt_policy. */
+typedef struct {
+  int32_t D;          /* head_dim: 256, 128 or 64 */
+  int32_t B;          /* batch */
+  int32_t Hq;         /* query heads */
+  int32_t Hkv;        /* KV heads */
+  int64_t n_tokens;   /* prompt rows */
+  int32_t dtype;      /* attn_dtype */
+  int32_t gfx;        /* the device's gfx number (950 for gfx950); 0 if unknown */
+  int32_t n_cus;      /* compute units of the device; 0 if unknown */
+} attn_prompt_query;
+
+typedef enum {
+  ATTN_POLICY_WHOLE = 0,   /* short prompt: one call for all of it */
+  ATTN_POLICY_TABLE = 1,   /* the block size measured fastest on this device */
+  ATTN_POLICY_DEFAULT = 2  /* device not the one the table was measured on: blocks of 512 */
+} attn_policy_reason;
+
+/* The route and query-block size attn_prompt_policy picks. */
+typedef struct {
+  int32_t route;      /* ATTN_OP_PREFILL (fused) or ATTN_OP_COMPOSED */
+  int32_t q_block;    /* rows per call (the last call may be shorter) */
+  int32_t qualified;  /* 1: the device is the one the table was measured on */
+  int32_t reason;     /* attn_policy_reason */
+  int64_t n_calls;    /* calls for the whole prompt: ceil(n_tokens / q_block) */
+} attn_prompt_choice;
+
 /* ABI version (GQA_ATTN_ABI_VERSION). */
 int attn_abi_version(void);
 
 /* sizeof of the argument structs as compiled into the library: which = 0 attn_args,
- * 1 kv_append_args, 2 merge_args, 3 attn_plan_info, 4 kv_keep_args.  Returns 0 for an unknown value. */
+ * 1 kv_append_args, 2 merge_args, 3 attn_plan_info, 4 kv_keep_args, 5 attn_prompt_query,
+ * 6 attn_prompt_choice.  Returns 0 for an unknown value. */
 size_t attn_struct_size(int which);
 
 /* Static description of a status code.  Never NULL. */
@@ -216,6 +245,21 @@ const char* attn_variant_name(int variant);
  * (cap too small). */
 int attn_head_chunk_plan(int rows, int n_q_heads, int n_kv_heads, int enabled, int* sizes, int cap,
                          int* n_chunks);
+
+/* The prompt policy ("perf(qwen36): qualify M4 head-256 attention", Summary and the review
+ * comment on eligibility: the query-block size and composed vs fused chosen per machine and per
+ * head dimension).  Keyed on the device (gfx number and compute units) and the head dim, from
+ * the fused prompt times measured per block size on gfx950 with 256 compute units (head dims
+ * 256, 128, 64; 24/4 and 16/2 heads; 2048, 8192 and 32768 tokens):
+ *   - the route is always the fused pass (the composed route is 9-13x slower at every head dim);
+ *   - prompts of at most 2048 rows run as one call;
+ *   - longer prompts run in blocks of 8192 rows when G = Hq / Hkv <= 6 and of 4096 rows when
+ *     G > 6 (the same at every head dim), divided by the batch (down to 512), at most the
+ *     prompt;
+ *   - any other device gets blocks of 512 rows, flagged unqualified.
+ * Pure host function; no device use.  Errors: ATTN_E_NULL, ATTN_E_HEAD_DIM, ATTN_E_HEADS
+ * (B < 1 or heads not a whole group), ATTN_E_ROWS (n_tokens < 1), ATTN_E_DTYPE. */
+int attn_prompt_policy(const attn_prompt_query* q, attn_prompt_choice* out);
 
 /* Workspace bytes a call with these arguments needs (0 when it needs none).  op is attn_op
  * (ATTN_OP_COMPOSED: attn_prefill_composed).  Validates `a` like the call itself would.  No

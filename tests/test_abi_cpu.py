@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
 def test_struct_sizes_and_version():
     lib = ga.lib()
     assert lib.attn_abi_version() == _abi.ABI_VERSION
-    for i, st in enumerate((_abi.AttnArgs, _abi.KvAppendArgs, _abi.MergeArgs, _abi.PlanInfo, _abi.KvKeepArgs)):
+    for i, st in enumerate((_abi.AttnArgs, _abi.KvAppendArgs, _abi.MergeArgs, _abi.PlanInfo, _abi.KvKeepArgs,
+                            _abi.PromptQuery, _abi.PromptChoice)):
         assert lib.attn_struct_size(i) == C.sizeof(st)
     assert lib.attn_struct_size(99) == 0
     for code in list(_abi.STATUS) + [12345]:
@@ -342,3 +343,56 @@ def test_launch_size_limits_are_rejected_by_planning_and_run_alike():
 def test_strerror_names_the_head_dims():
     msg = ga.lib().attn_strerror(_abi.STATUS_CODE["ATTN_E_HEAD_DIM"]).decode()
     assert "256" in msg and "128" in msg and "64" in msg
+
+
+# The prompt policy ("perf(qwen36): qualify M4 head-256 attention", Summary and the review comment
+# on eligibility): measured on gfx950 with 256 compute units, keyed on the device and head dim.
+MI355X = {"gfx": 950, "n_cus": 256}
+
+
+@pytest.mark.parametrize("D", [256, 128, 64])
+def test_prompt_policy_table_on_the_measured_device(D):
+    pol = lambda **kw: ga.prompt_policy(D=D, **{**MI355X, **kw})
+    # 24 query heads over 4 (G 6): blocks of 8192 rows past 2048 tokens; 16 over 2 (G 8): 4096
+    assert pol(B=1, Hq=24, Hkv=4, n_tokens=32768) == {"route": "fused", "q_block": 8192, "qualified": True,
+                                                      "reason": "table", "n_calls": 4}
+    assert pol(B=1, Hq=16, Hkv=2, n_tokens=32768) == {"route": "fused", "q_block": 4096, "qualified": True,
+                                                      "reason": "table", "n_calls": 8}
+    assert pol(B=1, Hq=16, Hkv=2, n_tokens=8192)["q_block"] == 4096
+    assert pol(B=1, Hq=24, Hkv=4, n_tokens=8192)["q_block"] == 8192
+    # at most the prompt, and short prompts in one call
+    assert pol(B=1, Hq=24, Hkv=4, n_tokens=5000)["q_block"] == 5000
+    for n in (1, 100, 2048):
+        c = pol(B=1, Hq=24, Hkv=4, n_tokens=n)
+        assert (c["q_block"], c["reason"], c["n_calls"]) == (n, "whole_prompt", 1)
+    # the group size decides the row (G 1 and 6 take 8192, G 7 and 16 take 4096)
+    assert pol(B=1, Hq=4, Hkv=4, n_tokens=32768)["q_block"] == 8192
+    assert pol(B=1, Hq=7, Hkv=1, n_tokens=32768)["q_block"] == 4096
+    assert pol(B=1, Hq=32, Hkv=2, n_tokens=32768)["q_block"] == 4096
+    # the batch divides the block (down to 512 rows)
+    assert pol(B=2, Hq=24, Hkv=4, n_tokens=32768)["q_block"] == 4096
+    assert pol(B=64, Hq=24, Hkv=4, n_tokens=32768)["q_block"] == 512
+    c = pol(B=1, Hq=24, Hkv=4, n_tokens=32769)
+    assert (c["q_block"], c["n_calls"]) == (8192, 5)
+
+
+@pytest.mark.parametrize("gfx,n_cus", [(942, 304), (950, 32), (950, 0), (0, 0), (1100, 256)])
+def test_prompt_policy_other_devices_get_the_default(gfx, n_cus):
+    # an MI300X, one 32-CU partition of an MI355X, or an unknown device: blocks of 512, unqualified
+    for n in (100, 32768):
+        c = ga.prompt_policy(D=256, B=1, Hq=24, Hkv=4, n_tokens=n, gfx=gfx, n_cus=n_cus)
+        assert c == {"route": "fused", "q_block": min(512, n), "qualified": False, "reason": "unqualified_default",
+                     "n_calls": -(-n // min(512, n))}
+
+
+def test_prompt_policy_rejections():
+    lib = ga.lib()
+    ok = dict(D=256, B=1, Hq=24, Hkv=4, n_tokens=32768, dtype=_abi.BF16, gfx=950, n_cus=256)
+    ch = _abi.PromptChoice()
+    assert lib.attn_prompt_policy(C.byref(_abi.PromptQuery(**ok)), C.byref(ch)) == _abi.OK
+    assert lib.attn_prompt_policy(None, C.byref(ch)) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    assert lib.attn_prompt_policy(C.byref(_abi.PromptQuery(**ok)), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    for bad, code in [(dict(D=96), "ATTN_E_HEAD_DIM"), (dict(B=0), "ATTN_E_HEADS"), (dict(Hq=5, Hkv=2), "ATTN_E_HEADS"),
+                      (dict(Hkv=0), "ATTN_E_HEADS"), (dict(n_tokens=0), "ATTN_E_ROWS"), (dict(dtype=7), "ATTN_E_DTYPE")]:
+        q = _abi.PromptQuery(**{**ok, **bad})
+        assert lib.attn_prompt_policy(C.byref(q), C.byref(ch)) == _abi.STATUS_CODE[code], bad
