@@ -267,6 +267,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
   p.causal = a->causal;
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.scale = scale;
   p.chunk = P.chunk;
   p.blocks_per_chunk = P.blocks_per_chunk;
   p.n_tiles = P.n_tiles;

@@ -757,12 +757,19 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   };
 
   // ---- element q of S block i is MFMA row 8 (q / 4) + 4 hf + q % 4, i.e. key jb +
-  // key_of<D>(q, i) + R hf of this lane's pair.  Scores in log2 units, with keys the pair cannot
-  // see at -inf.  Without a mask the scale folds into the exponent later (the max commutes with
-  // it, scale > 0) and only tiles that reach some pair's bound compare keys.
+  // key_of<D>(q, i) + R hf of this lane's pair.  Keys the pair cannot see go to -inf; only tiles
+  // that reach some pair's bound compare keys (wave-uniform test).  The scale is applied later,
+  // in the exponent (the max commutes with it, scale > 0), except that an additive mask adds its
+  // value to the scaled score: there the score becomes scale s + mask (natural-log units) and
+  // the exponent applies log2(e).  A bool mask only hides keys.
+  auto add_mask = [&](float s, uint32_t w) {
+    if constexpr (MK == 1) return w ? s : -INFINITY;
+    else if constexpr (MK == 2) return __builtin_fmaf(s, p.scale, lo16<DT>(w));
+    else return __builtin_fmaf(s, p.scale, __builtin_bit_cast(float, w));
+  };
   auto mask_scores = [&](f32x16(&sc)[kSB], int jb, int lim, int64_t mrow) {
     if constexpr (MK == 0) {
-      if (jb + kTileKeys > lim_min) {  // wave-uniform
+      if (jb + kTileKeys > lim_min) {
         const int jl = jb + kRpg * (int)(lane_fresh() >> 5);  // recomputed: not held across the loop
         static_for<kSB>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
@@ -773,12 +780,19 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
         });
       }
     } else {
+      // the mask word of key j is read only for keys the pair may see (row ends at kv_len)
+      auto word = [&](int j) {
+        if constexpr (MK == 1) return (uint32_t) static_cast<const uint8_t*>(p.mask)[mrow + j];
+        else if constexpr (MK == 2) return (uint32_t) static_cast<const uint16_t*>(p.mask)[mrow + j];
+        else return __builtin_bit_cast(uint32_t, static_cast<const float*>(p.mask)[mrow + j]);
+      };
+      const int jl = jb + kRpg * hf;
       static_for<kSB>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const int j = jb + key_of<D>(q, i) + kRpg * hf;
-          sc[i][q] = j < lim ? sc[i][q] * p.scale_log2 + mask_term<DT, MK>(p.mask, mrow, j) : -INFINITY;
+          const int j = jl + key_of<D>(q, i);
+          sc[i][q] = j < lim ? add_mask(sc[i][q], word(j)) : -INFINITY;
         }
       });
     }
@@ -792,10 +806,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       const uint32_t mst = lds0 + kFwdLdsBytes + ((sb - lds0) / kStageLds) * kMaskStageLds;
       static_for<kSB>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        auto apply = [&](int q, uint32_t w) {
-          const int j = jb + key_of<D>(q, i) + kRpg * hf;
-          sc[i][q] = j < lim ? sc[i][q] * p.scale_log2 + mask_term_of<DT, MK>(w) : -INFINITY;
-        };
+        auto apply = [&](int q, uint32_t w) { sc[i][q] = add_mask(sc[i][q], w); };
         if constexpr (ML == 2) {
           const uint32_t row = mst + word_row(rho) + kRpg * hf * 4;
 #pragma unroll
@@ -827,6 +838,17 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
           }
         }
       });
+      // keys past some pair's bound (wave-uniform test: only tiles that reach a bound)
+      if (jb + kTileKeys > lim_min) {
+        const int jl = jb + kRpg * hf;
+        static_for<kSB>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            if (jl + key_of<D>(q, i) >= lim) sc[i][q] = -INFINITY;
+          }
+        });
+      }
     }
   };
   auto mask_any = [&](f32x16(&sc)[kSB], int jb, int lim, int64_t mrow, uint32_t sb) {
@@ -850,7 +872,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 #pragma unroll
       for (int q = 0; q < 16; q += 2) mr = fmaxf(fmaxf(mr, sc[i][q]), sc[i][q + 1]);
     }
-    const float scale = MK == 0 ? p.scale_log2 : 1.0f;
+    const float scale = MK >= 2 ? kLog2e : p.scale_log2;
     alpha = 1.0f;
     if (__builtin_amdgcn_ballot_w64(mr * scale > m_run + kRescaleSlack)) {
       const float mx = max_halves(mr) * scale;
@@ -868,7 +890,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // l_run = alpha l_run + the sum of the rounded weights
   auto weights = [&](const f32x16(&sc)[kSB], float m_run, float alpha, float& l_run, u32x4(&pb0)[kSB],
                      u32x4(&pb1)[kSB]) {
-    const float scale = MK == 0 ? p.scale_log2 : 1.0f;
+    const float scale = MK >= 2 ? kLog2e : p.scale_log2;
     const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
     float lsum = 0.0f;
 #pragma unroll

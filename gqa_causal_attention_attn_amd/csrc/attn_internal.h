@@ -54,6 +54,7 @@ struct FwdParams {
   int B, Hq, Hkv, G, rows;
   int causal;
   float scale_log2;      // scale * log2(e)
+  float scale;           // the score scale itself (additive masks add in natural-log units)
   int chunk;             // heads per chunk
   int blocks_per_chunk;  // column blocks serving one chunk
   int n_tiles;           // workgroups per (batch, kv head, split)
