@@ -220,6 +220,31 @@ def probes(dev, timer):
                         "shader_clock_ghz": round(ghz, 3),
                         "peak_at_that_clock_tflops": round(PEAK_BF16_TFLOPS * ghz / 2.4, 1),
                         "kernel": "8 chains of v_mfma_f32_32x32x16_bf16 per wavefront, 8 wavefronts x 256 workgroups"}
+    # the same instruction with VALU work beside it (two wavefronts a SIMD, as in the main pass)
+    lib.gqa_probe_mfma_mix.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p]
+    mix = {}
+    for chains, nv, ex in ((1, 0, 0), (4, 0, 0), (1, 2, 0), (1, 4, 0), (4, 4, 0), (1, 1, 1), (1, 2, 1)):
+        it = 2000
+        fn = (lambda i: lib.gqa_probe_mfma_mix(out.data_ptr(), blocks, it, chains, nv, ex, s))
+        assert fn(0) == 0
+        ms = timer.time(fn, 1, 5)
+        tf = blocks * 8 * it * 16 * 32768.0 / (ms * 1e-3) / 1e12
+        mix[f"chains{chains}_{nv}{'exp' if ex else 'fma'}"] = round(tf, 1)
+    res["mfma_bf16_with_valu"] = {"tflops": mix, "kernel": "16 v_mfma_f32_32x32x16_bf16 per round on 1 (dependent) or "
+                                  "4 accumulators, each followed by 0-4 independent FMAs or v_exp_f32; 8 wavefronts x 256 "
+                                  "workgroups"}
+    # LDS read rate of the two read forms of the main pass, in bytes per CU per shader clock
+    lib.gqa_probe_lds.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p]
+    lds = {}
+    for kind, name, per in ((0, "ds_read_b128", 1024), (1, "ds_read_b64_tr_b16 (V-operand lanes)", 512)):
+        it = 20000
+        fn = (lambda i: lib.gqa_probe_lds(out.data_ptr(), blocks, it, kind, s))
+        assert fn(0) == 0
+        ms = timer.time(fn, 1, 5)
+        nbytes = blocks * 8 * 8 * it * per
+        lds[name] = {"tbps": round(nbytes / (ms * 1e-3) / 1e12, 2),
+                     "bytes_per_cu_per_clock": round(nbytes / blocks / (ms * 1e-3) / (ghz * 1e9), 1)}
+    res["lds_read"] = {**lds, "clock_ghz_used": round(ghz, 3)}
     # streaming read, cold: the decode workload's bytes (134 MB, rotating over 8 distinct buffers
     # so the 256 MB Infinity Cache cannot hold them) and one 1 GiB buffer; 2048 workgroups
     sink = torch.empty(2048 * 256, dtype=torch.int32, device=dev)

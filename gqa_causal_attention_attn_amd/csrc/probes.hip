@@ -1,5 +1,9 @@
 // Achievable-peak probes for the roofline figures (libgqa_probes.so, include/gqa_probes.h).
 //
+// mfma_mix_kernel and lds_read_kernel (below) measure what the main pass's schedule can expect:
+// the matrix-core rate of one dependent chain, how much VALU work runs beside it, and the LDS
+// read rates of the two read forms it uses.
+//
 // mfma_peak_kernel: every wavefront runs `iters` rounds of kChains independent accumulation
 // chains of v_mfma_f32_32x32x16_bf16 (the instruction of the attention kernels), nothing else
 // in the loop; 32 * 32 * 16 * 2 flops per instruction.  Lane 0 of each wavefront also reads the
@@ -79,6 +83,98 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* src, size
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
+// MFMA with VALU beside it: every wavefront runs `iters` rounds of 16 v_mfma_f32_32x32x16_bf16
+// on CHAINS independent accumulators (1: each MFMA depends on the one before), each MFMA
+// followed by NV independent VALU operations (EXP: v_exp_f32, else FMAs) on other registers.
+// Eight wavefronts a workgroup, two a SIMD, as in the attention main pass.
+template <int CHAINS, int NV, bool EXP>
+__global__ __launch_bounds__(512) void mfma_mix_kernel(float* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)(lane + i));
+    b[i] = (__bf16)(0.002f * (float)(lane - i));
+  }
+  f32x16 acc[CHAINS];
+#pragma unroll
+  for (int c = 0; c < CHAINS; ++c) acc[c] = (f32x16){};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = 0.01f * (float)(lane + i);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      acc[k % CHAINS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k % CHAINS], 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        if constexpr (EXP) x[v % 8] = __builtin_amdgcn_exp2f(x[v % 8]) * 0.5f;
+        else x[v % 8] = __builtin_fmaf(x[v % 8], 0.999f, 0.001f);
+      }
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CHAINS; ++c) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[c][i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// LDS read rate: eight wavefronts a workgroup read a 64 KiB array, eight reads in flight per
+// wavefront.  KIND 0: ds_read_b128 at consecutive 16-byte cells (1 KiB a read); KIND 1:
+// ds_read_b64_tr_b16 at the lane addresses the attention main pass uses for its V operand
+// (groups of 1040 bytes; 512 B a read).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int KIND>
+__global__ __launch_bounds__(512) void lds_read_kernel(float* out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint32_t buf[16384];
+  for (int i = threadIdx.x; i < 16384; i += blockDim.x) buf[i] = (uint32_t)i;
+  __syncthreads();
+  const uint32_t l = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)buf;
+  // the main pass's V lane address within a tile: (4 tq + hf) groups of 1040 B, then 16-byte
+  // and 8-byte steps (at most 13,584 + 448 + 8 bytes, inside the array)
+  const uint32_t vlane = (4 * ((l >> 2) & 3) + (l >> 5)) * 1040 + 16 * (2 * ((l >> 4) & 1) + ((l & 3) >> 1)) + 8 * (l & 1);
+  uint32_t accu = 0;
+  for (int it = 0; it < iters; ++it) {
+    const uint32_t off = ((uint32_t)(it + wave) & 3u) * 8192u;  // at most 24,576
+    // the eight reads and their wait in one asm statement: the registers an outstanding read
+    // will write are outputs of the statement that waits for it, so nothing else can use them
+    if constexpr (KIND == 0) {
+      u32x4 r0, r1, r2, r3, r4, r5, r6, r7;
+      const uint32_t a = base + off + l * 16;
+      asm volatile(
+          "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
+          "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
+          "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
+          "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+          : "v"(a)
+          : "memory");
+      accu ^= r0[0] ^ r1[1] ^ r2[2] ^ r3[3] ^ r4[0] ^ r5[1] ^ r6[2] ^ r7[3];
+    } else {
+      u32x2 r0, r1, r2, r3, r4, r5, r6, r7;
+      const uint32_t a = base + off + vlane;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %8 offset:64\n\t"
+          "ds_read_b64_tr_b16 %2, %8 offset:128\n\tds_read_b64_tr_b16 %3, %8 offset:192\n\t"
+          "ds_read_b64_tr_b16 %4, %8 offset:256\n\tds_read_b64_tr_b16 %5, %8 offset:320\n\t"
+          "ds_read_b64_tr_b16 %6, %8 offset:384\n\tds_read_b64_tr_b16 %7, %8 offset:448\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+          : "v"(a)
+          : "memory");
+      accu ^= r0[0] ^ r1[1] ^ r2[0] ^ r3[1] ^ r4[0] ^ r5[1] ^ r6[0] ^ r7[1];
+    }
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = (float)accu;
+}
+
 }  // namespace
 
 extern "C" {
@@ -87,6 +183,33 @@ int gqa_probe_mfma(float* out, uint64_t* clocks, int blocks, int waves_per_block
   if (!out || !clocks || blocks < 1 || iters < 1 || (waves_per_block != 4 && waves_per_block != 8)) return 1;
   hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)blocks), dim3((unsigned)(64 * waves_per_block)), 0,
                      static_cast<hipStream_t>(stream), out, clocks, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int gqa_probe_mfma_mix(float* out, int blocks, int iters, int chains, int n_valu, int exp_op, void* stream) {
+  if (!out || blocks < 1 || iters < 1) return 1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+#define GQA_MIX(C, N, E)                                                                            \
+  if (chains == C && n_valu == N && (exp_op != 0) == E) {                                           \
+    hipLaunchKernelGGL((mfma_mix_kernel<C, N, E>), dim3((unsigned)blocks), dim3(512), 0, s, out, iters); \
+    return hipGetLastError() == hipSuccess ? 0 : 2;                                                 \
+  }
+  GQA_MIX(1, 0, false)
+  GQA_MIX(1, 2, false)
+  GQA_MIX(1, 4, false)
+  GQA_MIX(1, 1, true)
+  GQA_MIX(1, 2, true)
+  GQA_MIX(4, 0, false)
+  GQA_MIX(4, 4, false)
+#undef GQA_MIX
+  return 1;
+}
+
+int gqa_probe_lds(float* out, int blocks, int iters, int kind, void* stream) {
+  if (!out || blocks < 1 || iters < 1 || (kind != 0 && kind != 1)) return 1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kind == 0) hipLaunchKernelGGL(lds_read_kernel<0>, dim3((unsigned)blocks), dim3(512), 0, s, out, iters);
+  else hipLaunchKernelGGL(lds_read_kernel<1>, dim3((unsigned)blocks), dim3(512), 0, s, out, iters);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

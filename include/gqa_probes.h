@@ -2,7 +2,7 @@
  * gqa_probes.h -- C ABI of libgqa_probes.so: achievable-peak probes for the roofline figures
  * of the attention library (not part of the attention path).
  *
- * Both calls enqueue one kernel on `stream` (a hipStream_t, NULL = default) and return 0, 1
+ * Each call enqueues one kernel on `stream` (a hipStream_t, NULL = default) and return 0, 1
  * for an invalid argument (nothing enqueued) or 2 if the HIP runtime refused the launch.
  * Every pointer is DEVICE memory owned by the caller; the library allocates nothing.
  */
@@ -22,6 +22,20 @@ extern "C" {
  * clocks: 2 words per wavefront, the s_memtime (shader clock) and s_memrealtime (100 MHz)
  * ticks its loop took, so the clock the matrix cores ran at is 100 MHz * clocks[0] / clocks[1]. */
 int gqa_probe_mfma(float* out, uint64_t* clocks, int blocks, int waves_per_block, int iters, void* stream);
+
+/* The same instruction with VALU work beside it: `blocks` workgroups of 8 wavefronts, each
+ * running `iters` rounds of 16 MFMAs on `chains` independent accumulators (1: each MFMA depends
+ * on the one before; or 4), each MFMA followed by `n_valu` independent VALU operations on other
+ * registers, v_exp_f32 if exp_op else FMAs.  Supported (chains, n_valu, exp_op): (1,0,0),
+ * (1,2,0), (1,4,0), (1,1,1), (1,2,1), (4,0,0), (4,4,0); others return 1.  out: blocks * 512
+ * floats. */
+int gqa_probe_mfma_mix(float* out, int blocks, int iters, int chains, int n_valu, int exp_op, void* stream);
+
+/* LDS read rate: `blocks` workgroups of 8 wavefronts read a 64 KiB LDS array, eight reads in
+ * flight per wavefront, `iters` rounds; kind 0 = ds_read_b128 (1 KiB a read), kind 1 =
+ * ds_read_b64_tr_b16 at the V-operand lane addresses of the attention main pass (512 B a
+ * read).  Bytes read: blocks * 8 * 8 * iters * (1024 or 512).  out: blocks * 512 floats. */
+int gqa_probe_lds(float* out, int blocks, int iters, int kind, void* stream);
 
 /* Streaming read of `bytes` bytes (a multiple of 16, src 16-byte aligned) by `blocks`
  * workgroups of 256 lanes, each workgroup one contiguous slice, 16-byte loads with eight in
