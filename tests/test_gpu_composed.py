@@ -233,3 +233,32 @@ def test_fused_small_head_dims_32k_prompt_sampled(D, dtype):
     ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=0,
                               kv_len=N, rows=rows)
     _say(assert_close(to_f64(out[:, :, rows]), ref, f"fused D={D} {dtype} 32k sampled"))
+
+
+@needs_gpu
+@pytest.mark.parametrize("D,Hq,Hkv,N", [(256, 16, 2, 8192), (128, 24, 4, 4608), (64, 24, 4, 1500)])
+def test_prompt_policy_block_size_on_this_device(D, Hq, Hkv, N):
+    # prompt_prefill(q_block=0) takes attn_prompt_policy's block size for this device (the table
+    # on an MI355X: 4096 rows for G 8, 8192 for G 6 at most the prompt, one call up to 2048
+    # rows); rows sampled across the prompt against the oracle
+    gfx, n_cus = ga.device_key()
+    pol = ga.prompt_policy(D=D, B=1, Hq=Hq, Hkv=Hkv, n_tokens=N)
+    _say("policy", D, Hq, Hkv, N, gfx, n_cus, pol)
+    if (gfx, n_cus) == (950, 256):
+        assert pol["qualified"] and pol["route"] == "fused"
+        assert pol["q_block"] == (N if N <= 2048 else min(N, 4096 if Hq // Hkv > 6 else 8192))
+    rng = syn.streams(5800 + D)
+    qb = syn.normal_bits(rng["q"], (1, Hq, N, D))
+    kb = syn.normal_bits(rng["k"], (1, Hkv, N, D))
+    vb = syn.normal_bits(rng["v"], (1, Hkv, N, D))
+    gb = syn.normal_bits(rng["gate"], (1, Hq, N, D))
+    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    kc = torch.zeros((1, Hkv, N, D), dtype=q.dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    out = ga.prompt_prefill(q, k, v, g, kc, vc, q_block=0)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k) and torch.equal(vc, v)
+    rows = np.unique(np.array([0, 1, N // 3, pol["q_block"] - 1, min(pol["q_block"], N - 1), N - 2, N - 1]))
+    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=0, kv_len=N,
+                              rows=rows)
+    _say(assert_close(to_f64(out[:, :, rows]), ref, f"policy D={D}"))
