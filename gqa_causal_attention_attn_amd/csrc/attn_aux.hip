@@ -9,8 +9,8 @@
 // wavefronts per row, each loading its share of the chunks at once.  HBM-bound
 // (n_chunks x 1 KiB per row).
 //
-// Append and keep (the same commit compares both bit for bit, keep a second time on the caches
-// the first call left): 16-byte copies of K/V rows into the cache, no arithmetic on the bits.
+// Append and keep (the same commit compares both bit for bit, keep also when it is repeated
+// on the caches its first call produced): 16-byte copies of K/V rows into the cache, no arithmetic on the bits.
 // Keep compacts the accepted rows of a verify block in place, one workgroup per (b, g) reading
 // every kept row before writing any.
 #include <hip/hip_runtime.h>

@@ -145,7 +145,7 @@ typedef struct {
  * the block's rows after the kept ones are left as they were.  An accepted path of a draft tree
  * whose rows are numbered parents first (a chain being the special case 0, 1, 2, ...) keeps
  * its order.  TensorFold PR #1009 (attention kernel-contract commit) compares keep bit for bit,
- * also a second time on the caches the first call left. */
+ * also when it is repeated on the caches its first call produced. */
 typedef struct {
   int32_t dtype;
   int32_t B;              /* 1..64 */

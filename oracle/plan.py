@@ -1,7 +1,7 @@
 """The head-chunk rule as "Qwen head-chunked SDPA (#113)" states it (test infrastructure only).
 
-Introduction of that page: when the policy is on (the default) and
-rows * GQA > 32 with rows <= 32, the query heads inside each KV group are split
+Introduction of that page: with the policy enabled (its default), for at most 32
+rows and more than 32 (row, head) pairs per group (rows * GQA > 32), the query heads inside each KV group are split
 into chunks of min(GQA, 32 / rows) heads, the remainder heads are kept as a
 last, smaller chunk, each chunk attends with its group's K/V, and the outputs
 are concatenated in the original head order.  An explicit off switch keeps the

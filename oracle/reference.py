@@ -6,10 +6,9 @@ of it, so the same definition serves every entry point of the library.
 
 Sources (the pages):
   * TensorFold PR #1009, attention kernel-contract commit: decode rows and
-    prompt rows of gated attention for 24 query heads over 4 KV heads and 16
-    over 2 are checked against float64 gated attention; a merge combines decode
+    prompt rows of gated attention at the 24/4 and 16/2 head shapes are checked against float64 gated attention; a merge combines decode
     chunks; pack/append/keep are bit copies.  Receipt, "Attention": the same,
-    with the controls (a row seeing one key past its own, a merge dropping
+    with the controls (a row that sees one key beyond its causal bound, a merge dropping
     later tail chunks, an append one row late).
   * "perf(qwen36): qualify M4 head-256 attention" (d-inference PR #640),
     Summary: prompts are processed in query blocks of qL rows (128 or 512).

@@ -1,7 +1,7 @@
 """Planted mistakes in the oracle must be caught by the parity comparison (CPU only).
 
 TensorFold PR #1009 (attention kernel-contract commit; Receipt, "Attention")
-runs three controls that must go red: a row seeing one key past its own, a
+runs three controls that must go red: a row that sees one key beyond its causal bound, a
 merge dropping later tail chunks, and an append one row late.  Each is planted
 here in a copy of the oracle's behaviour, with inputs built so the mistake is
 large, and the comparison used by the GPU parity tests must flag it.

@@ -1,8 +1,8 @@
 """Precision separation: the tolerance must catch low-precision score sums (CPU only).
 
-TensorFold PR #1009 (Receipt, "Attention") requires its attention stress inputs
-to make fp16 score sums miss without limit and bf16 sums miss by a wide margin,
-with fp32 as the rule.  Here the oracle's score step is re-evaluated with the
+TensorFold PR #1009 (Receipt, "Attention") wants attention stress inputs on
+which fp16 score sums fail outright and bf16 sums fail by a large factor while
+fp32 passes.  Here the oracle's score step is re-evaluated with the
 dot products accumulated sequentially in bf16, fp16 and fp32 on the stress
 inputs from ``synth.stress_cancellation``; the rest of the definition is the
 oracle's own.  bf16 must miss the max-abs tolerance by at least 100x, fp16 must
