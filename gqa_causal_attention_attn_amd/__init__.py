@@ -58,7 +58,7 @@ def _t4(t: torch.Tensor | None) -> _abi.Tensor:
     if t is None:
         return _abi.Tensor(None, 0, 0, 0)
     if t.dim() != 4:
-        raise ValueError("tensors are 4-d [B, H, rows, 256]")
+        raise ValueError("tensors are 4-d [B, H, rows, head_dim]")
     if t.stride(3) != 1:
         raise ValueError("the last (head_dim) dimension must be contiguous")
     return _abi.Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
@@ -164,7 +164,7 @@ def prefill_partials(q, k_cache, v_cache, gate, *, kv_offset: int, workspace, kv
 
 def prefill(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
             n_splits=0, mask=None, out=None, workspace=None):
-    """attn_prefill: q/gate [B, Hq, rows, 256], caches [B, Hkv, capacity, 256]; returns out."""
+    """attn_prefill: q/gate [B, Hq, rows, D], caches [B, Hkv, capacity, D] (D = 256, 128 or 64); returns out."""
     return _run(_abi.OP_PREFILL, q, k_cache, v_cache, gate, kv_offset=kv_offset, kv_len=kv_len, causal=causal,
                 scale=scale, head_chunk=head_chunk, n_splits=n_splits, mask=mask, out=out, workspace=workspace)
 
@@ -198,7 +198,7 @@ def prefill_composed(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, 
 
 
 def kv_append(k_new, v_new, k_cache, v_cache, *, kv_offset: int) -> None:
-    """kv_append: copy [B, Hkv, rows, 256] rows into the caches at kv_offset, bit for bit."""
+    """kv_append: copy [B, Hkv, rows, D] rows into the caches at kv_offset, bit for bit."""
     a = _abi.KvAppendArgs()
     a.dtype = _dtype_code(k_new)
     a.B, a.Hkv, a.rows, a.D = k_new.shape[0], k_new.shape[1], k_new.shape[2], k_new.shape[3]

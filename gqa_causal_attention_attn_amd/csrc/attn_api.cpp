@@ -1,5 +1,5 @@
 // Host side of libgqa_attn: argument validation, the head-chunk and KV-split plans, workspace
-// sizing, and the launches.  Every check runs before anything is enqueued, so an invalid call
+// sizing, the launches, and the prompt policy (block size and route per head dim and device).  Every check runs before anything is enqueued, so an invalid call
 // writes nothing.  Head counts are validated before any division (TensorFold PR #1009, the
 // config-reader commit: zero heads and uneven head groups are refused with ordinary errors).
 #include <hip/hip_runtime.h>

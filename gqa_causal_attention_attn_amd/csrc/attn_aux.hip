@@ -5,9 +5,9 @@
 // out = sum_c exp(lse_c - lse) o_c * sigmoid(gate), an empty chunk (lse_c = -Inf) adds
 // nothing (its slot is selected out, never multiplied in) and a row with every chunk empty
 // gives 0; a chunk whose lse is NaN makes the row NaN.  Few chunks: one wavefront per row
-// with every partial loaded at once; many chunks (decode): one workgroup of sixteen
-// wavefronts per row, each loading its share of the chunks at once.  HBM-bound
-// (n_chunks x 1 KiB per row).
+// with every partial loaded at once; many chunks (decode): one workgroup of 4, 8 or 16
+// wavefronts per row (the fewest that hold the chunks), each loading its share of the chunks
+// at once.  HBM-bound (n_chunks x (4 D + 4) bytes per row).
 //
 // Append and keep (the same commit compares both bit for bit, keep also when it is repeated
 // on the caches its first call produced): 16-byte copies of K/V rows into the cache, no arithmetic on the bits.

@@ -47,9 +47,9 @@
 // Masks.  A mask that is the same for every head may be staged in LDS beside each K/V tile
 // (chosen by the host), in one of two layouts.  Words: each key's mask word in a dword of its
 // own (1-, 2- and 4-byte direct loads each write one zero-extended dword per lane), the window's
-// rows at a 264-byte pitch so that lanes of different rows read different banks; any row stride
-// and any kv_len, at most 32 rows per workgroup; every wavefront issues 16 / W of the 16 loads of
-// a tile.  Rows: 16-byte chunks of rows whose pitch is a multiple of 16 bytes, up to 4 KiB of
+// rows at a 264- or 520-byte pitch so that lanes of different rows read different banks; any row
+// stride and any kv_len, at most 1024 / T rows per workgroup (T keys a tile: 32, 16 and 8 rows at
+// head dims 256, 128 and 64); every wavefront issues 16 / W of the 16 loads of a tile.  Rows: 16-byte chunks of rows whose pitch is a multiple of 16 bytes, up to 4 KiB of
 // rows, loaded by wavefronts 0-3 (kept for prompt workgroups whose pairs span more than 32
 // rows).  Otherwise each lane loads its words from memory.  All three give the same bits.
 //

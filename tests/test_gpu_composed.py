@@ -1,9 +1,11 @@
-"""The composed (materialised-score) route on the GPU against the float64 oracle.
+"""The composed (materialised-score) route, the main pass at head dims 128 and 64, and the
+prompt policy, on the GPU against the float64 oracle.
 
 attn_prefill_composed computes the same block as attn_prefill in three passes through HBM
 ("perf(qwen36): qualify M4 head-256 attention", Summary: composed against fused attention at
-head_dim 256 for query blocks of 128 and 512).  Same tolerance: max abs error <= 1.5e-2 and
-median relative error <= 4e-3 on 16-bit outputs with fp32 accumulation.
+head_dim 256 for query blocks of 128 and 512; its review comment: eligibility by head
+dimension).  Same tolerance: max abs error <= 1.5e-2 and median relative error <= 4e-3 on
+16-bit outputs with fp32 accumulation.
 """
 
 import numpy as np
