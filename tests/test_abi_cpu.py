@@ -396,3 +396,16 @@ def test_prompt_policy_rejections():
                       (dict(Hkv=0), "ATTN_E_HEADS"), (dict(n_tokens=0), "ATTN_E_ROWS"), (dict(dtype=7), "ATTN_E_DTYPE")]:
         q = _abi.PromptQuery(**{**ok, **bad})
         assert lib.attn_prompt_policy(C.byref(q), C.byref(ch)) == _abi.STATUS_CODE[code], bad
+
+
+def test_probe_library_exports_every_declared_symbol():
+    # include/gqa_probes.h: the benchmark's achievable-peak probes; loaded, never called here
+    from gqa_causal_attention_attn_amd import build as gbuild
+
+    with open(os.path.join(ROOT, "include", "gqa_probes.h")) as f:
+        body = f.read().split('extern "C" {', 1)[1]
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\(", body, flags=re.M))
+    assert declared == {"gqa_probe_mfma", "gqa_probe_mfma_mix", "gqa_probe_lds", "gqa_probe_read"}
+    lib = C.CDLL(gbuild.PROBES_LIB)
+    for name in declared:
+        assert hasattr(lib, name), name
