@@ -8,7 +8,7 @@ import torch
 import gqa_causal_attention_attn_amd as ga
 from oracle import reference
 from synth import inputs as syn
-from tests.gpu_util import prompt, to_dev, to_f64
+from tests.gpu_util import prompt, to_bits, to_dev, to_f64
 from tests.parity import assert_close
 
 pytestmark = pytest.mark.gpu
@@ -68,3 +68,31 @@ def test_27b_long_prefill_32768_full_size(q_block):
     sel = np.random.default_rng(1)
     rows = np.unique(np.concatenate([sel.choice(32768, 40, replace=False), [0, 127, 128, 511, 512, 16383, 32767]]))
     _sampled_check(out, qb, kb, vb, gb, 4, rows, f"32k qL{q_block}")
+
+
+@needs_gpu
+@pytest.mark.parametrize("B,Hq,Hkv,kv_len,rows,dtype", [
+    (1, 16, 2, 131072, 1, "bf16"),   # 128k context: 4096 tiles, the most splits a plan takes
+    (1, 24, 4, 131072, 4, "f16"),
+    (16, 16, 2, 4096, 1, "bf16"),    # a large batch: 32 (b, KV head) groups, fewer splits each
+    (64, 8, 1, 1024, 32, "bf16"),    # the largest batch kv_keep takes, verify-sized rows
+])
+def test_decode_long_context_and_large_batch(B, Hq, Hkv, kv_len, rows, dtype):
+    # decode / verify rows at the end of a long cache or over many batch entries, planned as the
+    # library plans them (splits, head chunks); every output element against the oracle
+    _say("decode size", B, Hq, Hkv, kv_len, rows, dtype)
+    rng = syn.streams(9100 + kv_len // 1024 + B)
+    off = kv_len - rows
+    qb = syn.normal_bits(rng["q"], (B, Hq, rows, 256), dtype)
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, 256), dtype)
+    kb = syn.normal_bits(rng["k"], (B, Hkv, kv_len, 256), dtype)
+    vb = syn.normal_bits(rng["v"], (B, Hkv, kv_len, 256), dtype)
+    q, g, k, v = (to_dev(x, dtype) for x in (qb, gb, kb, vb))
+    a = ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off, kv_len=kv_len, dtype=dtype)
+    plan = ga.describe_plan(a, 1)
+    _say(plan["variant_name"], plan["n_splits"], plan["grid_blocks"])
+    out = ga.decode(q, k, v, g, kv_offset=off, kv_len=kv_len)
+    torch.cuda.synchronize()
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off,
+                              kv_len=kv_len)
+    _say(assert_close(syn.widen(to_bits(out), dtype), ref, f"decode B={B} kv={kv_len} rows={rows}"))
