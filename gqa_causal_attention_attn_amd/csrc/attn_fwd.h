@@ -375,8 +375,10 @@ __device__ __forceinline__ uint32_t lane_fresh() {
 // MFMA row 4 hf + t (+8 a, +16 m) and dims 32 db + 16 (g16 % 2) + 4 u .. + 3, where a, m and
 // db are immediates
 __device__ __forceinline__ uint32_t v_lane_of(uint32_t l) {
-  const uint32_t g16 = l >> 4, tq = (l >> 2) & 3, uq = l & 3, hf = l >> 5;
-  return kTileLds + (4 * tq + hf) * kGroupStride + 16 * (2 * (g16 & 1) + (uq >> 1)) + 8 * (uq & 1);
+  // group 4 tq + hf = (l & 12) + (l >> 5); bytes 32 (g16 % 2) + 16 (uq >> 1) + 8 (uq % 2)
+  const uint32_t grp = (l & 12u) + (l >> 5);
+  const uint32_t lo = ((l & 16u) << 1) | ((l & 2u) << 3) | ((l & 1u) << 3);
+  return kTileLds + __umul24(grp, (uint32_t)kGroupStride) + lo;
 }
 
 // Key (within the tile, less R hf, R = 512 / D rows per group) of element q of S block sb: row
@@ -648,9 +650,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q is in registers before the tile stream starts
   const uint32_t koff = (uint32_t)(lane / kCells) * (uint32_t)p.k_st * 2 + 16 * (lane % kCells);
   const uint32_t voff = (uint32_t)(lane / kCells) * (uint32_t)p.v_st * 2 + 16 * (lane % kCells);
-  // the 8-wavefront shape issues every step's loads, past the last tile too (those read
-  // nothing), so its waits need no tail cases; the others stop at the last tile
-  constexpr bool EARLY = LAG;
+  // the 8-wavefront shapes issue every step's loads, past the last tile too (those read
+  // nothing), so their waits need no tail cases; the 4-wavefront shape stops at the last tile
+  constexpr bool EARLY = W == 8;
   for (int t = 0; t < PF && (EARLY || t < n_kt); ++t) {
     issue_mask(kv_lo + t * kTileKeys, t);
     issue_tile<W, D>(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kTileKeys, kv_end, lds + t * kStageLds, wave, koff,
@@ -676,8 +678,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
   float m0 = -INFINITY, l0 = 0.0f;
 
-  // One step of the tile stream: wait for tile t (issued kPrefetch steps ago), sync, and
-  // start tile t + kPrefetch.  Returns the LDS address of tile t's stage.
+  // One step of the 4-wavefront tile stream: wait for tile t (issued PF steps ago), sync, and
+  // start tile t + PF in one burst.  Returns the LDS address of tile t's stage.
   int stage = 0;
   auto stream_step = [&](int t) {
     // tile t landed for this wavefront once only the tiles issued after it remain in flight
@@ -697,12 +699,13 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   };
 
   // The 8-wavefront stream: after the barrier of tile t the loads of tile t + PF are prepared,
-  // and the S product of tile t issues them one by one between its MFMAs.  Exactly one tile is
-  // in flight beyond the one consumed at every wait.
+  // and the S product of tile t issues them one by one between its MFMAs (a burst of them at
+  // the barrier would hold up the wavefront that issues it).  PF - 1 tiles are in flight beyond
+  // the one consumed at every wait.
   TileDma<W, D> dma;
   dma.koff = koff, dma.voff = voff, dma.kst = (uint32_t)p.k_st, dma.vst = (uint32_t)p.v_st;
   auto sync_step = [&](int t) {
-    wait_tiles_in_flight<W, ML>(1, mwave);
+    wait_tiles_in_flight<W, ML>(PF - 1, mwave);
     __builtin_amdgcn_s_barrier();
     int st2 = stage + PF;
     if (st2 >= kStages) st2 -= kStages;
@@ -932,8 +935,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
   // ---- O^T += V^T P^T over the tile at sb in 8 steps (dim block s / kSB, S block s % kSB);
   // the V operands of step s + 1 are read while the two MFMAs of step s run
-  auto pv = [&](uint32_t sb, const u32x4(&pb0)[kSB], const u32x4(&pb1)[kSB], f32x16(&o)[kDB]) {
-    const uint32_t va = sb + v_lane_of(lane_fresh());
+  auto pv = [&](uint32_t sb, uint32_t vl, const u32x4(&pb0)[kSB], const u32x4(&pb1)[kSB], f32x16(&o)[kDB]) {
+    const uint32_t va = sb + vl;
     u32x4 va4[2][2];
     auto read_v = [&](auto sc_, u32x4(&dst)[2]) {
       constexpr int st = decltype(sc_)::value;
@@ -970,17 +973,18 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // operations on o keep the plain order (scale by alpha_t, then add P_t V_t).
   if constexpr (!LAG) {
     for (int t = 0; t < n_kt; ++t) {
-      const uint32_t sb = stream_step(t);
+      const uint32_t sb = EARLY ? sync_step(t) : stream_step(t);
       const int jb = kv_lo + t * kTileKeys;
       u32x4 pa0[kSB], pa1[kSB];
       float a0;
       f32x16 s0[kSB];
-      scores(sb, q0, no_hook, s0);
+      if constexpr (EARLY) scores(sb, q0, dma_hook, s0);
+      else scores(sb, q0, no_hook, s0);
       mask_any(s0, jb, lim0, mrow0, sb);
       const bool f0 = stats(s0, m0, a0);
       rescale(o0, a0, f0);
       weights(s0, m0, a0, l0, pa0, pa1);
-      pv(sb, pa0, pa1, o0);
+      pv(sb, v_lane_of(lane_fresh()), pa0, pa1, o0);
     }
   } else if (n_kt > 0) {
     u32x4 pa0[kSB], pa1[kSB];
@@ -1002,15 +1006,19 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       // o still owes tile t - 1's alpha: keep it until its P.V is issued
       const float a_prev = a0;
       const bool f_prev = f0;
+      // the lane's V read address is worked out while the S product drains (pinned here, ahead
+      // of the max's branch, instead of sinking to the head of P.V)
+      uint32_t vl = v_lane_of(lane_fresh());
+      asm volatile("" : "+v"(vl));
       f0 = stats(s0, m0, a0);
       rescale(o0, a_prev, f_prev);
       __builtin_amdgcn_sched_barrier(0);
-      pv(sprev, pa0, pa1, o0);
+      pv(sprev, vl, pa0, pa1, o0);
       weights(s0, m0, a0, l0, pa0, pa1);
       sprev = sb;
     }
     rescale(o0, a0, f0);
-    pv(sprev, pa0, pa1, o0);
+    pv(sprev, v_lane_of(lane_fresh()), pa0, pa1, o0);
   }
   // the loads past the last tile have landed before the workgroup's LDS is given up
   if constexpr (EARLY) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
