@@ -637,27 +637,38 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   };
 
   // ---- Q of this lane's pairs, in the B-operand order: element t of q*[kk] is dim
-  // 16 kk + 8 hf + t
+  // 16 kk + 8 hf + t.  A lane without a pair loads row 0 of the group's first head instead
+  // (in range, finite): its S column only feeds a P.V column that is never stored.  All 16
+  // loads go out unconditionally, back to back (a per-load branch on the lane's validity
+  // would split them and wait on some before issuing the rest).
   u32x4 q0[kKSteps];
-  {
-    const uint16_t* qa = p.q + (int64_t)b * p.q_sb + (int64_t)h0 * p.q_sh + (int64_t)r0 * p.q_sr + 8 * hf;
+  if (act0) {
+    const int hq = valid0 ? h0 : g * p.G, rq = valid0 ? r0 : 0;
+    const uint16_t* qa = p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + (int64_t)rq * p.q_sr + 8 * hf;
 #pragma unroll
-    for (int kk = 0; kk < kKSteps; ++kk) {
-      q0[kk] = valid0 ? *reinterpret_cast<const u32x4*>(qa + 16 * kk) : (u32x4){0u, 0u, 0u, 0u};
-    }
+    for (int kk = 0; kk < kKSteps; ++kk) q0[kk] = *reinterpret_cast<const u32x4*>(qa + 16 * kk);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) q0[kk] = (u32x4){0u, 0u, 0u, 0u};
   }
   const int64_t mrow0 = MK ? (int64_t)b * p.m_sb + (int64_t)h0 * p.m_sh + (int64_t)r0 * p.m_sr : 0;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // Q is in registers before the tile stream starts
+  // the first tiles are issued right behind Q, so that the two round trips overlap; Q is
+  // older than every tile load, so each wait for a tile covers it as well
   const uint32_t koff = (uint32_t)(lane / kCells) * (uint32_t)p.k_st * 2 + 16 * (lane % kCells);
   const uint32_t voff = (uint32_t)(lane / kCells) * (uint32_t)p.v_st * 2 + 16 * (lane % kCells);
-  // the 8-wavefront shapes issue every step's loads, past the last tile too (those read
-  // nothing), so their waits need no tail cases; the 4-wavefront shape stops at the last tile
-  constexpr bool EARLY = W == 8;
-  for (int t = 0; t < PF && (EARLY || t < n_kt); ++t) {
+  // Every shape issues PF tiles up front and every step's loads, past the last tile too (those
+  // read nothing), so the number of loads in flight is the same at every wait and the waits
+  // need no tail cases.
+  static_for<PF>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
     issue_mask(kv_lo + t * kTileKeys, t);
     issue_tile<W, D>(kbase, vbase, p.k_st, p.v_st, kv_lo + t * kTileKeys, kv_end, lds + t * kStageLds, wave, koff,
                      voff);
-  }
+  });
+  // a use of Q right behind those loads: the compiler's wait for Q then counts them as still
+  // in flight (left to the tile loop, it would wait for every load before entering it)
+#pragma unroll
+  for (int kk = 0; kk < kKSteps; ++kk) asm volatile("" ::"v"(q0[kk]));
 
   // per-lane LDS byte addresses (see the layout above); every read adds a compile-time offset.
   // MFMA row r of S block sb holds key R gamma(r % 16) + 2 sb + r / 16 with gamma(x) =
@@ -683,16 +694,14 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   int stage = 0;
   auto stream_step = [&](int t) {
     // tile t landed for this wavefront once only the tiles issued after it remain in flight
-    wait_tiles_in_flight<W, ML>(min(PF - 1, n_kt - 1 - t), mwave);
-    // ... and for everyone; everyone is done with tile t - 2, whose stage is refilled next
+    wait_tiles_in_flight<W, ML>(PF - 1, mwave);
+    // ... and for everyone; everyone is done with tile t - 1, whose stage is refilled next
     __builtin_amdgcn_s_barrier();
-    if (t + PF < n_kt) {
-      int st2 = stage + PF;
-      if (st2 >= kStages) st2 -= kStages;
-      issue_mask(kv_lo + (t + PF) * kTileKeys, st2);
-      issue_tile<W, D>(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + PF) * kTileKeys, kv_end, lds + st2 * kStageLds,
-                       wave, koff, voff);
-    }
+    int st2 = stage + PF;
+    if (st2 >= kStages) st2 -= kStages;
+    issue_mask(kv_lo + (t + PF) * kTileKeys, st2);
+    issue_tile<W, D>(kbase, vbase, p.k_st, p.v_st, kv_lo + (t + PF) * kTileKeys, kv_end, lds + st2 * kStageLds, wave,
+                     koff, voff);
     const uint32_t sb = lds0 + stage * kStageLds;
     stage = stage + 1 == kStages ? 0 : stage + 1;
     return sb;
@@ -724,15 +733,15 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
   if (!act0) {
     // a wavefront without pairs only helps stream the tiles
-    if constexpr (EARLY) {
+    if constexpr (W == 8) {
       for (int t = 0; t < n_kt; ++t) {
         sync_step(t);
         static_for<TileDma<W, D>::kLoads>([&](auto ic) { dma.template issue<decltype(ic)::value>(); });
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
       for (int t = 0; t < n_kt; ++t) stream_step(t);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     return;
   }
 
@@ -973,12 +982,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // operations on o keep the plain order (scale by alpha_t, then add P_t V_t).
   if constexpr (!LAG) {
     for (int t = 0; t < n_kt; ++t) {
-      const uint32_t sb = EARLY ? sync_step(t) : stream_step(t);
+      const uint32_t sb = W == 8 ? sync_step(t) : stream_step(t);
       const int jb = kv_lo + t * kTileKeys;
       u32x4 pa0[kSB], pa1[kSB];
       float a0;
       f32x16 s0[kSB];
-      if constexpr (EARLY) scores(sb, q0, dma_hook, s0);
+      if constexpr (W == 8) scores(sb, q0, dma_hook, s0);
       else scores(sb, q0, no_hook, s0);
       mask_any(s0, jb, lim0, mrow0, sb);
       const bool f0 = stats(s0, m0, a0);
@@ -1021,7 +1030,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     pv(sprev, v_lane_of(lane_fresh()), pa0, pa1, o0);
   }
   // the loads past the last tile have landed before the workgroup's LDS is given up
-  if constexpr (EARLY) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: element q of o*[db] is dim 32 db + 8 (q / 4) + 4 hf + (q % 4)
   const float lt0 = sum_halves(l0);
