@@ -32,7 +32,8 @@ struct Plan {
   int blocks_per_chunk;
   int shape;     // 0: 4 wavefronts of one column block each; 2: 8 wavefronts, P.V one tile behind
                  // (prompts); 3: 8 wavefronts without the lag (decode / verify); 1 is not used
-  int mask_lds;  // the main pass stages each tile's mask window in LDS: 0 no, 1 rows, 2 words
+  int mask_lds;  // the main pass stages each tile's mask window in LDS: 0 no, 1 rows, 2 words,
+                 // 3 words of the (head, row) pairs' rows (a full-head mask)
   int waves;     // wavefronts per workgroup
   int n_tiles;
   int n_splits;
@@ -186,9 +187,11 @@ int make_plan(const attn_args* a, int op, Plan* P) {
     const int64_t msb = m.Bm == 1 ? 0 : m.stride_b;
     const int64_t span = ((int64_t)(m.Bm - 1) * msb + (int64_t)(a->rows - 1) * m.stride_row + a->kv_len) * esz;
     int64_t window = 0;  // most mask rows any workgroup's pairs cover
+    int64_t pair_window = 0;  // most pairs of any workgroup; INT64_MAX when one has two blocks
     const int wg_blocks = P->waves;
     for (int t = 0; t < P->n_tiles; ++t) {
       int64_t lo = INT64_MAX, hi = -1;
+      int blocks_with_pairs = 0;
       for (int bj = t * wg_blocks; bj < (t + 1) * wg_blocks; ++bj) {
         const int cj = bj / P->blocks_per_chunk;
         const int64_t f0 = (int64_t)(bj - cj * P->blocks_per_chunk) * kPairsPerBlock;
@@ -200,8 +203,11 @@ int make_plan(const attn_args* a, int op, Plan* P) {
         const int64_t last = (f0 + kPairsPerBlock < npairs ? f0 + kPairsPerBlock : npairs) - 1;
         lo = f0 / csj < lo ? f0 / csj : lo;
         hi = last / csj > hi ? last / csj : hi;
+        ++blocks_with_pairs;
+        if (last - f0 + 1 > pair_window) pair_window = last - f0 + 1;
       }
       if (hi >= 0 && hi - lo + 1 > window) window = hi - lo + 1;
+      if (blocks_with_pairs > 1) pair_window = INT64_MAX;
     }
     const bool base = m.Hm == 1 && span < ((int64_t)1 << 31);
     const int64_t word_rows = 1024 / T;
@@ -211,7 +217,14 @@ int make_plan(const attn_args* a, int op, Plan* P) {
                         (m.stride_row * esz) % 16 == 0 &&
                         (msb * esz) % 16 == 0 && ((int64_t)a->kv_len * esz) % 16 == 0 &&
                         window <= 4096 / (kKeysPerTile * esz);
-    P->mask_lds = words ? 2 : rows16 ? 1 : 0;
+    // a full-head mask: one dword per key of each pair's own mask row, when every workgroup's
+    // pairs form one column block of at most 1024 / T pairs
+    const int64_t msh = m.Hm == 1 ? 0 : m.stride_h;
+    const int64_t head_span = ((int64_t)(a->Hq - 1) * msh + (int64_t)(a->rows - 1) * m.stride_row + a->kv_len) * esz;
+    const bool pair_words = m.Hm == a->Hq && m.Hm > 1 && pair_window <= word_rows &&
+                            (int64_t)(m.Bm - 1) * msb * esz + head_span < ((int64_t)1 << 31) &&
+                            head_span + T * esz < ((int64_t)1 << 31);
+    P->mask_lds = words ? 2 : pair_words ? 3 : rows16 ? 1 : 0;
   }
   P->grid = (int64_t)a->B * a->Hkv * S * P->n_tiles;
   if (P->grid > INT32_MAX || !gqa::grid_fits(P->grid, 64 * P->waves)) return ATTN_E_ARG;
@@ -226,10 +239,10 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   return ATTN_OK;
 }
 
-// id = mask layout * 32 + shape * 8 + dtype * 4 + mask kind; head dims 64 / 128: 96 / 97
+// id = head-dim slot * 128 + mask layout * 32 + shape * 8 + dtype * 4 + mask kind
 inline int variant_of(const attn_args* a, const Plan& P) {
   const int dslot = a->D == 256 ? 0 : a->D == 128 ? 1 : 2;
-  return dslot * 96 + P.mask_lds * 32 + P.shape * 8 + a->dtype * 4 + a->mask.kind;
+  return dslot * 128 + P.mask_lds * 32 + P.shape * 8 + a->dtype * 4 + a->mask.kind;
 }
 
 int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream, bool merge = true,
@@ -259,7 +272,8 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
     p.m_sb = a->mask.Bm == 1 ? 0 : a->mask.stride_b;  // an extent of 1 broadcasts
     p.m_sh = a->mask.Hm == 1 ? 0 : a->mask.stride_h;
     p.m_sr = a->mask.stride_row;
-    p.mask_lds = P.mask_lds;
+    p.mask_lds = P.mask_lds == 3 ? 2 : P.mask_lds;  // the word kernels, with per-pair window rows
+    p.mask_pairs = P.mask_lds == 3;
   }
   p.kv_offset = (int)a->kv_offset;
   p.kv_len = (int)a->kv_len;
@@ -344,16 +358,16 @@ const char* attn_strerror(int status) {
 }
 
 const char* attn_variant_name(int variant) {
-  // id = head-dim slot (256, 128, 64) * 96 + mask layout in LDS * 32 + shape * 8 + dtype * 4 +
+  // id = head-dim slot (256, 128, 64) * 128 + mask layout in LDS * 32 + shape * 8 + dtype * 4 +
   // mask kind (see variant_of); ids of variants that do not exist name "unknown"
   static const std::vector<std::string> names = [] {
-    std::vector<std::string> v(3 * 96);
+    std::vector<std::string> v(3 * 128);
     static const char* const kinds[4] = {"", "_maskbool", "_maskadd", "_maskf32"};
     static const char* const shapes[4] = {"_4x1", "", "_8x1", "_8x1_stream"};
-    static const char* const layouts[3] = {"", "_ldsrows", "_ldswords"};
+    static const char* const layouts[4] = {"", "_ldsrows", "_ldswords", "_ldspairwords"};
     static const char* const dims[3] = {"", "_d128", "_d64"};
-    for (int id = 0; id < 3 * 96; ++id) {
-      const int dslot = id / 96, r = id % 96, ml = r / 32, shape = (r / 8) % 4, dtype = (r / 4) % 2, kind = r % 4;
+    for (int id = 0; id < 3 * 128; ++id) {
+      const int dslot = id / 128, r = id % 128, ml = r / 32, shape = (r / 8) % 4, dtype = (r / 4) % 2, kind = r % 4;
       if (shape == 1 || (ml != 0 && kind == 0) || (ml == 1 && (shape != 2 || dslot != 0))) continue;
       v[id] = std::string("fwd_mfma32x32x16_") + (dtype ? "f16" : "bf16") + kinds[kind] + shapes[shape] + layouts[ml] +
               dims[dslot];

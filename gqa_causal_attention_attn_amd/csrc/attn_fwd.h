@@ -558,6 +558,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // ---- key range of the workgroup [kv_lo, kv_end) and the smallest bound of its pairs, from
   // the pair layout of its column blocks (uniform arithmetic)
   int kv_hi = 0, lim_min = 0x7fffffff, r_lo = 0x7fffffff, r_hi = 0;
+  // the (last) column block with pairs: first pair, first head and heads of its chunk, pairs
+  int pb_f0 = 0, pb_hs = 0, pb_cs = 1, pb_np = 0;
   for (int bj = tile * kGroupBlocks; bj < (tile + 1) * kGroupBlocks; ++bj) {
     const int cj = bj / p.blocks_per_chunk;
     const int f0 = (bj - cj * p.blocks_per_chunk) * kPairsPerBlock;
@@ -570,6 +572,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     lim_min = min(lim_min, lim_of(f0 / csj));
     r_lo = min(r_lo, f0 / csj);
     r_hi = max(r_hi, (min(f0 + kPairsPerBlock, npairs) - 1) / csj);
+    pb_f0 = f0, pb_hs = hs, pb_cs = csj, pb_np = min(kPairsPerBlock, npairs - f0);
   }
   const int kv_lo = split * p.keys_per_split;
   const int kv_end = __builtin_amdgcn_readfirstlane(min(kv_lo + p.keys_per_split, kv_hi));
@@ -580,7 +583,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   const uint16_t* vbase = p.v + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
 
   // ---- the mask in LDS (ML > 0: the mask is the same for every head and the workgroup's rows
-  // r_lo .. r_hi fit a mask stage, which the host checked).  ML = 1 (head dim 256): the 32-key
+  // r_lo .. r_hi fit a mask stage, or, with p.mask_pairs, the mask has a row per head and the
+  // workgroup's pairs form one column block of at most 1024 / T pairs; the host checked).  ML = 1 (head dim 256): the 32-key
   // window of those rows for each tile in 16-byte chunks (wavefronts 0-3 load 1 KiB each: stage
   // byte 1024 w + 16 l is byte (1024 w + 16 l) % kMaskRowBytes of window row (1024 w + 16 l) /
   // kMaskRowBytes).  ML = 2: one dword per key of the tile's window of 1024 / T rows of T keys;
@@ -605,7 +609,10 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   };
   static_assert(ML != 2 || kMaskRows * kTileKeys == 1024, "16 loads of 64 words a tile");
   const bool mwave = ML == 1 && wave < 4;  // ML = 1: this wavefront issues a mask load per tile
-  const int mbytes = ML ? (int)(((int64_t)(p.rows - 1) * p.m_sr + p.kv_len) * kMaskEsz) : 0;
+  const int mbytes =
+      ML ? (int)(((p.mask_pairs ? (int64_t)(p.Hq - 1) * p.m_sh : 0) + (int64_t)(p.rows - 1) * p.m_sr + p.kv_len) *
+                 kMaskEsz)
+         : 0;
   const __amdgpu_buffer_rsrc_t mrs =
       buffer_rsrc(static_cast<const uint8_t*>(p.mask) + (ML ? (int64_t)b * p.m_sb * kMaskEsz : 0), mbytes);
   const uint32_t mpos = (uint32_t)(wave * 1024 + lane * 16);
@@ -615,9 +622,14 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 #pragma unroll
   for (int i = 0; i < (ML == 2 ? kWordLoads : 1); ++i) {
     const int f = 64 * (wave * kWordLoads + i) + lane;
-    mwoff[i] = ML == 2 ? ((uint32_t)(r_lo + f / kTileKeys) * (uint32_t)p.m_sr + (uint32_t)(f % kTileKeys)) *
-                             (uint32_t)kMaskEsz
-                       : 0u;
+    uint32_t row_off = (uint32_t)(r_lo + f / kTileKeys) * (uint32_t)p.m_sr;
+    if (p.mask_pairs) {
+      // window row w: pair w of the column block (rows past its pairs repeat pair 0's row)
+      const int w = f / kTileKeys;
+      const int fp = pb_f0 + (w < pb_np ? w : 0);
+      row_off = (uint32_t)(g * p.G + pb_hs + fp % pb_cs) * (uint32_t)p.m_sh + (uint32_t)(fp / pb_cs) * (uint32_t)p.m_sr;
+    }
+    mwoff[i] = ML == 2 ? (row_off + (uint32_t)(f % kTileKeys)) * (uint32_t)kMaskEsz : 0u;
   }
   auto issue_mask = [&](int j0, int st) {
     if constexpr (ML == 1) {
@@ -814,7 +826,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // of keys q and q + 8 are adjacent, one read each.
   auto mask_lds_apply = [&](f32x16(&sc)[kSB], int jb, int lim, uint32_t sb) {
     if constexpr (ML != 0) {
-      const int rho = min(max(r0 - r_lo, 0), kMaskRows - 1);
+      // window row of this lane's pair: its query row, or (per-pair windows) its pair slot
+      const int rho = p.mask_pairs ? min(li, kMaskRows - 1) : min(max(r0 - r_lo, 0), kMaskRows - 1);
       const uint32_t mst = lds0 + kFwdLdsBytes + ((sb - lds0) / kStageLds) * kMaskStageLds;
       static_for<kSB>([&](auto ic) {
         constexpr int i = decltype(ic)::value;

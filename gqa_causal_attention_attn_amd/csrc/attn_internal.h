@@ -62,7 +62,10 @@ struct FwdParams {
   int keys_per_split;    // multiple of kKeysPerTile
   int grid;              // workgroups in the launch
   int mask_lds;          // mask window of each tile staged in LDS: 0 no (per-lane loads), 1 in
-                         // 16-byte row chunks, 2 one dword per key (see attn_fwd.hip)
+                         // 16-byte row chunks, 2 one dword per key (see attn_fwd.h)
+  int mask_pairs;        // with mask_lds 2: the window's rows are the mask rows of the workgroup's
+                         // (head, row) pairs (a full-head mask, one column block of pairs)
+                         // instead of its query rows (a mask the same for every head)
 };
 
 // The main pass's inputs, handed to the merge so that it can compute a chunk partial again

@@ -233,7 +233,11 @@ size_t attn_struct_size(int which);
 /* Static description of a status code.  Never NULL. */
 const char* attn_strerror(int status);
 
-/* Name of a kernel variant id from attn_plan_info.variant.  Never NULL. */
+/* Name of a kernel variant id from attn_plan_info.variant ("unknown" for an id no variant has).
+ * Never NULL.  The name lists the dtype, the mask kind, the shape (4x1, 8x1, 8x1_stream), how
+ * the mask reaches the main pass (nothing: per-lane loads; _ldsrows / _ldswords: staged in LDS
+ * with each K/V tile from a mask the same for every head; _ldspairwords: the same from a
+ * full-head mask, when each workgroup's pairs form one column block) and the head dim. */
 const char* attn_variant_name(int variant);
 
 /* The head-chunk rule of "Qwen head-chunked SDPA (#113)" (introduction; "Exact scope found

@@ -409,3 +409,41 @@ def test_probe_library_exports_every_declared_symbol():
     lib = C.CDLL(gbuild.PROBES_LIB)
     for name in declared:
         assert hasattr(lib, name), name
+
+
+def test_full_head_mask_window_choice():
+    # A full-head mask (a row per query head) is staged in LDS one dword per key of each pair's
+    # own row only when every workgroup holds one column block of at most 1024 / T pairs (T keys
+    # per tile: 32 pairs at head dim 256, 16 at 128, 8 at 64); otherwise each lane loads its words.
+    # A mask the same for every head keeps the word window of its query rows.
+    cases = [  # rows, Hq, Hkv, Hm, D, head_chunk, expected layout marker
+        (1, 16, 2, 16, 256, 0, "_ldspairwords"),
+        (4, 16, 2, 16, 256, 0, "_ldspairwords"),   # 8 heads x 4 rows = 32 pairs
+        (5, 24, 4, 24, 256, 0, "_ldspairwords"),   # 6 x 5 = 30
+        (6, 16, 2, 16, 256, 0, None),              # chunks [5, 3]: two blocks
+        (4, 16, 2, 16, 256, 4, None),              # forced chunks of 4 heads: two blocks
+        (32, 16, 2, 16, 256, 0, None),             # eight blocks
+        (2, 16, 2, 16, 128, 0, "_ldspairwords"),   # 16 pairs at head dim 128
+        (4, 16, 2, 16, 128, 0, None),              # 32 pairs > 16
+        (1, 16, 2, 16, 64, 0, "_ldspairwords"),    # 8 pairs at head dim 64
+        (2, 16, 2, 16, 64, 0, None),               # 16 pairs > 8
+        (4, 16, 2, 1, 256, 0, "_ldswords"),        # broadcast over heads
+    ]
+    for rows, Hq, Hkv, Hm, D, hc, marker in cases:
+        for mk in (_abi.MASK_BOOL_U8, _abi.MASK_ADD, _abi.MASK_ADD_F32):
+            a = ga.plan_args(B=2, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=32768, mask_kind=mk, Hm=Hm, D=D,
+                             head_chunk=hc)
+            name = ga.describe_plan(a, _abi.OP_DECODE)["variant_name"]
+            if marker:
+                assert marker in name, (rows, Hq, Hkv, Hm, D, hc, name)
+            else:
+                assert "lds" not in name, (rows, Hq, Hkv, Hm, D, hc, name)
+    # every variant id the library names decodes to its own name, and the per-pair layout exists
+    # for every shape at every head dim
+    lib = ga.lib()
+    names = [lib.attn_variant_name(i).decode() for i in range(3 * 128)]
+    known = [n for n in names if n != "unknown"]
+    assert len(known) == len(set(known))
+    for shape in ("_4x1", "_8x1", "_8x1_stream"):
+        for dim in ("", "_d128", "_d64"):
+            assert f"fwd_mfma32x32x16_bf16_maskadd{shape}_ldspairwords{dim}" in known

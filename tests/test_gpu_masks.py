@@ -9,6 +9,10 @@ staged in LDS beside each K/V tile as one dword per key or as 16-byte row chunks
 loads), which must give the same bits, on the four-wavefront decode shape and the eight-wavefront
 verify and prompt shapes, with one KV split (the gated output written by the main pass) and with
 the planned splits (partials and the merge), in bf16 and fp16, against the float64 oracle.
+
+A full-head mask (a row per query head) whose workgroups hold a single column block of pairs
+stages each pair's own mask row in the same word window; it must match the oracle, the per-lane
+loads of the same mask and, for a mask the same for every head, that mask's own word window.
 """
 
 import numpy as np
@@ -169,3 +173,68 @@ def test_nonfinite_repair_under_mask_values(dtype, n_splits, kind):
         res = compare(syn.widen(to_bits(out), dtype), ref)
         _say("head_chunk", hc, res)
         assert res["ok"], res
+
+
+# Full-head masks (a row per query head) whose workgroups hold one column block of at most
+# 1024 / T pairs (T keys per tile: 32 pairs at head dim 256, 16 at 128, 8 at 64) stage each pair's
+# own mask row beside the K/V tiles, one dword per key.  (B, Hq, Hkv, rows, kv_offset, D, Bm)
+PAIR_CASES = [
+    (2, 16, 2, 1, 4096, 256, 1),    # 8 pairs
+    (2, 16, 2, 4, 32768, 256, 2),   # 32 pairs, 61 KV splits, a mask per batch entry
+    (1, 24, 4, 5, 4091, 256, 1),    # 30 pairs (6 heads x 5 rows)
+    (2, 16, 2, 2, 4094, 128, 1),    # 16 pairs at head dim 128
+    (1, 16, 2, 1, 2047, 64, 1),     # 8 pairs at head dim 64
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("kind", ["bool", "add", "add_f32"])
+@pytest.mark.parametrize("case", range(len(PAIR_CASES)),
+                         ids=[f"B{c[0]}_{c[1]}x{c[2]}_r{c[3]}_D{c[5]}" for c in PAIR_CASES])
+def test_full_head_mask_pair_windows(case, kind, dtype):
+    B, Hq, Hkv, rows, off, D, Bm = PAIR_CASES[case]
+    _say("pair windows", PAIR_CASES[case], kind, dtype)
+    kv = off + rows
+    rng = syn.streams(5400 + 10 * case)
+    qb, gb = (syn.normal_bits(rng[n], (B, Hq, rows, D), dtype) for n in ("q", "gate"))
+    kb, vb = (syn.normal_bits(rng[n], (B, Hkv, kv, D), dtype) for n in ("k", "v"))
+    values = "zero" if kind == "bool" else "normal"
+    mb = syn.verify_mask(rng["mask"], rows=rows, kv_offset=off, heads=Hq, kind=kind, dtype=dtype, values=values,
+                         batch=Bm)
+    q, k, v, g = (to_dev(x, dtype) for x in (qb, kb, vb, gb))
+
+    def dev_mask(x):
+        return to_dev(x, dtype) if kind == "add" else torch.from_numpy(x).cuda()
+
+    def plan_name(m, head_chunk=0):
+        a = ga._args(q, k, v, g, torch.empty_like(q), kv_offset=off, kv_len=kv, causal=True, scale=0.0,
+                     head_chunk=head_chunk, n_splits=0, mask=m)
+        return ga.describe_plan(a, ga._abi.OP_DECODE)["variant_name"]
+
+    m = dev_mask(mb)
+    assert "_ldspairwords" in plan_name(m), plan_name(m)
+    out = ga.decode(q, k, v, g, kv_offset=off, mask=m)
+    # two head chunks put the pairs in two column blocks: the per-lane mask loads, the same bits
+    hc = (Hq // Hkv) // 2
+    assert "lds" not in plan_name(m, hc), plan_name(m, hc)
+    lane = ga.decode(q, k, v, g, kv_offset=off, mask=m, head_chunk=hc)
+    assert torch.equal(lane.view(torch.int16), out.view(torch.int16)), "pair window and per-lane loads differ"
+    if kind == "add":
+        mref, mk = syn.widen(mb, dtype), "add"
+    elif kind == "bool":
+        mref, mk = mb.astype(bool), "bool"
+    else:
+        mref, mk = mb.astype(np.float64), "add"
+    ref = reference.attention(*(syn.widen(x, dtype) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off,
+                              kv_len=kv, mask=mref, mask_kind=mk)
+    _say(assert_close(syn.widen(to_bits(out), dtype), ref, f"pair windows {case} {kind}"))
+    # a mask the same for every head: its own word window and its full-head copy give the same bits
+    mb1 = syn.verify_mask(rng["mask"], rows=rows, kv_offset=off, heads=1, kind=kind, dtype=dtype, values=values,
+                          batch=Bm)
+    m1 = dev_mask(mb1)
+    full = m1.expand(Bm, Hq, rows, kv).contiguous()
+    assert "_ldswords" in plan_name(m1) and "_ldspairwords" in plan_name(full)
+    one = ga.decode(q, k, v, g, kv_offset=off, mask=m1)
+    per_head = ga.decode(q, k, v, g, kv_offset=off, mask=full)
+    assert torch.equal(one.view(torch.int16), per_head.view(torch.int16)), "broadcast and full-head copy differ"
