@@ -155,14 +155,14 @@ class Plans:
         self.samples = []
 
     def check(self, name, *, op, B, Hq, Hkv, rows, kv_offset, D=256, dtype="bf16", mask_kind=0, head_chunk=0,
-              n_splits=0, workspace=None):
+              n_splits=0, workspace=None, Hm=1):
         ga = self.ga
         a = ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=kv_offset, D=D, dtype=dtype, mask_kind=mask_kind,
-                         head_chunk=head_chunk, n_splits=n_splits)
+                         head_chunk=head_chunk, n_splits=n_splits, Hm=Hm)
         d = ga.describe_plan(a, op)
         req = {"op": {0: "prefill", 1: "decode"}[op], "B": B, "Hq": Hq, "Hkv": Hkv, "rows": rows,
                "kv_offset": kv_offset, "head_dim": D, "dtype": dtype,
-               "mask": {0: "none", 1: "bool", 2: "add16", 3: "add32"}[mask_kind],
+               "mask": {0: "none", 1: "bool", 2: "add16", 3: "add32"}[mask_kind], "mask_heads": Hm,
                "head_chunk": "policy" if head_chunk == 0 else head_chunk,
                "n_splits": "auto" if n_splits == 0 else n_splits}
         res = {k: d[k] for k in self.KEYS}
@@ -329,9 +329,12 @@ def main():
         """Distinct caches (>= 1 GiB together, so the 256 MB Infinity Cache cannot hold them) and
         the inputs of the rows 1..32 of this workload."""
 
-        def __init__(self, seed, B_, Hq_, Hkv_, off, rows_max, dtype, masked):
+        def __init__(self, seed, B_, Hq_, Hkv_, off, rows_max, dtype, masked, mask_heads=1, mask_kind="add"):
             r = syn.streams(seed)
             self.B, self.Hq, self.Hkv, self.off, self.dtype, self.masked = B_, Hq_, Hkv_, off, dtype, masked
+            self.mask_heads, self.mask_kind = mask_heads, mask_kind
+            self.tag = "" if not masked or (mask_heads == 1 and mask_kind == "add") else (
+                ("_full_head" if mask_heads > 1 else "") + ("_bool" if mask_kind == "bool" else ""))
             cap = off + rows_max
             cache_bytes = 2 * B_ * Hkv_ * cap * 256 * 2
             self.n_rot = max(2, int(np.ceil(4 * MALL_BYTES / cache_bytes)))
@@ -352,11 +355,14 @@ def main():
             if rows in self.out:
                 return self.plans[rows]
             if self.masked:
-                mb = syn.verify_mask(self.mrng, rows=rows, kv_offset=self.off, heads=1, kind="add", dtype=self.dtype)
-                self.mask[rows] = _up(mb, dev, self.dtype)
+                mb = syn.verify_mask(self.mrng, rows=rows, kv_offset=self.off, heads=self.mask_heads,
+                                     kind=self.mask_kind, dtype=self.dtype)
+                self.mask[rows] = (_up(mb, dev, self.dtype) if self.mask_kind == "add"
+                                   else torch.from_numpy(mb).to(dev))
             self.out[rows] = torch.empty((self.B, self.Hq, rows, 256), dtype=self.q.dtype, device=dev)
+            mk = 0 if not self.masked else 2 if self.mask_kind == "add" else 1
             res = plans.check(name, op=1, B=self.B, Hq=self.Hq, Hkv=self.Hkv, rows=rows, kv_offset=self.off,
-                              dtype=self.dtype, mask_kind=2 if self.masked else 0)
+                              dtype=self.dtype, mask_kind=mk, Hm=self.mask_heads)
             self.ws[rows] = torch.empty(max(res["workspace_bytes"], 16), dtype=torch.uint8, device=dev)
             self.plans[rows] = res
             return res
@@ -370,7 +376,7 @@ def main():
 
         def bytes(self, rows):
             kv = self.off + rows
-            mask = rows * kv * 2 if self.masked else 0
+            mask = self.mask_heads * rows * kv * (2 if self.mask_kind == "add" else 1) if self.masked else 0
             return 2.0 * self.B * self.Hkv * kv * 256 * 2 + 3.0 * self.B * self.Hq * rows * 256 * 2 + mask
 
     need_dec = args.only in (None, "decode", "verify")
@@ -489,7 +495,7 @@ def main():
 
     # ---- the decode workload, device-timed (48 calls a batch), cold and MALL-warm
     def dec_figures(ds, rows, warm=True, append=True):
-        plan = ds.prep(rows, f"decode_{ds.B}x{ds.Hq}/{ds.Hkv}_off{ds.off}_rows{rows}_{ds.dtype}")
+        plan = ds.prep(rows, f"decode_{ds.B}x{ds.Hq}/{ds.Hkv}_off{ds.off}_rows{rows}_{ds.dtype}{ds.tag}")
         cold_ms = timer.time(lambda i: ds.call(rows, i), 48)
         r = {"us": round(cold_ms * 1e3, 2), "gbs": round(ds.bytes(rows) / (cold_ms * 1e-3) / 1e9, 1),
              "frac_of_hbm": round(ds.bytes(rows) / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -518,6 +524,15 @@ def main():
         dec_matrix["bf16_offset_4097"] = {f"rows_{rows}": dec_figures(oset, rows, warm=False, append=False)
                                           for rows in (1, 32)}
         del oset
+        # the same workload under a full-head additive mask [1, 16, rows, kv] and a bool mask
+        hset = DecodeSet(1034, 2, 16, 2, 32768, 32, "bf16", True, mask_heads=16)
+        dec_matrix["bf16_full_head_mask"] = {f"rows_{rows}": dec_figures(hset, rows, warm=False, append=False)
+                                             for rows in (1, 4, 32)}
+        del hset
+        bset = DecodeSet(1044, 2, 16, 2, 32768, 32, "bf16", True, mask_kind="bool")
+        dec_matrix["bf16_bool_mask"] = {f"rows_{rows}": dec_figures(bset, rows, warm=False, append=False)
+                                        for rows in (1, 32)}
+        del bset
         # [1] the 27B decode at 4096: rows 1 and 4, no mask, cold and MALL-warm
         kset = DecodeSet(1001, 1, 24, 4, 4096, 4, "bf16", False)
         extras["decode_27b_off4096"] = {f"rows_{rows}": dec_figures(kset, rows) for rows in (1, 4)}
