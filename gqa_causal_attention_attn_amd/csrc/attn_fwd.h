@@ -791,6 +791,34 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     else if constexpr (MK == 2) return __builtin_fmaf(s, p.scale, lo16<DT>(w));
     else return __builtin_fmaf(s, p.scale, __builtin_bit_cast(float, w));
   };
+  // Per-lane mask words (no window in LDS): the word of each of the lane's keys, every load
+  // unconditional (a key past the pair's bound reads the pair's key 0 instead, in range, and is
+  // hidden by mask_words_apply), so the 16 loads go out together and are waited for once.
+  auto mask_fetch = [&](uint32_t(&w)[kSB][16], int jb, int lim, int64_t mrow) {
+    const int jl = jb + kRpg * hf;
+    static_for<kSB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int j = jl + key_of<D>(q, i);
+        const int64_t at = mrow + (j < lim ? j : 0);
+        if constexpr (MK == 1) w[i][q] = static_cast<const uint8_t*>(p.mask)[at];
+        else if constexpr (MK == 2) w[i][q] = static_cast<const uint16_t*>(p.mask)[at];
+        else w[i][q] = __builtin_bit_cast(uint32_t, static_cast<const float*>(p.mask)[at]);
+      }
+    });
+  };
+  auto mask_words_apply = [&](f32x16(&sc)[kSB], const uint32_t(&w)[kSB][16], int jb, int lim) {
+    const int jl = jb + kRpg * hf;
+    static_for<kSB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int j = jl + key_of<D>(q, i);
+        sc[i][q] = j < lim ? add_mask(sc[i][q], w[i][q]) : -INFINITY;
+      }
+    });
+  };
   auto mask_scores = [&](f32x16(&sc)[kSB], int jb, int lim, int64_t mrow) {
     if constexpr (MK == 0) {
       if (jb + kTileKeys > lim_min) {
@@ -804,21 +832,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
         });
       }
     } else {
-      // the mask word of key j is read only for keys the pair may see (row ends at kv_len)
-      auto word = [&](int j) {
-        if constexpr (MK == 1) return (uint32_t) static_cast<const uint8_t*>(p.mask)[mrow + j];
-        else if constexpr (MK == 2) return (uint32_t) static_cast<const uint16_t*>(p.mask)[mrow + j];
-        else return __builtin_bit_cast(uint32_t, static_cast<const float*>(p.mask)[mrow + j]);
-      };
-      const int jl = jb + kRpg * hf;
-      static_for<kSB>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int j = jl + key_of<D>(q, i);
-          sc[i][q] = j < lim ? add_mask(sc[i][q], word(j)) : -INFINITY;
-        }
-      });
+      uint32_t w[kSB][16];
+      mask_fetch(w, jb, lim, mrow);
+      mask_words_apply(sc, w, jb, lim);
     }
   };
 
@@ -1000,9 +1016,19 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       u32x4 pa0[kSB], pa1[kSB];
       float a0;
       f32x16 s0[kSB];
-      if constexpr (W == 8) scores(sb, q0, dma_hook, s0);
-      else scores(sb, q0, no_hook, s0);
-      mask_any(s0, jb, lim0, mrow0, sb);
+      if constexpr (MK != 0 && ML == 0) {
+        // the tile's mask words are requested ahead of S (and of the tile loads it issues), so
+        // that waiting for them leaves those loads in flight
+        uint32_t mw[kSB][16];
+        mask_fetch(mw, jb, lim0, mrow0);
+        if constexpr (W == 8) scores(sb, q0, dma_hook, s0);
+        else scores(sb, q0, no_hook, s0);
+        mask_words_apply(s0, mw, jb, lim0);
+      } else {
+        if constexpr (W == 8) scores(sb, q0, dma_hook, s0);
+        else scores(sb, q0, no_hook, s0);
+        mask_any(s0, jb, lim0, mrow0, sb);
+      }
       const bool f0 = stats(s0, m0, a0);
       rescale(o0, a0, f0);
       weights(s0, m0, a0, l0, pa0, pa1);
