@@ -262,6 +262,13 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
     lc[c] = p.part_lse[(int64_t)cc * n_rows + row_id];
     oc[c] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * p.D + dl);
   }
+  // one use of every partial and lse here keeps all the loads together, in one round trip (left
+  // to the weighted sum, the compiler sinks each partial's load into its chunk's branch, after
+  // the lse loads have come back and the row's largest lse is known)
+  static_assert(kFewChunks == 8, "one use of the eight partials");
+  asm volatile("" ::"v"(oc[0]), "v"(oc[1]), "v"(oc[2]), "v"(oc[3]), "v"(oc[4]), "v"(oc[5]), "v"(oc[6]), "v"(oc[7]));
+  asm volatile("" : "+v"(lc[0]), "+v"(lc[1]), "+v"(lc[2]), "+v"(lc[3]), "+v"(lc[4]), "+v"(lc[5]), "+v"(lc[6]),
+               "+v"(lc[7]));
   float top = -INFINITY;
   bool nan_l = false;  // a chunk whose lse is NaN makes the row NaN, as the unsplit definition does
 #pragma unroll

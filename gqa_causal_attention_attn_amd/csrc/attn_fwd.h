@@ -1082,13 +1082,21 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
     if constexpr (!SPLIT) {
       const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
       uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
+      // every gate word of the lane is requested before the first store: one round trip (a load
+      // after each store would wait for that store and its own load in turn)
+      u32x2 gws[kDB][4];
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) gws[db][q4] = *reinterpret_cast<const u32x2*>(grow + 32 * db + 8 * q4 + 4 * hf);
+      }
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         if (db > 0) acc_step(o[db - 1], o[db]);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d0 = 32 * db + 8 * q4 + 4 * hf;
-          const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + d0);
+          const u32x2 gw = gws[db][q4];
           const float g0 = sigmoidf_(lo16<DT>(gw[0])), g1 = sigmoidf_(hi16<DT>(gw[0]));
           const float g2 = sigmoidf_(lo16<DT>(gw[1])), g3 = sigmoidf_(hi16<DT>(gw[1]));
           const float x0 = o[db][4 * q4 + 0] * inv, x1 = o[db][4 * q4 + 1] * inv;
