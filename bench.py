@@ -257,6 +257,23 @@ def probes(dev, timer):
                                     "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                     "us": round(ms * 1e3, 2), "distinct_buffers": n_buf}
         del srcs
+    # the decode main pass's key stream without its compute: one workgroup of four wavefronts
+    # per CU, 32 KiB tiles, three in flight; the main pass's buffer-to-LDS loads with its
+    # per-tile wait and barrier, without the barrier, and the same loads into registers
+    lib.gqa_probe_tile_stream.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
+    nbytes, n_buf = 134_270_976 // 16 * 16, 8
+    srcs = [torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev) for _ in range(n_buf)]
+    tiles = {}
+    for blocks_ in (244, 256):
+        for mode, name in ((0, "lds_dma_barrier"), (1, "lds_dma"), (2, "registers")):
+            fn = (lambda i: lib.gqa_probe_tile_stream(srcs[i % n_buf].data_ptr(), nbytes, sink.data_ptr(), blocks_,
+                                                      mode, s))
+            assert fn(0) == 0
+            ms = timer.time(fn, n_buf, 5)
+            tiles[f"{name}_{blocks_}wg"] = {"gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "us": round(ms * 1e3, 2)}
+    res["tile_stream_134MB"] = {**tiles, "kernel": "one 4-wavefront workgroup per CU streams its slice in 32 KiB "
+                                "tiles, 3 in flight (8 distinct buffers, cold)"}
+    del srcs
     del sink
     torch.cuda.empty_cache()
     return res

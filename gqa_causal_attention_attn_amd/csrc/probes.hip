@@ -83,6 +83,68 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* src, size
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
+// The decode main pass's key stream without its compute: one workgroup of four wavefronts per
+// CU (a 128 KiB LDS ring keeps it alone there) streams its contiguous slice in 32 KiB tiles,
+// each wavefront moving 8 KiB of every tile, three tiles in flight.  MODE 0: buffer-to-LDS loads
+// (the main pass's form) with a wait and a workgroup barrier per tile; MODE 1: the same without
+// the barrier; MODE 2: the same loads into registers (16-byte global loads, folded).  Loads past
+// the slice read zeros (the buffer's range ends there).
+typedef __attribute__((address_space(3))) void lds_void_t;
+// one 1 KiB buffer-to-LDS load of a wavefront (a device function: the LDS pointer cast has no
+// host form)
+__device__ __forceinline__ void dma_1k(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, off, 0, 0, 0);
+}
+template <int MODE>
+__global__ __launch_bounds__(256) void tile_stream_kernel(const uint8_t* src, size_t bytes, uint32_t* out) {
+  constexpr int kTile = 32768, kWaveBytes = 8192, kLoads = kWaveBytes / 1024, kPF = 3, kRing = 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing * kTile];
+  const size_t per = ((bytes + gridDim.x - 1) / gridDim.x + kTile - 1) / kTile * kTile;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t len = lo >= bytes ? 0 : (bytes - lo < per ? bytes - lo : per);
+  const int n_tiles = (int)((len + kTile - 1) / kTile);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const uint32_t lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(src) + (len ? lo : 0), (short)0, (int)len, 0x00020000);
+  auto off_of = [&](int t, int i) { return (uint32_t)t * kTile + (uint32_t)wave * kWaveBytes + lane * 16 + i * 1024; };
+  uint32_t x = 0;
+  if constexpr (MODE == 2) {
+    // three tiles of registers in flight, folded in turn (the loop runs in steps of three tiles)
+    u32x4 r0[kLoads], r1[kLoads], r2[kLoads];
+    auto load = [&](u32x4(&r)[kLoads], int t) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off_of(t, i), 0, 0);
+    };
+    auto fold = [&](const u32x4(&r)[kLoads]) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) x ^= r[i][0] ^ r[i][1] ^ r[i][2] ^ r[i][3];
+    };
+    load(r0, 0), load(r1, 1), load(r2, 2);
+    for (int t = 0; t < n_tiles; t += 3) {
+      fold(r0), load(r0, t + 3);
+      fold(r1), load(r1, t + 4);
+      fold(r2), load(r2, t + 5);
+    }
+    fold(r0), fold(r1), fold(r2);
+  } else {
+    auto issue = [&](int t) {
+      uint8_t* dst = ring + (t % kRing) * kTile + wave * kWaveBytes;
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) dma_1k(rs, dst + i * 1024, off_of(t, i));
+    };
+    for (int t = 0; t < kPF; ++t) issue(t);
+    for (int t = 0; t < n_tiles; ++t) {
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // this wavefront's 8 loads of tile t are in
+      if constexpr (MODE == 0) __builtin_amdgcn_s_barrier();
+      issue(t + kPF);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    x = ring[wave * kWaveBytes + lane * 16];  // this wavefront's own bytes of stage 0
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
+}
+
 // MFMA with VALU beside it: every wavefront runs `iters` rounds of 16 v_mfma_f32_32x32x16_bf16
 // on CHAINS independent accumulators (1: each MFMA depends on the one before), each MFMA
 // followed by NV independent VALU operations (EXP: v_exp_f32, else FMAs) on other registers.
@@ -218,6 +280,20 @@ int gqa_probe_read(const void* src, size_t bytes, uint32_t* out, int blocks, voi
     return 1;
   hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int gqa_probe_tile_stream(const void* src, size_t bytes, uint32_t* out, int blocks, int mode, void* stream) {
+  if (!src || !out || blocks < 1 || bytes < 16 || bytes > ((size_t)1 << 31) * (size_t)blocks ||
+      (reinterpret_cast<uintptr_t>(src) & 15u) || mode < 0 || mode > 2)
+    return 1;
+  const size_t per = (bytes + blocks - 1) / blocks;
+  if (per + 32768 * 4 > ((size_t)1 << 31)) return 1;  // 32-bit buffer offsets
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto src8 = static_cast<const uint8_t*>(src);
+  if (mode == 0) hipLaunchKernelGGL(tile_stream_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, src8, bytes, out);
+  else if (mode == 1) hipLaunchKernelGGL(tile_stream_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, src8, bytes, out);
+  else hipLaunchKernelGGL(tile_stream_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, src8, bytes, out);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -42,6 +42,15 @@ int gqa_probe_lds(float* out, int blocks, int iters, int kind, void* stream);
  * flight per lane; out: blocks * 256 words (a fold of the data, so the loads stay). */
 int gqa_probe_read(const void* src, size_t bytes, uint32_t* out, int blocks, void* stream);
 
+/* The decode main pass's key stream without its compute: `blocks` workgroups of four
+ * wavefronts (one a CU: each holds a 128 KiB LDS ring) each stream a contiguous slice of `bytes`
+ * (src 16-byte aligned) in 32 KiB tiles, every wavefront moving 8 KiB of each tile in 1 KiB
+ * loads, three tiles in flight.  mode 0: buffer-to-LDS loads with a wait and a workgroup
+ * barrier per tile (the main pass's cadence); 1: without the barrier; 2: the same loads into
+ * registers.  out: blocks * 256 words.  Returns 1 on a bad argument (a slice must stay below
+ * 2 GiB), 2 on a launch error. */
+int gqa_probe_tile_stream(const void* src, size_t bytes, uint32_t* out, int blocks, int mode, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

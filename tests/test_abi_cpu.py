@@ -405,7 +405,8 @@ def test_probe_library_exports_every_declared_symbol():
     with open(os.path.join(ROOT, "include", "gqa_probes.h")) as f:
         body = f.read().split('extern "C" {', 1)[1]
     declared = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\(", body, flags=re.M))
-    assert declared == {"gqa_probe_mfma", "gqa_probe_mfma_mix", "gqa_probe_lds", "gqa_probe_read"}
+    assert declared == {"gqa_probe_mfma", "gqa_probe_mfma_mix", "gqa_probe_lds", "gqa_probe_read",
+                        "gqa_probe_tile_stream"}
     lib = C.CDLL(gbuild.PROBES_LIB)
     for name in declared:
         assert hasattr(lib, name), name
