@@ -147,8 +147,8 @@ class Timer:
 class Plans:
     """Requested plan beside the resolved one for every sample; a mismatch stops the run."""
 
-    KEYS = ("variant_name", "n_splits", "keys_per_split", "n_head_chunks", "chunk_sizes", "waves_per_block",
-            "n_row_tiles", "grid_blocks", "workspace_bytes")
+    KEYS = ("variant_name", "n_splits", "partial_kind", "keys_per_split", "n_head_chunks", "chunk_sizes",
+            "waves_per_block", "n_row_tiles", "grid_blocks", "workspace_bytes")
 
     def __init__(self, ga):
         self.ga = ga
@@ -414,7 +414,7 @@ def main():
             if per_call is not None:
                 per_call[i][1].record(stream)
             if parts is not None:
-                ga.merge(parts[0], parts[1], g[:, :, s:e], out=out[:, :, s:e])
+                ga.merge(parts[0], parts[1], g[:, :, s:e], out=out[:, :, s:e], partial_exp=parts[2])
 
     # ---- profiler mode: one workload, --steps times
     if args.only:

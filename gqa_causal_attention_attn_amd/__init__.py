@@ -140,8 +140,11 @@ def prefill_partials(q, k_cache, v_cache, gate, *, kv_offset: int, workspace, kv
                      head_chunk=0, n_splits=0, mask=None, out=None):
     """attn_prefill_partials: the main pass only.  Returns (out, partials).  partials is None when
     the plan kept the keys in one chunk (out is then final); otherwise it is (partial_o,
-    partial_lse), views into `workspace` (a uint8 tensor) to finish with
-    merge(partial_o, partial_lse, gate, out) on a stream ordered after this one."""
+    partial_lse, partial_exp), views into `workspace` (a uint8 tensor) to finish with
+    merge(partial_o, partial_lse, gate, out, partial_exp=partial_exp) on a stream ordered after
+    this one.  partial_o [C, B, Hq, rows, D] is fp32 with partial_exp None (small plans), or
+    fp16 with partial_exp [C, B, Hq, rows] int32, the partial being partial_o times
+    2^partial_exp (merge_args partial_kind 0 and 1)."""
     if kv_len is None:
         kv_len = kv_offset + q.shape[2]
     if out is None:
@@ -150,16 +153,20 @@ def prefill_partials(q, k_cache, v_cache, gate, *, kv_offset: int, workspace, kv
               head_chunk=head_chunk, n_splits=n_splits, mask=mask)
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor")
-    n, off = C.c_int32(0), C.c_size_t(0)
+    n, kind, off, eoff = C.c_int32(0), C.c_int32(0), C.c_size_t(0), C.c_size_t(0)
     _check(lib().attn_prefill_partials(C.byref(a), workspace.data_ptr(), workspace.numel(), _stream_handle(q),
-                                       C.byref(n), C.byref(off)))
+                                       C.byref(n), C.byref(kind), C.byref(off), C.byref(eoff)))
     if n.value == 1:
         return out, None
     B, Hq, rows, D = q.shape
     cnt = n.value * B * Hq * rows
-    po = workspace[:cnt * D * 4].view(torch.float32).view(n.value, B, Hq, rows, D)
     pl = workspace[off.value:off.value + cnt * 4].view(torch.float32).view(n.value, B, Hq, rows)
-    return out, (po, pl)
+    if kind.value == 0:
+        po = workspace[:cnt * D * 4].view(torch.float32).view(n.value, B, Hq, rows, D)
+        return out, (po, pl, None)
+    po = workspace[:cnt * D * 2].view(torch.float16).view(n.value, B, Hq, rows, D)
+    pe = workspace[eoff.value:eoff.value + cnt * 4].view(torch.int32).view(n.value, B, Hq, rows)
+    return out, (po, pl, pe)
 
 
 def prefill(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
@@ -244,10 +251,18 @@ def kv_keep(k_cache, v_cache, *, kv_offset: int, rows: int, keep) -> None:
         raise ValueError("k_cache and v_cache differ")
     _check(lib().kv_keep(C.byref(a), _stream_handle(k_cache)))
 
-def merge(partial_o, partial_lse, gate, out=None):
-    """attn_merge: partial_o [C, B, Hq, rows, D] fp32 (D 256, 128 or 64), partial_lse [C, B, Hq, rows] fp32 (natural log)."""
-    if partial_o.dtype != torch.float32 or partial_lse.dtype != torch.float32:
-        raise TypeError("partials are float32")
+def merge(partial_o, partial_lse, gate, out=None, partial_exp=None):
+    """attn_merge: partial_o [C, B, Hq, rows, D] (D 256, 128 or 64) fp32, or fp16 with
+    partial_exp [C, B, Hq, rows] int32 (the form prefill_partials returns: the partial is
+    partial_o times 2^partial_exp); partial_lse [C, B, Hq, rows] fp32 (natural log)."""
+    if partial_o.dtype not in (torch.float32, torch.float16) or partial_lse.dtype != torch.float32:
+        raise TypeError("partial_o is float32 or float16, partial_lse float32")
+    fp16 = partial_o.dtype == torch.float16
+    if fp16 != (partial_exp is not None):
+        raise ValueError("partial_exp goes with float16 partials, and only with them")
+    if fp16 and (partial_exp.dtype != torch.int32 or tuple(partial_exp.shape) != tuple(partial_o.shape[:4])
+                 or not partial_exp.is_contiguous()):
+        raise ValueError("partial_exp is a contiguous int32 [C, B, Hq, rows]")
     if not partial_o.is_contiguous() or not partial_lse.is_contiguous():
         raise ValueError("partials must be contiguous")
     if out is None:
@@ -255,9 +270,11 @@ def merge(partial_o, partial_lse, gate, out=None):
     a = _abi.MergeArgs()
     a.dtype = _dtype_code(gate)
     a.n_chunks, a.B, a.Hq, a.rows, a.D = partial_o.shape
+    a.partial_kind = 1 if fp16 else 0
     if tuple(partial_lse.shape) != tuple(partial_o.shape[:4]) or tuple(gate.shape) != tuple(partial_o.shape[1:]):
         raise ValueError("partials and gate disagree in shape")
     a.partial_o, a.partial_lse = partial_o.data_ptr(), partial_lse.data_ptr()
+    a.partial_exp = partial_exp.data_ptr() if fp16 else None
     a.gate, a.out = _t4(gate), _t4(out)
     _check(lib().attn_merge(C.byref(a), _stream_handle(gate)))
     return out
@@ -385,7 +402,7 @@ def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int = 0, kv_offs
                     out=out[:, :, s:e], workspace=workspace, head_chunk=head_chunk, n_splits=n_splits)
         return out
     main = torch.cuda.current_stream(q.device)
-    side = torch.cuda.Stream(device=q.device)
+    side = merge_stream(q.device)
     spaces = [workspace, torch.empty_like(workspace)]
     merged = [None, None]  # per workspace: the event after the merge that last read it
     for i, s in enumerate(range(0, N, q_block)):
@@ -402,8 +419,22 @@ def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int = 0, kv_offs
             ready.record(main)
             side.wait_event(ready)
             with torch.cuda.stream(side):
-                merge(parts[0], parts[1], gate[:, :, s:e], out=out[:, :, s:e])
+                merge(parts[0], parts[1], gate[:, :, s:e], out=out[:, :, s:e], partial_exp=parts[2])
             merged[slot] = torch.cuda.Event()
             merged[slot].record(side)
     main.wait_stream(side)
     return out
+
+
+_MERGE_STREAMS = {}
+
+
+def merge_stream(device):
+    """The second stream prompt_prefill's overlapped merges run on: one per device, made once,
+    so that it keeps the hardware queue it was given (a stream made per call can land on the
+    queue of the caller's stream, which runs the two in turn)."""
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    if idx not in _MERGE_STREAMS:
+        _MERGE_STREAMS[idx] = torch.cuda.Stream(device=idx)
+    return _MERGE_STREAMS[idx]

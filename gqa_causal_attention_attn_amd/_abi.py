@@ -7,7 +7,7 @@ The struct sizes are checked against the library's own (attn_struct_size) when i
 import ctypes as C
 import os
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 HEAD_DIM = 256
 MAX_DECODE_ROWS = 32
 MAX_CHUNKS = 64
@@ -65,7 +65,8 @@ class KvKeepArgs(C.Structure):
 class MergeArgs(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("n_chunks", C.c_int32), ("B", C.c_int32), ("Hq", C.c_int32),
                 ("rows", C.c_int32), ("D", C.c_int32), ("partial_o", C.c_void_p), ("partial_lse", C.c_void_p),
-                ("gate", Tensor), ("out", Tensor)]
+                ("gate", Tensor), ("out", Tensor), ("partial_kind", C.c_int32),
+                ("partial_exp", C.c_void_p)]
 
 
 class PlanInfo(C.Structure):
@@ -73,7 +74,7 @@ class PlanInfo(C.Structure):
                 ("head_chunk", C.c_int32), ("rows_per_wave", C.c_int32), ("waves_per_block", C.c_int32),
                 ("n_row_tiles", C.c_int32), ("n_splits", C.c_int32), ("keys_per_split", C.c_int32),
                 ("keys_per_tile", C.c_int32), ("lds_bytes", C.c_int32), ("grid_blocks", C.c_int64),
-                ("workspace_bytes", C.c_int64), ("chunk_sizes", C.c_int32 * MAX_CHUNKS)]
+                ("workspace_bytes", C.c_int64), ("chunk_sizes", C.c_int32 * MAX_CHUNKS), ("partial_kind", C.c_int32)]
 
 
 class PromptQuery(C.Structure):
@@ -122,7 +123,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.attn_merge.argtypes = [P(MergeArgs), C.c_void_p]
     lib.attn_prefill_partials.restype = C.c_int
     lib.attn_prefill_partials.argtypes = [P(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p, P(C.c_int32),
-                                          P(C.c_size_t)]
+                                          P(C.c_int32), P(C.c_size_t), P(C.c_size_t)]
     lib.attn_decode_noalloc.restype = C.c_int
     lib.attn_decode_noalloc.argtypes = [P(AttnArgs), C.c_void_p]
     lib.kv_keep.restype = C.c_int

@@ -39,7 +39,9 @@ struct Plan {
   int n_splits;
   int keys_per_split;
   int64_t grid;
-  size_t ws_o_bytes;
+  int part_kind;       // partial rows in fp32 (0) or fp16 with a power of two per row (1)
+  size_t ws_o_bytes;  // partial rows at offset 0, then the lse ...
+  size_t ws_e_offset;  // ... and (kind 1) each row's power of two at this offset
   size_t ws_bytes;
 };
 
@@ -233,8 +235,11 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   if (S > 1 && !gqa::merge_fits((int)S, n_rows)) return ATTN_E_ARG;
   if (S > 1) {
     const int64_t nrow = S * a->B * a->Hq * (int64_t)a->rows;
-    P->ws_o_bytes = (size_t)cdiv(nrow * a->D * 4, 256) * 256;
-    P->ws_bytes = P->ws_o_bytes + (size_t)cdiv(nrow * 4, 256) * 256;
+    // the kind depends on the unchunked shape only, like the splits
+    P->part_kind = nrow * gqa::partial_row_bytes(a->D, 0) >= gqa::kHalfPartialsFromBytes ? 1 : 0;
+    P->ws_o_bytes = (size_t)cdiv(nrow * gqa::partial_row_bytes(a->D, P->part_kind), 256) * 256;
+    P->ws_e_offset = P->ws_o_bytes + (size_t)cdiv(nrow * 4, 256) * 256;
+    P->ws_bytes = P->ws_e_offset + (P->part_kind == 1 ? (size_t)cdiv(nrow * 4, 256) * 256 : 0);
   }
   return ATTN_OK;
 }
@@ -246,7 +251,8 @@ inline int variant_of(const attn_args* a, const Plan& P) {
 }
 
 int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream, bool merge = true,
-            int32_t* n_chunks = nullptr, size_t* lse_offset = nullptr) {
+            int32_t* n_chunks = nullptr, int32_t* part_kind = nullptr, size_t* lse_offset = nullptr,
+            size_t* exp_offset = nullptr) {
   int st = validate(a, op);
   if (st) return st;
   Plan P;
@@ -289,18 +295,24 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
   p.keys_per_split = P.keys_per_split;
   p.grid = (int)P.grid;
   if (P.n_splits > 1) {
-    p.part_o = static_cast<float*>(ws);
+    p.part_o = ws;
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + P.ws_o_bytes);
+    p.part_e = P.part_kind == 1 ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + P.ws_e_offset) : nullptr;
+    p.part_kind = P.part_kind;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_chunks) *n_chunks = P.n_splits;
+  if (part_kind) *part_kind = P.n_splits > 1 ? P.part_kind : 0;
   if (lse_offset) *lse_offset = P.n_splits > 1 ? P.ws_o_bytes : 0;
+  if (exp_offset) *exp_offset = P.n_splits > 1 && P.part_kind == 1 ? P.ws_e_offset : 0;
   if (gqa::launch_fwd(p, a->D, a->dtype, a->mask.kind, P.shape, s) != hipSuccess) return ATTN_E_HIP;
   if (P.n_splits > 1 && merge) {
     gqa::MergeParams mp;
     memset(&mp, 0, sizeof(mp));
     mp.part_o = p.part_o;
     mp.part_lse = p.part_lse;
+    mp.part_e = p.part_e;
+    mp.part_kind = p.part_kind;
     mp.gate = p.gate;
     mp.out = p.out;
     mp.g_sb = p.g_sb, mp.g_sh = p.g_sh, mp.g_sr = p.g_sr;
@@ -471,6 +483,7 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
   info->keys_per_tile = gqa::tile_keys(a->D);
   info->lds_bytes = gqa::kFwdLdsBytes + (P.mask_lds ? gqa::kStages * gqa::kMaskStageLds : 0);
   info->grid_blocks = P.grid;
+  info->partial_kind = P.n_splits > 1 ? P.part_kind : 0;
   info->workspace_bytes = (int64_t)P.ws_bytes;
   for (int i = 0; i < P.n_chunks; ++i) info->chunk_sizes[i] = P.chunk_sizes[i];
   return ATTN_OK;
@@ -481,9 +494,10 @@ int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* str
 }
 
 int attn_prefill_partials(const attn_args* a, void* workspace, size_t ws_bytes, void* stream, int32_t* n_chunks,
-                          size_t* lse_offset) {
-  if (!n_chunks || !lse_offset) return ATTN_E_NULL;
-  return run_fwd(a, ATTN_OP_PREFILL, workspace, ws_bytes, stream, false, n_chunks, lse_offset);
+                          int32_t* partial_kind, size_t* lse_offset, size_t* exp_offset) {
+  if (!n_chunks || !partial_kind || !lse_offset || !exp_offset) return ATTN_E_NULL;
+  return run_fwd(a, ATTN_OP_PREFILL, workspace, ws_bytes, stream, false, n_chunks, partial_kind, lse_offset,
+                 exp_offset);
 }
 
 int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stream) {
@@ -600,14 +614,19 @@ int attn_merge(const merge_args* a, void* stream) {
   if (a->n_chunks < 1) return ATTN_E_ARG;
   const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
   if (n_rows > (int64_t)INT32_MAX || !gqa::merge_fits(a->n_chunks, n_rows)) return ATTN_E_ARG;  // 32-bit rows, launch size
+  if (a->partial_kind != 0 && a->partial_kind != 1) return ATTN_E_ARG;
   if (!a->partial_o || !a->partial_lse || !a->gate.ptr || !a->out.ptr) return ATTN_E_NULL;
+  if (a->partial_kind == 1 && !a->partial_exp) return ATTN_E_NULL;
   if (!aligned16(a->partial_o) || !aligned16(a->gate.ptr) || !aligned16(a->out.ptr) || !strides_ok(a->gate) ||
-      !strides_ok(a->out) || (reinterpret_cast<uintptr_t>(a->partial_lse) & 3u))
+      !strides_ok(a->out) || (reinterpret_cast<uintptr_t>(a->partial_lse) & 3u) ||
+      (a->partial_kind == 1 && (reinterpret_cast<uintptr_t>(a->partial_exp) & 3u)))
     return ATTN_E_LAYOUT;
   gqa::MergeParams p;
   memset(&p, 0, sizeof(p));  // no main-pass inputs: no repair
   p.part_o = a->partial_o;
   p.part_lse = a->partial_lse;
+  p.part_e = a->partial_kind == 1 ? a->partial_exp : nullptr;
+  p.part_kind = a->partial_kind;
   p.gate = static_cast<const uint16_t*>(a->gate.ptr);
   p.out = static_cast<uint16_t*>(a->out.ptr);
   p.g_sb = a->gate.stride_b, p.g_sh = a->gate.stride_h, p.g_sr = a->gate.stride_row;

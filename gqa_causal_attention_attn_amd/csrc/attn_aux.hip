@@ -123,6 +123,37 @@ __device__ __forceinline__ void exact_row(const RepairParams& f, int D, int b, i
   if (on) *reinterpret_cast<u32x2*>(orow + dl) = ow;
 }
 
+// Four values of a split partial row: KIND 0 fp32 rows of D values; KIND 1 the main pass's
+// fp16 rows, value times 2^e (partial_row_bytes, e from its own array).  Loads (issued
+// together) and decode apart.
+template <int KIND>
+struct PartialLoad {
+  f32x4 f;    // KIND 0
+  u32x2 h;    // KIND 1: four fp16 values
+  int32_t e;  // KIND 1: the row's exponent
+};
+template <int KIND>
+__device__ __forceinline__ PartialLoad<KIND> load_partial(const MergeParams& p, int64_t row, int dl) {
+  PartialLoad<KIND> x;
+  if constexpr (KIND == 0) {
+    x.f = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.part_o) + row * p.D + dl);
+  } else {
+    x.h = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.part_o) + row * p.D + dl);
+    x.e = p.part_e[row];
+  }
+  return x;
+}
+template <int KIND>
+__device__ __forceinline__ f32x4 decode_partial(const PartialLoad<KIND>& x) {
+  if constexpr (KIND == 0) {
+    return x.f;
+  } else {
+    auto h2f = [](uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); };
+    return (f32x4){__builtin_amdgcn_ldexpf(h2f(x.h[0] & 0xffffu), x.e), __builtin_amdgcn_ldexpf(h2f(x.h[0] >> 16), x.e),
+                   __builtin_amdgcn_ldexpf(h2f(x.h[1] & 0xffffu), x.e), __builtin_amdgcn_ldexpf(h2f(x.h[1] >> 16), x.e)};
+  }
+}
+
 // whether any of the four values is NaN
 __device__ __forceinline__ bool has_nan4(const f32x4& x) { return __builtin_isnan(x[0] + x[1] + x[2] + x[3]); }
 
@@ -132,7 +163,7 @@ __device__ __forceinline__ bool has_nan4(const f32x4& x) { return __builtin_isna
 // once; only the row's largest lse crosses the wavefronts (through LDS) before the weights are
 // applied, so a row up to MW x kMergeBatch chunks costs one round trip to memory.  The partial
 // sums meet in LDS.
-template <int DT, int MW>
+template <int DT, int MW, int KIND>
 __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
   constexpr int kMergeWaves = MW;
   __shared__ f32x4 part_acc[kMergeWaves][64];
@@ -162,13 +193,16 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
     // this pass's chunks of the wavefront, all loads in flight together (indices past the
     // last chunk re-read it and are selected out)
     float lc[kMergeBatch];
-    f32x4 oc[kMergeBatch];
+    PartialLoad<KIND> raw[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       const int cc = min(c0 + wave + j * kMergeWaves, nch - 1);
       lc[j] = p.part_lse[(int64_t)cc * n_rows + row_id];
-      oc[j] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * p.D + dl);
+      raw[j] = load_partial<KIND>(p, (int64_t)cc * n_rows + row_id, dl);
     }
+    f32x4 oc[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) oc[j] = decode_partial<KIND>(raw[j]);
     float top = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
@@ -233,9 +267,9 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
 }
 
 // Few chunks (prompt blocks split a handful of ways): one wavefront per row, four rows per
-// workgroup, four dims per lane, and every chunk's partial loaded at once (independent
-// 16-byte loads), so the pass streams instead of waiting on one load after another.
-template <int DT>
+// workgroup, four dims per lane, and every chunk's partial loaded at once (independent loads),
+// so the pass streams instead of waiting on one load after another.
+template <int DT, int KIND>
 __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
@@ -252,7 +286,7 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   // every load is unconditional (chunk indices past the last one re-read the last one) so
   // they are all in flight together; chunks past the last one are selected out below
   float lc[kFewChunks];
-  f32x4 oc[kFewChunks];
+  PartialLoad<KIND> raw[kFewChunks];
   const int nch = GQA_CONTROL == 2 ? max(p.n_chunks - 1, 1) : p.n_chunks;
   const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
   const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + dl);
@@ -260,15 +294,23 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   for (int c = 0; c < kFewChunks; ++c) {
     const int cc = min(c, nch - 1);
     lc[c] = p.part_lse[(int64_t)cc * n_rows + row_id];
-    oc[c] = *reinterpret_cast<const f32x4*>(p.part_o + ((int64_t)cc * n_rows + row_id) * p.D + dl);
+    raw[c] = load_partial<KIND>(p, (int64_t)cc * n_rows + row_id, dl);
   }
   // one use of every partial and lse here keeps all the loads together, in one round trip (left
   // to the weighted sum, the compiler sinks each partial's load into its chunk's branch, after
   // the lse loads have come back and the row's largest lse is known)
-  static_assert(kFewChunks == 8, "one use of the eight partials");
-  asm volatile("" ::"v"(oc[0]), "v"(oc[1]), "v"(oc[2]), "v"(oc[3]), "v"(oc[4]), "v"(oc[5]), "v"(oc[6]), "v"(oc[7]));
-  asm volatile("" : "+v"(lc[0]), "+v"(lc[1]), "+v"(lc[2]), "+v"(lc[3]), "+v"(lc[4]), "+v"(lc[5]), "+v"(lc[6]),
-               "+v"(lc[7]));
+#pragma unroll
+  for (int c = 0; c < kFewChunks; ++c) {
+    if constexpr (KIND == 0) {
+      asm volatile("" ::"v"(raw[c].f));
+    } else {
+      asm volatile("" ::"v"(raw[c].h), "v"(raw[c].e));
+    }
+    asm volatile("" : "+v"(lc[c]));
+  }
+  f32x4 oc[kFewChunks];
+#pragma unroll
+  for (int c = 0; c < kFewChunks; ++c) oc[c] = decode_partial<KIND>(raw[c]);
   float top = -INFINITY;
   bool nan_l = false;  // a chunk whose lse is NaN makes the row NaN, as the unsplit definition does
 #pragma unroll
@@ -372,26 +414,32 @@ hipError_t launch_keep(const KeepParams& p, int B, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
+template <int KIND>
+void launch_merge_k(const MergeParams& p, int dtype, hipStream_t stream) {
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
   if (p.n_chunks <= kFewChunks) {
     const dim3 grid((unsigned)((n_rows + 3) / 4));
-    if (dtype == 0) hipLaunchKernelGGL(merge_few_kernel<0>, grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(merge_few_kernel<1>, grid, dim3(256), 0, stream, p);
+    if (dtype == 0) hipLaunchKernelGGL((merge_few_kernel<0, KIND>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((merge_few_kernel<1, KIND>), grid, dim3(256), 0, stream, p);
   } else {
     const dim3 grid((unsigned)n_rows);
     const int mw = merge_waves(p.n_chunks);
     if (mw == 4) {
-      if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 4>), grid, dim3(4 * 64), 0, stream, p);
-      else hipLaunchKernelGGL((merge_kernel<1, 4>), grid, dim3(4 * 64), 0, stream, p);
+      if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 4, KIND>), grid, dim3(4 * 64), 0, stream, p);
+      else hipLaunchKernelGGL((merge_kernel<1, 4, KIND>), grid, dim3(4 * 64), 0, stream, p);
     } else if (mw == 8) {
-      if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 8>), grid, dim3(8 * 64), 0, stream, p);
-      else hipLaunchKernelGGL((merge_kernel<1, 8>), grid, dim3(8 * 64), 0, stream, p);
+      if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 8, KIND>), grid, dim3(8 * 64), 0, stream, p);
+      else hipLaunchKernelGGL((merge_kernel<1, 8, KIND>), grid, dim3(8 * 64), 0, stream, p);
     } else {
-      if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 16>), grid, dim3(16 * 64), 0, stream, p);
-      else hipLaunchKernelGGL((merge_kernel<1, 16>), grid, dim3(16 * 64), 0, stream, p);
+      if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 16, KIND>), grid, dim3(16 * 64), 0, stream, p);
+      else hipLaunchKernelGGL((merge_kernel<1, 16, KIND>), grid, dim3(16 * 64), 0, stream, p);
     }
   }
+}
+
+hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
+  if (p.part_kind == 0) launch_merge_k<0>(p, dtype, stream);
+  else launch_merge_k<1>(p, dtype, stream);
   return hipGetLastError();
 }
 

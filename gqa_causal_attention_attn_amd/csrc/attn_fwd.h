@@ -487,7 +487,7 @@ __device__ __forceinline__ void exact_pair(const FwdParams& p, int b, int h, int
   }
 }
 
-template <int D, int DT, int MK, int W, bool LAG, int ML, bool SPLIT>
+template <int D, int DT, int MK, int W, bool LAG, int ML, int SPLIT>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) {
   static_assert(D == 256 || D == 128 || D == 64, "head dims 256, 128 and 64");
   // A K (or V) tile is 16 KiB whatever the head dim: 8192 / D keys in 16 groups of R = 512 / D
@@ -1110,21 +1110,54 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
       }
     } else {
       const int64_t row_id = (((int64_t)split * p.B + b) * p.Hq + h) * p.rows + r;
-      float* prow = p.part_o + row_id * D;
+      int e = 0;
+      if constexpr (SPLIT == 1) {
+        float* prow = static_cast<float*>(p.part_o) + row_id * D;
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        if (db > 0) acc_step(o[db - 1], o[db]);
+        for (int db = 0; db < kDB; ++db) {
+          if (db > 0) acc_step(o[db - 1], o[db]);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = 32 * db + 8 * q4 + 4 * hf;
-          f32x4 v4 = {o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
-                      o[db][4 * q4 + 3] * inv};
-          *reinterpret_cast<f32x4*>(prow + d0) = v4;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = 32 * db + 8 * q4 + 4 * hf;
+            f32x4 v4 = {o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
+                        o[db][4 * q4 + 3] * inv};
+            *reinterpret_cast<f32x4*>(prow + d0) = v4;
+          }
+        }
+      } else {
+        uint16_t* prow = static_cast<uint16_t*>(p.part_o) + row_id * D;
+        // the row's largest magnitude (this lane's half of the dims, then the other half's
+        // lane): o / l is stored as fp16 times 2^-e with that magnitude in [0.5, 1)
+        float mx = 0.0f;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          if (db > 0) acc_step(o[db - 1], o[db]);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) mx = fmaxf(mx, fabsf(o[db][q]));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * inv;
+        // (e at least -127: inv 2^-e stays finite, inv being at most 1 as l >= 1; a row below
+        // 2^-127 keeps its largest magnitude at or above 2^-14, an fp16 normal, down to 2^-141)
+        e = (mx > 0.0f && mx <= 3.4028234e38f) ? max(__builtin_amdgcn_frexp_expf(mx), -127) : 0;
+        // one multiply by inv 2^-e (a power-of-two scaling of inv: exact unless it falls below
+        // the normal range, for rows of magnitude near the fp32 maximum)
+        const float sc = __builtin_amdgcn_ldexpf(inv, -e);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          if (db > 0) acc_step(o[db - 1], o[db]);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            u32x2 w;
+            w[0] = pack2<1>(o[db][4 * q4] * sc, o[db][4 * q4 + 1] * sc);
+            w[1] = pack2<1>(o[db][4 * q4 + 2] * sc, o[db][4 * q4 + 3] * sc);
+            *reinterpret_cast<u32x2*>(prow + 32 * db + 8 * q4 + 4 * hf) = w;
+          }
         }
       }
       // an empty chunk has l = 0 and lse = -inf; a NaN sum keeps its NaN (the merge redoes the row)
       if (hf == 0) {
         p.part_lse[row_id] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : l_tot == 0.0f ? -INFINITY : NAN;
+        if constexpr (SPLIT == 2) p.part_e[row_id] = e;
       }
     }
     return nan_seen;
@@ -1154,7 +1187,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 
 // shape 0: four wavefronts; 2: eight with the lagged P.V; 3: eight without it.  ml: the mask
 // layout in LDS (0: none, per-lane loads; 1: 16-byte rows, shape 2 at head dim 256 only; 2: words).
-template <int D, int DT, int MK, bool SPLIT>
+template <int D, int DT, int MK, int SPLIT>
 hipError_t launch_fwd_s(const FwdParams& p, int shape, hipStream_t stream) {
   const dim3 grid(p.grid), b4(256), b8(512);
   const int ml = MK != 0 ? p.mask_lds : 0;
@@ -1181,12 +1214,15 @@ hipError_t launch_fwd_s(const FwdParams& p, int shape, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// the split flag is a compile-time choice: the epilogue writes either the gated output or the
-// split partials, and only the former carries the in-kernel nonfinite repair
+// the split form is a compile-time choice (0: no split, 1: fp32 partials, 2: fp16 partials
+// and their exponents): the epilogue writes either the gated output or the split partials, and
+// only the former carries the in-kernel nonfinite repair; the partials' kind is a template
+// argument as well, since a runtime choice between the two partial epilogues costs the kernel
+// a second copy of its accumulators
 template <int D, int DT, int MK>
 hipError_t launch_fwd_t(const FwdParams& p, int shape, hipStream_t stream) {
-  return p.n_splits > 1 ? launch_fwd_s<D, DT, MK, true>(p, shape, stream)
-                        : launch_fwd_s<D, DT, MK, false>(p, shape, stream);
+  if (p.n_splits <= 1) return launch_fwd_s<D, DT, MK, 0>(p, shape, stream);
+  return p.part_kind == 1 ? launch_fwd_s<D, DT, MK, 2>(p, shape, stream) : launch_fwd_s<D, DT, MK, 1>(p, shape, stream);
 }
 
 // every variant of head dim D (the planted-mistake builds: head dim 256 in bf16 without a mask)

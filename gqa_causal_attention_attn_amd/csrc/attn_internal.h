@@ -41,8 +41,10 @@ struct FwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const void* mask;
-  float* part_o;    // [n_splits, B, Hq, rows, D] when n_splits > 1
-  float* part_lse;  // [n_splits, B, Hq, rows]
+  void* part_o;      // [n_splits, B, Hq, rows, D]: fp32 (part_kind 0) or fp16 (1, partial_row_bytes)
+  float* part_lse;   // [n_splits, B, Hq, rows]
+  int32_t* part_e;   // [n_splits, B, Hq, rows]: the power of two of each fp16 partial row
+  int part_kind;     // 0 or 1, as the merge's
   int64_t q_sb, q_sh, q_sr;
   int64_t g_sb, g_sh, g_sr;
   int64_t o_sb, o_sh, o_sr;
@@ -85,8 +87,10 @@ struct RepairParams {
 };
 
 struct MergeParams {
-  const float* part_o;
+  const void* part_o;  // part_kind 0: fp32 rows of D; 1: the main pass's fp16 rows (partial_row_bytes)
   const float* part_lse;
+  const int32_t* part_e;  // part_kind 1: each row's power of two
+  int part_kind;
   const uint16_t* gate;
   uint16_t* out;
   int64_t g_sb, g_sh, g_sr;
@@ -136,6 +140,17 @@ struct ComposedParams {
   int B, Hq, G, rows, kv_offset, kv_len, causal, kv_hi;
   float scale_log2;
 };
+
+// Split partial rows.  Kind 0: the D values of o / l in fp32.  Kind 1: the D values of o / l
+// times 2^-e in fp16 (round to nearest even), e chosen so that the row's largest magnitude lands
+// in [0.5, 1) (0 when it is 0 or not finite); e goes to an int32 array of its own beside the lse,
+// so a row is whole 128-byte lines (D = 64, 128, 256) and no write covers part of a line.  The
+// merge multiplies each kind-1 value by 2^e exactly.
+constexpr int64_t partial_row_bytes(int D, int kind) { return (kind == 1 ? 2 : 4) * (int64_t)D; }
+// Kind 1 halves the partials' write and read-back at the price of an exponent pass in the main
+// pass's epilogue, which only pays where the partials are large: the planner takes it from
+// 8 MiB of fp32 partials up (prompt blocks, verify rows), kind 0 below (short decodes).
+constexpr int64_t kHalfPartialsFromBytes = (int64_t)8 << 20;
 
 // Merge launch shape, shared by the launcher and the host's checks: chunk counts up to
 // kFewChunks take one wavefront per row (four rows a workgroup); more take a workgroup of

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GQA_ATTN_ABI_VERSION 5
+#define GQA_ATTN_ABI_VERSION 6
 #define ATTN_HEAD_DIM 256
 #define ATTN_MAX_DECODE_ROWS 32
 #define ATTN_MAX_CHUNKS 64
@@ -169,10 +169,16 @@ typedef struct {
   int32_t Hq;
   int32_t rows;
   int32_t D;                /* head dim: 256, 128 or 64 (else ATTN_E_HEAD_DIM) */
-  const float* partial_o;   /* [n_chunks, B, Hq, rows, D] fp32, contiguous, normalised per chunk */
+  const void* partial_o;    /* [n_chunks, B, Hq, rows] rows, contiguous, normalised per chunk; see partial_kind */
   const float* partial_lse; /* [n_chunks, B, Hq, rows] fp32, contiguous, natural log; -Inf = empty chunk */
   attn_tensor gate;         /* [B, Hq, rows, D] */
   attn_tensor out;          /* [B, Hq, rows, D], written */
+  int32_t partial_kind;     /* 0: rows of D fp32 values; 1: the rows attn_prefill_partials leaves, D fp16
+                               values v_d each (round to nearest even), the partial being v_d 2^e with e
+                               the row's entry of partial_exp (it puts the row's largest magnitude in
+                               [0.5, 1)); anything else: ATTN_E_ARG */
+  const int32_t* partial_exp; /* partial_kind 1: [n_chunks, B, Hq, rows] int32, contiguous (NULL:
+                                 ATTN_E_NULL); ignored for partial_kind 0 */
 } merge_args;
 
 /* The resolved plan of one call (what would run, for logging and validation). */
@@ -192,6 +198,8 @@ typedef struct {
   int64_t grid_blocks;     /* workgroups of the main pass */
   int64_t workspace_bytes; /* bytes of workspace the call needs */
   int32_t chunk_sizes[ATTN_MAX_CHUNKS]; /* heads per chunk within a KV group, first n_head_chunks valid */
+  int32_t partial_kind;    /* with n_splits > 1: the split partials' form (merge_args partial_kind;
+                              1 from 8 MiB of fp32 partials up), else 0 */
 } attn_plan_info;
 
 /* A prompt to be run as query blocks (kv_append + attn_prefill per block), for
@@ -286,20 +294,24 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info);
 int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* stream);
 /* Head dims 128 and 64 (attn_prefill, attn_decode, attn_prefill_partials and
  * attn_decode_noalloc) take the same main pass, plans, head chunks, masks and nonfinite repair
- * as 256; the partials hold rows of head_dim floats, and scale = 0 means 1 / sqrt(head_dim). */
+ * as 256; the partials hold rows of head_dim values, and scale = 0 means 1 / sqrt(head_dim). */
 
 /* The main pass of attn_prefill alone, for callers that overlap one query block's merge with
  * the next block's main pass (two workspaces, the merges on a second stream).  *n_chunks
  * receives the number of KV chunks of the plan.  With *n_chunks = 1 the call is complete and out
  * is written.  With *n_chunks > 1 out is not written: the normalised partials stay in the
- * workspace, o at offset 0 ([n_chunks, B, Hq, rows, head_dim] fp32) and the natural-log lse at byte
- * offset *lse_offset ([n_chunks, B, Hq, rows] fp32), and the caller completes the call with
- * attn_merge (gate and out as here) on a stream ordered after this one, before the workspace is
- * reused.  Errors as attn_prefill, plus ATTN_E_NULL for a null n_chunks or lse_offset.  The
+ * workspace in the form *partial_kind gives (that of merge_args): o at offset 0
+ * ([n_chunks, B, Hq, rows, head_dim], fp32 for kind 0, fp16 for kind 1), the natural-log lse at
+ * byte offset *lse_offset ([n_chunks, B, Hq, rows] fp32) and, for kind 1, each row's power of
+ * two at byte offset *exp_offset ([n_chunks, B, Hq, rows] int32; 0 for kind 0).  The plan takes
+ * kind 1 from 8 MiB of fp32 partials up (n_chunks B Hq rows head_dim 4 bytes), kind 0 below.
+ * The caller completes the call with attn_merge (that partial_kind, gate and out as here) on a
+ * stream ordered after this one, before the workspace is reused.  Errors as attn_prefill, plus
+ * ATTN_E_NULL for a null n_chunks, partial_kind, lse_offset or exp_offset.  The
  * merge called on its own has no inputs to redo a row from: with nonfinite inputs a hidden key
  * may leave NaN in the result of this pair of calls (attn_prefill repairs it). */
 int attn_prefill_partials(const attn_args* a, void* workspace, size_t ws_bytes, void* stream, int32_t* n_chunks,
-                          size_t* lse_offset);
+                          int32_t* partial_kind, size_t* lse_offset, size_t* exp_offset);
 
 /* The same operation for 1..32 decode / verify rows: a split-KV pass in which each
  * workgroup reads its KV chunk once for all heads of the group, each wavefront serving one
@@ -318,8 +330,9 @@ int attn_decode(const attn_args* a, void* workspace, size_t ws_bytes, void* stre
  *     stream must belong to the current device.
  *   - A plan whose partials (attn_workspace_bytes(a, ATTN_OP_DECODE)) exceed the scratch is
  *     rejected with ATTN_E_WORKSPACE before anything is enqueued (set n_splits lower to fit).
- *     At head_dim 256 the partials of n_splits chunks take n_splits B Hq rows 1028 bytes: 32
- *     rows of 16 heads at batch 2 fit up to 63 chunks.
+ *     At head_dim 256 the partials of n_splits chunks take n_splits B Hq rows 1028 bytes (fp32)
+ *     below 8 MiB of values and 520 bytes (fp16 and a power of two) from there: 32 rows of 16
+ *     heads at batch 2 fit up to 126 chunks.
  *   - Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
  *     different streams) race and must be ordered by the caller.  Nothing in the scratch needs
  *     to start at zero: the main pass writes every partial the merge reads.

@@ -304,19 +304,30 @@ void sweep() {
                 CHECK((g_fwd_shape == 0 ? 4 : 8) == info.waves_per_block, "shape");
                 CHECK(g_fwd_shape != 3 || op == ATTN_OP_DECODE, "the streaming shape is for decode rows");
                 if (split) {
+                  const size_t nrow = (size_t)info.n_splits * B * hh[0] * rows;
+                  const char* o = reinterpret_cast<const char*>(g_fwd.part_o);
                   const char* lse = reinterpret_cast<const char*>(g_fwd.part_lse);
-                  CHECK(reinterpret_cast<const char*>(g_fwd.part_o) == kWs && lse > kWs &&
-                            lse + 4 * (size_t)info.n_splits * B * hh[0] * rows <= kWs + bytes,
-                        "partials outside the workspace");
-                  CHECK(g_merge.n_chunks == info.n_splits && g_merge.D == D, "merge chunks / head dim");
+                  const char* ex = reinterpret_cast<const char*>(g_fwd.part_e);
+                  const int kind = g_fwd.part_kind;
+                  CHECK(kind == (nrow * 4 * D >= (8u << 20) ? 1 : 0), "partial kind");
+                  CHECK(o == kWs && lse >= o + (kind ? 2 : 4) * D * nrow &&
+                            (kind ? ex >= lse + 4 * nrow && ex + 4 * nrow <= kWs + bytes
+                                  : !ex && lse + 4 * nrow <= kWs + bytes),
+                        "partials outside the workspace or overlapping");
+                  CHECK(g_merge.n_chunks == info.n_splits && g_merge.D == D && g_merge.part_kind == kind &&
+                            g_merge.part_o == g_fwd.part_o && g_merge.part_lse == g_fwd.part_lse &&
+                            g_merge.part_e == g_fwd.part_e,
+                        "merge chunks / head dim / partials");
                 }
                 if (op == ATTN_OP_PREFILL) {
-                  int32_t n = 0;
-                  size_t lse_off = 0;
+                  int32_t n = 0, kind = -1;
+                  size_t lse_off = 0, exp_off = 0;
                   const long m1 = g_launch_merge;
-                  CHECK(attn_prefill_partials(&a, kWs, bytes, kStream, &n, &lse_off) == ATTN_OK, "partials");
+                  CHECK(attn_prefill_partials(&a, kWs, bytes, kStream, &n, &kind, &lse_off, &exp_off) == ATTN_OK,
+                        "partials");
                   CHECK(n == info.n_splits && g_launch_merge == m1, "partials: chunks or a merge");
-                  CHECK(!split || lse_off > 0, "lse offset");
+                  CHECK(!split || (kind == g_fwd.part_kind && lse_off > 0 && (kind ? exp_off > lse_off : !exp_off)),
+                        "partial kind / lse / exponent offsets");
                 }
               }
             }
@@ -401,6 +412,14 @@ void aux_calls() {
   CHECK(attn_merge(&m2, kStream) == ATTN_E_LAYOUT, "merge lse alignment");
   m2 = m, m2.D = 32;
   CHECK(attn_merge(&m2, kStream) == ATTN_E_HEAD_DIM, "merge head dim");
+  m2 = m, m2.partial_kind = 2;
+  CHECK(attn_merge(&m2, kStream) == ATTN_E_ARG, "merge partial kind");
+  m2 = m, m2.partial_kind = 1;
+  CHECK(attn_merge(&m2, kStream) == ATTN_E_NULL, "merge fp16 partials without exponents");
+  m2.partial_exp = reinterpret_cast<const int32_t*>(kWs + 8192 + 2);
+  CHECK(attn_merge(&m2, kStream) == ATTN_E_LAYOUT, "merge exponent alignment");
+  m2.partial_exp = reinterpret_cast<const int32_t*>(kWs + 8192);
+  CHECK(attn_merge(&m2, kStream) == ATTN_OK, "merge fp16 partials");
 
   int sizes[64], n = 0;
   for (int rows = 0; rows <= 40; ++rows)

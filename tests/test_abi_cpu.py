@@ -183,8 +183,9 @@ def test_other_head_dims(D):
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_tile_keys_per_head_dim(D):
     # the main pass moves 16 KiB K and V tiles at every head dim: 8192 / D keys a tile; splits
-    # are whole tiles, the workspace holds fp32 partials of D per (split, b, h, row) and an lse per
-    # row, each part rounded up to 256 bytes
+    # are whole tiles, the workspace holds a partial row of D values per (split, b, h, row), fp32
+    # below 8 MiB of them and fp16 from there, then an fp32 lse per row and (fp16 only) an int32
+    # exponent per row, each part rounded up to 256 bytes
     lib = ga.lib()
     T = 8192 // D
     r256 = lambda x: (x + 255) // 256 * 256
@@ -201,8 +202,10 @@ def test_tile_keys_per_head_dim(D):
             if asked:
                 assert S <= asked
             nrow = S * B * Hq * rows
-            want = 0 if S == 1 else r256(nrow * D * 4) + r256(nrow * 4)
+            half = nrow * D * 4 >= 8 << 20
+            want = 0 if S == 1 else r256(nrow * D * (2 if half else 4)) + (2 if half else 1) * r256(nrow * 4)
             assert ga.workspace_bytes(a, op) == want and info["workspace_bytes"] == want
+            assert info["partial_kind"] == (1 if S > 1 and half else 0)
             if S > 1:
                 fn = lib.attn_prefill if op == _abi.OP_PREFILL else lib.attn_decode
                 assert fn(C.byref(a), C.c_void_p(1 << 20), want - 1, None) == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
@@ -273,6 +276,14 @@ def test_append_and_merge_rejections():
     m.n_chunks = 2
     m.partial_lse = (1 << 20) + 2
     assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_LAYOUT"]
+    m.partial_lse = 1 << 20
+    m.partial_kind = 2  # fp32 (0) and fp16 with exponents (1) only
+    assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_ARG"]
+    m.partial_kind = 1  # fp16 partials need their exponents, 4-byte aligned
+    assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    m.partial_exp = (1 << 20) + 2
+    assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_LAYOUT"]
+    m.partial_kind = 0
     m.partial_o = None
     assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
     for D in (96, 32, 512):  # head dims 256, 128 and 64 only
@@ -312,12 +323,15 @@ def test_keep_rejections():
 def test_prefill_partials_needs_its_outputs():
     lib = ga.lib()
     a = _good(rows=512, kv_offset=4096)
-    n, off = C.c_int32(7), C.c_size_t(7)
-    assert lib.attn_prefill_partials(C.byref(a), None, 0, None, None, C.byref(off)) == _abi.STATUS_CODE["ATTN_E_NULL"]
-    assert lib.attn_prefill_partials(C.byref(a), None, 0, None, C.byref(n), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    n, kind, off, eoff = C.c_int32(7), C.c_int32(7), C.c_size_t(7), C.c_size_t(7)
+    E = _abi.STATUS_CODE["ATTN_E_NULL"]
+    outs = [C.byref(n), C.byref(kind), C.byref(off), C.byref(eoff)]
+    for i in range(4):
+        assert lib.attn_prefill_partials(C.byref(a), None, 0, None, *[None if j == i else x for j, x in
+                                                                       enumerate(outs)]) == E
     need = ga.workspace_bytes(a, _abi.OP_PREFILL)
     assert need > 0
-    st = lib.attn_prefill_partials(C.byref(a), None, 0, None, C.byref(n), C.byref(off))
+    st = lib.attn_prefill_partials(C.byref(a), None, 0, None, *outs)
     assert st == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
 
 

@@ -182,8 +182,11 @@ def test_fused_small_head_dims_split_keys(D, dtype):
     ws = torch.empty(ga.workspace_bytes(ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off, D=D,
                                                      n_splits=3), 0), dtype=torch.uint8, device="cuda")
     out, parts = ga.prefill_partials(q, k, v, g, kv_offset=off, n_splits=3, workspace=ws)
+    kind = ga.describe_plan(ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off, D=D, n_splits=3),
+                            0)["partial_kind"]
     assert parts is not None and parts[0].shape == (3, B, Hq, rows, D)
-    ga.merge(parts[0], parts[1], g, out=out)
+    assert parts[0].dtype == (torch.float16 if kind else torch.float32) and (parts[2] is None) == (kind == 0)
+    ga.merge(parts[0], parts[1], g, out=out, partial_exp=parts[2])
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), outs[3].view(torch.int16))
 

@@ -339,6 +339,53 @@ def test_merge_matches_oracle(n_chunks, D):
     _say(assert_close(got, ref, f"merge {n_chunks} chunks, D={D}"))
 
 
+def _fp16_rows(o):
+    """The main pass's partial form (merge_args partial_kind 1) of float64 partials o [..., D]:
+    per row the exponent e that puts the largest magnitude in [0.5, 1) (0 for a zero or nonfinite
+    row) and the values times 2^-e rounded to fp16 (nearest even).  Returns the float16 values,
+    the int32 exponents [...] and the exact values they stand for (float64)."""
+    with np.errstate(invalid="ignore"):
+        mx = np.nanmax(np.abs(o), axis=-1)
+    e = np.where((mx > 0) & np.isfinite(mx), np.frexp(np.where(np.isfinite(mx), mx, 1.0))[1], 0).astype(np.int32)
+    vals = np.ldexp(o, -e[..., None]).astype(np.float16)
+    return vals, e, np.ldexp(vals.astype(np.float64), e[..., None])
+
+
+@needs_gpu
+@pytest.mark.parametrize("D", [256, 128, 64])
+@pytest.mark.parametrize("n_chunks", [5, 21, 100])
+@pytest.mark.parametrize("mag", [1.0, 1e-30, 1e30])
+def test_merge_fp16_rows(n_chunks, D, mag):
+    # the partial form the main pass leaves (fp16 values and a power-of-two exponent per row)
+    # through attn_merge: against the oracle at V magnitudes 1, 1e-30 and 1e30 (the exponent keeps
+    # fp16 in range), and bit for bit against the fp32 form of the same values (the decode is exact)
+    rng = syn.streams(9)
+    B, Hq, Hkv, rows, kv = 1, 8, 2, 5, 90
+    q = syn.widen(syn.normal_bits(rng["q"], (B, Hq, rows, D)))
+    k = syn.widen(syn.normal_bits(rng["k"], (B, Hkv, kv, D)))
+    v = syn.widen(syn.normal_bits(rng["v"], (B, Hkv, kv, D))) * mag
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D))
+    step = max(1, 120 // n_chunks)
+    chunks = [(c * step, (c + 1) * step) for c in range(n_chunks)]
+    o, l_ = reference.partials(q, k, v, n_kv_heads=Hkv, kv_offset=kv - rows, kv_len=kv, chunks=chunks)
+    l32 = l_.astype(np.float32)
+    l32[:, 0, 3, 2] = -np.inf  # a row empty in every chunk: 0 whatever its partials hold
+    o = o.copy()
+    o[:, 0, 3, 2, :] = np.nan
+    vals16, exps, exact = _fp16_rows(o)
+    out16 = torch.full((B, Hq, rows, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ga.merge(torch.from_numpy(vals16).cuda(), torch.from_numpy(l32).cuda(), to_dev(gb), out=out16,
+             partial_exp=torch.from_numpy(exps).cuda())
+    out32 = torch.full_like(out16, float("nan"))
+    ga.merge(torch.from_numpy(exact.astype(np.float32)).cuda(), torch.from_numpy(l32).cuda(), to_dev(gb), out=out32)
+    assert torch.equal(out16.view(torch.int16), out32.view(torch.int16)), "fp16 rows and their fp32 values differ"
+    ref = reference.merge(np.nan_to_num(o, nan=0.0), l_, syn.widen(gb))
+    ref[0, 3, 2, :] = 0.0
+    got = to_f64(out16)
+    assert np.all(got[0, 3, 2, :] == 0.0)
+    _say(assert_close(got / mag, ref / mag, f"merge fp16 rows {n_chunks} chunks, D={D}, |v|~{mag:g}"))
+
+
 @needs_gpu
 def test_closed_forms_on_gpu():
     # constant V: every row returns c * sigmoid(gate); row 0 of a prompt sees one key: V_0 * sigmoid(gate)
@@ -411,3 +458,36 @@ def test_planted_row_past_its_own_key_is_not_seen():
     past = reference.attention(syn.widen(qb2), k, syn.widen(vb), syn.widen(gb), n_kv_heads=Hkv, kv_offset=off + 1,
                                kv_len=off + rows + 1)
     assert not compare(out, past)["ok"]
+
+
+@needs_gpu
+@pytest.mark.parametrize("n_splits,kind", [(3, 0), (5, 1)])
+@pytest.mark.parametrize("mag", [1.0, 1e-30])
+def test_split_partials_either_side_of_the_fp16_line(n_splits, kind, mag):
+    # 512 rows of 8 heads at head dim 128: 2 MiB of fp32 partials per split, so 3 splits keep
+    # fp32 partials (6 MiB) and 5 take fp16 ones with a power of two per row (10 MiB); both against
+    # the oracle, through attn_prefill and through attn_prefill_partials + attn_merge (bit for
+    # bit with it), with V of magnitude 1 and 1e-30 (the exponent keeps fp16 in range)
+    D, B, Hq, Hkv, rows, off = 128, 1, 8, 2, 512, 1536
+    rng = syn.streams(77)
+    qb = syn.normal_bits(rng["q"], (B, Hq, rows, D))
+    kb = syn.normal_bits(rng["k"], (B, Hkv, off + rows, D))
+    vb = syn.normal_bits(rng["v"], (B, Hkv, off + rows, D), scale=mag)
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D))
+    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    a = ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off, D=D, n_splits=n_splits)
+    d = ga.describe_plan(a, 0)
+    _say("partials", n_splits, d["n_splits"], d["partial_kind"], mag)
+    assert d["n_splits"] == n_splits and d["partial_kind"] == kind
+    out = ga.prefill(q, k, v, g, kv_offset=off, n_splits=n_splits)
+    ws = torch.empty(d["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    out2, parts = ga.prefill_partials(q, k, v, g, kv_offset=off, n_splits=n_splits, workspace=ws)
+    assert parts is not None and parts[0].shape == (n_splits, B, Hq, rows, D)
+    assert parts[0].dtype == (torch.float16 if kind else torch.float32) and (parts[2] is None) == (kind == 0)
+    ga.merge(parts[0], parts[1], g, out=out2, partial_exp=parts[2])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    ref = reference.attention(*(syn.widen(x) for x in (qb, kb, vb, gb)), n_kv_heads=Hkv, kv_offset=off,
+                              kv_len=off + rows)
+    _say(assert_close(to_f64(out) / mag, ref / mag, f"split partials kind {kind}, |v|~{mag:g}"))
+

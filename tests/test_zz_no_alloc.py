@@ -67,13 +67,14 @@ def test_decode_noalloc_matches_decode_twice(dtype):
 
 @needs_gpu
 def test_decode_noalloc_refuses_partials_past_the_scratch():
-    # 32 rows of 16 heads at batch 4 over 32768 keys: 61 chunks need 125 MiB of partials
+    # 32 rows of 16 heads at batch 4 over 32768 keys, asked for 128 splits: 114 chunks of 532 bytes
+    # per row need 118 MiB of partials
     B, Hq, Hkv, rows, off = 4, 16, 2, 32, 32768
     q = torch.zeros((B, Hq, rows, 256), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((B, Hkv, off + rows, 256), dtype=torch.bfloat16, device="cuda")
     out = torch.full_like(q, float("nan"))
     a = ga._args(q, k, k, q, out, kv_offset=off, kv_len=off + rows, causal=True, scale=0.0, head_chunk=0,
-                 n_splits=0, mask=None)
+                 n_splits=128, mask=None)
     assert ga.workspace_bytes(a, _abi.OP_DECODE) > _abi.SCRATCH_BYTES
     assert ga.lib().attn_decode_noalloc(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_WORKSPACE"]
     torch.cuda.synchronize()
