@@ -133,14 +133,19 @@ struct PartialLoad {
   int32_t e;  // KIND 1: the row's exponent
 };
 template <int KIND>
-__device__ __forceinline__ PartialLoad<KIND> load_partial(const MergeParams& p, int64_t row, int dl) {
+__device__ __forceinline__ PartialLoad<KIND> load_values(const MergeParams& p, int64_t row, int dl) {
   PartialLoad<KIND> x;
   if constexpr (KIND == 0) {
     x.f = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.part_o) + row * p.D + dl);
   } else {
     x.h = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.part_o) + row * p.D + dl);
-    x.e = p.part_e[row];
   }
+  return x;
+}
+template <int KIND>
+__device__ __forceinline__ PartialLoad<KIND> load_partial(const MergeParams& p, int64_t row, int dl) {
+  PartialLoad<KIND> x = load_values<KIND>(p, row, dl);
+  if constexpr (KIND == 1) x.e = p.part_e[row];
   return x;
 }
 template <int KIND>
@@ -267,9 +272,11 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
 }
 
 // Few chunks (prompt blocks split a handful of ways): one wavefront per row, four rows per
-// workgroup, four dims per lane, and every chunk's partial loaded at once (independent loads),
-// so the pass streams instead of waiting on one load after another.
-template <int DT, int KIND>
+// workgroup, four dims per lane, NC (the chunk count, 1..8) partial loads issued at once
+// (independent loads), so the pass streams instead of waiting on one load after another.  The
+// row's NC lse values (and exponents) come in one load each, lane c holding chunk c's, and are
+// read out of those lanes.
+template <int DT, int KIND, int NC>
 __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
@@ -283,48 +290,50 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   const int h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
   const int d0 = 4 * lane;
   const int dl = min(d0, p.D - 4);  // lanes past the head dim re-read its last 4 dims and store nothing
-  // every load is unconditional (chunk indices past the last one re-read the last one) so
-  // they are all in flight together; chunks past the last one are selected out below
-  float lc[kFewChunks];
-  PartialLoad<KIND> raw[kFewChunks];
-  const int nch = GQA_CONTROL == 2 ? max(p.n_chunks - 1, 1) : p.n_chunks;
+  constexpr int nch = GQA_CONTROL == 2 ? (NC > 1 ? NC - 1 : 1) : NC;
   const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
   const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + dl);
+  // lane c (c < nch; the others re-read chunk nch - 1) loads chunk c's lse and exponent
+  const int64_t lrow = (int64_t)min(lane, nch - 1) * n_rows + row_id;
+  const float lse_lane = p.part_lse[lrow];
+  int32_t e_lane = 0;
+  if constexpr (KIND == 1) e_lane = p.part_e[lrow];
+  PartialLoad<KIND> raw[nch];
 #pragma unroll
-  for (int c = 0; c < kFewChunks; ++c) {
-    const int cc = min(c, nch - 1);
-    lc[c] = p.part_lse[(int64_t)cc * n_rows + row_id];
-    raw[c] = load_partial<KIND>(p, (int64_t)cc * n_rows + row_id, dl);
-  }
-  // one use of every partial and lse here keeps all the loads together, in one round trip (left
-  // to the weighted sum, the compiler sinks each partial's load into its chunk's branch, after
-  // the lse loads have come back and the row's largest lse is known)
+  for (int c = 0; c < nch; ++c) raw[c] = load_values<KIND>(p, (int64_t)c * n_rows + row_id, dl);
+  // one use of every partial here keeps all the loads together, in one round trip (left to the
+  // weighted sum, the compiler sinks each partial's load into its chunk's branch, after the lse
+  // loads have come back and the row's largest lse is known)
 #pragma unroll
-  for (int c = 0; c < kFewChunks; ++c) {
+  for (int c = 0; c < nch; ++c) {
     if constexpr (KIND == 0) {
       asm volatile("" ::"v"(raw[c].f));
     } else {
-      asm volatile("" ::"v"(raw[c].h), "v"(raw[c].e));
+      asm volatile("" ::"v"(raw[c].h));
     }
-    asm volatile("" : "+v"(lc[c]));
   }
-  f32x4 oc[kFewChunks];
+  float lc[nch];
+  f32x4 oc[nch];
 #pragma unroll
-  for (int c = 0; c < kFewChunks; ++c) oc[c] = decode_partial<KIND>(raw[c]);
+  for (int c = 0; c < nch; ++c) {
+    lc[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lse_lane), c));
+    if constexpr (KIND == 1) raw[c].e = __builtin_amdgcn_readlane(e_lane, c);
+    oc[c] = decode_partial<KIND>(raw[c]);
+  }
   float top = -INFINITY;
   bool nan_l = false;  // a chunk whose lse is NaN makes the row NaN, as the unsplit definition does
 #pragma unroll
-  for (int c = 0; c < kFewChunks; ++c) {
-    top = c < nch ? fmaxf(top, lc[c]) : top;
-    nan_l = nan_l || (c < nch && __builtin_isnan(lc[c]));
+  for (int c = 0; c < nch; ++c) {
+    top = fmaxf(top, lc[c]);
+    nan_l = nan_l || __builtin_isnan(lc[c]);
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
   if (top > -INFINITY) {
 #pragma unroll
-    for (int c = 0; c < kFewChunks; ++c) {
+    for (int c = 0; c < nch; ++c) {
       // an empty chunk is selected out, never multiplied in
-      if (c < nch && lc[c] != -INFINITY) {
+      if (lc[c] != -INFINITY) {
         const float w = exp2f((lc[c] - top) * kLog2e);
         acc += w * oc[c];
         wsum += w;
@@ -414,13 +423,31 @@ hipError_t launch_keep(const KeepParams& p, int B, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int KIND, int NC>
+void launch_few_nc(const MergeParams& p, int dtype, dim3 grid, hipStream_t stream) {
+  if (dtype == 0) hipLaunchKernelGGL((merge_few_kernel<0, KIND, NC>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((merge_few_kernel<1, KIND, NC>), grid, dim3(256), 0, stream, p);
+}
+template <int KIND>
+void launch_few(const MergeParams& p, int dtype, dim3 grid, hipStream_t stream) {
+  switch (p.n_chunks) {
+    case 1: launch_few_nc<KIND, 1>(p, dtype, grid, stream); break;
+    case 2: launch_few_nc<KIND, 2>(p, dtype, grid, stream); break;
+    case 3: launch_few_nc<KIND, 3>(p, dtype, grid, stream); break;
+    case 4: launch_few_nc<KIND, 4>(p, dtype, grid, stream); break;
+    case 5: launch_few_nc<KIND, 5>(p, dtype, grid, stream); break;
+    case 6: launch_few_nc<KIND, 6>(p, dtype, grid, stream); break;
+    case 7: launch_few_nc<KIND, 7>(p, dtype, grid, stream); break;
+    default: launch_few_nc<KIND, 8>(p, dtype, grid, stream); break;
+  }
+}
+
 template <int KIND>
 void launch_merge_k(const MergeParams& p, int dtype, hipStream_t stream) {
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
   if (p.n_chunks <= kFewChunks) {
     const dim3 grid((unsigned)((n_rows + 3) / 4));
-    if (dtype == 0) hipLaunchKernelGGL((merge_few_kernel<0, KIND>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((merge_few_kernel<1, KIND>), grid, dim3(256), 0, stream, p);
+    launch_few<KIND>(p, dtype, grid, stream);
   } else {
     const dim3 grid((unsigned)n_rows);
     const int mw = merge_waves(p.n_chunks);
