@@ -124,8 +124,8 @@ __device__ __forceinline__ void exact_row(const RepairParams& f, int D, int b, i
 }
 
 // Four values of a split partial row: KIND 0 fp32 rows of D values; KIND 1 the main pass's
-// fp16 rows, value times 2^e (partial_row_bytes, e from its own array).  Loads (issued
-// together) and decode apart.
+// fp16 rows, value times 2^e (partial_row_bytes; e from its own array, loaded by the caller).
+// Loads (issued together) and decode apart.
 template <int KIND>
 struct PartialLoad {
   f32x4 f;    // KIND 0
@@ -140,12 +140,6 @@ __device__ __forceinline__ PartialLoad<KIND> load_values(const MergeParams& p, i
   } else {
     x.h = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.part_o) + row * p.D + dl);
   }
-  return x;
-}
-template <int KIND>
-__device__ __forceinline__ PartialLoad<KIND> load_partial(const MergeParams& p, int64_t row, int dl) {
-  PartialLoad<KIND> x = load_values<KIND>(p, row, dl);
-  if constexpr (KIND == 1) x.e = p.part_e[row];
   return x;
 }
 template <int KIND>
@@ -197,17 +191,26 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
   for (int c0 = 0; c0 < nch; c0 += kMergeWaves * kMergeBatch) {
     // this pass's chunks of the wavefront, all loads in flight together (indices past the
     // last chunk re-read it and are selected out)
-    float lc[kMergeBatch];
+    // lane j (j < kMergeBatch) loads the lse and exponent of the wavefront's j-th chunk; they are
+    // read out of those lanes as scalars
+    const int64_t lrow = (int64_t)min(c0 + wave + min(lane, kMergeBatch - 1) * kMergeWaves, nch - 1) * n_rows + row_id;
+    const float lse_lane = p.part_lse[lrow];
+    int32_t e_lane = 0;
+    if constexpr (KIND == 1) e_lane = p.part_e[lrow];
     PartialLoad<KIND> raw[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       const int cc = min(c0 + wave + j * kMergeWaves, nch - 1);
-      lc[j] = p.part_lse[(int64_t)cc * n_rows + row_id];
-      raw[j] = load_partial<KIND>(p, (int64_t)cc * n_rows + row_id, dl);
+      raw[j] = load_values<KIND>(p, (int64_t)cc * n_rows + row_id, dl);
     }
+    float lc[kMergeBatch];
     f32x4 oc[kMergeBatch];
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) oc[j] = decode_partial<KIND>(raw[j]);
+    for (int j = 0; j < kMergeBatch; ++j) {
+      lc[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lse_lane), j));
+      if constexpr (KIND == 1) raw[j].e = __builtin_amdgcn_readlane(e_lane, j);
+      oc[j] = decode_partial<KIND>(raw[j]);
+    }
     float top = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
