@@ -3,9 +3,10 @@
 One step = one pass of the whole path over one batch of synthetic input:
   1. prefill: the 32768-token causal prompt of the 27B shape (batch 1, 24 query heads over
      4 KV heads, head_dim 256, bf16, gated) in query blocks of q_block rows: kv_append of the
-     block's K/V, then the block's attn_prefill, issued as its two launches (the main pass by
-     attn_prefill_partials, then attn_merge when the keys are split) on one stream, so that
-     events can bracket the main pass alone;
+     first block's K/V, then per block its attn_prefill, issued as its two launches (the main
+     pass by attn_prefill_partials, then attn_merge when the keys are split, carrying the next
+     block's kv_append in the same launch; a kv_append of its own otherwise) on one stream, so
+     that events can bracket the main pass alone;
   2. decode: the head-chunked verify workload of the 35B-A3B shape (batch 2, 16 query heads
      over 2 KV heads) at KV offset 32768 with one row and its broadcast additive mask holding
      -Inf entries: kv_append, then attn_decode, on a cache chosen round-robin from enough
@@ -404,17 +405,22 @@ def main():
     setup_s = time.time() - t_setup
 
     def prefill_pass(per_call=None):
+        ga.kv_append(k[:, :, :min(qL, N)], v[:, :, :min(qL, N)], kc, vc, kv_offset=0)
         for i, s in enumerate(range(0, N, qL)):
             e = min(s + qL, N)
-            ga.kv_append(k[:, :, s:e], v[:, :, s:e], kc, vc, kv_offset=s)
             if per_call is not None:
                 per_call[i][0].record(stream)
             _, parts = ga.prefill_partials(q[:, :, s:e], kc, vc, g[:, :, s:e], kv_offset=s, kv_len=e,
                                            out=out[:, :, s:e], workspace=ws)
             if per_call is not None:
                 per_call[i][1].record(stream)
+            # the next block's append rides on this block's merge (one launch), else goes alone
+            e2 = min(e + qL, N)
+            nxt = (k[:, :, e:e2], v[:, :, e:e2], kc, vc, e) if e < N else None
             if parts is not None:
-                ga.merge(parts[0], parts[1], g[:, :, s:e], out=out[:, :, s:e], partial_exp=parts[2])
+                ga.merge(parts[0], parts[1], g[:, :, s:e], out=out[:, :, s:e], partial_exp=parts[2], append=nxt)
+            elif nxt is not None:
+                ga.kv_append(*nxt[:4], kv_offset=e)
 
     # ---- profiler mode: one workload, --steps times
     if args.only:

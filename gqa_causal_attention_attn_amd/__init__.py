@@ -116,13 +116,17 @@ def _args(q, k_cache, v_cache, gate, out, *, kv_offset, kv_len, causal, scale, h
 
 
 def _run(op: int, q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
-         n_splits=0, mask=None, out=None, workspace=None):
+         n_splits=0, mask=None, out=None, workspace=None, append=None):
     if kv_len is None:
         kv_len = kv_offset + q.shape[2]
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     a = _args(q, k_cache, v_cache, gate, out, kv_offset=kv_offset, kv_len=kv_len, causal=causal, scale=scale,
               head_chunk=head_chunk, n_splits=n_splits, mask=mask)
+    app = None
+    if append is not None:  # (k_new, v_new, k_cache, v_cache, kv_offset) of a kv_append the call carries
+        app = _append_args(*append)
+        a.append = C.pointer(app)
     L = lib()
     need = C.c_size_t(0)
     _check(L.attn_workspace_bytes(C.byref(a), op, C.byref(need)))
@@ -170,10 +174,13 @@ def prefill_partials(q, k_cache, v_cache, gate, *, kv_offset: int, workspace, kv
 
 
 def prefill(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
-            n_splits=0, mask=None, out=None, workspace=None):
-    """attn_prefill: q/gate [B, Hq, rows, D], caches [B, Hkv, capacity, D] (D = 256, 128 or 64); returns out."""
+            n_splits=0, mask=None, out=None, workspace=None, append=None):
+    """attn_prefill: q/gate [B, Hq, rows, D], caches [B, Hkv, capacity, D] (D = 256, 128 or 64); returns out.
+    append = (k_new, v_new, k_cache, v_cache, kv_offset): a kv_append the call carries (attn_args
+    append: in the merge's launch when the keys are split), e.g. the next query block's rows."""
     return _run(_abi.OP_PREFILL, q, k_cache, v_cache, gate, kv_offset=kv_offset, kv_len=kv_len, causal=causal,
-                scale=scale, head_chunk=head_chunk, n_splits=n_splits, mask=mask, out=out, workspace=workspace)
+                scale=scale, head_chunk=head_chunk, n_splits=n_splits, mask=mask, out=out, workspace=workspace,
+                append=append)
 
 
 def decode(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
@@ -206,6 +213,11 @@ def prefill_composed(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, 
 
 def kv_append(k_new, v_new, k_cache, v_cache, *, kv_offset: int) -> None:
     """kv_append: copy [B, Hkv, rows, D] rows into the caches at kv_offset, bit for bit."""
+    a = _append_args(k_new, v_new, k_cache, v_cache, kv_offset)
+    _check(lib().kv_append(C.byref(a), _stream_handle(k_new)))
+
+
+def _append_args(k_new, v_new, k_cache, v_cache, kv_offset):
     a = _abi.KvAppendArgs()
     a.dtype = _dtype_code(k_new)
     a.B, a.Hkv, a.rows, a.D = k_new.shape[0], k_new.shape[1], k_new.shape[2], k_new.shape[3]
@@ -219,7 +231,7 @@ def kv_append(k_new, v_new, k_cache, v_cache, *, kv_offset: int) -> None:
         raise ValueError("k and v shapes differ")
     if k_cache.shape[0] != k_new.shape[0] or k_cache.shape[1] != k_new.shape[1]:
         raise ValueError("cache and new rows disagree on batch or KV heads")
-    _check(lib().kv_append(C.byref(a), _stream_handle(k_new)))
+    return a
 
 
 
@@ -251,10 +263,12 @@ def kv_keep(k_cache, v_cache, *, kv_offset: int, rows: int, keep) -> None:
         raise ValueError("k_cache and v_cache differ")
     _check(lib().kv_keep(C.byref(a), _stream_handle(k_cache)))
 
-def merge(partial_o, partial_lse, gate, out=None, partial_exp=None):
+def merge(partial_o, partial_lse, gate, out=None, partial_exp=None, append=None):
     """attn_merge: partial_o [C, B, Hq, rows, D] (D 256, 128 or 64) fp32, or fp16 with
     partial_exp [C, B, Hq, rows] int32 (the form prefill_partials returns: the partial is
-    partial_o times 2^partial_exp); partial_lse [C, B, Hq, rows] fp32 (natural log)."""
+    partial_o times 2^partial_exp); partial_lse [C, B, Hq, rows] fp32 (natural log).
+    append = (k_new, v_new, k_cache, v_cache, kv_offset): a kv_append of those rows carried by
+    the same launch (it must not touch what the merge reads or writes)."""
     if partial_o.dtype not in (torch.float32, torch.float16) or partial_lse.dtype != torch.float32:
         raise TypeError("partial_o is float32 or float16, partial_lse float32")
     fp16 = partial_o.dtype == torch.float16
@@ -276,6 +290,11 @@ def merge(partial_o, partial_lse, gate, out=None, partial_exp=None):
     a.partial_o, a.partial_lse = partial_o.data_ptr(), partial_lse.data_ptr()
     a.partial_exp = partial_exp.data_ptr() if fp16 else None
     a.gate, a.out = _t4(gate), _t4(out)
+    app = None
+    if append is not None:
+        k_new, v_new, k_cache, v_cache, kv_offset = append
+        app = _append_args(k_new, v_new, k_cache, v_cache, kv_offset)
+        a.append = C.pointer(app)
     _check(lib().attn_merge(C.byref(a), _stream_handle(gate)))
     return out
 
@@ -357,8 +376,11 @@ def prompt_policy(*, D: int, B: int, Hq: int, Hkv: int, n_tokens: int, dtype: st
 
 def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int = 0, kv_offset: int = 0, out=None,
                    workspace=None, head_chunk=0, n_splits=0, overlap_merge=False, composed=False):
-    """A prompt in query blocks: for each block, kv_append its K/V rows, then attn_prefill it
-    (attn_prefill_composed with composed=True).
+    """A prompt in query blocks: each block's K/V rows are appended to the caches (kv_append),
+    then the block runs attn_prefill (attn_prefill_composed with composed=True).  On the fused
+    route without overlap_merge the first block's rows go by kv_append and every block's
+    attn_prefill carries the next block's rows (attn_args append: in the merge's launch when the
+    keys are split), one launch fewer per block.
 
     q/gate [B, Hq, N, D] and k/v [B, Hkv, N, D] hold the prompt (positions kv_offset ..
     kv_offset + N - 1); k_cache/v_cache have room for them.  Block i attends to the cache plus
@@ -395,11 +417,14 @@ def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int = 0, kv_offs
             need = max(need, workspace_bytes(a, _abi.OP_PREFILL))
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if not overlap_merge:
+        # each block's call carries the next block's append (in its merge when the keys are split)
+        kv_append(k[:, :, :min(q_block, N)], v[:, :, :min(q_block, N)], k_cache, v_cache, kv_offset=kv_offset)
         for s in range(0, N, q_block):
             e = min(s + q_block, N)
-            kv_append(k[:, :, s:e], v[:, :, s:e], k_cache, v_cache, kv_offset=kv_offset + s)
+            e2 = min(e + q_block, N)
+            nxt = (k[:, :, e:e2], v[:, :, e:e2], k_cache, v_cache, kv_offset + e) if e < N else None
             prefill(q[:, :, s:e], k_cache, v_cache, gate[:, :, s:e], kv_offset=kv_offset + s, kv_len=kv_offset + e,
-                    out=out[:, :, s:e], workspace=workspace, head_chunk=head_chunk, n_splits=n_splits)
+                    out=out[:, :, s:e], workspace=workspace, head_chunk=head_chunk, n_splits=n_splits, append=nxt)
         return out
     main = torch.cuda.current_stream(q.device)
     side = merge_stream(q.device)

@@ -42,18 +42,18 @@ class Mask(C.Structure):
                 ("ptr", C.c_void_p), ("stride_b", C.c_int64), ("stride_h", C.c_int64), ("stride_row", C.c_int64)]
 
 
+class KvAppendArgs(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("B", C.c_int32), ("Hkv", C.c_int32), ("D", C.c_int32), ("rows", C.c_int32),
+                ("reserved", C.c_int32), ("kv_offset", C.c_int64), ("capacity", C.c_int64), ("k_new", Tensor),
+                ("v_new", Tensor), ("k_cache", Tensor), ("v_cache", Tensor)]
+
+
 class AttnArgs(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("D", C.c_int32),
                 ("rows", C.c_int32), ("kv_offset", C.c_int64), ("kv_len", C.c_int64), ("capacity", C.c_int64),
                 ("scale", C.c_float), ("causal", C.c_int32), ("head_chunk", C.c_int32), ("n_splits", C.c_int32),
                 ("q", Tensor), ("gate", Tensor), ("out", Tensor), ("k_cache", Tensor), ("v_cache", Tensor),
-                ("mask", Mask)]
-
-
-class KvAppendArgs(C.Structure):
-    _fields_ = [("dtype", C.c_int32), ("B", C.c_int32), ("Hkv", C.c_int32), ("D", C.c_int32), ("rows", C.c_int32),
-                ("reserved", C.c_int32), ("kv_offset", C.c_int64), ("capacity", C.c_int64), ("k_new", Tensor),
-                ("v_new", Tensor), ("k_cache", Tensor), ("v_cache", Tensor)]
+                ("mask", Mask), ("append", C.POINTER(KvAppendArgs))]
 
 
 class KvKeepArgs(C.Structure):
@@ -66,7 +66,7 @@ class MergeArgs(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("n_chunks", C.c_int32), ("B", C.c_int32), ("Hq", C.c_int32),
                 ("rows", C.c_int32), ("D", C.c_int32), ("partial_o", C.c_void_p), ("partial_lse", C.c_void_p),
                 ("gate", Tensor), ("out", Tensor), ("partial_kind", C.c_int32),
-                ("partial_exp", C.c_void_p)]
+                ("partial_exp", C.c_void_p), ("append", C.POINTER(KvAppendArgs))]
 
 
 class PlanInfo(C.Structure):

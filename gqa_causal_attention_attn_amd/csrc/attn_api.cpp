@@ -250,6 +250,37 @@ inline int variant_of(const attn_args* a, const Plan& P) {
   return dslot * 128 + P.mask_lds * 32 + P.shape * 8 + a->dtype * 4 + a->mask.kind;
 }
 
+// Checks a kv_append call and fills its kernel parameters (kv_append, and an append carried by
+// attn_merge).
+int append_params(const kv_append_args* a, gqa::AppendParams* pp) {
+  if (!a) return ATTN_E_NULL;
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
+  if (a->B <= 0 || a->Hkv <= 0) return ATTN_E_HEADS;
+  if (a->D != 64 && a->D != 128 && a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
+  if (a->rows < 1) return ATTN_E_ROWS;
+  // (the planted late-append build writes one row further: its bound moves with it)
+  if (a->kv_offset < 0 || a->capacity < 1 || a->kv_offset + a->rows + (GQA_CONTROL == 3 ? 1 : 0) > a->capacity ||
+      a->capacity > INT32_MAX)
+    return ATTN_E_KV;
+  const attn_tensor* ts[4] = {&a->k_new, &a->v_new, &a->k_cache, &a->v_cache};
+  for (const attn_tensor* t : ts)
+    if (!t->ptr) return ATTN_E_NULL;
+  for (const attn_tensor* t : ts)
+    if (!aligned16(t->ptr) || !strides_ok(*t)) return ATTN_E_LAYOUT;
+  gqa::AppendParams& p = *pp;
+  for (int t = 0; t < 2; ++t) {
+    const attn_tensor& s = t ? a->v_new : a->k_new;
+    const attn_tensor& d = t ? a->v_cache : a->k_cache;
+    p.src[t] = static_cast<const uint16_t*>(s.ptr);
+    p.dst[t] = static_cast<uint16_t*>(d.ptr);
+    p.s_sb[t] = s.stride_b, p.s_sh[t] = s.stride_h, p.s_sr[t] = s.stride_row;
+    p.d_sb[t] = d.stride_b, p.d_sh[t] = d.stride_h, p.d_st[t] = d.stride_row;
+  }
+  p.B = a->B, p.Hkv = a->Hkv, p.rows = a->rows, p.kv_offset = (int)a->kv_offset;
+  p.chunk_shift = a->D == 64 ? 3 : a->D == 128 ? 4 : 5;
+  return ATTN_OK;
+}
+
 int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream, bool merge = true,
             int32_t* n_chunks = nullptr, int32_t* part_kind = nullptr, size_t* lse_offset = nullptr,
             size_t* exp_offset = nullptr) {
@@ -260,6 +291,14 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
   if (st) return st;
   if (ws_bytes < P.ws_bytes || (P.ws_bytes && !ws)) return ATTN_E_WORKSPACE;
   if (P.ws_bytes && !aligned16(ws)) return ATTN_E_LAYOUT;
+  gqa::AppendParams app;  // the append the call carries, if any
+  if (a->append) {
+    st = append_params(a->append, &app);
+    if (st) return st;
+    const bool carried = P.n_splits > 1 && merge;
+    const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
+    if (carried && !gqa::merge_with_append_fits(P.n_splits, n_rows, app)) return ATTN_E_ARG;
+  }
 
   gqa::FwdParams p;
   memset(&p, 0, sizeof(p));
@@ -326,7 +365,13 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
     f.m_sb = p.m_sb, f.m_sh = p.m_sh, f.m_sr = p.m_sr;
     f.mask_kind = a->mask.kind, f.G = P.G, f.kv_offset = p.kv_offset, f.kv_len = p.kv_len;
     f.causal = p.causal, f.keys_per_split = P.keys_per_split, f.scale_log2 = p.scale_log2;
+    if (a->append) {
+      mp.carry = 1;
+      mp.app = app;
+    }
     if (gqa::launch_merge(mp, a->dtype, s) != hipSuccess) return ATTN_E_HIP;
+  } else if (a->append) {
+    if (gqa::launch_append(app, s) != hipSuccess) return ATTN_E_HIP;
   }
   return ATTN_OK;
 }
@@ -522,6 +567,8 @@ int attn_prefill_composed(const attn_args* a, void* workspace, size_t ws_bytes, 
   const ComposedLayout L = composed_layout(a);
   if (!workspace || ws_bytes < L.s_bytes + L.p_bytes + L.l_bytes) return ATTN_E_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_E_LAYOUT;
+  gqa::AppendParams app;  // the append the call carries: a launch of its own after the route's
+  if (a->append && (st = append_params(a->append, &app)) != ATTN_OK) return st;
   gqa::ComposedParams p;
   memset(&p, 0, sizeof(p));
   p.q = static_cast<const uint16_t*>(a->q.ptr);
@@ -545,35 +592,14 @@ int attn_prefill_composed(const attn_args* a, void* workspace, size_t ws_bytes, 
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   p.scale_log2 = scale * 1.4426950408889634f;
   if (gqa::launch_composed(p, a->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
+  if (a->append && gqa::launch_append(app, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
 }
 
 int kv_append(const kv_append_args* a, void* stream) {
-  if (!a) return ATTN_E_NULL;
-  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
-  if (a->B <= 0 || a->Hkv <= 0) return ATTN_E_HEADS;
-  if (a->D != 64 && a->D != 128 && a->D != ATTN_HEAD_DIM) return ATTN_E_HEAD_DIM;
-  if (a->rows < 1) return ATTN_E_ROWS;
-  // (the planted late-append build writes one row further: its bound moves with it)
-  if (a->kv_offset < 0 || a->capacity < 1 || a->kv_offset + a->rows + (GQA_CONTROL == 3 ? 1 : 0) > a->capacity ||
-      a->capacity > INT32_MAX)
-    return ATTN_E_KV;
-  const attn_tensor* ts[4] = {&a->k_new, &a->v_new, &a->k_cache, &a->v_cache};
-  for (const attn_tensor* t : ts)
-    if (!t->ptr) return ATTN_E_NULL;
-  for (const attn_tensor* t : ts)
-    if (!aligned16(t->ptr) || !strides_ok(*t)) return ATTN_E_LAYOUT;
   gqa::AppendParams p;
-  for (int t = 0; t < 2; ++t) {
-    const attn_tensor& s = t ? a->v_new : a->k_new;
-    const attn_tensor& d = t ? a->v_cache : a->k_cache;
-    p.src[t] = static_cast<const uint16_t*>(s.ptr);
-    p.dst[t] = static_cast<uint16_t*>(d.ptr);
-    p.s_sb[t] = s.stride_b, p.s_sh[t] = s.stride_h, p.s_sr[t] = s.stride_row;
-    p.d_sb[t] = d.stride_b, p.d_sh[t] = d.stride_h, p.d_st[t] = d.stride_row;
-  }
-  p.B = a->B, p.Hkv = a->Hkv, p.rows = a->rows, p.kv_offset = (int)a->kv_offset;
-  p.chunk_shift = a->D == 64 ? 3 : a->D == 128 ? 4 : 5;
+  const int st = append_params(a, &p);
+  if (st) return st;
   if (gqa::launch_append(p, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
 }
@@ -627,6 +653,12 @@ int attn_merge(const merge_args* a, void* stream) {
   p.part_lse = a->partial_lse;
   p.part_e = a->partial_kind == 1 ? a->partial_exp : nullptr;
   p.part_kind = a->partial_kind;
+  if (a->append) {  // checked as kv_append checks its arguments; nothing is enqueued on an error
+    const int st = append_params(a->append, &p.app);
+    if (st) return st;
+    if (!gqa::merge_with_append_fits(a->n_chunks, n_rows, p.app)) return ATTN_E_ARG;
+    p.carry = 1;
+  }
   p.gate = static_cast<const uint16_t*>(a->gate.ptr);
   p.out = static_cast<uint16_t*>(a->out.ptr);
   p.g_sb = a->gate.stride_b, p.g_sh = a->gate.stride_h, p.g_sr = a->gate.stride_row;

@@ -153,6 +153,41 @@ __device__ __forceinline__ f32x4 decode_partial(const PartialLoad<KIND>& x) {
   }
 }
 
+// One workgroup (bx, by) of a gx x gy append grid of `nt` threads: one 16-byte chunk per thread.
+// Grid row by = (tensor, b, g); x runs over (row r, chunk c of 8 elements) = (r << chunk_shift)
+// + c, so the index arithmetic is shifts (one division per grid row).
+__device__ __forceinline__ void append_part(const AppendParams& p, uint32_t bx, uint32_t by, uint32_t gx,
+                                            uint32_t gy, uint32_t nt) {
+  const int64_t bg = (int64_t)p.B * p.Hkv;
+  const int64_t n = (int64_t)p.rows << p.chunk_shift;
+  const int cmask = (1 << p.chunk_shift) - 1;
+  for (int64_t y = by; y < 2 * bg; y += gy) {
+    const int t = y >= bg;
+    const int64_t yb = y - (t ? bg : 0);
+    const int b = (int)(yb / p.Hkv), g = (int)(yb - (int64_t)b * p.Hkv);
+    const uint16_t* src = p.src[t] + b * p.s_sb[t] + g * p.s_sh[t];
+    uint16_t* dst = p.dst[t] + b * p.d_sb[t] + g * p.d_sh[t] +
+                    (int64_t)(p.kv_offset + (GQA_CONTROL == 3 ? 1 : 0)) * p.d_st[t];
+    const int64_t s_sr = p.s_sr[t], d_st = p.d_st[t];
+    for (int64_t u = (int64_t)bx * nt + threadIdx.x; u < n; u += (int64_t)gx * nt) {
+      const int64_t r = u >> p.chunk_shift;
+      const int c = (int)(u & cmask);
+      const u32x4 val = *reinterpret_cast<const u32x4*>(src + r * s_sr + 8 * c);
+      *reinterpret_cast<u32x4*>(dst + r * d_st + 8 * c) = val;
+    }
+  }
+}
+
+// Workgroups of a merge launch past the merge's own run the kv_append it carries; returns
+// whether this workgroup was one of them (the whole workgroup, so it leaves before any barrier).
+__device__ __forceinline__ bool merge_carried_append(const MergeParams& p) {
+  if (blockIdx.x < (uint32_t)p.merge_blocks) return false;
+  const uint32_t a = blockIdx.x - (uint32_t)p.merge_blocks;
+  const uint32_t by = a / (uint32_t)p.app_bx;
+  append_part(p.app, a - by * (uint32_t)p.app_bx, by, (uint32_t)p.app_bx, (uint32_t)p.app_by, blockDim.x);
+  return true;
+}
+
 // whether any of the four values is NaN
 __device__ __forceinline__ bool has_nan4(const f32x4& x) { return __builtin_isnan(x[0] + x[1] + x[2] + x[3]); }
 
@@ -164,6 +199,7 @@ __device__ __forceinline__ bool has_nan4(const f32x4& x) { return __builtin_isna
 // sums meet in LDS.
 template <int DT, int MW, int KIND>
 __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
+  if (merge_carried_append(p)) return;
   constexpr int kMergeWaves = MW;
   __shared__ f32x4 part_acc[kMergeWaves][64];
   __shared__ float part_w[kMergeWaves];
@@ -281,6 +317,7 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
 // read out of those lanes.
 template <int DT, int KIND, int NC>
 __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
+  if (merge_carried_append(p)) return;
   const int lane = threadIdx.x & 63;
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
   const uint32_t row32 = blockIdx.x * 4u + (threadIdx.x >> 6);
@@ -362,28 +399,9 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   if (d0 < p.D) *reinterpret_cast<u32x2*>(orow + d0) = ow;
 }
 
-// One 16-byte chunk per thread.  Workgroup row y = (tensor, b, g); x runs over (row r, chunk c
-// of 8 elements) = (r << chunk_shift) + c, so the index arithmetic is shifts (one division per
-// workgroup row).  Head dims 64, 128 and 256.
+// kv_append: one workgroup of the append grid (append_part).  Head dims 64, 128 and 256.
 __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
-  const int64_t bg = (int64_t)p.B * p.Hkv;
-  const int64_t n = (int64_t)p.rows << p.chunk_shift;
-  const int cmask = (1 << p.chunk_shift) - 1;
-  for (int64_t y = blockIdx.y; y < 2 * bg; y += gridDim.y) {
-    const int t = y >= bg;
-    const int64_t yb = y - (t ? bg : 0);
-    const int b = (int)(yb / p.Hkv), g = (int)(yb - (int64_t)b * p.Hkv);
-    const uint16_t* src = p.src[t] + b * p.s_sb[t] + g * p.s_sh[t];
-    uint16_t* dst = p.dst[t] + b * p.d_sb[t] + g * p.d_sh[t] +
-                    (int64_t)(p.kv_offset + (GQA_CONTROL == 3 ? 1 : 0)) * p.d_st[t];
-    const int64_t s_sr = p.s_sr[t], d_st = p.d_st[t];
-    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < n; u += (int64_t)gridDim.x * 256) {
-      const int64_t r = u >> p.chunk_shift;
-      const int c = (int)(u & cmask);
-      const u32x4 val = *reinterpret_cast<const u32x4*>(src + r * s_sr + 8 * c);
-      *reinterpret_cast<u32x4*>(dst + r * d_st + 8 * c) = val;
-    }
-  }
+  append_part(p, blockIdx.x, blockIdx.y, gridDim.x, gridDim.y, 256);
 }
 
 // kv_keep: one workgroup per (b, g).  Every kept row of the block is read into registers
@@ -446,14 +464,25 @@ void launch_few(const MergeParams& p, int dtype, dim3 grid, hipStream_t stream) 
 }
 
 template <int KIND>
-void launch_merge_k(const MergeParams& p, int dtype, hipStream_t stream) {
-  const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
+void launch_merge_k(const MergeParams& p0, int dtype, hipStream_t stream) {
+  const int64_t n_rows = (int64_t)p0.B * p0.Hq * p0.rows;
+  MergeParams p = p0;
+  int64_t blocks;
+  int threads;
+  merge_shape(p.n_chunks, n_rows, &blocks, &threads);
+  p.merge_blocks = (int)blocks;
+  int64_t extra = 0;
+  if (p.carry) {
+    int64_t bx, by;
+    append_grid(p.app, threads, &bx, &by);
+    p.app_bx = (int)bx, p.app_by = (int)by;
+    extra = bx * by;
+  }
+  const dim3 grid((unsigned)(blocks + extra));
   if (p.n_chunks <= kFewChunks) {
-    const dim3 grid((unsigned)((n_rows + 3) / 4));
     launch_few<KIND>(p, dtype, grid, stream);
   } else {
-    const dim3 grid((unsigned)n_rows);
-    const int mw = merge_waves(p.n_chunks);
+    const int mw = threads / 64;
     if (mw == 4) {
       if (dtype == 0) hipLaunchKernelGGL((merge_kernel<0, 4, KIND>), grid, dim3(4 * 64), 0, stream, p);
       else hipLaunchKernelGGL((merge_kernel<1, 4, KIND>), grid, dim3(4 * 64), 0, stream, p);
@@ -474,10 +503,8 @@ hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t stream) {
 }
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-  int64_t bx = (((int64_t)p.rows << p.chunk_shift) + 255) / 256;
-  if (bx > 1024) bx = 1024;
-  int64_t by = 2LL * p.B * p.Hkv;
-  if (by > 65535) by = 65535;
+  int64_t bx, by;
+  append_grid(p, 256, &bx, &by);
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)bx, (unsigned)by), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

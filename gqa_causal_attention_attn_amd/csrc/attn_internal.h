@@ -86,6 +86,25 @@ struct RepairParams {
   float scale_log2;
 };
 
+struct AppendParams {
+  const uint16_t* src[2];
+  uint16_t* dst[2];
+  int64_t s_sb[2], s_sh[2], s_sr[2];
+  int64_t d_sb[2], d_sh[2], d_st[2];
+  int B, Hkv, rows;
+  int kv_offset;
+  int chunk_shift;  // log2 of the 16-byte chunks per row: 3, 4 or 5 (head dim 64, 128 or 256)
+};
+
+// The append's workgroups: x over (row, 16-byte chunk) pairs of `threads` threads, y over
+// (tensor, b, g), each capped (the kernel strides over what a cap leaves).
+inline void append_grid(const AppendParams& p, int threads, int64_t* bx, int64_t* by) {
+  *bx = (((int64_t)p.rows << p.chunk_shift) + threads - 1) / threads;
+  if (*bx > 1024) *bx = 1024;
+  *by = 2LL * p.B * p.Hkv;
+  if (*by > 65535) *by = 65535;
+}
+
 struct MergeParams {
   const void* part_o;  // part_kind 0: fp32 rows of D; 1: the main pass's fp16 rows (partial_row_bytes)
   const float* part_lse;
@@ -98,16 +117,12 @@ struct MergeParams {
   int n_chunks, B, Hq, rows;
   int D;  // head dim: 256, 128 or 64 (the partials' row length)
   RepairParams fix;
-};
-
-struct AppendParams {
-  const uint16_t* src[2];
-  uint16_t* dst[2];
-  int64_t s_sb[2], s_sh[2], s_sr[2];
-  int64_t d_sb[2], d_sh[2], d_st[2];
-  int B, Hkv, rows;
-  int kv_offset;
-  int chunk_shift;  // log2 of the 16-byte chunks per row: 3, 4 or 5 (head dim 64, 128 or 256)
+  // carry = 1: a kv_append (app) carried by the same launch: workgroups from merge_blocks on run
+  // it, app_bx x app_by of them, as the append kernel's grid would (all three set by the launcher)
+  int carry;
+  AppendParams app;
+  int app_bx, app_by;
+  int merge_blocks;
 };
 
 constexpr int kKeepMaxBatch = 64;  // keep masks travel in the kernel arguments
@@ -162,8 +177,29 @@ inline int merge_waves(int n_chunks) {
 }
 // A launch dimension holds at most 2^32 - 1 work-items.
 inline bool grid_fits(int64_t blocks, int64_t threads) { return blocks >= 1 && blocks * threads <= 0xffffffffLL; }
+// The merge's own launch: workgroups and threads per workgroup.
+inline void merge_shape(int n_chunks, int64_t n_rows, int64_t* blocks, int* threads) {
+  if (n_chunks <= kFewChunks) {
+    *blocks = (n_rows + 3) / 4;
+    *threads = 256;
+  } else {
+    *blocks = n_rows;
+    *threads = 64 * merge_waves(n_chunks);
+  }
+}
 inline bool merge_fits(int n_chunks, int64_t n_rows) {
-  return n_chunks <= kFewChunks ? grid_fits((n_rows + 3) / 4, 256) : grid_fits(n_rows, 64 * merge_waves(n_chunks));
+  int64_t blocks;
+  int threads;
+  merge_shape(n_chunks, n_rows, &blocks, &threads);
+  return grid_fits(blocks, threads);
+}
+// The merge's launch with a carried append: the merge's workgroups plus the append's.
+inline bool merge_with_append_fits(int n_chunks, int64_t n_rows, const AppendParams& app) {
+  int64_t blocks, bx, by;
+  int threads;
+  merge_shape(n_chunks, n_rows, &blocks, &threads);
+  append_grid(app, threads, &bx, &by);
+  return grid_fits(blocks + bx * by, threads);
 }
 
 // Launchers (return hipGetLastError()).  dtype 0 = bf16, 1 = fp16; mask_kind as attn_mask_kind.

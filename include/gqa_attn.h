@@ -100,6 +100,8 @@ typedef struct {
   int64_t stride_row;
 } attn_mask;
 
+typedef struct kv_append_args kv_append_args;
+
 /* Arguments of attn_prefill / attn_decode. */
 typedef struct {
   int32_t dtype;       /* attn_dtype of q, k/v cache, gate, out and an ATTN_MASK_ADD mask */
@@ -121,10 +123,17 @@ typedef struct {
   attn_tensor k_cache; /* [B, Hkv, capacity, 256] */
   attn_tensor v_cache; /* [B, Hkv, capacity, 256] */
   attn_mask mask;
+  const kv_append_args* append; /* NULL, or a kv_append enqueued with the call's last launch: in
+                                   the merge's launch when the call splits the keys (workgroups of
+                                   its own, one launch fewer), else a launch of its own after the
+                                   call.  Checked as kv_append checks it, with the call's other
+                                   arguments, before anything is enqueued.  Unordered with the
+                                   merge, so it must not touch what the call reads or writes; a
+                                   prompt's loop passes the next query block's rows */
 } attn_args;
 
 /* Arguments of kv_append: k_cache[b, g, kv_offset + r, :] = k_new[b, g, r, :] (and V), bit for bit. */
-typedef struct {
+struct kv_append_args {
   int32_t dtype;
   int32_t B;
   int32_t Hkv;
@@ -137,7 +146,7 @@ typedef struct {
   attn_tensor v_new;   /* [B, Hkv, rows, 256] */
   attn_tensor k_cache; /* [B, Hkv, capacity, 256], written */
   attn_tensor v_cache; /* [B, Hkv, capacity, 256], written */
-} kv_append_args;
+};
 
 /* Arguments of kv_keep.  After a verify block of `rows` rows was appended at kv_offset and some
  * of its rows were accepted: for each batch entry b, the rows r with bit r of keep[b] set move,
@@ -179,6 +188,12 @@ typedef struct {
                                [0.5, 1)); anything else: ATTN_E_ARG */
   const int32_t* partial_exp; /* partial_kind 1: [n_chunks, B, Hq, rows] int32, contiguous (NULL:
                                  ATTN_E_NULL); ignored for partial_kind 0 */
+  const kv_append_args* append; /* NULL, or a kv_append carried by the merge's launch (workgroups of
+                                   their own, checked as kv_append checks it: its errors, and
+                                   ATTN_E_ARG if the two exceed a launch); the two are unordered, so
+                                   the append must not touch what the merge reads or writes.  A
+                                   prompt's loop enqueues block i's merge with block i + 1's append,
+                                   one launch fewer per block */
 } merge_args;
 
 /* The resolved plan of one call (what would run, for logging and validation). */

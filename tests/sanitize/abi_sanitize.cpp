@@ -110,6 +110,7 @@ hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t) {
   CHECK(dtype == 0 || dtype == 1, "dtype %d", dtype);
   CHECK(p.n_chunks >= 1, "n_chunks %d", p.n_chunks);
   CHECK(merge_fits(p.n_chunks, (int64_t)p.B * p.Hq * p.rows), "merge shape");
+  CHECK(!p.carry || merge_with_append_fits(p.n_chunks, (int64_t)p.B * p.Hq * p.rows, p.app), "merge + append shape");
   CHECK(p.D == 256 || p.D == 128 || p.D == 64, "D %d", p.D);
   return hipSuccess;
 }
@@ -412,6 +413,47 @@ void aux_calls() {
   CHECK(attn_merge(&m2, kStream) == ATTN_E_LAYOUT, "merge lse alignment");
   m2 = m, m2.D = 32;
   CHECK(attn_merge(&m2, kStream) == ATTN_E_HEAD_DIM, "merge head dim");
+  {  // a carried append: checked like kv_append, then one launch with the merge
+    kv_append_args ap;
+    memset(&ap, 0, sizeof(ap));
+    ap.dtype = 1, ap.B = 1, ap.Hkv = 2, ap.D = 128, ap.rows = 5, ap.kv_offset = 30, ap.capacity = 40;
+    ap.k_new = t4(2, 5, 128, 4), ap.v_new = t4(2, 5, 128, 5), ap.k_cache = t4(2, 40, 128, 6),
+    ap.v_cache = t4(2, 40, 128, 7);
+    m2 = m, m2.append = &ap;
+    const long merges = g_launch_merge, others = g_launch_other;
+    CHECK(attn_merge(&m2, kStream) == ATTN_OK && g_merge.carry == 1 && g_merge.app.rows == 5 &&
+              g_merge.app.kv_offset == 30 && g_merge.app.chunk_shift == 4 && g_launch_merge == merges + 1 &&
+              g_launch_other == others,
+          "merge carrying an append");
+    ap.kv_offset = 36;  // rows 36..40 past capacity 40
+    CHECK(attn_merge(&m2, kStream) == ATTN_E_KV && g_launch_merge == merges + 1, "carried append out of range");
+  }
+  {  // attn_prefill carrying the next query block's append: in its merge when it splits the keys,
+     // else a launch of its own after the main pass; a bad append is refused before any launch
+    kv_append_args ap;
+    memset(&ap, 0, sizeof(ap));
+    ap.dtype = 0, ap.B = 1, ap.Hkv = 4, ap.D = 256, ap.rows = 512, ap.kv_offset = 4608, ap.capacity = 8192;
+    ap.k_new = t4(4, 512, 256, 8), ap.v_new = t4(4, 512, 256, 9), ap.k_cache = t4(4, 8192, 256, 10),
+    ap.v_cache = t4(4, 8192, 256, 11);
+    auto pa = args(1, 24, 4, 512, 4096);
+    pa.capacity = 8192, pa.k_cache = t4(4, 8192, 256, 4), pa.v_cache = t4(4, 8192, 256, 5);
+    pa.append = &ap;
+    size_t need = 0;
+    CHECK(attn_workspace_bytes(&pa, ATTN_OP_PREFILL, &need) == ATTN_OK && need > 0, "split prompt block");
+    long f0 = g_launch_fwd, m0 = g_launch_merge, o0 = g_launch_other;
+    CHECK(attn_prefill(&pa, kWs, need, kStream) == ATTN_OK && g_launch_fwd == f0 + 1 && g_launch_merge == m0 + 1 &&
+              g_launch_other == o0 && g_merge.carry == 1 && g_merge.app.kv_offset == 4608 && g_merge.app.rows == 512,
+          "prefill carrying the next append in its merge");
+    pa.n_splits = 1;
+    f0 = g_launch_fwd, m0 = g_launch_merge, o0 = g_launch_other;
+    CHECK(attn_prefill(&pa, kWs, need, kStream) == ATTN_OK && g_launch_fwd == f0 + 1 && g_launch_merge == m0 &&
+              g_launch_other == o0 + 1,
+          "prefill without a split: the append after it");
+    ap.kv_offset = 8000;  // 8000 + 512 past capacity 8192
+    f0 = g_launch_fwd, m0 = g_launch_merge, o0 = g_launch_other;
+    CHECK(attn_prefill(&pa, kWs, need, kStream) == ATTN_E_KV && g_launch_fwd == f0 && g_launch_other == o0,
+          "bad carried append refused before any launch");
+  }
   m2 = m, m2.partial_kind = 2;
   CHECK(attn_merge(&m2, kStream) == ATTN_E_ARG, "merge partial kind");
   m2 = m, m2.partial_kind = 1;

@@ -284,6 +284,15 @@ def test_append_and_merge_rejections():
     m.partial_exp = (1 << 20) + 2
     assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_LAYOUT"]
     m.partial_kind = 0
+    # a carried append is checked as kv_append checks it, before anything is enqueued
+    app = _abi.KvAppendArgs(0, 1, 4, 256, 2, 0, 15, 16, t, t, t, t)  # rows 15..16 past capacity 16
+    m.append = C.pointer(app)
+    assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_KV"]
+    app.kv_offset, app.D = 14, 96
+    assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_HEAD_DIM"]
+    app.D, app.k_new = 256, _abi.Tensor(None, 0, 0, 0)
+    assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+    m.append = None
     m.partial_o = None
     assert lib.attn_merge(C.byref(m), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
     for D in (96, 32, 512):  # head dims 256, 128 and 64 only
@@ -318,6 +327,22 @@ def test_keep_rejections():
     a.keep = None
     assert lib.kv_keep(C.byref(a), None) == _abi.STATUS_CODE["ATTN_E_NULL"]
     assert lib.kv_keep(None, None) == _abi.STATUS_CODE["ATTN_E_NULL"]
+
+
+def test_carried_append_is_checked_before_the_call():
+    # attn_prefill / attn_decode with an append to carry: the append's own errors come back and
+    # nothing runs (no device here: a launch would fail with ATTN_E_HIP instead)
+    lib = ga.lib()
+    t = _abi.Tensor(1 << 20, 4 * 16 * 256, 16 * 256, 256)
+    app = _abi.KvAppendArgs(0, 1, 4, 256, 2, 0, 15, 16, t, t, t, t)  # rows 15..16 past capacity 16
+    for op, fn in ((_abi.OP_PREFILL, lib.attn_prefill), (_abi.OP_DECODE, lib.attn_decode)):
+        a = _good()
+        a.append = C.pointer(app)
+        need = ga.workspace_bytes(a, op)
+        assert fn(C.byref(a), C.c_void_p(1 << 20) if need else None, need, None) == _abi.STATUS_CODE["ATTN_E_KV"]
+        app.dtype = 9
+        assert fn(C.byref(a), C.c_void_p(1 << 20) if need else None, need, None) == _abi.STATUS_CODE["ATTN_E_DTYPE"]
+        app.dtype = 0
 
 
 def test_prefill_partials_needs_its_outputs():

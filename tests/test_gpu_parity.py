@@ -491,3 +491,44 @@ def test_split_partials_either_side_of_the_fp16_line(n_splits, kind, mag):
                               kv_len=off + rows)
     _say(assert_close(to_f64(out) / mag, ref / mag, f"split partials kind {kind}, |v|~{mag:g}"))
 
+
+
+@needs_gpu
+@pytest.mark.parametrize("n_chunks", [5, 21])
+@pytest.mark.parametrize("D", [256, 64])
+def test_merge_carrying_an_append(n_chunks, D):
+    # attn_merge with a kv_append in the same launch (the prompt loop's merge of one block with
+    # the next block's append): the merge's output bits and the cache bytes are those of the two
+    # calls made one after the other; the rest of the cache is untouched
+    rng = syn.streams(95)
+    B, Hq, Hkv, rows, kv = 2, 8, 2, 7, 60
+    q = syn.widen(syn.normal_bits(rng["q"], (B, Hq, rows, D)))
+    k = syn.widen(syn.normal_bits(rng["k"], (B, Hkv, kv, D)))
+    v = syn.widen(syn.normal_bits(rng["v"], (B, Hkv, kv, D)))
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D))
+    step = max(1, kv // n_chunks)
+    chunks = [(c * step, kv if c == n_chunks - 1 else (c + 1) * step) for c in range(n_chunks)]
+    o, l_ = reference.partials(q, k, v, n_kv_heads=Hkv, kv_offset=kv - rows, kv_len=kv, chunks=chunks)
+    po = torch.from_numpy(o.astype(np.float32)).cuda()
+    pl = torch.from_numpy(l_.astype(np.float32)).cuda()
+    g = to_dev(gb)
+    kn = to_dev(syn.normal_bits(rng["k"], (B, Hkv, 300, D)))
+    vn = to_dev(syn.normal_bits(rng["v"], (B, Hkv, 300, D)))
+    caches = []
+    for carried in (False, True):
+        kc = torch.full((B, Hkv, 1000, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        vc = torch.full_like(kc, float("nan"))
+        out = torch.full((B, Hq, rows, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if carried:
+            ga.merge(po, pl, g, out=out, append=(kn, vn, kc, vc, 517))
+        else:
+            ga.merge(po, pl, g, out=out)
+            ga.kv_append(kn, vn, kc, vc, kv_offset=517)
+        torch.cuda.synchronize()
+        caches.append((out, kc, vc))
+    (o0, k0, v0), (o1, k1, v1) = caches
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(k0.view(torch.int16), k1.view(torch.int16)) and torch.equal(v0.view(torch.int16), v1.view(torch.int16))
+    assert torch.equal(k1[:, :, 517:817].view(torch.int16), kn.view(torch.int16))
+    assert torch.isnan(k1[:, :, :517].float()).all() and torch.isnan(v1[:, :, 817:].float()).all()
+    _say(assert_close(to_f64(o1), reference.merge(o, l_, syn.widen(gb)), f"merge carrying an append, {n_chunks} chunks"))
