@@ -232,11 +232,11 @@ int make_plan(const attn_args* a, int op, Plan* P) {
   if (P->grid > INT32_MAX || !gqa::grid_fits(P->grid, 64 * P->waves)) return ATTN_E_ARG;
   const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
   if (n_rows > (int64_t)INT32_MAX) return ATTN_E_ARG;  // the merge indexes rows in 32 bits
-  if (S > 1 && !gqa::merge_fits((int)S, n_rows)) return ATTN_E_ARG;
   if (S > 1) {
     const int64_t nrow = S * a->B * a->Hq * (int64_t)a->rows;
     // the kind depends on the unchunked shape only, like the splits
     P->part_kind = nrow * gqa::partial_row_bytes(a->D, 0) >= gqa::kHalfPartialsFromBytes ? 1 : 0;
+    if (!gqa::merge_fits((int)S, P->part_kind, n_rows)) return ATTN_E_ARG;
     P->ws_o_bytes = (size_t)cdiv(nrow * gqa::partial_row_bytes(a->D, P->part_kind), 256) * 256;
     P->ws_e_offset = P->ws_o_bytes + (size_t)cdiv(nrow * 4, 256) * 256;
     P->ws_bytes = P->ws_e_offset + (P->part_kind == 1 ? (size_t)cdiv(nrow * 4, 256) * 256 : 0);
@@ -297,7 +297,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
     if (st) return st;
     const bool carried = P.n_splits > 1 && merge;
     const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
-    if (carried && !gqa::merge_with_append_fits(P.n_splits, n_rows, app)) return ATTN_E_ARG;
+    if (carried && !gqa::merge_with_append_fits(P.n_splits, P.part_kind, n_rows, app)) return ATTN_E_ARG;
   }
 
   gqa::FwdParams p;
@@ -639,8 +639,9 @@ int attn_merge(const merge_args* a, void* stream) {
   if (a->rows < 1) return ATTN_E_ROWS;
   if (a->n_chunks < 1) return ATTN_E_ARG;
   const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
-  if (n_rows > (int64_t)INT32_MAX || !gqa::merge_fits(a->n_chunks, n_rows)) return ATTN_E_ARG;  // 32-bit rows, launch size
   if (a->partial_kind != 0 && a->partial_kind != 1) return ATTN_E_ARG;
+  if (n_rows > (int64_t)INT32_MAX || !gqa::merge_fits(a->n_chunks, a->partial_kind, n_rows))
+    return ATTN_E_ARG;  // 32-bit rows, launch size
   if (!a->partial_o || !a->partial_lse || !a->gate.ptr || !a->out.ptr) return ATTN_E_NULL;
   if (a->partial_kind == 1 && !a->partial_exp) return ATTN_E_NULL;
   if (!aligned16(a->partial_o) || !aligned16(a->gate.ptr) || !aligned16(a->out.ptr) || !strides_ok(a->gate) ||
@@ -656,7 +657,7 @@ int attn_merge(const merge_args* a, void* stream) {
   if (a->append) {  // checked as kv_append checks its arguments; nothing is enqueued on an error
     const int st = append_params(a->append, &p.app);
     if (st) return st;
-    if (!gqa::merge_with_append_fits(a->n_chunks, n_rows, p.app)) return ATTN_E_ARG;
+    if (!gqa::merge_with_append_fits(a->n_chunks, a->partial_kind, n_rows, p.app)) return ATTN_E_ARG;
     p.carry = 1;
   }
   p.gate = static_cast<const uint16_t*>(a->gate.ptr);

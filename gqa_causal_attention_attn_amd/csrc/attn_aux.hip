@@ -310,11 +310,20 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
   if (d0 < p.D) *reinterpret_cast<u32x2*>(orow + d0) = ow;
 }
 
-// Few chunks (prompt blocks split a handful of ways): one wavefront per row, four rows per
-// workgroup, four dims per lane, NC (the chunk count, 1..8) partial loads issued at once
-// (independent loads), so the pass streams instead of waiting on one load after another.  The
-// row's NC lse values (and exponents) come in one load each, lane c holding chunk c's, and are
-// read out of those lanes.
+// largest value over the wavefront's 64 lanes (fmaxf: a NaN lane is passed over)
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Chunks up to 64 (merge_slots): one wavefront per row, four rows per workgroup, four dims per
+// lane, and a partial load of every chunk slot issued at once (independent loads), so the pass
+// costs one round trip instead of a load after another.  NC slots: NC = the chunk count for up
+// to 8 chunks; 16, 32 or 64 slots (fp32 partials: up to 32) for more, the slots past the row's
+// chunks re-reading its last chunk and selected out.  Lane c holds chunk c's lse (and
+// exponent) and works out its weight; the sum reads them out of the lanes in chunk order and
+// decodes each partial as it goes.
 template <int DT, int KIND, int NC>
 __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   if (merge_carried_append(p)) return;
@@ -330,52 +339,49 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   const int h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
   const int d0 = 4 * lane;
   const int dl = min(d0, p.D - 4);  // lanes past the head dim re-read its last 4 dims and store nothing
-  constexpr int nch = GQA_CONTROL == 2 ? (NC > 1 ? NC - 1 : 1) : NC;
+  constexpr bool kExact = NC <= kFewChunks;
+  int nch;
+  if constexpr (kExact) nch = GQA_CONTROL == 2 ? (NC > 1 ? NC - 1 : 1) : NC;
+  else nch = GQA_CONTROL == 2 ? max(p.n_chunks - 1, 1) : p.n_chunks;
   const uint16_t* grow = p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh + (int64_t)r * p.g_sr;
   const u32x2 gw = *reinterpret_cast<const u32x2*>(grow + dl);
   // lane c (c < nch; the others re-read chunk nch - 1) loads chunk c's lse and exponent
   const int64_t lrow = (int64_t)min(lane, nch - 1) * n_rows + row_id;
-  const float lse_lane = p.part_lse[lrow];
+  float lse_lane = p.part_lse[lrow];
   int32_t e_lane = 0;
   if constexpr (KIND == 1) e_lane = p.part_e[lrow];
-  PartialLoad<KIND> raw[nch];
+  PartialLoad<KIND> raw[NC];
 #pragma unroll
-  for (int c = 0; c < nch; ++c) raw[c] = load_values<KIND>(p, (int64_t)c * n_rows + row_id, dl);
-  // one use of every partial here keeps all the loads together, in one round trip (left to the
-  // weighted sum, the compiler sinks each partial's load into its chunk's branch, after the lse
-  // loads have come back and the row's largest lse is known)
+  for (int c = 0; c < NC; ++c) raw[c] = load_values<KIND>(p, (int64_t)min(c, nch - 1) * n_rows + row_id, dl);
+  // one use of every partial here, each passing the lse through, keeps all the loads together,
+  // in one round trip: left alone, the compiler sinks each partial's load into its chunk's
+  // branch, after the lse loads have come back, or works out the row's largest lse first
 #pragma unroll
-  for (int c = 0; c < nch; ++c) {
+  for (int c = 0; c < NC; ++c) {
     if constexpr (KIND == 0) {
-      asm volatile("" ::"v"(raw[c].f));
+      asm volatile("" : "+v"(lse_lane) : "v"(raw[c].f));
     } else {
-      asm volatile("" ::"v"(raw[c].h));
+      asm volatile("" : "+v"(lse_lane) : "v"(raw[c].h));
     }
   }
-  float lc[nch];
-  f32x4 oc[nch];
-#pragma unroll
-  for (int c = 0; c < nch; ++c) {
-    lc[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lse_lane), c));
-    if constexpr (KIND == 1) raw[c].e = __builtin_amdgcn_readlane(e_lane, c);
-    oc[c] = decode_partial<KIND>(raw[c]);
-  }
-  float top = -INFINITY;
-  bool nan_l = false;  // a chunk whose lse is NaN makes the row NaN, as the unsplit definition does
-#pragma unroll
-  for (int c = 0; c < nch; ++c) {
-    top = fmaxf(top, lc[c]);
-    nan_l = nan_l || __builtin_isnan(lc[c]);
-  }
+  // the row's largest lse, a NaN lse (which makes the row NaN, as the unsplit definition does)
+  // and each chunk's weight, all over the lanes that hold a chunk
+  const bool mine = lane < nch;
+  const float top = wave_max(mine ? lse_lane : -INFINITY);
+  const bool nan_l = __builtin_amdgcn_ballot_w64(mine && __builtin_isnan(lse_lane)) != 0;
+  const float w_lane = top > -INFINITY ? exp2f((lse_lane - top) * kLog2e) : 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
   if (top > -INFINITY) {
 #pragma unroll
-    for (int c = 0; c < nch; ++c) {
+    for (int c = 0; c < NC; ++c) {
+      const float lc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lse_lane), c));
       // an empty chunk is selected out, never multiplied in
-      if (lc[c] != -INFINITY) {
-        const float w = exp2f((lc[c] - top) * kLog2e);
-        acc += w * oc[c];
+      if (c < nch && lc != -INFINITY) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_lane), c));
+        PartialLoad<KIND> x = raw[c];
+        if constexpr (KIND == 1) x.e = __builtin_amdgcn_readlane(e_lane, c);
+        acc += w * decode_partial<KIND>(x);
         wsum += w;
       }
     }
@@ -451,7 +457,7 @@ void launch_few_nc(const MergeParams& p, int dtype, dim3 grid, hipStream_t strea
 }
 template <int KIND>
 void launch_few(const MergeParams& p, int dtype, dim3 grid, hipStream_t stream) {
-  switch (p.n_chunks) {
+  switch (merge_slots(p.n_chunks, KIND, (int64_t)p.B * p.Hq * p.rows)) {
     case 1: launch_few_nc<KIND, 1>(p, dtype, grid, stream); break;
     case 2: launch_few_nc<KIND, 2>(p, dtype, grid, stream); break;
     case 3: launch_few_nc<KIND, 3>(p, dtype, grid, stream); break;
@@ -459,7 +465,12 @@ void launch_few(const MergeParams& p, int dtype, dim3 grid, hipStream_t stream) 
     case 5: launch_few_nc<KIND, 5>(p, dtype, grid, stream); break;
     case 6: launch_few_nc<KIND, 6>(p, dtype, grid, stream); break;
     case 7: launch_few_nc<KIND, 7>(p, dtype, grid, stream); break;
-    default: launch_few_nc<KIND, 8>(p, dtype, grid, stream); break;
+    case 8: launch_few_nc<KIND, 8>(p, dtype, grid, stream); break;
+    case 16: launch_few_nc<KIND, 16>(p, dtype, grid, stream); break;
+    case 32: launch_few_nc<KIND, 32>(p, dtype, grid, stream); break;
+    default:
+      if constexpr (KIND == 1) launch_few_nc<KIND, 64>(p, dtype, grid, stream);
+      break;
   }
 }
 
@@ -469,7 +480,7 @@ void launch_merge_k(const MergeParams& p0, int dtype, hipStream_t stream) {
   MergeParams p = p0;
   int64_t blocks;
   int threads;
-  merge_shape(p.n_chunks, n_rows, &blocks, &threads);
+  merge_shape(p.n_chunks, KIND, n_rows, &blocks, &threads);
   p.merge_blocks = (int)blocks;
   int64_t extra = 0;
   if (p.carry) {
@@ -479,7 +490,7 @@ void launch_merge_k(const MergeParams& p0, int dtype, hipStream_t stream) {
     extra = bx * by;
   }
   const dim3 grid((unsigned)(blocks + extra));
-  if (p.n_chunks <= kFewChunks) {
+  if (merge_slots(p.n_chunks, KIND, n_rows) > 0) {
     launch_few<KIND>(p, dtype, grid, stream);
   } else {
     const int mw = threads / 64;

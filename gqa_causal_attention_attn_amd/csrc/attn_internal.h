@@ -167,19 +167,27 @@ constexpr int64_t partial_row_bytes(int D, int kind) { return (kind == 1 ? 2 : 4
 // 8 MiB of fp32 partials up (prompt blocks, verify rows), kind 0 below (short decodes).
 constexpr int64_t kHalfPartialsFromBytes = (int64_t)8 << 20;
 
-// Merge launch shape, shared by the launcher and the host's checks: chunk counts up to
-// kFewChunks take one wavefront per row (four rows a workgroup); more take a workgroup of
-// merge_waves(n) wavefronts per row.
+// Merge launch shape, shared by the launcher and the host's checks.  Up to kFewChunks chunks,
+// and up to 64 (32 of fp32 partials) where the rows fill the chip (kWideMergeRows: a workgroup
+// of four rows per CU), take one wavefront per row, four rows a workgroup, with
+// merge_slots(n, kind, rows) chunk slots: the chunk count itself up to kFewChunks, else 16, 32
+// or 64.  The rest take a workgroup of merge_waves(n) wavefronts per row.
 constexpr int kFewChunks = 8;
 constexpr int kMergeBatch = 4;  // chunks a wavefront of the many-chunk merge loads at once
+constexpr int64_t kWideMergeRows = 1024;
+inline int merge_slots(int n_chunks, int kind, int64_t n_rows) {
+  if (n_chunks <= kFewChunks) return n_chunks;
+  if (n_rows < kWideMergeRows) return 0;
+  return n_chunks <= 16 ? 16 : n_chunks <= 32 ? 32 : n_chunks <= 64 && kind == 1 ? 64 : 0;
+}
 inline int merge_waves(int n_chunks) {
-  return n_chunks <= kFewChunks ? 1 : n_chunks <= 4 * kMergeBatch ? 4 : n_chunks <= 8 * kMergeBatch ? 8 : 16;
+  return n_chunks <= 4 * kMergeBatch ? 4 : n_chunks <= 8 * kMergeBatch ? 8 : 16;
 }
 // A launch dimension holds at most 2^32 - 1 work-items.
 inline bool grid_fits(int64_t blocks, int64_t threads) { return blocks >= 1 && blocks * threads <= 0xffffffffLL; }
 // The merge's own launch: workgroups and threads per workgroup.
-inline void merge_shape(int n_chunks, int64_t n_rows, int64_t* blocks, int* threads) {
-  if (n_chunks <= kFewChunks) {
+inline void merge_shape(int n_chunks, int kind, int64_t n_rows, int64_t* blocks, int* threads) {
+  if (merge_slots(n_chunks, kind, n_rows) > 0) {
     *blocks = (n_rows + 3) / 4;
     *threads = 256;
   } else {
@@ -187,17 +195,17 @@ inline void merge_shape(int n_chunks, int64_t n_rows, int64_t* blocks, int* thre
     *threads = 64 * merge_waves(n_chunks);
   }
 }
-inline bool merge_fits(int n_chunks, int64_t n_rows) {
+inline bool merge_fits(int n_chunks, int kind, int64_t n_rows) {
   int64_t blocks;
   int threads;
-  merge_shape(n_chunks, n_rows, &blocks, &threads);
+  merge_shape(n_chunks, kind, n_rows, &blocks, &threads);
   return grid_fits(blocks, threads);
 }
 // The merge's launch with a carried append: the merge's workgroups plus the append's.
-inline bool merge_with_append_fits(int n_chunks, int64_t n_rows, const AppendParams& app) {
+inline bool merge_with_append_fits(int n_chunks, int kind, int64_t n_rows, const AppendParams& app) {
   int64_t blocks, bx, by;
   int threads;
-  merge_shape(n_chunks, n_rows, &blocks, &threads);
+  merge_shape(n_chunks, kind, n_rows, &blocks, &threads);
   append_grid(app, threads, &bx, &by);
   return grid_fits(blocks + bx * by, threads);
 }

@@ -109,8 +109,9 @@ hipError_t launch_merge(const MergeParams& p, int dtype, hipStream_t) {
   g_merge = p;
   CHECK(dtype == 0 || dtype == 1, "dtype %d", dtype);
   CHECK(p.n_chunks >= 1, "n_chunks %d", p.n_chunks);
-  CHECK(merge_fits(p.n_chunks, (int64_t)p.B * p.Hq * p.rows), "merge shape");
-  CHECK(!p.carry || merge_with_append_fits(p.n_chunks, (int64_t)p.B * p.Hq * p.rows, p.app), "merge + append shape");
+  CHECK(merge_fits(p.n_chunks, p.part_kind, (int64_t)p.B * p.Hq * p.rows), "merge shape");
+  CHECK(!p.carry || merge_with_append_fits(p.n_chunks, p.part_kind, (int64_t)p.B * p.Hq * p.rows, p.app),
+        "merge + append shape");
   CHECK(p.D == 256 || p.D == 128 || p.D == 64, "D %d", p.D);
   return hipSuccess;
 }
@@ -231,22 +232,24 @@ void rejection_matrix() {
 
 // Shapes whose launches would not fit are rejected by planning and run alike, before any launch.
 void launch_limits() {
-  // decode rows 32 at B 4096, 32/1 heads over a 4128-key cache, 40 splits asked (33 planned): the
-  // merge would run 4.19M rows x 1024 threads
+  // decode rows 32 at B 4096, 32/1 heads over a 4128-key cache, 100 splits asked (65 planned, more
+  // than the one-wavefront merge's 64 slots): the merge would run 4.19M rows x 1024 threads
   auto a = args(4096, 32, 1, 32, 4096);
-  a.n_splits = 40;
+  a.n_splits = 100;
   size_t bytes = 0;
   attn_plan_info info;
   const long before = launches();
   CHECK(attn_workspace_bytes(&a, ATTN_OP_DECODE, &bytes) == ATTN_E_ARG, "merge too large: workspace");
   CHECK(attn_describe_plan(&a, ATTN_OP_DECODE, &info) == ATTN_E_ARG, "merge too large: describe");
   CHECK(attn_decode(&a, kWs, SIZE_MAX / 2, kStream) == ATTN_E_ARG, "merge too large: run");
-  // fewer splits fit (one wavefront per row for <= 8 chunks)
+  // fewer splits fit (one wavefront per row for <= 64 chunks of fp16 partials)
   a.n_splits = 8;
   CHECK(attn_workspace_bytes(&a, ATTN_OP_DECODE, &bytes) == ATTN_OK, "8 splits fit");
-  // head dim 64 (128-key tiles): the same merge limit
+  a.n_splits = 40;
+  CHECK(attn_workspace_bytes(&a, ATTN_OP_DECODE, &bytes) == ATTN_OK, "33 splits fit");
+  // head dim 64 (128-key tiles): the same merge limit (100 splits asked, 65 planned)
   auto s64 = args(4096, 32, 1, 32, 8192, 64);
-  s64.n_splits = 40;
+  s64.n_splits = 100;
   CHECK(attn_workspace_bytes(&s64, ATTN_OP_DECODE, &bytes) == ATTN_E_ARG, "head dim 64 merge too large: workspace");
   CHECK(attn_decode(&s64, kWs, SIZE_MAX / 2, kStream) == ATTN_E_ARG, "head dim 64 merge too large: run");
   s64.n_splits = 8;

@@ -361,9 +361,10 @@ def test_prefill_partials_needs_its_outputs():
 
 
 def test_launch_size_limits_are_rejected_by_planning_and_run_alike():
-    # a decode whose merge would exceed a launch (4.19M rows x 16 wavefronts), at head dims 256 and
-    # 64: the planning calls reject it as the run would, before anything is enqueued
-    a = ga.plan_args(B=4096, Hq=32, Hkv=1, rows=32, kv_offset=4096, n_splits=40)
+    # a decode whose merge would exceed a launch (4.19M rows x 16 wavefronts: more than 64 chunks),
+    # at head dims 256 and 64: the planning calls reject it as the run would, before anything is
+    # enqueued (100 splits asked for: 65 chunks of 2 tiles)
+    a = ga.plan_args(B=4096, Hq=32, Hkv=1, rows=32, kv_offset=4096, n_splits=100)
     for fn in (lambda: ga.workspace_bytes(a, _abi.OP_DECODE), lambda: ga.describe_plan(a, _abi.OP_DECODE)):
         with pytest.raises(ga.AttnError) as e:
             fn()
@@ -371,7 +372,9 @@ def test_launch_size_limits_are_rejected_by_planning_and_run_alike():
     assert ga.lib().attn_decode(C.byref(a), None, 0, None) == _abi.STATUS_CODE["ATTN_E_ARG"]
     a.n_splits = 8  # one wavefront a row: fits
     assert ga.workspace_bytes(a, _abi.OP_DECODE) > 0
-    s = ga.plan_args(B=4096, Hq=32, Hkv=1, rows=32, kv_offset=8192, n_splits=40, D=64)
+    a.n_splits = 40  # one wavefront a row with 64 slots (fp16 partials): fits
+    assert ga.workspace_bytes(a, _abi.OP_DECODE) > 0
+    s = ga.plan_args(B=4096, Hq=32, Hkv=1, rows=32, kv_offset=8192, n_splits=100, D=64)
     with pytest.raises(ga.AttnError):
         ga.workspace_bytes(s, _abi.OP_DECODE)
     assert ga.lib().attn_decode(C.byref(s), None, 0, None) == _abi.STATUS_CODE["ATTN_E_ARG"]

@@ -532,3 +532,38 @@ def test_merge_carrying_an_append(n_chunks, D):
     assert torch.equal(k1[:, :, 517:817].view(torch.int16), kn.view(torch.int16))
     assert torch.isnan(k1[:, :, :517].float()).all() and torch.isnan(v1[:, :, 817:].float()).all()
     _say(assert_close(to_f64(o1), reference.merge(o, l_, syn.widen(gb)), f"merge carrying an append, {n_chunks} chunks"))
+
+
+@needs_gpu
+@pytest.mark.parametrize("n_chunks", [12, 21, 40])
+@pytest.mark.parametrize("fp16", [False, True])
+def test_merge_of_many_chunks_over_many_rows(n_chunks, fp16):
+    # 1024 rows (32 heads x 32 rows) fill the chip with one wavefront a row, so 9 to 64 chunks
+    # (32 of fp32 partials) take the one-wavefront merge with 16, 32 or 64 slots; 40 fp32 chunks
+    # take the many-wavefront one.  Against the oracle, with a row empty in every chunk.
+    rng = syn.streams(97)
+    D, B, Hq, Hkv, rows, kv = 64, 1, 32, 4, 32, 130
+    q = syn.widen(syn.normal_bits(rng["q"], (B, Hq, rows, D)))
+    k = syn.widen(syn.normal_bits(rng["k"], (B, Hkv, kv, D)))
+    v = syn.widen(syn.normal_bits(rng["v"], (B, Hkv, kv, D)))
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D))
+    step = kv // n_chunks
+    chunks = [(c * step, kv if c == n_chunks - 1 else (c + 1) * step) for c in range(n_chunks)]
+    o, l_ = reference.partials(q, k, v, n_kv_heads=Hkv, kv_offset=kv - rows, kv_len=kv, chunks=chunks)
+    l32 = l_.astype(np.float32)
+    l32[:, 0, 5, 3] = -np.inf  # a row empty in every chunk: 0 whatever its partials hold
+    o = o.copy()
+    o[:, 0, 5, 3, :] = np.nan
+    if fp16:
+        vals16, exps, exact = _fp16_rows(o)
+        po, pe = torch.from_numpy(vals16).cuda(), torch.from_numpy(exps).cuda()
+    else:
+        po, pe, exact = torch.from_numpy(o.astype(np.float32)).cuda(), None, o
+    out = torch.full((B, Hq, rows, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ga.merge(po, torch.from_numpy(l32).cuda(), to_dev(gb), out=out, partial_exp=pe)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    assert np.all(got[0, 5, 3, :] == 0.0)
+    ref = reference.merge(np.nan_to_num(o, nan=0.0), l_, syn.widen(gb))
+    ref[0, 5, 3, :] = 0.0
+    _say(assert_close(got, ref, f"merge of {n_chunks} chunks over 1024 rows, {'fp16' if fp16 else 'fp32'}"))
