@@ -567,3 +567,42 @@ def test_merge_of_many_chunks_over_many_rows(n_chunks, fp16):
     ref = reference.merge(np.nan_to_num(o, nan=0.0), l_, syn.widen(gb))
     ref[0, 5, 3, :] = 0.0
     _say(assert_close(got, ref, f"merge of {n_chunks} chunks over 1024 rows, {'fp16' if fp16 else 'fp32'}"))
+
+
+@needs_gpu
+@pytest.mark.parametrize("n_splits", [1, 3])
+@pytest.mark.parametrize("D", [256, 128])
+def test_prefill_carrying_the_next_blocks_append(n_splits, D):
+    # attn_prefill with attn_args append (the next query block's rows): in the merge's launch with
+    # the keys split, in a launch of its own after the main pass without; the block's output and
+    # both caches are those of the prefill and the kv_append made apart, bit for bit
+    rng = syn.streams(99)
+    B, Hq, Hkv, rows, off = 1, 8, 2, 40, 200
+    qb = syn.normal_bits(rng["q"], (B, Hq, rows, D))
+    gb = syn.normal_bits(rng["gate"], (B, Hq, rows, D))
+    kb = syn.normal_bits(rng["k"], (B, Hkv, off + 2 * rows, D))
+    vb = syn.normal_bits(rng["v"], (B, Hkv, off + 2 * rows, D))
+    q, g = to_dev(qb), to_dev(gb)
+    res = []
+    for carried in (False, True):
+        kc = torch.full((B, Hkv, off + 2 * rows, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        vc = torch.full_like(kc, float("nan"))
+        kc[:, :, :off + rows] = to_dev(kb[:, :, :off + rows])
+        vc[:, :, :off + rows] = to_dev(vb[:, :, :off + rows])
+        kn, vn = to_dev(kb[:, :, off + rows:]), to_dev(vb[:, :, off + rows:])
+        nxt = (kn, vn, kc, vc, off + rows)
+        if carried:
+            out = ga.prefill(q, kc, vc, g, kv_offset=off, n_splits=n_splits, append=nxt)
+        else:
+            out = ga.prefill(q, kc, vc, g, kv_offset=off, n_splits=n_splits)
+            ga.kv_append(kn, vn, kc, vc, kv_offset=off + rows)
+        torch.cuda.synchronize()
+        res.append((out, kc, vc))
+    (o0, k0, v0), (o1, k1, v1) = res
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(k1.view(torch.int16), to_dev(kb).view(torch.int16))
+    assert torch.equal(v1.view(torch.int16), to_dev(vb).view(torch.int16))
+    assert torch.equal(k0.view(torch.int16), k1.view(torch.int16)) and torch.equal(v0.view(torch.int16), v1.view(torch.int16))
+    ref = reference.attention(*(syn.widen(x) for x in (qb, kb[:, :, :off + rows], vb[:, :, :off + rows], gb)),
+                              n_kv_heads=Hkv, kv_offset=off, kv_len=off + rows)
+    _say(assert_close(to_f64(o1), ref, f"prefill carrying an append, n_splits={n_splits}, D={D}"))
