@@ -320,8 +320,9 @@ __device__ __forceinline__ float wave_max(float x) {
 // Chunks up to 64 (merge_slots): one wavefront per row, four rows per workgroup, four dims per
 // lane, and a partial load of every chunk slot issued at once (independent loads), so the pass
 // costs one round trip instead of a load after another.  NC slots: NC = the chunk count for up
-// to 8 chunks; 16, 32 or 64 slots (fp32 partials: up to 32) for more, the slots past the row's
-// chunks re-reading its last chunk and selected out.  Lane c holds chunk c's lse (and
+// to 8 chunks, else the chunk count rounded up to a multiple of 4 up to 32, of 8 up to 64 (fp32
+// partials: up to 32), the slots past the row's chunks re-reading its last chunk and selected
+// out (each slot costs its load: 17 chunks in 32 slots took 1.3x the time of 16 in 16).  Lane c holds chunk c's lse (and
 // exponent) and works out its weight; the sum reads them out of the lanes in chunk order and
 // decodes each partial as it goes.
 template <int DT, int KIND, int NC>
@@ -356,6 +357,7 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
   // one use of every partial here, each passing the lse through, keeps all the loads together,
   // in one round trip: left alone, the compiler sinks each partial's load into its chunk's
   // branch, after the lse loads have come back, or works out the row's largest lse first
+  // (loads made conditional on the slot holding a chunk were each followed by a wait)
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if constexpr (KIND == 0) {
@@ -466,10 +468,21 @@ void launch_few(const MergeParams& p, int dtype, dim3 grid, hipStream_t stream) 
     case 6: launch_few_nc<KIND, 6>(p, dtype, grid, stream); break;
     case 7: launch_few_nc<KIND, 7>(p, dtype, grid, stream); break;
     case 8: launch_few_nc<KIND, 8>(p, dtype, grid, stream); break;
+    case 12: launch_few_nc<KIND, 12>(p, dtype, grid, stream); break;
     case 16: launch_few_nc<KIND, 16>(p, dtype, grid, stream); break;
+    case 20: launch_few_nc<KIND, 20>(p, dtype, grid, stream); break;
+    case 24: launch_few_nc<KIND, 24>(p, dtype, grid, stream); break;
+    case 28: launch_few_nc<KIND, 28>(p, dtype, grid, stream); break;
     case 32: launch_few_nc<KIND, 32>(p, dtype, grid, stream); break;
     default:
-      if constexpr (KIND == 1) launch_few_nc<KIND, 64>(p, dtype, grid, stream);
+      if constexpr (KIND == 1) {
+        switch (merge_slots(p.n_chunks, KIND, (int64_t)p.B * p.Hq * p.rows)) {
+          case 40: launch_few_nc<KIND, 40>(p, dtype, grid, stream); break;
+          case 48: launch_few_nc<KIND, 48>(p, dtype, grid, stream); break;
+          case 56: launch_few_nc<KIND, 56>(p, dtype, grid, stream); break;
+          default: launch_few_nc<KIND, 64>(p, dtype, grid, stream); break;
+        }
+      }
       break;
   }
 }

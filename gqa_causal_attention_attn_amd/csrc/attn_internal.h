@@ -170,15 +170,17 @@ constexpr int64_t kHalfPartialsFromBytes = (int64_t)8 << 20;
 // Merge launch shape, shared by the launcher and the host's checks.  Up to kFewChunks chunks,
 // and up to 64 (32 of fp32 partials) where the rows fill the chip (kWideMergeRows: a workgroup
 // of four rows per CU), take one wavefront per row, four rows a workgroup, with
-// merge_slots(n, kind, rows) chunk slots: the chunk count itself up to kFewChunks, else 16, 32
-// or 64.  The rest take a workgroup of merge_waves(n) wavefronts per row.
+// merge_slots(n, kind, rows) chunk slots: the chunk count itself up to kFewChunks, else the
+// count rounded up to a multiple of 4 (up to 32) or of 8 (up to 64).  The rest take a workgroup
+// of merge_waves(n) wavefronts per row.
 constexpr int kFewChunks = 8;
 constexpr int kMergeBatch = 4;  // chunks a wavefront of the many-chunk merge loads at once
 constexpr int64_t kWideMergeRows = 1024;
 inline int merge_slots(int n_chunks, int kind, int64_t n_rows) {
   if (n_chunks <= kFewChunks) return n_chunks;
   if (n_rows < kWideMergeRows) return 0;
-  return n_chunks <= 16 ? 16 : n_chunks <= 32 ? 32 : n_chunks <= 64 && kind == 1 ? 64 : 0;
+  if (n_chunks <= 32) return (n_chunks + 3) / 4 * 4;
+  return n_chunks <= 64 && kind == 1 ? (n_chunks + 7) / 8 * 8 : 0;
 }
 inline int merge_waves(int n_chunks) {
   return n_chunks <= 4 * kMergeBatch ? 4 : n_chunks <= 8 * kMergeBatch ? 8 : 16;
