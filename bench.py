@@ -149,7 +149,7 @@ class Plans:
     """Requested plan beside the resolved one for every sample; a mismatch stops the run."""
 
     KEYS = ("variant_name", "n_splits", "partial_kind", "keys_per_split", "n_head_chunks", "chunk_sizes",
-            "waves_per_block", "n_row_tiles", "grid_blocks", "workspace_bytes")
+            "waves_per_block", "n_row_tiles", "grid_blocks", "carry_blocks", "workspace_bytes")
 
     def __init__(self, ga):
         self.ga = ga
@@ -404,23 +404,37 @@ def main():
         vplan = dset.prep(32, "verify_35b_off32768_rows32_bf16")
     setup_s = time.time() - t_setup
 
+    spaces = [ws, torch.empty_like(ws)] if need_prompt else None
+
     def prefill_pass(per_call=None):
         ga.kv_append(k[:, :, :min(qL, N)], v[:, :, :min(qL, N)], kc, vc, kv_offset=0)
+        pending = None  # a block's partials, gate and out, merged by the next block's call
         for i, s in enumerate(range(0, N, qL)):
             e = min(s + qL, N)
+            e2 = min(e + qL, N)
+            nxt = (k[:, :, e:e2], v[:, :, e:e2], kc, vc, e) if e < N else None
+            # a block whose main pass carries work (its plan's carry_blocks) takes the previous
+            # block's merge and the next block's append in its own launch; the others merge
+            # themselves, the next block's append riding on that merge
+            carries = block_plans[i]["carry_blocks"] > 0
+            if not carries and pending is not None:
+                ga.merge(pending[0], pending[1], pending[3], out=pending[4], partial_exp=pending[2])
+                pending = None
             if per_call is not None:
                 per_call[i][0].record(stream)
             _, parts = ga.prefill_partials(q[:, :, s:e], kc, vc, g[:, :, s:e], kv_offset=s, kv_len=e,
-                                           out=out[:, :, s:e], workspace=ws)
+                                           out=out[:, :, s:e], workspace=spaces[i % 2],
+                                           append=nxt if carries else None, carry=pending if carries else None)
             if per_call is not None:
                 per_call[i][1].record(stream)
-            # the next block's append rides on this block's merge (one launch), else goes alone
-            e2 = min(e + qL, N)
-            nxt = (k[:, :, e:e2], v[:, :, e:e2], kc, vc, e) if e < N else None
-            if parts is not None:
+            if carries:
+                pending = (*parts, g[:, :, s:e], out[:, :, s:e])
+            elif parts is not None:
                 ga.merge(parts[0], parts[1], g[:, :, s:e], out=out[:, :, s:e], partial_exp=parts[2], append=nxt)
             elif nxt is not None:
                 ga.kv_append(*nxt[:4], kv_offset=e)
+        if pending is not None:
+            ga.merge(pending[0], pending[1], pending[3], out=pending[4], partial_exp=pending[2])
 
     # ---- profiler mode: one workload, --steps times
     if args.only:

@@ -115,8 +115,19 @@ def _args(q, k_cache, v_cache, gate, out, *, kv_offset, kv_len, causal, scale, h
     return a
 
 
+def _carry_args(a, carry):
+    """Points attn_args `a` at the merge it carries: carry = (partial_o, partial_lse, partial_exp,
+    gate, out) of an earlier prefill_partials call.  Returns what must stay alive with `a`."""
+    if carry is None:
+        return None
+    po, pl, pe, cg, co = carry
+    m, app = _merge_args(po, pl, cg, co, pe)
+    a.carry = C.pointer(m)
+    return (m, app)
+
+
 def _run(op: int, q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
-         n_splits=0, mask=None, out=None, workspace=None, append=None):
+         n_splits=0, mask=None, out=None, workspace=None, append=None, carry=None):
     if kv_len is None:
         kv_len = kv_offset + q.shape[2]
     if out is None:
@@ -127,6 +138,7 @@ def _run(op: int, q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, cau
     if append is not None:  # (k_new, v_new, k_cache, v_cache, kv_offset) of a kv_append the call carries
         app = _append_args(*append)
         a.append = C.pointer(app)
+    _keep = _carry_args(a, carry)
     L = lib()
     need = C.c_size_t(0)
     _check(L.attn_workspace_bytes(C.byref(a), op, C.byref(need)))
@@ -141,14 +153,18 @@ def _run(op: int, q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, cau
 
 
 def prefill_partials(q, k_cache, v_cache, gate, *, kv_offset: int, workspace, kv_len=None, causal=True, scale=0.0,
-                     head_chunk=0, n_splits=0, mask=None, out=None):
+                     head_chunk=0, n_splits=0, mask=None, out=None, append=None, carry=None):
     """attn_prefill_partials: the main pass only.  Returns (out, partials).  partials is None when
     the plan kept the keys in one chunk (out is then final); otherwise it is (partial_o,
     partial_lse, partial_exp), views into `workspace` (a uint8 tensor) to finish with
     merge(partial_o, partial_lse, gate, out, partial_exp=partial_exp) on a stream ordered after
-    this one.  partial_o [C, B, Hq, rows, D] is fp32 with partial_exp None (small plans), or
-    fp16 with partial_exp [C, B, Hq, rows] int32, the partial being partial_o times
-    2^partial_exp (merge_args partial_kind 0 and 1)."""
+    this one, or by a later call's carry.  partial_o [C, B, Hq, rows, D] is fp32 with
+    partial_exp None (small plans), or fp16 with partial_exp [C, B, Hq, rows] int32, the partial
+    being partial_o times 2^partial_exp (merge_args partial_kind 0 and 1).
+    append = (k_new, v_new, k_cache, v_cache, kv_offset): a kv_append the call carries;
+    carry = (partial_o, partial_lse, partial_exp, gate, out) of an EARLIER call: its merge, done
+    by this call (attn_args carry: inside the main pass's launch where that has idle CUs); its
+    partials must not lie in `workspace`."""
     if kv_len is None:
         kv_len = kv_offset + q.shape[2]
     if out is None:
@@ -157,6 +173,11 @@ def prefill_partials(q, k_cache, v_cache, gate, *, kv_offset: int, workspace, kv
               head_chunk=head_chunk, n_splits=n_splits, mask=mask)
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor")
+    app = None
+    if append is not None:
+        app = _append_args(*append)
+        a.append = C.pointer(app)
+    _keep = _carry_args(a, carry)
     n, kind, off, eoff = C.c_int32(0), C.c_int32(0), C.c_size_t(0), C.c_size_t(0)
     _check(lib().attn_prefill_partials(C.byref(a), workspace.data_ptr(), workspace.numel(), _stream_handle(q),
                                        C.byref(n), C.byref(kind), C.byref(off), C.byref(eoff)))
@@ -174,13 +195,14 @@ def prefill_partials(q, k_cache, v_cache, gate, *, kv_offset: int, workspace, kv
 
 
 def prefill(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
-            n_splits=0, mask=None, out=None, workspace=None, append=None):
+            n_splits=0, mask=None, out=None, workspace=None, append=None, carry=None):
     """attn_prefill: q/gate [B, Hq, rows, D], caches [B, Hkv, capacity, D] (D = 256, 128 or 64); returns out.
     append = (k_new, v_new, k_cache, v_cache, kv_offset): a kv_append the call carries (attn_args
-    append: in the merge's launch when the keys are split), e.g. the next query block's rows."""
+    append: in the merge's launch when the keys are split), e.g. the next query block's rows.
+    carry: an earlier call's merge, as for prefill_partials."""
     return _run(_abi.OP_PREFILL, q, k_cache, v_cache, gate, kv_offset=kv_offset, kv_len=kv_len, causal=causal,
                 scale=scale, head_chunk=head_chunk, n_splits=n_splits, mask=mask, out=out, workspace=workspace,
-                append=append)
+                append=append, carry=carry)
 
 
 def decode(q, k_cache, v_cache, gate, *, kv_offset: int, kv_len=None, causal=True, scale=0.0, head_chunk=0,
@@ -263,12 +285,8 @@ def kv_keep(k_cache, v_cache, *, kv_offset: int, rows: int, keep) -> None:
         raise ValueError("k_cache and v_cache differ")
     _check(lib().kv_keep(C.byref(a), _stream_handle(k_cache)))
 
-def merge(partial_o, partial_lse, gate, out=None, partial_exp=None, append=None):
-    """attn_merge: partial_o [C, B, Hq, rows, D] (D 256, 128 or 64) fp32, or fp16 with
-    partial_exp [C, B, Hq, rows] int32 (the form prefill_partials returns: the partial is
-    partial_o times 2^partial_exp); partial_lse [C, B, Hq, rows] fp32 (natural log).
-    append = (k_new, v_new, k_cache, v_cache, kv_offset): a kv_append of those rows carried by
-    the same launch (it must not touch what the merge reads or writes)."""
+def _merge_args(partial_o, partial_lse, gate, out, partial_exp=None, append=None):
+    """MergeArgs for these partials (and the ctypes objects it points to, kept alive with it)."""
     if partial_o.dtype not in (torch.float32, torch.float16) or partial_lse.dtype != torch.float32:
         raise TypeError("partial_o is float32 or float16, partial_lse float32")
     fp16 = partial_o.dtype == torch.float16
@@ -279,8 +297,6 @@ def merge(partial_o, partial_lse, gate, out=None, partial_exp=None, append=None)
         raise ValueError("partial_exp is a contiguous int32 [C, B, Hq, rows]")
     if not partial_o.is_contiguous() or not partial_lse.is_contiguous():
         raise ValueError("partials must be contiguous")
-    if out is None:
-        out = torch.empty_like(gate, memory_format=torch.contiguous_format)
     a = _abi.MergeArgs()
     a.dtype = _dtype_code(gate)
     a.n_chunks, a.B, a.Hq, a.rows, a.D = partial_o.shape
@@ -295,6 +311,18 @@ def merge(partial_o, partial_lse, gate, out=None, partial_exp=None, append=None)
         k_new, v_new, k_cache, v_cache, kv_offset = append
         app = _append_args(k_new, v_new, k_cache, v_cache, kv_offset)
         a.append = C.pointer(app)
+    return a, app
+
+
+def merge(partial_o, partial_lse, gate, out=None, partial_exp=None, append=None):
+    """attn_merge: partial_o [C, B, Hq, rows, D] (D 256, 128 or 64) fp32, or fp16 with
+    partial_exp [C, B, Hq, rows] int32 (the form prefill_partials returns: the partial is
+    partial_o times 2^partial_exp); partial_lse [C, B, Hq, rows] fp32 (natural log).
+    append = (k_new, v_new, k_cache, v_cache, kv_offset): a kv_append of those rows carried by
+    the same launch (it must not touch what the merge reads or writes)."""
+    if out is None:
+        out = torch.empty_like(gate, memory_format=torch.contiguous_format)
+    a, _app = _merge_args(partial_o, partial_lse, gate, out, partial_exp, append)
     _check(lib().attn_merge(C.byref(a), _stream_handle(gate)))
     return out
 
@@ -375,12 +403,15 @@ def prompt_policy(*, D: int, B: int, Hq: int, Hkv: int, n_tokens: int, dtype: st
 
 
 def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int = 0, kv_offset: int = 0, out=None,
-                   workspace=None, head_chunk=0, n_splits=0, overlap_merge=False, composed=False):
+                   workspace=None, head_chunk=0, n_splits=0, overlap_merge=False, composed=False, carry_merge=True):
     """A prompt in query blocks: each block's K/V rows are appended to the caches (kv_append),
     then the block runs attn_prefill (attn_prefill_composed with composed=True).  On the fused
-    route without overlap_merge the first block's rows go by kv_append and every block's
-    attn_prefill carries the next block's rows (attn_args append: in the merge's launch when the
-    keys are split), one launch fewer per block.
+    route without overlap_merge the first block's rows go by kv_append and every block's call
+    carries the next block's rows (attn_args append).  With carry_merge (the default) each block
+    runs attn_prefill_partials into one of two workspaces, in turn, and carries the previous
+    block's merge (attn_args carry; inside its main pass's launch where that has idle CUs), the
+    last block's merge following on its own: one launch per block.  Without it each block runs
+    attn_prefill, its append in the merge's launch when the keys are split.
 
     q/gate [B, Hq, N, D] and k/v [B, Hkv, N, D] hold the prompt (positions kv_offset ..
     kv_offset + N - 1); k_cache/v_cache have room for them.  Block i attends to the cache plus
@@ -417,14 +448,44 @@ def prompt_prefill(q, k, v, gate, k_cache, v_cache, *, q_block: int = 0, kv_offs
             need = max(need, workspace_bytes(a, _abi.OP_PREFILL))
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if not overlap_merge:
-        # each block's call carries the next block's append (in its merge when the keys are split)
+        # each block's call carries the next block's append
         kv_append(k[:, :, :min(q_block, N)], v[:, :, :min(q_block, N)], k_cache, v_cache, kv_offset=kv_offset)
-        for s in range(0, N, q_block):
+
+        def nxt(e):
+            return (k[:, :, e:min(e + q_block, N)], v[:, :, e:min(e + q_block, N)], k_cache, v_cache,
+                    kv_offset + e) if e < N else None
+
+        if not carry_merge:
+            for s in range(0, N, q_block):
+                e = min(s + q_block, N)
+                prefill(q[:, :, s:e], k_cache, v_cache, gate[:, :, s:e], kv_offset=kv_offset + s,
+                        kv_len=kv_offset + e, out=out[:, :, s:e], workspace=workspace, head_chunk=head_chunk,
+                        n_splits=n_splits, append=nxt(e))
+            return out
+        # blocks whose plan carries work in the main pass's launch (attn_plan_info carry_blocks)
+        # take the previous block's merge there; the others run attn_prefill, their append in the
+        # merge's launch
+        spaces = [workspace, torch.empty_like(workspace)]
+        pending = None  # a block's partials, gate and out, merged by the next call
+        for i, s in enumerate(range(0, N, q_block)):
             e = min(s + q_block, N)
-            e2 = min(e + q_block, N)
-            nxt = (k[:, :, e:e2], v[:, :, e:e2], k_cache, v_cache, kv_offset + e) if e < N else None
+            a = plan_args(B=q.shape[0], Hq=q.shape[1], Hkv=k.shape[1], rows=e - s, kv_offset=kv_offset + s,
+                          capacity=k_cache.shape[2], head_chunk=head_chunk, n_splits=n_splits, D=q.shape[3],
+                          dtype="bf16" if q.dtype == torch.bfloat16 else "f16")
+            if describe_plan(a)["carry_blocks"] > 0:
+                _, parts = prefill_partials(q[:, :, s:e], k_cache, v_cache, gate[:, :, s:e], kv_offset=kv_offset + s,
+                                            kv_len=kv_offset + e, out=out[:, :, s:e], workspace=spaces[i % 2],
+                                            head_chunk=head_chunk, n_splits=n_splits, append=nxt(e), carry=pending)
+                pending = (*parts, gate[:, :, s:e], out[:, :, s:e])
+                continue
+            if pending is not None:
+                merge(pending[0], pending[1], pending[3], out=pending[4], partial_exp=pending[2])
+                pending = None
             prefill(q[:, :, s:e], k_cache, v_cache, gate[:, :, s:e], kv_offset=kv_offset + s, kv_len=kv_offset + e,
-                    out=out[:, :, s:e], workspace=workspace, head_chunk=head_chunk, n_splits=n_splits, append=nxt)
+                    out=out[:, :, s:e], workspace=spaces[i % 2], head_chunk=head_chunk, n_splits=n_splits,
+                    append=nxt(e))
+        if pending is not None:
+            merge(pending[0], pending[1], pending[3], out=pending[4], partial_exp=pending[2])
         return out
     main = torch.cuda.current_stream(q.device)
     side = merge_stream(q.device)

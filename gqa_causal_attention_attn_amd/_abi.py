@@ -7,7 +7,7 @@ The struct sizes are checked against the library's own (attn_struct_size) when i
 import ctypes as C
 import os
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 HEAD_DIM = 256
 MAX_DECODE_ROWS = 32
 MAX_CHUNKS = 64
@@ -48,12 +48,19 @@ class KvAppendArgs(C.Structure):
                 ("v_new", Tensor), ("k_cache", Tensor), ("v_cache", Tensor)]
 
 
+class MergeArgs(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("n_chunks", C.c_int32), ("B", C.c_int32), ("Hq", C.c_int32),
+                ("rows", C.c_int32), ("D", C.c_int32), ("partial_o", C.c_void_p), ("partial_lse", C.c_void_p),
+                ("gate", Tensor), ("out", Tensor), ("partial_kind", C.c_int32),
+                ("partial_exp", C.c_void_p), ("append", C.POINTER(KvAppendArgs))]
+
+
 class AttnArgs(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("D", C.c_int32),
                 ("rows", C.c_int32), ("kv_offset", C.c_int64), ("kv_len", C.c_int64), ("capacity", C.c_int64),
                 ("scale", C.c_float), ("causal", C.c_int32), ("head_chunk", C.c_int32), ("n_splits", C.c_int32),
                 ("q", Tensor), ("gate", Tensor), ("out", Tensor), ("k_cache", Tensor), ("v_cache", Tensor),
-                ("mask", Mask), ("append", C.POINTER(KvAppendArgs))]
+                ("mask", Mask), ("append", C.POINTER(KvAppendArgs)), ("carry", C.POINTER(MergeArgs))]
 
 
 class KvKeepArgs(C.Structure):
@@ -62,19 +69,13 @@ class KvKeepArgs(C.Structure):
                 ("keep", C.POINTER(C.c_uint32)), ("k_cache", Tensor), ("v_cache", Tensor)]
 
 
-class MergeArgs(C.Structure):
-    _fields_ = [("dtype", C.c_int32), ("n_chunks", C.c_int32), ("B", C.c_int32), ("Hq", C.c_int32),
-                ("rows", C.c_int32), ("D", C.c_int32), ("partial_o", C.c_void_p), ("partial_lse", C.c_void_p),
-                ("gate", Tensor), ("out", Tensor), ("partial_kind", C.c_int32),
-                ("partial_exp", C.c_void_p), ("append", C.POINTER(KvAppendArgs))]
-
-
 class PlanInfo(C.Structure):
     _fields_ = [("op", C.c_int32), ("variant", C.c_int32), ("group_size", C.c_int32), ("n_head_chunks", C.c_int32),
                 ("head_chunk", C.c_int32), ("rows_per_wave", C.c_int32), ("waves_per_block", C.c_int32),
                 ("n_row_tiles", C.c_int32), ("n_splits", C.c_int32), ("keys_per_split", C.c_int32),
                 ("keys_per_tile", C.c_int32), ("lds_bytes", C.c_int32), ("grid_blocks", C.c_int64),
-                ("workspace_bytes", C.c_int64), ("chunk_sizes", C.c_int32 * MAX_CHUNKS), ("partial_kind", C.c_int32)]
+                ("workspace_bytes", C.c_int64), ("chunk_sizes", C.c_int32 * MAX_CHUNKS), ("partial_kind", C.c_int32),
+                ("carry_blocks", C.c_int32)]
 
 
 class PromptQuery(C.Structure):

@@ -250,6 +250,19 @@ inline int variant_of(const attn_args* a, const Plan& P) {
   return dslot * 128 + P.mask_lds * 32 + P.shape * 8 + a->dtype * 4 + a->mask.kind;
 }
 
+// Workgroups a call of plan P adds to its main pass's launch for the work it carries (unmasked
+// prompt blocks writing fp16 partials that leave CUs idle and run long enough to cover a merge
+// the size of their own on those CUs).
+inline int carry_blocks_of(const attn_args* a, const Plan& P) {
+  if (P.shape != 2 || P.n_splits < 2 || P.part_kind != 1 || a->mask.kind != ATTN_MASK_NONE ||
+      P.grid >= gqa::kTargetBlocks)
+    return 0;
+  const int64_t idle = gqa::kTargetBlocks - P.grid;
+  const int64_t tiles = P.keys_per_split / gqa::tile_keys(a->D);
+  const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
+  return n_rows <= gqa::kCarryRowsPerTile * idle * tiles ? (int)idle : 0;
+}
+
 // Checks a kv_append call and fills its kernel parameters (kv_append, and an append carried by
 // attn_merge).
 int append_params(const kv_append_args* a, gqa::AppendParams* pp) {
@@ -281,6 +294,65 @@ int append_params(const kv_append_args* a, gqa::AppendParams* pp) {
   return ATTN_OK;
 }
 
+// Checks an attn_merge call and fills its kernel parameters (attn_merge, and a merge carried by
+// attn_args carry); no repair inputs.
+int merge_params(const merge_args* a, gqa::MergeParams* pp) {
+  if (!a) return ATTN_E_NULL;
+  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
+  if (a->B <= 0 || a->Hq <= 0) return ATTN_E_HEADS;
+  if (a->D != ATTN_HEAD_DIM && a->D != 64 && a->D != 128) return ATTN_E_HEAD_DIM;
+  if (a->rows < 1) return ATTN_E_ROWS;
+  if (a->n_chunks < 1) return ATTN_E_ARG;
+  const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
+  if (a->partial_kind != 0 && a->partial_kind != 1) return ATTN_E_ARG;
+  if (n_rows > (int64_t)INT32_MAX || !gqa::merge_fits(a->n_chunks, a->partial_kind, n_rows))
+    return ATTN_E_ARG;  // 32-bit rows, launch size
+  if (!a->partial_o || !a->partial_lse || !a->gate.ptr || !a->out.ptr) return ATTN_E_NULL;
+  if (a->partial_kind == 1 && !a->partial_exp) return ATTN_E_NULL;
+  if (!aligned16(a->partial_o) || !aligned16(a->gate.ptr) || !aligned16(a->out.ptr) || !strides_ok(a->gate) ||
+      !strides_ok(a->out) || (reinterpret_cast<uintptr_t>(a->partial_lse) & 3u) ||
+      (a->partial_kind == 1 && (reinterpret_cast<uintptr_t>(a->partial_exp) & 3u)))
+    return ATTN_E_LAYOUT;
+  gqa::MergeParams& p = *pp;
+  memset(&p, 0, sizeof(p));  // no main-pass inputs: no repair
+  p.part_o = a->partial_o;
+  p.part_lse = a->partial_lse;
+  p.part_e = a->partial_kind == 1 ? a->partial_exp : nullptr;
+  p.part_kind = a->partial_kind;
+  if (a->append) {  // checked as kv_append checks its arguments; nothing is enqueued on an error
+    const int st = append_params(a->append, &p.app);
+    if (st) return st;
+    if (!gqa::merge_with_append_fits(a->n_chunks, a->partial_kind, n_rows, p.app)) return ATTN_E_ARG;
+    p.carry = 1;
+  }
+  p.gate = static_cast<const uint16_t*>(a->gate.ptr);
+  p.out = static_cast<uint16_t*>(a->out.ptr);
+  p.g_sb = a->gate.stride_b, p.g_sh = a->gate.stride_h, p.g_sr = a->gate.stride_row;
+  p.o_sb = a->out.stride_b, p.o_sh = a->out.stride_h, p.o_sr = a->out.stride_row;
+  p.n_chunks = a->n_chunks, p.B = a->B, p.Hq = a->Hq, p.rows = a->rows, p.D = a->D;
+  return ATTN_OK;
+}
+
+// whether [p, p + n) and [q, q + m) share a byte
+inline bool overlaps(const void* p, size_t n, const void* q, size_t m) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return n && m && a < b + m && b < a + n;
+}
+
+// Checks the merge a call carries (attn_args carry): attn_merge's checks, no append of its own,
+// and partials clear of the `used` bytes of the call's workspace, which the call overwrites.
+int carry_params(const merge_args* c, const void* ws, size_t used, gqa::MergeParams* cm) {
+  const int st = merge_params(c, cm);
+  if (st) return st;
+  if (c->append) return ATTN_E_ARG;
+  const size_t nrow = (size_t)c->n_chunks * c->B * c->Hq * c->rows;
+  const size_t obytes = nrow * (size_t)gqa::partial_row_bytes(c->D, c->partial_kind);
+  if (overlaps(c->partial_o, obytes, ws, used) || overlaps(c->partial_lse, nrow * 4, ws, used) ||
+      (c->partial_kind == 1 && overlaps(c->partial_exp, nrow * 4, ws, used)))
+    return ATTN_E_ARG;
+  return ATTN_OK;
+}
+
 int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream, bool merge = true,
             int32_t* n_chunks = nullptr, int32_t* part_kind = nullptr, size_t* lse_offset = nullptr,
             size_t* exp_offset = nullptr) {
@@ -298,6 +370,19 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
     const bool carried = P.n_splits > 1 && merge;
     const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
     if (carried && !gqa::merge_with_append_fits(P.n_splits, P.part_kind, n_rows, app)) return ATTN_E_ARG;
+  }
+  gqa::MergeParams cm;  // the earlier call's merge this call carries, if any
+  if (a->carry && (st = carry_params(a->carry, ws, P.ws_bytes, &cm)) != ATTN_OK) return st;
+  // Work the main pass's launch carries, on the CUs it leaves idle (prompt blocks writing fp16
+  // partials, long enough to cover it): the carried merge when it is an fp16 merge of at most
+  // kFewChunks chunks in this call's dtype, and the append of a call that does not merge.
+  int extra = 0;
+  bool merge_in_launch = false, append_in_launch = false;
+  if (const int cb = carry_blocks_of(a, P)) {
+    merge_in_launch = a->carry && a->carry->partial_kind == 1 && a->carry->n_chunks <= gqa::kFewChunks &&
+                      a->carry->dtype == a->dtype;
+    append_in_launch = a->append && !merge;
+    if (merge_in_launch || append_in_launch) extra = cb;
   }
 
   gqa::FwdParams p;
@@ -339,7 +424,16 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
     p.part_e = P.part_kind == 1 ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + P.ws_e_offset) : nullptr;
     p.part_kind = P.part_kind;
   }
+  p.extra_blocks = extra;
+  if (merge_in_launch) p.carried = cm;
+  if (append_in_launch) {
+    p.carried.carry = 1;
+    p.carried.app = app;
+    p.carried.app_by = 2 * a->B * a->Hkv < extra ? 2 * a->B * a->Hkv : extra;
+    p.carried.app_bx = extra / p.carried.app_by;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a->carry && !merge_in_launch && gqa::launch_merge(cm, a->carry->dtype, s) != hipSuccess) return ATTN_E_HIP;
   if (n_chunks) *n_chunks = P.n_splits;
   if (part_kind) *part_kind = P.n_splits > 1 ? P.part_kind : 0;
   if (lse_offset) *lse_offset = P.n_splits > 1 ? P.ws_o_bytes : 0;
@@ -370,7 +464,7 @@ int run_fwd(const attn_args* a, int op, void* ws, size_t ws_bytes, void* stream,
       mp.app = app;
     }
     if (gqa::launch_merge(mp, a->dtype, s) != hipSuccess) return ATTN_E_HIP;
-  } else if (a->append) {
+  } else if (a->append && !append_in_launch) {
     if (gqa::launch_append(app, s) != hipSuccess) return ATTN_E_HIP;
   }
   return ATTN_OK;
@@ -529,6 +623,7 @@ int attn_describe_plan(const attn_args* a, int op, attn_plan_info* info) {
   info->lds_bytes = gqa::kFwdLdsBytes + (P.mask_lds ? gqa::kStages * gqa::kMaskStageLds : 0);
   info->grid_blocks = P.grid;
   info->partial_kind = P.n_splits > 1 ? P.part_kind : 0;
+  info->carry_blocks = carry_blocks_of(a, P);
   info->workspace_bytes = (int64_t)P.ws_bytes;
   for (int i = 0; i < P.n_chunks; ++i) info->chunk_sizes[i] = P.chunk_sizes[i];
   return ATTN_OK;
@@ -569,6 +664,9 @@ int attn_prefill_composed(const attn_args* a, void* workspace, size_t ws_bytes, 
   if (!aligned16(workspace)) return ATTN_E_LAYOUT;
   gqa::AppendParams app;  // the append the call carries: a launch of its own after the route's
   if (a->append && (st = append_params(a->append, &app)) != ATTN_OK) return st;
+  gqa::MergeParams cm;  // the merge the call carries: a launch of its own ahead of the route's
+  if (a->carry && (st = carry_params(a->carry, workspace, L.s_bytes + L.p_bytes + L.l_bytes, &cm)) != ATTN_OK)
+    return st;
   gqa::ComposedParams p;
   memset(&p, 0, sizeof(p));
   p.q = static_cast<const uint16_t*>(a->q.ptr);
@@ -591,6 +689,8 @@ int attn_prefill_composed(const attn_args* a, void* workspace, size_t ws_bytes, 
   p.kv_offset = (int)a->kv_offset, p.kv_len = (int)a->kv_len, p.causal = a->causal, p.kv_hi = (int)L.kv_hi;
   const float scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->D);
   p.scale_log2 = scale * 1.4426950408889634f;
+  if (a->carry && gqa::launch_merge(cm, a->carry->dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_E_HIP;
   if (gqa::launch_composed(p, a->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
   if (a->append && gqa::launch_append(app, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
@@ -632,39 +732,9 @@ int kv_keep(const kv_keep_args* a, void* stream) {
 }
 
 int attn_merge(const merge_args* a, void* stream) {
-  if (!a) return ATTN_E_NULL;
-  if (a->dtype != ATTN_BF16 && a->dtype != ATTN_F16) return ATTN_E_DTYPE;
-  if (a->B <= 0 || a->Hq <= 0) return ATTN_E_HEADS;
-  if (a->D != ATTN_HEAD_DIM && a->D != 64 && a->D != 128) return ATTN_E_HEAD_DIM;
-  if (a->rows < 1) return ATTN_E_ROWS;
-  if (a->n_chunks < 1) return ATTN_E_ARG;
-  const int64_t n_rows = (int64_t)a->B * a->Hq * a->rows;
-  if (a->partial_kind != 0 && a->partial_kind != 1) return ATTN_E_ARG;
-  if (n_rows > (int64_t)INT32_MAX || !gqa::merge_fits(a->n_chunks, a->partial_kind, n_rows))
-    return ATTN_E_ARG;  // 32-bit rows, launch size
-  if (!a->partial_o || !a->partial_lse || !a->gate.ptr || !a->out.ptr) return ATTN_E_NULL;
-  if (a->partial_kind == 1 && !a->partial_exp) return ATTN_E_NULL;
-  if (!aligned16(a->partial_o) || !aligned16(a->gate.ptr) || !aligned16(a->out.ptr) || !strides_ok(a->gate) ||
-      !strides_ok(a->out) || (reinterpret_cast<uintptr_t>(a->partial_lse) & 3u) ||
-      (a->partial_kind == 1 && (reinterpret_cast<uintptr_t>(a->partial_exp) & 3u)))
-    return ATTN_E_LAYOUT;
   gqa::MergeParams p;
-  memset(&p, 0, sizeof(p));  // no main-pass inputs: no repair
-  p.part_o = a->partial_o;
-  p.part_lse = a->partial_lse;
-  p.part_e = a->partial_kind == 1 ? a->partial_exp : nullptr;
-  p.part_kind = a->partial_kind;
-  if (a->append) {  // checked as kv_append checks its arguments; nothing is enqueued on an error
-    const int st = append_params(a->append, &p.app);
-    if (st) return st;
-    if (!gqa::merge_with_append_fits(a->n_chunks, a->partial_kind, n_rows, p.app)) return ATTN_E_ARG;
-    p.carry = 1;
-  }
-  p.gate = static_cast<const uint16_t*>(a->gate.ptr);
-  p.out = static_cast<uint16_t*>(a->out.ptr);
-  p.g_sb = a->gate.stride_b, p.g_sh = a->gate.stride_h, p.g_sr = a->gate.stride_row;
-  p.o_sb = a->out.stride_b, p.o_sh = a->out.stride_h, p.o_sr = a->out.stride_row;
-  p.n_chunks = a->n_chunks, p.B = a->B, p.Hq = a->Hq, p.rows = a->rows, p.D = a->D;
+  const int st = merge_params(a, &p);
+  if (st) return st;
   if (gqa::launch_merge(p, a->dtype, static_cast<hipStream_t>(stream)) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
 }

@@ -17,30 +17,21 @@
 #include <math.h>
 
 #include "attn_internal.h"
+#include "attn_merge_core.h"
 
 namespace gqa {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-template <int DT>
-__device__ __forceinline__ float to_f32(uint16_t w) {
-  if constexpr (DT == 0) return __builtin_bit_cast(float, (uint32_t)w << 16);
-  else return (float)__builtin_bit_cast(_Float16, w);
-}
-
-template <int DT>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  if constexpr (DT == 0) return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
-  else return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
-}
+using mcore::u32x4;
+using mcore::u32x2;
+using mcore::f32x4;
+using mcore::kLog2e;
+using mcore::to_f32;
+using mcore::pack2;
+using mcore::wave_max;
+using mcore::PartialLoad;
+using mcore::load_values;
+using mcore::decode_partial;
 
 // Nonfinite repair of a row (b, h, r) whose chunk partials hold a NaN (a key hidden from the
 // row met a nonfinite V value in a tile the row shared with others, and 0 * Inf became NaN):
@@ -123,68 +114,13 @@ __device__ __forceinline__ void exact_row(const RepairParams& f, int D, int b, i
   if (on) *reinterpret_cast<u32x2*>(orow + dl) = ow;
 }
 
-// Four values of a split partial row: KIND 0 fp32 rows of D values; KIND 1 the main pass's
-// fp16 rows, value times 2^e (partial_row_bytes; e from its own array, loaded by the caller).
-// Loads (issued together) and decode apart.
-template <int KIND>
-struct PartialLoad {
-  f32x4 f;    // KIND 0
-  u32x2 h;    // KIND 1: four fp16 values
-  int32_t e;  // KIND 1: the row's exponent
-};
-template <int KIND>
-__device__ __forceinline__ PartialLoad<KIND> load_values(const MergeParams& p, int64_t row, int dl) {
-  PartialLoad<KIND> x;
-  if constexpr (KIND == 0) {
-    x.f = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.part_o) + row * p.D + dl);
-  } else {
-    x.h = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.part_o) + row * p.D + dl);
-  }
-  return x;
-}
-template <int KIND>
-__device__ __forceinline__ f32x4 decode_partial(const PartialLoad<KIND>& x) {
-  if constexpr (KIND == 0) {
-    return x.f;
-  } else {
-    auto h2f = [](uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); };
-    return (f32x4){__builtin_amdgcn_ldexpf(h2f(x.h[0] & 0xffffu), x.e), __builtin_amdgcn_ldexpf(h2f(x.h[0] >> 16), x.e),
-                   __builtin_amdgcn_ldexpf(h2f(x.h[1] & 0xffffu), x.e), __builtin_amdgcn_ldexpf(h2f(x.h[1] >> 16), x.e)};
-  }
-}
-
-// One workgroup (bx, by) of a gx x gy append grid of `nt` threads: one 16-byte chunk per thread.
-// Grid row by = (tensor, b, g); x runs over (row r, chunk c of 8 elements) = (r << chunk_shift)
-// + c, so the index arithmetic is shifts (one division per grid row).
-__device__ __forceinline__ void append_part(const AppendParams& p, uint32_t bx, uint32_t by, uint32_t gx,
-                                            uint32_t gy, uint32_t nt) {
-  const int64_t bg = (int64_t)p.B * p.Hkv;
-  const int64_t n = (int64_t)p.rows << p.chunk_shift;
-  const int cmask = (1 << p.chunk_shift) - 1;
-  for (int64_t y = by; y < 2 * bg; y += gy) {
-    const int t = y >= bg;
-    const int64_t yb = y - (t ? bg : 0);
-    const int b = (int)(yb / p.Hkv), g = (int)(yb - (int64_t)b * p.Hkv);
-    const uint16_t* src = p.src[t] + b * p.s_sb[t] + g * p.s_sh[t];
-    uint16_t* dst = p.dst[t] + b * p.d_sb[t] + g * p.d_sh[t] +
-                    (int64_t)(p.kv_offset + (GQA_CONTROL == 3 ? 1 : 0)) * p.d_st[t];
-    const int64_t s_sr = p.s_sr[t], d_st = p.d_st[t];
-    for (int64_t u = (int64_t)bx * nt + threadIdx.x; u < n; u += (int64_t)gx * nt) {
-      const int64_t r = u >> p.chunk_shift;
-      const int c = (int)(u & cmask);
-      const u32x4 val = *reinterpret_cast<const u32x4*>(src + r * s_sr + 8 * c);
-      *reinterpret_cast<u32x4*>(dst + r * d_st + 8 * c) = val;
-    }
-  }
-}
-
 // Workgroups of a merge launch past the merge's own run the kv_append it carries; returns
 // whether this workgroup was one of them (the whole workgroup, so it leaves before any barrier).
 __device__ __forceinline__ bool merge_carried_append(const MergeParams& p) {
   if (blockIdx.x < (uint32_t)p.merge_blocks) return false;
   const uint32_t a = blockIdx.x - (uint32_t)p.merge_blocks;
   const uint32_t by = a / (uint32_t)p.app_bx;
-  append_part(p.app, a - by * (uint32_t)p.app_bx, by, (uint32_t)p.app_bx, (uint32_t)p.app_by, blockDim.x);
+  mcore::append_part<1>(p.app, a - by * (uint32_t)p.app_bx, by, (uint32_t)p.app_bx, (uint32_t)p.app_by, blockDim.x);
   return true;
 }
 
@@ -310,13 +246,6 @@ __global__ __launch_bounds__(MW * 64) void merge_kernel(const MergeParams p) {
   if (d0 < p.D) *reinterpret_cast<u32x2*>(orow + d0) = ow;
 }
 
-// largest value over the wavefront's 64 lanes (fmaxf: a NaN lane is passed over)
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
 // Chunks up to 64 (merge_slots): one wavefront per row, four rows per workgroup, four dims per
 // lane, and a partial load of every chunk slot issued at once (independent loads), so the pass
 // costs one round trip instead of a load after another.  NC slots: NC = the chunk count for up
@@ -366,50 +295,22 @@ __global__ __launch_bounds__(256) void merge_few_kernel(const MergeParams p) {
       asm volatile("" : "+v"(lse_lane) : "v"(raw[c].h));
     }
   }
-  // the row's largest lse, a NaN lse (which makes the row NaN, as the unsplit definition does)
-  // and each chunk's weight, all over the lanes that hold a chunk
-  const bool mine = lane < nch;
-  const float top = wave_max(mine ? lse_lane : -INFINITY);
-  const bool nan_l = __builtin_amdgcn_ballot_w64(mine && __builtin_isnan(lse_lane)) != 0;
-  const float w_lane = top > -INFINITY ? exp2f((lse_lane - top) * kLog2e) : 0.0f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.0f;
-  if (top > -INFINITY) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const float lc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lse_lane), c));
-      // an empty chunk is selected out, never multiplied in
-      if (c < nch && lc != -INFINITY) {
-        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_lane), c));
-        PartialLoad<KIND> x = raw[c];
-        if constexpr (KIND == 1) x.e = __builtin_amdgcn_readlane(e_lane, c);
-        acc += w * decode_partial<KIND>(x);
-        wsum += w;
-      }
-    }
-  }
+  const mcore::RowSums sums = mcore::row_sums<KIND, NC>(nch, lane, lse_lane, e_lane, raw);
   uint16_t* orow = p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr;
   // a NaN in a chunk's partial or lse with the main pass's inputs at hand: the row is computed
   // again (one wavefront per row)
-  if (p.fix.q && __builtin_amdgcn_ballot_w64(nan_l || __builtin_isnan(wsum) || (d0 < p.D && has_nan4(acc))) != 0) {
+  if (p.fix.q &&
+      __builtin_amdgcn_ballot_w64(sums.nan_l || __builtin_isnan(sums.wsum) || (d0 < p.D && has_nan4(sums.acc))) != 0) {
     exact_row<DT>(p.fix, p.D, b, h, r, lane, gw, orow);
     return;
   }
-  const float inv = nan_l ? NAN : wsum > 0.0f ? __builtin_amdgcn_rcpf(wsum) : 0.0f;
-  float gv[4] = {to_f32<DT>((uint16_t)(gw[0] & 0xffffu)), to_f32<DT>((uint16_t)(gw[0] >> 16)),
-                 to_f32<DT>((uint16_t)(gw[1] & 0xffffu)), to_f32<DT>((uint16_t)(gw[1] >> 16))};
-  float res[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) res[i] = acc[i] * inv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[i]));
-  u32x2 ow;
-  ow[0] = pack2<DT>(res[0], res[1]);
-  ow[1] = pack2<DT>(res[2], res[3]);
+  const u32x2 ow = mcore::gated_row<DT>(sums, gw);
   if (d0 < p.D) *reinterpret_cast<u32x2*>(orow + d0) = ow;
 }
 
 // kv_append: one workgroup of the append grid (append_part).  Head dims 64, 128 and 256.
 __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
-  append_part(p, blockIdx.x, blockIdx.y, gridDim.x, gridDim.y, 256);
+  mcore::append_part<1>(p, blockIdx.x, blockIdx.y, gridDim.x, gridDim.y, 256);
 }
 
 // kv_keep: one workgroup per (b, g).  Every kept row of the block is read into registers

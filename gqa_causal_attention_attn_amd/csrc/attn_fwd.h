@@ -74,6 +74,7 @@
 #include <type_traits>
 
 #include "attn_internal.h"
+#include "attn_merge_core.h"
 
 namespace gqa {
 namespace {
@@ -487,6 +488,79 @@ __device__ __forceinline__ void exact_pair(const FwdParams& p, int b, int h, int
   }
 }
 
+// ---- work carried by a prompt main pass's launch, in its workgroups past the main pass's own
+// (FwdParams extra_blocks, on CUs the main pass leaves idle): workgroup e of n_extra runs its
+// share of a kv_append (8 steps of its grid at a time) and then of the merge of an earlier query
+// block's fp16 partials.  The merge takes one wavefront per row with the merge kernel's
+// arithmetic (mcore::row_sums, gated_row) over kFewChunks chunk slots, so each row comes out
+// as attn_merge would give it; a wavefront has the loads of kCarriedRows rows in flight at
+// once.  No repair inputs travel with it: a NaN stays NaN, as with attn_merge on its own.
+constexpr int kCarriedRows = 4;
+template <int DT>
+__device__ void carried_work(const MergeParams& p, int e, int n_extra) {
+  if (p.carry && e < p.app_bx * p.app_by) {
+    const int by = e / p.app_bx;
+    mcore::append_part<8>(p.app, (uint32_t)(e - by * p.app_bx), (uint32_t)by, (uint32_t)p.app_bx,
+                          (uint32_t)p.app_by, blockDim.x);
+  }
+  if (p.n_chunks <= 0) return;
+  constexpr int NC = kFewChunks, R = kCarriedRows;
+  const int lane = threadIdx.x & 63;
+  const int wv = e * (int)(blockDim.x >> 6) + (int)(threadIdx.x >> 6);
+  const int n_wv = n_extra * (int)(blockDim.x >> 6);
+  const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
+  const int nch = GQA_CONTROL == 2 ? max(p.n_chunks - 1, 1) : p.n_chunks;
+  const int d0 = 4 * lane;
+  const int dl = min(d0, p.D - 4);  // lanes past the head dim re-read its last 4 dims and store nothing
+  for (int64_t base = (int64_t)wv * R; base < n_rows; base += (int64_t)n_wv * R) {
+    float lse_l[R];
+    int32_t e_l[R];
+    u32x2 gw[R];
+    uint32_t rw[R];
+    mcore::PartialLoad<1> raw[R][NC];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      // rows past the last re-read it and store nothing; (b, h, r) in 32-bit arithmetic (the
+      // host keeps B Hq rows below 2^31)
+      const uint32_t row32 = (uint32_t)min(base + i, n_rows - 1);
+      const uint32_t bh = row32 / (uint32_t)p.rows;
+      const int r = (int)(row32 - bh * (uint32_t)p.rows);
+      const int b = (int)(bh / (uint32_t)p.Hq);
+      const int h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
+      rw[i] = row32;
+      gw[i] = *reinterpret_cast<const u32x2*>(p.gate + (int64_t)b * p.g_sb + (int64_t)h * p.g_sh +
+                                              (int64_t)r * p.g_sr + dl);
+      const int64_t lrow = (int64_t)min(lane, nch - 1) * n_rows + row32;
+      lse_l[i] = p.part_lse[lrow];
+      e_l[i] = p.part_e[lrow];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) raw[i][c] = mcore::load_values<1>(p, (int64_t)min(c, nch - 1) * n_rows + row32, dl);
+    }
+    // every load of the R rows goes out before the first row's sums (one round trip)
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(lse_l[0]) : "v"(raw[i][c].h));
+      asm volatile("" : "+v"(lse_l[0]) : "v"(lse_l[i]), "v"(e_l[i]), "v"(gw[i]));
+    }
+    // the R rows' sums are independent (no branch between them, so their cross-lane steps
+    // interleave); a row past the last is computed and not stored
+    u32x2 ow[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) ow[i] = mcore::gated_row<DT>(mcore::row_sums<1, NC>(nch, lane, lse_l[i], e_l[i], raw[i]), gw[i]);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (base + i < n_rows && d0 < p.D) {
+        const uint32_t bh = rw[i] / (uint32_t)p.rows;
+        const int r = (int)(rw[i] - bh * (uint32_t)p.rows);
+        const int b = (int)(bh / (uint32_t)p.Hq);
+        const int h = (int)(bh - (uint32_t)b * (uint32_t)p.Hq);
+        *reinterpret_cast<u32x2*>(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr + d0) = ow[i];
+      }
+    }
+  }
+}
+
 template <int D, int DT, int MK, int W, bool LAG, int ML, int SPLIT>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) {
   static_assert(D == 256 || D == 128 || D == 64, "head dims 256, 128 and 64");
@@ -516,6 +590,15 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
   // the one before it finishes its P.V product.  Stage of tile t: t % kStages.
   // with the mask in LDS, kStages stages of its window follow the K/V stages
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kFwdLdsBytes + (ML ? kStages * kMaskStageLds : 0)];
+
+  // workgroups past the main pass's own run the work the launch carries (unmasked prompts: in
+  // the masked kernels the extra code cost the main loop registers)
+  if constexpr (LAG && SPLIT == 2 && MK == 0) {
+    if ((int)blockIdx.x >= p.grid) {
+      carried_work<DT>(p.carried, (int)blockIdx.x - p.grid, p.extra_blocks);
+      return;
+    }
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1189,7 +1272,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(const FwdParams p) 
 // layout in LDS (0: none, per-lane loads; 1: 16-byte rows, shape 2 at head dim 256 only; 2: words).
 template <int D, int DT, int MK, int SPLIT>
 hipError_t launch_fwd_s(const FwdParams& p, int shape, hipStream_t stream) {
-  const dim3 grid(p.grid), b4(256), b8(512);
+  // the carried work rides on the unmasked lagged shape with fp16 partials only (the host's plan)
+  if (p.extra_blocks != 0 && (SPLIT != 2 || shape != 2 || MK != 0)) return hipErrorInvalidValue;
+  const dim3 grid(p.grid + p.extra_blocks), b4(256), b8(512);
   const int ml = MK != 0 ? p.mask_lds : 0;
   if constexpr (MK != 0) {
     if (ml == 2) {

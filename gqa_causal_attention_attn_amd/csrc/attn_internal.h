@@ -30,45 +30,14 @@ constexpr int kStages = 4;                                   // LDS stages of (K
 constexpr int kPrefetch = 2;                                 // tiles in flight ahead of the one consumed
 constexpr int kFwdLdsBytes = kStages * kStageLds;            // 133,120 B
 constexpr int kTargetBlocks = 256;   // main-pass workgroups aimed for (one per CU)
+// A prompt main pass carries work on its idle CUs (FwdParams extra_blocks) when that work is
+// covered by the main pass: a merge the size of the call's own (n_rows rows) takes about 1.5 us
+// per row on one wavefront there, eight wavefronts a CU, and a main-pass tile 1.7 us or more at
+// every head dim, so the launch carries it when n_rows <= kCarryRowsPerTile x idle CUs x tiles
+// per split (8 leaves a margin of about 1.15).
+constexpr int64_t kCarryRowsPerTile = 8;
 constexpr int kMaskStageLds = 4352;  // LDS bytes per stage for the mask window of a tile (masked kernels)
 constexpr size_t kScratchBytes = (size_t)64 << 20;  // the device scratch of attn_decode_noalloc, per GPU
-
-// Parameters of the main (flash / split-KV) pass.  Strides are in elements.
-struct FwdParams {
-  const uint16_t* q;
-  const uint16_t* gate;
-  uint16_t* out;
-  const uint16_t* k;
-  const uint16_t* v;
-  const void* mask;
-  void* part_o;      // [n_splits, B, Hq, rows, D]: fp32 (part_kind 0) or fp16 (1, partial_row_bytes)
-  float* part_lse;   // [n_splits, B, Hq, rows]
-  int32_t* part_e;   // [n_splits, B, Hq, rows]: the power of two of each fp16 partial row
-  int part_kind;     // 0 or 1, as the merge's
-  int64_t q_sb, q_sh, q_sr;
-  int64_t g_sb, g_sh, g_sr;
-  int64_t o_sb, o_sh, o_sr;
-  int64_t k_sb, k_sh, k_st;
-  int64_t v_sb, v_sh, v_st;
-  int64_t m_sb, m_sh, m_sr;
-  int kv_offset;
-  int kv_len;
-  int B, Hq, Hkv, G, rows;
-  int causal;
-  float scale_log2;      // scale * log2(e)
-  float scale;           // the score scale itself (additive masks add in natural-log units)
-  int chunk;             // heads per chunk
-  int blocks_per_chunk;  // column blocks serving one chunk
-  int n_tiles;           // workgroups per (batch, kv head, split)
-  int n_splits;
-  int keys_per_split;    // multiple of kKeysPerTile
-  int grid;              // workgroups in the launch
-  int mask_lds;          // mask window of each tile staged in LDS: 0 no (per-lane loads), 1 in
-                         // 16-byte row chunks, 2 one dword per key (see attn_fwd.h)
-  int mask_pairs;        // with mask_lds 2: the window's rows are the mask rows of the workgroup's
-                         // (head, row) pairs (a full-head mask, one column block of pairs)
-                         // instead of its query rows (a mask the same for every head)
-};
 
 // The main pass's inputs, handed to the merge so that it can compute a chunk partial again
 // when the main pass left a NaN in it (a key hidden from a row met a nonfinite V value in a
@@ -123,6 +92,50 @@ struct MergeParams {
   AppendParams app;
   int app_bx, app_by;
   int merge_blocks;
+};
+
+// Parameters of the main (flash / split-KV) pass.  Strides are in elements.
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* gate;
+  uint16_t* out;
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* mask;
+  void* part_o;      // [n_splits, B, Hq, rows, D]: fp32 (part_kind 0) or fp16 (1, partial_row_bytes)
+  float* part_lse;   // [n_splits, B, Hq, rows]
+  int32_t* part_e;   // [n_splits, B, Hq, rows]: the power of two of each fp16 partial row
+  int part_kind;     // 0 or 1, as the merge's
+  int64_t q_sb, q_sh, q_sr;
+  int64_t g_sb, g_sh, g_sr;
+  int64_t o_sb, o_sh, o_sr;
+  int64_t k_sb, k_sh, k_st;
+  int64_t v_sb, v_sh, v_st;
+  int64_t m_sb, m_sh, m_sr;
+  int kv_offset;
+  int kv_len;
+  int B, Hq, Hkv, G, rows;
+  int causal;
+  float scale_log2;      // scale * log2(e)
+  float scale;           // the score scale itself (additive masks add in natural-log units)
+  int chunk;             // heads per chunk
+  int blocks_per_chunk;  // column blocks serving one chunk
+  int n_tiles;           // workgroups per (batch, kv head, split)
+  int n_splits;
+  int keys_per_split;    // multiple of kKeysPerTile
+  int grid;              // workgroups in the launch
+  int mask_lds;          // mask window of each tile staged in LDS: 0 no (per-lane loads), 1 in
+                         // 16-byte row chunks, 2 one dword per key (see attn_fwd.h)
+  int mask_pairs;        // with mask_lds 2: the window's rows are the mask rows of the workgroup's
+                         // (head, row) pairs (a full-head mask, one column block of pairs)
+                         // instead of its query rows (a mask the same for every head)
+  // Work carried by the launch (prompt main passes writing fp16 partials, on CUs the main pass
+  // leaves idle): workgroups grid .. grid + extra_blocks - 1 run it instead of the main pass.
+  // carried.n_chunks > 0: the merge of an earlier call's fp16 partials (at most kFewChunks
+  // chunks, no repair inputs); carried.carry = 1: the kv_append carried.app over an
+  // app_bx x app_by grid of those workgroups.
+  int extra_blocks;
+  MergeParams carried;
 };
 
 constexpr int kKeepMaxBatch = 64;  // keep masks travel in the kernel arguments

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GQA_ATTN_ABI_VERSION 6
+#define GQA_ATTN_ABI_VERSION 7
 #define ATTN_HEAD_DIM 256
 #define ATTN_MAX_DECODE_ROWS 32
 #define ATTN_MAX_CHUNKS 64
@@ -101,6 +101,7 @@ typedef struct {
 } attn_mask;
 
 typedef struct kv_append_args kv_append_args;
+typedef struct merge_args merge_args;
 
 /* Arguments of attn_prefill / attn_decode. */
 typedef struct {
@@ -123,13 +124,29 @@ typedef struct {
   attn_tensor k_cache; /* [B, Hkv, capacity, 256] */
   attn_tensor v_cache; /* [B, Hkv, capacity, 256] */
   attn_mask mask;
-  const kv_append_args* append; /* NULL, or a kv_append enqueued with the call's last launch: in
-                                   the merge's launch when the call splits the keys (workgroups of
-                                   its own, one launch fewer), else a launch of its own after the
-                                   call.  Checked as kv_append checks it, with the call's other
-                                   arguments, before anything is enqueued.  Unordered with the
-                                   merge, so it must not touch what the call reads or writes; a
-                                   prompt's loop passes the next query block's rows */
+  const kv_append_args* append; /* NULL, or a kv_append enqueued with the call: in the merge's
+                                   launch when the call splits the keys and merges them (workgroups
+                                   of its own, one launch fewer); for attn_prefill_partials, in the
+                                   main pass's launch where that carries work (see carry), else a
+                                   launch of its own after the call.  Checked as kv_append checks
+                                   it, with the call's other arguments, before anything is
+                                   enqueued.  Unordered with the call's own work, so it must not
+                                   touch what the call reads or writes; a prompt's loop passes the
+                                   next query block's rows */
+  const merge_args* carry;      /* NULL, or an attn_merge of an EARLIER call's split partials (say
+                                   the previous query block's, from attn_prefill_partials), done by
+                                   this call and unordered with the rest of it: its partials, gate
+                                   and out must not be touched by this call (partials overlapping
+                                   this call's workspace: ATTN_E_ARG), and its own append must be
+                                   NULL (else ATTN_E_ARG).  Checked as attn_merge checks it, before
+                                   anything is enqueued.  Where the call's plan has carry_blocks
+                                   (attn_plan_info: an unmasked prompt block writing fp16 partials
+                                   that leaves CUs idle) and the merge is of at most 8 chunks of
+                                   fp16 partials in the call's dtype, it runs on those CUs inside
+                                   the main pass's launch (the same bits as attn_merge); otherwise
+                                   it is a launch of its own ahead of the main pass.  A prompt's
+                                   loop carries block i - 1's merge with block i's main pass: one
+                                   launch per block */
 } attn_args;
 
 /* Arguments of kv_append: k_cache[b, g, kv_offset + r, :] = k_new[b, g, r, :] (and V), bit for bit. */
@@ -171,7 +188,7 @@ typedef struct {
 } kv_keep_args;
 
 /* Arguments of attn_merge. */
-typedef struct {
+struct merge_args {
   int32_t dtype;
   int32_t n_chunks;         /* >= 1 */
   int32_t B;
@@ -194,7 +211,7 @@ typedef struct {
                                    the append must not touch what the merge reads or writes.  A
                                    prompt's loop enqueues block i's merge with block i + 1's append,
                                    one launch fewer per block */
-} merge_args;
+};
 
 /* The resolved plan of one call (what would run, for logging and validation). */
 typedef struct {
@@ -215,6 +232,12 @@ typedef struct {
   int32_t chunk_sizes[ATTN_MAX_CHUNKS]; /* heads per chunk within a KV group, first n_head_chunks valid */
   int32_t partial_kind;    /* with n_splits > 1: the split partials' form (merge_args partial_kind;
                               1 from 8 MiB of fp32 partials up), else 0 */
+  int32_t carry_blocks;    /* workgroups the main pass's launch adds for work a call carries on the
+                              CUs it leaves idle (attn_args carry, and the append of
+                              attn_prefill_partials): unmasked prompt blocks with fp16 partials
+                              whose main pass is long enough to cover, on those CUs, a merge of
+                              its own size (B Hq rows <= 8 x idle CUs x tiles per split); 0 where
+                              such work gets launches of its own */
 } attn_plan_info;
 
 /* A prompt to be run as query blocks (kv_append + attn_prefill per block), for

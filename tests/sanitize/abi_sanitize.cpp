@@ -91,6 +91,17 @@ hipError_t launch_fwd_any(const FwdParams& p, int dtype, int mask_kind, int shap
   CHECK(p.keys_per_split % 32 == 0, "keys_per_split %d", p.keys_per_split);
   CHECK((p.n_splits > 1) == (p.part_o != nullptr), "partials %d", p.n_splits);
   CHECK(p.G * p.Hkv == p.Hq && p.chunk >= 1 && p.chunk <= p.G, "chunk %d", p.chunk);
+  // carried work: only on the lagged shape writing fp16 partials, and only on CUs left idle
+  CHECK(p.extra_blocks == 0 || (shape == 2 && p.n_splits > 1 && p.part_kind == 1 &&
+                                p.grid + p.extra_blocks == kTargetBlocks),
+        "extra blocks %d on shape %d, grid %d", p.extra_blocks, shape, p.grid);
+  CHECK(p.extra_blocks > 0 || (p.carried.n_chunks == 0 && p.carried.carry == 0), "carried work without blocks");
+  CHECK(p.carried.n_chunks == 0 || (p.carried.part_kind == 1 && p.carried.n_chunks <= kFewChunks &&
+                                    p.carried.part_e && !p.carried.fix.q),
+        "carried merge %d chunks kind %d", p.carried.n_chunks, p.carried.part_kind);
+  CHECK(!p.carried.carry || (p.carried.app_bx >= 1 && p.carried.app_by >= 1 &&
+                             p.carried.app_bx * p.carried.app_by <= p.extra_blocks),
+        "carried append grid %d x %d", p.carried.app_bx, p.carried.app_by);
   return hipSuccess;
 }
 
@@ -480,8 +491,109 @@ void aux_calls() {
 
 }  // namespace
 
+// attn_args carry: an earlier block's merge inside the main pass's launch where the plan allows
+// it (attn_plan_info carry_blocks), a launch of its own ahead of the main pass otherwise, and the
+// checks that refuse it before anything is enqueued.
+void carried_merge() {
+  kv_append_args ap;
+  memset(&ap, 0, sizeof(ap));
+  ap.dtype = 0, ap.B = 1, ap.Hkv = 4, ap.D = 256, ap.rows = 512, ap.capacity = 32768;
+  ap.k_new = t4(4, 512, 256, 8), ap.v_new = t4(4, 512, 256, 9), ap.k_cache = t4(4, 32768, 256, 10),
+  ap.v_cache = t4(4, 32768, 256, 11);
+  // the last 512-row block of a 32k prompt at 24/4 heads: 5 splits over 240 workgroups
+  auto pa = args(1, 24, 4, 512, 32256);
+  pa.capacity = 32768, pa.k_cache = t4(4, 32768, 256, 4), pa.v_cache = t4(4, 32768, 256, 5);
+  attn_plan_info info;
+  CHECK(attn_describe_plan(&pa, ATTN_OP_PREFILL, &info) == ATTN_OK && info.n_splits == 5 &&
+            info.partial_kind == 1 && info.grid_blocks == 240 && info.carry_blocks == 16,
+        "last prompt block: %d splits, kind %d, grid %ld, carry %d", info.n_splits, info.partial_kind,
+        (long)info.grid_blocks, info.carry_blocks);
+  const size_t need = (size_t)info.workspace_bytes;
+  // the previous block's partials, in a second workspace
+  const int64_t nrow = 5LL * 24 * 512;
+  char* const ws2 = kDev + (uintptr_t(12) << 36);
+  merge_args m;
+  memset(&m, 0, sizeof(m));
+  m.dtype = 0, m.n_chunks = 5, m.B = 1, m.Hq = 24, m.rows = 512, m.D = 256, m.partial_kind = 1;
+  m.partial_o = ws2;
+  m.partial_lse = reinterpret_cast<const float*>(ws2 + nrow * 512);
+  m.partial_exp = reinterpret_cast<const int32_t*>(ws2 + nrow * 512 + nrow * 4);
+  m.gate = t4(24, 512, 256, 13), m.out = t4(24, 512, 256, 14);
+  pa.carry = &m;
+  pa.append = &ap;
+  ap.kv_offset = 32768 - 512;  // (any rows the call does not read; here the block's own, as a placeholder)
+  int32_t nc = 0, kind = 0;
+  size_t lo = 0, eo = 0;
+  long f0 = g_launch_fwd, m0 = g_launch_merge, o0 = g_launch_other;
+  CHECK(attn_prefill_partials(&pa, kWs, need, kStream, &nc, &kind, &lo, &eo) == ATTN_OK && g_launch_fwd == f0 + 1 &&
+            g_launch_merge == m0 && g_launch_other == o0,
+        "merge and append carried in the main pass's launch");
+  CHECK(g_fwd.extra_blocks == 16 && g_fwd.carried.n_chunks == 5 && g_fwd.carried.part_o == ws2 &&
+            g_fwd.carried.carry == 1 && g_fwd.carried.app.rows == 512 && g_fwd.carried.app_by == 8 &&
+            g_fwd.carried.app_bx == 2,
+        "carried work: %d blocks, %d chunks, append %d x %d", g_fwd.extra_blocks, g_fwd.carried.n_chunks,
+        g_fwd.carried.app_bx, g_fwd.carried.app_by);
+  // attn_prefill merges itself: the append rides on that merge, the carried merge in the launch
+  f0 = g_launch_fwd, m0 = g_launch_merge, o0 = g_launch_other;
+  CHECK(attn_prefill(&pa, kWs, need, kStream) == ATTN_OK && g_launch_fwd == f0 + 1 && g_launch_merge == m0 + 1 &&
+            g_launch_other == o0 && g_fwd.extra_blocks == 16 && g_fwd.carried.n_chunks == 5 &&
+            g_fwd.carried.carry == 0 && g_merge.carry == 1,
+        "attn_prefill carrying a merge");
+  // fp32 partials or more than 8 chunks: a merge launch of its own ahead of the main pass (the
+  // append still rides in the launch)
+  merge_args m32 = m;
+  m32.partial_kind = 0, m32.partial_exp = nullptr;
+  pa.carry = &m32;
+  f0 = g_launch_fwd, m0 = g_launch_merge, o0 = g_launch_other;
+  CHECK(attn_prefill_partials(&pa, kWs, need, kStream, &nc, &kind, &lo, &eo) == ATTN_OK && g_launch_fwd == f0 + 1 &&
+            g_launch_merge == m0 + 1 && g_launch_other == o0 && g_fwd.extra_blocks == 16 &&
+            g_fwd.carried.n_chunks == 0 && g_fwd.carried.carry == 1,
+        "fp32 carried merge launched on its own");
+  merge_args m12 = m;
+  m12.n_chunks = 12;
+  pa.carry = &m12;
+  pa.append = nullptr;
+  f0 = g_launch_fwd, m0 = g_launch_merge, o0 = g_launch_other;
+  CHECK(attn_prefill_partials(&pa, kWs, need, kStream, &nc, &kind, &lo, &eo) == ATTN_OK && g_launch_fwd == f0 + 1 &&
+            g_launch_merge == m0 + 1 && g_launch_other == o0 && g_fwd.extra_blocks == 0,
+        "12-chunk carried merge launched on its own, nothing carried");
+  // refused before any launch: partials in this call's workspace, an append of its own, null
+  // partials, a bad kind
+  merge_args bad = m;
+  bad.partial_lse = reinterpret_cast<const float*>(kWs + 4096);
+  pa.carry = &bad;
+  const long before = launches();
+  CHECK(attn_prefill_partials(&pa, kWs, need, kStream, &nc, &kind, &lo, &eo) == ATTN_E_ARG, "carry in the workspace");
+  bad = m, bad.append = &ap;
+  CHECK(attn_prefill(&pa, kWs, need, kStream) == ATTN_E_ARG, "carry with an append of its own");
+  bad = m, bad.partial_o = nullptr;
+  CHECK(attn_prefill(&pa, kWs, need, kStream) == ATTN_E_NULL, "carry without partials");
+  bad = m, bad.partial_kind = 3;
+  CHECK(attn_prefill(&pa, kWs, need, kStream) == ATTN_E_ARG, "carry of an unknown kind");
+  CHECK(launches() == before, "refused carries launch nothing");
+  // a short block (16 tiles over 4 splits): nothing carried in the launch
+  auto pb = args(1, 24, 4, 512, 0);
+  pb.capacity = 32768, pb.k_cache = t4(4, 32768, 256, 4), pb.v_cache = t4(4, 32768, 256, 5);
+  CHECK(attn_describe_plan(&pb, ATTN_OP_PREFILL, &info) == ATTN_OK && info.n_splits > 1 && info.carry_blocks == 0,
+        "first prompt block carries nothing (%d splits)", info.n_splits);
+  pb.carry = &m;
+  pb.append = &ap;
+  ap.kv_offset = 512;
+  f0 = g_launch_fwd, m0 = g_launch_merge, o0 = g_launch_other;
+  CHECK(attn_prefill_partials(&pb, kWs, (size_t)info.workspace_bytes, kStream, &nc, &kind, &lo, &eo) == ATTN_OK &&
+            g_launch_fwd == f0 + 1 && g_launch_merge == m0 + 1 && g_launch_other == o0 + 1 && g_fwd.extra_blocks == 0,
+        "short block: merge before, append after");
+  // the composed route: the carried merge ahead of it
+  pb.append = nullptr;
+  m0 = g_launch_merge, o0 = g_launch_other;
+  CHECK(attn_prefill_composed(&pb, kWs, (size_t)1 << 34, kStream) == ATTN_OK && g_launch_merge == m0 + 1 &&
+            g_launch_other == o0 + 1,
+        "composed route carrying a merge");
+}
+
 int main() {
   rejection_matrix();
+  carried_merge();
   launch_limits();
   sweep();
   aux_calls();

@@ -345,6 +345,67 @@ def test_carried_append_is_checked_before_the_call():
         app.dtype = 0
 
 
+@pytest.mark.parametrize("D", [256, 128])
+def test_carry_blocks_of_prompt_plans(D):
+    # a 512-row block of the 24/4-head prompt (12,288 rows, 240 workgroups over 5 splits) carries
+    # work in its main pass's launch (attn_args carry, the append of attn_prefill_partials) on the
+    # 16 CUs left idle once 8 x 16 x its tiles per split reach its rows: from 96 tiles per split
+    # (480 tiles of keys) on; earlier blocks carry nothing.  A 1024-row block (192 workgroups over
+    # 2 splits, 24,576 rows) carries from 48 tiles per split on, on 64 idle CUs.
+    T = 8192 // D
+    cases = [(512, 0, 0), (512, 460 * T - 512, 0), (512, 480 * T - 512, 16), (512, 32768 - 512, 16),
+             (1024, 94 * T - 1024, 0), (1024, 96 * T - 1024, 64)]
+    for rows, off, want in cases:
+        d = ga.describe_plan(_good(rows=rows, kv_offset=off, capacity=32768, D=D))
+        assert d["carry_blocks"] == want, (rows, off, d)
+        if want:
+            assert d["partial_kind"] == 1 and d["grid_blocks"] + want == 256
+    # decode rows never carry
+    assert ga.describe_plan(_good(rows=32, kv_offset=32768, capacity=40000, D=D), _abi.OP_DECODE)["carry_blocks"] == 0
+
+
+def test_carried_merge_is_checked_before_the_call():
+    # attn_args carry: attn_merge's checks, no append of its own, partials clear of the call's
+    # workspace; each error comes back before anything runs (no device here: a launch would
+    # fail with ATTN_E_HIP instead)
+    lib = ga.lib()
+    t = _abi.Tensor(1 << 40, 24 * 512 * 256, 512 * 256, 256)
+    a = _good(rows=512, kv_offset=32256, capacity=32768)
+    need = ga.workspace_bytes(a, _abi.OP_PREFILL)
+    ws = 1 << 36
+    m = _abi.MergeArgs(0, 5, 1, 24, 512, 256, 1 << 38, (1 << 38) + (1 << 30), t, t)
+    m.partial_kind, m.partial_exp = 1, (1 << 38) + (1 << 31)
+    a.carry = C.pointer(m)
+    n, kind, off, eoff = C.c_int32(0), C.c_int32(0), C.c_size_t(0), C.c_size_t(0)
+    outs = [C.byref(n), C.byref(kind), C.byref(off), C.byref(eoff)]
+    S = _abi.STATUS_CODE
+
+    def run():
+        return lib.attn_prefill_partials(C.byref(a), ws, need, None, *outs)
+    m.partial_lse = ws + 4096  # inside this call's workspace
+    assert run() == S["ATTN_E_ARG"]
+    m.partial_lse = (1 << 38) + 2
+    assert run() == S["ATTN_E_LAYOUT"]
+    m.partial_lse = (1 << 38) + (1 << 30)
+    m.partial_kind = 2
+    assert run() == S["ATTN_E_ARG"]
+    m.partial_kind, m.partial_exp = 1, None
+    assert run() == S["ATTN_E_NULL"]
+    m.partial_exp = (1 << 38) + (1 << 31)
+    m.D = 96
+    assert run() == S["ATTN_E_HEAD_DIM"]
+    m.D = 256
+    app = _abi.KvAppendArgs(0, 1, 4, 256, 512, 0, 32256, 32768, t, t, t, t)
+    m.append = C.pointer(app)  # a carried merge carries no append of its own
+    assert run() == S["ATTN_E_ARG"]
+    assert lib.attn_prefill(C.byref(a), ws, need, None) == S["ATTN_E_ARG"]
+    m.append = None
+    comp = _good(rows=64, kv_offset=0)
+    comp.carry = C.pointer(m)
+    m.partial_o = None
+    assert lib.attn_prefill_composed(C.byref(comp), ws, 1 << 30, None) == S["ATTN_E_NULL"]
+
+
 def test_prefill_partials_needs_its_outputs():
     lib = ga.lib()
     a = _good(rows=512, kv_offset=4096)

@@ -339,6 +339,31 @@ def test_merge_matches_oracle(n_chunks, D):
     _say(assert_close(got, ref, f"merge {n_chunks} chunks, D={D}"))
 
 
+@needs_gpu
+@pytest.mark.parametrize("n_chunks", [2, 5, 8, 24, 40])
+def test_merge_with_lse_far_apart(n_chunks):
+    # chunk lse values drawn over [-600, 0] (natural log) with each row's largest in a random
+    # chunk, so in any lane of the wavefront that holds the chunks: weights below the largest
+    # underflow, and a row max taken short of the true one would overflow exp (Inf or NaN rows).
+    # 1024 rows: the one-wavefront merge with the chunk count (up to 8) or 24 / 40 slots.
+    rng = np.random.default_rng(600 + n_chunks)
+    B, Hq, rows, D = 1, 8, 128, 256
+    o = rng.standard_normal((n_chunks, B, Hq, rows, D))
+    lse = rng.uniform(-600.0, 0.0, (n_chunks, B, Hq, rows))
+    top = rng.integers(0, n_chunks, (B, Hq, rows))
+    np.put_along_axis(lse, top[None], rng.uniform(-1.0, 1.0, (1, B, Hq, rows)), axis=0)
+    gb = syn.normal_bits(np.random.default_rng(7), (B, Hq, rows, D))
+    out = torch.full((B, Hq, rows, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ga.merge(torch.from_numpy(o.astype(np.float32)).cuda(), torch.from_numpy(lse.astype(np.float32)).cuda(),
+             to_dev(gb), out=out)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    assert np.isfinite(got).all()
+    ref = reference.merge(o.astype(np.float32).astype(np.float64), lse.astype(np.float32).astype(np.float64),
+                          syn.widen(gb))
+    _say(assert_close(got, ref, f"merge of {n_chunks} chunks with lse far apart"))
+
+
 def _fp16_rows(o):
     """The main pass's partial form (merge_args partial_kind 1) of float64 partials o [..., D]:
     per row the exponent e that puts the largest magnitude in [0.5, 1) (0 for a zero or nonfinite
@@ -606,3 +631,112 @@ def test_prefill_carrying_the_next_blocks_append(n_splits, D):
     ref = reference.attention(*(syn.widen(x) for x in (qb, kb[:, :, :off + rows], vb[:, :, :off + rows], gb)),
                               n_kv_heads=Hkv, kv_offset=off, kv_len=off + rows)
     _say(assert_close(to_f64(o1), ref, f"prefill carrying an append, n_splits={n_splits}, D={D}"))
+
+
+def _sampled_rows(o, qx, gx, kb, vb, off, rows_sel, Hkv, what):
+    """Oracle rows one by one: row r of a block at kv_offset off sees keys 0 .. off + r."""
+    ref = np.stack([reference.attention(syn.widen(qx[:, :, r:r + 1]), syn.widen(kb[:, :, :off + r + 1]),
+                                        syn.widen(vb[:, :, :off + r + 1]), syn.widen(gx[:, :, r:r + 1]),
+                                        n_kv_heads=Hkv, kv_offset=off + int(r), kv_len=off + int(r) + 1)[:, :, 0]
+                    for r in rows_sel], axis=2)
+    got = to_f64(o[:, :, torch.as_tensor(rows_sel, device=o.device)])
+    _say(assert_close(got, ref, what))
+
+
+@needs_gpu
+@pytest.mark.parametrize("D", [256, 128])
+def test_prefill_carrying_the_previous_blocks_merge(D):
+    # Two 512-row query blocks of a 24/4-head prompt whose plans carry work in the main pass's
+    # launch (5 splits of 96 and 100 tiles, fp16 partials, 16 idle CUs): block B's
+    # attn_prefill_partials carries block A's merge (attn_args carry) and the next block's
+    # append.  Block A's output is attn_merge's, block B's partials and output are those of the
+    # calls made apart, and the caches those of a kv_append, all bit for bit; sampled rows of
+    # both outputs match the oracle.
+    rng = syn.streams(131)
+    B, Hq, Hkv, rows = 1, 24, 4, 512
+    off_a = 480 * (8192 // D) - rows
+    off_b = off_a + rows
+    kv = off_b + 2 * rows
+    qb = syn.normal_bits(rng["q"], (B, Hq, 2 * rows, D))
+    gb = syn.normal_bits(rng["gate"], (B, Hq, 2 * rows, D))
+    kb = syn.normal_bits(rng["k"], (B, Hkv, kv, D))
+    vb = syn.normal_bits(rng["v"], (B, Hkv, kv, D))
+    q, g = to_dev(qb), to_dev(gb)
+    qa, qb_, ga_, gb_ = q[:, :, :rows], q[:, :, rows:], g[:, :, :rows], g[:, :, rows:]
+    for off in (off_a, off_b):
+        d = ga.describe_plan(ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off, capacity=kv, D=D))
+        _say("plan at", off, {k_: d[k_] for k_ in ("n_splits", "partial_kind", "grid_blocks", "carry_blocks")})
+        assert d["carry_blocks"] > 0 and d["partial_kind"] == 1
+    need = ga.workspace_bytes(ga.plan_args(B=B, Hq=Hq, Hkv=Hkv, rows=rows, kv_offset=off_b, capacity=kv, D=D))
+
+    def caches():
+        kc = torch.full((B, Hkv, kv, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        vc = torch.full_like(kc, float("nan"))
+        kc[:, :, :off_b + rows] = to_dev(kb[:, :, :off_b + rows])
+        vc[:, :, :off_b + rows] = to_dev(vb[:, :, :off_b + rows])
+        return kc, vc
+
+    kn, vn = to_dev(kb[:, :, off_b + rows:]), to_dev(vb[:, :, off_b + rows:])
+    res = []
+    for carried in (False, True):
+        kc, vc = caches()
+        ws = [torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        oa = torch.full((B, Hq, rows, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ob = torch.full_like(oa, float("nan"))
+        _, pa = ga.prefill_partials(qa, kc, vc, ga_, kv_offset=off_a, out=oa, workspace=ws[0])
+        if carried:
+            _, pb = ga.prefill_partials(qb_, kc, vc, gb_, kv_offset=off_b, out=ob, workspace=ws[1],
+                                        carry=(*pa, ga_, oa), append=(kn, vn, kc, vc, off_b + rows))
+        else:
+            ga.merge(pa[0], pa[1], ga_, out=oa, partial_exp=pa[2])
+            _, pb = ga.prefill_partials(qb_, kc, vc, gb_, kv_offset=off_b, out=ob, workspace=ws[1])
+            ga.kv_append(kn, vn, kc, vc, kv_offset=off_b + rows)
+        parts = [t.clone() for t in pb]
+        ga.merge(pb[0], pb[1], gb_, out=ob, partial_exp=pb[2])
+        torch.cuda.synchronize()
+        res.append((oa, ob, parts, kc, vc))
+    (oa0, ob0, p0, k0, v0), (oa1, ob1, p1, k1, v1) = res
+    assert torch.equal(oa0.view(torch.int16), oa1.view(torch.int16)), "carried merge differs from attn_merge"
+    assert torch.equal(ob0.view(torch.int16), ob1.view(torch.int16))
+    for x, y in zip(p0, p1):
+        assert torch.equal(x.view(torch.int32) if x.element_size() == 4 else x.view(torch.int16),
+                           y.view(torch.int32) if y.element_size() == 4 else y.view(torch.int16))
+    assert torch.equal(k1.view(torch.int16), to_dev(kb).view(torch.int16))
+    assert torch.equal(v1.view(torch.int16), to_dev(vb).view(torch.int16))
+    sel = np.unique(np.concatenate([[0, 1, 255, 511], np.random.default_rng(D).choice(rows, 12, replace=False)]))
+    _sampled_rows(oa1, qb[:, :, :rows], gb[:, :, :rows], kb, vb, off_a, sel, Hkv, f"block A (D={D}), merge carried")
+    _sampled_rows(ob1, qb[:, :, rows:], gb[:, :, rows:], kb, vb, off_b, sel, Hkv, f"block B (D={D})")
+
+
+@needs_gpu
+def test_prompt_with_carried_merges_matches_the_plain_loop():
+    # prompt_prefill over 4 blocks of 1024 rows (24/4 heads, 2 splits, 64 idle CUs): with
+    # carry_merge the blocks whose plans carry work (blocks 2 and 3: 48 tiles per split and more)
+    # take the previous block's merge and the next block's append in their main pass's launch; the
+    # output and the caches are those of the loop of attn_prefill calls, bit for bit, and sampled
+    # rows match the oracle
+    _say("prompt with carried merges")
+    N = 4096
+    carrying = [ga.describe_plan(ga.plan_args(B=1, Hq=24, Hkv=4, rows=1024, kv_offset=s, capacity=N))["carry_blocks"]
+                for s in range(0, N, 1024)]
+    assert carrying[0] == 0 and carrying[2] > 0 and carrying[3] > 0, carrying
+    qb, kb, vb, gb, _ = prompt(2200, B=1, Hq=24, Hkv=4, N=N)
+    q, k, v, g = (to_dev(x) for x in (qb, kb, vb, gb))
+    outs = []
+    for carry in (False, True):
+        kc = torch.full((1, 4, N, 256), float("nan"), dtype=q.dtype, device="cuda")
+        vc = torch.full_like(kc, float("nan"))
+        out = torch.full_like(q, float("nan"))
+        ga.prompt_prefill(q, k, v, g, kc, vc, q_block=1024, out=out, carry_merge=carry)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(kc), kb) and np.array_equal(to_bits(vc), vb)
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    rows = np.unique(np.concatenate([[0, 1023, 1024, 2047, 2048, 3071, 3072, 4095],
+                                     np.random.default_rng(5).choice(N, 10, replace=False)]))
+    k64, v64 = syn.widen(kb), syn.widen(vb)
+    ref = np.stack([reference.attention(syn.widen(qb[:, :, r:r + 1]), k64, v64, syn.widen(gb[:, :, r:r + 1]),
+                                        n_kv_heads=4, kv_offset=int(r), kv_len=int(r) + 1)[:, :, 0] for r in rows],
+                   axis=2)
+    got = to_f64(outs[1][:, :, torch.as_tensor(rows, device="cuda")])
+    _say(assert_close(got, ref, "prompt with carried merges, sampled rows"))
