@@ -716,7 +716,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic and traffic.get("prefill_main_bytes"),
-                     "kernel": "attn_fwd_kernel (main pass of a prefill block)",
+                     "kernel": "attn_fwd_kernel (main pass of a prefill block; where the block's plan has "
+                               "carry_blocks, the launch also runs the previous block's merge and the next "
+                               "block's append on the CUs the main pass leaves idle)",
                      "avg_launch_us": round(float(call_mean_ms.mean()) * 1e3, 2)},
         "plans": {"validated": len(plans.samples), "samples": [s for s in plans.samples
                                                                if "block" not in s["sample"]
