@@ -334,8 +334,9 @@ int attn_prefill(const attn_args* a, void* workspace, size_t ws_bytes, void* str
  * attn_decode_noalloc) take the same main pass, plans, head chunks, masks and nonfinite repair
  * as 256; the partials hold rows of head_dim values, and scale = 0 means 1 / sqrt(head_dim). */
 
-/* The main pass of attn_prefill alone, for callers that overlap one query block's merge with
- * the next block's main pass (two workspaces, the merges on a second stream).  *n_chunks
+/* The main pass of attn_prefill alone, for callers that put one query block's merge beside the
+ * next block's main pass (two workspaces, in turn): the next call's attn_args carry (inside its
+ * main pass's launch where its plan has carry_blocks), or attn_merge on a second stream.  *n_chunks
  * receives the number of KV chunks of the plan.  With *n_chunks = 1 the call is complete and out
  * is written.  With *n_chunks > 1 out is not written: the normalised partials stay in the
  * workspace in the form *partial_kind gives (that of merge_args): o at offset 0
