@@ -491,25 +491,19 @@ __device__ __forceinline__ void exact_pair(const FwdParams& p, int b, int h, int
 // ---- work carried by a prompt main pass's launch, in its workgroups past the main pass's own
 // (FwdParams extra_blocks, on CUs the main pass leaves idle): workgroup e of n_extra runs its
 // share of a kv_append (8 steps of its grid at a time) and then of the merge of an earlier query
-// block's fp16 partials.  The merge takes one wavefront per row with the merge kernel's
-// arithmetic (mcore::row_sums, gated_row) over kFewChunks chunk slots, so each row comes out
-// as attn_merge would give it; a wavefront has the loads of kCarriedRows rows in flight at
-// once.  No repair inputs travel with it: a NaN stays NaN, as with attn_merge on its own.
-constexpr int kCarriedRows = 4;
-template <int DT>
-__device__ void carried_work(const MergeParams& p, int e, int n_extra) {
-  if (p.carry && e < p.app_bx * p.app_by) {
-    const int by = e / p.app_bx;
-    mcore::append_part<8>(p.app, (uint32_t)(e - by * p.app_bx), (uint32_t)by, (uint32_t)p.app_bx,
-                          (uint32_t)p.app_by, blockDim.x);
-  }
-  if (p.n_chunks <= 0) return;
-  constexpr int NC = kFewChunks, R = kCarriedRows;
+// block's fp16 partials.  The merge takes one wavefront per row with the arithmetic of the merge
+// kernel of as many chunk slots as chunks (mcore::row_sums<1, NC>, gated_row), so each row comes
+// out as attn_merge gives it; a wavefront has the loads of R rows in flight at once (R from the
+// registers NC slots leave).  No repair inputs travel with it: a NaN stays NaN, as with
+// attn_merge on its own.
+template <int DT, int NC>
+__device__ void carried_merge(const MergeParams& p, int e, int n_extra) {
+  constexpr int R = NC <= 3 ? 8 : NC <= 5 ? 6 : 4;  // rows in flight per wavefront
   const int lane = threadIdx.x & 63;
   const int wv = e * (int)(blockDim.x >> 6) + (int)(threadIdx.x >> 6);
   const int n_wv = n_extra * (int)(blockDim.x >> 6);
   const int64_t n_rows = (int64_t)p.B * p.Hq * p.rows;
-  const int nch = GQA_CONTROL == 2 ? max(p.n_chunks - 1, 1) : p.n_chunks;
+  const int nch = GQA_CONTROL == 2 ? (NC > 1 ? NC - 1 : 1) : NC;
   const int d0 = 4 * lane;
   const int dl = min(d0, p.D - 4);  // lanes past the head dim re-read its last 4 dims and store nothing
   for (int64_t base = (int64_t)wv * R; base < n_rows; base += (int64_t)n_wv * R) {
@@ -558,6 +552,26 @@ __device__ void carried_work(const MergeParams& p, int e, int n_extra) {
         *reinterpret_cast<u32x2*>(p.out + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)r * p.o_sr + d0) = ow[i];
       }
     }
+  }
+}
+
+template <int DT>
+__device__ void carried_work(const MergeParams& p, int e, int n_extra) {
+  if (p.carry && e < p.app_bx * p.app_by) {
+    const int by = e / p.app_bx;
+    mcore::append_part<8>(p.app, (uint32_t)(e - by * p.app_bx), (uint32_t)by, (uint32_t)p.app_bx,
+                          (uint32_t)p.app_by, blockDim.x);
+  }
+  switch (p.n_chunks) {  // 0: no merge carried; the host carries merges of at most kFewChunks chunks
+    case 1: carried_merge<DT, 1>(p, e, n_extra); break;
+    case 2: carried_merge<DT, 2>(p, e, n_extra); break;
+    case 3: carried_merge<DT, 3>(p, e, n_extra); break;
+    case 4: carried_merge<DT, 4>(p, e, n_extra); break;
+    case 5: carried_merge<DT, 5>(p, e, n_extra); break;
+    case 6: carried_merge<DT, 6>(p, e, n_extra); break;
+    case 7: carried_merge<DT, 7>(p, e, n_extra); break;
+    case 8: carried_merge<DT, 8>(p, e, n_extra); break;
+    default: break;
   }
 }
 

@@ -31,11 +31,11 @@ constexpr int kPrefetch = 2;                                 // tiles in flight 
 constexpr int kFwdLdsBytes = kStages * kStageLds;            // 133,120 B
 constexpr int kTargetBlocks = 256;   // main-pass workgroups aimed for (one per CU)
 // A prompt main pass carries work on its idle CUs (FwdParams extra_blocks) when that work is
-// covered by the main pass: a merge the size of the call's own (n_rows rows) takes about 1.5 us
-// per row on one wavefront there, eight wavefronts a CU, and a main-pass tile 1.7 us or more at
-// every head dim, so the launch carries it when n_rows <= kCarryRowsPerTile x idle CUs x tiles
-// per split (8 leaves a margin of about 1.15).
-constexpr int64_t kCarryRowsPerTile = 8;
+// covered by the main pass: a merge the size of the call's own (n_rows rows, five fp16 chunks)
+// takes about 1.25 us per row on one wavefront there, eight wavefronts a CU, and a main-pass tile
+// 1.7 us or more at every head dim, so the launch carries it when n_rows <= kCarryRowsPerTile x
+// idle CUs x tiles per split (10 leaves a margin of about 1.1).
+constexpr int64_t kCarryRowsPerTile = 10;
 constexpr int kMaskStageLds = 4352;  // LDS bytes per stage for the mask window of a tile (masked kernels)
 constexpr size_t kScratchBytes = (size_t)64 << 20;  // the device scratch of attn_decode_noalloc, per GPU
 

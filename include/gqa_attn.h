@@ -236,7 +236,7 @@ typedef struct {
                               CUs it leaves idle (attn_args carry, and the append of
                               attn_prefill_partials): unmasked prompt blocks with fp16 partials
                               whose main pass is long enough to cover, on those CUs, a merge of
-                              its own size (B Hq rows <= 8 x idle CUs x tiles per split); 0 where
+                              its own size (B Hq rows <= 10 x idle CUs x tiles per split); 0 where
                               such work gets launches of its own */
 } attn_plan_info;
 

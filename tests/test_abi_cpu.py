@@ -349,12 +349,12 @@ def test_carried_append_is_checked_before_the_call():
 def test_carry_blocks_of_prompt_plans(D):
     # a 512-row block of the 24/4-head prompt (12,288 rows, 240 workgroups over 5 splits) carries
     # work in its main pass's launch (attn_args carry, the append of attn_prefill_partials) on the
-    # 16 CUs left idle once 8 x 16 x its tiles per split reach its rows: from 96 tiles per split
-    # (480 tiles of keys) on; earlier blocks carry nothing.  A 1024-row block (192 workgroups over
-    # 2 splits, 24,576 rows) carries from 48 tiles per split on, on 64 idle CUs.
+    # 16 CUs left idle once 10 x 16 x its tiles per split reach its rows: from 77 tiles per split
+    # (381 tiles of keys) on; earlier blocks carry nothing.  A 1024-row block (192 workgroups over
+    # 2 splits, 24,576 rows) carries from 39 tiles per split on, on 64 idle CUs.
     T = 8192 // D
-    cases = [(512, 0, 0), (512, 460 * T - 512, 0), (512, 480 * T - 512, 16), (512, 32768 - 512, 16),
-             (1024, 94 * T - 1024, 0), (1024, 96 * T - 1024, 64)]
+    cases = [(512, 0, 0), (512, 380 * T - 512, 0), (512, 385 * T - 512, 16), (512, 32768 - 512, 16),
+             (1024, 76 * T - 1024, 0), (1024, 78 * T - 1024, 64)]
     for rows, off, want in cases:
         d = ga.describe_plan(_good(rows=rows, kv_offset=off, capacity=32768, D=D))
         assert d["carry_blocks"] == want, (rows, off, d)
